@@ -1,0 +1,247 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module draws random numbers and rounds them to the storage precision of
+each workload. It holds none of the attention arithmetic: the HIP library and
+the fp64 oracle both receive exactly the values produced here.
+
+Recipe (every workload):
+  * one numpy ``Generator(PCG64)`` per (workload, tensor, b, h[, step]) slice,
+    seeded with ``SeedSequence([workload_id, tensor_id, b, h(, step)])``;
+  * draw fp64 standard normals, multiply by the workload's scale in fp64,
+    round to fp32 (round-to-nearest-even), and for bf16 workloads round the
+    fp32 value once more to bf16 (round-to-nearest-even);
+  * tensor ids: Q=0, K=1, V=2, W=3, decode q=4, k=5, v=6.
+
+The FAVOR+ projection W (m rows of dimension d) is an *input*: the random
+features of the Performer map are drawn here once and handed to both sides.
+Rows come in blocks of d mutually orthogonal directions (QR of a Gaussian
+d x d matrix with the sign of R's diagonal folded in), each row rescaled to
+the length of an independent N(0, I_d) draw, so every row keeps the N(0, I_d)
+marginal the Performer map assumes while rows within a block are orthogonal
+(Story of Attention Part 5, section 1b).
+"""
+from __future__ import annotations
+
+import math
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_W = 0, 1, 2, 3
+TENSOR_QSTEP, TENSOR_KSTEP, TENSOR_VSTEP = 4, 5, 6
+
+
+# ---------------------------------------------------------------------------
+# rounding helpers (storage formats, not attention arithmetic)
+# ---------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounding = ((u >> 16) & 1) + 0x7FFF
+    out = ((u + rounding) >> 16).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to the fp32 values they encode (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class HostTensor:
+    """A seeded tensor in its storage format plus its exact fp32 value.
+
+    ``store`` is what the device receives (fp32 values, or uint16 bf16 bits);
+    ``f32`` is the same set of numbers as fp32, which the oracle widens to
+    fp64 without any rounding.
+    """
+    store: np.ndarray
+    f32: np.ndarray
+    dtype: str  # "f32" or "bf16"
+
+    @property
+    def shape(self):
+        return self.f32.shape
+
+
+def _round_to(x64: np.ndarray, dtype: str) -> HostTensor:
+    x32 = x64.astype(np.float32)
+    if dtype == "f32":
+        return HostTensor(store=x32, f32=x32, dtype="f32")
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x32)
+        return HostTensor(store=bits, f32=bf16_bits_to_f32(bits), dtype="bf16")
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _slice_draw(key, n):
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+    return rng.standard_normal(n)
+
+
+def _fill_slices(args):
+    """Worker body: draw a run of slices into a shared fp32 buffer."""
+    shm_name, shape, key_prefix, scale, lo, hi, per = args
+    from multiprocessing import shared_memory
+    shm = shared_memory.SharedMemory(name=shm_name)
+    try:
+        buf = np.ndarray(shape, dtype=np.float32, buffer=shm.buf)
+        flat = buf.reshape(-1, per)
+        H = shape[1]
+        for s in range(lo, hi):
+            b, h = divmod(s, H)
+            flat[s] = (_slice_draw(tuple(key_prefix) + (b, h), per) * scale).astype(np.float32)
+    finally:
+        shm.close()
+    return hi - lo
+
+
+def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: str,
+                extra=(), workers: int | None = None) -> HostTensor:
+    """Seeded N(0, scale^2) tensor of shape [B, H, n, d] (n may be 1).
+
+    Slice (b, h) depends only on (workload_id, tensor_id, *extra, b, h), so any
+    slice can be regenerated on its own.  Large tensors are drawn in a small
+    pool of spawned worker processes; the values do not depend on the pool.
+    """
+    B, H = shape[0], shape[1]
+    per = int(np.prod(shape[2:]))
+    key_prefix = (workload_id, tensor_id) + tuple(extra)
+    total = B * H * per
+    if workers is None:
+        workers = 1 if total < (1 << 26) else min(16, os.cpu_count() or 1)
+    if workers <= 1:
+        out = np.empty((B * H, per), dtype=np.float64)
+        for s in range(B * H):
+            b, h = divmod(s, H)
+            out[s] = _slice_draw(key_prefix + (b, h), per)
+        out *= scale
+        return _round_to(out.reshape(shape), dtype)
+
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    shm = shared_memory.SharedMemory(create=True, size=total * 4)
+    try:
+        ctx = mp.get_context("spawn")
+        nsl = B * H
+        step = (nsl + workers * 4 - 1) // (workers * 4)
+        jobs = [(shm.name, tuple(shape), key_prefix, scale, lo, min(nsl, lo + step), per)
+                for lo in range(0, nsl, step)]
+        with ctx.Pool(workers) as pool:
+            done = sum(pool.map(_fill_slices, jobs))
+        assert done == nsl
+        x32 = np.ndarray(tuple(shape), dtype=np.float32, buffer=shm.buf).copy()
+    finally:
+        shm.close()
+        shm.unlink()
+    if dtype == "f32":
+        return HostTensor(store=x32, f32=x32, dtype="f32")
+    bits = f32_to_bf16_bits(x32)
+    return HostTensor(store=bits, f32=bf16_bits_to_f32(bits), dtype="bf16")
+
+
+def orthogonal_gaussian_rows(workload_id: int, m: int, d: int) -> np.ndarray:
+    """FAVOR+ projection rows w_1..w_m (fp32 [m, d]), orthogonal within blocks of d."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, TENSOR_W])))
+    rows = []
+    while len(rows) * d < m:
+        g = rng.standard_normal((d, d))
+        qm, rm = np.linalg.qr(g)
+        qm = qm * np.sign(np.diag(rm))[None, :]
+        rows.append(qm.T)  # rows of an orthogonal matrix
+    w = np.concatenate(rows, axis=0)[:m]
+    lengths = np.linalg.norm(rng.standard_normal((m, d)), axis=1)
+    return (w * lengths[:, None]).astype(np.float32)
+
+
+def iid_gaussian_rows(seed: int, m: int, d: int) -> np.ndarray:
+    """Plain i.i.d. N(0, I_d) projection rows (fp64), used by statistical checks."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TENSOR_W, 1])))
+    return rng.standard_normal((m, d))
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int
+    phi: str            # "elu1" or "favor"
+    dtype: str          # "f32" or "bf16"
+    B: int
+    H: int
+    N: int
+    dk: int
+    dv: int
+    scale: float
+    chunk: int
+    m: int = 0          # FAVOR+ feature count
+    modes: tuple = ("causal",)
+    decode_steps: int = 0  # > 0: N is the prefix length, then this many decode steps
+
+    @property
+    def dprime(self) -> int:
+        return self.m if self.phi == "favor" else self.dk
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.N
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("elu1_f32_b1h2n256d64", 1, "elu1", "f32", 1, 2, 256, 64, 64, 1.0, 64,
+                 modes=("noncausal", "causal")),
+        Workload("elu1_bf16_b4h8n2048d64_c64", 2, "elu1", "bf16", 4, 8, 2048, 64, 64,
+                 1.0 / math.sqrt(64), 64),
+        Workload("elu1_bf16_b2h16n16384d128_c128", 3, "elu1", "bf16", 2, 16, 16384, 128, 128,
+                 1.0 / math.sqrt(128), 128),
+        Workload("decode_elu1_f32_s256h32d128_prefix1024_steps64", 4, "elu1", "f32", 256, 32,
+                 1024, 128, 128, 1.0 / math.sqrt(128), 64, decode_steps=64),
+        Workload("favor_bf16_b2h8n8192d64_m256_c64", 5, "favor", "bf16", 2, 8, 8192, 64, 64,
+                 64 ** -0.25, 64, m=256),
+    ]
+}
+
+
+@dataclass
+class ForwardInputs:
+    wl: Workload
+    Q: HostTensor
+    K: HostTensor
+    V: HostTensor
+    W: np.ndarray | None = None  # fp32 [m, dk] for FAVOR+
+
+
+def forward_inputs(wl: Workload, N: int | None = None, workers=None) -> ForwardInputs:
+    """Q, K, V of a forward workload (optionally a shorter prefix length N)."""
+    n = wl.N if N is None else N
+    shp_k = (wl.B, wl.H, n, wl.dk)
+    shp_v = (wl.B, wl.H, n, wl.dv)
+    Q = normal_bhnd(wl.wid, TENSOR_Q, shp_k, wl.scale, wl.dtype, workers=workers)
+    K = normal_bhnd(wl.wid, TENSOR_K, shp_k, wl.scale, wl.dtype, workers=workers)
+    V = normal_bhnd(wl.wid, TENSOR_V, shp_v, wl.scale, wl.dtype, workers=workers)
+    W = orthogonal_gaussian_rows(wl.wid, wl.m, wl.dk) if wl.phi == "favor" else None
+    return ForwardInputs(wl, Q, K, V, W)
+
+
+def decode_step_inputs(wl: Workload, step: int):
+    """Single-token q, k, v ([B, H, 1, d]) of one decode step."""
+    q = normal_bhnd(wl.wid, TENSOR_QSTEP, (wl.B, wl.H, 1, wl.dk), wl.scale, wl.dtype, extra=(step,))
+    k = normal_bhnd(wl.wid, TENSOR_KSTEP, (wl.B, wl.H, 1, wl.dk), wl.scale, wl.dtype, extra=(step,))
+    v = normal_bhnd(wl.wid, TENSOR_VSTEP, (wl.B, wl.H, 1, wl.dv), wl.scale, wl.dtype, extra=(step,))
+    return q, k, v
+
+
+def custom_inputs(seed: int, B, H, N, dk, dv, scale=1.0, dtype="f32", phi="elu1", m=0):
+    """Small seeded inputs for edge-case tests (any shape)."""
+    Q = normal_bhnd(1000 + seed, TENSOR_Q, (B, H, N, dk), scale, dtype)
+    K = normal_bhnd(1000 + seed, TENSOR_K, (B, H, N, dk), scale, dtype)
+    V = normal_bhnd(1000 + seed, TENSOR_V, (B, H, N, dv), scale, dtype)
+    W = orthogonal_gaussian_rows(1000 + seed, m, dk) if phi == "favor" else None
+    wl = Workload(f"custom{seed}", 1000 + seed, phi, dtype, B, H, N, dk, dv, scale, 64, m=m)
+    return ForwardInputs(wl, Q, K, V, W)

@@ -1,0 +1,192 @@
+"""fp64 CPU oracle for kernelized linear attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library
+(``kernelized_linear_attention_la_amd``) never imports, links or runs it, and
+the two share no code.
+
+The arithmetic lives in ``la_oracle.c`` (plain C, double precision, OpenMP
+over independent (batch, head) slices); this module only builds it with gcc,
+loads it with ctypes and widens numpy inputs to float64.  Each wrapper below
+names the definition it evaluates; the C source cites the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+_LIB = os.path.join(_HERE, "liblaoracle.so")
+
+PHI_ELU1 = 0
+PHI_FAVOR = 1
+_PHI = {"elu1": PHI_ELU1, "favor": PHI_FAVOR}
+
+
+def build(force: bool = False) -> str:
+    """Compile la_oracle.c into liblaoracle.so with gcc (fp64, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+               "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        D = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        L.ora_phi.argtypes = [i, i, i, D, i, D, D]
+        L.ora_state_read.argtypes = [i, i, i, D, D, D, D, D]
+        L.ora_noncausal.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_causal_recurrent.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D, D, D]
+        L.ora_quadratic.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, i, D]
+        L.ora_causal_chunked.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, i, D, D, D]
+        L.ora_decode_step.argtypes = [i, i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_num_threads.restype = ctypes.c_int
+        L.ora_set_num_threads.argtypes = [i]
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return lib().ora_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().ora_set_num_threads(int(n))
+
+
+def _d(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _kind(phi):
+    return _PHI[phi] if isinstance(phi, str) else int(phi)
+
+
+def _dp(phi, dk, W):
+    return W.shape[0] if _kind(phi) == PHI_FAVOR else dk
+
+
+def _flat4(x):
+    x = _d(x)
+    B, H = x.shape[0], x.shape[1]
+    return x.reshape(B * H, *x.shape[2:]), (B, H)
+
+
+def phi(kind, X, W=None):
+    """Feature map applied to each row of X [n, d] -> [n, dp]."""
+    X = _d(X)
+    n, d = X.shape
+    Wd = _d(W) if W is not None else None
+    m = Wd.shape[0] if Wd is not None else 0
+    dp = m if _kind(kind) == PHI_FAVOR else d
+    out = np.empty((n, dp))
+    lib().ora_phi(_kind(kind), n, d, _p(X), m, _p(Wd), _p(out))
+    return out
+
+
+def state_read(phiQ, S, z):
+    """num = phiQ S and den = phiQ z for phiQ [n, dp], S [dp, dv], z [dp]."""
+    phiQ, S, z = _d(phiQ), _d(S), _d(z)
+    n, dp = phiQ.shape
+    dv = S.shape[1]
+    num = np.empty((n, dv))
+    den = np.empty((n,))
+    lib().ora_state_read(n, dp, dv, _p(phiQ), _p(S), _p(z), _p(num), _p(den))
+    return num, den
+
+
+def _prep(phi_kind, Q, K, V, W):
+    (Qf, (B, H)), (Kf, _), (Vf, _) = _flat4(Q), _flat4(K), _flat4(V)
+    BH, N, dk = Qf.shape
+    dv = Vf.shape[2]
+    Wd = _d(W) if W is not None else None
+    m = Wd.shape[0] if Wd is not None else 0
+    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    return Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp
+
+
+def noncausal(phi_kind, Q, K, V, W=None):
+    """Non-causal factorised attention. Returns O [B,H,N,dv], S [B,H,dp,dv], z [B,H,dp]."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dp, dv)); z = np.empty((BH, dp))
+    lib().ora_noncausal(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf),
+                        _p(O), _p(S), _p(z))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv), z.reshape(B, H, dp)
+
+
+def _state_in(S_in, z_in, BH, dp, dv):
+    if S_in is None:
+        return None, None
+    return _d(S_in).reshape(BH, dp, dv), _d(z_in).reshape(BH, dp)
+
+
+def causal_recurrent(phi_kind, Q, K, V, W=None, S_in=None, z_in=None):
+    """Causal token-by-token recurrence. Returns O, S_final, z_final."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    Si, zi = _state_in(S_in, z_in, BH, dp, dv)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dp, dv)); z = np.empty((BH, dp))
+    lib().ora_causal_recurrent(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf),
+                               _p(Si), _p(zi), _p(O), _p(S), _p(z))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv), z.reshape(B, H, dp)
+
+
+def quadratic(phi_kind, Q, K, V, W=None, S_in=None, z_in=None, causal=True):
+    """Explicit pairwise (parallel-mode) form; O only."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    Si, zi = _state_in(S_in, z_in, BH, dp, dv)
+    O = np.empty((BH, N, dv))
+    lib().ora_quadratic(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf),
+                        _p(Si), _p(zi), int(bool(causal)), _p(O))
+    return O.reshape(B, H, N, dv)
+
+
+def causal_chunked(phi_kind, Q, K, V, chunk, W=None, S_in=None, z_in=None):
+    """Chunkwise hybrid (quadratic inside chunks, state between). Returns O, S, z."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    Si, zi = _state_in(S_in, z_in, BH, dp, dv)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dp, dv)); z = np.empty((BH, dp))
+    lib().ora_causal_chunked(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf),
+                             _p(Si), _p(zi), int(chunk), _p(O), _p(S), _p(z))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv), z.reshape(B, H, dp)
+
+
+def decode_step(phi_kind, q, k, v, S, z, W=None):
+    """One decode step; q,k [B,H,dk] (or [B,H,1,dk]), v [B,H,dv].
+
+    Returns (o [B,H,dv], S_new, z_new); the inputs are not modified.
+    """
+    q = _d(q); k = _d(k); v = _d(v)
+    B, H = q.shape[0], q.shape[1]
+    dk = q.shape[-1]; dv = v.shape[-1]
+    BH = B * H
+    Wd = _d(W) if W is not None else None
+    m = Wd.shape[0] if Wd is not None else 0
+    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    Sn = _d(S).reshape(BH, dp, dv).copy()
+    zn = _d(z).reshape(BH, dp).copy()
+    qf = q.reshape(BH, dk); kf = k.reshape(BH, dk); vf = v.reshape(BH, dv)
+    o = np.empty((BH, dv))
+    lib().ora_decode_step(BH, dk, dv, _kind(phi_kind), m, _p(Wd), _p(qf), _p(kf), _p(vf),
+                          _p(Sn), _p(zn), _p(o))
+    return o.reshape(B, H, dv), Sn.reshape(B, H, dp, dv), zn.reshape(B, H, dp)

@@ -1,0 +1,337 @@
+/*
+ * la_oracle.c -- fp64 CPU oracle for kernelized (linear) attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * includes this file; it exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can check the HIP library against the plain
+ * definitions.  It shares no code, header or constant with the HIP sources.
+ *
+ * Everything is computed in double precision with plain loops in the order
+ * the definitions are written, ascending token index.  Independent
+ * (batch, head) slices are spread over OpenMP threads; no arithmetic is
+ * reordered inside a slice.
+ *
+ * Sources (cited by page title and section):
+ *  [LA]   "Linear Attention" (aiwiki.ai): the generalised kernel attention,
+ *         the factorised form, the causal running sums S_i, z_i, the
+ *         feature-map table and the chunkwise parallel form.
+ *  [ASSOC] "Linear Attention: Removing the Softmax Buys Associativity"
+ *         (anylearn.cc): the state as a running sum of outer products that
+ *         starts at zero; parallel and recurrent modes compute one function.
+ *  [SOA5] "Story of Attention Part 5": section 1a (kernel linear attention,
+ *         its matrix form, its recurrence and the n = 4 worked example),
+ *         section 1b (Performer / FAVOR+ feature map), section 5
+ *         (Infini-attention memory read), section 6 (Lightning Attention
+ *         blockwise split, used here with decay lambda = 1).
+ *
+ * Memory layout of every array (row-major, slices independent):
+ *   Q, K  [BH, N, dk]     V, O  [BH, N, dv]
+ *   S     [BH, dp, dv]    z     [BH, dp]         dp = dk (ELU+1) or m (FAVOR+)
+ *   W     [m, dk]         (FAVOR+ projection rows w_r, shared by all slices)
+ *
+ * Parity status: every function below is pinned by tests/test_oracle_pins.py
+ * (printed worked examples, brute force agreement of independent forms,
+ * closed forms, invariants, a library routine).  The FAVOR+ map is pinned
+ * statistically (unbiasedness, convergence to softmax attention) and by
+ * closed forms for special W; the exact value of a given finite-m FAVOR+
+ * estimate has no independent pin beyond those.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORA_PHI_ELU1 0
+#define ORA_PHI_FAVOR 1
+
+int ora_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void ora_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * Feature maps.
+ * ELU+1 [LA feature-map table; SOA5 1a]: elu with alpha = 1 plus one, applied
+ * per coordinate.  For x > 0 that is x + 1; otherwise exp(x) - 1 + 1, which is
+ * exp(x) exactly.  Output dimension dp = d.
+ * FAVOR+ [SOA5 1b]: phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), r = 1..m.
+ * ------------------------------------------------------------------------- */
+static void phi_elu1_row(const double *x, int d, double *out) {
+    for (int f = 0; f < d; ++f) out[f] = x[f] > 0.0 ? x[f] + 1.0 : exp(x[f]);
+}
+
+static void phi_favor_row(const double *x, int d, const double *W, int m, double *out) {
+    double sq = 0.0;
+    for (int c = 0; c < d; ++c) sq += x[c] * x[c];
+    double inv_sqrt_m = 1.0 / sqrt((double)m);
+    for (int r = 0; r < m; ++r) {
+        double proj = 0.0;
+        for (int c = 0; c < d; ++c) proj += W[(size_t)r * d + c] * x[c];
+        out[r] = exp(proj - 0.5 * sq) * inv_sqrt_m;
+    }
+}
+
+static void phi_row(int kind, const double *x, int d, const double *W, int m, double *out) {
+    if (kind == ORA_PHI_FAVOR) phi_favor_row(x, d, W, m, out);
+    else phi_elu1_row(x, d, out);
+}
+
+static int feat_dim(int kind, int dk, int m) { return kind == ORA_PHI_FAVOR ? m : dk; }
+
+/* phi applied to n rows of X [n, d] -> out [n, dp]. */
+void ora_phi(int kind, int n, int d, const double *X, int m, const double *W, double *out) {
+    int dp = feat_dim(kind, d, m);
+    for (int i = 0; i < n; ++i) phi_row(kind, X + (size_t)i * d, d, W, m, out + (size_t)i * dp);
+}
+
+/* ---------------------------------------------------------------------------
+ * State read [SOA5 5 (memory read num = sigma(Q) M, den = sigma(Q) z);
+ * SOA5 6 (the Q_i S_{i-1} inter-block term)]:
+ *   num[i, j] = sum_f phiQ[i, f] S[f, j],   den[i] = sum_f phiQ[i, f] z[f].
+ * ------------------------------------------------------------------------- */
+void ora_state_read(int n, int dp, int dv, const double *phiQ, const double *S, const double *z,
+                    double *num, double *den) {
+    for (int i = 0; i < n; ++i) {
+        const double *pq = phiQ + (size_t)i * dp;
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int f = 0; f < dp; ++f) acc += pq[f] * S[(size_t)f * dv + j];
+            num[(size_t)i * dv + j] = acc;
+        }
+        double dacc = 0.0;
+        for (int f = 0; f < dp; ++f) dacc += pq[f] * z[f];
+        den[i] = dacc;
+    }
+}
+
+/* helpers: per-slice phi of all rows */
+static double *phi_all(int kind, int N, int dk, const double *X, int m, const double *W) {
+    int dp = feat_dim(kind, dk, m);
+    double *out = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * dp);
+    ora_phi(kind, N, dk, X, m, W, out);
+    return out;
+}
+
+/* ---------------------------------------------------------------------------
+ * Non-causal factorised attention [LA factorised form; SOA5 1a matrix form]:
+ *   S = sum_j phi(k_j) v_j^T,  z = sum_j phi(k_j),
+ *   y_i = (phi(q_i)^T S) / (phi(q_i)^T z).
+ * S_out, z_out (may be NULL) receive S and z.
+ * ------------------------------------------------------------------------- */
+void ora_noncausal(int BH, int N, int dk, int dv, int kind, int m, const double *W,
+                   const double *Q, const double *K, const double *V,
+                   double *O, double *S_out, double *z_out) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *pk = phi_all(kind, N, dk, k, m, W);
+        double *pq = phi_all(kind, N, dk, q, m, W);
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)dp, sizeof(double));
+        for (int j = 0; j < N; ++j)
+            for (int f = 0; f < dp; ++f) {
+                double a = pk[(size_t)j * dp + f];
+                z[f] += a;
+                for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += a * v[(size_t)j * dv + c];
+            }
+        double *num = (double *)malloc(sizeof(double) * dv);
+        double den;
+        for (int i = 0; i < N; ++i) {
+            ora_state_read(1, dp, dv, pq + (size_t)i * dp, S, z, num, &den);
+            for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] = num[c] / den;
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dp * dv, S, sizeof(double) * dp * dv);
+        if (z_out) memcpy(z_out + (size_t)s * dp, z, sizeof(double) * dp);
+        free(num); free(S); free(z); free(pk); free(pq);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Causal recurrence [LA causal running sums; SOA5 1a recurrence;
+ * ASSOC: the state starts from zero]:
+ *   S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i),
+ *   y_i = phi(q_i)^T S_i / phi(q_i)^T z_i      (update, then read)
+ * with S_0, z_0 = S_in, z_in (zero when S_in == NULL).
+ * ------------------------------------------------------------------------- */
+void ora_causal_recurrent(int BH, int N, int dk, int dv, int kind, int m, const double *W,
+                          const double *Q, const double *K, const double *V,
+                          const double *S_in, const double *z_in,
+                          double *O, double *S_out, double *z_out) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)dp, sizeof(double));
+        if (S_in) {
+            memcpy(S, S_in + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+            memcpy(z, z_in + (size_t)s * dp, sizeof(double) * dp);
+        }
+        double *pk = (double *)malloc(sizeof(double) * dp);
+        double *pq = (double *)malloc(sizeof(double) * dp);
+        double *num = (double *)malloc(sizeof(double) * dv);
+        double den;
+        for (int i = 0; i < N; ++i) {
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, pk);
+            for (int f = 0; f < dp; ++f) {
+                z[f] += pk[f];
+                for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += pk[f] * v[(size_t)i * dv + c];
+            }
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, pq);
+            ora_state_read(1, dp, dv, pq, S, z, num, &den);
+            for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] = num[c] / den;
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dp * dv, S, sizeof(double) * dp * dv);
+        if (z_out) memcpy(z_out + (size_t)s * dp, z, sizeof(double) * dp);
+        free(S); free(z); free(pk); free(pq); free(num);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Quadratic (parallel-mode) brute force [LA generalised kernel attention with
+ * sim(q, k) = phi(q)^T phi(k); ASSOC parallel mode]:
+ *   y_i = [phi(q_i)^T S_in + sum_j sim(q_i, k_j) v_j]
+ *         / [phi(q_i)^T z_in + sum_j sim(q_i, k_j)]
+ * with j over all positions (causal == 0) or j <= i (causal != 0).
+ * No state is formed: every similarity is an explicit pair.
+ * ------------------------------------------------------------------------- */
+void ora_quadratic(int BH, int N, int dk, int dv, int kind, int m, const double *W,
+                   const double *Q, const double *K, const double *V,
+                   const double *S_in, const double *z_in, int causal, double *O) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *pk = phi_all(kind, N, dk, k, m, W);
+        double *pq = phi_all(kind, N, dk, q, m, W);
+        double *num = (double *)malloc(sizeof(double) * dv);
+        for (int i = 0; i < N; ++i) {
+            double den = 0.0;
+            const double *pqi = pq + (size_t)i * dp;
+            if (S_in) {
+                ora_state_read(1, dp, dv, pqi, S_in + (size_t)s * dp * dv, z_in + (size_t)s * dp, num, &den);
+            } else {
+                for (int c = 0; c < dv; ++c) num[c] = 0.0;
+            }
+            int jmax = causal ? i : N - 1;
+            for (int j = 0; j <= jmax; ++j) {
+                double sim = 0.0;
+                for (int f = 0; f < dp; ++f) sim += pqi[f] * pk[(size_t)j * dp + f];
+                den += sim;
+                for (int c = 0; c < dv; ++c) num[c] += sim * v[(size_t)j * dv + c];
+            }
+            for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] = num[c] / den;
+        }
+        free(num); free(pk); free(pq);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Chunkwise form [LA chunkwise parallel form; SOA5 6 blockwise split with
+ * lambda = 1, plus the kernel-attention normaliser of SOA5 1a].  Tokens are
+ * cut into consecutive chunks of C (the last may be shorter).  For a chunk
+ * with rows i and state (S, z) carried from the previous chunks:
+ *   P[i, t]  = phi(q_i)^T phi(k_t) for t <= i in the chunk, else 0,
+ *   num_i    = sum_t P[i, t] v_t + phi(q_i)^T S,
+ *   den_i    = sum_t P[i, t]     + phi(q_i)^T z,
+ *   y_i      = num_i / den_i,
+ * then S += phi(K_c)^T V_c and z += phi(K_c)^T 1.
+ * ------------------------------------------------------------------------- */
+void ora_causal_chunked(int BH, int N, int dk, int dv, int kind, int m, const double *W,
+                        const double *Q, const double *K, const double *V,
+                        const double *S_in, const double *z_in, int C,
+                        double *O, double *S_out, double *z_out) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)dp, sizeof(double));
+        if (S_in) {
+            memcpy(S, S_in + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+            memcpy(z, z_in + (size_t)s * dp, sizeof(double) * dp);
+        }
+        double *pq = (double *)malloc(sizeof(double) * (size_t)C * dp);
+        double *pk = (double *)malloc(sizeof(double) * (size_t)C * dp);
+        double *P = (double *)malloc(sizeof(double) * (size_t)C * C);
+        double *num = (double *)malloc(sizeof(double) * (size_t)C * dv);
+        double *den = (double *)malloc(sizeof(double) * (size_t)C);
+        for (int t0 = 0; t0 < N; t0 += C) {
+            int L = N - t0 < C ? N - t0 : C;
+            ora_phi(kind, L, dk, q + (size_t)t0 * dk, m, W, pq);
+            ora_phi(kind, L, dk, k + (size_t)t0 * dk, m, W, pk);
+            /* masked intra-chunk similarities */
+            for (int i = 0; i < L; ++i)
+                for (int t = 0; t < L; ++t) {
+                    double a = 0.0;
+                    if (t <= i)
+                        for (int f = 0; f < dp; ++f) a += pq[(size_t)i * dp + f] * pk[(size_t)t * dp + f];
+                    P[(size_t)i * C + t] = a;
+                }
+            /* inter-chunk read of the carried state */
+            ora_state_read(L, dp, dv, pq, S, z, num, den);
+            /* intra-chunk numerator and denominator, then normalise */
+            for (int i = 0; i < L; ++i) {
+                for (int t = 0; t < L; ++t) {
+                    double a = P[(size_t)i * C + t];
+                    den[i] += a;
+                    for (int c = 0; c < dv; ++c) num[(size_t)i * dv + c] += a * v[(size_t)(t0 + t) * dv + c];
+                }
+                for (int c = 0; c < dv; ++c)
+                    O[((size_t)s * N + t0 + i) * dv + c] = num[(size_t)i * dv + c] / den[i];
+            }
+            /* carry the state past this chunk */
+            for (int f = 0; f < dp; ++f)
+                for (int t = 0; t < L; ++t) {
+                    double a = pk[(size_t)t * dp + f];
+                    z[f] += a;
+                    for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += a * v[(size_t)(t0 + t) * dv + c];
+                }
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dp * dv, S, sizeof(double) * dp * dv);
+        if (z_out) memcpy(z_out + (size_t)s * dp, z, sizeof(double) * dp);
+        free(S); free(z); free(pq); free(pk); free(P); free(num); free(den);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * One recurrent decode step [LA: constant work per generated token; SOA5 1a
+ * recurrence]: S += phi(k) v^T, z += phi(k), o = phi(q)^T S / phi(q)^T z.
+ * q, k [BH, dk]; v, o [BH, dv]; S [BH, dp, dv] and z [BH, dp] updated in place.
+ * ------------------------------------------------------------------------- */
+void ora_decode_step(int BH, int dk, int dv, int kind, int m, const double *W,
+                     const double *q, const double *k, const double *v,
+                     double *S, double *z, double *o) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < BH; ++s) {
+        double *pk = (double *)malloc(sizeof(double) * dp);
+        double *pq = (double *)malloc(sizeof(double) * dp);
+        double *Ss = S + (size_t)s * dp * dv, *zs = z + (size_t)s * dp;
+        const double *vs = v + (size_t)s * dv;
+        phi_row(kind, k + (size_t)s * dk, dk, W, m, pk);
+        phi_row(kind, q + (size_t)s * dk, dk, W, m, pq);
+        for (int f = 0; f < dp; ++f) {
+            zs[f] += pk[f];
+            for (int c = 0; c < dv; ++c) Ss[(size_t)f * dv + c] += pk[f] * vs[c];
+        }
+        double den;
+        ora_state_read(1, dp, dv, pq, Ss, zs, o + (size_t)s * dv, &den);
+        for (int c = 0; c < dv; ++c) o[(size_t)s * dv + c] /= den;
+        free(pk); free(pq);
+    }
+}
