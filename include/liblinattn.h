@@ -1,0 +1,132 @@
+/*
+ * liblinattn -- causal kernelized linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, all slices independent):
+ *
+ *   phi      feature map R^{d_k} -> R^{d'} with positive outputs:
+ *            ELU+1:  phi(x)_f = elu(x_f) + 1  (x_f + 1 for x_f > 0, else exp(x_f));  d' = d_k
+ *            FAVOR+: phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), r = 1..m;         d' = m
+ *            ("Linear Attention" (aiwiki.ai), feature-map table; "Story of Attention
+ *            Part 5", sections 1a and 1b.)
+ *   causal   S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i),
+ *            out_i = phi(q_i)^T S_i / (phi(q_i)^T z_i)          (update, then read)
+ *            ("Linear Attention", causal running sums; "Story of Attention Part 5", 1a.)
+ *   non-causal  out_i = phi(q_i)^T S / (phi(q_i)^T z) with S, z summed over all tokens
+ *            ("Story of Attention Part 5", 1a, matrix form.)
+ *
+ * Tensors (caller-owned device memory, row-major, innermost dimension last):
+ *   Q, K      [B, H, N, d_k]      dtype LA_F32 (float) or LA_BF16 (uint16 bf16 bits)
+ *   V, O      [B, H, N, d_v]      same dtype as Q
+ *   S         [B, H, d', d_v]     float32, feature-major: S[b][h][f][j]
+ *   z         [B, H, d']          float32
+ *   W         [m, d_k]            float32, FAVOR+ projection rows, shared by all (b, h)
+ * Every pointer must be 16-byte aligned.  The library never allocates, frees or
+ * synchronises: all work is enqueued on `stream` (a hipStream_t passed as void*,
+ * NULL = the legacy default stream) and the call returns once it is enqueued.
+ * Results are valid after the caller synchronises that stream.  Faults during
+ * execution surface at that synchronisation, not as a return value.
+ *
+ * Validation happens on the host before anything is enqueued: on any non-zero
+ * la_status nothing has been launched and no buffer was touched.  No C++
+ * exception crosses this interface.  The library holds no mutable global state;
+ * calls on different streams may run concurrently when their buffers do not
+ * overlap.  Q, K, V, O must not overlap each other or the state buffers.
+ */
+#ifndef LIBLINATTN_H
+#define LIBLINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL, or S/z pointers not paired     */
+    LA_ERR_SHAPE = 2,       /* B,H,N < 1; d_k, d_v outside [1,128]; m outside [1,256];
+                               decode with N != 1; sizes overflowing 2^31 elements/slice */
+    LA_ERR_DTYPE = 3,       /* dtype not LA_F32 / LA_BF16                                */
+    LA_ERR_UNSUPPORTED = 4, /* phi kind unknown; chunk not in {16, 32, 64, 128}           */
+    LA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                          */
+    LA_ERR_WORKSPACE = 6,   /* ws NULL or ws_bytes below la_workspace_bytes()            */
+    LA_ERR_DEVICE = 7       /* the HIP runtime refused a launch                          */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1 } la_phi_kind;
+
+typedef struct {
+    int B, H, N;        /* batch, heads, tokens (N = 1 for la_decode_step)                   */
+    int d_k, d_v;       /* key/query and value widths, each in [1, 128]                     */
+    la_dtype dtype;     /* storage type of Q, K, V and O; S and z are always float32        */
+    la_phi_kind phi;    /* feature map                                                      */
+    int m;              /* FAVOR+: number of random features in [1, 256]; ELU+1: must be 0  */
+    const float *W;     /* FAVOR+: device pointer to W [m, d_k] float32; ELU+1: NULL         */
+} la_problem;
+
+/* ABI version of the loaded library (LA_ABI_VERSION of the build). */
+int la_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *la_status_string(la_status s);
+
+/* Feature dimension d' of a problem: d_k for ELU+1, m for FAVOR+ (0 if p is NULL). */
+int la_feature_dim(const la_problem *p);
+
+/*
+ * Device workspace (bytes) that la_forward_causal_chunked(p, chunk, ...) and
+ * la_forward_noncausal(p, ...) need; 0 means ws may be NULL.  The value depends
+ * only on the problem shape and chunk.  Returns 0 for an invalid problem.
+ */
+size_t la_workspace_bytes(const la_problem *p, int chunk);
+
+/*
+ * Non-causal forward ("Story of Attention Part 5", 1a, matrix form):
+ *   S = phi(K)^T V,  z = phi(K)^T 1,  O = (phi(Q) S) / (phi(Q) z)  row-wise.
+ * S_out/z_out (both or neither; may be NULL) receive S and z.
+ * ws: caller-provided device scratch of at least la_workspace_bytes(p, 64) bytes.
+ */
+la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K, const void *V,
+                               void *O, float *S_out, float *z_out, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * Causal forward in the chunkwise hybrid ("Linear Attention", chunkwise parallel
+ * form; "Story of Attention Part 5", section 6 blockwise split, with decay 1 and
+ * the normaliser of 1a): tokens are cut into chunks of `chunk` tokens; inside a
+ * chunk the masked pairwise form phi(Q_c) phi(K_c)^T (j <= i) is applied to V_c,
+ * the state carried from earlier chunks is read as phi(Q_c) S, phi(Q_c) z, and
+ * the state then absorbs phi(K_c)^T V_c, phi(K_c)^T 1.
+ *   chunk        in {16, 32, 64, 128}; it changes speed, never the result
+ *                beyond floating-point rounding.  N need not be a multiple.
+ *   S_in, z_in   initial state (both NULL = zero state), [B,H,d',d_v] / [B,H,d'].
+ *   S_out, z_out final state after token N (both NULL = not exported).  May be
+ *                the same buffers as S_in, z_in (updated in place).
+ *   ws           device scratch of at least la_workspace_bytes(p, chunk) bytes
+ *                (NULL allowed when that is 0).  Contents on entry are ignored.
+ */
+la_status la_forward_causal_chunked(const la_problem *p, int chunk,
+                                    const void *Q, const void *K, const void *V, void *O,
+                                    const float *S_in, const float *z_in,
+                                    float *S_out, float *z_out,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One recurrent decode step for every (b, h) ("Linear Attention": constant work
+ * and memory per generated token; "Story of Attention Part 5", 1a recurrence):
+ *   S += phi(k) v^T,  z += phi(k),  o = (phi(q)^T S) / (phi(q)^T z).
+ * p->N must be 1.  q, k: [B, H, 1, d_k]; v, o: [B, H, 1, d_v] (dtype p->dtype).
+ * S [B,H,d',d_v] and z [B,H,d'] (float32) are read and overwritten in place.
+ */
+la_status la_decode_step(const la_problem *p, const void *q, const void *k, const void *v,
+                         void *o, float *S, float *z, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLINATTN_H */

@@ -1,0 +1,257 @@
+// liblinattn C ABI: host-side validation and dispatch.  Everything here runs on
+// the host; the arithmetic is in the kernels (la_generic.hip, la_mfma.hip,
+// la_decode.hip).  No allocation, no synchronisation, no global state.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/liblinattn.h"
+#include "la_internal.h"
+
+#define LA_API extern "C" __attribute__((visibility("default")))
+
+namespace la {
+namespace {
+
+constexpr int kTargetWorkgroups = 1024;  // enough to keep every CU of the chip busy
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+la_status check_problem(const la_problem *p) {
+    if (!p) return LA_ERR_NULL;
+    if (p->dtype != LA_F32 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (p->phi != LA_PHI_ELU1 && p->phi != LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
+    if (p->B < 1 || p->H < 1 || p->N < 1) return LA_ERR_SHAPE;
+    if (p->d_k < 1 || p->d_k > 128 || p->d_v < 1 || p->d_v > 128) return LA_ERR_SHAPE;
+    if (p->phi == LA_PHI_FAVOR) {
+        if (p->m < 1 || p->m > 256) return LA_ERR_SHAPE;
+        if (!p->W) return LA_ERR_NULL;
+        if (!aligned16(p->W)) return LA_ERR_ALIGN;
+    } else if (p->m != 0 || p->W) {
+        return LA_ERR_SHAPE;
+    }
+    // element counts of one slice must fit comfortably in 32-bit kernel indices
+    const long long per_slice = (long long)p->N * (p->d_k > p->d_v ? p->d_k : p->d_v);
+    if (per_slice > (long long)INT_MAX) return LA_ERR_SHAPE;
+    if ((long long)p->B * p->H > (long long)INT_MAX / 4) return LA_ERR_SHAPE;
+    return LA_OK;
+}
+
+Shape make_shape(const la_problem *p) {
+    Shape s;
+    s.BH = p->B * p->H;
+    s.N = p->N;
+    s.dk = p->d_k;
+    s.dv = p->d_v;
+    s.phi = p->phi == LA_PHI_FAVOR ? kFavor : kElu1;
+    s.m = p->phi == LA_PHI_FAVOR ? p->m : 0;
+    s.dp = p->phi == LA_PHI_FAVOR ? p->m : p->d_k;
+    s.W = p->phi == LA_PHI_FAVOR ? p->W : nullptr;
+    s.dtype = p->dtype == LA_BF16 ? kBF16 : kF32;
+    return s;
+}
+
+bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128; }
+
+// Split each slice into P segments of whole chunks so that B*H*P*(columns)
+// workgroups fill the device.  Depends on the shape only.
+Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int min_seg_chunks) {
+    Segments g;
+    g.chunk = chunk;
+    g.n_chunks = (sh.N + chunk - 1) / chunk;
+    const long long units = (long long)sh.BH * columns_per_slice;
+    int want = (int)((kTargetWorkgroups + units - 1) / units);
+    if (want < 1) want = 1;
+    int max_p = (g.n_chunks + min_seg_chunks - 1) / min_seg_chunks;
+    if (want > max_p) want = max_p;
+    if (want < 1) want = 1;
+    g.seg_chunks = (g.n_chunks + want - 1) / want;
+    g.P = (g.n_chunks + g.seg_chunks - 1) / g.seg_chunks;
+    return g;
+}
+
+int generic_columns(const Shape &sh) { return (sh.dv + 31) / 32; }
+
+Segments causal_plan(const Shape &sh, int chunk, bool *use_mfma) {
+    const bool mf = mfma_supported(sh, chunk);
+    if (use_mfma) *use_mfma = mf;
+    return mf ? plan_segments(sh, chunk, 1, 1) : plan_segments(sh, chunk, generic_columns(sh), 1);
+}
+
+constexpr int kNoncausalChunk = 64;
+
+Segments noncausal_plan(const Shape &sh, bool *use_mfma) {
+    const bool mf = mfma_supported(sh, kNoncausalChunk);
+    if (use_mfma) *use_mfma = mf;
+    return mf ? plan_segments(sh, kNoncausalChunk, 1, 1)
+              : plan_segments(sh, kNoncausalChunk, generic_columns(sh), 1);
+}
+
+struct WsLayout {
+    size_t s_bytes, z_bytes, total;
+};
+
+WsLayout ws_layout(const Shape &sh, int P) {
+    WsLayout w;
+    w.s_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp * sh.dv, kAlign);
+    w.z_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp, kAlign);
+    w.total = w.s_bytes + w.z_bytes;
+    return w;
+}
+
+// A single workgroup per slice can start from S_in and finish into S_out by
+// itself (safe even when they alias).  Several segments, or several value
+// slabs that would all read z_in while one of them writes z_out, go through
+// the workspace: per-segment sums, a prefix scan, then the chunk loop.
+bool causal_direct(const Shape &sh, const Segments &g, bool mfma) {
+    return g.P == 1 && (mfma || generic_columns(sh) == 1);
+}
+
+size_t causal_ws(const Shape &sh, int chunk) {
+    bool mf = false;
+    Segments g = causal_plan(sh, chunk, &mf);
+    return causal_direct(sh, g, mf) ? 0 : ws_layout(sh, g.P).total;
+}
+
+size_t noncausal_ws(const Shape &sh) {
+    Segments g = noncausal_plan(sh, nullptr);
+    return ws_layout(sh, g.P).total;
+}
+
+hipError_t launch_fwd(bool mfma, const FwdArgs &a, hipStream_t st) {
+    return mfma ? launch_mfma(a, st) : launch_generic(a, st);
+}
+
+}  // namespace
+}  // namespace la
+
+using namespace la;
+
+LA_API int la_abi_version(void) { return LA_ABI_VERSION; }
+
+LA_API const char *la_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_NULL: return "required pointer is NULL (or S/z pointers not paired)";
+        case LA_ERR_SHAPE: return "shape out of range";
+        case LA_ERR_DTYPE: return "unsupported dtype";
+        case LA_ERR_UNSUPPORTED: return "unsupported feature map or chunk size";
+        case LA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case LA_ERR_WORKSPACE: return "workspace missing or too small";
+        case LA_ERR_DEVICE: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+LA_API int la_feature_dim(const la_problem *p) {
+    if (!p) return 0;
+    return p->phi == LA_PHI_FAVOR ? p->m : p->d_k;
+}
+
+LA_API size_t la_workspace_bytes(const la_problem *p, int chunk) {
+    if (check_problem(p) != LA_OK || !chunk_ok(chunk)) return 0;
+    Shape sh = make_shape(p);
+    size_t a = causal_ws(sh, chunk), b = noncausal_ws(sh);
+    return a > b ? a : b;
+}
+
+LA_API la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K, const void *V, void *O,
+                                      float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (!Q || !K || !V || !O) return LA_ERR_NULL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_out) ||
+        !aligned16(z_out) || !aligned16(ws))
+        return LA_ERR_ALIGN;
+    Shape sh = make_shape(p);
+    bool mf = false;
+    Segments g = noncausal_plan(sh, &mf);
+    WsLayout wl = ws_layout(sh, g.P);
+    if (!ws || ws_bytes < wl.total) return LA_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    float *wsS = static_cast<float *>(ws);
+    float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
+    const size_t nS = (size_t)sh.dp * sh.dv, nz = (size_t)sh.dp;
+
+    // 1. per-segment sums phi(K)^T V, phi(K)^T 1
+    FwdArgs a{};
+    a.sh = sh; a.sg = g; a.mode = kModeState;
+    a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
+    a.st.S_dst = wsS; a.st.z_dst = wsz;
+    a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
+    if (launch_fwd(mf, a, hs) != hipSuccess) return LA_ERR_DEVICE;
+    // 2. fixed-order total into slot 0 (and S_out)
+    if (launch_scan(sh, g.P, wsS, wsz, nullptr, nullptr, S_out, z_out, true, hs) != hipSuccess) return LA_ERR_DEVICE;
+    // 3. O = phi(Q) S / phi(Q) z
+    FwdArgs r{};
+    r.sh = sh; r.sg = g; r.mode = kModeRead;
+    r.Q = Q; r.K = K; r.V = V; r.O = O;
+    r.st.S_src = wsS; r.st.z_src = wsz;
+    r.st.src_slice = g.P * nS; r.st.src_seg = 0; r.st.zsrc_slice = g.P * nz; r.st.zsrc_seg = 0;
+    if (launch_fwd(mf, r, hs) != hipSuccess) return LA_ERR_DEVICE;
+    return LA_OK;
+}
+
+LA_API la_status la_forward_causal_chunked(const la_problem *p, int chunk, const void *Q, const void *K,
+                                           const void *V, void *O, const float *S_in, const float *z_in,
+                                           float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O) return LA_ERR_NULL;
+    if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_in) || !aligned16(z_in) ||
+        !aligned16(S_out) || !aligned16(z_out) || !aligned16(ws))
+        return LA_ERR_ALIGN;
+    Shape sh = make_shape(p);
+    bool mf = false;
+    Segments g = causal_plan(sh, chunk, &mf);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)sh.dp * sh.dv, nz = (size_t)sh.dp;
+
+    FwdArgs c{};
+    c.sh = sh; c.sg = g; c.mode = kModeCausal;
+    c.Q = Q; c.K = K; c.V = V; c.O = O;
+    if (causal_direct(sh, g, mf)) {
+        // one workgroup per slice: start from S_in, finish into S_out
+        c.st.S_src = S_in; c.st.z_src = z_in;
+        c.st.src_slice = nS; c.st.zsrc_slice = nz;
+        c.st.S_dst = S_out; c.st.z_dst = z_out;
+        c.st.dst_slice = nS; c.st.zdst_slice = nz;
+        return launch_fwd(mf, c, hs) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+    }
+    WsLayout wl = ws_layout(sh, g.P);
+    if (!ws || ws_bytes < wl.total) return LA_ERR_WORKSPACE;
+    float *wsS = static_cast<float *>(ws);
+    float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
+
+    // A. each segment's own sums phi(K)^T V, phi(K)^T 1
+    FwdArgs a{};
+    a.sh = sh; a.sg = g; a.mode = kModeState;
+    a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
+    a.st.S_dst = wsS; a.st.z_dst = wsz;
+    a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
+    if (launch_fwd(mf, a, hs) != hipSuccess) return LA_ERR_DEVICE;
+    // B. exclusive prefix over segments (+ S_in); final state to S_out
+    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, S_out, z_out, false, hs) != hipSuccess) return LA_ERR_DEVICE;
+    // C. chunk loop of every segment from its prefix state
+    c.st.S_src = wsS; c.st.z_src = wsz;
+    c.st.src_slice = g.P * nS; c.st.src_seg = nS; c.st.zsrc_slice = g.P * nz; c.st.zsrc_seg = nz;
+    if (launch_fwd(mf, c, hs) != hipSuccess) return LA_ERR_DEVICE;
+    return LA_OK;
+}
+
+LA_API la_status la_decode_step(const la_problem *p, const void *q, const void *k, const void *v, void *o, float *S,
+                                float *z, void *stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->N != 1) return LA_ERR_SHAPE;
+    if (!q || !k || !v || !o || !S || !z) return LA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(S) || !aligned16(z))
+        return LA_ERR_ALIGN;
+    Shape sh = make_shape(p);
+    return launch_decode(sh, q, k, v, o, S, z, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK
+                                                                                             : LA_ERR_DEVICE;
+}

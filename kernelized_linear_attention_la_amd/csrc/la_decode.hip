@@ -1,0 +1,171 @@
+// One recurrent decode step for every (batch, head) slice:
+//   S += phi(k) v^T,  z += phi(k),  o = phi(q)^T S / phi(q)^T z
+// ("Linear Attention": constant work and memory per generated token;
+// "Story of Attention Part 5", 1a recurrence, update before read).
+//
+// The step is a single streaming pass over the fp32 state (d' x d_v per
+// slice): each element is read once, updated with the rank-1 term and written
+// back, and the column sums phi(q)^T S' are formed on the fly from the updated
+// value.  One 256-thread workgroup per slice; thread (row group g, column
+// quad c) owns rows g, g + G, g + 2G, ... of columns 4c..4c+3, so a wavefront
+// touches whole contiguous rows (coalesced 16-byte accesses).  Partial column
+// sums meet in LDS; phi(q)^T z' is a block reduction.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxDp = 256;
+constexpr int kMaxD = 128;
+constexpr int kBatch = 8;  // rows in flight per thread between load and store
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restrict__ q, const T *__restrict__ k,
+                                                     const T *__restrict__ v, T *__restrict__ o,
+                                                     float *__restrict__ S, float *__restrict__ z) {
+    __shared__ float s_pq[kMaxDp], s_pk[kMaxDp], s_v[kMaxD];
+    __shared__ float s_x[2][kMaxD];
+    __shared__ float s_red[kThreads * 4];  // partial column sums [row group][dv] (G * dv <= 4 * 256)
+    __shared__ float s_den[kThreads / 64];
+    __shared__ float s_sq[2];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int dk = sh.dk, dv = sh.dv, dp = sh.dp;
+
+    const T *qs = q + (size_t)bh * dk;
+    const T *ks = k + (size_t)bh * dk;
+    const T *vs = v + (size_t)bh * dv;
+    float *Ss = S + (size_t)bh * dp * dv;
+    float *zs = z + (size_t)bh * dp;
+
+    // feature maps of q and k, value row
+    if (tid < dv) s_v[tid] = load_as_f32(vs, tid);
+    if (sh.phi == kElu1) {
+        if (tid < dk) {
+            s_pq[tid] = elu1_accurate(load_as_f32(qs, tid));
+            s_pk[tid] = elu1_accurate(load_as_f32(ks, tid));
+        }
+    } else {
+        if (tid < dk) {
+            s_x[0][tid] = load_as_f32(qs, tid);
+            s_x[1][tid] = load_as_f32(ks, tid);
+        }
+        __syncthreads();
+        if (tid < 2) {
+            float a = 0.f;
+            for (int c = 0; c < dk; ++c) a += s_x[tid][c] * s_x[tid][c];
+            s_sq[tid] = a;
+        }
+        __syncthreads();
+        const float inv_sqrt_m = 1.0f / sqrtf(static_cast<float>(sh.m));
+        for (int f = tid; f < dp; f += kThreads) {
+            const float *w = sh.W + (size_t)f * dk;
+            float aq = 0.f, ak = 0.f;
+            for (int c = 0; c < dk; ++c) {
+                float wc = w[c];
+                aq += wc * s_x[0][c];
+                ak += wc * s_x[1][c];
+            }
+            s_pq[f] = expf(aq - 0.5f * s_sq[0]) * inv_sqrt_m;
+            s_pk[f] = expf(ak - 0.5f * s_sq[1]) * inv_sqrt_m;
+        }
+    }
+    __syncthreads();
+
+    // streaming rank-1 update of S and column sums of phi(q)^T S'
+    const int cols = dv / VW;               // column groups
+    const int G = kThreads / cols;          // row groups
+    const int g = tid / cols, cg = tid - g * cols;
+    float acc[VW];
+#pragma unroll
+    for (int u = 0; u < VW; ++u) acc[u] = 0.f;
+    if (g < G) {
+        float vv[VW];
+#pragma unroll
+        for (int u = 0; u < VW; ++u) vv[u] = s_v[cg * VW + u];
+        for (int f0 = g; f0 < dp; f0 += G * kBatch) {
+            float buf[kBatch][VW];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int f = f0 + b * G;
+                if (f < dp) {
+                    const float *src = Ss + (size_t)f * dv + cg * VW;
+                    if constexpr (VW == 4) {
+                        float4 t4 = *reinterpret_cast<const float4 *>(src);
+                        buf[b][0] = t4.x; buf[b][1] = t4.y; buf[b][2] = t4.z; buf[b][3] = t4.w;
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < VW; ++u) buf[b][u] = src[u];
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int f = f0 + b * G;
+                if (f < dp) {
+                    const float pk = s_pk[f], pq = s_pq[f];
+#pragma unroll
+                    for (int u = 0; u < VW; ++u) {
+                        buf[b][u] += pk * vv[u];
+                        acc[u] += pq * buf[b][u];
+                    }
+                    float *dst = Ss + (size_t)f * dv + cg * VW;
+                    if constexpr (VW == 4) {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(buf[b][0], buf[b][1], buf[b][2], buf[b][3]);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < VW; ++u) dst[u] = buf[b][u];
+                    }
+                }
+            }
+        }
+    }
+
+    // z' = z + phi(k) and its read phi(q)^T z'
+    float dpart = 0.f;
+    for (int f = tid; f < dp; f += kThreads) {
+        float zn = zs[f] + s_pk[f];
+        zs[f] = zn;
+        dpart += s_pq[f] * zn;
+    }
+    for (int off = 32; off > 0; off >>= 1) dpart += __shfl_down(dpart, off, 64);
+    if ((tid & 63) == 0) s_den[tid >> 6] = dpart;
+
+    // column sums across row groups
+    if (g < G) {
+#pragma unroll
+        for (int u = 0; u < VW; ++u) s_red[g * dv + cg * VW + u] = acc[u];
+    }
+    __syncthreads();
+    if (tid < dv) {
+        float num = 0.f;
+        for (int gg = 0; gg < G; ++gg) num += s_red[gg * dv + tid];
+        float den = 0.f;
+        for (int w = 0; w < kThreads / 64; ++w) den += s_den[w];
+        store_from_f32(o + (size_t)bh * dv, tid, num / den);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o, float *S, float *z,
+                         hipStream_t stream) {
+    const bool vec = (sh.dv % 4) == 0;
+    dim3 grid((unsigned)sh.BH), block(kThreads);
+    if (sh.dtype == kF32) {
+        auto *qq = static_cast<const float *>(q); auto *kk = static_cast<const float *>(k);
+        auto *vv = static_cast<const float *>(v); auto *oo = static_cast<float *>(o);
+        if (vec) hipLaunchKernelGGL((k_decode<float, 4>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+        else hipLaunchKernelGGL((k_decode<float, 1>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+    } else {
+        auto *qq = static_cast<const uint16_t *>(q); auto *kk = static_cast<const uint16_t *>(k);
+        auto *vv = static_cast<const uint16_t *>(v); auto *oo = static_cast<uint16_t *>(o);
+        if (vec) hipLaunchKernelGGL((k_decode<uint16_t, 4>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+        else hipLaunchKernelGGL((k_decode<uint16_t, 1>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

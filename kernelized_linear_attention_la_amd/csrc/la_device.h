@@ -1,0 +1,42 @@
+// Device-side helpers shared by the liblinattn kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// bf16 storage is the upper half of an fp32 bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaNs stay NaN (quiet bit forced).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_as_f32(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_as_f32<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, size_t i) {
+    return bf16_to_f32(p[i]);
+}
+
+template <typename T> __device__ __forceinline__ void store_from_f32(T *p, size_t i, float v);
+template <> __device__ __forceinline__ void store_from_f32<float>(float *p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p, size_t i, float v) {
+    p[i] = f32_to_bf16(v);
+}
+
+// ELU+1 feature map ("Linear Attention", feature-map table): elu(x) + 1 with
+// alpha = 1, which is x + 1 for x > 0 and exp(x) otherwise.  Accurate expf.
+__device__ __forceinline__ float elu1_accurate(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// Same map with the hardware exp2 (about 1 ulp); used where the result is
+// rounded to bf16 right after.
+__device__ __forceinline__ float elu1_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+}  // namespace la

@@ -1,0 +1,301 @@
+// Generic chunkwise kernels: fp32 arithmetic, any d_k, d_v <= 128, any m <= 256,
+// fp32 or bf16 storage.  This is the path for fp32 problems (where bf16 matrix
+// cores would not meet fp32 accuracy) and for shapes without an MFMA variant.
+//
+// One workgroup owns one (slice, segment, 32-column value slab).  It walks its
+// chunks in order ("Linear Attention", chunkwise parallel form; "Story of
+// Attention Part 5", section 6 blockwise split with decay 1 plus the
+// normaliser of section 1a):
+//   for each chunk c:
+//     for each query tile (T rows):  O = [phiQ S + (phiQ phiK^T (masked j<=i)) V]
+//                                      / [phiQ z + (phiQ phiK^T (masked)) 1]
+//     then S += phiK_c^T V_c, z += phiK_c^T 1
+// The state S (d' x 32 slab) and z live in LDS in fp32 for the whole segment.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVS = 32;  // value columns per workgroup
+
+struct GenLayout {
+    int T;    // rows per tile
+    int dpp;  // padded row stride of the phi tiles (avoids LDS bank conflicts)
+    int offS, offZ, offX, offSq, offPQ, offPK, offV, offP, total;
+};
+
+__host__ __device__ inline GenLayout gen_layout(int dk, int dp) {
+    GenLayout L;
+    L.T = dp <= 128 ? 16 : 8;
+    L.dpp = dp + 1;
+    int o = 0;
+    L.offS = o;  o += dp * kVS;
+    L.offZ = o;  o += dp;
+    L.offX = o;  o += L.T * dk;
+    L.offSq = o; o += L.T;
+    L.offPQ = o; o += L.T * L.dpp;
+    L.offPK = o; o += L.T * L.dpp;
+    L.offV = o;  o += L.T * kVS;
+    L.offP = o;  o += L.T * L.T;
+    L.total = o;
+    return L;
+}
+
+// phi of `nvalid` rows starting at row0 of X [*, dk] into out [T][dpp]; rows
+// past nvalid become zero (they must not contribute to any sum).
+template <typename T>
+__device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int row0, int nvalid,
+                         float *sX, float *sSq, float *out) {
+    const int tid = threadIdx.x;
+    const int dk = sh.dk;
+    if (sh.phi == kElu1) {
+        for (int e = tid; e < L.T * dk; e += kThreads) {
+            int r = e / dk, c = e - r * dk;
+            float v = 0.f;
+            if (r < nvalid) v = elu1_accurate(load_as_f32(X, (size_t)(row0 + r) * dk + c));
+            out[r * L.dpp + c] = v;
+        }
+        return;
+    }
+    // FAVOR+ ("Story of Attention Part 5", 1b): exp(w_r . x - |x|^2/2) / sqrt(m)
+    for (int e = tid; e < L.T * dk; e += kThreads) {
+        int r = e / dk, c = e - r * dk;
+        sX[e] = r < nvalid ? load_as_f32(X, (size_t)(row0 + r) * dk + c) : 0.f;
+    }
+    __syncthreads();
+    if (tid < L.T) {
+        float s = 0.f;
+        for (int c = 0; c < dk; ++c) s += sX[tid * dk + c] * sX[tid * dk + c];
+        sSq[tid] = s;
+    }
+    __syncthreads();
+    const float inv_sqrt_m = 1.0f / sqrtf(static_cast<float>(sh.m));
+    for (int f = tid; f < sh.m; f += kThreads) {
+        const float *w = sh.W + (size_t)f * dk;
+        float acc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int c = 0; c < dk; ++c) {
+            float wc = w[c];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (r < L.T) acc[r] += wc * sX[r * dk + c];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (r < L.T) out[r * L.dpp + f] = r < nvalid ? expf(acc[r] - 0.5f * sSq[r]) * inv_sqrt_m : 0.f;
+    }
+}
+
+template <typename T>
+__device__ void value_tile(const Shape &sh, const GenLayout &L, const T *V, int row0, int nvalid, int j0, int vw,
+                           float *sV) {
+    for (int e = threadIdx.x; e < L.T * kVS; e += kThreads) {
+        int r = e / kVS, j = e - r * kVS;
+        float v = 0.f;
+        if (r < nvalid && j < vw) v = load_as_f32(V, (size_t)(row0 + r) * sh.dv + j0 + j);
+        sV[e] = v;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
+    extern __shared__ float smem[];
+    const Shape sh = a.sh;
+    const Segments sg = a.sg;
+    const int dp = sh.dp, dk = sh.dk, dv = sh.dv;
+    const GenLayout L = gen_layout(dk, dp);
+    float *sS = smem + L.offS, *sz = smem + L.offZ, *sX = smem + L.offX, *sSq = smem + L.offSq;
+    float *sPQ = smem + L.offPQ, *sPK = smem + L.offPK, *sV = smem + L.offV, *sP = smem + L.offP;
+    const int tid = threadIdx.x;
+
+    const int nslab = (dv + kVS - 1) / kVS;
+    const int slab = blockIdx.x % nslab;
+    const int seg = (blockIdx.x / nslab) % sg.P;
+    const int bh = blockIdx.x / (nslab * sg.P);
+    const int j0 = slab * kVS;
+    const int vw = min(kVS, dv - j0);
+
+    const int c_begin = seg * sg.seg_chunks;
+    const int c_end = min(sg.n_chunks, c_begin + sg.seg_chunks);
+    const int N = sh.N, C = sg.chunk;
+
+    const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
+    const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * dk;
+    const T *Vs = static_cast<const T *>(a.V) + (size_t)bh * N * dv;
+    T *Os = a.O ? static_cast<T *>(a.O) + (size_t)bh * N * dv : nullptr;
+
+    // starting state
+    const float *Ssrc = a.st.S_src ? a.st.S_src + bh * a.st.src_slice + seg * a.st.src_seg : nullptr;
+    const float *zsrc = a.st.z_src ? a.st.z_src + bh * a.st.zsrc_slice + seg * a.st.zsrc_seg : nullptr;
+    for (int e = tid; e < dp * kVS; e += kThreads) {
+        int f = e / kVS, j = e - f * kVS;
+        sS[e] = (Ssrc && j < vw) ? Ssrc[(size_t)f * dv + j0 + j] : 0.f;
+    }
+    for (int f = tid; f < dp; f += kThreads) sz[f] = zsrc ? zsrc[f] : 0.f;
+    __syncthreads();
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * C;
+        const int Lc = min(C, N - t0);
+        if (a.mode != kModeState) {
+            for (int qt = 0; qt < Lc; qt += L.T) {
+                const int nq = min(L.T, Lc - qt);
+                phi_tile(sh, L, Qs, t0 + qt, nq, sX, sSq, sPQ);
+                __syncthreads();
+                // inter-chunk read of the carried state: phiQ S, phiQ z
+                float acc[2], den[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    int e = tid + r * kThreads;
+                    acc[r] = 0.f; den[r] = 0.f;
+                    if (e < L.T * kVS) {
+                        int i = e / kVS, j = e - i * kVS;
+                        const float *pq = sPQ + i * L.dpp;
+                        for (int f = 0; f < dp; ++f) {
+                            acc[r] += pq[f] * sS[f * kVS + j];
+                            den[r] += pq[f] * sz[f];
+                        }
+                    }
+                }
+                if (a.mode == kModeCausal) {
+                    // intra-chunk masked pairwise part, key tiles up to the query tile
+                    for (int kt = 0; kt <= qt; kt += L.T) {
+                        const int nk = min(L.T, Lc - kt);
+                        __syncthreads();  // previous users of sX / sPK / sV / sP are done
+                        phi_tile(sh, L, Ks, t0 + kt, nk, sX, sSq, sPK);
+                        value_tile(sh, L, Vs, t0 + kt, nk, j0, vw, sV);
+                        __syncthreads();
+                        for (int e = tid; e < L.T * L.T; e += kThreads) {
+                            int i = e / L.T, t = e - i * L.T;
+                            float p = 0.f;
+                            if (kt + t <= qt + i) {
+                                const float *pq = sPQ + i * L.dpp, *pk = sPK + t * L.dpp;
+                                for (int f = 0; f < dp; ++f) p += pq[f] * pk[f];
+                            }
+                            sP[e] = p;
+                        }
+                        __syncthreads();
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            int e = tid + r * kThreads;
+                            if (e < L.T * kVS) {
+                                int i = e / kVS, j = e - i * kVS;
+                                for (int t = 0; t < L.T; ++t) {
+                                    float p = sP[i * L.T + t];
+                                    acc[r] += p * sV[t * kVS + j];
+                                    den[r] += p;
+                                }
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    int e = tid + r * kThreads;
+                    if (e < L.T * kVS) {
+                        int i = e / kVS, j = e - i * kVS;
+                        if (i < nq && j < vw)
+                            store_from_f32(Os, (size_t)(t0 + qt + i) * dv + j0 + j, acc[r] / den[r]);
+                    }
+                }
+                __syncthreads();  // sPQ is reused by the next query tile
+            }
+        }
+        if (a.mode != kModeRead) {
+            // carry the state past this chunk: S += phiK^T V, z += phiK^T 1
+            for (int kt = 0; kt < Lc; kt += L.T) {
+                const int nk = min(L.T, Lc - kt);
+                phi_tile(sh, L, Ks, t0 + kt, nk, sX, sSq, sPK);
+                value_tile(sh, L, Vs, t0 + kt, nk, j0, vw, sV);
+                __syncthreads();
+                for (int e = tid; e < dp * kVS; e += kThreads) {
+                    int f = e / kVS, j = e - f * kVS;
+                    float s = sS[e];
+                    for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f] * sV[t * kVS + j];
+                    sS[e] = s;
+                }
+                for (int f = tid; f < dp; f += kThreads) {
+                    float s = sz[f];
+                    for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f];
+                    sz[f] = s;
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    if (a.st.S_dst) {
+        float *Sd = a.st.S_dst + bh * a.st.dst_slice + seg * a.st.dst_seg;
+        for (int e = tid; e < dp * kVS; e += kThreads) {
+            int f = e / kVS, j = e - f * kVS;
+            if (j < vw) Sd[(size_t)f * dv + j0 + j] = sS[e];
+        }
+        if (slab == 0) {
+            float *zd = a.st.z_dst + bh * a.st.zdst_slice + seg * a.st.zdst_seg;
+            for (int f = tid; f < dp; f += kThreads) zd[f] = sz[f];
+        }
+    }
+}
+
+// Exclusive prefix over the P segment states of each slice, in place:
+//   slot s <- S_in + sum_{s' < s} slot s'   and   S_out <- S_in + sum_s slot s.
+// With total_to_slot0, slot 0 <- sum_s slot s instead (non-causal total).
+// One thread per state element; the segment order is fixed, so repeated runs
+// give identical bits.
+__global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz, float *ws_S, float *ws_z,
+                                                   const float *S_in, const float *z_in, float *S_out,
+                                                   float *z_out, int total_to_slot0) {
+    const int per = nS + nz;
+    const int blocks_per_slice = (per + kThreads - 1) / kThreads;
+    const int bh = blockIdx.x / blocks_per_slice;
+    const int e = (blockIdx.x - bh * blocks_per_slice) * kThreads + threadIdx.x;
+    if (bh >= BH || e >= per) return;
+    const bool isS = e < nS;
+    const int idx = isS ? e : e - nS;
+    const int n = isS ? nS : nz;
+    float *slots = (isS ? ws_S : ws_z) + (size_t)bh * P * n + idx;
+    const float *in = isS ? S_in : z_in;
+    float *out = isS ? S_out : z_out;
+    float acc = in ? in[(size_t)bh * n + idx] : 0.f;
+    if (total_to_slot0) {
+        acc = 0.f;
+        for (int s = 0; s < P; ++s) acc += slots[(size_t)s * n];
+        slots[0] = acc;
+    } else {
+        for (int s = 0; s < P; ++s) {
+            float d = slots[(size_t)s * n];
+            slots[(size_t)s * n] = acc;
+            acc += d;
+        }
+    }
+    if (out) out[(size_t)bh * n + idx] = acc;
+}
+
+}  // namespace
+
+size_t generic_lds_bytes(int dk, int dp) { return sizeof(float) * (size_t)gen_layout(dk, dp).total; }
+
+hipError_t launch_generic(const FwdArgs &a, hipStream_t stream) {
+    const int nslab = (a.sh.dv + kVS - 1) / kVS;
+    const size_t grid = (size_t)a.sh.BH * a.sg.P * nslab;
+    const size_t lds = generic_lds_bytes(a.sh.dk, a.sh.dp);
+    if (a.sh.dtype == kF32)
+        hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL(k_generic<uint16_t>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in, const float *z_in,
+                       float *S_out, float *z_out, bool total_to_slot0, hipStream_t stream) {
+    const int nS = sh.dp * sh.dv, nz = sh.dp;
+    const int bps = (nS + nz + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)((size_t)sh.BH * bps)), dim3(kThreads), 0, stream, sh.BH, P, nS, nz,
+                       ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace la

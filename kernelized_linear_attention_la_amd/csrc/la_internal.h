@@ -1,0 +1,73 @@
+// Internal declarations shared by the liblinattn HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+enum Phi : int { kElu1 = 0, kFavor = 1 };
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// What one launch of the chunked kernels does over its token range.
+enum Mode : int {
+    kModeState = 0,   // accumulate phi(K)^T [V, 1] of the segment into a state slot
+    kModeCausal = 1,  // chunkwise causal forward starting from a prefix state
+    kModeRead = 2     // non-causal read: O = phi(Q) S / phi(Q) z with a fixed state
+};
+
+// Shape of one call, after host validation.
+struct Shape {
+    int BH;       // B * H slices
+    int N;        // tokens per slice
+    int dk, dv;   // widths
+    int dp;       // feature dimension d' (dk or m)
+    int phi;      // Phi
+    int m;        // FAVOR+ features (0 for ELU+1)
+    const float *W;  // FAVOR+ rows [m, dk] (device)
+    int dtype;    // Dtype of Q/K/V/O
+};
+
+// Token ranges split into segments of whole chunks; one workgroup column per segment.
+struct Segments {
+    int chunk;        // tokens per chunk
+    int n_chunks;     // ceil(N / chunk)
+    int seg_chunks;   // chunks per segment
+    int P;            // number of segments = ceil(n_chunks / seg_chunks)
+};
+
+// State storage of a launch.  Slot s of slice b lives at
+// S + ((size_t)b * P + s) * dp * dv (and z + ((size_t)b * P + s) * dp).
+struct StateArgs {
+    const float *S_src;   // prefix/total state to start from (NULL = zero)
+    const float *z_src;
+    size_t src_slice, src_seg;    // floats between slices / segments in S_src
+    size_t zsrc_slice, zsrc_seg;  // same for z_src
+    float *S_dst;         // where the final state of the range goes (NULL = nowhere)
+    float *z_dst;
+    size_t dst_slice, dst_seg;
+    size_t zdst_slice, zdst_seg;
+};
+
+struct FwdArgs {
+    Shape sh;
+    Segments sg;
+    int mode;
+    const void *Q, *K, *V;
+    void *O;
+    StateArgs st;
+};
+
+// Host-side launchers (return hipSuccess or the launch error).
+hipError_t launch_generic(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in,
+                       const float *z_in, float *S_out, float *z_out, bool total_to_slot0,
+                       hipStream_t stream);
+hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o,
+                         float *S, float *z, hipStream_t stream);
+// bf16 MFMA path; returns hipErrorNotSupported when the shape has no MFMA variant.
+hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream);
+bool mfma_supported(const Shape &sh, int chunk);
+
+}  // namespace la

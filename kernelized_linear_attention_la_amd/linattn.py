@@ -1,0 +1,221 @@
+"""Thin ctypes binding of liblinattn (the C ABI in include/liblinattn.h).
+
+The Python functions carry the names of the C entry points and do argument
+marshalling only: they check torch dtypes, shapes, devices and contiguity,
+allocate outputs and workspace with torch (device memory is torch's job),
+pass raw device pointers and the current HIP stream, and raise on a non-zero
+status.  Every arithmetic step runs in the HIP kernels of liblinattn.so.
+There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "liblinattn.so")
+
+LA_OK = 0
+LA_F32, LA_BF16 = 0, 1
+LA_PHI_ELU1, LA_PHI_FAVOR = 0, 1
+STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_UNSUPPORTED",
+                5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
+EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
+            "la_forward_noncausal", "la_forward_causal_chunked", "la_decode_step")
+
+
+class LaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("phi", ctypes.c_int),
+                ("m", ctypes.c_int), ("W", ctypes.c_void_p)]
+
+
+class LaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblinattn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"liblinattn is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(LaProblem)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.la_abi_version.restype = i
+        L.la_status_string.restype = ctypes.c_char_p
+        L.la_status_string.argtypes = [i]
+        L.la_feature_dim.restype = i
+        L.la_feature_dim.argtypes = [P]
+        L.la_workspace_bytes.restype = sz
+        L.la_workspace_bytes.argtypes = [P, i]
+        L.la_forward_noncausal.restype = i
+        L.la_forward_noncausal.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.la_forward_causal_chunked.restype = i
+        L.la_forward_causal_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.la_decode_step.restype = i
+        L.la_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def la_abi_version() -> int:
+    return lib().la_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().la_status_string(int(status)).decode()
+
+
+def problem(B, H, N, d_k, d_v, dtype=LA_F32, phi=LA_PHI_ELU1, m=0, W_ptr=0) -> LaProblem:
+    return LaProblem(int(B), int(H), int(N), int(d_k), int(d_v), int(dtype), int(phi), int(m),
+                     ctypes.c_void_p(int(W_ptr)) if W_ptr else None)
+
+
+def la_feature_dim(p: LaProblem) -> int:
+    return lib().la_feature_dim(ctypes.byref(p))
+
+
+def la_workspace_bytes(p: LaProblem, chunk: int) -> int:
+    return int(lib().la_workspace_bytes(ctypes.byref(p), int(chunk)))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+_DT = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("Q", q), ("K", k), ("V", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA/HIP tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype not in _DT:
+            raise TypeError(f"{name} must be float32 or bfloat16")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    if q.shape != k.shape or q.shape[:3] != v.shape[:3]:
+        raise ValueError(f"shape mismatch Q{tuple(q.shape)} K{tuple(k.shape)} V{tuple(v.shape)}")
+
+
+def _problem_of(q, v, phi, W):
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    if phi in ("favor", LA_PHI_FAVOR):
+        if W is None:
+            raise ValueError("FAVOR+ needs the projection W [m, d_k]")
+        if W.dtype != torch.float32 or not W.is_contiguous() or not W.is_cuda or W.dim() != 2 or W.shape[1] != dk:
+            raise ValueError("W must be a contiguous float32 device tensor [m, d_k]")
+        return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_FAVOR, W.shape[0], W.data_ptr())
+    return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_ELU1, 0, 0)
+
+
+def _state_pair(S, z, B, H, dp, dv, device, what):
+    if S is None and z is None:
+        return None, None
+    if S is None or z is None:
+        raise ValueError(f"{what}: S and z go together")
+    if S.dtype != torch.float32 or z.dtype != torch.float32 or not S.is_contiguous() or not z.is_contiguous():
+        raise ValueError(f"{what}: S and z must be contiguous float32")
+    if tuple(S.shape) != (B, H, dp, dv) or tuple(z.shape) != (B, H, dp):
+        raise ValueError(f"{what}: expected S [{B},{H},{dp},{dv}] and z [{B},{H},{dp}]")
+    if S.device != device or z.device != device:
+        raise ValueError(f"{what}: state must live on the inputs' device")
+    return S, z
+
+
+def _raise(status, where):
+    if status != LA_OK:
+        raise LaError(status, where)
+
+
+def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, z_in=None,
+                              S_out=None, z_out=None, out=None, workspace=None, stream=None):
+    """Causal chunkwise forward; returns O (same dtype as q).
+
+    S_out/z_out, when given, receive the final state (they may be S_in/z_in).
+    """
+    _check_qkv(q, k, v)
+    p = _problem_of(q, v, phi, W)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    S_in, z_in = _state_pair(S_in, z_in, B, H, dp, dv, q.device, "initial state")
+    S_out, z_out = _state_pair(S_out, z_out, B, H, dp, dv, q.device, "final state")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    nbytes = la_workspace_bytes(p, chunk)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_forward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                         _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                         _ptr(workspace), wsb, _stream(stream))
+    _raise(st, "la_forward_causal_chunked")
+    return out
+
+
+def la_forward_noncausal(q, k, v, phi="elu1", W=None, S_out=None, z_out=None, out=None, workspace=None,
+                         stream=None):
+    """Non-causal forward; returns O. S_out/z_out, when given, receive phi(K)^T V and phi(K)^T 1."""
+    _check_qkv(q, k, v)
+    p = _problem_of(q, v, phi, W)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    S_out, z_out = _state_pair(S_out, z_out, B, H, dp, dv, q.device, "state")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    nbytes = la_workspace_bytes(p, 64)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().la_forward_noncausal(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_out), _ptr(z_out),
+                                    _ptr(workspace), wsb, _stream(stream))
+    _raise(st, "la_forward_noncausal")
+    return out
+
+
+def la_decode_step(q, k, v, S, z, phi="elu1", W=None, out=None, stream=None):
+    """One decode step; q, k [B,H,1,d_k] (or [B,H,d_k]); v [B,H,1,d_v]. Updates S, z in place; returns o."""
+    if q.dim() == 3:
+        q, k, v = q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2)
+    _check_qkv(q, k, v)
+    if q.shape[2] != 1:
+        raise ValueError("decode takes one token per slice")
+    p = _problem_of(q, v, phi, W)
+    B, H, _, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    S, z = _state_pair(S, z, B, H, dp, dv, q.device, "state")
+    if S is None:
+        raise ValueError("decode needs the state S, z")
+    if out is None:
+        out = torch.empty((B, H, 1, dv), dtype=q.dtype, device=q.device)
+    st = lib().la_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z),
+                              _stream(stream))
+    _raise(st, "la_decode_step")
+    return out

@@ -1,0 +1,56 @@
+"""Helpers for GPU-vs-oracle parity tests: error metrics and device transfer.
+
+Error metric for outputs (one number per call): the largest, over rows
+r = (b, h, i), of max_c |y_rc - yref_rc| / max_c |yref_rc|.  Outputs are
+weighted means of zero-mean values, so many single entries sit near zero and
+an entry-wise relative error would be meaningless; a row's own scale is the
+natural yardstick.  States: per (b, h) slice max|dS| / max|S|; z is positive,
+so it is compared entry-wise.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def to_device(ht, device="cuda"):
+    """HostTensor (inputs module) -> torch device tensor in its storage dtype."""
+    if ht.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(ht.store)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(ht.store)).to(device)
+
+
+def to_f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def row_rel_err(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.abs(ref).max(axis=-1)
+    diff = np.abs(y - ref).max(axis=-1)
+    scale = np.where(scale > 0, scale, 1.0)
+    return float((diff / scale).max()) if diff.size else 0.0
+
+
+def state_rel_err(S, Sref):
+    S = np.asarray(S, np.float64)
+    Sref = np.asarray(Sref, np.float64)
+    lead = S.shape[:-2]
+    d = np.abs(S - Sref).reshape(*lead, -1).max(-1)
+    s = np.abs(Sref).reshape(*lead, -1).max(-1)
+    s = np.where(s > 0, s, 1.0)
+    return float((d / s).max()) if d.size else 0.0
+
+
+def z_rel_err(z, zref):
+    z = np.asarray(z, np.float64)
+    zref = np.asarray(zref, np.float64)
+    return float((np.abs(z - zref) / np.abs(zref)).max()) if z.size else 0.0
+
+
+def tol_for(dtype):
+    return TOL_BF16 if dtype == "bf16" else TOL_F32

@@ -1,0 +1,131 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every declared entry
+point, and its host validation rejects bad arguments before any launch.
+
+None of these calls reaches the GPU: every argument set used here fails
+validation (or is a pure host query), so they run on a machine without one.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kernelized_linear_attention_la_amd import linattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "liblinattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(linattn.LIB_PATH), reason="liblinattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("la_forward_noncausal", "la_forward_causal_chunked", "la_decode_step", "la_workspace_bytes"):
+        assert n in names
+    assert set(names) == set(linattn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = linattn.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", linattn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (la_\w+)", out))
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in exported, n
+    # nothing else leaks out of the library under the la_ prefix
+    assert exported == set(declared_functions())
+
+
+def test_abi_version_and_status_strings():
+    assert linattn.la_abi_version() == 1
+    for s in range(8):
+        assert linattn.status_string(s)
+    assert "unknown" in linattn.status_string(99)
+
+
+def _p(**kw):
+    d = dict(B=2, H=3, N=100, d_k=64, d_v=64, dtype=linattn.LA_BF16, phi=linattn.LA_PHI_ELU1, m=0, W_ptr=0)
+    d.update(kw)
+    return linattn.problem(**d)
+
+
+def test_feature_dim_and_workspace_queries():
+    p = _p()
+    assert linattn.la_feature_dim(p) == 64
+    pf = _p(phi=linattn.LA_PHI_FAVOR, m=256, W_ptr=0x1000)
+    assert linattn.la_feature_dim(pf) == 256
+    for c in (16, 32, 64, 128):
+        ws = linattn.la_workspace_bytes(p, c)
+        assert ws >= 0 and ws % 256 == 0
+    # invalid inputs give 0
+    assert linattn.la_workspace_bytes(p, 48) == 0
+    assert linattn.la_workspace_bytes(_p(d_k=129), 64) == 0
+    # large problems need segment workspace: B*H*P*(d'*d_v + d') floats
+    big = _p(B=2, H=16, N=16384, d_k=128, d_v=128)
+    assert linattn.la_workspace_bytes(big, 128) >= 2 * 16 * 2 * (128 * 128 + 128) * 4
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x100004)
+
+
+def _causal(p, chunk=64, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, Si=None, zi=None, So=None, zo=None, ws=None, wsb=0):
+    return linattn.lib().la_forward_causal_chunked(ctypes.byref(p), chunk, Q, K, V, O, Si, zi, So, zo, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(d_k=0), 2), (dict(d_k=129), 2), (dict(d_v=200), 2),
+    (dict(dtype=7), 3), (dict(phi=5), 4), (dict(m=3), 2),
+    (dict(phi=linattn.LA_PHI_FAVOR, m=0, W_ptr=0x1000), 2), (dict(phi=linattn.LA_PHI_FAVOR, m=257, W_ptr=0x1000), 2),
+    (dict(phi=linattn.LA_PHI_FAVOR, m=16, W_ptr=0), 1), (dict(phi=linattn.LA_PHI_FAVOR, m=16, W_ptr=0x1004), 5),
+])
+def test_causal_rejects_bad_problem(kw, status):
+    assert _causal(_p(**kw)) == status
+
+
+def test_causal_rejects_bad_arguments():
+    p = _p()
+    assert linattn.lib().la_forward_causal_chunked(None, 64, FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                                                   None, 0, None) == 1
+    for c in (0, 8, 48, 256, -64):
+        assert _causal(p, chunk=c) == 4
+    assert _causal(p, Q=None) == 1
+    assert _causal(p, O=None) == 1
+    assert _causal(p, Si=FAKE) == 1          # S_in without z_in
+    assert _causal(p, So=FAKE) == 1          # S_out without z_out
+    assert _causal(p, K=MIS) == 5
+    assert _causal(p, Si=MIS, zi=FAKE) == 5
+    # a problem that needs workspace, called without it
+    big = _p(B=1, H=1, N=8192)
+    assert linattn.la_workspace_bytes(big, 64) > 0
+    assert _causal(big, ws=None, wsb=0) == 6
+    need = linattn.la_workspace_bytes(big, 64)
+    assert _causal(big, ws=FAKE, wsb=need - 1) == 6
+
+
+def test_noncausal_and_decode_validation():
+    L = linattn.lib()
+    p = _p()
+    assert L.la_forward_noncausal(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, FAKE, 1 << 30, None) == 1
+    assert L.la_forward_noncausal(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert L.la_forward_noncausal(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None) == 6
+    assert L.la_forward_noncausal(ctypes.byref(p), FAKE, FAKE, MIS, FAKE, None, None, FAKE, 1 << 30, None) == 5
+    # decode: N must be 1, state required
+    assert L.la_decode_step(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    p1 = _p(N=1)
+    assert L.la_decode_step(ctypes.byref(p1), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    assert L.la_decode_step(ctypes.byref(p1), FAKE, FAKE, FAKE, FAKE, FAKE, MIS, None) == 5
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 4)
+    with pytest.raises(TypeError):
+        linattn.la_forward_causal_chunked(q, q, q, 16)

@@ -1,0 +1,263 @@
+"""GPU parity: liblinattn (through its C ABI) against the fp64 oracle.
+
+Every case generates seeded inputs, runs the HIP library on cuda:0 and the
+oracle on the host with the very same values, and compares with the metric of
+tests/parity.py: 1e-4 for fp32 storage, 2e-2 for bf16 storage with fp32
+accumulation and state.  Full-size workloads are checked on a seeded sample of
+(b, h) slices that the oracle recomputes one by one.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kernelized_linear_attention_la_amd import inputs
+from kernelized_linear_attention_la_amd import linattn as la
+from tests.parity import (TOL_BF16, TOL_F32, row_rel_err, state_rel_err, tol_for, to_device, to_f64,
+                          z_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(*a):
+    print("[parity]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(fi):
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    W = torch.from_numpy(fi.W).cuda() if fi.W is not None else None
+    return q, k, v, W
+
+
+def _zero_state(B, H, dp, dv):
+    return (torch.zeros(B, H, dp, dv, device="cuda", dtype=torch.float32),
+            torch.zeros(B, H, dp, device="cuda", dtype=torch.float32))
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked example through the GPU path
+# ---------------------------------------------------------------------------
+def test_worked_example_through_gpu():
+    with open(os.path.join(GOLDEN, "t1_kernel_la_worked_example.json")) as f:
+        g = json.load(f)
+    _say("worked example n=4 d=4")
+    Q = torch.tensor(g["Q"], dtype=torch.float32).view(1, 1, 4, 4).cuda()
+    K = torch.tensor(g["K"], dtype=torch.float32).view(1, 1, 4, 4).cuda()
+    V = torch.tensor(g["V"], dtype=torch.float32).view(1, 1, 4, 4).cuda()
+    S, z = _zero_state(1, 1, 4, 4)
+    O = la.la_forward_noncausal(Q, K, V, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(S[0, 0].cpu().numpy(), np.array(g["phiK_T_V"], np.float32))
+    np.testing.assert_array_equal(np.round(O[0, 0, 0].cpu().numpy().astype(np.float64), 2),
+                                  np.array(g["output_1_2dp"]))
+    ref, _, _ = oracle.noncausal("elu1", Q.cpu().numpy(), K.cpu().numpy(), V.cpu().numpy())
+    assert row_rel_err(to_f64(O), ref) < TOL_F32
+    for chunk in (16, 32, 64, 128):
+        S2, z2 = _zero_state(1, 1, 4, 4)
+        Oc = la.la_forward_causal_chunked(Q, K, V, chunk, S_out=S2, z_out=z2)
+        torch.cuda.synchronize()
+        refc, _, _ = oracle.causal_recurrent("elu1", Q.cpu().numpy(), K.cpu().numpy(), V.cpu().numpy())
+        assert row_rel_err(to_f64(Oc), refc) < TOL_F32
+        np.testing.assert_array_equal(S2[0, 0].cpu().numpy(), np.array(g["phiK_T_V"], np.float32))
+        np.testing.assert_array_equal(Oc[0, 0, 0].cpu().numpy(), V[0, 0, 0].cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# the small fp32 workload, both forms, every chunk size
+# ---------------------------------------------------------------------------
+def test_small_fp32_noncausal_and_causal():
+    wl = inputs.WORKLOADS["elu1_f32_b1h2n256d64"]
+    fi = inputs.forward_inputs(wl)
+    q, k, v, _ = _dev(fi)
+    _say(wl.name, "noncausal")
+    S, z = _zero_state(wl.B, wl.H, wl.dk, wl.dv)
+    O = la.la_forward_noncausal(q, k, v, S_out=S, z_out=z)
+    ref, Sref, zref = oracle.noncausal("elu1", fi.Q.f32, fi.K.f32, fi.V.f32)
+    torch.cuda.synchronize()
+    assert row_rel_err(to_f64(O), ref) < TOL_F32
+    assert state_rel_err(to_f64(S), Sref) < TOL_F32
+    assert z_rel_err(to_f64(z), zref) < TOL_F32
+    refc, Sc, zc = oracle.causal_recurrent("elu1", fi.Q.f32, fi.K.f32, fi.V.f32)
+    for chunk in (16, 32, 64, 128):
+        _say(wl.name, "causal chunk", chunk)
+        S, z = _zero_state(wl.B, wl.H, wl.dk, wl.dv)
+        O = la.la_forward_causal_chunked(q, k, v, chunk, S_out=S, z_out=z)
+        torch.cuda.synchronize()
+        e = row_rel_err(to_f64(O), refc)
+        assert e < TOL_F32, (chunk, e)
+        assert state_rel_err(to_f64(S), Sc) < TOL_F32
+        assert z_rel_err(to_f64(z), zc) < TOL_F32
+
+
+# ---------------------------------------------------------------------------
+# ragged and odd shapes, both dtypes, both feature maps
+# ---------------------------------------------------------------------------
+CASES = [
+    # (B, H, N, dk, dv, dtype, phi, m, chunk)
+    (1, 1, 1, 64, 64, "f32", "elu1", 0, 64),
+    (1, 1, 13, 64, 64, "bf16", "elu1", 0, 64),
+    (2, 3, 200, 40, 24, "f32", "elu1", 0, 32),
+    (1, 2, 333, 64, 64, "bf16", "elu1", 0, 64),
+    (1, 2, 300, 128, 128, "bf16", "elu1", 0, 128),
+    (1, 1, 517, 128, 96, "f32", "elu1", 0, 16),
+    (1, 2, 190, 64, 64, "bf16", "favor", 256, 64),
+    (2, 1, 77, 16, 8, "f32", "favor", 24, 32),
+    (1, 1, 5000, 64, 64, "bf16", "elu1", 0, 64),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)), ids=[f"B{c[0]}H{c[1]}N{c[2]}dk{c[3]}dv{c[4]}{c[5]}{c[6]}{c[8]}"
+                                                    for c in CASES])
+def test_shapes_against_oracle(ci):
+    case = CASES[ci]
+    B, H, N, dk, dv, dtype, phi, m, chunk = case
+    scale = (dk ** -0.25) if phi == "favor" else (dk ** -0.5)
+    fi = inputs.custom_inputs(ci, B, H, N, dk, dv, scale=scale, dtype=dtype, phi=phi, m=m)
+    q, k, v, W = _dev(fi)
+    dp = m if phi == "favor" else dk
+    _say("case", case)
+    S, z = _zero_state(B, H, dp, dv)
+    O = la.la_forward_causal_chunked(q, k, v, chunk, phi=phi, W=W, S_out=S, z_out=z)
+    ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    e = row_rel_err(to_f64(O), ref)
+    assert e < tol, e
+    assert state_rel_err(to_f64(S), Sref) < tol
+    assert z_rel_err(to_f64(z), zref) < tol
+    On = la.la_forward_noncausal(q, k, v, phi=phi, W=W)
+    refn, _, _ = oracle.noncausal(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
+    torch.cuda.synchronize()
+    assert row_rel_err(to_f64(On), refn) < tol
+
+
+def test_state_handoff_and_in_place_state():
+    """forward(0..M) then forward(M..N) from its state == forward(0..N), S_in aliasing S_out."""
+    B, H, N, d = 2, 2, 300, 64
+    fi = inputs.custom_inputs(42, B, H, N, d, d, scale=d ** -0.5, dtype="f32")
+    q, k, v, _ = _dev(fi)
+    ref, Sref, zref = oracle.causal_recurrent("elu1", fi.Q.f32, fi.K.f32, fi.V.f32)
+    for M in (1, 64, 100, 299):
+        _say("handoff M", M)
+        S, z = _zero_state(B, H, d, d)
+        O1 = la.la_forward_causal_chunked(q[:, :, :M].contiguous(), k[:, :, :M].contiguous(),
+                                          v[:, :, :M].contiguous(), 64, S_out=S, z_out=z)
+        O2 = la.la_forward_causal_chunked(q[:, :, M:].contiguous(), k[:, :, M:].contiguous(),
+                                          v[:, :, M:].contiguous(), 32, S_in=S, z_in=z, S_out=S, z_out=z)
+        torch.cuda.synchronize()
+        assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < TOL_F32
+        assert state_rel_err(to_f64(S), Sref) < TOL_F32
+        assert z_rel_err(to_f64(z), zref) < TOL_F32
+
+
+def test_decode_matches_forward_and_oracle():
+    B, H, N, d = 3, 4, 40, 128
+    for phi, m in (("elu1", 0), ("favor", 64)):
+        fi = inputs.custom_inputs(7, B, H, N, d, d, scale=(d ** -0.25 if phi == "favor" else d ** -0.5),
+                                  dtype="f32", phi=phi, m=m)
+        q, k, v, W = _dev(fi)
+        dp = m if phi == "favor" else d
+        _say("decode steps", phi)
+        S, z = _zero_state(B, H, dp, d)
+        outs = []
+        for t in range(N):
+            outs.append(la.la_decode_step(q[:, :, t:t + 1].contiguous(), k[:, :, t:t + 1].contiguous(),
+                                          v[:, :, t:t + 1].contiguous(), S, z, phi=phi, W=W))
+        torch.cuda.synchronize()
+        ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
+        assert row_rel_err(to_f64(torch.cat(outs, 2)), ref) < TOL_F32
+        assert state_rel_err(to_f64(S), Sref) < TOL_F32
+        assert z_rel_err(to_f64(z), zref) < TOL_F32
+
+
+def test_deterministic_repeat():
+    wl = inputs.WORKLOADS["elu1_bf16_b4h8n2048d64_c64"]
+    fi = inputs.forward_inputs(wl)
+    q, k, v, _ = _dev(fi)
+    a = la.la_forward_causal_chunked(q, k, v, wl.chunk)
+    b = la.la_forward_causal_chunked(q, k, v, wl.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled slices
+# ---------------------------------------------------------------------------
+def _sample(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [divmod(int(i), H) for i in sorted(idx)]
+
+
+def _gather(x, samp):
+    """Stack the sampled (b, h) slices of x [B, H, ...] into [1, len(samp), ...]."""
+    return np.stack([x[b, h] for (b, h) in samp])[None]
+
+
+@pytest.mark.parametrize("name", ["elu1_bf16_b4h8n2048d64_c64", "elu1_bf16_b2h16n16384d128_c128",
+                                  "favor_bf16_b2h8n8192d64_m256_c64"])
+def test_full_size_forward_sampled(name):
+    wl = inputs.WORKLOADS[name]
+    _say("full", name, "generating")
+    fi = inputs.forward_inputs(wl)
+    q, k, v, W = _dev(fi)
+    S, z = _zero_state(wl.B, wl.H, wl.dprime, wl.dv)
+    _say("full", name, "gpu")
+    O = la.la_forward_causal_chunked(q, k, v, wl.chunk, phi=wl.phi, W=W, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    samp = _sample(wl.B, wl.H, 4, wl.wid)
+    _say("full", name, "oracle on slices", samp)
+    ref, Sref, zref = oracle.causal_recurrent(wl.phi, _gather(fi.Q.f32, samp), _gather(fi.K.f32, samp),
+                                              _gather(fi.V.f32, samp), fi.W)
+    Oh, Sh, zh = to_f64(O), to_f64(S), to_f64(z)
+    e = row_rel_err(_gather(Oh, samp), ref)
+    assert e < TOL_BF16, e
+    assert state_rel_err(_gather(Sh, samp), Sref) < TOL_BF16
+    assert z_rel_err(_gather(zh, samp), zref) < TOL_BF16
+    assert torch.isfinite(O.float()).all()
+
+
+def test_full_size_decode_sampled():
+    wl = inputs.WORKLOADS["decode_elu1_f32_s256h32d128_prefix1024_steps64"]
+    _say("decode full: generating prefix")
+    fi = inputs.forward_inputs(wl)
+    q, k, v, _ = _dev(fi)
+    S, z = _zero_state(wl.B, wl.H, wl.dk, wl.dv)
+    _say("decode full: prefix forward")
+    la.la_forward_causal_chunked(q, k, v, wl.chunk, S_out=S, z_out=z)
+    del q, k, v
+    torch.cuda.synchronize()
+    samp = _sample(wl.B, wl.H, 8, 4)
+    _, S_ref, z_ref = oracle.causal_recurrent("elu1", _gather(fi.Q.f32, samp), _gather(fi.K.f32, samp),
+                                              _gather(fi.V.f32, samp))
+    assert state_rel_err(_gather(to_f64(S), samp), S_ref) < TOL_F32
+    assert z_rel_err(_gather(to_f64(z), samp), z_ref) < TOL_F32
+    del fi
+    worst = 0.0
+    for step in range(wl.decode_steps):
+        qs, ks, vs = inputs.decode_step_inputs(wl, step)
+        o = la.la_decode_step(to_device(qs), to_device(ks), to_device(vs), S, z)
+        torch.cuda.synchronize()
+        if step % 16 == 0 or step == wl.decode_steps - 1:
+            _say("decode full: step", step)
+        oref, S_ref, z_ref = oracle.decode_step("elu1", _gather(qs.f32, samp)[:, :, 0], _gather(ks.f32, samp)[:, :, 0],
+                                                _gather(vs.f32, samp)[:, :, 0], S_ref, z_ref)
+        worst = max(worst, row_rel_err(_gather(to_f64(o), samp)[:, :, 0], oref))
+    assert worst < TOL_F32, worst
+    assert state_rel_err(_gather(to_f64(S), samp), S_ref) < TOL_F32
+    assert z_rel_err(_gather(to_f64(z), samp), z_ref) < TOL_F32
