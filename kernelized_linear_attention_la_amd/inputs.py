@@ -154,7 +154,7 @@ def orthogonal_gaussian_rows(workload_id: int, m: int, d: int) -> np.ndarray:
         rows.append(qm.T)  # rows of an orthogonal matrix
     w = np.concatenate(rows, axis=0)[:m]
     lengths = np.linalg.norm(rng.standard_normal((m, d)), axis=1)
-    return (w * lengths[:, None]).astype(np.float32)
+    return np.ascontiguousarray((w * lengths[:, None]).astype(np.float32))
 
 
 def iid_gaussian_rows(seed: int, m: int, d: int) -> np.ndarray:
