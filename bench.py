@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal kernelized linear attention hot path on one MI355X.
+
+A step is one full pass of the hot path over one batch of seeded synthetic
+input: la_forward_causal_chunked (feature map, intra-chunk masked products,
+inter-chunk state read, fused normalisation, state scan, final state export)
+for a forward workload, or one la_decode_step over every sequence and head for
+the decode workload.  Inputs are resident in HBM before timing starts; the
+forward workloads rotate through enough copies of the batch to overflow the
+256 MB Infinity Cache, so every step streams from HBM.
+
+Prints ONE JSON line (rank 0, N=1):
+  value         whole-job throughput (tokens/s; decode: generated tokens/s,
+                one token per sequence per step)
+  roofline      the dominant kernel's achieved algorithmic bytes (or flops)
+                per launch / its average duration, from HIP events recorded
+                around that kernel on its own stream, against the MI355X peak
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "elu1_bf16_b4h8n2048d64_c64"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+ROTATE_BYTES = 768 << 20     # > 256 MB Infinity Cache
+
+
+def elem_bytes(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def forward_alg_bytes(wl):
+    """Algorithmic HBM bytes of one causal forward: Q, K, V read once, O written once, final state written."""
+    e = elem_bytes(wl.dtype)
+    tok = wl.B * wl.H * wl.N
+    state = wl.B * wl.H * (wl.dprime * wl.dv + wl.dprime) * 4
+    return tok * (2 * wl.dk + 2 * wl.dv) * e + state
+
+
+def forward_alg_flops(wl):
+    """Algorithmic flops of one causal forward (causal half of the intra-chunk products).
+
+    per token: state update 2 d' d_v, inter-chunk read 2 d' d_v (+2 d' for z),
+    intra-chunk scores and values (C+1)(d' + d_v) on average, normalisation d_v,
+    FAVOR+ projection 2 d_k m for q and for k.
+    """
+    C, dp, dv, dk = wl.chunk, wl.dprime, wl.dv, wl.dk
+    per = 4 * dp * dv + 2 * dp + (C + 1) * (dp + dv) + dv
+    if wl.phi == "favor":
+        per += 4 * dk * wl.m
+    return wl.B * wl.H * wl.N * per
+
+
+def decode_alg_bytes(wl):
+    """Algorithmic bytes of one decode step: S and z read and written once, q, k, v read, o written."""
+    e = elem_bytes(wl.dtype)
+    slices = wl.B * wl.H
+    return slices * (2 * (wl.dprime * wl.dv + wl.dprime) * 4 + (2 * wl.dk + 2 * wl.dv) * e)
+
+
+class HipEvents:
+    """Raw HIP events through the runtime liblinattn is linked against."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        t = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def run_cpu_baseline(wl, fi, seconds):
+    """Time the fp64 oracle (causal recurrence) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    nthreads = oracle.num_threads()
+    BH = wl.B * wl.H
+    # per-slice cost estimate from a 1-slice probe, then enough slices for `seconds`
+    t0 = time.perf_counter()
+    oracle.causal_recurrent(wl.phi, fi.Q.f32[:1, :1], fi.K.f32[:1, :1], fi.V.f32[:1, :1], fi.W)
+    t1 = time.perf_counter() - t0
+    n_slices = int(max(1, min(BH, round(seconds * nthreads / max(t1, 1e-6)))))
+    Qf = fi.Q.f32.reshape(1, BH, wl.N, wl.dk)[:, :n_slices]
+    Kf = fi.K.f32.reshape(1, BH, wl.N, wl.dk)[:, :n_slices]
+    Vf = fi.V.f32.reshape(1, BH, wl.N, wl.dv)[:, :n_slices]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.causal_recurrent(wl.phi, Qf, Kf, Vf, fi.W)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds * 0.5 or reps >= 50:
+            break
+    tokens = reps * n_slices * wl.N
+    return {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 causal recurrence on {n_slices} of {BH} (b,h) slices x {wl.N} tokens, "
+                      f"{reps} pass(es), {el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
+
+
+def bench_forward(args, wl):
+    import torch
+    from kernelized_linear_attention_la_amd import inputs
+    from kernelized_linear_attention_la_amd import linattn as la
+
+    fi = inputs.forward_inputs(wl)
+    dev = torch.device("cuda:0")
+
+    def to_dev(ht):
+        t = torch.from_numpy(ht.store)
+        return (t.view(torch.bfloat16) if ht.dtype == "bf16" else t).to(dev)
+
+    q0, k0, v0 = to_dev(fi.Q), to_dev(fi.K), to_dev(fi.V)
+    W = torch.from_numpy(fi.W).to(dev) if fi.W is not None else None
+    set_bytes = 2 * q0.nbytes + k0.nbytes + 2 * v0.nbytes
+    R = max(1, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
+    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(v0)) for _ in range(R)]
+    S = torch.zeros(wl.B, wl.H, wl.dprime, wl.dv, device=dev)
+    z = torch.zeros(wl.B, wl.H, wl.dprime, device=dev)
+    p = la._problem_of(q0, v0, wl.phi, W)
+    ws = torch.empty(max(1, la.la_workspace_bytes(p, wl.chunk)), dtype=torch.uint8, device=dev)
+
+    def step(i, stream=None, events=None):
+        q, k, v, o = sets[i % R]
+        la.la_forward_causal_chunked(q, k, v, wl.chunk, phi=wl.phi, W=W, S_out=S, z_out=z, out=o,
+                                     workspace=ws, stream=stream, events=events)
+
+    # the step sequence is launch-bound at small sizes: capture it in HIP graphs
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(R):  # eager warm-up on the capture stream
+            step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # live per-kernel timing of the dominant kernel (the chunk loop) over K steps
+    hev = HipEvents(la.lib())
+    ev_pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    kev = la.LaKernelEvents()
+    raw_stream = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            kev.start[la.LA_KSLOT_CHUNK] = ev_pairs[i][0]
+            kev.stop[la.LA_KSLOT_CHUNK] = ev_pairs[i][1]
+            step(i, stream=stream, events=kev)
+    torch.cuda.synchronize()
+    durs = [hev.elapsed_ms(a, b) for a, b in ev_pairs]
+    for a, b in ev_pairs:
+        hev.destroy(a)
+        hev.destroy(b)
+    kern_ms = sum(durs) / len(durs)
+
+    tokens = wl.B * wl.H * wl.N
+    value = tokens / (ms_per_step * 1e-3)
+    alg_bytes = forward_alg_bytes(wl)
+    alg_flops = forward_alg_flops(wl)
+    # chunk kernel's algorithmic bytes: Q, K, V read, O written (state traffic excluded)
+    chunk_bytes = tokens * (2 * wl.dk + 2 * wl.dv) * elem_bytes(wl.dtype)
+    flop_per_byte = alg_flops / alg_bytes
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flop_per_byte < ridge:
+        ach = chunk_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    else:
+        ach = alg_flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
+    roof["kernel"] = "chunk loop (la_forward_causal_chunked, LA_KSLOT_CHUNK)"
+    roof["kernel_avg_us"] = kern_ms * 1e3
+    extra = {
+        "step_hbm_frac": alg_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "step_mfma_frac": alg_flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12),
+        "rotated_input_sets": R,
+    }
+    return value, ms_per_step, roof, extra, fi
+
+
+def bench_decode(args, wl):
+    import torch
+    from kernelized_linear_attention_la_amd import inputs
+    from kernelized_linear_attention_la_amd import linattn as la
+
+    dev = torch.device("cuda:0")
+    fi = inputs.forward_inputs(wl)
+
+    def to_dev(ht):
+        t = torch.from_numpy(ht.store)
+        return (t.view(torch.bfloat16) if ht.dtype == "bf16" else t).to(dev)
+
+    S = torch.zeros(wl.B, wl.H, wl.dprime, wl.dv, device=dev)
+    z = torch.zeros(wl.B, wl.H, wl.dprime, device=dev)
+    q, k, v = to_dev(fi.Q), to_dev(fi.K), to_dev(fi.V)
+    la.la_forward_causal_chunked(q, k, v, wl.chunk, S_out=S, z_out=z)  # prefix (not timed)
+    torch.cuda.synchronize()
+    del q, k, v
+    steps_in = []
+    for s in range(wl.decode_steps):
+        qs, ks, vs = inputs.decode_step_inputs(wl, s)
+        steps_in.append((to_dev(qs), to_dev(ks), to_dev(vs)))
+    o = torch.empty(wl.B, wl.H, 1, wl.dv, device=dev, dtype=steps_in[0][0].dtype)
+    stream = torch.cuda.current_stream()
+    raw_stream = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        qs, ks, vs = steps_in[i % len(steps_in)]
+        la.la_decode_step(qs, ks, vs, S, z, phi=wl.phi, out=o)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    hev = HipEvents(la.lib())
+    ev_pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        hev.record(ev_pairs[i][0], raw_stream)
+        step(args.warmup + i)
+        hev.record(ev_pairs[i][1], raw_stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [hev.elapsed_ms(a, b) for a, b in ev_pairs]
+    for a, b in ev_pairs:
+        hev.destroy(a)
+        hev.destroy(b)
+    kern_ms = sum(durs) / len(durs)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = wl.B / (ms_per_step * 1e-3)  # one generated token per sequence per step
+    nbytes = decode_alg_bytes(wl)
+    ach = nbytes / (kern_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+            "traffic": None, "kernel": "decode step (la_decode_step)", "kernel_avg_us": kern_ms * 1e3}
+    extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3)}
+    return value, ms_per_step, roof, extra, fi
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget; 0 skips it")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the hot path shards over (batch, head) slices and sequence segments; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    from kernelized_linear_attention_la_amd import inputs
+    if args.workload not in inputs.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(inputs.WORKLOADS)}")
+    wl = inputs.WORKLOADS[args.workload]
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    if wl.decode_steps:
+        value, ms, roof, extra, fi = bench_decode(args, wl)
+        metric = "decode tokens/s"
+    else:
+        value, ms, roof, extra, fi = bench_forward(args, wl)
+        metric = "causal linear-attn fwd tokens/s (B*H*N/s)"
+    cpu = None
+    if args.cpu_seconds > 0:
+        if wl.decode_steps:
+            cpu = None  # the oracle baseline is defined on the forward workloads
+        else:
+            cpu = run_cpu_baseline(wl, fi, args.cpu_seconds)
+    config = {"workload": wl.name, "phi": wl.phi, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,
+              "chunk": wl.chunk}
+    if wl.m:
+        config["m"] = wl.m
+    if wl.decode_steps:
+        config.update({"prefix": wl.N, "decode_steps_cycled": wl.decode_steps})
+    line = {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded i.i.d. Gaussian)",
+            "config": config, "roofline": roof, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

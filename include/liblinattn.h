@@ -116,6 +116,38 @@ la_status la_forward_causal_chunked(const la_problem *p, int chunk,
                                     void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Per-kernel timing hook for profiling and benchmarking.  A causal call
+ * enqueues up to three kernels, each in its own slot:
+ *   LA_KSLOT_STATE  per-segment sums phi(K)^T V, phi(K)^T 1 (only when the
+ *                   sequence is split into several segments),
+ *   LA_KSLOT_SCAN   exclusive prefix of those sums over segments (same case),
+ *   LA_KSLOT_CHUNK  the chunk loop that writes O (always).
+ * For every slot whose kernel is enqueued, the library records start[slot]
+ * right before and stop[slot] right after that kernel, on the call's stream
+ * (hipEventRecord).  Entries may be NULL (not recorded).  The events are
+ * created, owned and queried by the caller (hipEvent_t passed as void*).
+ * launched[slot] is set to 1 for each kernel enqueued, 0 otherwise.
+ */
+enum { LA_KSLOT_STATE = 0, LA_KSLOT_SCAN = 1, LA_KSLOT_CHUNK = 2, LA_KSLOTS = 3 };
+
+typedef struct {
+    void *start[LA_KSLOTS];
+    void *stop[LA_KSLOTS];
+    int launched[LA_KSLOTS];
+} la_kernel_events;
+
+/*
+ * la_forward_causal_chunked with the timing hook above; identical results.
+ * ev may be NULL (then this is exactly la_forward_causal_chunked).
+ */
+la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
+                                          const void *Q, const void *K, const void *V, void *O,
+                                          const float *S_in, const float *z_in,
+                                          float *S_out, float *z_out,
+                                          void *ws, size_t ws_bytes, void *stream,
+                                          la_kernel_events *ev);
+
+/*
  * One recurrent decode step for every (b, h) ("Linear Attention": constant work
  * and memory per generated token; "Story of Attention Part 5", 1a recurrence):
  *   S += phi(k) v^T,  z += phi(k),  o = (phi(q)^T S) / (phi(q)^T z).

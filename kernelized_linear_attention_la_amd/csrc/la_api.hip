@@ -123,6 +123,20 @@ hipError_t launch_fwd(bool mfma, const FwdArgs &a, hipStream_t st) {
     return mfma ? launch_mfma(a, st) : launch_generic(a, st);
 }
 
+// Optional event records around one kernel of a call (profiling hook).
+struct Timing {
+    la_kernel_events *ev;
+    hipStream_t st;
+    void begin(int slot) const {
+        if (!ev) return;
+        ev->launched[slot] = 1;
+        if (ev->start[slot]) (void)hipEventRecord(static_cast<hipEvent_t>(ev->start[slot]), st);
+    }
+    void end(int slot) const {
+        if (ev && ev->stop[slot]) (void)hipEventRecord(static_cast<hipEvent_t>(ev->stop[slot]), st);
+    }
+};
+
 }  // namespace
 }  // namespace la
 
@@ -194,9 +208,10 @@ LA_API la_status la_forward_noncausal(const la_problem *p, const void *Q, const 
     return LA_OK;
 }
 
-LA_API la_status la_forward_causal_chunked(const la_problem *p, int chunk, const void *Q, const void *K,
-                                           const void *V, void *O, const float *S_in, const float *z_in,
-                                           float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream) {
+LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk, const void *Q, const void *K,
+                                                 const void *V, void *O, const float *S_in, const float *z_in,
+                                                 float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream,
+                                                 la_kernel_events *ev) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
@@ -210,20 +225,27 @@ LA_API la_status la_forward_causal_chunked(const la_problem *p, int chunk, const
     Segments g = causal_plan(sh, chunk, &mf);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)sh.dp * sh.dv, nz = (size_t)sh.dp;
+    const bool direct = causal_direct(sh, g, mf);
+    WsLayout wl = ws_layout(sh, g.P);
+    if (!direct && (!ws || ws_bytes < wl.total)) return LA_ERR_WORKSPACE;
+    if (ev)
+        for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
+    Timing tm{ev, hs};
 
     FwdArgs c{};
     c.sh = sh; c.sg = g; c.mode = kModeCausal;
     c.Q = Q; c.K = K; c.V = V; c.O = O;
-    if (causal_direct(sh, g, mf)) {
+    if (direct) {
         // one workgroup per slice: start from S_in, finish into S_out
         c.st.S_src = S_in; c.st.z_src = z_in;
         c.st.src_slice = nS; c.st.zsrc_slice = nz;
         c.st.S_dst = S_out; c.st.z_dst = z_out;
         c.st.dst_slice = nS; c.st.zdst_slice = nz;
-        return launch_fwd(mf, c, hs) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+        tm.begin(LA_KSLOT_CHUNK);
+        hipError_t e = launch_fwd(mf, c, hs);
+        tm.end(LA_KSLOT_CHUNK);
+        return e == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
-    WsLayout wl = ws_layout(sh, g.P);
-    if (!ws || ws_bytes < wl.total) return LA_ERR_WORKSPACE;
     float *wsS = static_cast<float *>(ws);
     float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
 
@@ -233,14 +255,27 @@ LA_API la_status la_forward_causal_chunked(const la_problem *p, int chunk, const
     a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
     a.st.S_dst = wsS; a.st.z_dst = wsz;
     a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
+    tm.begin(LA_KSLOT_STATE);
     if (launch_fwd(mf, a, hs) != hipSuccess) return LA_ERR_DEVICE;
+    tm.end(LA_KSLOT_STATE);
     // B. exclusive prefix over segments (+ S_in); final state to S_out
+    tm.begin(LA_KSLOT_SCAN);
     if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, S_out, z_out, false, hs) != hipSuccess) return LA_ERR_DEVICE;
+    tm.end(LA_KSLOT_SCAN);
     // C. chunk loop of every segment from its prefix state
     c.st.S_src = wsS; c.st.z_src = wsz;
     c.st.src_slice = g.P * nS; c.st.src_seg = nS; c.st.zsrc_slice = g.P * nz; c.st.zsrc_seg = nz;
+    tm.begin(LA_KSLOT_CHUNK);
     if (launch_fwd(mf, c, hs) != hipSuccess) return LA_ERR_DEVICE;
+    tm.end(LA_KSLOT_CHUNK);
     return LA_OK;
+}
+
+LA_API la_status la_forward_causal_chunked(const la_problem *p, int chunk, const void *Q, const void *K,
+                                           const void *V, void *O, const float *S_in, const float *z_in,
+                                           float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream) {
+    return la_forward_causal_chunked_timed(p, chunk, Q, K, V, O, S_in, z_in, S_out, z_out, ws, ws_bytes, stream,
+                                           nullptr);
 }
 
 LA_API la_status la_decode_step(const la_problem *p, const void *q, const void *k, const void *v, void *o, float *S,

@@ -100,7 +100,7 @@ __device__ void value_tile(const Shape &sh, const GenLayout &L, const T *V, int 
     }
 }
 
-template <typename T>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
     extern __shared__ float smem[];
     const Shape sh = a.sh;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         const int Lc = min(C, N - t0);
-        if (a.mode != kModeState) {
+        if constexpr (MODE != kModeState) {
             for (int qt = 0; qt < Lc; qt += L.T) {
                 const int nq = min(L.T, Lc - qt);
                 phi_tile(sh, L, Qs, t0 + qt, nq, sX, sSq, sPQ);
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
                         }
                     }
                 }
-                if (a.mode == kModeCausal) {
+                if constexpr (MODE == kModeCausal) {
                     // intra-chunk masked pairwise part, key tiles up to the query tile
                     for (int kt = 0; kt <= qt; kt += L.T) {
                         const int nk = min(L.T, Lc - kt);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
                 __syncthreads();  // sPQ is reused by the next query tile
             }
         }
-        if (a.mode != kModeRead) {
+        if constexpr (MODE != kModeRead) {
             // carry the state past this chunk: S += phiK^T V, z += phiK^T 1
             for (int kt = 0; kt < Lc; kt += L.T) {
                 const int nk = min(L.T, Lc - kt);
@@ -282,10 +282,22 @@ hipError_t launch_generic(const FwdArgs &a, hipStream_t stream) {
     const int nslab = (a.sh.dv + kVS - 1) / kVS;
     const size_t grid = (size_t)a.sh.BH * a.sg.P * nslab;
     const size_t lds = generic_lds_bytes(a.sh.dk, a.sh.dp);
-    if (a.sh.dtype == kF32)
-        hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL(k_generic<uint16_t>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+    const dim3 gr((unsigned)grid), bl(kThreads);
+    const bool f32 = a.sh.dtype == kF32;
+    switch (a.mode) {
+        case kModeState:
+            if (f32) hipLaunchKernelGGL((k_generic<float, kModeState>), gr, bl, lds, stream, a);
+            else hipLaunchKernelGGL((k_generic<uint16_t, kModeState>), gr, bl, lds, stream, a);
+            break;
+        case kModeCausal:
+            if (f32) hipLaunchKernelGGL((k_generic<float, kModeCausal>), gr, bl, lds, stream, a);
+            else hipLaunchKernelGGL((k_generic<uint16_t, kModeCausal>), gr, bl, lds, stream, a);
+            break;
+        default:
+            if (f32) hipLaunchKernelGGL((k_generic<float, kModeRead>), gr, bl, lds, stream, a);
+            else hipLaunchKernelGGL((k_generic<uint16_t, kModeRead>), gr, bl, lds, stream, a);
+            break;
+    }
     return hipGetLastError();
 }
 

@@ -23,7 +23,9 @@ LA_PHI_ELU1, LA_PHI_FAVOR = 0, 1
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_UNSUPPORTED",
                 5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
-            "la_forward_noncausal", "la_forward_causal_chunked", "la_decode_step")
+            "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
+            "la_decode_step")
+LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 
 
 class LaProblem(ctypes.Structure):
@@ -31,6 +33,11 @@ class LaProblem(ctypes.Structure):
                 ("d_k", ctypes.c_int), ("d_v", ctypes.c_int),
                 ("dtype", ctypes.c_int), ("phi", ctypes.c_int),
                 ("m", ctypes.c_int), ("W", ctypes.c_void_p)]
+
+
+class LaKernelEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p * LA_KSLOTS), ("stop", ctypes.c_void_p * LA_KSLOTS),
+                ("launched", ctypes.c_int * LA_KSLOTS)]
 
 
 class LaError(RuntimeError):
@@ -62,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.la_forward_noncausal.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.la_forward_causal_chunked.restype = i
         L.la_forward_causal_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.la_forward_causal_chunked_timed.restype = i
+        L.la_forward_causal_chunked_timed.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                      ctypes.POINTER(LaKernelEvents)]
         L.la_decode_step.restype = i
         L.la_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -153,10 +163,12 @@ def _raise(status, where):
 
 
 def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, z_in=None,
-                              S_out=None, z_out=None, out=None, workspace=None, stream=None):
+                              S_out=None, z_out=None, out=None, workspace=None, stream=None, events=None):
     """Causal chunkwise forward; returns O (same dtype as q).
 
     S_out/z_out, when given, receive the final state (they may be S_in/z_in).
+    events: optional LaKernelEvents (per-kernel hipEvent records; see
+    la_forward_causal_chunked_timed in the C header).
     """
     _check_qkv(q, k, v)
     p = _problem_of(q, v, phi, W)
@@ -171,10 +183,16 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().la_forward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                         _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
-                                         _ptr(workspace), wsb, _stream(stream))
-    _raise(st, "la_forward_causal_chunked")
+    if events is None:
+        st = lib().la_forward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                             _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                             _ptr(workspace), wsb, _stream(stream))
+        _raise(st, "la_forward_causal_chunked")
+    else:
+        st = lib().la_forward_causal_chunked_timed(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(out), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                                   _ptr(workspace), wsb, _stream(stream), ctypes.byref(events))
+        _raise(st, "la_forward_causal_chunked_timed")
     return out
 
 

@@ -118,6 +118,13 @@ CASES = [
     (1, 2, 190, 64, 64, "bf16", "favor", 256, 64),
     (2, 1, 77, 16, 8, "f32", "favor", 24, 32),
     (1, 1, 5000, 64, 64, "bf16", "elu1", 0, 64),
+    # bf16 matrix-core variants: every (d, chunk) pair, ragged tails, tiny N
+    (2, 2, 1000, 128, 128, "bf16", "elu1", 0, 64),
+    (1, 3, 777, 64, 64, "bf16", "elu1", 0, 128),
+    (1, 1, 1, 128, 128, "bf16", "elu1", 0, 128),
+    (3, 1, 65, 64, 64, "bf16", "favor", 256, 64),
+    (1, 1, 1, 64, 64, "bf16", "favor", 256, 64),
+    (1, 2, 2100, 64, 64, "bf16", "favor", 256, 64),
 ]
 
 
@@ -163,6 +170,32 @@ def test_state_handoff_and_in_place_state():
         assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < TOL_F32
         assert state_rel_err(to_f64(S), Sref) < TOL_F32
         assert z_rel_err(to_f64(z), zref) < TOL_F32
+
+
+@pytest.mark.parametrize("phi,d,m", [("elu1", 64, 0), ("elu1", 128, 0), ("favor", 64, 256)])
+def test_bf16_handoff_and_chunk_invariance(phi, d, m):
+    """bf16 path: split forward with state hand-off, and every supported chunk, against the oracle."""
+    B, H, N = 2, 2, 700
+    fi = inputs.custom_inputs(55, B, H, N, d, d, scale=(d ** -0.25 if phi == "favor" else d ** -0.5),
+                              dtype="bf16", phi=phi, m=m)
+    q, k, v, W = _dev(fi)
+    dp = m if phi == "favor" else d
+    ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
+    for chunk in (16, 32, 64, 128):
+        _say("bf16 chunk", phi, d, chunk)
+        O = la.la_forward_causal_chunked(q, k, v, chunk, phi=phi, W=W)
+        torch.cuda.synchronize()
+        assert row_rel_err(to_f64(O), ref) < TOL_BF16, chunk
+    M = 301
+    S, z = _zero_state(B, H, dp, d)
+    O1 = la.la_forward_causal_chunked(q[:, :, :M].contiguous(), k[:, :, :M].contiguous(), v[:, :, :M].contiguous(),
+                                      64, phi=phi, W=W, S_out=S, z_out=z)
+    O2 = la.la_forward_causal_chunked(q[:, :, M:].contiguous(), k[:, :, M:].contiguous(), v[:, :, M:].contiguous(),
+                                      64, phi=phi, W=W, S_in=S, z_in=z, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < TOL_BF16
+    assert state_rel_err(to_f64(S), Sref) < TOL_BF16
+    assert z_rel_err(to_f64(z), zref) < TOL_BF16
 
 
 def test_decode_matches_forward_and_oracle():
