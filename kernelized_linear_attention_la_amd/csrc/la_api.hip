@@ -76,6 +76,17 @@ int generic_columns(const Shape &sh) { return (sh.dv + 31) / 32; }
 Segments causal_plan(const Shape &sh, int chunk, bool *use_mfma) {
     const bool mf = mfma_supported(sh, chunk);
     if (use_mfma) *use_mfma = mf;
+#ifdef LA_SEGMENTS_OVERRIDE
+    if (mf) {  // tuning builds only: fixed segment count per slice
+        Segments g;
+        g.chunk = chunk;
+        g.n_chunks = (sh.N + chunk - 1) / chunk;
+        int want = LA_SEGMENTS_OVERRIDE < g.n_chunks ? LA_SEGMENTS_OVERRIDE : g.n_chunks;
+        g.seg_chunks = (g.n_chunks + want - 1) / want;
+        g.P = (g.n_chunks + g.seg_chunks - 1) / g.seg_chunks;
+        return g;
+    }
+#endif
     return mf ? plan_segments(sh, chunk, 1, 1) : plan_segments(sh, chunk, generic_columns(sh), 1);
 }
 

@@ -260,17 +260,25 @@ __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz
     const float *in = isS ? S_in : z_in;
     float *out = isS ? S_out : z_out;
     float acc = in ? in[(size_t)bh * n + idx] : 0.f;
-    if (total_to_slot0) {
-        acc = 0.f;
-        for (int s = 0; s < P; ++s) acc += slots[(size_t)s * n];
-        slots[0] = acc;
-    } else {
-        for (int s = 0; s < P; ++s) {
-            float d = slots[(size_t)s * n];
-            slots[(size_t)s * n] = acc;
-            acc += d;
+    // batches of loads in flight, then the ordered running sum
+    constexpr int kB = 8;
+    if (total_to_slot0) acc = 0.f;
+    for (int s0 = 0; s0 < P; s0 += kB) {
+        float d[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) d[b] = s0 + b < P ? slots[(size_t)(s0 + b) * n] : 0.f;
+        if (total_to_slot0) {
+#pragma unroll
+            for (int b = 0; b < kB; ++b) acc += d[b];
+        } else {
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                if (s0 + b < P) slots[(size_t)(s0 + b) * n] = acc;
+                acc += d[b];
+            }
         }
     }
+    if (total_to_slot0) slots[0] = acc;
     if (out) out[(size_t)bh * n + idx] = acc;
 }
 

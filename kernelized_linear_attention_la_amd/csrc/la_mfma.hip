@@ -14,18 +14,21 @@
 //
 // All products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  For
 // that instruction lane l supplies A[l%16][k-slots 8(l/16)..8(l/16)+7],
-// B[k-slots][l%16] and receives D[4(l/16)+e][l%16], e = 0..3.  Every LDS
-// tile is stored pre-swizzled as the exact 16 bytes a lane feeds to the
-// instruction, so each operand fetch is one conflict-free 128-bit LDS read.
-// Contractions over tokens use the slot order
-//     slot 8g+e  <->  token 16*(e/4) + 4g + (e%4)   inside each 32-token block,
-// which is the order in which a lane already holds the scores of two
-// consecutive 16x16 P^T accumulator tiles: P converts to an A operand in
-// registers, without a trip through LDS.
+// B[k-slots][l%16] and receives D[4(l/16)+e][l%16], e = 0..3.
 //
-// The state S_aug (d' x (d_v+16), fp32) lives in the accumulators of the
-// waves that own its 16-row feature blocks for the whole segment; a bf16
-// copy in LDS feeds the next chunk's phi(Q) S read.
+// phi(K_c) and V_aug sit in LDS token-major, exactly as they arrive from HBM
+// (16-byte row writes).  Products that contract over features read rows with
+// 128-bit loads; products that contract over tokens (P V and the state
+// update) read their operands with ds_read_b64_tr_b16, which hands each lane
+// a column slice of four token rows, so no transposed copy is ever written.
+// Token k-slots follow the order
+//     slot 8g+e  <->  token 16*(e/4) + 4g + (e%4)   inside each 32-token block,
+// the order in which a lane already holds the scores of two consecutive
+// 16x16 P^T accumulator tiles: P becomes an A operand in registers.
+//
+// The fp32 state S_aug (d' x (d_v+16)) lives in the accumulators of the waves
+// that own its 16-row feature blocks for the whole segment; a pre-swizzled
+// bf16 image in LDS feeds the next chunk's phi(Q) S read.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -34,11 +37,14 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 union Op8 {
     bf16x8_t v;
     uint4 u;
     uint2 q[2];
+    uint32_t u32[4];
     uint16_t h[8];
 };
 
@@ -52,46 +58,96 @@ __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
     return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
 
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-    return make_uint2(pack_bf16x2(f32_to_bf16(a), f32_to_bf16(b)), pack_bf16x2(f32_to_bf16(c), f32_to_bf16(d)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// slot (0..31) of index x (0..31) inside a 32-block, for the token order above
-__device__ __forceinline__ int slot_of(int x) { return 8 * ((x >> 2) & 3) + 4 * (x >> 4) + (x & 3); }
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) { return make_uint2(cvt2(a, b), cvt2(c, d)); }
+
+__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ELU+1 ("Linear Attention", feature-map table): max(x, 0) + exp(min(x, 0)),
+// which is x + 1 for x > 0 and exp(x) otherwise; hardware exp2 (~1 ulp).
+__device__ __forceinline__ float elu1_hw(float x) {
+    return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896341f);
+}
+
+// ELU+1 of eight packed bf16 values, rounded back to packed bf16
+__device__ __forceinline__ uint4 elu1_bf16x8(uint4 x) {
+    uint4 r;
+    r.x = cvt2(elu1_hw(lo_bf16(x.x)), elu1_hw(hi_bf16(x.x)));
+    r.y = cvt2(elu1_hw(lo_bf16(x.y)), elu1_hw(hi_bf16(x.y)));
+    r.z = cvt2(elu1_hw(lo_bf16(x.z)), elu1_hw(hi_bf16(x.z)));
+    r.w = cvt2(elu1_hw(lo_bf16(x.w)), elu1_hw(hi_bf16(x.w)));
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// LDS transpose read: within each 16-lane group, lane i receives element i%4
+// of the 8-byte fragments addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ uint2 tr_read(const uint16_t *p) {
+    i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Operand whose k-slots run over the 32 tokens of block kt (slot order above)
+// and whose 16 rows/columns are the columns cb..cb+15 of a token-major LDS
+// array with row stride R: lane i + 16g receives arr[token(g, s)][cb + i].
+template <int R>
+__device__ __forceinline__ Op8 token_operand(const uint16_t *arr, int kt, int cb, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const uint16_t *p = arr + (32 * kt + 4 * g + (j >> 2)) * R + cb + 4 * (j & 3);
+    Op8 o;
+    o.q[0] = tr_read(p);
+    o.q[1] = tr_read(p + 16 * R);
+    return o;
+}
 
 template <int DK, int DV, int C, int PHI>
 struct Cfg {
+    static constexpr bool F = PHI == kFavor;
     static constexpr int NW = C / 16;            // waves
     static constexpr int THREADS = 64 * NW;
-    static constexpr int DP = PHI == kFavor ? 256 : DK;  // feature dimension
-    static constexpr int M = PHI == kFavor ? 256 : 0;
+    static constexpr int DP = F ? 256 : DK;      // feature dimension
+    static constexpr int M = F ? 256 : 0;
     static constexpr int NJ = DV / 16 + 1;       // value column blocks incl. the normaliser block
+    static constexpr int DVA = DV + 16;
     static constexpr int KBT = C / 32;           // 32-token k-blocks per chunk
     static constexpr int KBF = DP / 32;          // 32-feature k-blocks
-    static constexpr int KBD = DK / 32;          // 32-wide k-blocks of the raw input (FAVOR projection)
+    static constexpr int KBD = DK / 32;          // 32-wide k-blocks of the raw input (FAVOR+ projection)
     static constexpr int FB = DP / 16;           // 16-row feature blocks of the state
     static constexpr int FBW = (FB + NW - 1) / NW;  // feature blocks owned per wave
-    // FAVOR+ feature slots follow the token order (they come out of
-    // accumulator tiles); ELU+1 features keep natural order (16-byte loads).
-    static constexpr bool FEAT_PI = PHI == kFavor;
+    // LDS row strides (bf16 elements).  phi(K): 8 extra elements keep the
+    // 16-row 128-bit reads conflict free.  V_aug: a stride of 16 mod 128
+    // elements keeps the transpose reads of 8 consecutive rows conflict free
+    // (FAVOR+ takes the short stride to stay inside 160 KB).
+    static constexpr int RK = DP + 8;
+    static constexpr int RV = F ? DVA + 8 : ((DVA + 111) / 128) * 128 + 16;
+    static constexpr int RO = DV + 8;
+    // FAVOR+ feature slots follow the accumulator order of the projection
+    // tiles; ELU+1 features keep their natural order.
+    static constexpr bool FEAT_PI = F;
 };
 
-// LDS image, every entry one lane's 16-byte operand.
 template <int DK, int DV, int C, int PHI>
 struct Smem {
     using G = Cfg<DK, DV, C, PHI>;
-    static constexpr bool F = PHI == kFavor;
-    uint4 KA[C / 16][G::KBF][64];                       // phi(K) rows: A operand of P^T
-    uint4 KTA[F ? 1 : G::FB][F ? 1 : G::KBT][F ? 1 : 64];  // phi(K)^T: A operand of the state update (ELU+1)
-    uint4 VTB[G::NJ][G::KBT][64];                       // V_aug: B operand of P V and of the state update
-    uint4 STB[G::NJ][G::KBF][64];                       // bf16 S_aug: B operand of phi(Q) S
-    uint4 WA[F ? 2 : 1][F ? G::M / 16 : 1][F ? G::KBD : 1][F ? 64 : 1];  // FAVOR+ W rows, bf16 hi and lo parts
-    uint4 XA[F ? C / 16 : 1][F ? G::KBD : 1][F ? 64 : 1];     // FAVOR+ raw K rows (bf16)
-    float ksq[F ? C : 1];                               // FAVOR+ |k_t|^2
+    static constexpr bool F = G::F;
+    uint16_t K[C * G::RK];              // phi(K_c), token-major
+    uint16_t V[C * G::RV];              // V_aug, token-major
+    uint4 STB[G::NJ][G::KBF][64];       // bf16 S_aug: B operand of phi(Q) S
+    uint16_t O[G::NW][16 * G::RO];      // per-wave output staging for 16-byte stores
+    uint4 WA[F ? 2 : 1][F ? G::M / 16 : 1][F ? G::KBD : 1][F ? 64 : 1];  // FAVOR+ W rows, bf16 hi / lo
 };
 
-// Map an fp32 state row block (16 features) x column block to the B-operand
-// image of S_aug: lane l holds S[16fb + 4g + e][16nb + l%16], e = 0..3.
+// Store a 16x16 fp32 state tile (lane l holds S[16fb + 4g + e][16nb + l%16])
+// into the bf16 B-operand image of S_aug.
 template <typename G>
 __device__ __forceinline__ void put_state_block(uint4 (*STB)[G::KBF][64], int fb, int nb, int lane, f32x4 s) {
     const int g = lane >> 4, c = lane & 15;
@@ -104,18 +160,32 @@ __device__ __forceinline__ void put_state_block(uint4 (*STB)[G::KBF][64], int fb
     }
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (vmcnt(0)), which
+// would drain the next chunk's prefetch at each barrier; the cross-wave
+// hand-offs in these kernels go through LDS alone.
+__device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int DK, int DV, int C, int PHI, int MODE>
 __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     using G = Cfg<DK, DV, C, PHI>;
     using T = uint16_t;
     __shared__ Smem<DK, DV, C, PHI> sm;
     constexpr int NW = G::NW, NJ = G::NJ, KBT = G::KBT, KBF = G::KBF, FB = G::FB, FBW = G::FBW;
+    constexpr int RK = G::RK, RV = G::RV, RO = G::RO;
     constexpr bool DO_OUT = MODE != kModeState;
     constexpr bool DO_STATE = MODE != kModeRead;
     constexpr bool DO_INTRA = MODE == kModeCausal;
+    constexpr bool NEED_K = MODE != kModeRead;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform across the wave
     const int g = lane >> 4, c16 = lane & 15;
 
     const Segments sg = a.sg;
@@ -135,7 +205,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // inputs are exact in bf16, so x . w_r = x . hi_r + x . lo_r is accurate to
     // about 2^-16 relative, where a single bf16 W would shift every exponent
     // of the feature map by ~2^-9 |w_r| |x|.
-    if constexpr (PHI == kFavor) {
+    if constexpr (G::F) {
         for (int u = tid; u < G::M * DK / 8; u += G::THREADS) {
             const int r = u / (DK / 8), d8 = u % (DK / 8);
             const float *src = a.sh.W + (size_t)r * DK + 8 * d8;
@@ -144,9 +214,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
             Op8 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                hi.h[e] = f32_to_bf16(wv[e]);
-                lo.h[e] = f32_to_bf16(wv[e] - bf16_to_f32(hi.h[e]));
+            for (int e = 0; e < 8; e += 2) {
+                const uint32_t h2 = cvt2(wv[e], wv[e + 1]);
+                hi.u32[e / 2] = h2;
+                lo.u32[e / 2] = cvt2(wv[e] - lo_bf16(h2), wv[e + 1] - hi_bf16(h2));
             }
             const int l = (r & 15) + 16 * (d8 & 3);
             sm.WA[0][r >> 4][d8 >> 2][l] = hi.u;
@@ -177,123 +248,146 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             }
         }
     }
-    // normaliser block of V_aug: column d_v is 1 for every token (fixed up
-    // per chunk for tokens past the end), the other 15 columns are 0
-    if constexpr (DO_OUT || DO_STATE) {
-        for (int u = tid; u < KBT * 64; u += G::THREADS) {
-            const int l = u & 63;
-            const uint32_t one2 = (l & 15) == 0 ? 0x3f803f80u : 0u;
-            sm.VTB[NJ - 1][u >> 6][l] = make_uint4(one2, one2, one2, one2);
+    // normaliser block of V_aug: column d_v is 1 for every token, the other
+    // 15 columns 0.  Tokens past the end of the sequence have phi(k) = 0, so
+    // their 1 contributes nothing.
+    if constexpr (NEED_K) {
+        for (int u = tid; u < C * 2; u += G::THREADS) {
+            const int t = u >> 1, half = u & 1;
+            const uint32_t first = half == 0 ? 0x3f80u : 0u;
+            *reinterpret_cast<uint4 *>(&sm.V[t * RV + DV + 8 * half]) = make_uint4(first, 0, 0, 0);
         }
     }
+    block_sync_lds();
 
-    const float inv_sqrt_m = PHI == kFavor ? 1.0f / 16.0f : 1.0f;  // m = 256
-    __syncthreads();
+    const float inv_sqrt_m = G::F ? 1.0f / 16.0f : 1.0f;  // m = 256
 
+    // ---- register prefetch of one chunk: K (ELU+1) and V rows in 8-column
+    // pieces, plus this wave's query rows (and, for FAVOR+, its key rows).
+    // Chunk c+1 is fetched right after chunk c is staged, so its loads are in
+    // flight during chunk c's matrix work.
+    constexpr int UK = (NEED_K && !G::F) ? C * DK / 8 : 0;
+    constexpr int UV = NEED_K ? C * DV / 8 : 0;
+    constexpr int KBQ = G::F ? G::KBD : KBF;  // 16-byte query pieces per lane
+    Op8 praw[(UK + UV) / G::THREADS > 0 ? (UK + UV) / G::THREADS : 1];
+    Op8 pq[KBQ];
+    Op8 pk[G::F ? G::KBD : 1];
+    const int row = 16 * w + c16;  // this lane's query (and FAVOR+ key) row inside a chunk
+
+    static_assert(UK % G::THREADS == 0 && UV % G::THREADS == 0, "units must tile the workgroup");
+    constexpr int UKT = UK / G::THREADS, UVT = UV / G::THREADS;  // K and V pieces per thread
+
+    // Piece i of a thread is row t = piece / W8, columns 8 * (piece % W8).
+    // A whole chunk inside the sequence (the common case) takes the path
+    // without per-row guards; the branch is uniform across the workgroup.
+    auto fetch = [&](int cc) {
+        const int tt0 = cc * C;
+        const bool full = tt0 + C <= N;
+        const bool rv = tt0 + row < N;
+        if (full) {
+#pragma unroll
+            for (int i = 0; i < UKT; ++i) {
+                const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
+                praw[i].u = *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8);
+            }
+#pragma unroll
+            for (int i = 0; i < UVT; ++i) {
+                const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
+                praw[UKT + i].u = *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < UKT; ++i) {
+                const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
+                praw[i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8)
+                                        : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < UVT; ++i) {
+                const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
+                praw[UKT + i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8)
+                                              : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if constexpr (DO_OUT) {
+            const T *qrow = Qs + (size_t)(tt0 + row) * DK + 8 * g;
+            if (full) {
+#pragma unroll
+                for (int kb = 0; kb < KBQ; ++kb) pq[kb].u = *reinterpret_cast<const uint4 *>(qrow + 32 * kb);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KBQ; ++kb)
+                    pq[kb].u = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kb) : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if constexpr (G::F && NEED_K) {
+            const T *krow = Ks + (size_t)(tt0 + row) * DK + 8 * g;
+            if (full) {
+#pragma unroll
+                for (int kb = 0; kb < G::KBD; ++kb) pk[kb].u = *reinterpret_cast<const uint4 *>(krow + 32 * kb);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < G::KBD; ++kb)
+                    pk[kb].u = rv ? *reinterpret_cast<const uint4 *>(krow + 32 * kb) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- write one prefetched chunk into LDS (token-major rows)
+    auto stage = [&](int tt0) {
+        const bool full = tt0 + C <= N;
+#pragma unroll
+        for (int i = 0; i < UKT; ++i) {
+            // ELU+1 on the way in; tokens past the end get phi = 0, not phi(0) = 1
+            const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
+            uint4 ph = elu1_bf16x8(praw[i].u);
+            if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
+        }
+#pragma unroll
+        for (int i = 0; i < UVT; ++i) {
+            const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
+            *reinterpret_cast<uint4 *>(&sm.V[t * RV + 8 * c8]) = praw[UKT + i].u;
+        }
+    };
+
+    fetch(c_begin);
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
-        // ---------------- stage K_c, V_c into LDS
-        if constexpr (MODE != kModeRead) {
-            constexpr int UK = (C / 4) * (DK / 8);  // 4-token x 8-column units
-            constexpr int UV = (C / 4) * (DV / 8);
-            for (int u = tid; u < UK + UV; u += G::THREADS) {
-                const bool isK = u < UK;
-                const int uu = isK ? u : u - UK;
-                const int W8 = isK ? DK / 8 : DV / 8;
-                const int t4 = 4 * (uu / W8), c8 = uu % W8;
-                const int D = isK ? DK : DV;
-                const T *src = isK ? Ks : Vs;
-                Op8 raw[4];
-                bool valid[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    valid[r] = t0 + t4 + r < N;
-                    raw[r].u = valid[r] ? *reinterpret_cast<const uint4 *>(src + (size_t)(t0 + t4 + r) * D + 8 * c8)
-                                        : make_uint4(0, 0, 0, 0);
-                }
-                const int x = t4 & 31;                       // token offset inside its 32-block
-                const int gt = (x >> 2) & 3, ht = x >> 4;    // slot group and half
-                if (isK) {
-                    if constexpr (PHI == kElu1) {
-                        Op8 ph[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                ph[r].h[e] = valid[r] ? f32_to_bf16(elu1_fast(bf16_to_f32(raw[r].h[e]))) : 0;
-                        if (DO_INTRA) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = t4 + r;
-                                sm.KA[j >> 4][c8 >> 2][(j & 15) + 16 * (c8 & 3)] = ph[r].u;
-                            }
-                        }
-                        if (DO_STATE) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int f = 8 * c8 + e;
-                                uint2 v = make_uint2(pack_bf16x2(ph[0].h[e], ph[1].h[e]),
-                                                     pack_bf16x2(ph[2].h[e], ph[3].h[e]));
-                                reinterpret_cast<uint2 *>(&sm.KTA[f >> 4][t4 >> 5][(f & 15) + 16 * gt])[ht] = v;
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = t4 + r;
-                            sm.XA[j >> 4][c8 >> 2][(j & 15) + 16 * (c8 & 3)] = raw[r].u;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 8 * c8 + e;
-                        uint2 v = make_uint2(pack_bf16x2(raw[0].h[e], raw[1].h[e]), pack_bf16x2(raw[2].h[e], raw[3].h[e]));
-                        reinterpret_cast<uint2 *>(&sm.VTB[j >> 4][t4 >> 5][(j & 15) + 16 * gt])[ht] = v;
-                    }
-                    if (c8 == 0) {  // normaliser column: 1 for valid tokens, 0 past the end
-                        uint2 v = make_uint2(pack_bf16x2(valid[0] ? 0x3f80 : 0, valid[1] ? 0x3f80 : 0),
-                                             pack_bf16x2(valid[2] ? 0x3f80 : 0, valid[3] ? 0x3f80 : 0));
-                        reinterpret_cast<uint2 *>(&sm.VTB[NJ - 1][t4 >> 5][16 * gt])[ht] = v;
-                    }
-                }
-            }
-        }
-        // ---------------- this wave's query rows (ELU+1: straight from HBM)
-        const int row = 16 * w + c16;             // query row inside the chunk
-        const bool qvalid = t0 + row < N;
+        stage(t0);
+        const bool rvalid = t0 + row < N;  // FAVOR+: key row of this lane exists
         Op8 phq[KBF];
-        if constexpr (DO_OUT && PHI == kElu1) {
+        Op8 xq[G::F ? G::KBD : 1], xk[G::F ? G::KBD : 1];
+        if constexpr (DO_OUT && !G::F) {
 #pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) {
-                Op8 raw;
-                raw.u = qvalid ? *reinterpret_cast<const uint4 *>(Qs + (size_t)(t0 + row) * DK + 32 * kb + 8 * g)
-                               : make_uint4(0, 0, 0, 0);
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = elu1_bf16x8(pq[kb].u);  // rows past the end are not stored
+        }
+        if constexpr (G::F) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) phq[kb].h[e] = qvalid ? f32_to_bf16(elu1_fast(bf16_to_f32(raw.h[e]))) : 0;
+            for (int kb = 0; kb < G::KBD; ++kb) {
+                xq[kb] = pq[kb];
+                xk[kb] = pk[kb];
             }
         }
-        __syncthreads();
+        block_sync_lds();
+        if (c + 1 < c_end) fetch(c + 1);
 
-        // ---------------- FAVOR+: feature maps through projections on the matrix cores
-        Op8 kta[FBW][KBT];  // this wave's phi(K)^T operands (FAVOR+)
-        if constexpr (PHI == kFavor) {
-            if constexpr (DO_OUT) {
-                // query rows: U^T = W Q^T for this wave's 16 rows, |q|^2 from the operand lanes
-                Op8 xq[G::KBD];
+        // ---------------- FAVOR+: feature maps through projections on the matrix cores.
+        // U^T = W X^T for this wave's 16 rows: accumulator lane (4g+e, c16)
+        // holds feature 16rb + 4g + e of row c16, which is the operand order.
+        if constexpr (G::F) {
+            auto project = [&](const Op8 *x, auto &&emit) {
                 float sq = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < G::KBD; ++kb) {
-                    xq[kb].u = qvalid ? *reinterpret_cast<const uint4 *>(Qs + (size_t)(t0 + row) * DK + 32 * kb + 8 * g)
-                                      : make_uint4(0, 0, 0, 0);
+                for (int kb = 0; kb < G::KBD; ++kb)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float x = bf16_to_f32(xq[kb].h[e]);
-                        sq += x * x;
+                    for (int e = 0; e < 4; ++e) {
+                        const float v0 = lo_bf16(x[kb].u32[e]), v1 = hi_bf16(x[kb].u32[e]);
+                        sq += v0 * v0 + v1 * v1;
                     }
-                }
                 sq += __shfl_xor(sq, 16, 64);
                 sq += __shfl_xor(sq, 32, 64);
+                const float shift = 0.5f * sq;
 #pragma unroll
                 for (int kf = 0; kf < KBF; ++kf) {
                     f32x4 u0 = zero4(), u1 = zero4();
@@ -304,94 +398,37 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                             Op8 w0, w1;
                             w0.u = sm.WA[part][2 * kf][kb][lane];
                             w1.u = sm.WA[part][2 * kf + 1][kb][lane];
-                            u0 = mfma(w0, xq[kb], u0);
-                            u1 = mfma(w1, xq[kb], u1);
+                            u0 = mfma(w0, x[kb], u0);
+                            u1 = mfma(w1, x[kb], u1);
                         }
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        phq[kf].h[e] = f32_to_bf16(__expf(u0[e] - 0.5f * sq) * inv_sqrt_m);
-                        phq[kf].h[4 + e] = f32_to_bf16(__expf(u1[e] - 0.5f * sq) * inv_sqrt_m);
-                    }
+                    emit(kf, u0, u1, shift);
                 }
+            };
+            if constexpr (DO_OUT) {
+                project(xq, [&](int kf, f32x4 u0, f32x4 u1, float shift) {
+                    phq[kf].q[0] = pack4(fast_exp(u0[0] - shift) * inv_sqrt_m, fast_exp(u0[1] - shift) * inv_sqrt_m,
+                                         fast_exp(u0[2] - shift) * inv_sqrt_m, fast_exp(u0[3] - shift) * inv_sqrt_m);
+                    phq[kf].q[1] = pack4(fast_exp(u1[0] - shift) * inv_sqrt_m, fast_exp(u1[1] - shift) * inv_sqrt_m,
+                                         fast_exp(u1[2] - shift) * inv_sqrt_m, fast_exp(u1[3] - shift) * inv_sqrt_m);
+                });
             }
-            if constexpr (MODE != kModeRead) {
-                // key rows of token block w: U^T = W K^T -> A operand of P^T; and |k|^2
-                const int tb = w;
-                Op8 xk[G::KBD];
-                float sq = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < G::KBD; ++kb) {
-                    xk[kb].u = sm.XA[tb][kb][lane];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float x = bf16_to_f32(xk[kb].h[e]);
-                        sq += x * x;
+            if constexpr (NEED_K) {
+                // keys of token block w -> phi(K) rows 16w.., features in natural order
+                project(xk, [&](int kf, f32x4 u0, f32x4 u1, float shift) {
+                    uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+                    if (rvalid) {
+                        lo = pack4(fast_exp(u0[0] - shift) * inv_sqrt_m, fast_exp(u0[1] - shift) * inv_sqrt_m,
+                                   fast_exp(u0[2] - shift) * inv_sqrt_m, fast_exp(u0[3] - shift) * inv_sqrt_m);
+                        hi = pack4(fast_exp(u1[0] - shift) * inv_sqrt_m, fast_exp(u1[1] - shift) * inv_sqrt_m,
+                                   fast_exp(u1[2] - shift) * inv_sqrt_m, fast_exp(u1[3] - shift) * inv_sqrt_m);
                     }
-                }
-                sq += __shfl_xor(sq, 16, 64);
-                sq += __shfl_xor(sq, 32, 64);
-                const bool kvalid = t0 + 16 * tb + c16 < N;
-                if (g == 0) sm.ksq[16 * tb + c16] = sq;
-                if constexpr (DO_INTRA) {
-#pragma unroll
-                    for (int kf = 0; kf < KBF; ++kf) {
-                        f32x4 u0 = zero4(), u1 = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < G::KBD; ++kb) {
-#pragma unroll
-                            for (int part = 0; part < 2; ++part) {
-                                Op8 w0, w1;
-                                w0.u = sm.WA[part][2 * kf][kb][lane];
-                                w1.u = sm.WA[part][2 * kf + 1][kb][lane];
-                                u0 = mfma(w0, xk[kb], u0);
-                                u1 = mfma(w1, xk[kb], u1);
-                            }
-                        }
-                        Op8 o;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            o.h[e] = kvalid ? f32_to_bf16(__expf(u0[e] - 0.5f * sq) * inv_sqrt_m) : 0;
-                            o.h[4 + e] = kvalid ? f32_to_bf16(__expf(u1[e] - 0.5f * sq) * inv_sqrt_m) : 0;
-                        }
-                        sm.KA[tb][kf][lane] = o.u;
-                    }
-                }
+                    uint16_t *dst = &sm.K[row * RK + 32 * kf + 4 * g];
+                    *reinterpret_cast<uint2 *>(dst) = lo;
+                    *reinterpret_cast<uint2 *>(dst + 16) = hi;
+                });
             }
-            __syncthreads();
-            if constexpr (DO_STATE) {
-                // phi(K)^T for the feature blocks this wave owns: U = K W^T,
-                // accumulator rows are tokens in slot order -> A operands
-#pragma unroll
-                for (int q = 0; q < FBW; ++q) {
-                    const int fb = w + NW * q;
-#pragma unroll
-                    for (int kt = 0; kt < KBT; ++kt) {
-                        f32x4 u0 = zero4(), u1 = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < G::KBD; ++kb) {
-                            Op8 x0, x1;
-                            x0.u = sm.XA[2 * kt][kb][lane];
-                            x1.u = sm.XA[2 * kt + 1][kb][lane];
-#pragma unroll
-                            for (int part = 0; part < 2; ++part) {
-                                Op8 wb;
-                                wb.u = sm.WA[part][fb][kb][lane];
-                                u0 = mfma(x0, wb, u0);
-                                u1 = mfma(x1, wb, u1);
-                            }
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int ta = 32 * kt + 4 * g + e, tb2 = ta + 16;
-                            kta[q][kt].h[e] =
-                                t0 + ta < N ? f32_to_bf16(__expf(u0[e] - 0.5f * sm.ksq[ta]) * inv_sqrt_m) : 0;
-                            kta[q][kt].h[4 + e] =
-                                t0 + tb2 < N ? f32_to_bf16(__expf(u1[e] - 0.5f * sm.ksq[tb2]) * inv_sqrt_m) : 0;
-                        }
-                    }
-                }
-            }
+            block_sync_lds();
         }
 
         // ---------------- outputs of this wave's 16 query rows
@@ -410,10 +447,16 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                             const int jb = 2 * kt + h;
                             p[h] = zero4();
                             if (jb <= w) {
+                                const uint16_t *krow = &sm.K[(16 * jb + c16) * RK];
 #pragma unroll
                                 for (int kf = 0; kf < KBF; ++kf) {
                                     Op8 ka;
-                                    ka.u = sm.KA[jb][kf][lane];
+                                    if constexpr (G::FEAT_PI) {
+                                        ka.q[0] = *reinterpret_cast<const uint2 *>(krow + 32 * kf + 4 * g);
+                                        ka.q[1] = *reinterpret_cast<const uint2 *>(krow + 32 * kf + 16 + 4 * g);
+                                    } else {
+                                        ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
+                                    }
                                     p[h] = mfma(ka, phq[kf], p[h]);
                                 }
                                 if (jb == w) {  // causal mask on the diagonal block: key 4g+e <= query c16
@@ -427,11 +470,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         pa.q[0] = pack4(p[0][0], p[0][1], p[0][2], p[0][3]);
                         pa.q[1] = pack4(p[1][0], p[1][1], p[1][2], p[1][3]);
 #pragma unroll
-                        for (int nb = 0; nb < NJ; ++nb) {
-                            Op8 vb;
-                            vb.u = sm.VTB[nb][kt][lane];
-                            acc[nb] = mfma(pa, vb, acc[nb]);
-                        }
+                        for (int nb = 0; nb < NJ; ++nb)
+                            acc[nb] = mfma(pa, token_operand<RV>(sm.V, kt, 16 * nb, lane), acc[nb]);
                     }
                 }
             }
@@ -445,18 +485,29 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     acc[nb] = mfma(phq[kf], sb, acc[nb]);
                 }
             }
-            // epilogue: divide by the normaliser column, round, store
+            // epilogue: divide by the normaliser column, round, stage, store 16 B per lane
             float rden[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rden[e] = 1.0f / __shfl(acc[NJ - 1][e], lane & 48, 64);
+            for (int e = 0; e < 4; ++e) rden[e] = __builtin_amdgcn_rcpf(__shfl(acc[NJ - 1][e], lane & 48, 64));
+            uint16_t *so = sm.O[w];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int orow = 16 * w + 4 * g + e;
-                if (t0 + orow < N) {
-                    T *dst = Os + (size_t)(t0 + orow) * DV + c16;
+            for (int nb = 0; nb < NJ - 1; ++nb)
 #pragma unroll
-                    for (int nb = 0; nb < NJ - 1; ++nb) dst[16 * nb] = f32_to_bf16(acc[nb][e] * rden[e]);
+                for (int e = 0; e < 4; e += 2) {
+                    const uint32_t two = cvt2(acc[nb][e] * rden[e], acc[nb][e + 1] * rden[e + 1]);
+                    so[(4 * g + e) * RO + 16 * nb + c16] = static_cast<uint16_t>(two);
+                    so[(4 * g + e + 1) * RO + 16 * nb + c16] = static_cast<uint16_t>(two >> 16);
                 }
+            wave_lds_sync();
+            constexpr int PIECES = 16 * DV / 8;  // 16-byte pieces of the wave's 16 rows
+            const bool full = t0 + C <= N;
+#pragma unroll
+            for (int it = 0; it < PIECES / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int r = idx / (DV / 8), c8 = idx % (DV / 8);
+                const uint4 val = *reinterpret_cast<const uint4 *>(&so[r * RO + 8 * c8]);
+                T *dst = Os + (size_t)(t0 + 16 * w + r) * DV + 8 * c8;
+                if (full || t0 + 16 * w + r < N) *reinterpret_cast<uint4 *>(dst) = val;
             }
         }
 
@@ -468,21 +519,16 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 if (fb < FB) {
 #pragma unroll
                     for (int kt = 0; kt < KBT; ++kt) {
-                        Op8 ka;
-                        if constexpr (PHI == kFavor) ka = kta[q][kt];
-                        else ka.u = sm.KTA[fb][kt][lane];
+                        const Op8 ka = token_operand<RK>(sm.K, kt, 16 * fb, lane);
 #pragma unroll
-                        for (int nb = 0; nb < NJ; ++nb) {
-                            Op8 vb;
-                            vb.u = sm.VTB[nb][kt][lane];
-                            S[q][nb] = mfma(ka, vb, S[q][nb]);
-                        }
+                        for (int nb = 0; nb < NJ; ++nb)
+                            S[q][nb] = mfma(ka, token_operand<RV>(sm.V, kt, 16 * nb, lane), S[q][nb]);
                     }
                 }
             }
         }
+        block_sync_lds();  // every wave is done with this chunk's tiles and the old state image
         if constexpr (MODE == kModeCausal) {
-            __syncthreads();  // every wave is done reading this chunk's tiles and the old state image
 #pragma unroll
             for (int q = 0; q < FBW; ++q) {
                 const int fb = w + NW * q;
@@ -491,10 +537,6 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     for (int nb = 0; nb < NJ; ++nb) put_state_block<G>(sm.STB, fb, nb, lane, S[q][nb]);
                 }
             }
-        } else if constexpr (MODE == kModeState) {
-            __syncthreads();  // tiles are rewritten by the next chunk
-        } else {
-            __syncthreads();
         }
     }
 

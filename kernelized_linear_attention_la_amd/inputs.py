@@ -82,21 +82,21 @@ def _slice_draw(key, n):
     return rng.standard_normal(n)
 
 
-def _fill_slices(args):
-    """Worker body: draw a run of slices into a shared fp32 buffer."""
-    shm_name, shape, key_prefix, scale, lo, hi, per = args
-    from multiprocessing import shared_memory
+def _fill_slices(shm_name, shape, key_prefix, scale, lo, hi):
+    """Worker body: draw slices [lo, hi) into a shared fp32 buffer."""
+    from multiprocessing import resource_tracker, shared_memory
     shm = shared_memory.SharedMemory(name=shm_name)
+    # the creating process owns the segment; this worker must not unlink it at exit
+    resource_tracker.unregister(shm._name, "shared_memory")
     try:
-        buf = np.ndarray(shape, dtype=np.float32, buffer=shm.buf)
-        flat = buf.reshape(-1, per)
+        per = int(np.prod(shape[2:]))
+        flat = np.ndarray((shape[0] * shape[1], per), dtype=np.float32, buffer=shm.buf)
         H = shape[1]
         for s in range(lo, hi):
             b, h = divmod(s, H)
             flat[s] = (_slice_draw(tuple(key_prefix) + (b, h), per) * scale).astype(np.float32)
     finally:
         shm.close()
-    return hi - lo
 
 
 def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: str,
@@ -121,18 +121,27 @@ def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: st
         out *= scale
         return _round_to(out.reshape(shape), dtype)
 
-    import multiprocessing as mp
+    # worker processes run this module directly (python -m ...), so they never
+    # re-import the caller's main script
+    import json
+    import subprocess
+    import sys
     from multiprocessing import shared_memory
     shm = shared_memory.SharedMemory(create=True, size=total * 4)
     try:
-        ctx = mp.get_context("spawn")
         nsl = B * H
-        step = (nsl + workers * 4 - 1) // (workers * 4)
-        jobs = [(shm.name, tuple(shape), key_prefix, scale, lo, min(nsl, lo + step), per)
-                for lo in range(0, nsl, step)]
-        with ctx.Pool(workers) as pool:
-            done = sum(pool.map(_fill_slices, jobs))
-        assert done == nsl
+        step = (nsl + workers - 1) // workers
+        procs = []
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""),
+                   OMP_NUM_THREADS="1")
+        for lo in range(0, nsl, step):
+            job = json.dumps([shm.name, list(shape), list(key_prefix), scale, lo, min(nsl, lo + step)])
+            procs.append(subprocess.Popen([sys.executable, "-m", "kernelized_linear_attention_la_amd.inputs", job],
+                                          env=env))
+        codes = [p.wait() for p in procs]
+        if any(codes):
+            raise RuntimeError(f"input generator workers failed: {codes}")
         x32 = np.ndarray(tuple(shape), dtype=np.float32, buffer=shm.buf).copy()
     finally:
         shm.close()
@@ -245,3 +254,11 @@ def custom_inputs(seed: int, B, H, N, dk, dv, scale=1.0, dtype="f32", phi="elu1"
     W = orthogonal_gaussian_rows(1000 + seed, m, dk) if phi == "favor" else None
     wl = Workload(f"custom{seed}", 1000 + seed, phi, dtype, B, H, N, dk, dv, scale, 64, m=m)
     return ForwardInputs(wl, Q, K, V, W)
+
+
+if __name__ == "__main__":
+    # worker entry of normal_bhnd's process pool
+    import json
+    import sys
+    _a = json.loads(sys.argv[1])
+    _fill_slices(_a[0], tuple(_a[1]), tuple(_a[2]), _a[3], _a[4], _a[5])
