@@ -12,7 +12,11 @@
 namespace la {
 namespace {
 
-constexpr int kTargetWorkgroups = 1024;  // enough to keep every CU of the chip busy
+constexpr int kTargetWorkgroups = 1024;  // generic path: several workgroups per CU
+// MFMA path: one workgroup per CU of the 256-CU part.  Every workgroup streams
+// its segment chunk after chunk, so more segments only add state traffic and
+// shorten the stream (measured on MI355X for d = 64 / 128 and FAVOR+).
+constexpr int kMfmaWorkgroups = 256;
 constexpr size_t kAlign = 256;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -56,12 +60,13 @@ bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || c
 
 // Split each slice into P segments of whole chunks so that B*H*P*(columns)
 // workgroups fill the device.  Depends on the shape only.
-Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int min_seg_chunks) {
+Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int min_seg_chunks,
+                       int target = kTargetWorkgroups) {
     Segments g;
     g.chunk = chunk;
     g.n_chunks = (sh.N + chunk - 1) / chunk;
     const long long units = (long long)sh.BH * columns_per_slice;
-    int want = (int)((kTargetWorkgroups + units - 1) / units);
+    int want = (int)((target + units - 1) / units);
     if (want < 1) want = 1;
     int max_p = (g.n_chunks + min_seg_chunks - 1) / min_seg_chunks;
     if (want > max_p) want = max_p;
@@ -87,7 +92,7 @@ Segments causal_plan(const Shape &sh, int chunk, bool *use_mfma) {
         return g;
     }
 #endif
-    return mf ? plan_segments(sh, chunk, 1, 1) : plan_segments(sh, chunk, generic_columns(sh), 1);
+    return mf ? plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups) : plan_segments(sh, chunk, generic_columns(sh), 1);
 }
 
 constexpr int kNoncausalChunk = 64;
@@ -95,7 +100,7 @@ constexpr int kNoncausalChunk = 64;
 Segments noncausal_plan(const Shape &sh, bool *use_mfma) {
     const bool mf = mfma_supported(sh, kNoncausalChunk);
     if (use_mfma) *use_mfma = mf;
-    return mf ? plan_segments(sh, kNoncausalChunk, 1, 1)
+    return mf ? plan_segments(sh, kNoncausalChunk, 1, 1, kMfmaWorkgroups)
               : plan_segments(sh, kNoncausalChunk, generic_columns(sh), 1);
 }
 

@@ -260,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz
     const float *in = isS ? S_in : z_in;
     float *out = isS ? S_out : z_out;
     float acc = in ? in[(size_t)bh * n + idx] : 0.f;
-    // batches of loads in flight, then the ordered running sum
-    constexpr int kB = 8;
+    // up to kB loads in flight at once, then the ordered running sum
+    constexpr int kB = 32;
     if (total_to_slot0) acc = 0.f;
     for (int s0 = 0; s0 < P; s0 += kB) {
         float d[kB];

@@ -225,41 +225,6 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
     }
 
-    // ---- starting state into the owners' accumulators (+ bf16 image)
-    f32x4 S[FBW][NJ];
-    {
-        const float *Ssrc = a.st.S_src ? a.st.S_src + bh * a.st.src_slice + seg * a.st.src_seg : nullptr;
-        const float *zsrc = a.st.z_src ? a.st.z_src + bh * a.st.zsrc_slice + seg * a.st.zsrc_seg : nullptr;
-#pragma unroll
-        for (int q = 0; q < FBW; ++q) {
-            const int fb = w + NW * q;
-#pragma unroll
-            for (int nb = 0; nb < NJ; ++nb) {
-                f32x4 v = zero4();
-                if (fb < FB && Ssrc) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int f = 16 * fb + 4 * g + e, j = 16 * nb + c16;
-                        v[e] = j < DV ? Ssrc[(size_t)f * DV + j] : (j == DV ? zsrc[f] : 0.f);
-                    }
-                }
-                S[q][nb] = v;
-                if (DO_OUT && fb < FB) put_state_block<G>(sm.STB, fb, nb, lane, v);
-            }
-        }
-    }
-    // normaliser block of V_aug: column d_v is 1 for every token, the other
-    // 15 columns 0.  Tokens past the end of the sequence have phi(k) = 0, so
-    // their 1 contributes nothing.
-    if constexpr (NEED_K) {
-        for (int u = tid; u < C * 2; u += G::THREADS) {
-            const int t = u >> 1, half = u & 1;
-            const uint32_t first = half == 0 ? 0x3f80u : 0u;
-            *reinterpret_cast<uint4 *>(&sm.V[t * RV + DV + 8 * half]) = make_uint4(first, 0, 0, 0);
-        }
-    }
-    block_sync_lds();
-
     const float inv_sqrt_m = G::F ? 1.0f / 16.0f : 1.0f;  // m = 256
 
     // ---- register prefetch of one chunk: K (ELU+1) and V rows in 8-column
@@ -351,7 +316,43 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
     };
 
+    // the first chunk's loads go out before the starting state is read
     fetch(c_begin);
+    // ---- starting state into the owners' accumulators (+ bf16 image)
+    f32x4 S[FBW][NJ];
+    {
+        const float *Ssrc = a.st.S_src ? a.st.S_src + bh * a.st.src_slice + seg * a.st.src_seg : nullptr;
+        const float *zsrc = a.st.z_src ? a.st.z_src + bh * a.st.zsrc_slice + seg * a.st.zsrc_seg : nullptr;
+#pragma unroll
+        for (int q = 0; q < FBW; ++q) {
+            const int fb = w + NW * q;
+#pragma unroll
+            for (int nb = 0; nb < NJ; ++nb) {
+                f32x4 v = zero4();
+                if (fb < FB && Ssrc) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 16 * fb + 4 * g + e, j = 16 * nb + c16;
+                        v[e] = j < DV ? Ssrc[(size_t)f * DV + j] : (j == DV ? zsrc[f] : 0.f);
+                    }
+                }
+                S[q][nb] = v;
+                if (DO_OUT && fb < FB) put_state_block<G>(sm.STB, fb, nb, lane, v);
+            }
+        }
+    }
+    // normaliser block of V_aug: column d_v is 1 for every token, the other
+    // 15 columns 0.  Tokens past the end of the sequence have phi(k) = 0, so
+    // their 1 contributes nothing.
+    if constexpr (NEED_K) {
+        for (int u = tid; u < C * 2; u += G::THREADS) {
+            const int t = u >> 1, half = u & 1;
+            const uint32_t first = half == 0 ? 0x3f80u : 0u;
+            *reinterpret_cast<uint4 *>(&sm.V[t * RV + DV + 8 * half]) = make_uint4(first, 0, 0, 0);
+        }
+    }
+    block_sync_lds();
+
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         stage(t0);
