@@ -135,12 +135,71 @@ def run_cpu_baseline(wl, fi, seconds):
         oracle.causal_recurrent(wl.phi, Qf, Kf, Vf, fi.W)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds * 0.5 or reps >= 50:
+        if el >= seconds or reps >= 100000:
             break
     tokens = reps * n_slices * wl.N
     return {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"fp64 causal recurrence on {n_slices} of {BH} (b,h) slices x {wl.N} tokens, "
                       f"{reps} pass(es), {el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
+
+
+def run_cpu_baseline_decode(wl, fi, seconds):
+    """Time the fp64 oracle's decode step on a bounded sample of sequences (all heads)."""
+    import numpy as np
+    import oracle
+    from kernelized_linear_attention_la_amd import inputs
+    nthreads = oracle.num_threads()
+    n_seq = min(wl.B, 8)
+    sl = (slice(0, n_seq), slice(None))
+    # starting states from the same 1024-token prefix (not timed)
+    _, S, z = oracle.causal_recurrent(wl.phi, fi.Q.f32[sl], fi.K.f32[sl], fi.V.f32[sl], fi.W)
+    steps = []
+    for s in range(wl.decode_steps):
+        q, k, v = inputs.decode_step_inputs(wl, s)
+        steps.append((q.f32[sl][:, :, 0], k.f32[sl][:, :, 0], v.f32[sl][:, :, 0]))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q, k, v = steps[n % len(steps)]
+        _, S, z = oracle.decode_step(wl.phi, q, k, v, S, z, fi.W)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= len(steps)) or n >= 1000000:
+            break
+    return {"value": n_seq * n / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 decode steps for {n_seq} of {wl.B} sequences x {wl.H} heads, {n} steps "
+                      f"(64 seeded step inputs cycled, states from the same 1024-token prefix), {el:.1f} s on "
+                      f"{nthreads} threads of '{cpu_model()}'"}
+
+
+def kernel_symbol(wl, slot):
+    """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
+    if wl.decode_steps and slot == "decode":
+        t = "float" if wl.dtype == "f32" else "unsigned short"
+        return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}>"
+    mode = {"state": 0, "chunk": 1}[slot]
+    mfma = wl.dtype == "bf16" and (
+        (wl.phi == "elu1" and wl.dk == wl.dv and wl.dk in (64, 128) and wl.chunk in (64, 128)) or
+        (wl.phi == "favor" and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64))
+    if mfma:
+        return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {1 if wl.phi == 'favor' else 0}, {mode}>"
+    return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"
+
+
+def stored_traffic(wl, kernel):
+    """HBM bytes per launch from a committed counter summary, if the kernels are unchanged since."""
+    import glob
+    from kernelized_linear_attention_la_amd import build as hip_build
+    want = hip_build.source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
+        try:
+            with open(path) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if rec.get("workload") == wl.name and rec.get("kernel") == kernel and rec.get("source_hash") == want:
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def bench_forward(args, wl):
@@ -195,23 +254,43 @@ def bench_forward(args, wl):
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # live per-kernel timing of the dominant kernel (the chunk loop) over K steps
+    # live per-kernel timing over K steps: HIP events recorded around each
+    # kernel of the step (timing hook), inside HIP graphs like the timed loop
     hev = HipEvents(la.lib())
-    ev_pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
-    kev = la.LaKernelEvents()
-    raw_stream = ctypes.c_void_p(stream.cuda_stream)
+    slots = (la.LA_KSLOT_STATE, la.LA_KSLOT_SCAN, la.LA_KSLOT_CHUNK)
+    ev = [{sl: (hev.create(), hev.create()) for sl in slots} for _ in range(R)]
+    kevs = []
+    for i in range(R):
+        kev = la.LaKernelEvents()
+        for sl in slots:
+            kev.start[sl], kev.stop[sl] = ev[i][sl][0], ev[i][sl][1]
+        kevs.append(kev)
+    durs = {sl: [] for sl in slots}
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            kev.start[la.LA_KSLOT_CHUNK] = ev_pairs[i][0]
-            kev.stop[la.LA_KSLOT_CHUNK] = ev_pairs[i][1]
-            step(i, stream=stream, events=kev)
-    torch.cuda.synchronize()
-    durs = [hev.elapsed_ms(a, b) for a, b in ev_pairs]
-    for a, b in ev_pairs:
-        hev.destroy(a)
-        hev.destroy(b)
-    kern_ms = sum(durs) / len(durs)
+    # Launches are queued behind a short GPU sleep so the device runs them
+    # back to back, as in the graph-timed loop; each event pair then brackets
+    # exactly one kernel on the GPU timeline.
+    done = 0
+    while done < args.steps:
+        n = min(R, args.steps - done)
+        with torch.cuda.stream(stream):
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(20_000_000)
+            for i in range(n):
+                step(done + i, stream=stream, events=kevs[i])
+        torch.cuda.synchronize()
+        for i in range(n):
+            for sl in slots:
+                if kevs[i].launched[sl]:
+                    durs[sl].append(hev.elapsed_ms(*ev[i][sl]))
+        done += n
+    timing_mode = "hip events around each kernel, launches queued back to back"
+    for e in ev:
+        for a_, b_ in e.values():
+            hev.destroy(a_)
+            hev.destroy(b_)
+    avg_us = {sl: 1e3 * sum(v) / len(v) for sl, v in durs.items() if v}
+    kern_ms = avg_us[la.LA_KSLOT_CHUNK] * 1e-3
 
     tokens = wl.B * wl.H * wl.N
     value = tokens / (ms_per_step * 1e-3)
@@ -229,9 +308,17 @@ def bench_forward(args, wl):
         ach = alg_flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
-    roof["kernel"] = "chunk loop (la_forward_causal_chunked, LA_KSLOT_CHUNK)"
+    kname = kernel_symbol(wl, "chunk")
+    tb = stored_traffic(wl, kname)
+    roof["traffic"] = tb
+    roof["kernel"] = kname
     roof["kernel_avg_us"] = kern_ms * 1e3
+    roof["alg_bytes_per_launch"] = chunk_bytes
+    roof["timing"] = timing_mode
     extra = {
+        "kernel_avg_us": {name: round(avg_us[sl], 2) for name, sl in
+                          (("state", la.LA_KSLOT_STATE), ("scan", la.LA_KSLOT_SCAN), ("chunk", la.LA_KSLOT_CHUNK))
+                          if sl in avg_us},
         "step_hbm_frac": alg_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "step_mfma_frac": alg_flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12),
         "rotated_input_sets": R,
@@ -290,8 +377,10 @@ def bench_decode(args, wl):
     value = wl.B / (ms_per_step * 1e-3)  # one generated token per sequence per step
     nbytes = decode_alg_bytes(wl)
     ach = nbytes / (kern_ms * 1e-3) / 1e9
+    kname = kernel_symbol(wl, "decode")
     roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-            "traffic": None, "kernel": "decode step (la_decode_step)", "kernel_avg_us": kern_ms * 1e3}
+            "traffic": stored_traffic(wl, kname), "kernel": kname, "kernel_avg_us": kern_ms * 1e3,
+            "alg_bytes_per_launch": nbytes, "timing": "hip events around each launch"}
     extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3)}
     return value, ms_per_step, roof, extra, fi
 
@@ -325,7 +414,7 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         if wl.decode_steps:
-            cpu = None  # the oracle baseline is defined on the forward workloads
+            cpu = run_cpu_baseline_decode(wl, fi, args.cpu_seconds)
         else:
             cpu = run_cpu_baseline(wl, fi, args.cpu_seconds)
     config = {"workload": wl.name, "phi": wl.phi, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,

@@ -122,11 +122,12 @@ la_status la_forward_causal_chunked(const la_problem *p, int chunk,
  *                   sequence is split into several segments),
  *   LA_KSLOT_SCAN   exclusive prefix of those sums over segments (same case),
  *   LA_KSLOT_CHUNK  the chunk loop that writes O (always).
- * For every slot whose kernel is enqueued, the library records start[slot]
- * right before and stop[slot] right after that kernel, on the call's stream
- * (hipEventRecord).  Entries may be NULL (not recorded).  The events are
- * created, owned and queried by the caller (hipEvent_t passed as void*).
- * launched[slot] is set to 1 for each kernel enqueued, 0 otherwise.
+ * For every slot whose kernel is enqueued, the launch of that kernel records
+ * start[slot] when it begins and stop[slot] when it ends (hipExtLaunchKernel),
+ * so the pair brackets exactly that kernel.  Entries may be NULL (not
+ * recorded).  The events are created, owned and queried by the caller
+ * (hipEvent_t passed as void*).  launched[slot] is set to 1 for each kernel
+ * enqueued, 0 otherwise.
  */
 enum { LA_KSLOT_STATE = 0, LA_KSLOT_SCAN = 1, LA_KSLOT_CHUNK = 2, LA_KSLOTS = 3 };
 

@@ -63,5 +63,20 @@ def build(extra_flags=(), verbose: bool = False) -> str:
     return LIB_PATH
 
 
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the public header (identifies a kernel build)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(INCLUDE, "liblinattn.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 if __name__ == "__main__":
     build(sys.argv[1:], verbose=True)

@@ -135,23 +135,19 @@ size_t noncausal_ws(const Shape &sh) {
     return ws_layout(sh, g.P).total;
 }
 
-hipError_t launch_fwd(bool mfma, const FwdArgs &a, hipStream_t st) {
-    return mfma ? launch_mfma(a, st) : launch_generic(a, st);
+hipError_t launch_fwd(bool mfma, const FwdArgs &a, hipStream_t st, KEvents ev = {}) {
+    return mfma ? launch_mfma(a, st, ev) : launch_generic(a, st, ev);
 }
 
-// Optional event records around one kernel of a call (profiling hook).
-struct Timing {
-    la_kernel_events *ev;
-    hipStream_t st;
-    void begin(int slot) const {
-        if (!ev) return;
-        ev->launched[slot] = 1;
-        if (ev->start[slot]) (void)hipEventRecord(static_cast<hipEvent_t>(ev->start[slot]), st);
-    }
-    void end(int slot) const {
-        if (ev && ev->stop[slot]) (void)hipEventRecord(static_cast<hipEvent_t>(ev->stop[slot]), st);
-    }
-};
+// Timing events of one kernel slot of a call (profiling hook); marks the slot launched.
+KEvents slot_events(la_kernel_events *ev, int slot) {
+    KEvents k;
+    if (!ev) return k;
+    ev->launched[slot] = 1;
+    k.start = static_cast<hipEvent_t>(ev->start[slot]);
+    k.stop = static_cast<hipEvent_t>(ev->stop[slot]);
+    return k;
+}
 
 }  // namespace
 }  // namespace la
@@ -246,7 +242,6 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
     if (!direct && (!ws || ws_bytes < wl.total)) return LA_ERR_WORKSPACE;
     if (ev)
         for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
-    Timing tm{ev, hs};
 
     FwdArgs c{};
     c.sh = sh; c.sg = g; c.mode = kModeCausal;
@@ -257,10 +252,7 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
         c.st.src_slice = nS; c.st.zsrc_slice = nz;
         c.st.S_dst = S_out; c.st.z_dst = z_out;
         c.st.dst_slice = nS; c.st.zdst_slice = nz;
-        tm.begin(LA_KSLOT_CHUNK);
-        hipError_t e = launch_fwd(mf, c, hs);
-        tm.end(LA_KSLOT_CHUNK);
-        return e == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+        return launch_fwd(mf, c, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
     float *wsS = static_cast<float *>(ws);
     float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
@@ -271,19 +263,15 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
     a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
     a.st.S_dst = wsS; a.st.z_dst = wsz;
     a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
-    tm.begin(LA_KSLOT_STATE);
-    if (launch_fwd(mf, a, hs) != hipSuccess) return LA_ERR_DEVICE;
-    tm.end(LA_KSLOT_STATE);
+    if (launch_fwd(mf, a, hs, slot_events(ev, LA_KSLOT_STATE)) != hipSuccess) return LA_ERR_DEVICE;
     // B. exclusive prefix over segments (+ S_in); final state to S_out
-    tm.begin(LA_KSLOT_SCAN);
-    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, S_out, z_out, false, hs) != hipSuccess) return LA_ERR_DEVICE;
-    tm.end(LA_KSLOT_SCAN);
+    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, S_out, z_out, false, hs, slot_events(ev, LA_KSLOT_SCAN)) !=
+        hipSuccess)
+        return LA_ERR_DEVICE;
     // C. chunk loop of every segment from its prefix state
     c.st.S_src = wsS; c.st.z_src = wsz;
     c.st.src_slice = g.P * nS; c.st.src_seg = nS; c.st.zsrc_slice = g.P * nz; c.st.zsrc_seg = nz;
-    tm.begin(LA_KSLOT_CHUNK);
-    if (launch_fwd(mf, c, hs) != hipSuccess) return LA_ERR_DEVICE;
-    tm.end(LA_KSLOT_CHUNK);
+    if (launch_fwd(mf, c, hs, slot_events(ev, LA_KSLOT_CHUNK)) != hipSuccess) return LA_ERR_DEVICE;
     return LA_OK;
 }
 

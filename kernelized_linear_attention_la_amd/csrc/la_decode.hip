@@ -157,15 +157,13 @@ hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const vo
     if (sh.dtype == kF32) {
         auto *qq = static_cast<const float *>(q); auto *kk = static_cast<const float *>(k);
         auto *vv = static_cast<const float *>(v); auto *oo = static_cast<float *>(o);
-        if (vec) hipLaunchKernelGGL((k_decode<float, 4>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
-        else hipLaunchKernelGGL((k_decode<float, 1>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
-    } else {
-        auto *qq = static_cast<const uint16_t *>(q); auto *kk = static_cast<const uint16_t *>(k);
-        auto *vv = static_cast<const uint16_t *>(v); auto *oo = static_cast<uint16_t *>(o);
-        if (vec) hipLaunchKernelGGL((k_decode<uint16_t, 4>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
-        else hipLaunchKernelGGL((k_decode<uint16_t, 1>), grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+        return vec ? launch_kernel(k_decode<float, 4>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
+                   : launch_kernel(k_decode<float, 1>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
     }
-    return hipGetLastError();
+    auto *qq = static_cast<const uint16_t *>(q); auto *kk = static_cast<const uint16_t *>(k);
+    auto *vv = static_cast<const uint16_t *>(v); auto *oo = static_cast<uint16_t *>(o);
+    return vec ? launch_kernel(k_decode<uint16_t, 4>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
+               : launch_kernel(k_decode<uint16_t, 1>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
 }
 
 }  // namespace la

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz
 
 size_t generic_lds_bytes(int dk, int dp) { return sizeof(float) * (size_t)gen_layout(dk, dp).total; }
 
-hipError_t launch_generic(const FwdArgs &a, hipStream_t stream) {
+hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev) {
     const int nslab = (a.sh.dv + kVS - 1) / kVS;
     const size_t grid = (size_t)a.sh.BH * a.sg.P * nslab;
     const size_t lds = generic_lds_bytes(a.sh.dk, a.sh.dp);
@@ -294,28 +294,23 @@ hipError_t launch_generic(const FwdArgs &a, hipStream_t stream) {
     const bool f32 = a.sh.dtype == kF32;
     switch (a.mode) {
         case kModeState:
-            if (f32) hipLaunchKernelGGL((k_generic<float, kModeState>), gr, bl, lds, stream, a);
-            else hipLaunchKernelGGL((k_generic<uint16_t, kModeState>), gr, bl, lds, stream, a);
-            break;
+            return f32 ? launch_kernel_ev(k_generic<float, kModeState>, gr, bl, lds, stream, ev, a)
+                       : launch_kernel_ev(k_generic<uint16_t, kModeState>, gr, bl, lds, stream, ev, a);
         case kModeCausal:
-            if (f32) hipLaunchKernelGGL((k_generic<float, kModeCausal>), gr, bl, lds, stream, a);
-            else hipLaunchKernelGGL((k_generic<uint16_t, kModeCausal>), gr, bl, lds, stream, a);
-            break;
+            return f32 ? launch_kernel_ev(k_generic<float, kModeCausal>, gr, bl, lds, stream, ev, a)
+                       : launch_kernel_ev(k_generic<uint16_t, kModeCausal>, gr, bl, lds, stream, ev, a);
         default:
-            if (f32) hipLaunchKernelGGL((k_generic<float, kModeRead>), gr, bl, lds, stream, a);
-            else hipLaunchKernelGGL((k_generic<uint16_t, kModeRead>), gr, bl, lds, stream, a);
-            break;
+            return f32 ? launch_kernel_ev(k_generic<float, kModeRead>, gr, bl, lds, stream, ev, a)
+                       : launch_kernel_ev(k_generic<uint16_t, kModeRead>, gr, bl, lds, stream, ev, a);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in, const float *z_in,
-                       float *S_out, float *z_out, bool total_to_slot0, hipStream_t stream) {
+                       float *S_out, float *z_out, bool total_to_slot0, hipStream_t stream, KEvents ev) {
     const int nS = sh.dp * sh.dv, nz = sh.dp;
     const int bps = (nS + nz + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)((size_t)sh.BH * bps)), dim3(kThreads), 0, stream, sh.BH, P, nS, nz,
-                       ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0);
-    return hipGetLastError();
+    return launch_kernel_ev(k_scan, dim3((unsigned)((size_t)sh.BH * bps)), dim3(kThreads), 0, stream, ev, sh.BH, P,
+                            nS, nz, ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0);
 }
 
 }  // namespace la

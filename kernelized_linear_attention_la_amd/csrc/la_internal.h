@@ -5,6 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace la {
 
 enum Phi : int { kElu1 = 0, kFavor = 1 };
@@ -59,15 +62,45 @@ struct FwdArgs {
     StateArgs st;
 };
 
+// Optional timing events of one kernel launch (profiling hook).
+struct KEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch `kernel` and return the status of this launch alone, never an error
+// left pending by earlier runtime calls of the caller.  With events, the
+// launch itself records them (hipExtLaunchKernel), so they bracket exactly
+// the kernel's execution.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel_ev(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                                   KEvents ev, Args &&...args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+    return std::apply(
+        [&](auto &...v) {
+            void *ptrs[] = {static_cast<void *>(&v)...};
+            const void *f = reinterpret_cast<const void *>(kernel);
+            if (ev.start || ev.stop) return hipExtLaunchKernel(f, grid, block, ptrs, lds, st, ev.start, ev.stop, 0);
+            return hipLaunchKernel(f, grid, block, ptrs, lds, st);
+        },
+        vals);
+}
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                                Args &&...args) {
+    return launch_kernel_ev(kernel, grid, block, lds, st, KEvents{}, std::forward<Args>(args)...);
+}
+
 // Host-side launchers (return hipSuccess or the launch error).
-hipError_t launch_generic(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in,
                        const float *z_in, float *S_out, float *z_out, bool total_to_slot0,
-                       hipStream_t stream);
+                       hipStream_t stream, KEvents ev = {});
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o,
                          float *S, float *z, hipStream_t stream);
 // bf16 MFMA path; returns hipErrorNotSupported when the shape has no MFMA variant.
-hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 bool mfma_supported(const Shape &sh, int chunk);
 
 }  // namespace la

@@ -564,14 +564,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 }
 
 template <int DK, int DV, int C, int PHI>
-hipError_t launch_variant(const FwdArgs &a, hipStream_t st) {
+hipError_t launch_variant(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.sh.BH * a.sg.P)), block(C / 16 * 64);
     switch (a.mode) {
-        case kModeState: hipLaunchKernelGGL((k_mfma<DK, DV, C, PHI, kModeState>), grid, block, 0, st, a); break;
-        case kModeCausal: hipLaunchKernelGGL((k_mfma<DK, DV, C, PHI, kModeCausal>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((k_mfma<DK, DV, C, PHI, kModeRead>), grid, block, 0, st, a); break;
+        case kModeState: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeState>, grid, block, 0, st, ev, a);
+        case kModeCausal: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeCausal>, grid, block, 0, st, ev, a);
+        default: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeRead>, grid, block, 0, st, ev, a);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -583,13 +582,14 @@ bool mfma_supported(const Shape &sh, int chunk) {
     return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
 }
 
-hipError_t launch_mfma(const FwdArgs &a, hipStream_t st) {
+hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const Shape &s = a.sh;
     const int C = a.sg.chunk;
     if (!mfma_supported(s, C)) return hipErrorNotSupported;
-    if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st);
-    if (s.dk == 64) return C == 64 ? launch_variant<64, 64, 64, kElu1>(a, st) : launch_variant<64, 64, 128, kElu1>(a, st);
-    return C == 64 ? launch_variant<128, 128, 64, kElu1>(a, st) : launch_variant<128, 128, 128, kElu1>(a, st);
+    if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st, ev);
+    if (s.dk == 64)
+        return C == 64 ? launch_variant<64, 64, 64, kElu1>(a, st, ev) : launch_variant<64, 64, 128, kElu1>(a, st, ev);
+    return C == 64 ? launch_variant<128, 128, 64, kElu1>(a, st, ev) : launch_variant<128, 128, 128, kElu1>(a, st, ev);
 }
 
 }  // namespace la
