@@ -236,20 +236,28 @@ def bench_forward(args, wl):
         for i in range(R):  # eager warm-up on the capture stream
             step(i)
     torch.cuda.synchronize()
-    graphs = []
-    for i in range(R):
+    # one graph replays all R rotated input sets back to back (launch cost is
+    # paid once per R steps); a second graph covers the K mod R remainder
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            step(i)
-        graphs.append(g)
+            for i in range(n):
+                step(i)
+        return g
+
+    g_all = capture(R)
+    rem = args.steps % R
+    g_rem = capture(rem) if rem else None
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        graphs[i % R].replay()
+    for _ in range(max(1, args.warmup // R)):
+        g_all.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    for _ in range(args.steps // R):
+        g_all.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps

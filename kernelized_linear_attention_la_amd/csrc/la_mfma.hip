@@ -227,16 +227,21 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 
     const float inv_sqrt_m = G::F ? 1.0f / 16.0f : 1.0f;  // m = 256
 
-    // ---- register prefetch of one chunk: K (ELU+1) and V rows in 8-column
+    // ---- register prefetch of a chunk: K (ELU+1) and V rows in 8-column
     // pieces, plus this wave's query rows (and, for FAVOR+, its key rows).
-    // Chunk c+1 is fetched right after chunk c is staged, so its loads are in
-    // flight during chunk c's matrix work.
+    // Chunk c+DEPTH is fetched right after chunk c is staged, so its loads are
+    // in flight during the matrix work of chunks c and c+1.
     constexpr int UK = (NEED_K && !G::F) ? C * DK / 8 : 0;
     constexpr int UV = NEED_K ? C * DV / 8 : 0;
     constexpr int KBQ = G::F ? G::KBD : KBF;  // 16-byte query pieces per lane
-    Op8 praw[(UK + UV) / G::THREADS > 0 ? (UK + UV) / G::THREADS : 1];
-    Op8 pq[KBQ];
-    Op8 pk[G::F ? G::KBD : 1];
+    // prefetch ring: two chunks in flight ahead of the one being computed
+    constexpr int DEPTH = 2;
+    struct Pref {
+        Op8 raw[(UK + UV) / G::THREADS > 0 ? (UK + UV) / G::THREADS : 1];
+        Op8 q[KBQ];
+        Op8 k[G::F ? G::KBD : 1];
+    };
+    Pref pf[DEPTH];
     const int row = 16 * w + c16;  // this lane's query (and FAVOR+ key) row inside a chunk
 
     static_assert(UK % G::THREADS == 0 && UV % G::THREADS == 0, "units must tile the workgroup");
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // Piece i of a thread is row t = piece / W8, columns 8 * (piece % W8).
     // A whole chunk inside the sequence (the common case) takes the path
     // without per-row guards; the branch is uniform across the workgroup.
-    auto fetch = [&](int cc) {
+    auto fetch = [&](Pref &p, int cc) {
         const int tt0 = cc * C;
         const bool full = tt0 + C <= N;
         const bool rv = tt0 + row < N;
@@ -253,24 +258,24 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < UKT; ++i) {
                 const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
-                praw[i].u = *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8);
+                p.raw[i].u = *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8);
             }
 #pragma unroll
             for (int i = 0; i < UVT; ++i) {
                 const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
-                praw[UKT + i].u = *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8);
+                p.raw[UKT + i].u = *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < UKT; ++i) {
                 const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
-                praw[i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8)
+                p.raw[i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Ks + (size_t)(tt0 + t) * DK + 8 * c8)
                                         : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < UVT; ++i) {
                 const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
-                praw[UKT + i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8)
+                p.raw[UKT + i].u = tt0 + t < N ? *reinterpret_cast<const uint4 *>(Vs + (size_t)(tt0 + t) * DV + 8 * c8)
                                               : make_uint4(0, 0, 0, 0);
             }
         }
@@ -278,46 +283,48 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             const T *qrow = Qs + (size_t)(tt0 + row) * DK + 8 * g;
             if (full) {
 #pragma unroll
-                for (int kb = 0; kb < KBQ; ++kb) pq[kb].u = *reinterpret_cast<const uint4 *>(qrow + 32 * kb);
+                for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = *reinterpret_cast<const uint4 *>(qrow + 32 * kb);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < KBQ; ++kb)
-                    pq[kb].u = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kb) : make_uint4(0, 0, 0, 0);
+                    p.q[kb].u = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kb) : make_uint4(0, 0, 0, 0);
             }
         }
         if constexpr (G::F && NEED_K) {
             const T *krow = Ks + (size_t)(tt0 + row) * DK + 8 * g;
             if (full) {
 #pragma unroll
-                for (int kb = 0; kb < G::KBD; ++kb) pk[kb].u = *reinterpret_cast<const uint4 *>(krow + 32 * kb);
+                for (int kb = 0; kb < G::KBD; ++kb) p.k[kb].u = *reinterpret_cast<const uint4 *>(krow + 32 * kb);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < G::KBD; ++kb)
-                    pk[kb].u = rv ? *reinterpret_cast<const uint4 *>(krow + 32 * kb) : make_uint4(0, 0, 0, 0);
+                    p.k[kb].u = rv ? *reinterpret_cast<const uint4 *>(krow + 32 * kb) : make_uint4(0, 0, 0, 0);
             }
         }
     };
 
     // ---- write one prefetched chunk into LDS (token-major rows)
-    auto stage = [&](int tt0) {
+    auto stage = [&](const Pref &p, int tt0) {
         const bool full = tt0 + C <= N;
 #pragma unroll
         for (int i = 0; i < UKT; ++i) {
             // ELU+1 on the way in; tokens past the end get phi = 0, not phi(0) = 1
             const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
-            uint4 ph = elu1_bf16x8(praw[i].u);
+            uint4 ph = elu1_bf16x8(p.raw[i].u);
             if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
         }
 #pragma unroll
         for (int i = 0; i < UVT; ++i) {
             const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
-            *reinterpret_cast<uint4 *>(&sm.V[t * RV + 8 * c8]) = praw[UKT + i].u;
+            *reinterpret_cast<uint4 *>(&sm.V[t * RV + 8 * c8]) = p.raw[UKT + i].u;
         }
     };
 
-    // the first chunk's loads go out before the starting state is read
-    fetch(c_begin);
+    // the first chunks' loads go out before the starting state is read
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (c_begin + d < c_end) fetch(pf[d], c_begin + d);
     // ---- starting state into the owners' accumulators (+ bf16 image)
     f32x4 S[FBW][NJ];
     {
@@ -353,25 +360,25 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     }
     block_sync_lds();
 
-    for (int c = c_begin; c < c_end; ++c) {
+    auto body = [&](Pref &p, int c) {
         const int t0 = c * C;
-        stage(t0);
+        stage(p, t0);
         const bool rvalid = t0 + row < N;  // FAVOR+: key row of this lane exists
         Op8 phq[KBF];
         Op8 xq[G::F ? G::KBD : 1], xk[G::F ? G::KBD : 1];
         if constexpr (DO_OUT && !G::F) {
 #pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = elu1_bf16x8(pq[kb].u);  // rows past the end are not stored
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
         }
         if constexpr (G::F) {
 #pragma unroll
             for (int kb = 0; kb < G::KBD; ++kb) {
-                xq[kb] = pq[kb];
-                xk[kb] = pk[kb];
+                xq[kb] = p.q[kb];
+                xk[kb] = p.k[kb];
             }
         }
         block_sync_lds();
-        if (c + 1 < c_end) fetch(c + 1);
+        if (c + DEPTH < c_end) fetch(p, c + DEPTH);
 
         // ---------------- FAVOR+: feature maps through projections on the matrix cores.
         // U^T = W X^T for this wave's 16 rows: accumulator lane (4g+e, c16)
@@ -539,6 +546,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 }
             }
         }
+    };
+    for (int c0 = c_begin; c0 < c_end; c0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            if (c0 + d < c_end) body(pf[d], c0 + d);
     }
 
     // ---- final state of the range
