@@ -71,10 +71,11 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) { ret
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// ELU+1 ("Linear Attention", feature-map table): max(x, 0) + exp(min(x, 0)),
-// which is x + 1 for x > 0 and exp(x) otherwise; hardware exp2 (~1 ulp).
+// ELU+1 ("Linear Attention", feature-map table): x + 1 for x > 0, else exp(x)
+// (hardware exp2, ~1 ulp; its value for x > 0 is discarded by the select).
 __device__ __forceinline__ float elu1_hw(float x) {
-    return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896341f);
+    const float e = __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+    return x > 0.f ? x + 1.f : e;
 }
 
 // ELU+1 of eight packed bf16 values, rounded back to packed bf16
@@ -242,7 +243,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         Op8 k[G::F ? G::KBD : 1];
     };
     Pref pf[DEPTH];
-    const int row = 16 * w + c16;  // this lane's query (and FAVOR+ key) row inside a chunk
+    // Query block of this wave.  Waves w and w + 4 share a SIMD; with eight
+    // waves the blocks are paired (0,7) (2,5) (4,3) (6,1) so every SIMD gets
+    // the same share of the causal triangle.
+    const int qb = NW == 8 ? (w < 4 ? 2 * w : 15 - 2 * w) : w;
+    const int row = 16 * qb + c16;  // this lane's query (and FAVOR+ key) row inside a chunk
 
     static_assert(UK % G::THREADS == 0 && UV % G::THREADS == 0, "units must tile the workgroup");
     constexpr int UKT = UK / G::THREADS, UVT = UV / G::THREADS;  // K and V pieces per thread
@@ -448,13 +453,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 // (P (.) M) V_aug over the key blocks up to the diagonal
 #pragma unroll
                 for (int kt = 0; kt < KBT; ++kt) {
-                    if (2 * kt <= w) {
+                    if (2 * kt <= qb) {
                         f32x4 p[2];
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
                             const int jb = 2 * kt + h;
                             p[h] = zero4();
-                            if (jb <= w) {
+                            if (jb <= qb) {
                                 const uint16_t *krow = &sm.K[(16 * jb + c16) * RK];
 #pragma unroll
                                 for (int kf = 0; kf < KBF; ++kf) {
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                                     }
                                     p[h] = mfma(ka, phq[kf], p[h]);
                                 }
-                                if (jb == w) {  // causal mask on the diagonal block: key 4g+e <= query c16
+                                if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
 #pragma unroll
                                     for (int e = 0; e < 4; ++e)
                                         if (4 * g + e > c16) p[h][e] = 0.f;
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 const int idx = it * 64 + lane;
                 const int r = idx / (DV / 8), c8 = idx % (DV / 8);
                 const uint4 val = *reinterpret_cast<const uint4 *>(&so[r * RO + 8 * c8]);
-                T *dst = Os + (size_t)(t0 + 16 * w + r) * DV + 8 * c8;
-                if (full || t0 + 16 * w + r < N) *reinterpret_cast<uint4 *>(dst) = val;
+                T *dst = Os + (size_t)(t0 + 16 * qb + r) * DV + 8 * c8;
+                if (full || t0 + 16 * qb + r < N) *reinterpret_cast<uint4 *>(dst) = val;
             }
         }
 
