@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum {
     LA_OK = 0,
@@ -81,6 +81,11 @@ int la_feature_dim(const la_problem *p);
  * Device workspace (bytes) that la_forward_causal_chunked(p, chunk, ...) and
  * la_forward_noncausal(p, ...) need; 0 means ws may be NULL.  The value depends
  * only on the problem shape and chunk.  Returns 0 for an invalid problem.
+ * Fill a workspace with zeros before the first call that uses it; every call
+ * leaves it ready for the next one (whatever the shape).  Its first 256 bytes
+ * hold the hand-off state of the single-pass causal path: keep them between
+ * calls, and give calls that may run at the same time (on any streams)
+ * workspaces of their own.
  */
 size_t la_workspace_bytes(const la_problem *p, int chunk);
 
@@ -88,7 +93,8 @@ size_t la_workspace_bytes(const la_problem *p, int chunk);
  * Non-causal forward ("Story of Attention Part 5", 1a, matrix form):
  *   S = phi(K)^T V,  z = phi(K)^T 1,  O = (phi(Q) S) / (phi(Q) z)  row-wise.
  * S_out/z_out (both or neither; may be NULL) receive S and z.
- * ws: caller-provided device scratch of at least la_workspace_bytes(p, 64) bytes.
+ * ws: caller-provided device scratch of at least la_workspace_bytes(p, 64)
+ * bytes (its first 256 bytes are left untouched).
  */
 la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K, const void *V,
                                void *O, float *S_out, float *z_out, void *ws, size_t ws_bytes,
@@ -107,7 +113,13 @@ la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K
  *   S_out, z_out final state after token N (both NULL = not exported).  May be
  *                the same buffers as S_in, z_in (updated in place).
  *   ws           device scratch of at least la_workspace_bytes(p, chunk) bytes
- *                (NULL allowed when that is 0).  Contents on entry are ignored.
+ *                (NULL allowed when that is 0), zero-filled before its first
+ *                use and otherwise as the previous call left it.
+ * With the bf16 matrix-core kernels and more than one segment per slice the
+ * call is a single launch: each workgroup sums its segment, hands the sums to
+ * the later segments of its slice through ws and runs its chunks from the
+ * prefix it receives.  Each hand-off wait is bounded (about 10 s); should one
+ * ever expire, the outputs that depend on it are NaN instead of a hung device.
  */
 la_status la_forward_causal_chunked(const la_problem *p, int chunk,
                                     const void *Q, const void *K, const void *V, void *O,
@@ -118,10 +130,11 @@ la_status la_forward_causal_chunked(const la_problem *p, int chunk,
 /*
  * Per-kernel timing hook for profiling and benchmarking.  A causal call
  * enqueues up to three kernels, each in its own slot:
- *   LA_KSLOT_STATE  per-segment sums phi(K)^T V, phi(K)^T 1 (only when the
- *                   sequence is split into several segments),
+ *   LA_KSLOT_STATE  per-segment sums phi(K)^T V, phi(K)^T 1 (only on the
+ *                   fp32 path when the sequence is split into segments),
  *   LA_KSLOT_SCAN   exclusive prefix of those sums over segments (same case),
- *   LA_KSLOT_CHUNK  the chunk loop that writes O (always).
+ *   LA_KSLOT_CHUNK  the kernel that writes O (always; on the single-pass
+ *                   path the one kernel of the call).
  * For every slot whose kernel is enqueued, the launch of that kernel records
  * start[slot] when it begins and stop[slot] when it ends (hipExtLaunchKernel),
  * so the pair brackets exactly that kernel.  Entries may be NULL (not

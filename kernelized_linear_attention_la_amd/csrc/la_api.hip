@@ -104,17 +104,35 @@ Segments noncausal_plan(const Shape &sh, bool *use_mfma) {
               : plan_segments(sh, kNoncausalChunk, generic_columns(sh), 1);
 }
 
+// Workspace: [control block][segment flags][S part][z part].
+//  * control block (kCtlBytes, fixed offset for every shape): launch counter,
+//    done count and error word of the single-pass mode;
+//  * flags: one word per (slice, segment);
+//  * S part: P + 1 single-pass slots of d' x (d_v + 16) floats per slice (S,
+//    z and padding in the matrix-core accumulator order); the separate passes
+//    use P x d' x d_v of it, with the z part.
+constexpr size_t kCtlBytes = 256;
+
 struct WsLayout {
-    size_t s_bytes, z_bytes, total;
+    size_t f_off, s_off, z_off, total;
 };
 
 WsLayout ws_layout(const Shape &sh, int P) {
+    const size_t f_bytes = round_up(sizeof(uint32_t) * (size_t)sh.BH * P, kAlign);
+    const size_t s_bytes = round_up(sizeof(float) * (size_t)sh.BH * (P + 1) * sh.dp * (sh.dv + 16), kAlign);
+    const size_t z_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp, kAlign);
     WsLayout w;
-    w.s_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp * sh.dv, kAlign);
-    w.z_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp, kAlign);
-    w.total = w.s_bytes + w.z_bytes;
+    w.f_off = kCtlBytes;
+    w.s_off = w.f_off + f_bytes;
+    w.z_off = w.s_off + s_bytes;
+    w.total = w.z_off + z_bytes;
     return w;
 }
+
+// Bound of one hand-off wait of the single-pass mode: 10 s of the 100 MHz
+// constant-rate clock.  A correct launch waits microseconds; the bound only
+// turns a lost hand-off into NaN output instead of a hung device.
+constexpr long long kSpinTicks = 1000000000LL;
 
 // A single workgroup per slice can start from S_in and finish into S_out by
 // itself (safe even when they alias).  Several segments, or several value
@@ -197,8 +215,8 @@ LA_API la_status la_forward_noncausal(const la_problem *p, const void *Q, const 
     WsLayout wl = ws_layout(sh, g.P);
     if (!ws || ws_bytes < wl.total) return LA_ERR_WORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    float *wsS = static_cast<float *>(ws);
-    float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
+    float *wsS = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_off);
+    float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.z_off);
     const size_t nS = (size_t)sh.dp * sh.dv, nz = (size_t)sh.dp;
 
     // 1. per-segment sums phi(K)^T V, phi(K)^T 1
@@ -254,8 +272,24 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
         c.st.dst_slice = nS; c.st.zdst_slice = nz;
         return launch_fwd(mf, c, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
-    float *wsS = static_cast<float *>(ws);
-    float *wsz = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.s_bytes);
+    char *wsb = static_cast<char *>(ws);
+    float *wsS = reinterpret_cast<float *>(wsb + wl.s_off);
+    float *wsz = reinterpret_cast<float *>(wsb + wl.z_off);
+
+    if (mf) {
+        // single pass on the matrix cores: every workgroup sums its segment,
+        // hands the sums on through the workspace and runs its chunks
+        FwdArgs f = c;
+        f.mode = kModeFused;
+        f.st.S_src = S_in; f.st.z_src = z_in;
+        f.st.src_slice = nS; f.st.zsrc_slice = nz;
+        f.fu.ctl = reinterpret_cast<uint32_t *>(wsb);
+        f.fu.flags = reinterpret_cast<uint32_t *>(wsb + wl.f_off);
+        f.fu.slots = wsS;
+        f.fu.spin_ticks = kSpinTicks;
+        f.fu.S_out = S_out; f.fu.z_out = z_out;
+        return launch_mfma(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+    }
 
     // A. each segment's own sums phi(K)^T V, phi(K)^T 1
     FwdArgs a{};

@@ -17,7 +17,8 @@ enum Dtype : int { kF32 = 0, kBF16 = 1 };
 enum Mode : int {
     kModeState = 0,   // accumulate phi(K)^T [V, 1] of the segment into a state slot
     kModeCausal = 1,  // chunkwise causal forward starting from a prefix state
-    kModeRead = 2     // non-causal read: O = phi(Q) S / phi(Q) z with a fixed state
+    kModeRead = 2,    // non-causal read: O = phi(Q) S / phi(Q) z with a fixed state
+    kModeFused = 3    // causal, single pass: segment sums, hand-off between segments, chunk loop
 };
 
 // Shape of one call, after host validation.
@@ -53,6 +54,22 @@ struct StateArgs {
     size_t zdst_slice, zdst_seg;
 };
 
+// Hand-off of the single-pass causal mode (one launch, P segments per slice).
+// ctl[0] counts completed launches on this workspace, ctl[1] counts the
+// workgroups of the running launch that are done, ctl[2] is set to 1 when a
+// wait expired (the affected outputs are then NaN).  A launch tags its flags
+// with ctl[0] + 1; the last workgroup to finish advances ctl[0] and clears
+// ctl[1].  The control block and flags must be zero before the first launch
+// on a workspace.  Slot 0 of a slice holds S_in, slot 1 + s the sums of
+// segment s (slot P also parks the last segment's own sums).
+struct FusedArgs {
+    uint32_t *ctl;         // [3] launch counter, done count, error word
+    uint32_t *flags;       // [B*H*P] tag of the launch whose segment sums are ready
+    float *slots;          // [B*H][P+1][d' * (d_v + 16)] accumulator-order states
+    long long spin_ticks;  // wall-clock bound of one wait (s_memrealtime ticks)
+    float *S_out, *z_out;  // final state of each slice (NULL = not exported)
+};
+
 struct FwdArgs {
     Shape sh;
     Segments sg;
@@ -60,6 +77,7 @@ struct FwdArgs {
     const void *Q, *K, *V;
     void *O;
     StateArgs st;
+    FusedArgs fu;
 };
 
 // Optional timing events of one kernel launch (profiling hook).

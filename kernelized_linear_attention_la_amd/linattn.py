@@ -167,6 +167,8 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
     """Causal chunkwise forward; returns O (same dtype as q).
 
     S_out/z_out, when given, receive the final state (they may be S_in/z_in).
+    workspace: optional uint8 device tensor of la_workspace_bytes(p, chunk)
+    bytes, zero-filled before its first use and reused as the last call left it.
     events: optional LaKernelEvents (per-kernel hipEvent records; see
     la_forward_causal_chunked_timed in the C header).
     """
@@ -181,7 +183,9 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     nbytes = la_workspace_bytes(p, chunk)
     if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        # a fresh workspace starts zero-filled (the C contract); a caller that
+        # passes its own keeps it between calls
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is None:
         st = lib().la_forward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert linattn.la_abi_version() == 1
+    assert linattn.la_abi_version() == 2
     for s in range(8):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)

@@ -125,6 +125,11 @@ CASES = [
     (3, 1, 65, 64, 64, "bf16", "favor", 256, 64),
     (1, 1, 1, 64, 64, "bf16", "favor", 256, 64),
     (1, 2, 2100, 64, 64, "bf16", "favor", 256, 64),
+    # single-pass hand-off with segments of three chunks (odd ring phase),
+    # a shorter last segment and a ragged tail
+    (4, 16, 700, 64, 64, "bf16", "elu1", 0, 64),
+    (8, 16, 768, 128, 128, "bf16", "elu1", 0, 128),
+    (4, 16, 740, 64, 64, "bf16", "favor", 256, 64),
 ]
 
 
@@ -294,3 +299,55 @@ def test_full_size_decode_sampled():
     assert worst < TOL_F32, worst
     assert state_rel_err(_gather(to_f64(S), samp), S_ref) < TOL_F32
     assert z_rel_err(_gather(to_f64(z), samp), z_ref) < TOL_F32
+
+
+def test_single_pass_workspace_reuse_and_graph_replay():
+    """One zero-filled workspace serves many single-pass calls of different shapes (segment counts),
+    eagerly and replayed from a HIP graph; every result equals the fresh-workspace result bit for bit."""
+    shapes = [(2, 4, 700, 64, 64), (4, 16, 700, 64, 64), (1, 2, 1500, 128, 128)]
+    data = []
+    for i, (B, H, N, dk, dv) in enumerate(shapes):
+        fi = inputs.custom_inputs(300 + i, B, H, N, dk, dv, scale=dk ** -0.5, dtype="bf16")
+        q, k, v, _ = _dev(fi)
+        chunk = 64 if dk == 64 else 128
+        S, z = _zero_state(B, H, dk, dv)
+        O = la.la_forward_causal_chunked(q, k, v, chunk, S_out=S, z_out=z)  # fresh zero-filled workspace
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.causal_recurrent("elu1", fi.Q.f32, fi.K.f32, fi.V.f32)
+        assert row_rel_err(to_f64(O), ref) < TOL_BF16
+        data.append((q, k, v, chunk, O.clone(), S.clone(), z.clone()))
+    nbytes = max(la.la_workspace_bytes(la._problem_of(d[0], d[2], "elu1", None), d[3]) for d in data)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rnd in range(3):
+        for i, (q, k, v, chunk, O0, S0, z0) in enumerate(data):
+            _say("shared workspace round", rnd, "shape", shapes[i])
+            S, z = torch.empty_like(S0), torch.empty_like(z0)
+            O = la.la_forward_causal_chunked(q, k, v, chunk, S_out=S, z_out=z, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(O, O0) and torch.equal(S, S0) and torch.equal(z, z0), (rnd, i)
+    # graph capture of two calls (two shapes) on the shared workspace, replayed with eager calls in between
+    q, k, v, chunk, O0, S0, z0 = data[0]
+    q2, k2, v2, chunk2, O20, _, _ = data[1]
+    O, S, z = torch.empty_like(O0), torch.empty_like(S0), torch.empty_like(z0)
+    O2 = torch.empty_like(O20)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        la.la_forward_causal_chunked(q, k, v, chunk, S_out=S, z_out=z, out=O, workspace=ws)
+        la.la_forward_causal_chunked(q2, k2, v2, chunk2, out=O2, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        la.la_forward_causal_chunked(q, k, v, chunk, S_out=S, z_out=z, out=O, workspace=ws)
+        la.la_forward_causal_chunked(q2, k2, v2, chunk2, out=O2, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        _say("graph replay", rep)
+        O.zero_(), O2.zero_(), S.zero_(), z.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O, O0) and torch.equal(S, S0) and torch.equal(z, z0), rep
+        assert torch.equal(O2, O20), rep
+        la.la_forward_causal_chunked(q2, k2, v2, chunk2, out=O2, workspace=ws)  # eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(O2, O20), rep
