@@ -157,9 +157,7 @@ struct Cfg {
     static constexpr int RK = DP + 8;
     static constexpr int RV = F ? DVA + 8 : ((DVA + 111) / 128) * 128 + 16;
     static constexpr int RO = DV + 8;
-    // FAVOR+ feature slots follow the accumulator order of the projection
-    // tiles; ELU+1 features keep their natural order.
-    static constexpr bool FEAT_PI = F;
+    static constexpr int RX = DK + 8;  // FAVOR+: raw key / query rows (16-row 128-bit reads conflict free)
 };
 
 template <int DK, int DV, int C, int PHI>
@@ -170,7 +168,9 @@ struct Smem {
     uint16_t V[C * G::RV];              // V_aug, token-major
     uint4 STB[G::NJ][G::KBF][64];       // bf16 S_aug: B operand of phi(Q) S
     uint16_t O[G::NW][16 * G::RO];      // per-wave output staging for 16-byte stores
-    uint4 WA[F ? 2 : 1][F ? G::M / 16 : 1][F ? G::KBD : 1][F ? 64 : 1];  // FAVOR+ W rows, bf16 hi / lo
+    uint16_t XK[F ? C * G::RX : 1];     // FAVOR+: raw K_c, token-major
+    uint16_t XQ[F ? C * G::RX : 1];     // FAVOR+: raw Q_c, token-major
+    uint16_t QP[F ? C * G::RK : 1];     // FAVOR+: phi(Q_c), token-major
 };
 
 // Store a 16x16 fp32 state tile (lane l holds S[16fb + 4g + e][16nb + l%16])
@@ -179,12 +179,8 @@ template <typename G>
 __device__ __forceinline__ void put_state_block(uint4 (*STB)[G::KBF][64], int fb, int nb, int lane, f32x4 s) {
     const int g = lane >> 4, c = lane & 15;
     uint2 v = pack4(s[0], s[1], s[2], s[3]);
-    if (G::FEAT_PI) {
-        reinterpret_cast<uint2 *>(&STB[nb][fb >> 1][lane])[fb & 1] = v;
-    } else {
-        const int x = 16 * (fb & 1) + 4 * g;  // natural order: slot = x
-        reinterpret_cast<uint2 *>(&STB[nb][fb >> 1][c + 16 * (x >> 3)])[(x >> 2) & 1] = v;
-    }
+    const int x = 16 * (fb & 1) + 4 * g;  // feature slot inside the 32-feature k-block
+    reinterpret_cast<uint2 *>(&STB[nb][fb >> 1][c + 16 * (x >> 3)])[(x >> 2) & 1] = v;
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
@@ -227,46 +223,49 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     const T *Vs = static_cast<const T *>(a.V) + (size_t)bh * N * DV;
     T *Os = DO_OUT ? static_cast<T *>(a.O) + (size_t)bh * N * DV : nullptr;
 
-    // ---- FAVOR+ projection rows into LDS, once per workgroup.  W is split as
-    // W = W_hi + W_lo with both parts bf16 (W_lo = bf16(W - W_hi)); the
-    // inputs are exact in bf16, so x . w_r = x . hi_r + x . lo_r is accurate to
-    // about 2^-16 relative, where a single bf16 W would shift every exponent
-    // of the feature map by ~2^-9 |w_r| |x|.
+    // ---- FAVOR+ projection rows in registers, once per workgroup: wave w
+    // owns features 64w..64w+63 and holds their rows of W as MFMA A operands
+    // (lane l: row 64w + 16fbl + l%16, columns 32kb + 8(l/16)..+7).  W is
+    // split as W = W_hi + W_lo with both parts bf16 (W_lo = bf16(W - W_hi));
+    // the inputs are exact in bf16, so x . w_r = x . hi_r + x . lo_r is
+    // accurate to about 2^-16 relative, where a single bf16 W would shift
+    // every exponent of the feature map by ~2^-9 |w_r| |x|.
+    constexpr int FWB = G::F ? 4 : 1;  // 16-feature blocks of W per wave
+    static_assert(!G::F || NW * 64 == G::M, "FAVOR+: one wave per 64 features");
+    Op8 wreg[FWB][G::F ? G::KBD : 1][2];
     if constexpr (G::F) {
-        for (int u = tid; u < G::M * DK / 8; u += G::THREADS) {
-            const int r = u / (DK / 8), d8 = u % (DK / 8);
-            const float *src = a.sh.W + (size_t)r * DK + 8 * d8;
-            float4 w0 = *reinterpret_cast<const float4 *>(src);
-            float4 w1 = *reinterpret_cast<const float4 *>(src + 4);
-            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            Op8 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const uint32_t h2 = cvt2(wv[e], wv[e + 1]);
-                hi.u32[e / 2] = h2;
-                lo.u32[e / 2] = cvt2(wv[e] - lo_bf16(h2), wv[e + 1] - hi_bf16(h2));
+        for (int fbl = 0; fbl < FWB; ++fbl)
+#pragma unroll
+            for (int kb = 0; kb < G::KBD; ++kb) {
+                const float *src = a.sh.W + (size_t)(64 * w + 16 * fbl + c16) * DK + 32 * kb + 8 * g;
+                const float4 w0 = *reinterpret_cast<const float4 *>(src);
+                const float4 w1 = *reinterpret_cast<const float4 *>(src + 4);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t h2 = cvt2(wv[e], wv[e + 1]);
+                    wreg[fbl][kb][0].u32[e / 2] = h2;
+                    wreg[fbl][kb][1].u32[e / 2] = cvt2(wv[e] - lo_bf16(h2), wv[e + 1] - hi_bf16(h2));
+                }
             }
-            const int l = (r & 15) + 16 * (d8 & 3);
-            sm.WA[0][r >> 4][d8 >> 2][l] = hi.u;
-            sm.WA[1][r >> 4][d8 >> 2][l] = lo.u;
-        }
     }
 
     const float inv_sqrt_m = G::F ? 1.0f / 16.0f : 1.0f;  // m = 256
 
-    // ---- register prefetch of a chunk: K (ELU+1) and V rows in 8-column
-    // pieces, plus this wave's query rows (and, for FAVOR+, its key rows).
-    // Chunk c+DEPTH is fetched right after chunk c is staged, so its loads are
-    // in flight during the matrix work of chunks c and c+1.
-    constexpr int UK = (NEED_K && !G::F) ? C * DK / 8 : 0;
+    // ---- register prefetch of a chunk: K and V rows in 8-column pieces
+    // (FAVOR+: also Q), plus, for ELU+1, this wave's query rows.  Chunk
+    // c+DEPTH is fetched right after chunk c is staged, so its loads are in
+    // flight during the matrix work of chunks c and c+1.
+    constexpr int UK = NEED_K ? C * DK / 8 : 0;
     constexpr int UV = NEED_K ? C * DV / 8 : 0;
-    constexpr int KBQ = G::F ? G::KBD : KBF;  // 16-byte query pieces per lane
+    constexpr int UQ = (G::F && DO_OUT) ? C * DK / 8 : 0;
+    constexpr int KBQ = G::F ? 1 : KBF;  // ELU+1: 16-byte query pieces per lane
     // prefetch ring: two chunks in flight ahead of the one being computed
     constexpr int DEPTH = 2;
     struct Pref {
-        Op8 raw[(UK + UV) / G::THREADS > 0 ? (UK + UV) / G::THREADS : 1];
+        Op8 raw[(UK + UV + UQ) / G::THREADS > 0 ? (UK + UV + UQ) / G::THREADS : 1];
         Op8 q[KBQ];
-        Op8 k[G::F ? G::KBD : 1];
     };
     Pref pf[DEPTH];
     // Query block of this wave.  Waves w and w + 4 share a SIMD; with eight
@@ -275,8 +274,9 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     const int qb = NW == 8 ? (w < 4 ? 2 * w : 15 - 2 * w) : w;
     const int row = 16 * qb + c16;  // this lane's query (and FAVOR+ key) row inside a chunk
 
-    static_assert(UK % G::THREADS == 0 && UV % G::THREADS == 0, "units must tile the workgroup");
-    constexpr int UKT = UK / G::THREADS, UVT = UV / G::THREADS;  // K and V pieces per thread
+    static_assert(UK % G::THREADS == 0 && UV % G::THREADS == 0 && UQ % G::THREADS == 0,
+                  "units must tile the workgroup");
+    constexpr int UKT = UK / G::THREADS, UVT = UV / G::THREADS, UQT = UQ / G::THREADS;  // pieces per thread
 
     // Piece i of a thread is row t = piece / W8, columns 8 * (piece % W8);
     // its byte offset inside the chunk is 16 * piece.  Every chunk index,
@@ -309,12 +309,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         for (int i = 0; i < UVT; ++i) p.raw[UKT + i].u = bload16(rv, 16 * (tid + i * G::THREADS));
         if constexpr (DO_OUT) {
             const auto rq = make_rsrc(Qs + (size_t)tt0 * DK, qlive ? rows * DK * 2 : 0);
+            if constexpr (G::F) {
 #pragma unroll
-            for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = bload16(rq, 2 * (row * DK + 8 * g + 32 * kb));
-        }
-        if constexpr (G::F && NEED_K) {
+                for (int i = 0; i < UQT; ++i) p.raw[UKT + UVT + i].u = bload16(rq, 16 * (tid + i * G::THREADS));
+            } else {
 #pragma unroll
-            for (int kb = 0; kb < G::KBD; ++kb) p.k[kb].u = bload16(rk, 2 * (row * DK + 8 * g + 32 * kb));
+                for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = bload16(rq, 2 * (row * DK + 8 * g + 32 * kb));
+            }
         }
     };
 
@@ -323,11 +324,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         const bool full = tt0 + C <= N;
 #pragma unroll
         for (int i = 0; i < UKT; ++i) {
-            // ELU+1 on the way in; tokens past the end get phi = 0, not phi(0) = 1
             const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
-            uint4 ph = elu1_bf16x8(p.raw[i].u);
-            if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
+            if constexpr (G::F) {  // raw rows; the feature map runs on the matrix cores
+                *reinterpret_cast<uint4 *>(&sm.XK[t * G::RX + 8 * c8]) = p.raw[i].u;
+            } else {
+                // ELU+1 on the way in; tokens past the end get phi = 0, not phi(0) = 1
+                uint4 ph = elu1_bf16x8(p.raw[i].u);
+                if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < UQT; ++i) {
+            const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
+            *reinterpret_cast<uint4 *>(&sm.XQ[t * G::RX + 8 * c8]) = p.raw[UKT + UVT + i].u;
         }
 #pragma unroll
         for (int i = 0; i < UVT; ++i) {
@@ -382,80 +392,65 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         constexpr bool CARRY = OUT && MODE != kModeRead;  // refresh the state image for the next chunk
         const int t0 = c * C;
         stage(p, t0);
-        const bool rvalid = t0 + row < N;  // FAVOR+: key row of this lane exists
         Op8 phq[KBF];
-        Op8 xq[G::F ? G::KBD : 1], xk[G::F ? G::KBD : 1];
         if constexpr (OUT && !G::F) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
-        }
-        if constexpr (G::F) {
-#pragma unroll
-            for (int kb = 0; kb < G::KBD; ++kb) {
-                xq[kb] = p.q[kb];
-                xk[kb] = p.k[kb];
-            }
         }
         block_sync_lds();
         fetch(p, step + DEPTH);
 
         // ---------------- FAVOR+: feature maps through projections on the matrix cores.
-        // U^T = W X^T for this wave's 16 rows: accumulator lane (4g+e, c16)
-        // holds feature 16rb + 4g + e of row c16, which is the operand order.
+        // Wave w forms U = W_w X^T for its 64 features and all C tokens: the
+        // A operands (W) are in registers, the B operands are the raw rows
+        // (lane l: token 16tb + l%16, columns 32kb + 8(l/16)..+7), and
+        // accumulator lane (4g+e, c16) of tile (fbl, tb) holds feature
+        // 64w + 16fbl + 4g + e of token 16tb + c16.  phi = exp(u - |x|^2/2)/sqrt(m)
+        // goes to LDS token-major, in natural feature order.
         if constexpr (G::F) {
-            auto project = [&](const Op8 *x, auto &&emit) {
-                float sq = 0.f;
+            static_assert(C == 64, "FAVOR+: four 16-token blocks per chunk");
+            auto project = [&](const uint16_t *xr, uint16_t *dst, bool mask_tail) {
+                Op8 xb[4][G::KBD];
+                float shift[4];
 #pragma unroll
-                for (int kb = 0; kb < G::KBD; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v0 = lo_bf16(x[kb].u32[e]), v1 = hi_bf16(x[kb].u32[e]);
-                        sq += v0 * v0 + v1 * v1;
-                    }
-                sq += __shfl_xor(sq, 16, 64);
-                sq += __shfl_xor(sq, 32, 64);
-                const float shift = 0.5f * sq;
-#pragma unroll
-                for (int kf = 0; kf < KBF; ++kf) {
-                    f32x4 u0 = zero4(), u1 = zero4();
+                for (int tb = 0; tb < 4; ++tb) {
+                    float sq = 0.f;
 #pragma unroll
                     for (int kb = 0; kb < G::KBD; ++kb) {
+                        xb[tb][kb].u = *reinterpret_cast<const uint4 *>(&xr[(16 * tb + c16) * G::RX + 32 * kb + 8 * g]);
 #pragma unroll
-                        for (int part = 0; part < 2; ++part) {
-                            Op8 w0, w1;
-                            w0.u = sm.WA[part][2 * kf][kb][lane];
-                            w1.u = sm.WA[part][2 * kf + 1][kb][lane];
-                            u0 = mfma(w0, x[kb], u0);
-                            u1 = mfma(w1, x[kb], u1);
+                        for (int e = 0; e < 4; ++e) {
+                            const float v0 = lo_bf16(xb[tb][kb].u32[e]), v1 = hi_bf16(xb[tb][kb].u32[e]);
+                            sq += v0 * v0 + v1 * v1;
                         }
                     }
-                    emit(kf, u0, u1, shift);
+                    sq += __shfl_xor(sq, 16, 64);
+                    sq += __shfl_xor(sq, 32, 64);
+                    shift[tb] = 0.5f * sq;
                 }
-            };
-            if constexpr (OUT) {
-                project(xq, [&](int kf, f32x4 u0, f32x4 u1, float shift) {
-                    phq[kf].q[0] = pack4(fast_exp(u0[0] - shift) * inv_sqrt_m, fast_exp(u0[1] - shift) * inv_sqrt_m,
-                                         fast_exp(u0[2] - shift) * inv_sqrt_m, fast_exp(u0[3] - shift) * inv_sqrt_m);
-                    phq[kf].q[1] = pack4(fast_exp(u1[0] - shift) * inv_sqrt_m, fast_exp(u1[1] - shift) * inv_sqrt_m,
-                                         fast_exp(u1[2] - shift) * inv_sqrt_m, fast_exp(u1[3] - shift) * inv_sqrt_m);
-                });
-            }
-            if constexpr (NEED_K) {
-                // keys of token block w -> phi(K) rows 16w.., features in natural order
-                project(xk, [&](int kf, f32x4 u0, f32x4 u1, float shift) {
-                    uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
-                    if (rvalid) {
-                        lo = pack4(fast_exp(u0[0] - shift) * inv_sqrt_m, fast_exp(u0[1] - shift) * inv_sqrt_m,
-                                   fast_exp(u0[2] - shift) * inv_sqrt_m, fast_exp(u0[3] - shift) * inv_sqrt_m);
-                        hi = pack4(fast_exp(u1[0] - shift) * inv_sqrt_m, fast_exp(u1[1] - shift) * inv_sqrt_m,
-                                   fast_exp(u1[2] - shift) * inv_sqrt_m, fast_exp(u1[3] - shift) * inv_sqrt_m);
+#pragma unroll
+                for (int fbl = 0; fbl < FWB; ++fbl)
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        f32x4 u = zero4();
+#pragma unroll
+                        for (int kb = 0; kb < G::KBD; ++kb)
+#pragma unroll
+                            for (int part = 0; part < 2; ++part) u = mfma(wreg[fbl][kb][part], xb[tb][kb], u);
+                        const int t = 16 * tb + c16;
+                        uint2 v = pack4(fast_exp(u[0] - shift[tb]) * inv_sqrt_m, fast_exp(u[1] - shift[tb]) * inv_sqrt_m,
+                                        fast_exp(u[2] - shift[tb]) * inv_sqrt_m, fast_exp(u[3] - shift[tb]) * inv_sqrt_m);
+                        if (mask_tail && t0 + t >= N) v = make_uint2(0, 0);  // keys past the end: phi = 0
+                        *reinterpret_cast<uint2 *>(&dst[t * RK + 64 * w + 16 * fbl + 4 * g]) = v;
                     }
-                    uint16_t *dst = &sm.K[row * RK + 32 * kf + 4 * g];
-                    *reinterpret_cast<uint2 *>(dst) = lo;
-                    *reinterpret_cast<uint2 *>(dst + 16) = hi;
-                });
-            }
+            };
+            if constexpr (NEED_K) project(sm.XK, sm.K, true);
+            if constexpr (OUT) project(sm.XQ, sm.QP, false);
             block_sync_lds();
+            if constexpr (OUT) {
+#pragma unroll
+                for (int kf = 0; kf < KBF; ++kf) phq[kf].u = *reinterpret_cast<const uint4 *>(&sm.QP[row * RK + 32 * kf + 8 * g]);
+            }
         }
 
         // ---------------- outputs of this wave's 16 query rows
@@ -478,12 +473,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                                 for (int kf = 0; kf < KBF; ++kf) {
                                     Op8 ka;
-                                    if constexpr (G::FEAT_PI) {
-                                        ka.q[0] = *reinterpret_cast<const uint2 *>(krow + 32 * kf + 4 * g);
-                                        ka.q[1] = *reinterpret_cast<const uint2 *>(krow + 32 * kf + 16 + 4 * g);
-                                    } else {
-                                        ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
-                                    }
+                                    ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
                                     p[h] = mfma(ka, phq[kf], p[h]);
                                 }
                                 if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
@@ -585,7 +575,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     constexpr int PER = FBW * NJ;            // 16-byte pieces per lane per slot
     float *const slots = FUSED ? a.fu.slots + (size_t)bh * (sg.P + 1) * SLOT : nullptr;
     auto slot_rsrc = [&](int i, bool live) { return make_rsrc(slots + (size_t)i * SLOT, live ? SLOT * 4 : 0); };
-    auto piece_off = [&](int fb, int nb) { return ((fb * NJ + nb) * 64 + lane) * 16; };
+    // Piece (fb, nb) of this lane.  In the normaliser block only column d_v
+    // (lanes with c16 == 0) is data; the other lanes get an offset past the
+    // slot, so their loads read zeros and their stores are dropped, moving
+    // no bytes.
+    auto piece_off = [&](int fb, int nb) {
+        return nb == NJ - 1 && c16 != 0 ? SLOT * 4 : ((fb * NJ + nb) * 64 + lane) * 16;
+    };
     auto store_slot = [&](int i) {  // this lane's pieces of S into slot i
         const auto r = slot_rsrc(i, true);
 #pragma unroll
@@ -642,20 +638,23 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         for (int q = 0; q < FBW; ++q)
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) S[q][nb] = zero4();
-        f32x4 buf[2][PER];
-        load_slot(buf[0], 0, has_in);
-        load_slot(buf[1], 1, seg >= 1);
+        // GD slots in flight (as many as the registers allow)
+        constexpr int GD = PER <= 6 ? 4 : 2;
+        f32x4 buf[GD][PER];
+#pragma unroll
+        for (int d = 0; d < GD; ++d) load_slot(buf[d], d, d == 0 ? has_in : d <= seg);
         auto add_slot = [&](const f32x4 *src) {
 #pragma unroll
             for (int q = 0; q < FBW; ++q)
 #pragma unroll
                 for (int nb = 0; nb < NJ; ++nb) S[q][nb] += src[q * NJ + nb];
         };
-        for (int i = 0; i <= seg; i += 2) {  // a slot read as zeros adds exactly nothing
-            add_slot(buf[0]);
-            load_slot(buf[0], i + 2, i + 2 <= seg);
-            add_slot(buf[1]);
-            load_slot(buf[1], i + 3, i + 3 <= seg);
+        for (int i = 0; i <= seg; i += GD) {  // a slot read as zeros adds exactly nothing
+#pragma unroll
+            for (int d = 0; d < GD; ++d) {
+                add_slot(buf[d]);
+                load_slot(buf[d], i + d + GD, i + d + GD <= seg);
+            }
         }
         if (late)
 #pragma unroll
