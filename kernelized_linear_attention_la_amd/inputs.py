@@ -191,10 +191,15 @@ class Workload:
     m: int = 0          # FAVOR+ feature count
     modes: tuple = ("causal",)
     decode_steps: int = 0  # > 0: N is the prefix length, then this many decode steps
+    retention: bool = False  # decayed, unnormalised variant (per-head decays, no normaliser)
 
     @property
     def dprime(self) -> int:
         return self.m if self.phi == "favor" else self.dk
+
+    def gammas(self) -> np.ndarray:
+        """Per-head decays of a retention workload (float32 [H])."""
+        return retention_decays(self.H)
 
     @property
     def tokens(self) -> int:
@@ -213,8 +218,28 @@ WORKLOADS = {
                  1024, 128, 128, 1.0 / math.sqrt(128), 64, decode_steps=64),
         Workload("favor_bf16_b2h8n8192d64_m256_c64", 5, "favor", "bf16", 2, 8, 8192, 64, 64,
                  64 ** -0.25, 64, m=256),
+        # retention (decayed, unnormalised; raw q and k): the shapes of the
+        # normalised workloads above, one decay per head
+        Workload("ret_f32_b1h2n256d64_c64", 6, "identity", "f32", 1, 2, 256, 64, 64, 1.0 / math.sqrt(64), 64,
+                 retention=True),
+        Workload("ret_bf16_b4h8n2048d64_c64", 7, "identity", "bf16", 4, 8, 2048, 64, 64, 1.0 / math.sqrt(64), 64,
+                 retention=True),
+        Workload("ret_bf16_b2h16n16384d128_c128", 8, "identity", "bf16", 2, 16, 16384, 128, 128,
+                 1.0 / math.sqrt(128), 128, retention=True),
     ]
 }
+
+
+def retention_decays(H: int) -> np.ndarray:
+    """Per-head decays for the retention workloads: log-spaced forgetting rates,
+    gamma_h = 1 - 2^-(3 + 7 h / (H - 1)), from 1 - 1/8 (head 0) to 1 - 1/1024
+    (last head); a single head gets 1 - 1/32.  Rounded to float32 (the storage
+    type of the decays), so both sides see identical values."""
+    if H == 1:
+        e = np.array([5.0])
+    else:
+        e = 3.0 + 7.0 * np.arange(H) / (H - 1)
+    return (1.0 - 2.0 ** (-e)).astype(np.float32)
 
 
 @dataclass

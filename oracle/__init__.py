@@ -24,7 +24,8 @@ _LIB = os.path.join(_HERE, "liblaoracle.so")
 
 PHI_ELU1 = 0
 PHI_FAVOR = 1
-_PHI = {"elu1": PHI_ELU1, "favor": PHI_FAVOR}
+PHI_IDENTITY = 2
+_PHI = {"elu1": PHI_ELU1, "favor": PHI_FAVOR, "identity": PHI_IDENTITY}
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +56,10 @@ def lib():
         L.ora_quadratic.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, i, D]
         L.ora_causal_chunked.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, i, D, D, D]
         L.ora_decode_step.argtypes = [i, i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_retention_recurrent.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, D, D]
+        L.ora_retention_parallel.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_retention_chunked.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, i, D, D]
+        L.ora_retention_decode_step.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D]
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_set_num_threads.argtypes = [i]
         _lib = L
@@ -190,3 +195,67 @@ def decode_step(phi_kind, q, k, v, S, z, W=None):
     lib().ora_decode_step(BH, dk, dv, _kind(phi_kind), m, _p(Wd), _p(qf), _p(kf), _p(vf),
                           _p(Sn), _p(zn), _p(o))
     return o.reshape(B, H, dv), Sn.reshape(B, H, dp, dv), zn.reshape(B, H, dp)
+
+
+# ---------------------------------------------------------------------------
+# Retention: decayed, unnormalised ("Story of Attention Part 5", sections 4 and 6)
+# ---------------------------------------------------------------------------
+def _gamma(gamma, H):
+    """Per-head decays as float64 [H]; a scalar applies to every head."""
+    g = np.asarray(gamma, dtype=np.float64)
+    if g.ndim == 0:
+        g = np.full(H, float(g))
+    if g.shape != (H,):
+        raise ValueError(f"gamma must be a scalar or have {H} entries")
+    return np.ascontiguousarray(g)
+
+
+def _rstate_in(S_in, BH, dp, dv):
+    return None if S_in is None else _d(S_in).reshape(BH, dp, dv)
+
+
+def retention_recurrent(phi_kind, Q, K, V, gamma, W=None, S_in=None):
+    """S_n = gamma S_{n-1} + phi(k_n) v_n^T, o_n = phi(q_n)^T S_n. Returns O, S_final."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    g = _gamma(gamma, H)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dp, dv))
+    lib().ora_retention_recurrent(BH, H, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(g), _p(Qf), _p(Kf), _p(Vf),
+                                  _p(_rstate_in(S_in, BH, dp, dv)), _p(O), _p(S))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv)
+
+
+def retention_parallel(phi_kind, Q, K, V, gamma, W=None, S_in=None):
+    """O = (phi(Q) phi(K)^T (.) D) V (+ gamma^(i+1) phi(q_i)^T S_in), every pair explicit."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    g = _gamma(gamma, H)
+    O = np.empty((BH, N, dv))
+    lib().ora_retention_parallel(BH, H, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(g), _p(Qf), _p(Kf), _p(Vf),
+                                 _p(_rstate_in(S_in, BH, dp, dv)), _p(O))
+    return O.reshape(B, H, N, dv)
+
+
+def retention_chunked(phi_kind, Q, K, V, gamma, chunk, W=None, S_in=None):
+    """Lightning blockwise form with blocks of `chunk` tokens. Returns O, S_final."""
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    g = _gamma(gamma, H)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dp, dv))
+    lib().ora_retention_chunked(BH, H, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(g), _p(Qf), _p(Kf), _p(Vf),
+                                _p(_rstate_in(S_in, BH, dp, dv)), int(chunk), _p(O), _p(S))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv)
+
+
+def retention_decode_step(phi_kind, q, k, v, S, gamma, W=None):
+    """One retention step for every (b, h); q,k [B,H,dk], v [B,H,dv]. Returns (o, S_new)."""
+    q = _d(q); k = _d(k); v = _d(v)
+    B, H = q.shape[0], q.shape[1]
+    dk = q.shape[-1]; dv = v.shape[-1]
+    BH = B * H
+    Wd = _d(W) if W is not None else None
+    m = Wd.shape[0] if Wd is not None else 0
+    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    g = _gamma(gamma, H)
+    Sn = _d(S).reshape(BH, dp, dv).copy()
+    o = np.empty((BH, dv))
+    lib().ora_retention_decode_step(BH, H, dk, dv, _kind(phi_kind), m, _p(Wd), _p(g), _p(q.reshape(BH, dk)),
+                                    _p(k.reshape(BH, dk)), _p(v.reshape(BH, dv)), _p(Sn), _p(o))
+    return o.reshape(B, H, dv), Sn.reshape(B, H, dp, dv)

@@ -20,14 +20,22 @@
  *         starts at zero; parallel and recurrent modes compute one function.
  *  [SOA5] "Story of Attention Part 5": section 1a (kernel linear attention,
  *         its matrix form, its recurrence and the n = 4 worked example),
- *         section 1b (Performer / FAVOR+ feature map), section 5
- *         (Infini-attention memory read), section 6 (Lightning Attention
- *         blockwise split, used here with decay lambda = 1).
+ *         section 1b (Performer / FAVOR+ feature map), section 4 (RetNet
+ *         retention: parallel form with the causal decay matrix D, recurrent
+ *         form S_n = gamma S_{n-1} + k_n^T v_n, and its n = 4 worked
+ *         example), section 5 (Infini-attention memory read), section 6
+ *         (Lightning Attention blockwise split: with decay lambda = 1 for the
+ *         normalised kernel attention, and with its decay for retention).
  *
  * Memory layout of every array (row-major, slices independent):
  *   Q, K  [BH, N, dk]     V, O  [BH, N, dv]
  *   S     [BH, dp, dv]    z     [BH, dp]         dp = dk (ELU+1) or m (FAVOR+)
  *   W     [m, dk]         (FAVOR+ projection rows w_r, shared by all slices)
+ *
+ * Retention (the decayed, unnormalised variant of section 4 / 6) uses a
+ * decay gamma per head: slice s of BH = B * H has head h = s % H and decay
+ * gamma[h].  The identity feature map (phi(x) = x, RetNet's raw q and k) is
+ * kind 2; ELU+1 and FAVOR+ may be used with retention as well.
  *
  * Parity status: every function below is pinned by tests/test_oracle_pins.py
  * (printed worked examples, brute force agreement of independent forms,
@@ -45,6 +53,7 @@
 
 #define ORA_PHI_ELU1 0
 #define ORA_PHI_FAVOR 1
+#define ORA_PHI_IDENTITY 2
 
 int ora_num_threads(void) {
 #ifdef _OPENMP
@@ -86,6 +95,7 @@ static void phi_favor_row(const double *x, int d, const double *W, int m, double
 
 static void phi_row(int kind, const double *x, int d, const double *W, int m, double *out) {
     if (kind == ORA_PHI_FAVOR) phi_favor_row(x, d, W, m, out);
+    else if (kind == ORA_PHI_IDENTITY) memcpy(out, x, sizeof(double) * d);
     else phi_elu1_row(x, d, out);
 }
 
@@ -332,6 +342,168 @@ void ora_decode_step(int BH, int dk, int dv, int kind, int m, const double *W,
         double den;
         ora_state_read(1, dp, dv, pq, Ss, zs, o + (size_t)s * dv, &den);
         for (int c = 0; c < dv; ++c) o[(size_t)s * dv + c] /= den;
+        free(pk); free(pq);
+    }
+}
+
+/* ===========================================================================
+ * Retention: decayed, unnormalised linear attention [SOA5 4 RetNet; SOA5 6
+ * Lightning Attention].  There is no normaliser z: the outputs are the
+ * decayed numerators.  gamma[H]: decay of head h; slice s uses gamma[s % H].
+ * S [BH, dp, dv] only.
+ * ======================================================================== */
+
+/* Recurrent form [SOA5 4]: S_n = gamma S_{n-1} + phi(k_n) v_n^T,
+ * o_n = phi(q_n)^T S_n (update, then read), S_0 = S_in or zero. */
+void ora_retention_recurrent(int BH, int H, int N, int dk, int dv, int kind, int m, const double *W,
+                             const double *gamma, const double *Q, const double *K, const double *V,
+                             const double *S_in, double *O, double *S_out) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double g = gamma[s % H];
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        if (S_in) memcpy(S, S_in + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+        double *pk = (double *)malloc(sizeof(double) * dp);
+        double *pq = (double *)malloc(sizeof(double) * dp);
+        for (int i = 0; i < N; ++i) {
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, pk);
+            for (int f = 0; f < dp; ++f)
+                for (int c = 0; c < dv; ++c)
+                    S[(size_t)f * dv + c] = g * S[(size_t)f * dv + c] + pk[f] * v[(size_t)i * dv + c];
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, pq);
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < dp; ++f) acc += pq[f] * S[(size_t)f * dv + c];
+                O[((size_t)s * N + i) * dv + c] = acc;
+            }
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dp * dv, S, sizeof(double) * dp * dv);
+        free(S); free(pk); free(pq);
+    }
+}
+
+/* Parallel form [SOA5 4]: O = (phi(Q) phi(K)^T (.) D) V with the causal decay
+ * matrix D_ij = gamma^(i-j) for i >= j, else 0.  A starting state S_in
+ * enters as it does in the recurrence unrolled from it: token i (counting
+ * from 0) reads gamma^(i+1) phi(q_i)^T S_in.  Every pair is explicit. */
+void ora_retention_parallel(int BH, int H, int N, int dk, int dv, int kind, int m, const double *W,
+                            const double *gamma, const double *Q, const double *K, const double *V,
+                            const double *S_in, double *O) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double g = gamma[s % H];
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *pk = phi_all(kind, N, dk, k, m, W);
+        double *pq = phi_all(kind, N, dk, q, m, W);
+        for (int i = 0; i < N; ++i) {
+            const double *pqi = pq + (size_t)i * dp;
+            for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] = 0.0;
+            if (S_in) {
+                const double *Si = S_in + (size_t)s * dp * dv;
+                const double w = pow(g, (double)(i + 1));
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int f = 0; f < dp; ++f) acc += pqi[f] * Si[(size_t)f * dv + c];
+                    O[((size_t)s * N + i) * dv + c] += w * acc;
+                }
+            }
+            for (int j = 0; j <= i; ++j) {
+                double qk = 0.0;
+                for (int f = 0; f < dp; ++f) qk += pqi[f] * pk[(size_t)j * dp + f];
+                const double a = qk * pow(g, (double)(i - j)); /* (Q K^T (.) D)_ij */
+                for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] += a * v[(size_t)j * dv + c];
+            }
+        }
+        free(pk); free(pq);
+    }
+}
+
+/* Blockwise form [SOA5 6, Lightning Attention], blocks of C tokens (the last
+ * may be shorter, of length L).  With rows s, t = 1..L of a block and
+ * lambda = gamma[h]:
+ *   O_i = (phi(Q_i) phi(K_i)^T (.) M) V_i + Lambda phi(Q_i) S_{i-1},
+ *   S_i = lambda^L S_{i-1} + (lambda^L Lambda^{-1} phi(K_i))^T V_i,
+ * M_st = lambda^(s-t) for s >= t else 0, Lambda = diag(lambda^1..lambda^L).
+ * The key scale lambda^L (Lambda^{-1})_tt is evaluated as lambda^(L-t), the
+ * same number without the overflow of lambda^-t on its own. */
+void ora_retention_chunked(int BH, int H, int N, int dk, int dv, int kind, int m, const double *W,
+                           const double *gamma, const double *Q, const double *K, const double *V,
+                           const double *S_in, int C, double *O, double *S_out) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double lam = gamma[s % H];
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        if (S_in) memcpy(S, S_in + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+        double *pq = (double *)malloc(sizeof(double) * (size_t)C * dp);
+        double *pk = (double *)malloc(sizeof(double) * (size_t)C * dp);
+        double *A = (double *)malloc(sizeof(double) * (size_t)C * C);
+        double *Sn = (double *)malloc(sizeof(double) * (size_t)dp * dv);
+        for (int t0 = 0; t0 < N; t0 += C) {
+            int L = N - t0 < C ? N - t0 : C;
+            ora_phi(kind, L, dk, q + (size_t)t0 * dk, m, W, pq);
+            ora_phi(kind, L, dk, k + (size_t)t0 * dk, m, W, pk);
+            /* intra-block scores with the causal-decay mask M (rows i, cols t, 0-based) */
+            for (int i = 0; i < L; ++i)
+                for (int t = 0; t < L; ++t) {
+                    double a = 0.0;
+                    if (t <= i) {
+                        for (int f = 0; f < dp; ++f) a += pq[(size_t)i * dp + f] * pk[(size_t)t * dp + f];
+                        a *= pow(lam, (double)(i - t));
+                    }
+                    A[(size_t)i * C + t] = a;
+                }
+            for (int i = 0; i < L; ++i) {
+                const double lam_row = pow(lam, (double)(i + 1)); /* Lambda_ii */
+                for (int c = 0; c < dv; ++c) {
+                    double intra = 0.0, inter = 0.0;
+                    for (int t = 0; t < L; ++t) intra += A[(size_t)i * C + t] * v[(size_t)(t0 + t) * dv + c];
+                    for (int f = 0; f < dp; ++f) inter += pq[(size_t)i * dp + f] * S[(size_t)f * dv + c];
+                    O[((size_t)s * N + t0 + i) * dv + c] = intra + lam_row * inter;
+                }
+            }
+            /* state carried past the block */
+            const double lamL = pow(lam, (double)L);
+            for (int f = 0; f < dp; ++f)
+                for (int c = 0; c < dv; ++c) {
+                    double acc = lamL * S[(size_t)f * dv + c];
+                    for (int t = 0; t < L; ++t)
+                        acc += pow(lam, (double)(L - (t + 1))) * pk[(size_t)t * dp + f] * v[(size_t)(t0 + t) * dv + c];
+                    Sn[(size_t)f * dv + c] = acc;
+                }
+            memcpy(S, Sn, sizeof(double) * dp * dv);
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dp * dv, S, sizeof(double) * dp * dv);
+        free(S); free(pq); free(pk); free(A); free(Sn);
+    }
+}
+
+/* One retention decode step [SOA5 4 recurrent form]: S = gamma S + phi(k) v^T,
+ * o = phi(q)^T S.  q, k [BH, dk]; v, o [BH, dv]; S [BH, dp, dv] in place. */
+void ora_retention_decode_step(int BH, int H, int dk, int dv, int kind, int m, const double *W,
+                               const double *gamma, const double *q, const double *k, const double *v,
+                               double *S, double *o) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < BH; ++s) {
+        const double g = gamma[s % H];
+        double *pk = (double *)malloc(sizeof(double) * dp);
+        double *pq = (double *)malloc(sizeof(double) * dp);
+        double *Ss = S + (size_t)s * dp * dv;
+        const double *vs = v + (size_t)s * dv;
+        phi_row(kind, k + (size_t)s * dk, dk, W, m, pk);
+        phi_row(kind, q + (size_t)s * dk, dk, W, m, pq);
+        for (int f = 0; f < dp; ++f)
+            for (int c = 0; c < dv; ++c) Ss[(size_t)f * dv + c] = g * Ss[(size_t)f * dv + c] + pk[f] * vs[c];
+        for (int c = 0; c < dv; ++c) {
+            double acc = 0.0;
+            for (int f = 0; f < dp; ++f) acc += pq[f] * Ss[(size_t)f * dv + c];
+            o[(size_t)s * dv + c] = acc;
+        }
         free(pk); free(pq);
     }
 }
