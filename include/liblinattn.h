@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-typedef enum { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1 } la_phi_kind;
+typedef enum { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 2 } la_phi_kind;
 
 typedef struct {
     int B, H, N;        /* batch, heads, tokens (N = 1 for la_decode_step)                   */
@@ -170,6 +170,42 @@ la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
  */
 la_status la_decode_step(const la_problem *p, const void *q, const void *k, const void *v,
                          void *o, float *S, float *z, void *stream);
+
+/*
+ * Retention: decayed, unnormalised linear attention ("Story of Attention
+ * Part 5", section 4 RetNet and section 6 Lightning Attention), per head h
+ * with decay lambda = gamma[h]:
+ *   recurrent   S_n = lambda S_{n-1} + phi(k_n) v_n^T,  o_n = phi(q_n)^T S_n,
+ *   parallel    O = (phi(Q) phi(K)^T (.) D) V,  D_ij = lambda^(i-j) for i >= j,
+ *   blockwise   O_i = (phi(Q_i) phi(K_i)^T (.) M) V_i + Lambda phi(Q_i) S_{i-1},
+ *               S_i = lambda^B S_{i-1} + (lambda^B Lambda^{-1} phi(K_i))^T V_i,
+ * the form this call runs (blocks of `chunk` tokens).  No normaliser: there
+ * is no z and no division.
+ *   p->phi       LA_PHI_IDENTITY (RetNet's raw q and k: the bf16 matrix-core
+ *                kernels for d_k = d_v in {64, 128}, chunk in {64, 128}), or
+ *                LA_PHI_ELU1 / LA_PHI_FAVOR (fp32-arithmetic kernels).
+ *   gamma        device float [H], decay of each head, in (0, 1]; 4-byte aligned.
+ *   S_in, S_out  [B,H,d',d_v] fp32 initial / final state (NULL = zero / not
+ *                exported); S_out may be S_in.
+ *   ws           as for la_forward_causal_chunked (la_workspace_bytes covers
+ *                retention; zero-filled before its first use).
+ *   ev           per-kernel timing hook as in la_forward_causal_chunked_timed,
+ *                or NULL.
+ */
+la_status la_forward_retention_chunked(const la_problem *p, const float *gamma, int chunk,
+                                       const void *Q, const void *K, const void *V, void *O,
+                                       const float *S_in, float *S_out,
+                                       void *ws, size_t ws_bytes, void *stream,
+                                       la_kernel_events *ev);
+
+/*
+ * One retention decode step for every (b, h) ("Story of Attention Part 5",
+ * section 4 recurrent form): S = gamma[h] S + phi(k) v^T, o = phi(q)^T S.
+ * p->N must be 1; q, k [B,H,1,d_k], v, o [B,H,1,d_v]; S [B,H,d',d_v] fp32 in
+ * place.  gamma as for la_forward_retention_chunked.
+ */
+la_status la_retention_decode_step(const la_problem *p, const float *gamma, const void *q, const void *k,
+                                   const void *v, void *o, float *S, void *stream);
 
 #ifdef __cplusplus
 }

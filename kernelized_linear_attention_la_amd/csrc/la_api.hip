@@ -25,7 +25,7 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 la_status check_problem(const la_problem *p) {
     if (!p) return LA_ERR_NULL;
     if (p->dtype != LA_F32 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
-    if (p->phi != LA_PHI_ELU1 && p->phi != LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
+    if (p->phi != LA_PHI_ELU1 && p->phi != LA_PHI_FAVOR && p->phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
     if (p->B < 1 || p->H < 1 || p->N < 1) return LA_ERR_SHAPE;
     if (p->d_k < 1 || p->d_k > 128 || p->d_v < 1 || p->d_v > 128) return LA_ERR_SHAPE;
     if (p->phi == LA_PHI_FAVOR) {
@@ -48,11 +48,14 @@ Shape make_shape(const la_problem *p) {
     s.N = p->N;
     s.dk = p->d_k;
     s.dv = p->d_v;
-    s.phi = p->phi == LA_PHI_FAVOR ? kFavor : kElu1;
+    s.phi = p->phi == LA_PHI_FAVOR ? kFavor : (p->phi == LA_PHI_IDENTITY ? kIdentity : kElu1);
     s.m = p->phi == LA_PHI_FAVOR ? p->m : 0;
     s.dp = p->phi == LA_PHI_FAVOR ? p->m : p->d_k;
     s.W = p->phi == LA_PHI_FAVOR ? p->W : nullptr;
     s.dtype = p->dtype == LA_BF16 ? kBF16 : kF32;
+    s.ret = 0;
+    s.gamma = nullptr;
+    s.H = p->H;
     return s;
 }
 
@@ -196,14 +199,21 @@ LA_API int la_feature_dim(const la_problem *p) {
 LA_API size_t la_workspace_bytes(const la_problem *p, int chunk) {
     if (check_problem(p) != LA_OK || !chunk_ok(chunk)) return 0;
     Shape sh = make_shape(p);
-    size_t a = causal_ws(sh, chunk), b = noncausal_ws(sh);
-    return a > b ? a : b;
+    size_t need = 0;
+    if (p->phi != LA_PHI_IDENTITY) {  // normalised causal and non-causal calls
+        const size_t a = causal_ws(sh, chunk), b = noncausal_ws(sh);
+        need = a > b ? a : b;
+    }
+    sh.ret = 1;  // retention calls plan their own segments
+    const size_t r = causal_ws(sh, chunk);
+    return r > need ? r : need;
 }
 
 LA_API la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K, const void *V, void *O,
                                       float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if (p->phi == LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // the normaliser needs a positive map
     if (!Q || !K || !V || !O) return LA_ERR_NULL;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_out) ||
@@ -244,6 +254,7 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
                                                  la_kernel_events *ev) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if (p->phi == LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // the normaliser needs a positive map
     if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
     if (!Q || !K || !V || !O) return LA_ERR_NULL;
     if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
@@ -320,6 +331,7 @@ LA_API la_status la_decode_step(const la_problem *p, const void *q, const void *
                                 float *z, void *stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if (p->phi == LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // the normaliser needs a positive map
     if (p->N != 1) return LA_ERR_SHAPE;
     if (!q || !k || !v || !o || !S || !z) return LA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(S) || !aligned16(z))
@@ -327,4 +339,81 @@ LA_API la_status la_decode_step(const la_problem *p, const void *q, const void *
     Shape sh = make_shape(p);
     return launch_decode(sh, q, k, v, o, S, z, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK
                                                                                              : LA_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// Retention: decayed, unnormalised ("Story of Attention Part 5", sections 4, 6)
+// ---------------------------------------------------------------------------
+LA_API la_status la_forward_retention_chunked(const la_problem *p, const float *gamma, int chunk, const void *Q,
+                                              const void *K, const void *V, void *O, const float *S_in,
+                                              float *S_out, void *ws, size_t ws_bytes, void *stream,
+                                              la_kernel_events *ev) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if (!gamma || !Q || !K || !V || !O) return LA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LA_ERR_ALIGN;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_in) ||
+        !aligned16(S_out) || !aligned16(ws))
+        return LA_ERR_ALIGN;
+    Shape sh = make_shape(p);
+    sh.ret = 1;
+    sh.gamma = gamma;
+    bool mf = false;
+    Segments g = causal_plan(sh, chunk, &mf);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)sh.dp * sh.dv;
+    const bool direct = causal_direct(sh, g, mf);
+    WsLayout wl = ws_layout(sh, g.P);
+    if (!direct && (!ws || ws_bytes < wl.total)) return LA_ERR_WORKSPACE;
+    if (ev)
+        for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
+
+    FwdArgs c{};
+    c.sh = sh; c.sg = g; c.mode = kModeCausal;
+    c.Q = Q; c.K = K; c.V = V; c.O = O;
+    if (direct) {
+        c.st.S_src = S_in; c.st.src_slice = nS;
+        c.st.S_dst = S_out; c.st.dst_slice = nS;
+        return launch_fwd(mf, c, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+    }
+    char *wsb = static_cast<char *>(ws);
+    float *wsS = reinterpret_cast<float *>(wsb + wl.s_off);
+    if (mf) {
+        FwdArgs f = c;
+        f.mode = kModeFused;
+        f.st.S_src = S_in; f.st.src_slice = nS;
+        f.fu.ctl = reinterpret_cast<uint32_t *>(wsb);
+        f.fu.flags = reinterpret_cast<uint32_t *>(wsb + wl.f_off);
+        f.fu.slots = wsS;
+        f.fu.spin_ticks = kSpinTicks;
+        f.fu.S_out = S_out;
+        return launch_mfma(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+    }
+    // fp32 path: segment sums (decayed to the segment end), Horner scan, chunk loop
+    FwdArgs a{};
+    a.sh = sh; a.sg = g; a.mode = kModeState;
+    a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
+    a.st.S_dst = wsS; a.st.dst_slice = g.P * nS; a.st.dst_seg = nS;
+    if (launch_fwd(false, a, hs, slot_events(ev, LA_KSLOT_STATE)) != hipSuccess) return LA_ERR_DEVICE;
+    if (launch_scan(sh, g.P, wsS, nullptr, S_in, nullptr, S_out, nullptr, false, hs, slot_events(ev, LA_KSLOT_SCAN),
+                    g.seg_chunks * chunk) != hipSuccess)
+        return LA_ERR_DEVICE;
+    c.st.S_src = wsS; c.st.src_slice = g.P * nS; c.st.src_seg = nS;
+    return launch_fwd(false, c, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+LA_API la_status la_retention_decode_step(const la_problem *p, const float *gamma, const void *q, const void *k,
+                                          const void *v, void *o, float *S, void *stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->N != 1) return LA_ERR_SHAPE;
+    if (!gamma || !q || !k || !v || !o || !S) return LA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LA_ERR_ALIGN;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(S)) return LA_ERR_ALIGN;
+    Shape sh = make_shape(p);
+    sh.ret = 1;
+    sh.gamma = gamma;
+    return launch_decode(sh, q, k, v, o, S, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK
+                                                                                                    : LA_ERR_DEVICE;
 }

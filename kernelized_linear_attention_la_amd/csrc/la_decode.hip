@@ -10,6 +10,9 @@
 // quad c) owns rows g, g + G, g + 2G, ... of columns 4c..4c+3, so a wavefront
 // touches whole contiguous rows (coalesced 16-byte accesses).  Partial column
 // sums meet in LDS; phi(q)^T z' is a block reduction.
+//
+// Retention variant (RET; "Story of Attention Part 5", section 4 recurrent
+// form): S = gamma S + phi(k) v^T, o = phi(q)^T S, with no z and no division.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -21,7 +24,7 @@ constexpr int kMaxDp = 256;
 constexpr int kMaxD = 128;
 constexpr int kBatch = 8;  // rows in flight per thread between load and store
 
-template <typename T, int VW>
+template <typename T, int VW, bool RET>
 __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restrict__ q, const T *__restrict__ k,
                                                      const T *__restrict__ v, T *__restrict__ o,
                                                      float *__restrict__ S, float *__restrict__ z) {
@@ -38,11 +41,17 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
     const T *ks = k + (size_t)bh * dk;
     const T *vs = v + (size_t)bh * dv;
     float *Ss = S + (size_t)bh * dp * dv;
-    float *zs = z + (size_t)bh * dp;
+    float *zs = RET ? nullptr : z + (size_t)bh * dp;
+    const float gam = RET ? sh.gamma[bh % sh.H] : 1.f;
 
     // feature maps of q and k, value row
     if (tid < dv) s_v[tid] = load_as_f32(vs, tid);
-    if (sh.phi == kElu1) {
+    if (sh.phi == kIdentity) {
+        if (tid < dk) {
+            s_pq[tid] = load_as_f32(qs, tid);
+            s_pk[tid] = load_as_f32(ks, tid);
+        }
+    } else if (sh.phi == kElu1) {
         if (tid < dk) {
             s_pq[tid] = elu1_accurate(load_as_f32(qs, tid));
             s_pk[tid] = elu1_accurate(load_as_f32(ks, tid));
@@ -108,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
                     const float pk = s_pk[f], pq = s_pq[f];
 #pragma unroll
                     for (int u = 0; u < VW; ++u) {
-                        buf[b][u] += pk * vv[u];
+                        if constexpr (RET) buf[b][u] = gam * buf[b][u] + pk * vv[u];
+                        else buf[b][u] += pk * vv[u];
                         acc[u] += pq * buf[b][u];
                     }
                     float *dst = Ss + (size_t)f * dv + cg * VW;
@@ -125,11 +135,12 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
 
     // z' = z + phi(k) and its read phi(q)^T z'
     float dpart = 0.f;
-    for (int f = tid; f < dp; f += kThreads) {
-        float zn = zs[f] + s_pk[f];
-        zs[f] = zn;
-        dpart += s_pq[f] * zn;
-    }
+    if constexpr (!RET)
+        for (int f = tid; f < dp; f += kThreads) {
+            float zn = zs[f] + s_pk[f];
+            zs[f] = zn;
+            dpart += s_pq[f] * zn;
+        }
     for (int off = 32; off > 0; off >>= 1) dpart += __shfl_down(dpart, off, 64);
     if ((tid & 63) == 0) s_den[tid >> 6] = dpart;
 
@@ -142,28 +153,39 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
     if (tid < dv) {
         float num = 0.f;
         for (int gg = 0; gg < G; ++gg) num += s_red[gg * dv + tid];
-        float den = 0.f;
-        for (int w = 0; w < kThreads / 64; ++w) den += s_den[w];
-        store_from_f32(o + (size_t)bh * dv, tid, num / den);
+        if constexpr (RET) {
+            store_from_f32(o + (size_t)bh * dv, tid, num);
+        } else {
+            float den = 0.f;
+            for (int w = 0; w < kThreads / 64; ++w) den += s_den[w];
+            store_from_f32(o + (size_t)bh * dv, tid, num / den);
+        }
     }
+}
+
+template <bool RET>
+hipError_t launch_decode_t(const Shape &sh, const void *q, const void *k, const void *v, void *o, float *S, float *z,
+                           hipStream_t stream) {
+    const bool vec = (sh.dv % 4) == 0;
+    dim3 grid((unsigned)sh.BH), block(kThreads);
+    if (sh.dtype == kF32) {
+        auto *qq = static_cast<const float *>(q); auto *kk = static_cast<const float *>(k);
+        auto *vv = static_cast<const float *>(v); auto *oo = static_cast<float *>(o);
+        return vec ? launch_kernel(k_decode<float, 4, RET>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
+                   : launch_kernel(k_decode<float, 1, RET>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+    }
+    auto *qq = static_cast<const uint16_t *>(q); auto *kk = static_cast<const uint16_t *>(k);
+    auto *vv = static_cast<const uint16_t *>(v); auto *oo = static_cast<uint16_t *>(o);
+    return vec ? launch_kernel(k_decode<uint16_t, 4, RET>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
+               : launch_kernel(k_decode<uint16_t, 1, RET>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o, float *S, float *z,
                          hipStream_t stream) {
-    const bool vec = (sh.dv % 4) == 0;
-    dim3 grid((unsigned)sh.BH), block(kThreads);
-    if (sh.dtype == kF32) {
-        auto *qq = static_cast<const float *>(q); auto *kk = static_cast<const float *>(k);
-        auto *vv = static_cast<const float *>(v); auto *oo = static_cast<float *>(o);
-        return vec ? launch_kernel(k_decode<float, 4>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
-                   : launch_kernel(k_decode<float, 1>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
-    }
-    auto *qq = static_cast<const uint16_t *>(q); auto *kk = static_cast<const uint16_t *>(k);
-    auto *vv = static_cast<const uint16_t *>(v); auto *oo = static_cast<uint16_t *>(o);
-    return vec ? launch_kernel(k_decode<uint16_t, 4>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z)
-               : launch_kernel(k_decode<uint16_t, 1>, grid, block, 0, stream, sh, qq, kk, vv, oo, S, z);
+    return sh.ret ? launch_decode_t<true>(sh, q, k, v, o, S, z, stream)
+                    : launch_decode_t<false>(sh, q, k, v, o, S, z, stream);
 }
 
 }  // namespace la

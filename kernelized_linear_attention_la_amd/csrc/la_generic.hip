@@ -11,6 +11,12 @@
 //                                      / [phiQ z + (phiQ phiK^T (masked)) 1]
 //     then S += phiK_c^T V_c, z += phiK_c^T 1
 // The state S (d' x 32 slab) and z live in LDS in fp32 for the whole segment.
+//
+// Retention (sh.ret: decayed, unnormalised; "Story of Attention Part
+// 5", section 6 blockwise form with its decay lambda): no z, no division, and
+// with chunk rows i, t counted from 0 and Lc the tokens of the chunk
+//     O_i = sum_{t<=i} lambda^(i-t) P[i,t] v_t + lambda^(i+1) phiQ_i S,
+//     S   = lambda^Lc S + sum_t lambda^(Lc-1-t) phiK_t v_t^T.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -23,7 +29,7 @@ constexpr int kVS = 32;  // value columns per workgroup
 struct GenLayout {
     int T;    // rows per tile
     int dpp;  // padded row stride of the phi tiles (avoids LDS bank conflicts)
-    int offS, offZ, offX, offSq, offPQ, offPK, offV, offP, total;
+    int offS, offZ, offX, offSq, offPQ, offPK, offV, offP, offW, total;
 };
 
 __host__ __device__ inline GenLayout gen_layout(int dk, int dp) {
@@ -39,6 +45,7 @@ __host__ __device__ inline GenLayout gen_layout(int dk, int dp) {
     L.offPK = o; o += L.T * L.dpp;
     L.offV = o;  o += L.T * kVS;
     L.offP = o;  o += L.T * L.T;
+    L.offW = o;  o += L.T;
     L.total = o;
     return L;
 }
@@ -50,6 +57,13 @@ __device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int ro
                          float *sX, float *sSq, float *out) {
     const int tid = threadIdx.x;
     const int dk = sh.dk;
+    if (sh.phi == kIdentity) {  // raw rows (retention's q and k)
+        for (int e = tid; e < L.T * dk; e += kThreads) {
+            int r = e / dk, c = e - r * dk;
+            out[r * L.dpp + c] = r < nvalid ? load_as_f32(X, (size_t)(row0 + r) * dk + c) : 0.f;
+        }
+        return;
+    }
     if (sh.phi == kElu1) {
         for (int e = tid; e < L.T * dk; e += kThreads) {
             int r = e / dk, c = e - r * dk;
@@ -100,6 +114,10 @@ __device__ void value_tile(const Shape &sh, const GenLayout &L, const T *V, int 
     }
 }
 
+// lambda^x for x >= 0 from l2 = log2(lambda): exactly 1 at x = 0 (also for
+// lambda = 0), accurate exp2f otherwise.
+__device__ __forceinline__ float decay_pow(float l2, float x) { return x == 0.f ? 1.f : exp2f(x * l2); }
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
     extern __shared__ float smem[];
@@ -109,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
     const GenLayout L = gen_layout(dk, dp);
     float *sS = smem + L.offS, *sz = smem + L.offZ, *sX = smem + L.offX, *sSq = smem + L.offSq;
     float *sPQ = smem + L.offPQ, *sPK = smem + L.offPK, *sV = smem + L.offV, *sP = smem + L.offP;
+    float *sW = smem + L.offW;
     const int tid = threadIdx.x;
 
     const int nslab = (dv + kVS - 1) / kVS;
@@ -121,6 +140,8 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
     const int c_begin = seg * sg.seg_chunks;
     const int c_end = min(sg.n_chunks, c_begin + sg.seg_chunks);
     const int N = sh.N, C = sg.chunk;
+    const bool ret = sh.ret != 0;  // retention
+    const float l2 = ret ? log2f(sh.gamma[bh % sh.H]) : 0.f;
 
     const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
     const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * dk;
@@ -154,9 +175,14 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
                     if (e < L.T * kVS) {
                         int i = e / kVS, j = e - i * kVS;
                         const float *pq = sPQ + i * L.dpp;
-                        for (int f = 0; f < dp; ++f) {
-                            acc[r] += pq[f] * sS[f * kVS + j];
-                            den[r] += pq[f] * sz[f];
+                        if (ret) {
+                            for (int f = 0; f < dp; ++f) acc[r] += pq[f] * sS[f * kVS + j];
+                            acc[r] *= decay_pow(l2, (float)(qt + i + 1));
+                        } else {
+                            for (int f = 0; f < dp; ++f) {
+                                acc[r] += pq[f] * sS[f * kVS + j];
+                                den[r] += pq[f] * sz[f];
+                            }
                         }
                     }
                 }
@@ -174,6 +200,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
                             if (kt + t <= qt + i) {
                                 const float *pq = sPQ + i * L.dpp, *pk = sPK + t * L.dpp;
                                 for (int f = 0; f < dp; ++f) p += pq[f] * pk[f];
+                                if (ret) p *= decay_pow(l2, (float)(qt + i - kt - t));
                             }
                             sP[e] = p;
                         }
@@ -198,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
                     if (e < L.T * kVS) {
                         int i = e / kVS, j = e - i * kVS;
                         if (i < nq && j < vw)
-                            store_from_f32(Os, (size_t)(t0 + qt + i) * dv + j0 + j, acc[r] / den[r]);
+                            store_from_f32(Os, (size_t)(t0 + qt + i) * dv + j0 + j, ret ? acc[r] : acc[r] / den[r]);
                     }
                 }
                 __syncthreads();  // sPQ is reused by the next query tile
@@ -206,21 +233,33 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
         }
         if constexpr (MODE != kModeRead) {
             // carry the state past this chunk: S += phiK^T V, z += phiK^T 1
+            // (retention: S = lambda^Lc S + sum_t lambda^(Lc-1-t) phiK_t v_t^T)
             for (int kt = 0; kt < Lc; kt += L.T) {
                 const int nk = min(L.T, Lc - kt);
                 phi_tile(sh, L, Ks, t0 + kt, nk, sX, sSq, sPK);
                 value_tile(sh, L, Vs, t0 + kt, nk, j0, vw, sV);
+                if (ret && tid < L.T) sW[tid] = tid < nk ? decay_pow(l2, (float)(Lc - 1 - kt - tid)) : 0.f;
                 __syncthreads();
-                for (int e = tid; e < dp * kVS; e += kThreads) {
-                    int f = e / kVS, j = e - f * kVS;
-                    float s = sS[e];
-                    for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f] * sV[t * kVS + j];
-                    sS[e] = s;
-                }
-                for (int f = tid; f < dp; f += kThreads) {
-                    float s = sz[f];
-                    for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f];
-                    sz[f] = s;
+                if (ret) {
+                    const float carry = kt == 0 ? decay_pow(l2, (float)Lc) : 1.f;
+                    for (int e = tid; e < dp * kVS; e += kThreads) {
+                        int f = e / kVS, j = e - f * kVS;
+                        float s = carry * sS[e];
+                        for (int t = 0; t < L.T; ++t) s += sW[t] * sPK[t * L.dpp + f] * sV[t * kVS + j];
+                        sS[e] = s;
+                    }
+                } else {
+                    for (int e = tid; e < dp * kVS; e += kThreads) {
+                        int f = e / kVS, j = e - f * kVS;
+                        float s = sS[e];
+                        for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f] * sV[t * kVS + j];
+                        sS[e] = s;
+                    }
+                    for (int f = tid; f < dp; f += kThreads) {
+                        float s = sz[f];
+                        for (int t = 0; t < L.T; ++t) s += sPK[t * L.dpp + f];
+                        sz[f] = s;
+                    }
                 }
                 __syncthreads();
             }
@@ -233,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
             int f = e / kVS, j = e - f * kVS;
             if (j < vw) Sd[(size_t)f * dv + j0 + j] = sS[e];
         }
-        if (slab == 0) {
+        if (slab == 0 && a.st.z_dst) {
             float *zd = a.st.z_dst + bh * a.st.zdst_slice + seg * a.st.zdst_seg;
             for (int f = tid; f < dp; f += kThreads) zd[f] = sz[f];
         }
@@ -243,11 +282,15 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
 // Exclusive prefix over the P segment states of each slice, in place:
 //   slot s <- S_in + sum_{s' < s} slot s'   and   S_out <- S_in + sum_s slot s.
 // With total_to_slot0, slot 0 <- sum_s slot s instead (non-causal total).
+// Retention (gamma set): the state decays across each segment, so the
+// running value is acc <- lambda^(len s) acc + slot s (Horner form), with
+// len s the tokens of segment s (seg_tokens, the last one shorter).
 // One thread per state element; the segment order is fixed, so repeated runs
 // give identical bits.
 __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz, float *ws_S, float *ws_z,
                                                    const float *S_in, const float *z_in, float *S_out,
-                                                   float *z_out, int total_to_slot0) {
+                                                   float *z_out, int total_to_slot0, const float *gamma, int H,
+                                                   int seg_tokens, int N) {
     const int per = nS + nz;
     const int blocks_per_slice = (per + kThreads - 1) / kThreads;
     const int bh = blockIdx.x / blocks_per_slice;
@@ -270,6 +313,16 @@ __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz
         if (total_to_slot0) {
 #pragma unroll
             for (int b = 0; b < kB; ++b) acc += d[b];
+        } else if (gamma) {
+            const float l2 = log2f(gamma[bh % H]);
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                if (s0 + b < P) {
+                    slots[(size_t)(s0 + b) * n] = acc;
+                    const int len = min(seg_tokens, N - (s0 + b) * seg_tokens);
+                    acc = decay_pow(l2, (float)len) * acc + d[b];
+                }
+            }
         } else {
 #pragma unroll
             for (int b = 0; b < kB; ++b) {
@@ -306,11 +359,14 @@ hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev) {
 }
 
 hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in, const float *z_in,
-                       float *S_out, float *z_out, bool total_to_slot0, hipStream_t stream, KEvents ev) {
-    const int nS = sh.dp * sh.dv, nz = sh.dp;
+                       float *S_out, float *z_out, bool total_to_slot0, hipStream_t stream, KEvents ev,
+                       int seg_tokens) {
+    const int nS = sh.dp * sh.dv, nz = sh.ret ? 0 : sh.dp;  // retention carries no z
     const int bps = (nS + nz + kThreads - 1) / kThreads;
     return launch_kernel_ev(k_scan, dim3((unsigned)((size_t)sh.BH * bps)), dim3(kThreads), 0, stream, ev, sh.BH, P,
-                            nS, nz, ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0);
+                            nS, nz, ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0,
+                            sh.ret ? sh.gamma : nullptr, sh.H,
+                            seg_tokens, sh.N);
 }
 
 }  // namespace la

@@ -10,7 +10,7 @@
 
 namespace la {
 
-enum Phi : int { kElu1 = 0, kFavor = 1 };
+enum Phi : int { kElu1 = 0, kFavor = 1, kIdentity = 2 };
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // What one launch of the chunked kernels does over its token range.
@@ -31,6 +31,12 @@ struct Shape {
     int m;        // FAVOR+ features (0 for ELU+1)
     const float *W;  // FAVOR+ rows [m, dk] (device)
     int dtype;    // Dtype of Q/K/V/O
+    // Retention (decayed, unnormalised): ret = 1 and the decay of head h is
+    // gamma[h] (device, [H]; slice b*H + h uses gamma[h]).  Normalised kernel
+    // attention: ret = 0, gamma = NULL.
+    int ret;
+    const float *gamma;
+    int H;
 };
 
 // Token ranges split into segments of whole chunks; one workgroup column per segment.
@@ -114,7 +120,7 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in,
                        const float *z_in, float *S_out, float *z_out, bool total_to_slot0,
-                       hipStream_t stream, KEvents ev = {});
+                       hipStream_t stream, KEvents ev = {}, int seg_tokens = 0);
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o,
                          float *S, float *z, hipStream_t stream);
 // bf16 MFMA path; returns hipErrorNotSupported when the shape has no MFMA variant.

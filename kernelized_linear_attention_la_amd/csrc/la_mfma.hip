@@ -143,8 +143,11 @@ struct Cfg {
     static constexpr int THREADS = 64 * NW;
     static constexpr int DP = F ? 256 : DK;      // feature dimension
     static constexpr int M = F ? 256 : 0;
-    static constexpr int NJ = DV / 16 + 1;       // value column blocks incl. the normaliser block
-    static constexpr int DVA = DV + 16;
+    // Retention ("Story of Attention Part 5", sections 4 and 6): raw q and k,
+    // decay per head, no normaliser.
+    static constexpr bool RET = PHI == kIdentity;
+    static constexpr int NJ = DV / 16 + (RET ? 0 : 1);  // value column blocks incl. the normaliser block
+    static constexpr int DVA = DV + (RET ? 0 : 16);
     static constexpr int KBT = C / 32;           // 32-token k-blocks per chunk
     static constexpr int KBF = DP / 32;          // 32-feature k-blocks
     static constexpr int KBD = DK / 32;          // 32-wide k-blocks of the raw input (FAVOR+ projection)
@@ -205,6 +208,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     constexpr bool DO_OUT = MODE != kModeState;  // some chunk of the launch writes outputs
     constexpr bool DO_STATE = MODE != kModeRead;
     constexpr bool NEED_K = MODE != kModeRead;
+    constexpr bool RET = G::RET;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -217,6 +221,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     const int bh = blockIdx.x / sg.P;
     const int c_begin = seg * sg.seg_chunks;
     const int c_end = min(sg.n_chunks, c_begin + sg.seg_chunks);
+
+    // retention decay lambda = gamma[h]; lambda^x = exp2(x log2 lambda), 1 at x = 0
+    const float l2 = RET ? log2f(a.sh.gamma[bh % a.sh.H]) : 0.f;
+    auto dpow = [&](float x) { return x == 0.f ? 1.f : __builtin_amdgcn_exp2f(x * l2); };
 
     const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * DK;
     const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * DK;
@@ -328,8 +336,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             if constexpr (G::F) {  // raw rows; the feature map runs on the matrix cores
                 *reinterpret_cast<uint4 *>(&sm.XK[t * G::RX + 8 * c8]) = p.raw[i].u;
             } else {
-                // ELU+1 on the way in; tokens past the end get phi = 0, not phi(0) = 1
-                uint4 ph = elu1_bf16x8(p.raw[i].u);
+                // ELU+1 on the way in (retention: raw keys); tokens past the end get phi = 0, not phi(0) = 1
+                uint4 ph;
+                if constexpr (RET) ph = p.raw[i].u;
+                else ph = elu1_bf16x8(p.raw[i].u);
                 if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
                 *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
             }
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // normaliser block of V_aug: column d_v is 1 for every token, the other
     // 15 columns 0.  Tokens past the end of the sequence have phi(k) = 0, so
     // their 1 contributes nothing.
-    if constexpr (NEED_K) {
+    if constexpr (NEED_K && !RET) {
         for (int u = tid; u < C * 2; u += G::THREADS) {
             const int t = u >> 1, half = u & 1;
             const uint32_t first = half == 0 ? 0x3f80u : 0u;
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         Op8 phq[KBF];
         if constexpr (OUT && !G::F) {
 #pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = RET ? p.q[kb].u : elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
         }
         block_sync_lds();
         fetch(p, step + DEPTH);
@@ -458,6 +468,29 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             f32x4 acc[NJ];
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) acc[nb] = zero4();
+            // phi(Q) S_aug with the state carried into this chunk
+            auto inter = [&]() {
+#pragma unroll
+                for (int kf = 0; kf < KBF; ++kf) {
+#pragma unroll
+                    for (int nb = 0; nb < NJ; ++nb) {
+                        Op8 sb;
+                        sb.u = sm.STB[nb][kf][lane];
+                        acc[nb] = mfma(phq[kf], sb, acc[nb]);
+                    }
+                }
+            };
+            if constexpr (RET) {
+                // retention reads the carried state first, scaled per query row by
+                // lambda^(i+1) (the Lambda of the blockwise form), then adds the intra part
+                inter();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float r = dpow((float)(16 * qb + 4 * g + e + 1));
+#pragma unroll
+                    for (int nb = 0; nb < NJ; ++nb) acc[nb][e] *= r;
+                }
+            }
             if constexpr (INTRA) {
                 // (P (.) M) V_aug over the key blocks up to the diagonal
 #pragma unroll
@@ -481,6 +514,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                                     for (int e = 0; e < 4; ++e)
                                         if (4 * g + e > c16) p[h][e] = 0.f;
                                 }
+                                if constexpr (RET) {  // decay mask lambda^(query - key)
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const int d = 16 * (qb - jb) + c16 - 4 * g - e;
+                                        p[h][e] *= d >= 0 ? dpow((float)d) : 0.f;
+                                    }
+                                }
                             }
                         }
                         Op8 pa;
@@ -492,26 +532,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     }
                 }
             }
-            // phi(Q) S_aug with the state carried into this chunk
-#pragma unroll
-            for (int kf = 0; kf < KBF; ++kf) {
-#pragma unroll
-                for (int nb = 0; nb < NJ; ++nb) {
-                    Op8 sb;
-                    sb.u = sm.STB[nb][kf][lane];
-                    acc[nb] = mfma(phq[kf], sb, acc[nb]);
-                }
-            }
-            // epilogue: divide by the normaliser column, round, stage, store 16 B per lane
+            if constexpr (!RET) inter();
+            // epilogue: divide by the normaliser column (retention: none), round,
+            // stage, store 16 B per lane
             float rden[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rden[e] = __builtin_amdgcn_rcpf(__shfl(acc[NJ - 1][e], lane & 48, 64));
+            for (int e = 0; e < 4; ++e)
+                rden[e] = RET ? 1.f : __builtin_amdgcn_rcpf(__shfl(acc[NJ - 1][e], lane & 48, 64));
             uint16_t *so = sm.O[w];
 #pragma unroll
-            for (int nb = 0; nb < NJ - 1; ++nb)
+            for (int nb = 0; nb < DV / 16; ++nb)
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
-                    const uint32_t two = cvt2(acc[nb][e] * rden[e], acc[nb][e + 1] * rden[e + 1]);
+                    const uint32_t two = RET ? cvt2(acc[nb][e], acc[nb][e + 1])
+                                             : cvt2(acc[nb][e] * rden[e], acc[nb][e + 1] * rden[e + 1]);
                     so[(4 * g + e) * RO + 16 * nb + c16] = static_cast<uint16_t>(two);
                     so[(4 * g + e + 1) * RO + 16 * nb + c16] = static_cast<uint16_t>(two >> 16);
                 }
@@ -528,14 +562,37 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
 
         // ---------------- state update S_aug += phi(K_c)^T V_aug
+        // (retention: S = lambda^Lc S + sum_t lambda^(Lc-1-t) phi(k_t) v_t^T over
+        // the Lc tokens of the chunk; the key weights scale the operand slots)
         if constexpr (DO_STATE) {
+            const int Lc = min(C, N - t0);
+            float kw[RET ? KBT : 1][8];
+            if constexpr (RET) {
+#pragma unroll
+                for (int kt = 0; kt < KBT; ++kt)
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl) {  // slot sl <-> token 32kt + 16(sl/4) + 4g + sl%4
+                        const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
+                        kw[kt][sl] = t < Lc ? dpow((float)(Lc - 1 - t)) : 0.f;
+                    }
+                const float carry = dpow((float)Lc);
+#pragma unroll
+                for (int q = 0; q < FBW; ++q)
+#pragma unroll
+                    for (int nb = 0; nb < NJ; ++nb) S[q][nb] *= carry;
+            }
 #pragma unroll
             for (int q = 0; q < FBW; ++q) {
                 const int fb = w + NW * q;
                 if (fb < FB) {
 #pragma unroll
                     for (int kt = 0; kt < KBT; ++kt) {
-                        const Op8 ka = token_operand<RK>(sm.K, kt, 16 * fb, lane);
+                        Op8 ka = token_operand<RK>(sm.K, kt, 16 * fb, lane);
+                        if constexpr (RET) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw[kt][2 * j], hi_bf16(ka.u32[j]) * kw[kt][2 * j + 1]);
+                        }
 #pragma unroll
                         for (int nb = 0; nb < NJ; ++nb)
                             S[q][nb] = mfma(ka, token_operand<RV>(sm.V, kt, 16 * nb, lane), S[q][nb]);
@@ -580,7 +637,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // slot, so their loads read zeros and their stores are dropped, moving
     // no bytes.
     auto piece_off = [&](int fb, int nb) {
-        return nb == NJ - 1 && c16 != 0 ? SLOT * 4 : ((fb * NJ + nb) * 64 + lane) * 16;
+        return !RET && nb == NJ - 1 && c16 != 0 ? SLOT * 4 : ((fb * NJ + nb) * 64 + lane) * 16;
     };
     auto store_slot = [&](int i) {  // this lane's pieces of S into slot i
         const auto r = slot_rsrc(i, true);
@@ -643,16 +700,23 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         f32x4 buf[GD][PER];
 #pragma unroll
         for (int d = 0; d < GD; ++d) load_slot(buf[d], d, d == 0 ? has_in : d <= seg);
-        auto add_slot = [&](const f32x4 *src) {
+        // retention: the state decays across each segment, so slot j enters as
+        // S = lambda^(tokens of segment j-1) S + slot j (Horner form)
+        auto seg_len = [&](int k) { return min(sg.seg_chunks * C, N - k * sg.seg_chunks * C); };
+        auto add_slot = [&](const f32x4 *src, int j) {
+            const float mul = RET && j >= 1 && j <= seg ? dpow((float)seg_len(j - 1)) : 1.f;
 #pragma unroll
             for (int q = 0; q < FBW; ++q)
 #pragma unroll
-                for (int nb = 0; nb < NJ; ++nb) S[q][nb] += src[q * NJ + nb];
+                for (int nb = 0; nb < NJ; ++nb) {
+                    if constexpr (RET) S[q][nb] = S[q][nb] * mul + src[q * NJ + nb];
+                    else S[q][nb] += src[q * NJ + nb];
+                }
         };
         for (int i = 0; i <= seg; i += GD) {  // a slot read as zeros adds exactly nothing
 #pragma unroll
             for (int d = 0; d < GD; ++d) {
-                add_slot(buf[d]);
+                add_slot(buf[d], i + d);
                 load_slot(buf[d], i + d + GD, i + d + GD <= seg);
             }
         }
@@ -669,6 +733,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             float *zo = a.fu.z_out + (size_t)bh * G::DP;
             f32x4 own[PER];
             load_slot(own, P, true);
+            const float tail = RET ? dpow((float)seg_len(seg)) : 1.f;  // decay across the own segment
 #pragma unroll
             for (int q = 0; q < FBW; ++q) {
                 const int fb = w + NW * q;
@@ -678,7 +743,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int f = 16 * fb + 4 * g + e, j = 16 * nb + c16;
-                            const float tot = S[q][nb][e] + own[q * NJ + nb][e];
+                            const float tot = RET ? tail * S[q][nb][e] + own[q * NJ + nb][e]
+                                                  : S[q][nb][e] + own[q * NJ + nb][e];
                             if (j < DV) So[(size_t)f * DV + j] = tot;
                             else if (j == DV) zo[f] = tot;
                         }
@@ -790,11 +856,19 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 template <int DK, int DV, int C, int PHI>
 hipError_t launch_variant(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.sh.BH * a.sg.P)), block(C / 16 * 64);
-    switch (a.mode) {
-        case kModeState: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeState>, grid, block, 0, st, ev, a);
-        case kModeCausal: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeCausal>, grid, block, 0, st, ev, a);
-        case kModeFused: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFused>, grid, block, 0, st, ev, a);
-        default: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeRead>, grid, block, 0, st, ev, a);
+    if constexpr (PHI == kIdentity) {  // retention: causal only
+        if (a.mode == kModeFused)
+            return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFused>, grid, block, 0, st, ev, a);
+        if (a.mode == kModeCausal)
+            return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeCausal>, grid, block, 0, st, ev, a);
+        return hipErrorNotSupported;
+    } else {
+        switch (a.mode) {
+            case kModeState: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeState>, grid, block, 0, st, ev, a);
+            case kModeCausal: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeCausal>, grid, block, 0, st, ev, a);
+            case kModeFused: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFused>, grid, block, 0, st, ev, a);
+            default: return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeRead>, grid, block, 0, st, ev, a);
+        }
     }
 }
 
@@ -802,7 +876,8 @@ hipError_t launch_variant(const FwdArgs &a, hipStream_t st, KEvents ev) {
 
 bool mfma_supported(const Shape &sh, int chunk) {
     if (sh.dtype != kBF16) return false;
-    if (sh.phi == kElu1)
+    if ((sh.phi == kIdentity) != (sh.ret != 0)) return false;  // identity map <=> retention here
+    if (sh.phi == kElu1 || sh.phi == kIdentity)
         return ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128)) && (chunk == 64 || chunk == 128);
     return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
 }
@@ -812,6 +887,13 @@ hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const int C = a.sg.chunk;
     if (!mfma_supported(s, C)) return hipErrorNotSupported;
     if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st, ev);
+    if (s.phi == kIdentity) {
+        if (s.dk == 64)
+            return C == 64 ? launch_variant<64, 64, 64, kIdentity>(a, st, ev)
+                           : launch_variant<64, 64, 128, kIdentity>(a, st, ev);
+        return C == 64 ? launch_variant<128, 128, 64, kIdentity>(a, st, ev)
+                       : launch_variant<128, 128, 128, kIdentity>(a, st, ev);
+    }
     if (s.dk == 64)
         return C == 64 ? launch_variant<64, 64, 64, kElu1>(a, st, ev) : launch_variant<64, 64, 128, kElu1>(a, st, ev);
     return C == 64 ? launch_variant<128, 128, 64, kElu1>(a, st, ev) : launch_variant<128, 128, 128, kElu1>(a, st, ev);

@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_HERE, "_lib", "liblinattn.so")
 
 LA_OK = 0
 LA_F32, LA_BF16 = 0, 1
-LA_PHI_ELU1, LA_PHI_FAVOR = 0, 1
+LA_PHI_ELU1, LA_PHI_FAVOR, LA_PHI_IDENTITY = 0, 1, 2
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_UNSUPPORTED",
                 5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
             "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
-            "la_decode_step")
+            "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 
 
@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
                                                       ctypes.POINTER(LaKernelEvents)]
         L.la_decode_step.restype = i
         L.la_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.la_forward_retention_chunked.restype = i
+        L.la_forward_retention_chunked.argtypes = [P, vp, i, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                   ctypes.POINTER(LaKernelEvents)]
+        L.la_retention_decode_step.restype = i
+        L.la_retention_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -140,6 +145,8 @@ def _problem_of(q, v, phi, W):
         if W.dtype != torch.float32 or not W.is_contiguous() or not W.is_cuda or W.dim() != 2 or W.shape[1] != dk:
             raise ValueError("W must be a contiguous float32 device tensor [m, d_k]")
         return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_FAVOR, W.shape[0], W.data_ptr())
+    if phi in ("identity", LA_PHI_IDENTITY):
+        return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_IDENTITY, 0, 0)
     return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_ELU1, 0, 0)
 
 
@@ -240,4 +247,73 @@ def la_decode_step(q, k, v, S, z, phi="elu1", W=None, out=None, stream=None):
     st = lib().la_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z),
                               _stream(stream))
     _raise(st, "la_decode_step")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# retention (decayed, unnormalised)
+# ---------------------------------------------------------------------------
+def _check_gamma(gamma, H, device):
+    if not isinstance(gamma, torch.Tensor) or gamma.dtype != torch.float32 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 device tensor [H]")
+    if tuple(gamma.shape) != (H,) or gamma.device != device:
+        raise ValueError(f"gamma must have shape [{H}] on the inputs' device")
+
+
+def _state_only(S, B, H, dp, dv, device, what):
+    if S is None:
+        return None
+    if S.dtype != torch.float32 or not S.is_contiguous() or tuple(S.shape) != (B, H, dp, dv) or S.device != device:
+        raise ValueError(f"{what}: expected a contiguous float32 [{B},{H},{dp},{dv}] tensor on the inputs' device")
+    return S
+
+
+def la_forward_retention_chunked(q, k, v, gamma, chunk=64, phi="identity", W=None, S_in=None, S_out=None, out=None,
+                                 workspace=None, stream=None, events=None):
+    """Retention (decayed, unnormalised) forward in the blockwise form; returns O.
+
+    gamma: float32 device tensor [H] of per-head decays in (0, 1].
+    S_out, when given, receives the final state (it may be S_in).
+    """
+    _check_qkv(q, k, v)
+    p = _problem_of(q, v, phi, W)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    _check_gamma(gamma, H, q.device)
+    S_in = _state_only(S_in, B, H, dp, dv, q.device, "initial state")
+    S_out = _state_only(S_out, B, H, dp, dv, q.device, "final state")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    nbytes = la_workspace_bytes(p, chunk)
+    if workspace is None and nbytes > 0:
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_forward_retention_chunked(ctypes.byref(p), _ptr(gamma), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(out), _ptr(S_in), _ptr(S_out), _ptr(workspace), wsb,
+                                            _stream(stream), None if events is None else ctypes.byref(events))
+    _raise(st, "la_forward_retention_chunked")
+    return out
+
+
+def la_retention_decode_step(q, k, v, S, gamma, phi="identity", W=None, out=None, stream=None):
+    """One retention step; q, k [B,H,1,d_k] (or [B,H,d_k]); v [B,H,1,d_v]. Updates S in place; returns o."""
+    if q.dim() == 3:
+        q, k, v = q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2)
+    _check_qkv(q, k, v)
+    if q.shape[2] != 1:
+        raise ValueError("decode takes one token per slice")
+    p = _problem_of(q, v, phi, W)
+    B, H, _, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    _check_gamma(gamma, H, q.device)
+    S = _state_only(S, B, H, dp, dv, q.device, "state")
+    if S is None:
+        raise ValueError("decode needs the state S")
+    if out is None:
+        out = torch.empty((B, H, 1, dv), dtype=q.dtype, device=q.device)
+    st = lib().la_retention_decode_step(ctypes.byref(p), _ptr(gamma), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S),
+                                        _stream(stream))
+    _raise(st, "la_retention_decode_step")
     return out

@@ -129,3 +129,39 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 4)
     with pytest.raises(TypeError):
         linattn.la_forward_causal_chunked(q, q, q, 16)
+
+
+def test_retention_validation():
+    L = linattn.lib()
+    pid = _p(phi=linattn.LA_PHI_IDENTITY)
+    g = FAKE
+
+    def ret(p, gamma=g, chunk=64, Q=FAKE, O=FAKE, Si=None, So=None, ws=None, wsb=0):
+        return L.la_forward_retention_chunked(ctypes.byref(p), gamma, chunk, Q, FAKE, FAKE, O, Si, So, ws, wsb,
+                                              None, None)
+
+    # the identity map has no normaliser: the normalised entry points refuse it
+    assert _causal(pid) == 4
+    assert L.la_forward_noncausal(ctypes.byref(pid), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 4
+    assert L.la_decode_step(ctypes.byref(_p(N=1, phi=linattn.LA_PHI_IDENTITY)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            None) == 4
+    # retention: decays required and 4-byte aligned, chunk checked, workspace checked
+    assert ret(pid, gamma=None) == 1
+    assert ret(pid, gamma=ctypes.c_void_p(0x100002)) == 5
+    assert ret(pid, chunk=48) == 4
+    assert ret(pid, Q=None) == 1
+    assert ret(pid, Si=MIS) == 5
+    big = _p(B=1, H=1, N=8192, phi=linattn.LA_PHI_IDENTITY)
+    need = linattn.la_workspace_bytes(big, 64)
+    assert need > 0
+    assert ret(big, ws=None, wsb=0) == 6
+    assert ret(big, ws=FAKE, wsb=need - 1) == 6
+    # decode
+    p1 = _p(N=1, phi=linattn.LA_PHI_IDENTITY)
+    assert L.la_retention_decode_step(ctypes.byref(p1), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.la_retention_decode_step(ctypes.byref(p1), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert L.la_retention_decode_step(ctypes.byref(pid), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    # the workspace query covers retention plans of every feature map
+    for phi, m, W in ((linattn.LA_PHI_ELU1, 0, 0), (linattn.LA_PHI_FAVOR, 256, 0x1000)):
+        pp = _p(B=1, H=2, N=4096, phi=phi, m=m, W_ptr=W)
+        assert linattn.la_workspace_bytes(pp, 64) > 0

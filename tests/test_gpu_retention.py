@@ -1,0 +1,198 @@
+"""GPU parity of retention (decayed, unnormalised linear attention) through the C ABI.
+
+la_forward_retention_chunked / la_retention_decode_step against the fp64
+oracle's retention functions (recurrent form), which tests/
+test_retention_oracle_pins.py pins to the pages' worked example and to the
+parallel and blockwise forms.  Tolerances as for the normalised path: 1e-4
+for fp32 storage, 2e-2 for bf16 storage with fp32 accumulation and state.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kernelized_linear_attention_la_amd import inputs
+from kernelized_linear_attention_la_amd import linattn as la
+from tests.parity import TOL_BF16, TOL_F32, row_rel_err, state_rel_err, tol_for, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(*a):
+    print("[retention]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _gam(g):
+    return torch.tensor(np.asarray(g, dtype=np.float32), device="cuda")
+
+
+def test_worked_example_through_gpu():
+    with open(os.path.join(GOLDEN, "t4_retnet_worked_example.json")) as f:
+        g = json.load(f)
+    _say("RetNet worked example n=4 d=4 gamma=0.5")
+    Q, K, V = (torch.tensor(g[x], dtype=torch.float32).view(1, 1, 4, 4).cuda() for x in ("Q", "K", "V"))
+    gam = _gam([g["gamma"]])
+    for chunk in (16, 32, 64, 128):
+        S = torch.zeros(1, 1, 4, 4, device="cuda")
+        O = la.la_forward_retention_chunked(Q, K, V, gam, chunk, S_out=S)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(O.cpu().numpy()[0, 0], np.array(g["output_parallel"]), rtol=1e-6, atol=1e-6)
+    for n in (1, 2, 3):
+        S = torch.zeros(1, 1, 4, 4, device="cuda")
+        la.la_forward_retention_chunked(Q[:, :, :n].contiguous(), K[:, :, :n].contiguous(), V[:, :, :n].contiguous(),
+                                        gam, 64, S_out=S)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(S.cpu().numpy()[0, 0], np.array(g[f"S_{n}"]), rtol=1e-6, atol=1e-6)
+    # the recurrent step of the page, token by token
+    S = torch.zeros(1, 1, 4, 4, device="cuda")
+    for i in range(4):
+        o = la.la_retention_decode_step(Q[:, :, i], K[:, :, i], V[:, :, i], S, gam)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(o.cpu().numpy()[0, 0, 0], np.array(g["output_parallel"][i]), rtol=1e-6, atol=1e-6)
+
+
+CASES = [
+    # (B, H, N, dk, dv, dtype, phi, m, chunk, with_state)
+    (1, 2, 256, 64, 64, "f32", "identity", 0, 64, False),
+    (2, 3, 200, 40, 24, "f32", "identity", 0, 32, True),
+    (1, 1, 517, 128, 96, "f32", "identity", 0, 16, True),
+    (1, 2, 300, 64, 64, "f32", "elu1", 0, 64, True),
+    (2, 1, 77, 16, 8, "f32", "favor", 24, 32, False),
+    (1, 2, 333, 64, 64, "bf16", "elu1", 0, 64, False),
+    # bf16 matrix-core retention: every (d, chunk) pair, one and several segments, ragged tails, tiny N
+    (1, 1, 13, 64, 64, "bf16", "identity", 0, 64, False),
+    (1, 2, 333, 64, 64, "bf16", "identity", 0, 64, True),
+    (2, 2, 1000, 128, 128, "bf16", "identity", 0, 64, True),
+    (1, 3, 777, 64, 64, "bf16", "identity", 0, 128, False),
+    (1, 2, 300, 128, 128, "bf16", "identity", 0, 128, True),
+    (1, 1, 1, 128, 128, "bf16", "identity", 0, 128, False),
+    (1, 1, 5000, 64, 64, "bf16", "identity", 0, 64, False),
+    # single-pass hand-off with segments of three chunks and a shorter last one
+    (4, 16, 700, 64, 64, "bf16", "identity", 0, 64, True),
+    (8, 16, 768, 128, 128, "bf16", "identity", 0, 128, False),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)),
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}dk{c[3]}dv{c[4]}{c[5]}{c[6]}{c[8]}{'S' if c[9] else ''}"
+                              for c in CASES])
+def test_shapes_against_oracle(ci):
+    B, H, N, dk, dv, dtype, phi, m, chunk, with_state = CASES[ci]
+    _say("case", CASES[ci])
+    scale = (dk ** -0.25) if phi == "favor" else (dk ** -0.5)
+    fi = inputs.custom_inputs(500 + ci, B, H, N, dk, dv, scale=scale, dtype=dtype, phi=phi, m=m)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    W = torch.from_numpy(fi.W).cuda() if fi.W is not None else None
+    gam = inputs.retention_decays(H)
+    dp = m if phi == "favor" else dk
+    S0 = (np.random.default_rng(ci).standard_normal((B, H, dp, dv)) * 0.1).astype(np.float32) if with_state else None
+    S_in = torch.from_numpy(S0).cuda() if with_state else None
+    S = torch.zeros(B, H, dp, dv, device="cuda")
+    O = la.la_forward_retention_chunked(q, k, v, _gam(gam), chunk, phi=phi, W=W, S_in=S_in, S_out=S)
+    ref, Sref = oracle.retention_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, gam.astype(np.float64), W=fi.W,
+                                           S_in=S0)
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    e = row_rel_err(to_f64(O), ref)
+    assert e < tol, e
+    es = state_rel_err(to_f64(S), Sref)
+    assert es < tol, es
+
+
+def test_handoff_in_place_state_and_chunk_invariance():
+    """forward(0..M) then forward(M..N) from its state (S_in aliasing S_out) == forward(0..N), for each chunk."""
+    for dtype, d in (("f32", 64), ("bf16", 64), ("bf16", 128)):
+        B, H, N = 2, 2, 700
+        fi = inputs.custom_inputs(42, B, H, N, d, d, scale=d ** -0.5, dtype=dtype)
+        q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+        gam = inputs.retention_decays(H)
+        ref, Sref = oracle.retention_recurrent("identity", fi.Q.f32, fi.K.f32, fi.V.f32, gam.astype(np.float64))
+        tol = tol_for(dtype)
+        for chunk in (16, 32, 64, 128):
+            _say("chunk invariance", dtype, d, chunk)
+            O = la.la_forward_retention_chunked(q, k, v, _gam(gam), chunk)
+            torch.cuda.synchronize()
+            assert row_rel_err(to_f64(O), ref) < tol, (dtype, d, chunk)
+        for M in (1, 64, 301):
+            _say("handoff", dtype, d, M)
+            S = torch.zeros(B, H, d, d, device="cuda")
+            O1 = la.la_forward_retention_chunked(q[:, :, :M].contiguous(), k[:, :, :M].contiguous(),
+                                                 v[:, :, :M].contiguous(), _gam(gam), 64, S_out=S)
+            O2 = la.la_forward_retention_chunked(q[:, :, M:].contiguous(), k[:, :, M:].contiguous(),
+                                                 v[:, :, M:].contiguous(), _gam(gam), 64, S_in=S, S_out=S)
+            torch.cuda.synchronize()
+            assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < tol
+            assert state_rel_err(to_f64(S), Sref) < tol
+
+
+def test_decode_matches_forward_and_oracle():
+    B, H, N, d = 3, 4, 40, 64
+    for dtype in ("f32", "bf16"):
+        _say("decode", dtype)
+        fi = inputs.custom_inputs(77, B, H, N, d, d, scale=d ** -0.5, dtype=dtype)
+        q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+        gam = inputs.retention_decays(H)
+        ref, Sref = oracle.retention_recurrent("identity", fi.Q.f32, fi.K.f32, fi.V.f32, gam.astype(np.float64))
+        S = torch.zeros(B, H, d, d, device="cuda")
+        outs = []
+        for i in range(N):
+            outs.append(la.la_retention_decode_step(q[:, :, i:i + 1].contiguous(), k[:, :, i:i + 1].contiguous(),
+                                                    v[:, :, i:i + 1].contiguous(), S, _gam(gam)))
+        torch.cuda.synchronize()
+        tol = tol_for(dtype)
+        assert row_rel_err(to_f64(torch.cat(outs, 2)), ref) < tol
+        assert state_rel_err(to_f64(S), Sref) < tol
+
+
+def test_deterministic_and_workspace_reuse():
+    B, H, N, d = 4, 16, 700, 64
+    fi = inputs.custom_inputs(88, B, H, N, d, d, scale=d ** -0.5, dtype="bf16")
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    gam = _gam(inputs.retention_decays(H))
+    p = la._problem_of(q, v, "identity", None)
+    ws = torch.zeros(la.la_workspace_bytes(p, 64), dtype=torch.uint8, device="cuda")
+    S0 = torch.zeros(B, H, d, d, device="cuda")
+    O0 = la.la_forward_retention_chunked(q, k, v, gam, 64, S_out=S0, workspace=ws)
+    for rep in range(3):
+        S = torch.zeros_like(S0)
+        O = la.la_forward_retention_chunked(q, k, v, gam, 64, S_out=S, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(O, O0) and torch.equal(S, S0), rep
+
+
+@pytest.mark.parametrize("name", ["ret_bf16_b4h8n2048d64_c64", "ret_bf16_b2h16n16384d128_c128"])
+def test_full_size_forward_sampled(name):
+    """Full-size workload in the launch configuration the benchmark times; the
+    oracle recomputes a seeded sample of (b, h) slices."""
+    wl = inputs.WORKLOADS[name]
+    _say("full size", name)
+    fi = inputs.forward_inputs(wl)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    gam = wl.gammas()
+    S = torch.zeros(wl.B, wl.H, wl.dk, wl.dv, device="cuda")
+    O = la.la_forward_retention_chunked(q, k, v, _gam(gam), wl.chunk, S_out=S)
+    torch.cuda.synchronize()
+    Oh, Sh = to_f64(O), to_f64(S)
+    rng = np.random.default_rng(1234)
+    picks = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(3)]
+    for b, h in picks:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref, Sref = oracle.retention_recurrent("identity", fi.Q.f32[sl], fi.K.f32[sl], fi.V.f32[sl],
+                                               np.array([gam[h]], dtype=np.float64))
+        assert row_rel_err(Oh[sl], ref) < TOL_BF16, (b, h)
+        assert state_rel_err(Sh[sl], Sref) < TOL_BF16, (b, h)
