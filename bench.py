@@ -43,10 +43,11 @@ def elem_bytes(dtype):
 
 
 def forward_alg_bytes(wl):
-    """Algorithmic HBM bytes of one causal forward: Q, K, V read once, O written once, final state written."""
+    """Algorithmic HBM bytes of one causal forward: Q, K, V read once, O written once, final state written
+    (retention carries no normaliser z)."""
     e = elem_bytes(wl.dtype)
     tok = wl.B * wl.H * wl.N
-    state = wl.B * wl.H * (wl.dprime * wl.dv + wl.dprime) * 4
+    state = wl.B * wl.H * (wl.dprime * wl.dv + (0 if wl.retention else wl.dprime)) * 4
     return tok * (2 * wl.dk + 2 * wl.dv) * e + state
 
 
@@ -58,7 +59,10 @@ def forward_alg_flops(wl):
     FAVOR+ projection 2 d_k m for q and for k.
     """
     C, dp, dv, dk = wl.chunk, wl.dprime, wl.dv, wl.dk
-    per = 4 * dp * dv + 2 * dp + (C + 1) * (dp + dv) + dv
+    if wl.retention:  # no normaliser: no z read, no division
+        per = 4 * dp * dv + (C + 1) * (dp + dv)
+    else:
+        per = 4 * dp * dv + 2 * dp + (C + 1) * (dp + dv) + dv
     if wl.phi == "favor":
         per += 4 * dk * wl.m
     return wl.B * wl.H * wl.N * per
@@ -121,9 +125,20 @@ def run_cpu_baseline(wl, fi, seconds):
     import oracle
     nthreads = oracle.num_threads()
     BH = wl.B * wl.H
+    if wl.retention:
+        # the sample runs over the first heads' slices; their decays, in slice order
+        gam_all = np.tile(wl.gammas().astype(np.float64), wl.B)
+
+        def run(Qs, Ks, Vs):  # Qs [1, n, N, d]: n slices as the "heads" of one batch row
+            return oracle.retention_recurrent(wl.phi, Qs, Ks, Vs, gam_all[:Qs.shape[1]], W=fi.W)
+        form = "retention recurrence"
+    else:
+        def run(Qs, Ks, Vs):
+            return oracle.causal_recurrent(wl.phi, Qs, Ks, Vs, fi.W)
+        form = "causal recurrence"
     # per-slice cost estimate from a 1-slice probe, then enough slices for `seconds`
     t0 = time.perf_counter()
-    oracle.causal_recurrent(wl.phi, fi.Q.f32[:1, :1], fi.K.f32[:1, :1], fi.V.f32[:1, :1], fi.W)
+    run(fi.Q.f32[:1, :1], fi.K.f32[:1, :1], fi.V.f32[:1, :1])
     t1 = time.perf_counter() - t0
     n_slices = int(max(1, min(BH, round(seconds * nthreads / max(t1, 1e-6)))))
     Qf = fi.Q.f32.reshape(1, BH, wl.N, wl.dk)[:, :n_slices]
@@ -132,14 +147,14 @@ def run_cpu_baseline(wl, fi, seconds):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.causal_recurrent(wl.phi, Qf, Kf, Vf, fi.W)
+        run(Qf, Kf, Vf)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 100000:
             break
     tokens = reps * n_slices * wl.N
     return {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"fp64 causal recurrence on {n_slices} of {BH} (b,h) slices x {wl.N} tokens, "
+            "sample": f"fp64 {form} on {n_slices} of {BH} (b,h) slices x {wl.N} tokens, "
                       f"{reps} pass(es), {el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
 
 
@@ -176,15 +191,18 @@ def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
-        return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}>"
+        return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}, {'true' if wl.retention else 'false'}>"
     mode = {"state": 0, "chunk": 1}[slot]
+    square = wl.dk == wl.dv and wl.dk in (64, 128) and wl.chunk in (64, 128)
     mfma = wl.dtype == "bf16" and (
-        (wl.phi == "elu1" and wl.dk == wl.dv and wl.dk in (64, 128) and wl.chunk in (64, 128)) or
-        (wl.phi == "favor" and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64))
+        (wl.phi == "elu1" and not wl.retention and square) or
+        (wl.phi == "identity" and wl.retention and square) or
+        (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64))
     if mfma:
         # the forward workloads all split into several segments per slice: the
         # matrix-core path runs them in one single-pass launch (mode 3)
-        return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {1 if wl.phi == 'favor' else 0}, 3>"
+        phi_id = {"elu1": 0, "favor": 1, "identity": 2}[wl.phi]
+        return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {phi_id}, 3>"
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"
 
 
@@ -218,6 +236,7 @@ def bench_forward(args, wl):
 
     q0, k0, v0 = to_dev(fi.Q), to_dev(fi.K), to_dev(fi.V)
     W = torch.from_numpy(fi.W).to(dev) if fi.W is not None else None
+    gam = torch.from_numpy(wl.gammas()).to(dev) if wl.retention else None
     set_bytes = 2 * q0.nbytes + k0.nbytes + 2 * v0.nbytes
     R = max(1, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(v0)) for _ in range(R)]
@@ -228,8 +247,12 @@ def bench_forward(args, wl):
 
     def step(i, stream=None, events=None):
         q, k, v, o = sets[i % R]
-        la.la_forward_causal_chunked(q, k, v, wl.chunk, phi=wl.phi, W=W, S_out=S, z_out=z, out=o,
-                                     workspace=ws, stream=stream, events=events)
+        if wl.retention:
+            la.la_forward_retention_chunked(q, k, v, gam, wl.chunk, phi=wl.phi, W=W, S_out=S, out=o, workspace=ws,
+                                            stream=stream, events=events)
+        else:
+            la.la_forward_causal_chunked(q, k, v, wl.chunk, phi=wl.phi, W=W, S_out=S, z_out=z, out=o,
+                                         workspace=ws, stream=stream, events=events)
 
     # the step sequence is launch-bound at small sizes: capture it in HIP graphs
     stream = torch.cuda.Stream()
@@ -424,7 +447,8 @@ def main():
         metric = "decode tokens/s"
     else:
         value, ms, roof, extra, fi = bench_forward(args, wl)
-        metric = "causal linear-attn fwd tokens/s (B*H*N/s)"
+        metric = ("causal retention fwd tokens/s (B*H*N/s)" if wl.retention
+                  else "causal linear-attn fwd tokens/s (B*H*N/s)")
     cpu = None
     if args.cpu_seconds > 0:
         if wl.decode_steps:
@@ -435,6 +459,8 @@ def main():
               "chunk": wl.chunk}
     if wl.m:
         config["m"] = wl.m
+    if wl.retention:
+        config["decay_per_head"] = [float(x) for x in wl.gammas()]
     if wl.decode_steps:
         config.update({"prefix": wl.N, "decode_steps_cycled": wl.decode_steps})
     line = {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

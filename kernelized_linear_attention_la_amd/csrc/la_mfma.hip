@@ -269,8 +269,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     constexpr int UV = NEED_K ? C * DV / 8 : 0;
     constexpr int UQ = (G::F && DO_OUT) ? C * DK / 8 : 0;
     constexpr int KBQ = G::F ? 1 : KBF;  // ELU+1: 16-byte query pieces per lane
-    // prefetch ring: two chunks in flight ahead of the one being computed
-    constexpr int DEPTH = 2;
+    // prefetch ring: chunks in flight ahead of the one being computed.  Two
+    // for the smaller tiles; one for d = 128 with 128-token chunks, whose
+    // chunk takes several load latencies to compute and whose registers are
+    // needed by the 8-wave tiles.
+    constexpr int DEPTH = (DK == 128 && C == 128) ? 1 : 2;
     struct Pref {
         Op8 raw[(UK + UV + UQ) / G::THREADS > 0 ? (UK + UV + UQ) / G::THREADS : 1];
         Op8 q[KBQ];
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         bool live, qlive;
         int cc;
         if constexpr (FUSED) {
-            const int n = c_end - c_begin, cbase = n + (n & 1);
+            const int n = c_end - c_begin, cbase = DEPTH == 2 ? n + (n & 1) : n;
             const bool pa = s < n, pc = s >= cbase && s < cbase + n;
             live = pa || pc;
             cc = c_begin + (pa ? s : (pc ? s - cbase : 0));
@@ -566,15 +569,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         // the Lc tokens of the chunk; the key weights scale the operand slots)
         if constexpr (DO_STATE) {
             const int Lc = min(C, N - t0);
-            float kw[RET ? KBT : 1][8];
             if constexpr (RET) {
-#pragma unroll
-                for (int kt = 0; kt < KBT; ++kt)
-#pragma unroll
-                    for (int sl = 0; sl < 8; ++sl) {  // slot sl <-> token 32kt + 16(sl/4) + 4g + sl%4
-                        const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
-                        kw[kt][sl] = t < Lc ? dpow((float)(Lc - 1 - t)) : 0.f;
-                    }
                 const float carry = dpow((float)Lc);
 #pragma unroll
                 for (int q = 0; q < FBW; ++q)
@@ -589,9 +584,14 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     for (int kt = 0; kt < KBT; ++kt) {
                         Op8 ka = token_operand<RK>(sm.K, kt, 16 * fb, lane);
                         if constexpr (RET) {
+                            // key weight of slot sl: token 32kt + 16(sl/4) + 4g + sl%4
+                            auto kw = [&](int sl) {
+                                const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
+                                return t < Lc ? dpow((float)(Lc - 1 - t)) : 0.f;
+                            };
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw[kt][2 * j], hi_bf16(ka.u32[j]) * kw[kt][2 * j + 1]);
+                                ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw(2 * j), hi_bf16(ka.u32[j]) * kw(2 * j + 1));
                         }
 #pragma unroll
                         for (int nb = 0; nb < NJ; ++nb)
@@ -786,10 +786,19 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 
     // Chunks go in pairs, then an odd last one: the loop back edge always
     // sees the same outstanding loads, so the waits stay partial.  Step s
-    // uses ring slot s % 2.
-    static_assert(DEPTH == 2, "the loops below walk the ring in pairs");
+    // uses ring slot s % 2.  (A one-slot ring walks the chunks one by one.)
+    static_assert(DEPTH == 1 || DEPTH == 2, "ring of one or two slots");
     using Out = std::integral_constant<bool, DO_OUT>;
-    if constexpr (!FUSED) {
+    if constexpr (DEPTH == 1) {
+        if constexpr (!FUSED) {
+            for (int c = c_begin; c < c_end; ++c) body(pf[0], c, c, Out{});
+        } else {
+            const int n = c_end - c_begin;
+            for (int i = 0; i < n; ++i) body(pf[0], c_begin + i, i, std::false_type{});
+            publish_and_gather();
+            for (int k = 0; k < n; ++k) body(pf[0], c_begin + k, n + k, std::true_type{});
+        }
+    } else if constexpr (!FUSED) {
         int c = c_begin;
         for (; c + 2 <= c_end; c += 2) {
             body(pf[0], c, c, Out{});
@@ -806,7 +815,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
         if (i < n) {
             body(pf[0], c_begin + i, i, std::false_type{});  // prefetches step cbase into slot 0
-            fetch(pf[1], cbase + 1);                          // slot 1 held the empty step n
+            fetch(pf[DEPTH - 1], cbase + 1);                  // slot 1 held the empty step n
         }
         // ---- phase 2: publish the sums, gather the prefix of the earlier segments
         publish_and_gather();
