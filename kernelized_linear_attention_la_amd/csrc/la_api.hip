@@ -145,6 +145,13 @@ bool causal_direct(const Shape &sh, const Segments &g, bool mfma) {
     return g.P == 1 && (mfma || generic_columns(sh) == 1);
 }
 
+// Single-pass mode: the LDS-resident variant when a segment's phi(K), V fit
+// (d = 64, 64-token chunks, at most kResChunks chunks per segment).
+int fused_mode(const Shape &sh, const Segments &g) {
+    const bool res = g.seg_chunks <= kResChunks && sh.dk == 64 && sh.dv == 64 && g.chunk == 64 && sh.phi != kFavor;
+    return res ? kModeFusedRes : kModeFused;
+}
+
 size_t causal_ws(const Shape &sh, int chunk) {
     bool mf = false;
     Segments g = causal_plan(sh, chunk, &mf);
@@ -291,7 +298,7 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
         // single pass on the matrix cores: every workgroup sums its segment,
         // hands the sums on through the workspace and runs its chunks
         FwdArgs f = c;
-        f.mode = kModeFused;
+        f.mode = fused_mode(sh, g);
         f.st.S_src = S_in; f.st.z_src = z_in;
         f.st.src_slice = nS; f.st.zsrc_slice = nz;
         f.fu.ctl = reinterpret_cast<uint32_t *>(wsb);
@@ -381,7 +388,7 @@ LA_API la_status la_forward_retention_chunked(const la_problem *p, const float *
     float *wsS = reinterpret_cast<float *>(wsb + wl.s_off);
     if (mf) {
         FwdArgs f = c;
-        f.mode = kModeFused;
+        f.mode = fused_mode(sh, g);
         f.st.S_src = S_in; f.st.src_slice = nS;
         f.fu.ctl = reinterpret_cast<uint32_t *>(wsb);
         f.fu.flags = reinterpret_cast<uint32_t *>(wsb + wl.f_off);

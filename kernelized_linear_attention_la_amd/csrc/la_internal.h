@@ -18,8 +18,12 @@ enum Mode : int {
     kModeState = 0,   // accumulate phi(K)^T [V, 1] of the segment into a state slot
     kModeCausal = 1,  // chunkwise causal forward starting from a prefix state
     kModeRead = 2,    // non-causal read: O = phi(Q) S / phi(Q) z with a fixed state
-    kModeFused = 3    // causal, single pass: segment sums, hand-off between segments, chunk loop
+    kModeFused = 3,   // causal, single pass: segment sums, hand-off between segments, chunk loop
+    kModeFusedRes = 4 // single pass with the segment's phi(K), V kept in LDS between the phases
 };
+
+// Chunks per segment that the LDS-resident single pass can hold (d = 64, 64-token chunks).
+constexpr int kResChunks = 4;
 
 // Shape of one call, after host validation.
 struct Shape {

@@ -163,12 +163,12 @@ struct Cfg {
     static constexpr int RX = DK + 8;  // FAVOR+: raw key / query rows (16-row 128-bit reads conflict free)
 };
 
-template <int DK, int DV, int C, int PHI>
+template <int DK, int DV, int C, int PHI, int NKS>
 struct Smem {
     using G = Cfg<DK, DV, C, PHI>;
     static constexpr bool F = G::F;
-    uint16_t K[C * G::RK];              // phi(K_c), token-major
-    uint16_t V[C * G::RV];              // V_aug, token-major
+    uint16_t K[NKS][C * G::RK];         // phi(K_c), token-major (NKS chunks when LDS-resident)
+    uint16_t V[NKS][C * G::RV];         // V_aug, token-major
     uint4 STB[G::NJ][G::KBF][64];       // bf16 S_aug: B operand of phi(Q) S
     uint16_t O[G::NW][16 * G::RO];      // per-wave output staging for 16-byte stores
     uint16_t XK[F ? C * G::RX : 1];     // FAVOR+: raw K_c, token-major
@@ -201,10 +201,14 @@ template <int DK, int DV, int C, int PHI, int MODE>
 __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     using G = Cfg<DK, DV, C, PHI>;
     using T = uint16_t;
-    __shared__ Smem<DK, DV, C, PHI> sm;
+    // LDS-resident single pass: phase 1 keeps every chunk's phi(K), V_aug of
+    // the segment (at most kResChunks) in LDS, phase 3 reads them back.
+    constexpr bool RES = MODE == kModeFusedRes;
+    constexpr int NKS = RES ? kResChunks : 1;
+    __shared__ Smem<DK, DV, C, PHI, NKS> sm;
     constexpr int NW = G::NW, NJ = G::NJ, KBT = G::KBT, KBF = G::KBF, FB = G::FB, FBW = G::FBW;
     constexpr int RK = G::RK, RV = G::RV, RO = G::RO;
-    constexpr bool FUSED = MODE == kModeFused;
+    constexpr bool FUSED = MODE == kModeFused || MODE == kModeFusedRes;
     constexpr bool DO_OUT = MODE != kModeState;  // some chunk of the launch writes outputs
     constexpr bool DO_STATE = MODE != kModeRead;
     constexpr bool NEED_K = MODE != kModeRead;
@@ -305,6 +309,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             live = pa || pc;
             cc = c_begin + (pa ? s : (pc ? s - cbase : 0));
             qlive = pc;
+            if (RES && pc) live = false, cc = c_begin + (s - cbase);  // keys, values are in LDS already
         } else {
             live = s < c_end;
             cc = live ? s : c_begin;
@@ -312,6 +317,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
         const int tt0 = cc * C;
         const int rows = live ? min(C, N - tt0) : 0;
+        const int qrows = qlive ? min(C, N - tt0) : 0;
         const auto rk = make_rsrc(Ks + (size_t)tt0 * DK, rows * DK * 2);
         const auto rv = make_rsrc(Vs + (size_t)tt0 * DV, rows * DV * 2);
 #pragma unroll
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < UVT; ++i) p.raw[UKT + i].u = bload16(rv, 16 * (tid + i * G::THREADS));
         if constexpr (DO_OUT) {
-            const auto rq = make_rsrc(Qs + (size_t)tt0 * DK, qlive ? rows * DK * 2 : 0);
+            const auto rq = make_rsrc(Qs + (size_t)tt0 * DK, qrows * DK * 2);
             if constexpr (G::F) {
 #pragma unroll
                 for (int i = 0; i < UQT; ++i) p.raw[UKT + UVT + i].u = bload16(rq, 16 * (tid + i * G::THREADS));
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     };
 
     // ---- write one prefetched chunk into LDS (token-major rows)
-    auto stage = [&](const Pref &p, int tt0) {
+    auto stage = [&](const Pref &p, int tt0, int ks) {
         const bool full = tt0 + C <= N;
 #pragma unroll
         for (int i = 0; i < UKT; ++i) {
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 if constexpr (RET) ph = p.raw[i].u;
                 else ph = elu1_bf16x8(p.raw[i].u);
                 if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(&sm.K[t * RK + 8 * c8]) = ph;
+                *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = ph;
             }
         }
 #pragma unroll
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < UVT; ++i) {
             const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
-            *reinterpret_cast<uint4 *>(&sm.V[t * RV + 8 * c8]) = p.raw[UKT + i].u;
+            *reinterpret_cast<uint4 *>(&sm.V[ks][t * RV + 8 * c8]) = p.raw[UKT + i].u;
         }
     };
 
@@ -389,10 +395,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // 15 columns 0.  Tokens past the end of the sequence have phi(k) = 0, so
     // their 1 contributes nothing.
     if constexpr (NEED_K && !RET) {
-        for (int u = tid; u < C * 2; u += G::THREADS) {
-            const int t = u >> 1, half = u & 1;
+        for (int u = tid; u < NKS * C * 2; u += G::THREADS) {
+            const int ks = u / (C * 2), t = (u >> 1) % C, half = u & 1;
             const uint32_t first = half == 0 ? 0x3f80u : 0u;
-            *reinterpret_cast<uint4 *>(&sm.V[t * RV + DV + 8 * half]) = make_uint4(first, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&sm.V[ks][t * RV + DV + 8 * half]) = make_uint4(first, 0, 0, 0);
         }
     }
     block_sync_lds();
@@ -404,7 +410,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         constexpr bool INTRA = OUT && MODE != kModeRead;  // causal: intra-chunk products
         constexpr bool CARRY = OUT && MODE != kModeRead;  // refresh the state image for the next chunk
         const int t0 = c * C;
-        stage(p, t0);
+        const int ks = RES ? c - c_begin : 0;  // LDS chunk slot
+        if (!(RES && OUT)) stage(p, t0, ks);  // the resident phase 3 finds phi(K), V in LDS
         Op8 phq[KBF];
         if constexpr (OUT && !G::F) {
 #pragma unroll
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         *reinterpret_cast<uint2 *>(&dst[t * RK + 64 * w + 16 * fbl + 4 * g]) = v;
                     }
             };
-            if constexpr (NEED_K) project(sm.XK, sm.K, true);
+            if constexpr (NEED_K) project(sm.XK, sm.K[ks], true);
             if constexpr (OUT) project(sm.XQ, sm.QP, false);
             block_sync_lds();
             if constexpr (OUT) {
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                             const int jb = 2 * kt + h;
                             p[h] = zero4();
                             if (jb <= qb) {
-                                const uint16_t *krow = &sm.K[(16 * jb + c16) * RK];
+                                const uint16_t *krow = &sm.K[ks][(16 * jb + c16) * RK];
 #pragma unroll
                                 for (int kf = 0; kf < KBF; ++kf) {
                                     Op8 ka;
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         pa.q[1] = pack4(p[1][0], p[1][1], p[1][2], p[1][3]);
 #pragma unroll
                         for (int nb = 0; nb < NJ; ++nb)
-                            acc[nb] = mfma(pa, token_operand<RV>(sm.V, kt, 16 * nb, lane), acc[nb]);
+                            acc[nb] = mfma(pa, token_operand<RV>(sm.V[ks], kt, 16 * nb, lane), acc[nb]);
                     }
                 }
             }
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 if (fb < FB) {
 #pragma unroll
                     for (int kt = 0; kt < KBT; ++kt) {
-                        Op8 ka = token_operand<RK>(sm.K, kt, 16 * fb, lane);
+                        Op8 ka = token_operand<RK>(sm.K[ks], kt, 16 * fb, lane);
                         if constexpr (RET) {
                             // key weight of slot sl: token 32kt + 16(sl/4) + 4g + sl%4
                             auto kw = [&](int sl) {
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         }
 #pragma unroll
                         for (int nb = 0; nb < NJ; ++nb)
-                            S[q][nb] = mfma(ka, token_operand<RV>(sm.V, kt, 16 * nb, lane), S[q][nb]);
+                            S[q][nb] = mfma(ka, token_operand<RV>(sm.V[ks], kt, 16 * nb, lane), S[q][nb]);
                     }
                 }
             }
@@ -676,17 +683,25 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
         const bool last = seg == P - 1 && a.fu.S_out;
         if (last) store_slot(P);  // park the own sums
+        // Wave 0 polls every earlier flag at once (lane i reads flag i, one
+        // coalesced access per poll) until all carry this launch's tag.
         bool late = false;
-        if (tid == 0) {
+        if (w == 0) {
+            const uint32_t want = __shfl(tag, 0, 64);  // the tag lives in thread 0
             const long long t_begin = wall_clock64();
-            for (int s2 = 0; s2 < seg && !late; ++s2)
-                while (__hip_atomic_load(fl + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
+            for (int base = 0; base < seg; base += 64) {
+                const int i = base + lane;
+                while (true) {
+                    const bool ok = i >= seg || __hip_atomic_load(fl + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
                     if (wall_clock64() - t_begin > a.fu.spin_ticks) {
                         late = true;
                         break;
                     }
                     __builtin_amdgcn_s_sleep(10);
                 }
+                if (late) break;
+            }
         }
         late = __syncthreads_or(late);  // every flag was seen before any slot is read
         if (late && tid == 0) __hip_atomic_store(a.fu.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -696,7 +711,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) S[q][nb] = zero4();
         // GD slots in flight (as many as the registers allow)
-        constexpr int GD = PER <= 6 ? 4 : 2;
+        constexpr int GD = PER > 6 ? 2 : C == 64 ? 8 : 4;
         f32x4 buf[GD][PER];
 #pragma unroll
         for (int d = 0; d < GD; ++d) load_slot(buf[d], d, d == 0 ? has_in : d <= seg);
@@ -865,6 +880,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 template <int DK, int DV, int C, int PHI>
 hipError_t launch_variant(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.sh.BH * a.sg.P)), block(C / 16 * 64);
+    if (a.mode == kModeFusedRes) {
+        if constexpr (DK == 64 && DV == 64 && C == 64 && PHI != kFavor)
+            return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFusedRes>, grid, block, 0, st, ev, a);
+        return hipErrorNotSupported;
+    }
     if constexpr (PHI == kIdentity) {  // retention: causal only
         if (a.mode == kModeFused)
             return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFused>, grid, block, 0, st, ev, a);

@@ -129,6 +129,8 @@ CASES = [
     # a shorter last segment and a ragged tail
     (4, 16, 700, 64, 64, "bf16", "elu1", 0, 64),
     (8, 16, 768, 128, 128, "bf16", "elu1", 0, 128),
+    # d = 64 segments too long to keep in LDS (nine chunks each)
+    (4, 8, 4100, 64, 64, "bf16", "elu1", 0, 64),
     (4, 16, 740, 64, 64, "bf16", "favor", 256, 64),
 ]
 

@@ -85,6 +85,7 @@ CASES = [
     # single-pass hand-off with segments of three chunks and a shorter last one
     (4, 16, 700, 64, 64, "bf16", "identity", 0, 64, True),
     (8, 16, 768, 128, 128, "bf16", "identity", 0, 128, False),
+    (4, 8, 4100, 64, 64, "bf16", "identity", 0, 64, True),
 ]
 
 
