@@ -217,7 +217,7 @@ def stored_traffic(wl, kernel):
     """HBM bytes per launch from a committed counter summary, if the kernels are unchanged since."""
     import glob
     from kernelized_linear_attention_la_amd import build as hip_build
-    want = hip_build.source_hash()
+    want = hip_build.source_hash(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
         try:
             with open(path) as f:

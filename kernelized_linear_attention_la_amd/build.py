@@ -64,17 +64,34 @@ def build(extra_flags=(), verbose: bool = False) -> str:
 
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and the public header (identifies a kernel build)."""
+# The sources that decide each kernel family's code and launch plan: its own
+# file, the shared device helpers and argument structs, and the host code that
+# sizes its grid and segments.
+KERNEL_SOURCES = {
+    "k_mfma": ("la_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_generic": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_scan": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_decode": ("la_decode.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+}
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """sha256 over the HIP sources behind one kernel family (all sources when
+    `kernel` is None or not a known family); identifies a kernel build."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    fam = None if kernel is None else kernel.split("<")[0]
+    if fam in KERNEL_SOURCES:
+        files = sorted(KERNEL_SOURCES[fam])
+    else:
+        files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
     for f in files:
         h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(INCLUDE, "liblinattn.h"), "rb") as fh:
-        h.update(fh.read())
+    if fam not in KERNEL_SOURCES:
+        with open(os.path.join(INCLUDE, "liblinattn.h"), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -140,7 +140,7 @@ def main():
         alg = bench.decode_alg_bytes(wl)
     else:
         alg = wl.B * wl.H * wl.N * (2 * wl.dk + 2 * wl.dv) * bench.elem_bytes(wl.dtype)
-    src = hip_build.source_hash()
+    src = hip_build.source_hash(kernel)
     safe = re.sub(r"[^A-Za-z0-9]+", "_", kernel).strip("_")
     rec = {"workload": wl.name, "kernel": kernel, "source_hash": src, "bytes_per_launch": bytes_per_launch,
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "copy_fetch_scale": scale_f,
