@@ -60,6 +60,7 @@ def lib():
         L.ora_retention_parallel.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, D]
         L.ora_retention_chunked.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, i, D, D]
         L.ora_retention_decode_step.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_causal_backward.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D, D, D, D, D, D, D, D]
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_set_num_threads.argtypes = [i]
         _lib = L
@@ -174,6 +175,26 @@ def causal_chunked(phi_kind, Q, K, V, chunk, W=None, S_in=None, z_in=None):
     lib().ora_causal_chunked(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf),
                              _p(Si), _p(zi), int(chunk), _p(O), _p(S), _p(z))
     return O.reshape(B, H, N, dv), S.reshape(B, H, dp, dv), z.reshape(B, H, dp)
+
+
+def causal_backward(phi_kind, Q, K, V, dO, W=None, S_in=None, z_in=None, dS_out=None, dz_out=None):
+    """Gradients of the causal form (reverse-mode through the recurrence).
+
+    For a loss with dL/dO = dO and, optionally, dL/dS_out, dL/dz_out, returns
+    (dQ, dK, dV, dS_in, dz_in); dS_in, dz_in are the gradients with respect to
+    the starting state (returned whether or not S_in was given).
+    """
+    Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp = _prep(phi_kind, Q, K, V, W)
+    Si, zi = _state_in(S_in, z_in, BH, dp, dv)
+    dOf = _d(dO).reshape(BH, N, dv)
+    dSo = None if dS_out is None else _d(dS_out).reshape(BH, dp, dv)
+    dzo = None if dz_out is None else _d(dz_out).reshape(BH, dp)
+    dQ = np.empty((BH, N, dk)); dK = np.empty((BH, N, dk)); dV = np.empty((BH, N, dv))
+    dSi = np.empty((BH, dp, dv)); dzi = np.empty((BH, dp))
+    lib().ora_causal_backward(BH, N, dk, dv, _kind(phi_kind), m, _p(Wd), _p(Qf), _p(Kf), _p(Vf), _p(Si), _p(zi),
+                              _p(dOf), _p(dSo), _p(dzo), _p(dQ), _p(dK), _p(dV), _p(dSi), _p(dzi))
+    return (dQ.reshape(B, H, N, dk), dK.reshape(B, H, N, dk), dV.reshape(B, H, N, dv),
+            dSi.reshape(B, H, dp, dv), dzi.reshape(B, H, dp))
 
 
 def decode_step(phi_kind, q, k, v, S, z, W=None):

@@ -507,3 +507,117 @@ void ora_retention_decode_step(int BH, int H, int dk, int dv, int kind, int m, c
         free(pk); free(pq);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward of the causal form.  The pages present the parallel (quadratic)
+ * mode as the training mode [ASSOC, the two computation modes] but give no
+ * gradients; this is reverse-mode differentiation of the causal recurrence
+ * above, written out.  With kappa_j = phi(k_j), psi_i = phi(q_i):
+ *   forward:  S_i = S_{i-1} + kappa_i v_i^T, z_i = z_{i-1} + kappa_i,
+ *             num_i = S_i^T psi_i, den_i = z_i^T psi_i, o_i = num_i / den_i,
+ *             S_out = S_N, z_out = z_N.
+ * For a loss L with dO_i = dL/do_i and dS_out, dz_out = dL/dS_N, dL/dz_N:
+ *   g_i = dL/dnum_i = dO_i / den_i,   h_i = dL/dden_i = -(dO_i . o_i) / den_i,
+ *   dpsi_i = S_i g_i + z_i h_i                         (forward sweep),
+ *   R_j = dS_out + sum_{i >= j} psi_i g_i^T,  r_j = dz_out + sum_{i >= j} psi_i h_i,
+ *   dkappa_j = R_j v_j + r_j,   dv_j = R_j^T kappa_j   (reverse sweep),
+ *   dS_in = R_1, dz_in = r_1.
+ * The map's Jacobian takes dpsi, dkappa back to the inputs:
+ *   ELU+1: dx = dphi * (x > 0 ? 1 : exp(x));  identity: dx = dphi;
+ *   FAVOR+: dphi_r/dx = phi_r (w_r - x), so dx = sum_r dphi_r phi_r (w_r - x)
+ *   (W is a fixed random projection: no gradient for it).
+ * dS_out / dz_out may be NULL (zero); dS_in / dz_in may be NULL (not wanted).
+ * ------------------------------------------------------------------------- */
+static void phi_vjp_row(int kind, const double *x, int d, const double *W, int m, const double *dphi, double *dx) {
+    if (kind == ORA_PHI_FAVOR) {
+        double *ph = (double *)malloc(sizeof(double) * m);
+        phi_favor_row(x, d, W, m, ph);
+        double s = 0.0;
+        for (int r = 0; r < m; ++r) s += dphi[r] * ph[r];
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int r = 0; r < m; ++r) acc += dphi[r] * ph[r] * W[(size_t)r * d + c];
+            dx[c] = acc - s * x[c];
+        }
+        free(ph);
+    } else if (kind == ORA_PHI_IDENTITY) {
+        for (int c = 0; c < d; ++c) dx[c] = dphi[c];
+    } else {
+        for (int c = 0; c < d; ++c) dx[c] = dphi[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]));
+    }
+}
+
+void ora_causal_backward(int BH, int N, int dk, int dv, int kind, int m, const double *W,
+                         const double *Q, const double *K, const double *V,
+                         const double *S_in, const double *z_in,
+                         const double *dO, const double *dS_out, const double *dz_out,
+                         double *dQ, double *dK, double *dV, double *dS_in, double *dz_in) {
+    int dp = feat_dim(kind, dk, m);
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        const double *dOs = dO + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dp * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)dp, sizeof(double));
+        if (S_in) {
+            memcpy(S, S_in + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+            memcpy(z, z_in + (size_t)s * dp, sizeof(double) * dp);
+        }
+        double *psi = (double *)malloc(sizeof(double) * (size_t)N * dp);  /* phi(q_i), kept for the reverse sweep */
+        double *g = (double *)malloc(sizeof(double) * (size_t)N * dv);
+        double *h = (double *)malloc(sizeof(double) * (size_t)N);
+        double *kap = (double *)malloc(sizeof(double) * dp);
+        double *num = (double *)malloc(sizeof(double) * dv);
+        double *dphi = (double *)malloc(sizeof(double) * dp);
+        /* forward sweep: the state after token i, the output, g_i, h_i and dpsi_i */
+        for (int i = 0; i < N; ++i) {
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, kap);
+            for (int f = 0; f < dp; ++f) {
+                z[f] += kap[f];
+                for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += kap[f] * v[(size_t)i * dv + c];
+            }
+            double *ps = psi + (size_t)i * dp;
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, ps);
+            double den;
+            ora_state_read(1, dp, dv, ps, S, z, num, &den);
+            double dot = 0.0;
+            for (int c = 0; c < dv; ++c) dot += dOs[(size_t)i * dv + c] * (num[c] / den);
+            for (int c = 0; c < dv; ++c) g[(size_t)i * dv + c] = dOs[(size_t)i * dv + c] / den;
+            h[i] = -dot / den;
+            for (int f = 0; f < dp; ++f) {
+                double acc = 0.0;
+                for (int c = 0; c < dv; ++c) acc += S[(size_t)f * dv + c] * g[(size_t)i * dv + c];
+                dphi[f] = acc + z[f] * h[i];
+            }
+            phi_vjp_row(kind, q + (size_t)i * dk, dk, W, m, dphi, dQ + ((size_t)s * N + i) * dk);
+        }
+        /* reverse sweep: R, r accumulate psi_i g_i^T, psi_i h_i from the end */
+        double *R = S, *r = z; /* reuse the buffers */
+        if (dS_out) memcpy(R, dS_out + (size_t)s * dp * dv, sizeof(double) * dp * dv);
+        else memset(R, 0, sizeof(double) * dp * dv);
+        if (dz_out) memcpy(r, dz_out + (size_t)s * dp, sizeof(double) * dp);
+        else memset(r, 0, sizeof(double) * dp);
+        for (int j = N - 1; j >= 0; --j) {
+            const double *ps = psi + (size_t)j * dp;
+            for (int f = 0; f < dp; ++f) {
+                r[f] += ps[f] * h[j];
+                for (int c = 0; c < dv; ++c) R[(size_t)f * dv + c] += ps[f] * g[(size_t)j * dv + c];
+            }
+            phi_row(kind, k + (size_t)j * dk, dk, W, m, kap);
+            for (int f = 0; f < dp; ++f) {
+                double acc = r[f];
+                for (int c = 0; c < dv; ++c) acc += R[(size_t)f * dv + c] * v[(size_t)j * dv + c];
+                dphi[f] = acc;
+            }
+            phi_vjp_row(kind, k + (size_t)j * dk, dk, W, m, dphi, dK + ((size_t)s * N + j) * dk);
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < dp; ++f) acc += R[(size_t)f * dv + c] * kap[f];
+                dV[((size_t)s * N + j) * dv + c] = acc;
+            }
+        }
+        if (dS_in) memcpy(dS_in + (size_t)s * dp * dv, R, sizeof(double) * dp * dv);
+        if (dz_in) memcpy(dz_in + (size_t)s * dp, r, sizeof(double) * dp);
+        free(S); free(z); free(psi); free(g); free(h); free(kap); free(num); free(dphi);
+    }
+}
