@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum {
     LA_OK = 0,
@@ -206,6 +206,64 @@ la_status la_forward_retention_chunked(const la_problem *p, const float *gamma, 
  */
 la_status la_retention_decode_step(const la_problem *p, const float *gamma, const void *q, const void *k,
                                    const void *v, void *o, float *S, void *stream);
+
+/*
+ * Backward of the causal form (la_forward_causal_chunked with the ELU+1 or
+ * FAVOR+ map).  The pages use the parallel mode for training ("Linear
+ * Attention: Removing the Softmax Buys Associativity", the two computation
+ * modes) but print no gradients; these are the reverse-mode derivatives of the
+ * causal recurrence.  With psi_i = phi(q_i), kappa_j = phi(k_j), den_i =
+ * psi_i^T z_i and o_i the forward output:
+ *   g_i = dO_i / den_i,  h_i = -(dO_i . o_i) / den_i,
+ *   dpsi_i   = S_i g_i + z_i h_i,
+ *   dkappa_j = R_j v_j + r_j,  dv_j = R_j^T kappa_j,
+ *   R_j = dS_out + sum_{i >= j} psi_i g_i^T,  r_j = dz_out + sum_{i >= j} psi_i h_i,
+ *   dS_in = R_1, dz_in = r_1,
+ * and dQ, dK are dpsi, dkappa through the map's Jacobian (ELU+1: 1 for x > 0,
+ * exp(x) otherwise; FAVOR+: d phi_r / dx = phi_r (w_r - x); W gets no
+ * gradient).  The forward is recomputed inside the call; O is not an input.
+ *   p            as for the forward; LA_PHI_IDENTITY is refused.  Supported
+ *                while d' * (d_v + 1) <= 16640 (d' = 128 with d_v <= 128, or
+ *                d' = 256 with d_v <= 64); larger: LA_ERR_UNSUPPORTED.
+ *   chunk        16, 32, 64 or 128: tokens per chunk of the chunked form.
+ *   Q, K, V      forward inputs; dO [B,H,N,d_v] the gradient of the loss with
+ *                respect to O (all of dtype p->dtype).
+ *   S_in, z_in   the forward's starting state, or both NULL (zero).
+ *   dS_out, dz_out  gradient with respect to the forward's final state
+ *                [B,H,d',d_v], [B,H,d'] fp32, or both NULL (zero).
+ *   dQ, dK, dV   outputs, [B,H,N,d_k] / [B,H,N,d_v] of dtype p->dtype
+ *                (fp32 arithmetic, rounded once at the store).
+ *   dS_in, dz_in gradient with respect to S_in, z_in, or both NULL (not
+ *                written).
+ *   ws           device workspace of at least la_backward_workspace_bytes()
+ *                bytes (no initial contents required).
+ *   ev           per-kernel timing hook (slots below), or NULL.
+ * Five kernels are enqueued: the forward's per-segment sums and their prefix
+ * scan, then the forward-direction pass (recomputes the outputs, writes dQ and
+ * the per-token g, h to ws), the reverse scan of the per-segment sums of
+ * psi g^T, psi h (writes dS_in, dz_in), and the reverse-direction pass (dK,
+ * dV).  Outputs must not overlap inputs or each other.
+ */
+enum { LA_BSLOT_FWD_SUMS = 0, LA_BSLOT_FWD_SCAN = 1, LA_BSLOT_DQ = 2, LA_BSLOT_RSCAN = 3, LA_BSLOT_DKV = 4,
+       LA_BSLOTS = 5 };
+
+typedef struct {
+    void *start[LA_BSLOTS];
+    void *stop[LA_BSLOTS];
+    int launched[LA_BSLOTS];
+} la_backward_events;
+
+/* Workspace bytes for la_backward_causal_chunked; 0 for an invalid or unsupported problem. */
+size_t la_backward_workspace_bytes(const la_problem *p, int chunk);
+
+la_status la_backward_causal_chunked(const la_problem *p, int chunk,
+                                     const void *Q, const void *K, const void *V, const void *dO,
+                                     const float *S_in, const float *z_in,
+                                     const float *dS_out, const float *dz_out,
+                                     void *dQ, void *dK, void *dV,
+                                     float *dS_in, float *dz_in,
+                                     void *ws, size_t ws_bytes, void *stream,
+                                     la_backward_events *ev);
 
 #ifdef __cplusplus
 }

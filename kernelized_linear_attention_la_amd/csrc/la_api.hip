@@ -424,3 +424,97 @@ LA_API la_status la_retention_decode_step(const la_problem *p, const float *gamm
     return launch_decode(sh, q, k, v, o, S, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK
                                                                                                     : LA_ERR_DEVICE;
 }
+
+// ---------------------------------------------------------------------------
+// Backward of the causal normalised form (kernels in la_backward.hip)
+// ---------------------------------------------------------------------------
+namespace la {
+namespace {
+
+// [forward prefix S][forward prefix z][per-segment sums psi^T G_aug][G_aug per token]
+struct BwdWs {
+    size_t s_off, z_off, u_off, g_off, total;
+};
+
+Segments backward_plan(const Shape &sh, int chunk) { return plan_segments(sh, chunk, 1, 1, kTargetWorkgroups); }
+
+BwdWs bwd_ws(const Shape &sh, const Segments &g) {
+    const size_t bh = (size_t)sh.BH, dp = (size_t)sh.dp, dv = (size_t)sh.dv;
+    BwdWs w;
+    w.s_off = 0;
+    w.z_off = w.s_off + round_up(sizeof(float) * bh * g.P * dp * dv, kAlign);
+    w.u_off = w.z_off + round_up(sizeof(float) * bh * g.P * dp, kAlign);
+    w.g_off = w.u_off + round_up(sizeof(float) * bh * g.P * dp * (dv + 1), kAlign);
+    w.total = w.g_off + round_up(sizeof(float) * bh * sh.N * (dv + 1), kAlign);
+    return w;
+}
+
+}  // namespace
+}  // namespace la
+
+LA_API size_t la_backward_workspace_bytes(const la_problem *p, int chunk) {
+    if (check_problem(p) != LA_OK || !chunk_ok(chunk) || p->phi == LA_PHI_IDENTITY) return 0;
+    const Shape sh = make_shape(p);
+    if (!backward_supported(sh)) return 0;
+    return bwd_ws(sh, backward_plan(sh, chunk)).total;
+}
+
+LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, const void *Q, const void *K,
+                                            const void *V, const void *dO, const float *S_in, const float *z_in,
+                                            const float *dS_out, const float *dz_out, void *dQ, void *dK, void *dV,
+                                            float *dS_in, float *dz_in, void *ws, size_t ws_bytes, void *stream,
+                                            la_backward_events *ev) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->phi == LA_PHI_IDENTITY || !chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LA_ERR_NULL;
+    if ((S_in == nullptr) != (z_in == nullptr) || (dS_out == nullptr) != (dz_out == nullptr) ||
+        (dS_in == nullptr) != (dz_in == nullptr))
+        return LA_ERR_NULL;
+    const void *ptrs[] = {Q, K, V, dO, S_in, z_in, dS_out, dz_out, dQ, dK, dV, dS_in, dz_in, ws};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return LA_ERR_ALIGN;
+    const Shape sh = make_shape(p);
+    if (!backward_supported(sh)) return LA_ERR_UNSUPPORTED;
+    const Segments g = backward_plan(sh, chunk);
+    const BwdWs wl = bwd_ws(sh, g);
+    if (!ws || ws_bytes < wl.total) return LA_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    float *wsS = reinterpret_cast<float *>(wsb + wl.s_off);
+    float *wsz = reinterpret_cast<float *>(wsb + wl.z_off);
+    const size_t nS = (size_t)sh.dp * sh.dv, nz = (size_t)sh.dp;
+    auto slot = [&](int i) {
+        KEvents k;
+        if (!ev) return k;
+        ev->launched[i] = 1;
+        k.start = static_cast<hipEvent_t>(ev->start[i]);
+        k.stop = static_cast<hipEvent_t>(ev->stop[i]);
+        return k;
+    };
+    if (ev)
+        for (int i = 0; i < LA_BSLOTS; ++i) ev->launched[i] = 0;
+
+    // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan
+    FwdArgs a{};
+    a.sh = sh; a.sg = g; a.mode = kModeState;
+    a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
+    a.st.S_dst = wsS; a.st.z_dst = wsz;
+    a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
+    if (launch_generic(a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
+    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, nullptr, nullptr, false, hs, slot(LA_BSLOT_FWD_SCAN)) !=
+        hipSuccess)
+        return LA_ERR_DEVICE;
+    BwdLaunch b;
+    b.sh = sh; b.sg = g;
+    b.Q = Q; b.K = K; b.V = V; b.dO = dO;
+    b.dQ = dQ; b.dK = dK; b.dV = dV;
+    b.Spre = wsS; b.zpre = wsz;
+    b.U = reinterpret_cast<float *>(wsb + wl.u_off);
+    b.G = reinterpret_cast<float *>(wsb + wl.g_off);
+    b.dS_out = dS_out; b.dz_out = dz_out;
+    b.dS_in = dS_in; b.dz_in = dz_in;
+    return launch_backward(b, hs, slot(LA_BSLOT_DQ), slot(LA_BSLOT_RSCAN), slot(LA_BSLOT_DKV)) == hipSuccess
+               ? LA_OK
+               : LA_ERR_DEVICE;
+}

@@ -131,4 +131,22 @@ hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const vo
 hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 bool mfma_supported(const Shape &sh, int chunk);
 
+// Backward of the causal normalised form (la_backward.hip): three launches
+// per call after the forward prefix is in Spre / zpre.
+struct BwdLaunch {
+    Shape sh;
+    Segments sg;
+    const void *Q, *K, *V, *dO;
+    void *dQ, *dK, *dV;
+    const float *Spre, *zpre;       // forward prefix entering each segment
+    float *U;                       // [BH][P][d' (d_v + 1)] workspace
+    float *G;                       // [BH][N][d_v + 1] workspace
+    const float *dS_out, *dz_out;   // NULL = zero
+    float *dS_in, *dz_in;           // NULL = not wanted
+};
+bool backward_supported(const Shape &sh);
+size_t backward_lds_bytes(const Shape &sh);
+hipError_t launch_backward(const BwdLaunch &b, hipStream_t stream, KEvents ev_dq = {}, KEvents ev_scan = {},
+                           KEvents ev_dkv = {});
+
 }  // namespace la

@@ -10,7 +10,8 @@ Recipe (every workload):
   * draw fp64 standard normals, multiply by the workload's scale in fp64,
     round to fp32 (round-to-nearest-even), and for bf16 workloads round the
     fp32 value once more to bf16 (round-to-nearest-even);
-  * tensor ids: Q=0, K=1, V=2, W=3, decode q=4, k=5, v=6.
+  * tensor ids: Q=0, K=1, V=2, W=3, decode q=4, k=5, v=6, and for the
+    backward dO=7, dS_out=8, dz_out=9, S_in=10, z_in=11.
 
 The FAVOR+ projection W (m rows of dimension d) is an *input*: the random
 features of the Performer map are drawn here once and handed to both sides.
@@ -30,6 +31,7 @@ import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_W = 0, 1, 2, 3
 TENSOR_QSTEP, TENSOR_KSTEP, TENSOR_VSTEP = 4, 5, 6
+TENSOR_DO, TENSOR_DS, TENSOR_DZ, TENSOR_SIN, TENSOR_ZIN = 7, 8, 9, 10, 11
 
 
 # ---------------------------------------------------------------------------
@@ -279,6 +281,27 @@ def custom_inputs(seed: int, B, H, N, dk, dv, scale=1.0, dtype="f32", phi="elu1"
     W = orthogonal_gaussian_rows(1000 + seed, m, dk) if phi == "favor" else None
     wl = Workload(f"custom{seed}", 1000 + seed, phi, dtype, B, H, N, dk, dv, scale, 64, m=m)
     return ForwardInputs(wl, Q, K, V, W)
+
+
+def grad_output(wid: int, B, H, N, dv, dtype, scale=1.0, workers=None) -> HostTensor:
+    """Seeded dL/dO [B, H, N, d_v] for the backward (N(0, scale^2), storage dtype)."""
+    return normal_bhnd(wid, TENSOR_DO, (B, H, N, dv), scale, dtype, workers=workers)
+
+
+def state_grads(wid: int, B, H, dp, dv):
+    """Seeded dL/dS_out [B, H, d', d_v] and dL/dz_out [B, H, d'] (fp32, N(0, 1))."""
+    dS = normal_bhnd(wid, TENSOR_DS, (B, H, dp, dv), 1.0, "f32").f32
+    dz = normal_bhnd(wid, TENSOR_DZ, (B, H, 1, dp), 1.0, "f32").f32.reshape(B, H, dp)
+    return np.ascontiguousarray(dS), np.ascontiguousarray(dz)
+
+
+def positive_state(wid: int, B, H, dp, dv, tokens=64):
+    """A starting state (S_in, z_in) shaped like the sums of `tokens` earlier
+    tokens with positive features: S_in ~ N(0, tokens), z_in ~ tokens * U(0.5, 1.5)."""
+    S = normal_bhnd(wid, TENSOR_SIN, (B, H, dp, dv), math.sqrt(tokens), "f32").f32
+    u = normal_bhnd(wid, TENSOR_ZIN, (B, H, 1, dp), 1.0, "f32").f32.reshape(B, H, dp)
+    z = (tokens * (1.0 + 0.5 * np.tanh(u))).astype(np.float32)
+    return np.ascontiguousarray(S), np.ascontiguousarray(z)
 
 
 if __name__ == "__main__":

@@ -24,8 +24,10 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYP
                 5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
             "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
-            "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step")
+            "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step",
+            "la_backward_workspace_bytes", "la_backward_causal_chunked")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
+LA_BSLOT_FWD_SUMS, LA_BSLOT_FWD_SCAN, LA_BSLOT_DQ, LA_BSLOT_RSCAN, LA_BSLOT_DKV, LA_BSLOTS = 0, 1, 2, 3, 4, 5
 
 
 class LaProblem(ctypes.Structure):
@@ -38,6 +40,11 @@ class LaProblem(ctypes.Structure):
 class LaKernelEvents(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p * LA_KSLOTS), ("stop", ctypes.c_void_p * LA_KSLOTS),
                 ("launched", ctypes.c_int * LA_KSLOTS)]
+
+
+class LaBackwardEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p * LA_BSLOTS), ("stop", ctypes.c_void_p * LA_BSLOTS),
+                ("launched", ctypes.c_int * LA_BSLOTS)]
 
 
 class LaError(RuntimeError):
@@ -79,6 +86,11 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.POINTER(LaKernelEvents)]
         L.la_retention_decode_step.restype = i
         L.la_retention_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.la_backward_workspace_bytes.argtypes = [P, i]
+        L.la_backward_workspace_bytes.restype = sz
+        L.la_backward_causal_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                 ctypes.POINTER(LaBackwardEvents)]
+        L.la_backward_causal_chunked.restype = i
         _lib = L
     return _lib
 
@@ -317,3 +329,47 @@ def la_retention_decode_step(q, k, v, S, gamma, phi="identity", W=None, out=None
                                         _stream(stream))
     _raise(st, "la_retention_decode_step")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward of the causal form
+# ---------------------------------------------------------------------------
+def la_backward_workspace_bytes(p: LaProblem, chunk: int) -> int:
+    return int(lib().la_backward_workspace_bytes(ctypes.byref(p), int(chunk)))
+
+
+def la_backward_causal_chunked(q, k, v, dO, chunk=64, phi="elu1", W=None, S_in=None, z_in=None, dS_out=None,
+                               dz_out=None, state_grad=False, dQ=None, dK=None, dV=None, workspace=None, stream=None,
+                               events=None):
+    """Gradients of the causal chunkwise forward for dL/dO = dO (and dL/dS_out,
+    dL/dz_out when given).  Returns (dQ, dK, dV, dS_in, dz_in); the last two
+    are None unless S_in is given or state_grad is True."""
+    _check_qkv(q, k, v)
+    if not isinstance(dO, torch.Tensor) or dO.shape != v.shape or dO.dtype != v.dtype or not dO.is_contiguous() \
+            or dO.device != v.device:
+        raise ValueError("dO must be a contiguous device tensor shaped and typed like V")
+    p = _problem_of(q, v, phi, W)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    S_in, z_in = _state_pair(S_in, z_in, B, H, dp, dv, q.device, "initial state")
+    dS_out, dz_out = _state_pair(dS_out, dz_out, B, H, dp, dv, q.device, "final-state gradient")
+    dQ = torch.empty_like(q) if dQ is None else dQ
+    dK = torch.empty_like(k) if dK is None else dK
+    dV = torch.empty_like(v) if dV is None else dV
+    dS_in = dz_in = None
+    if state_grad or S_in is not None:
+        dS_in = torch.empty((B, H, dp, dv), dtype=torch.float32, device=q.device)
+        dz_in = torch.empty((B, H, dp), dtype=torch.float32, device=q.device)
+    nbytes = la_backward_workspace_bytes(p, chunk)
+    if nbytes == 0:
+        raise LaError(4, "la_backward_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().la_backward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dO),
+                                          _ptr(S_in), _ptr(z_in), _ptr(dS_out), _ptr(dz_out), _ptr(dQ), _ptr(dK),
+                                          _ptr(dV), _ptr(dS_in), _ptr(dz_in), _ptr(workspace), wsb, _stream(stream),
+                                          None if events is None else ctypes.byref(events))
+    _raise(st, "la_backward_causal_chunked")
+    return dQ, dK, dV, dS_in, dz_in

@@ -52,5 +52,19 @@ def z_rel_err(z, zref):
     return float((np.abs(z - zref) / np.abs(zref)).max()) if z.size else 0.0
 
 
+def slice_rel_err(y, ref):
+    """Gradients: per (b, h) slice, max |y - ref| over the slice / max |ref| over
+    the slice.  Gradient rows can vanish exactly (the first token's dq is 0
+    without a starting state), so a row's own scale is no yardstick here; the
+    slice's largest gradient is."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    B, H = ref.shape[0], ref.shape[1]
+    d = np.abs(y - ref).reshape(B, H, -1).max(-1) if ref.size else np.zeros((B, H))
+    s = np.abs(ref).reshape(B, H, -1).max(-1) if ref.size else np.ones((B, H))
+    s = np.where(s > 0, s, 1.0)
+    return float((d / s).max()) if d.size else 0.0
+
+
 def tol_for(dtype):
     return TOL_BF16 if dtype == "bf16" else TOL_F32

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert linattn.la_abi_version() == 2
+    assert linattn.la_abi_version() == 3
     for s in range(8):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)
@@ -165,3 +165,38 @@ def test_retention_validation():
     for phi, m, W in ((linattn.LA_PHI_ELU1, 0, 0), (linattn.LA_PHI_FAVOR, 256, 0x1000)):
         pp = _p(B=1, H=2, N=4096, phi=phi, m=m, W_ptr=W)
         assert linattn.la_workspace_bytes(pp, 64) > 0
+
+
+def test_backward_validation():
+    L = linattn.lib()
+    p = _p()
+
+    def bwd(p=p, chunk=64, Q=FAKE, dO=FAKE, dQ=FAKE, Si=None, zi=None, dSo=None, dzo=None, dSi=None, dzi=None,
+            ws=FAKE, wsb=1 << 40):
+        return L.la_backward_causal_chunked(ctypes.byref(p), chunk, Q, FAKE, FAKE, dO, Si, zi, dSo, dzo, dQ, FAKE,
+                                            FAKE, dSi, dzi, ws, wsb, None, None)
+
+    need = linattn.la_backward_workspace_bytes(p, 64)
+    assert need > 0 and need % 256 == 0
+    # G_aug per token alone is B*H*N*(d_v + 1) floats
+    assert need >= 2 * 3 * 100 * 65 * 4
+    assert linattn.la_backward_workspace_bytes(p, 48) == 0
+    assert linattn.la_backward_workspace_bytes(_p(phi=linattn.LA_PHI_IDENTITY), 64) == 0
+    # largest supported states: d' (d_v + 1) <= 16640
+    assert linattn.la_backward_workspace_bytes(_p(d_k=128, d_v=128), 64) > 0
+    assert linattn.la_backward_workspace_bytes(_p(phi=linattn.LA_PHI_FAVOR, m=256, W_ptr=0x1000, d_v=64), 64) > 0
+    assert linattn.la_backward_workspace_bytes(_p(phi=linattn.LA_PHI_FAVOR, m=256, W_ptr=0x1000, d_v=65), 64) == 0
+    assert bwd(p=_p(phi=linattn.LA_PHI_FAVOR, m=256, W_ptr=0x1000, d_v=65)) == 4
+    assert bwd(p=_p(phi=linattn.LA_PHI_IDENTITY)) == 4
+    assert bwd(chunk=48) == 4
+    assert bwd(Q=None) == 1
+    assert bwd(dO=None) == 1
+    assert bwd(dQ=None) == 1
+    assert bwd(Si=FAKE) == 1                 # S_in without z_in
+    assert bwd(dSo=FAKE) == 1                # dS_out without dz_out
+    assert bwd(dzi=FAKE) == 1                # dz_in without dS_in
+    assert bwd(dO=MIS) == 5
+    assert bwd(dSi=FAKE, dzi=MIS) == 5
+    assert bwd(ws=None) == 6
+    assert bwd(wsb=need - 1) == 6
+    assert bwd(p=_p(B=0)) == 2
