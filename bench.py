@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 DEFAULT_WORKLOAD = "elu1_bf16_b4h8n2048d64_c64"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+FP32_VECTOR_PEAK_TFS = 157.3  # MI355X fp32 vector ALUs (256 CUs x 256 flop/clk x 2.4 GHz), TFLOP/s
 ROTATE_BYTES = 768 << 20     # > 256 MB Infinity Cache
 
 
@@ -65,6 +66,31 @@ def forward_alg_flops(wl):
         per = 4 * dp * dv + 2 * dp + (C + 1) * (dp + dv) + dv
     if wl.phi == "favor":
         per += 4 * dk * wl.m
+    return wl.B * wl.H * wl.N * per
+
+
+def backward_alg_flops(wl, kernel):
+    """Algorithmic flops of one backward kernel (causal half of the intra-chunk products).
+
+    Per token, with a = d_v + 1 (the value block plus the normaliser column):
+      forward-direction pass (dQ): state carry 2 d' a, output recompute 2 d' a +
+        (C+1)(d' + a), dphi(q) 2 d' a + (C+1)(a + d'), segment sums 2 d' a;
+      reverse-direction pass (dK, dV): dphi(k) from later chunks 2 d' a, dV from
+        later chunks 2 d' d_v, in-chunk scores and sums (C+1)(2 d' + d_v + a),
+        carry 2 d' a;
+    FAVOR+ adds the projection 2 d_k m per recomputed row (q in the first pass,
+    k in both) and its Jacobian 2 d_k m + 2 m per row.
+    """
+    C, dp, dv, dk = wl.chunk, wl.dprime, wl.dv, wl.dk
+    a = dv + 1
+    if kernel == "dq":
+        per = 8 * dp * a + 2 * (C + 1) * (dp + a)
+        if wl.phi == "favor":
+            per += 2 * 2 * dk * wl.m + 2 * dk * wl.m + 2 * wl.m
+    else:
+        per = 4 * dp * a + 2 * dp * dv + (C + 1) * (2 * dp + dv + a)
+        if wl.phi == "favor":
+            per += 2 * 2 * dk * wl.m + 2 * dk * wl.m + 2 * wl.m
     return wl.B * wl.H * wl.N * per
 
 
@@ -189,6 +215,8 @@ def run_cpu_baseline_decode(wl, fi, seconds):
 
 def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
+    if wl.backward:
+        return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
         return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}, {'true' if wl.retention else 'false'}>"
@@ -370,6 +398,125 @@ def bench_forward(args, wl):
     return value, ms_per_step, roof, extra, fi
 
 
+def bench_backward(args, wl):
+    """One step = la_backward_causal_chunked over the whole batch (forward prefix
+    sums and scan, dQ pass, reverse scan, dK/dV pass)."""
+    import torch
+    from kernelized_linear_attention_la_amd import inputs
+    from kernelized_linear_attention_la_amd import linattn as la
+
+    fi = inputs.forward_inputs(wl)
+    dO_h = inputs.grad_output(wl.wid, wl.B, wl.H, wl.N, wl.dv, wl.dtype)
+    dev = torch.device("cuda:0")
+
+    def to_dev(ht):
+        t = torch.from_numpy(ht.store)
+        return (t.view(torch.bfloat16) if ht.dtype == "bf16" else t).to(dev)
+
+    q0, k0, v0, g0 = to_dev(fi.Q), to_dev(fi.K), to_dev(fi.V), to_dev(dO_h)
+    W = torch.from_numpy(fi.W).to(dev) if fi.W is not None else None
+    set_bytes = 2 * q0.nbytes + 2 * k0.nbytes + 2 * v0.nbytes + g0.nbytes
+    R = max(1, min(32, math.ceil(ROTATE_BYTES / set_bytes)))
+    sets = [(q0.clone(), k0.clone(), v0.clone(), g0.clone(), torch.empty_like(q0), torch.empty_like(k0),
+             torch.empty_like(v0)) for _ in range(R)]
+    p = la._problem_of(q0, v0, wl.phi, W)
+    ws = torch.empty(la.la_backward_workspace_bytes(p, wl.chunk), dtype=torch.uint8, device=dev)
+
+    def step(i, stream=None, events=None):
+        q, k, v, g, dq, dk, dv = sets[i % R]
+        la.la_backward_causal_chunked(q, k, v, g, wl.chunk, phi=wl.phi, W=W, dQ=dq, dK=dk, dV=dv, workspace=ws,
+                                      stream=stream, events=events)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(R):
+            step(i)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        with torch.cuda.stream(stream):
+            step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    hev = HipEvents(la.lib())
+    slots = (la.LA_BSLOT_FWD_SUMS, la.LA_BSLOT_FWD_SCAN, la.LA_BSLOT_DQ, la.LA_BSLOT_RSCAN, la.LA_BSLOT_DKV)
+    durs = {sl: [] for sl in slots}
+    ev = [{sl: (hev.create(), hev.create()) for sl in slots} for _ in range(R)]
+    kevs = []
+    for i in range(R):
+        kev = la.LaBackwardEvents()
+        for sl in slots:
+            kev.start[sl], kev.stop[sl] = ev[i][sl][0], ev[i][sl][1]
+        kevs.append(kev)
+    done = 0
+    while done < args.steps:
+        n = min(R, args.steps - done)
+        with torch.cuda.stream(stream):
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(20_000_000)
+            for i in range(n):
+                step(done + i, stream=stream, events=kevs[i])
+        torch.cuda.synchronize()
+        for i in range(n):
+            for sl in slots:
+                if kevs[i].launched[sl]:
+                    durs[sl].append(hev.elapsed_ms(*ev[i][sl]))
+        done += n
+    for e in ev:
+        for a_, b_ in e.values():
+            hev.destroy(a_)
+            hev.destroy(b_)
+    avg_us = {sl: 1e3 * sum(v) / len(v) for sl, v in durs.items() if v}
+    which = "dq" if avg_us[la.LA_BSLOT_DQ] >= avg_us[la.LA_BSLOT_DKV] else "dkv"
+    kern_ms = avg_us[la.LA_BSLOT_DQ if which == "dq" else la.LA_BSLOT_DKV] * 1e-3
+    flops = backward_alg_flops(wl, which)
+    ach = flops / (kern_ms * 1e-3) / 1e12
+    kname = kernel_symbol(wl, which)
+    roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": ach / FP32_VECTOR_PEAK_TFS, "traffic": stored_traffic(wl, kname), "kernel": kname,
+            "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
+            "timing": "hip events around each kernel, launches queued back to back"}
+    names = {la.LA_BSLOT_FWD_SUMS: "fwd_sums", la.LA_BSLOT_FWD_SCAN: "fwd_scan", la.LA_BSLOT_DQ: "dq",
+             la.LA_BSLOT_RSCAN: "rscan", la.LA_BSLOT_DKV: "dkv"}
+    tokens = wl.B * wl.H * wl.N
+    extra = {"kernel_avg_us": {names[sl]: round(v, 2) for sl, v in avg_us.items()},
+             "rotated_input_sets": R,
+             "step_hbm_frac": tokens * (3 * wl.dk + 4 * wl.dv) * elem_bytes(wl.dtype) / (ms_per_step * 1e-3) /
+             (HBM_PEAK_GBS * 1e9)}
+    return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, (fi, dO_h)
+
+
+def run_cpu_baseline_backward(wl, fi, dO_h, seconds):
+    """Time the fp64 oracle's backward (reverse-mode through the recurrence) on a sample of slices."""
+    import oracle
+    nthreads = oracle.num_threads()
+    BH = wl.B * wl.H
+    shp = lambda x, d: x.reshape(1, BH, wl.N, d)  # noqa: E731
+    Q, K, V, G = shp(fi.Q.f32, wl.dk), shp(fi.K.f32, wl.dk), shp(fi.V.f32, wl.dv), shp(dO_h.f32, wl.dv)
+    t0 = time.perf_counter()
+    oracle.causal_backward(wl.phi, Q[:, :1], K[:, :1], V[:, :1], G[:, :1], W=fi.W)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(BH, round(seconds * nthreads / max(t1, 1e-6)))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.causal_backward(wl.phi, Q[:, :n], K[:, :n], V[:, :n], G[:, :n], W=fi.W)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 100000:
+            break
+    return {"value": reps * n * wl.N / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 backward through the recurrence on {n} of {BH} (b,h) slices x {wl.N} tokens, "
+                      f"{reps} pass(es), {el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
+
+
 def bench_decode(args, wl):
     import torch
     from kernelized_linear_attention_la_amd import inputs
@@ -452,6 +599,9 @@ def main():
     if wl.decode_steps:
         value, ms, roof, extra, fi = bench_decode(args, wl)
         metric = "decode tokens/s"
+    elif wl.backward:
+        value, ms, roof, extra, fi = bench_backward(args, wl)
+        metric = "causal linear-attn bwd tokens/s (B*H*N/s)"
     else:
         value, ms, roof, extra, fi = bench_forward(args, wl)
         metric = ("causal retention fwd tokens/s (B*H*N/s)" if wl.retention
@@ -460,6 +610,8 @@ def main():
     if args.cpu_seconds > 0:
         if wl.decode_steps:
             cpu = run_cpu_baseline_decode(wl, fi, args.cpu_seconds)
+        elif wl.backward:
+            cpu = run_cpu_baseline_backward(wl, fi[0], fi[1], args.cpu_seconds)
         else:
             cpu = run_cpu_baseline(wl, fi, args.cpu_seconds)
     config = {"workload": wl.name, "phi": wl.phi, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,

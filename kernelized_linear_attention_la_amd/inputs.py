@@ -194,6 +194,7 @@ class Workload:
     modes: tuple = ("causal",)
     decode_steps: int = 0  # > 0: N is the prefix length, then this many decode steps
     retention: bool = False  # decayed, unnormalised variant (per-head decays, no normaliser)
+    backward: bool = False   # gradients of the causal form for a seeded dL/dO
 
     @property
     def dprime(self) -> int:
@@ -228,6 +229,11 @@ WORKLOADS = {
                  retention=True),
         Workload("ret_bf16_b2h16n16384d128_c128", 8, "identity", "bf16", 2, 16, 16384, 128, 128,
                  1.0 / math.sqrt(128), 128, retention=True),
+        # backward of the causal form at the bf16 forward workloads' shapes
+        Workload("bwd_elu1_bf16_b4h8n2048d64_c64", 9, "elu1", "bf16", 4, 8, 2048, 64, 64,
+                 1.0 / math.sqrt(64), 64, backward=True),
+        Workload("bwd_elu1_bf16_b2h16n16384d128_c128", 10, "elu1", "bf16", 2, 16, 16384, 128, 128,
+                 1.0 / math.sqrt(128), 128, backward=True),
     ]
 }
 

@@ -96,7 +96,7 @@ def main():
     from kernelized_linear_attention_la_amd import inputs
     import bench
     wl = inputs.WORKLOADS[args.workload]
-    slot = "decode" if wl.decode_steps else "chunk"
+    slot = "decode" if wl.decode_steps else ("dq" if wl.backward else "chunk")
     kernel = bench.kernel_symbol(wl, slot)
     out = os.path.join(args.out, wl.name)
     os.makedirs(out, exist_ok=True)
@@ -138,6 +138,8 @@ def main():
     bytes_per_launch = kf * 1024.0 * scale_f + kw * 1024.0 * scale_w
     if wl.decode_steps:
         alg = bench.decode_alg_bytes(wl)
+    elif wl.backward:  # Q, K, V, dO read, dQ, dK, dV written (whole backward)
+        alg = wl.B * wl.H * wl.N * (3 * wl.dk + 4 * wl.dv) * bench.elem_bytes(wl.dtype)
     else:
         alg = wl.B * wl.H * wl.N * (2 * wl.dk + 2 * wl.dv) * bench.elem_bytes(wl.dtype)
     src = hip_build.source_hash(kernel)
