@@ -61,6 +61,8 @@ def lib():
         L.ora_retention_chunked.argtypes = [i, i, i, i, i, i, i, D, D, D, D, D, D, i, D, D]
         L.ora_retention_decode_step.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D]
         L.ora_causal_backward.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D, D, D, D, D, D, D, D]
+        L.ora_gla_recurrent.argtypes = [i, i, i, i, D, D, D, D, D, D, D]
+        L.ora_delta_recurrent.argtypes = [i, i, i, i, D, D, D, D, D, D, D, D]
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_set_num_threads.argtypes = [i]
         _lib = L
@@ -280,3 +282,31 @@ def retention_decode_step(phi_kind, q, k, v, S, gamma, W=None):
     lib().ora_retention_decode_step(BH, H, dk, dv, _kind(phi_kind), m, _p(Wd), _p(g), _p(q.reshape(BH, dk)),
                                     _p(k.reshape(BH, dk)), _p(v.reshape(BH, dv)), _p(Sn), _p(o))
     return o.reshape(B, H, dv), Sn.reshape(B, H, dp, dv)
+
+
+# ---------------------------------------------------------------------------
+# Gated and delta-rule states ("Linear Attention", GLA and the delta rule;
+# "Story of Attention Part 5", section 7).  Raw q, k; S feature-major [dk, dv].
+# ---------------------------------------------------------------------------
+def gla_recurrent(Q, K, V, alpha, S_in=None):
+    """S_t = diag(alpha_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t; alpha [B,H,N,dk]. Returns O, S_final."""
+    Qf, Kf, Vf, _, B, H, BH, N, dk, dv, _, _ = _prep("identity", Q, K, V, None)
+    A = _d(alpha).reshape(BH, N, dk)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dk, dv))
+    lib().ora_gla_recurrent(BH, N, dk, dv, _p(Qf), _p(Kf), _p(Vf), _p(A), _p(_rstate_in(S_in, BH, dk, dv)),
+                            _p(O), _p(S))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dk, dv)
+
+
+def delta_recurrent(Q, K, V, beta, alpha=None, S_in=None):
+    """Gated delta rule: S_t = a_t S_{t-1} + b_t k_t (v_t - a_t S_{t-1}^T k_t)^T, o_t = S_t^T q_t.
+
+    beta, alpha [B,H,N] (alpha None: the plain delta rule). Returns O, S_final.
+    """
+    Qf, Kf, Vf, _, B, H, BH, N, dk, dv, _, _ = _prep("identity", Q, K, V, None)
+    b = _d(beta).reshape(BH, N)
+    a = None if alpha is None else _d(alpha).reshape(BH, N)
+    O = np.empty((BH, N, dv)); S = np.empty((BH, dk, dv))
+    lib().ora_delta_recurrent(BH, N, dk, dv, _p(Qf), _p(Kf), _p(Vf), _p(a), _p(b),
+                              _p(_rstate_in(S_in, BH, dk, dv)), _p(O), _p(S))
+    return O.reshape(B, H, N, dv), S.reshape(B, H, dk, dv)

@@ -621,3 +621,78 @@ void ora_causal_backward(int BH, int N, int dk, int dv, int kind, int m, const d
         free(S); free(z); free(psi); free(g); free(h); free(kap); free(num); free(dphi);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Gated and delta-rule states ("Linear Attention" (aiwiki.ai), the GLA gated
+ * recurrence and the delta-rule update; "Story of Attention Part 5", section 7
+ * Gated DeltaNet).  Raw q, k (no feature map), no normaliser; the state is
+ * feature-major S [dk][dv] as everywhere in this file, so the page's S k
+ * (what the state returns for key k) is S^T k here, and the page's outer
+ * product x k^T is k x^T here.  Output after the update: o_t = S_t^T q_t.
+ *
+ * GLA with a diagonal gate over the key channels (the gate matrix G_t =
+ * alpha_t 1^T multiplies row f of S by alpha_t[f]):
+ *   S_t = diag(alpha_t) S_{t-1} + k_t v_t^T,        alpha [BH, N, dk]
+ * ------------------------------------------------------------------------- */
+void ora_gla_recurrent(int BH, int N, int dk, int dv, const double *Q, const double *K, const double *V,
+                       const double *A, const double *S_in, double *O, double *S_out) {
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        const double *a = A + (size_t)s * N * dk;
+        double *S = (double *)calloc((size_t)dk * dv, sizeof(double));
+        if (S_in) memcpy(S, S_in + (size_t)s * dk * dv, sizeof(double) * dk * dv);
+        for (int t = 0; t < N; ++t) {
+            for (int f = 0; f < dk; ++f)
+                for (int c = 0; c < dv; ++c)
+                    S[(size_t)f * dv + c] = a[(size_t)t * dk + f] * S[(size_t)f * dv + c] +
+                                            k[(size_t)t * dk + f] * v[(size_t)t * dv + c];
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < dk; ++f) acc += q[(size_t)t * dk + f] * S[(size_t)f * dv + c];
+                O[((size_t)s * N + t) * dv + c] = acc;
+            }
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dk * dv, S, sizeof(double) * dk * dv);
+        free(S);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Gated delta rule [SOA5 7]: with a scalar forget gate alpha_t (1 when alpha
+ * is NULL: the plain delta rule) and write strength beta_t,
+ *   prediction  p_t = alpha_t S_{t-1}^T k_t
+ *   S_t = alpha_t S_{t-1} + beta_t k_t (v_t - p_t)^T,   o_t = S_t^T q_t.
+ * alpha, beta [BH, N].
+ * ------------------------------------------------------------------------- */
+void ora_delta_recurrent(int BH, int N, int dk, int dv, const double *Q, const double *K, const double *V,
+                         const double *alpha, const double *beta, const double *S_in, double *O,
+                         double *S_out) {
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < BH; ++s) {
+        const double *q = Q + (size_t)s * N * dk, *k = K + (size_t)s * N * dk, *v = V + (size_t)s * N * dv;
+        double *S = (double *)calloc((size_t)dk * dv, sizeof(double));
+        double *pred = (double *)malloc(sizeof(double) * dv);
+        if (S_in) memcpy(S, S_in + (size_t)s * dk * dv, sizeof(double) * dk * dv);
+        for (int t = 0; t < N; ++t) {
+            const double a = alpha ? alpha[(size_t)s * N + t] : 1.0;
+            const double b = beta[(size_t)s * N + t];
+            const double *kt = k + (size_t)t * dk;
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < dk; ++f) acc += S[(size_t)f * dv + c] * kt[f];
+                pred[c] = a * acc;
+            }
+            for (int f = 0; f < dk; ++f)
+                for (int c = 0; c < dv; ++c)
+                    S[(size_t)f * dv + c] = a * S[(size_t)f * dv + c] + b * kt[f] * (v[(size_t)t * dv + c] - pred[c]);
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < dk; ++f) acc += q[(size_t)t * dk + f] * S[(size_t)f * dv + c];
+                O[((size_t)s * N + t) * dv + c] = acc;
+            }
+        }
+        if (S_out) memcpy(S_out + (size_t)s * dk * dv, S, sizeof(double) * dk * dv);
+        free(S); free(pred);
+    }
+}
