@@ -265,6 +265,30 @@ la_status la_backward_causal_chunked(const la_problem *p, int chunk,
                                      void *ws, size_t ws_bytes, void *stream,
                                      la_backward_events *ev);
 
+/*
+ * Gated and delta-rule states, run as the recurrence token by token ("Linear
+ * Attention" (aiwiki.ai), GLA's gated recurrence and the delta-rule update;
+ * "Story of Attention Part 5", section 7 Gated DeltaNet).  Raw q and k (p->phi
+ * must be LA_PHI_IDENTITY), no normaliser, state S [B,H,d_k,d_v] fp32
+ * feature-major (the pages' S k, the value the state returns for key k, is
+ * S^T k here), output read after the update: o_t = S_t^T q_t.
+ *   GLA:   S_t = diag(alpha_t) S_{t-1} + k_t v_t^T, a gate per key channel,
+ *          alpha [B,H,N,d_k] fp32.
+ *   delta: p_t = alpha_t S_{t-1}^T k_t,  S_t = alpha_t S_{t-1} + beta_t k_t (v_t - p_t)^T,
+ *          beta [B,H,N] fp32 (write strength), alpha [B,H,N] fp32 scalar
+ *          forget gate or NULL (alpha = 1: the plain delta rule).
+ * Q, K [B,H,N,d_k], V, O [B,H,N,d_v] of dtype p->dtype; the state stays fp32
+ * and every step is computed in fp32 in token order.  S_in NULL = zero;
+ * S_out (may be S_in, may be NULL) receives the final state.  N = 1 is the
+ * decode step.  One workgroup per (b, h): no workspace.
+ */
+la_status la_forward_gla_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
+                                   const float *alpha, const float *S_in, float *S_out, void *O, void *stream);
+
+la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
+                                     const float *alpha, const float *beta, const float *S_in, float *S_out,
+                                     void *O, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -518,3 +518,45 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
                ? LA_OK
                : LA_ERR_DEVICE;
 }
+
+// ---------------------------------------------------------------------------
+// Gated and delta-rule recurrences (kernel in la_gated.hip)
+// ---------------------------------------------------------------------------
+namespace la {
+namespace {
+
+la_status gated_call(const la_problem *p, bool gla, const void *Q, const void *K, const void *V, const float *alpha,
+                     const float *beta, const float *S_in, float *S_out, void *O, void *stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // raw q, k
+    if (!Q || !K || !V || !O) return LA_ERR_NULL;
+    if (gla ? !alpha : !beta) return LA_ERR_NULL;
+    const void *ptrs[] = {Q, K, V, O, S_in, S_out};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return LA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u)) return LA_ERR_ALIGN;
+    GatedArgs a;
+    a.BH = p->B * p->H; a.N = p->N; a.dk = p->d_k; a.dv = p->d_v;
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.alpha = alpha; a.beta = gla ? nullptr : beta;
+    a.S_in = S_in; a.S_out = S_out;
+    return launch_gated(a, gla, p->dtype == LA_BF16 ? kBF16 : kF32, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LA_OK
+               : LA_ERR_DEVICE;
+}
+
+}  // namespace
+}  // namespace la
+
+LA_API la_status la_forward_gla_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
+                                          const float *alpha, const float *S_in, float *S_out, void *O,
+                                          void *stream) {
+    return gated_call(p, true, Q, K, V, alpha, nullptr, S_in, S_out, O, stream);
+}
+
+LA_API la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
+                                            const float *alpha, const float *beta, const float *S_in, float *S_out,
+                                            void *O, void *stream) {
+    return gated_call(p, false, Q, K, V, alpha, beta, S_in, S_out, O, stream);
+}

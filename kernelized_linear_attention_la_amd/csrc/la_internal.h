@@ -145,6 +145,18 @@ struct BwdLaunch {
     float *dS_in, *dz_in;           // NULL = not wanted
 };
 bool backward_supported(const Shape &sh);
+
+// Gated / delta-rule recurrences (la_gated.hip): one workgroup per slice.
+struct GatedArgs {
+    int BH, N, dk, dv;
+    const void *Q, *K, *V;
+    void *O;
+    const float *alpha;  // GLA: [BH, N, dk]; delta rule: [BH, N] or NULL (no gate)
+    const float *beta;   // delta rule: [BH, N]; GLA: unused
+    const float *S_in;   // [BH, dk, dv] or NULL (zero)
+    float *S_out;        // [BH, dk, dv] or NULL; may be S_in
+};
+hipError_t launch_gated(const GatedArgs &a, bool gla, int dtype, hipStream_t stream, KEvents ev = {});
 size_t backward_lds_bytes(const Shape &sh);
 hipError_t launch_backward(const BwdLaunch &b, hipStream_t stream, KEvents ev_dq = {}, KEvents ev_scan = {},
                            KEvents ev_dkv = {});

@@ -11,7 +11,8 @@ Recipe (every workload):
     round to fp32 (round-to-nearest-even), and for bf16 workloads round the
     fp32 value once more to bf16 (round-to-nearest-even);
   * tensor ids: Q=0, K=1, V=2, W=3, decode q=4, k=5, v=6, and for the
-    backward dO=7, dS_out=8, dz_out=9, S_in=10, z_in=11.
+    backward dO=7, dS_out=8, dz_out=9, S_in=10, z_in=11; gated states: GLA gate
+    12, scalar gate 13, write strength 14.
 
 The FAVOR+ projection W (m rows of dimension d) is an *input*: the random
 features of the Performer map are drawn here once and handed to both sides.
@@ -32,6 +33,7 @@ import numpy as np
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_W = 0, 1, 2, 3
 TENSOR_QSTEP, TENSOR_KSTEP, TENSOR_VSTEP = 4, 5, 6
 TENSOR_DO, TENSOR_DS, TENSOR_DZ, TENSOR_SIN, TENSOR_ZIN = 7, 8, 9, 10, 11
+TENSOR_GATE_CH, TENSOR_GATE, TENSOR_BETA = 12, 13, 14
 
 
 # ---------------------------------------------------------------------------
@@ -308,6 +310,39 @@ def positive_state(wid: int, B, H, dp, dv, tokens=64):
     u = normal_bhnd(wid, TENSOR_ZIN, (B, H, 1, dp), 1.0, "f32").f32.reshape(B, H, dp)
     z = (tokens * (1.0 + 0.5 * np.tanh(u))).astype(np.float32)
     return np.ascontiguousarray(S), np.ascontiguousarray(z)
+
+
+@dataclass
+class GatedInputs:
+    Q: HostTensor
+    K: HostTensor
+    V: HostTensor
+    alpha_ch: np.ndarray   # GLA gate per key channel, fp32 [B, H, N, d_k] in (0.9, 1)
+    alpha: np.ndarray      # scalar forget gate, fp32 [B, H, N] in (0.95, 1)
+    beta: np.ndarray       # write strength, fp32 [B, H, N] in (0, 1)
+
+
+def gated_inputs(wid: int, B, H, N, dk, dv, dtype="f32", workers=None) -> GatedInputs:
+    """Seeded inputs of the gated / delta-rule recurrences.
+
+    q, v ~ N(0, 1/d); keys are N(0, I) rows scaled to unit length in fp64 before
+    rounding (the delta rule's erase step I - beta k k^T then stays a
+    contraction for beta in [0, 1]).  Gates and strengths are logistic
+    transforms of seeded normals: alpha_ch = 1 - 0.1 s, alpha = 1 - 0.05 s,
+    beta = s, s = 1 / (1 + exp(-x)).
+    """
+    sc = 1.0 / math.sqrt(dk)
+    Q = normal_bhnd(wid, TENSOR_Q, (B, H, N, dk), sc, dtype, workers=workers)
+    Kraw = normal_bhnd(wid, TENSOR_K, (B, H, N, dk), 1.0, "f32", workers=workers).f32.astype(np.float64)
+    Kraw /= np.maximum(np.linalg.norm(Kraw, axis=-1, keepdims=True), 1e-30)
+    K = _round_to(Kraw, dtype)
+    V = normal_bhnd(wid, TENSOR_V, (B, H, N, dv), 1.0 / math.sqrt(dv), dtype, workers=workers)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x.astype(np.float64)))  # noqa: E731
+    ach = normal_bhnd(wid, TENSOR_GATE_CH, (B, H, N, dk), 1.0, "f32", workers=workers).f32
+    al = normal_bhnd(wid, TENSOR_GATE, (B, H, N, 1), 1.0, "f32").f32.reshape(B, H, N)
+    be = normal_bhnd(wid, TENSOR_BETA, (B, H, N, 1), 1.0, "f32").f32.reshape(B, H, N)
+    return GatedInputs(Q, K, V, (1.0 - 0.1 * sig(ach)).astype(np.float32), (1.0 - 0.05 * sig(al)).astype(np.float32),
+                       sig(be).astype(np.float32))
 
 
 if __name__ == "__main__":

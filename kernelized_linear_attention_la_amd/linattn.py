@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYP
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
             "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
             "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step",
-            "la_backward_workspace_bytes", "la_backward_causal_chunked")
+            "la_backward_workspace_bytes", "la_backward_causal_chunked", "la_forward_gla_recurrent",
+            "la_forward_delta_recurrent")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 LA_BSLOT_FWD_SUMS, LA_BSLOT_FWD_SCAN, LA_BSLOT_DQ, LA_BSLOT_RSCAN, LA_BSLOT_DKV, LA_BSLOTS = 0, 1, 2, 3, 4, 5
 
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.la_backward_causal_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                  ctypes.POINTER(LaBackwardEvents)]
         L.la_backward_causal_chunked.restype = i
+        L.la_forward_gla_recurrent.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.la_forward_gla_recurrent.restype = i
+        L.la_forward_delta_recurrent.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.la_forward_delta_recurrent.restype = i
         _lib = L
     return _lib
 
@@ -373,3 +378,52 @@ def la_backward_causal_chunked(q, k, v, dO, chunk=64, phi="elu1", W=None, S_in=N
                                           None if events is None else ctypes.byref(events))
     _raise(st, "la_backward_causal_chunked")
     return dQ, dK, dV, dS_in, dz_in
+
+
+# ---------------------------------------------------------------------------
+# Gated and delta-rule states (token-by-token recurrence)
+# ---------------------------------------------------------------------------
+def _gate(x, shape, device, what):
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_contiguous() or x.device != device \
+            or tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{what} must be a contiguous float32 device tensor of shape {tuple(shape)}")
+    return x
+
+
+def _gated_common(q, k, v, S_in, S_out, out):
+    _check_qkv(q, k, v)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    p = problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_IDENTITY, 0, 0)
+    S_in = _state_only(S_in, B, H, dk, dv, q.device, "initial state")
+    S_out = _state_only(S_out, B, H, dk, dv, q.device, "final state")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    return p, S_in, S_out, out
+
+
+def la_forward_gla_recurrent(q, k, v, alpha, S_in=None, S_out=None, out=None, stream=None):
+    """GLA with a per-key-channel gate: S_t = diag(alpha_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+
+    alpha: float32 [B, H, N, d_k].  Returns O."""
+    p, S_in, S_out, out = _gated_common(q, k, v, S_in, S_out, out)
+    alpha = _gate(alpha, q.shape, q.device, "alpha")
+    st = lib().la_forward_gla_recurrent(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(S_in),
+                                        _ptr(S_out), _ptr(out), _stream(stream))
+    _raise(st, "la_forward_gla_recurrent")
+    return out
+
+
+def la_forward_delta_recurrent(q, k, v, beta, alpha=None, S_in=None, S_out=None, out=None, stream=None):
+    """Gated delta rule: S_t = a_t S_{t-1} + b_t k_t (v_t - a_t S_{t-1}^T k_t)^T, o_t = S_t^T q_t.
+
+    beta, alpha: float32 [B, H, N] (alpha None: the plain delta rule).  Returns O."""
+    p, S_in, S_out, out = _gated_common(q, k, v, S_in, S_out, out)
+    beta = _gate(beta, q.shape[:3], q.device, "beta")
+    alpha = _gate(alpha, q.shape[:3], q.device, "alpha")
+    st = lib().la_forward_delta_recurrent(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(S_in), _ptr(S_out), _ptr(out), _stream(stream))
+    _raise(st, "la_forward_delta_recurrent")
+    return out

@@ -200,3 +200,19 @@ def test_backward_validation():
     assert bwd(ws=None) == 6
     assert bwd(wsb=need - 1) == 6
     assert bwd(p=_p(B=0)) == 2
+
+
+def test_gated_validation():
+    L = linattn.lib()
+    pid = _p(phi=linattn.LA_PHI_IDENTITY)
+    assert L.la_forward_gla_recurrent(ctypes.byref(_p()), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == 4
+    assert L.la_forward_gla_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    assert L.la_forward_gla_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1
+    assert L.la_forward_gla_recurrent(ctypes.byref(pid), MIS, FAKE, FAKE, FAKE, None, None, FAKE, None) == 5
+    assert L.la_forward_gla_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100002), None, None,
+                                      FAKE, None) == 5
+    # delta: beta required, alpha optional
+    assert L.la_forward_delta_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    assert L.la_forward_delta_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, None, FAKE, MIS, None, FAKE, None) == 5
+    assert L.la_forward_delta_recurrent(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=129)), FAKE, FAKE, FAKE,
+                                        None, FAKE, None, None, FAKE, None) == 2

@@ -1,0 +1,92 @@
+"""GPU parity of the gated and delta-rule recurrences (la_forward_gla_recurrent,
+la_forward_delta_recurrent, through the C ABI) against the oracle.
+
+Outputs: per (b, h) slice max |gpu - oracle| / max |oracle| (slice_rel_err);
+final states: state_rel_err.  1e-4 for fp32 storage, 2e-2 for bf16 (fp32
+state and arithmetic, outputs rounded once).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kernelized_linear_attention_la_amd import inputs
+from kernelized_linear_attention_la_amd import linattn as la
+from tests.parity import slice_rel_err, state_rel_err, to_device, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gated]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+CASES = [
+    # (B, H, N, dk, dv, dtype, with S_in)
+    (1, 2, 256, 64, 64, "f32", False),
+    (2, 3, 100, 16, 8, "f32", True),
+    (1, 1, 1, 32, 32, "f32", True),       # one token: the decode step
+    (1, 2, 77, 5, 3, "f32", True),        # odd widths, columns not a multiple of 8
+    (1, 1, 50, 128, 128, "f32", True),    # largest widths
+    (2, 4, 1000, 128, 128, "bf16", False),
+    (4, 8, 2048, 64, 64, "bf16", True),   # the bf16 d = 64 forward workload's shape
+]
+
+
+def _run(ci, case, kind):
+    B, H, N, dk, dv, dtype, state = case
+    gi = inputs.gated_inputs(2000 + ci, B, H, N, dk, dv, dtype)
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    S_in = inputs.positive_state(2000 + ci, B, H, dk, dv, tokens=4)[0] if state else None
+    dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    S_out = torch.empty(B, H, dk, dv, device="cuda")
+    if kind == "gla":
+        O = la.la_forward_gla_recurrent(q, k, v, dev(gi.alpha_ch), S_in=dev(S_in), S_out=S_out)
+        ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch, S_in=S_in)
+    else:
+        alpha = gi.alpha if kind == "gated_delta" else None
+        O = la.la_forward_delta_recurrent(q, k, v, dev(gi.beta), alpha=dev(alpha), S_in=dev(S_in), S_out=S_out)
+        ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=alpha, S_in=S_in)
+    torch.cuda.synchronize()
+    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    _say(kind, case, f"O {eo:.2e} S {es:.2e}")
+    tol = tol_for(dtype)
+    assert eo < tol and es < tol, (eo, es)
+
+
+@pytest.mark.parametrize("kind", ["gla", "delta", "gated_delta"])
+@pytest.mark.parametrize("ci", range(len(CASES)),
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}dk{c[3]}dv{c[4]}{c[5]}{'S' if c[6] else ''}" for c in CASES])
+def test_gated_against_oracle(ci, kind):
+    _run(ci, CASES[ci], kind)
+
+
+def test_state_handoff_in_place():
+    """Two calls (0..M, then M..N from the first call's state, S_out aliasing S_in) == one call."""
+    B, H, N, d = 2, 2, 300, 32
+    gi = inputs.gated_inputs(2100, B, H, N, d, d, "f32")
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    be, al = torch.from_numpy(gi.beta).cuda(), torch.from_numpy(gi.alpha).cuda()
+    ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=gi.alpha)
+    for M in (1, 100, 299):
+        _say("handoff M", M)
+        S = torch.zeros(B, H, d, d, device="cuda")
+        c = lambda x, a, b: x[:, :, a:b].contiguous()  # noqa: E731
+        O1 = la.la_forward_delta_recurrent(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(be, 0, M), alpha=c(al, 0, M),
+                                           S_out=S)
+        O2 = la.la_forward_delta_recurrent(c(q, M, N), c(k, M, N), c(v, M, N), c(be, M, N), alpha=c(al, M, N),
+                                           S_in=S, S_out=S)
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
+        assert state_rel_err(to_f64(S), Sref) < 1e-4
