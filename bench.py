@@ -217,6 +217,8 @@ def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
+    if wl.gated:
+        return f"k_gated<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {'true' if wl.gated == 'gla' else 'false'}>"
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
         return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}, {'true' if wl.retention else 'false'}>"
@@ -493,6 +495,102 @@ def bench_backward(args, wl):
     return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, (fi, dO_h)
 
 
+def gated_alg_flops(wl):
+    """Flops of one token-by-token pass: per token GLA updates S (2 d_k d_v) and
+    reads S^T q (2 d_k d_v); the gated delta rule adds S^T k (2 d_k d_v) and its
+    update costs 3 d_k d_v (scale, scale, add)."""
+    per = 4 * wl.dk * wl.dv if wl.gated == "gla" else 7 * wl.dk * wl.dv
+    return wl.B * wl.H * wl.N * per
+
+
+def bench_gated(args, wl):
+    """One step = one gated recurrence over the whole batch (every (b, h) slice, all N tokens)."""
+    import numpy as np
+    import torch
+    from kernelized_linear_attention_la_amd import inputs
+    from kernelized_linear_attention_la_amd import linattn as la
+
+    gi = inputs.gated_inputs(wl.wid, wl.B, wl.H, wl.N, wl.dk, wl.dv, wl.dtype)
+    dev = torch.device("cuda:0")
+
+    def to_dev(ht):
+        t = torch.from_numpy(ht.store)
+        return (t.view(torch.bfloat16) if ht.dtype == "bf16" else t).to(dev)
+
+    q, k, v = to_dev(gi.Q), to_dev(gi.K), to_dev(gi.V)
+    a_ch = torch.from_numpy(np.ascontiguousarray(gi.alpha_ch)).to(dev)
+    al, be = torch.from_numpy(gi.alpha).to(dev), torch.from_numpy(gi.beta).to(dev)
+    S = torch.zeros(wl.B, wl.H, wl.dk, wl.dv, device=dev)
+    o = torch.empty_like(v)
+    raw = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        if wl.gated == "gla":
+            la.la_forward_gla_recurrent(q, k, v, a_ch, S_out=S, out=o)
+        else:
+            la.la_forward_delta_recurrent(q, k, v, be, alpha=al, S_out=S, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hev = HipEvents(la.lib())
+    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        hev.record(pairs[i][0], raw)
+        step()
+        hev.record(pairs[i][1], raw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [hev.elapsed_ms(a_, b_) for a_, b_ in pairs]
+    for a_, b_ in pairs:
+        hev.destroy(a_)
+        hev.destroy(b_)
+    kern_ms = sum(durs) / len(durs)
+    ms_per_step = elapsed * 1e3 / args.steps
+    flops = gated_alg_flops(wl)
+    ach = flops / (kern_ms * 1e-3) / 1e12
+    kname = kernel_symbol(wl, "chunk")
+    roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": ach / FP32_VECTOR_PEAK_TFS, "traffic": stored_traffic(wl, kname), "kernel": kname,
+            "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
+            "timing": "hip events around each launch"}
+    tokens = wl.B * wl.H * wl.N
+    extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
+    return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, gi
+
+
+def run_cpu_baseline_gated(wl, gi, seconds):
+    """Time the fp64 oracle's recurrence on a sample of slices."""
+    import oracle
+    nthreads = oracle.num_threads()
+    BH = wl.B * wl.H
+    r4 = lambda x, d: x.reshape(1, BH, wl.N, d)  # noqa: E731
+    Q, K, V = r4(gi.Q.f32, wl.dk), r4(gi.K.f32, wl.dk), r4(gi.V.f32, wl.dv)
+    ach, al, be = r4(gi.alpha_ch, wl.dk), gi.alpha.reshape(1, BH, wl.N), gi.beta.reshape(1, BH, wl.N)
+
+    def run(n):
+        if wl.gated == "gla":
+            oracle.gla_recurrent(Q[:, :n], K[:, :n], V[:, :n], ach[:, :n])
+        else:
+            oracle.delta_recurrent(Q[:, :n], K[:, :n], V[:, :n], be[:, :n], alpha=al[:, :n])
+    t0 = time.perf_counter()
+    run(1)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(BH, round(seconds * nthreads / max(t1, 1e-6)))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        run(n)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 100000:
+            break
+    return {"value": reps * n * wl.N / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"fp64 {wl.gated} recurrence on {n} of {BH} (b,h) slices x {wl.N} tokens, {reps} pass(es), "
+                      f"{el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
+
+
 def run_cpu_baseline_backward(wl, fi, dO_h, seconds):
     """Time the fp64 oracle's backward (reverse-mode through the recurrence) on a sample of slices."""
     import oracle
@@ -602,6 +700,10 @@ def main():
     elif wl.backward:
         value, ms, roof, extra, fi = bench_backward(args, wl)
         metric = "causal linear-attn bwd tokens/s (B*H*N/s)"
+    elif wl.gated:
+        value, ms, roof, extra, fi = bench_gated(args, wl)
+        metric = ("GLA recurrence tokens/s (B*H*N/s)" if wl.gated == "gla"
+                  else "gated delta-rule recurrence tokens/s (B*H*N/s)")
     else:
         value, ms, roof, extra, fi = bench_forward(args, wl)
         metric = ("causal retention fwd tokens/s (B*H*N/s)" if wl.retention
@@ -612,6 +714,8 @@ def main():
             cpu = run_cpu_baseline_decode(wl, fi, args.cpu_seconds)
         elif wl.backward:
             cpu = run_cpu_baseline_backward(wl, fi[0], fi[1], args.cpu_seconds)
+        elif wl.gated:
+            cpu = run_cpu_baseline_gated(wl, fi, args.cpu_seconds)
         else:
             cpu = run_cpu_baseline(wl, fi, args.cpu_seconds)
     config = {"workload": wl.name, "phi": wl.phi, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,

@@ -197,6 +197,7 @@ class Workload:
     decode_steps: int = 0  # > 0: N is the prefix length, then this many decode steps
     retention: bool = False  # decayed, unnormalised variant (per-head decays, no normaliser)
     backward: bool = False   # gradients of the causal form for a seeded dL/dO
+    gated: str = ""          # "gla" or "delta" (gated delta rule): token-by-token recurrences
 
     @property
     def dprime(self) -> int:
@@ -236,6 +237,11 @@ WORKLOADS = {
                  1.0 / math.sqrt(64), 64, backward=True),
         Workload("bwd_elu1_bf16_b2h16n16384d128_c128", 10, "elu1", "bf16", 2, 16, 16384, 128, 128,
                  1.0 / math.sqrt(128), 128, backward=True),
+        # gated / delta-rule states at the bf16 d = 64 shape (raw q, k; unit-norm keys)
+        Workload("gla_bf16_b4h8n2048d64", 11, "identity", "bf16", 4, 8, 2048, 64, 64, 1.0 / math.sqrt(64), 1,
+                 gated="gla"),
+        Workload("gdelta_bf16_b4h8n2048d64", 12, "identity", "bf16", 4, 8, 2048, 64, 64, 1.0 / math.sqrt(64), 1,
+                 gated="delta"),
     ]
 }
 

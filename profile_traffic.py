@@ -138,6 +138,9 @@ def main():
     bytes_per_launch = kf * 1024.0 * scale_f + kw * 1024.0 * scale_w
     if wl.decode_steps:
         alg = bench.decode_alg_bytes(wl)
+    elif wl.gated:  # q, k, v read, o written, gates read
+        alg = wl.B * wl.H * wl.N * ((2 * wl.dk + 2 * wl.dv) * bench.elem_bytes(wl.dtype) +
+                                    4 * (wl.dk if wl.gated == "gla" else 2))
     elif wl.backward:  # Q, K, V, dO read, dQ, dK, dV written (whole backward)
         alg = wl.B * wl.H * wl.N * (3 * wl.dk + 4 * wl.dv) * bench.elem_bytes(wl.dtype)
     else:
