@@ -25,7 +25,11 @@ _LIB = os.path.join(_HERE, "liblaoracle.so")
 PHI_ELU1 = 0
 PHI_FAVOR = 1
 PHI_IDENTITY = 2
-_PHI = {"elu1": PHI_ELU1, "favor": PHI_FAVOR, "identity": PHI_IDENTITY}
+PHI_DPFP = 3
+PHI_TRIG = 4
+PHI_COSFORMER = 5
+_PHI = {"elu1": PHI_ELU1, "favor": PHI_FAVOR, "identity": PHI_IDENTITY, "dpfp": PHI_DPFP, "trig": PHI_TRIG,
+        "cosformer": PHI_COSFORMER}
 
 
 def build(force: bool = False) -> str:
@@ -63,6 +67,9 @@ def lib():
         L.ora_causal_backward.argtypes = [i, i, i, i, i, i, D, D, D, D, D, D, D, D, D, D, D, D, D, D]
         L.ora_gla_recurrent.argtypes = [i, i, i, i, D, D, D, D, D, D, D]
         L.ora_delta_recurrent.argtypes = [i, i, i, i, D, D, D, D, D, D, D, D]
+        L.ora_set_map.argtypes = [i, ctypes.c_longlong]
+        L.ora_feature_dim.argtypes = [i, i, i]
+        L.ora_feature_dim.restype = i
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_set_num_threads.argtypes = [i]
         _lib = L
@@ -91,8 +98,19 @@ def _kind(phi):
     return _PHI[phi] if isinstance(phi, str) else int(phi)
 
 
+def set_map(param=0, pos0=0):
+    """Parameters of the maps that take one (DPFP: nu; cosFormer: the horizon M)
+    and the position of the first token (cosFormer).  They stay in effect for
+    every later call until set again."""
+    lib().ora_set_map(int(param), int(pos0))
+
+
+def feature_dim(phi, dk, m=0):
+    return lib().ora_feature_dim(_kind(phi), int(dk), int(m))
+
+
 def _dp(phi, dk, W):
-    return W.shape[0] if _kind(phi) == PHI_FAVOR else dk
+    return feature_dim(phi, dk, 0 if W is None else W.shape[0])
 
 
 def _flat4(x):
@@ -107,7 +125,7 @@ def phi(kind, X, W=None):
     n, d = X.shape
     Wd = _d(W) if W is not None else None
     m = Wd.shape[0] if Wd is not None else 0
-    dp = m if _kind(kind) == PHI_FAVOR else d
+    dp = feature_dim(kind, d, m)
     out = np.empty((n, dp))
     lib().ora_phi(_kind(kind), n, d, _p(X), m, _p(Wd), _p(out))
     return out
@@ -130,7 +148,7 @@ def _prep(phi_kind, Q, K, V, W):
     dv = Vf.shape[2]
     Wd = _d(W) if W is not None else None
     m = Wd.shape[0] if Wd is not None else 0
-    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    dp = feature_dim(phi_kind, dk, m)
     return Qf, Kf, Vf, Wd, B, H, BH, N, dk, dv, m, dp
 
 
@@ -210,7 +228,7 @@ def decode_step(phi_kind, q, k, v, S, z, W=None):
     BH = B * H
     Wd = _d(W) if W is not None else None
     m = Wd.shape[0] if Wd is not None else 0
-    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    dp = feature_dim(phi_kind, dk, m)
     Sn = _d(S).reshape(BH, dp, dv).copy()
     zn = _d(z).reshape(BH, dp).copy()
     qf = q.reshape(BH, dk); kf = k.reshape(BH, dk); vf = v.reshape(BH, dv)
@@ -275,7 +293,7 @@ def retention_decode_step(phi_kind, q, k, v, S, gamma, W=None):
     BH = B * H
     Wd = _d(W) if W is not None else None
     m = Wd.shape[0] if Wd is not None else 0
-    dp = m if _kind(phi_kind) == PHI_FAVOR else dk
+    dp = feature_dim(phi_kind, dk, m)
     g = _gamma(gamma, H)
     Sn = _d(S).reshape(BH, dp, dv).copy()
     o = np.empty((BH, dv))

@@ -54,6 +54,21 @@
 #define ORA_PHI_ELU1 0
 #define ORA_PHI_FAVOR 1
 #define ORA_PHI_IDENTITY 2
+#define ORA_PHI_DPFP 3
+#define ORA_PHI_TRIG 4
+#define ORA_PHI_COSFORMER 5
+
+/* Parameters of the maps that have one: DPFP's number of shifts nu, the
+ * cosFormer horizon M, and the position of the first token of a call (the
+ * cosFormer reweighting depends on absolute positions).  Set by
+ * ora_set_map before a call; 0 by default. */
+static int g_map_param = 0;
+static long long g_pos0 = 0;
+
+void ora_set_map(int param, long long pos0) {
+    g_map_param = param;
+    g_pos0 = pos0;
+}
 
 int ora_num_threads(void) {
 #ifdef _OPENMP
@@ -77,6 +92,15 @@ void ora_set_num_threads(int n) {
  * per coordinate.  For x > 0 that is x + 1; otherwise exp(x) - 1 + 1, which is
  * exp(x) exactly.  Output dimension dp = d.
  * FAVOR+ [SOA5 1b]: phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), r = 1..m.
+ * DPFP [LA feature-map table: concatenation of products of ReLU shifts]:
+ *   r = ReLU([x, -x]) (2d entries); for shift i = 1..nu, block i holds
+ *   r_j * r_{(j + i) mod 2d}, j = 0..2d-1.  Output dimension 2 d nu.
+ * Cosine / sine projections [LA feature-map table]: [cos(W x); sin(W x)],
+ *   cos(w_r . x) for r = 1..m, then sin(w_r . x).  Output dimension 2m.
+ * cosFormer [SOA5 3]: ReLU(x) times cos(pi p / 2M), then ReLU(x) times
+ *   sin(pi p / 2M), for the token at position p (counted from 0, plus the
+ *   call's first position); the product of two such features is
+ *   ReLU(q)^T ReLU(k) cos(pi (p_q - p_k) / 2M).  Output dimension 2d.
  * ------------------------------------------------------------------------- */
 static void phi_elu1_row(const double *x, int d, double *out) {
     for (int f = 0; f < d; ++f) out[f] = x[f] > 0.0 ? x[f] + 1.0 : exp(x[f]);
@@ -93,19 +117,71 @@ static void phi_favor_row(const double *x, int d, const double *W, int m, double
     }
 }
 
-static void phi_row(int kind, const double *x, int d, const double *W, int m, double *out) {
+static void phi_dpfp_row(const double *x, int d, int nu, double *out) {
+    const int n2 = 2 * d;
+    double *r = (double *)malloc(sizeof(double) * n2);
+    for (int j = 0; j < d; ++j) {
+        r[j] = x[j] > 0.0 ? x[j] : 0.0;
+        r[d + j] = -x[j] > 0.0 ? -x[j] : 0.0;
+    }
+    for (int i = 1; i <= nu; ++i)
+        for (int j = 0; j < n2; ++j) out[(size_t)(i - 1) * n2 + j] = r[j] * r[(j + i) % n2];
+    free(r);
+}
+
+static void phi_trig_row(const double *x, int d, const double *W, int m, double *out) {
+    for (int r = 0; r < m; ++r) {
+        double proj = 0.0;
+        for (int c = 0; c < d; ++c) proj += W[(size_t)r * d + c] * x[c];
+        out[r] = cos(proj);
+        out[m + r] = sin(proj);
+    }
+}
+
+static void phi_cosformer_row(const double *x, int d, long long pos, double *out) {
+    const double pi = 3.14159265358979323846;
+    const double ang = pi * (double)pos / (2.0 * (double)g_map_param);
+    const double cw = cos(ang), sw = sin(ang);
+    for (int c = 0; c < d; ++c) {
+        const double r = x[c] > 0.0 ? x[c] : 0.0;
+        out[c] = r * cw;
+        out[d + c] = r * sw;
+    }
+}
+
+/* phi of one row x [d] of the token at position `pos` within the call */
+static void phi_row(int kind, const double *x, int d, const double *W, int m, long long pos, double *out) {
     if (kind == ORA_PHI_FAVOR) phi_favor_row(x, d, W, m, out);
     else if (kind == ORA_PHI_IDENTITY) memcpy(out, x, sizeof(double) * d);
+    else if (kind == ORA_PHI_DPFP) phi_dpfp_row(x, d, g_map_param, out);
+    else if (kind == ORA_PHI_TRIG) phi_trig_row(x, d, W, m, out);
+    else if (kind == ORA_PHI_COSFORMER) phi_cosformer_row(x, d, g_pos0 + pos, out);
     else phi_elu1_row(x, d, out);
 }
 
-static int feat_dim(int kind, int dk, int m) { return kind == ORA_PHI_FAVOR ? m : dk; }
-
-/* phi applied to n rows of X [n, d] -> out [n, dp]. */
-void ora_phi(int kind, int n, int d, const double *X, int m, const double *W, double *out) {
-    int dp = feat_dim(kind, d, m);
-    for (int i = 0; i < n; ++i) phi_row(kind, X + (size_t)i * d, d, W, m, out + (size_t)i * dp);
+static int feat_dim(int kind, int dk, int m) {
+    switch (kind) {
+        case ORA_PHI_FAVOR: return m;
+        case ORA_PHI_DPFP: return 2 * dk * g_map_param;
+        case ORA_PHI_TRIG: return 2 * m;
+        case ORA_PHI_COSFORMER: return 2 * dk;
+        default: return dk;
+    }
 }
+
+/* phi applied to n rows of X [n, d] at positions row0.. -> out [n, dp]. */
+static void phi_rows_at(int kind, int n, int d, const double *X, int m, const double *W, long long row0,
+                        double *out) {
+    int dp = feat_dim(kind, d, m);
+    for (int i = 0; i < n; ++i) phi_row(kind, X + (size_t)i * d, d, W, m, row0 + i, out + (size_t)i * dp);
+}
+
+/* phi applied to n rows of X [n, d] (positions 0..n-1) -> out [n, dp]. */
+void ora_phi(int kind, int n, int d, const double *X, int m, const double *W, double *out) {
+    phi_rows_at(kind, n, d, X, m, W, 0, out);
+}
+
+int ora_feature_dim(int kind, int dk, int m) { return feat_dim(kind, dk, m); }
 
 /* ---------------------------------------------------------------------------
  * State read [SOA5 5 (memory read num = sigma(Q) M, den = sigma(Q) z);
@@ -196,12 +272,12 @@ void ora_causal_recurrent(int BH, int N, int dk, int dv, int kind, int m, const 
         double *num = (double *)malloc(sizeof(double) * dv);
         double den;
         for (int i = 0; i < N; ++i) {
-            phi_row(kind, k + (size_t)i * dk, dk, W, m, pk);
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, i, pk);
             for (int f = 0; f < dp; ++f) {
                 z[f] += pk[f];
                 for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += pk[f] * v[(size_t)i * dv + c];
             }
-            phi_row(kind, q + (size_t)i * dk, dk, W, m, pq);
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, i, pq);
             ora_state_read(1, dp, dv, pq, S, z, num, &den);
             for (int c = 0; c < dv; ++c) O[((size_t)s * N + i) * dv + c] = num[c] / den;
         }
@@ -282,8 +358,8 @@ void ora_causal_chunked(int BH, int N, int dk, int dv, int kind, int m, const do
         double *den = (double *)malloc(sizeof(double) * (size_t)C);
         for (int t0 = 0; t0 < N; t0 += C) {
             int L = N - t0 < C ? N - t0 : C;
-            ora_phi(kind, L, dk, q + (size_t)t0 * dk, m, W, pq);
-            ora_phi(kind, L, dk, k + (size_t)t0 * dk, m, W, pk);
+            phi_rows_at(kind, L, dk, q + (size_t)t0 * dk, m, W, t0, pq);
+            phi_rows_at(kind, L, dk, k + (size_t)t0 * dk, m, W, t0, pk);
             /* masked intra-chunk similarities */
             for (int i = 0; i < L; ++i)
                 for (int t = 0; t < L; ++t) {
@@ -333,8 +409,8 @@ void ora_decode_step(int BH, int dk, int dv, int kind, int m, const double *W,
         double *pq = (double *)malloc(sizeof(double) * dp);
         double *Ss = S + (size_t)s * dp * dv, *zs = z + (size_t)s * dp;
         const double *vs = v + (size_t)s * dv;
-        phi_row(kind, k + (size_t)s * dk, dk, W, m, pk);
-        phi_row(kind, q + (size_t)s * dk, dk, W, m, pq);
+        phi_row(kind, k + (size_t)s * dk, dk, W, m, 0, pk);
+        phi_row(kind, q + (size_t)s * dk, dk, W, m, 0, pq);
         for (int f = 0; f < dp; ++f) {
             zs[f] += pk[f];
             for (int c = 0; c < dv; ++c) Ss[(size_t)f * dv + c] += pk[f] * vs[c];
@@ -368,11 +444,11 @@ void ora_retention_recurrent(int BH, int H, int N, int dk, int dv, int kind, int
         double *pk = (double *)malloc(sizeof(double) * dp);
         double *pq = (double *)malloc(sizeof(double) * dp);
         for (int i = 0; i < N; ++i) {
-            phi_row(kind, k + (size_t)i * dk, dk, W, m, pk);
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, i, pk);
             for (int f = 0; f < dp; ++f)
                 for (int c = 0; c < dv; ++c)
                     S[(size_t)f * dv + c] = g * S[(size_t)f * dv + c] + pk[f] * v[(size_t)i * dv + c];
-            phi_row(kind, q + (size_t)i * dk, dk, W, m, pq);
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, i, pq);
             for (int c = 0; c < dv; ++c) {
                 double acc = 0.0;
                 for (int f = 0; f < dp; ++f) acc += pq[f] * S[(size_t)f * dv + c];
@@ -445,8 +521,8 @@ void ora_retention_chunked(int BH, int H, int N, int dk, int dv, int kind, int m
         double *Sn = (double *)malloc(sizeof(double) * (size_t)dp * dv);
         for (int t0 = 0; t0 < N; t0 += C) {
             int L = N - t0 < C ? N - t0 : C;
-            ora_phi(kind, L, dk, q + (size_t)t0 * dk, m, W, pq);
-            ora_phi(kind, L, dk, k + (size_t)t0 * dk, m, W, pk);
+            phi_rows_at(kind, L, dk, q + (size_t)t0 * dk, m, W, t0, pq);
+            phi_rows_at(kind, L, dk, k + (size_t)t0 * dk, m, W, t0, pk);
             /* intra-block scores with the causal-decay mask M (rows i, cols t, 0-based) */
             for (int i = 0; i < L; ++i)
                 for (int t = 0; t < L; ++t) {
@@ -495,8 +571,8 @@ void ora_retention_decode_step(int BH, int H, int dk, int dv, int kind, int m, c
         double *pq = (double *)malloc(sizeof(double) * dp);
         double *Ss = S + (size_t)s * dp * dv;
         const double *vs = v + (size_t)s * dv;
-        phi_row(kind, k + (size_t)s * dk, dk, W, m, pk);
-        phi_row(kind, q + (size_t)s * dk, dk, W, m, pq);
+        phi_row(kind, k + (size_t)s * dk, dk, W, m, 0, pk);
+        phi_row(kind, q + (size_t)s * dk, dk, W, m, 0, pq);
         for (int f = 0; f < dp; ++f)
             for (int c = 0; c < dv; ++c) Ss[(size_t)f * dv + c] = g * Ss[(size_t)f * dv + c] + pk[f] * vs[c];
         for (int c = 0; c < dv; ++c) {
@@ -542,6 +618,8 @@ static void phi_vjp_row(int kind, const double *x, int d, const double *W, int m
         free(ph);
     } else if (kind == ORA_PHI_IDENTITY) {
         for (int c = 0; c < d; ++c) dx[c] = dphi[c];
+    } else if (kind != ORA_PHI_ELU1) {  /* the other maps are not differentiated here */
+        for (int c = 0; c < d; ++c) dx[c] = NAN;
     } else {
         for (int c = 0; c < d; ++c) dx[c] = dphi[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]));
     }
@@ -571,13 +649,13 @@ void ora_causal_backward(int BH, int N, int dk, int dv, int kind, int m, const d
         double *dphi = (double *)malloc(sizeof(double) * dp);
         /* forward sweep: the state after token i, the output, g_i, h_i and dpsi_i */
         for (int i = 0; i < N; ++i) {
-            phi_row(kind, k + (size_t)i * dk, dk, W, m, kap);
+            phi_row(kind, k + (size_t)i * dk, dk, W, m, i, kap);
             for (int f = 0; f < dp; ++f) {
                 z[f] += kap[f];
                 for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += kap[f] * v[(size_t)i * dv + c];
             }
             double *ps = psi + (size_t)i * dp;
-            phi_row(kind, q + (size_t)i * dk, dk, W, m, ps);
+            phi_row(kind, q + (size_t)i * dk, dk, W, m, i, ps);
             double den;
             ora_state_read(1, dp, dv, ps, S, z, num, &den);
             double dot = 0.0;
@@ -603,7 +681,7 @@ void ora_causal_backward(int BH, int N, int dk, int dv, int kind, int m, const d
                 r[f] += ps[f] * h[j];
                 for (int c = 0; c < dv; ++c) R[(size_t)f * dv + c] += ps[f] * g[(size_t)j * dv + c];
             }
-            phi_row(kind, k + (size_t)j * dk, dk, W, m, kap);
+            phi_row(kind, k + (size_t)j * dk, dk, W, m, j, kap);
             for (int f = 0; f < dp; ++f) {
                 double acc = r[f];
                 for (int c = 0; c < dv; ++c) acc += R[(size_t)f * dv + c] * v[(size_t)j * dv + c];
