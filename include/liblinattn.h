@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 
 typedef enum {
     LA_OK = 0,
@@ -57,15 +57,39 @@ typedef enum {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-typedef enum { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 2 } la_phi_kind;
+/*
+ * Feature maps (d' = feature dimension):
+ *   LA_PHI_ELU1       elu(x) + 1 per coordinate; d' = d_k
+ *   LA_PHI_FAVOR      exp(w_r . x - |x|^2 / 2) / sqrt(m), W [m, d_k]; d' = m
+ *   LA_PHI_IDENTITY   raw x (retention and the gated recurrences only); d' = d_k
+ *   LA_PHI_DPFP       r = ReLU([x, -x]); for shift i = 1..nu the block r_j r_{(j+i) mod 2d_k},
+ *                     j = 0..2d_k-1 ("Linear Attention", feature-map table); nu = map_param;
+ *                     d' = 2 d_k nu
+ *   LA_PHI_TRIG       [cos(W x); sin(W x)], W [m, d_k] (same table); d' = 2m
+ *   LA_PHI_COSFORMER  [ReLU(x) cos(pi p / 2M); ReLU(x) sin(pi p / 2M)] for the token at
+ *                     position p = pos0 + (index within the call), M = map_param ("Story of
+ *                     Attention Part 5", section 3); d' = 2 d_k
+ * d' <= 256 for every map.  DPFP, TRIG and cosFormer run on the fp32-arithmetic
+ * kernels for either storage type.
+ */
+typedef enum {
+    LA_PHI_ELU1 = 0,
+    LA_PHI_FAVOR = 1,
+    LA_PHI_IDENTITY = 2,
+    LA_PHI_DPFP = 3,
+    LA_PHI_TRIG = 4,
+    LA_PHI_COSFORMER = 5
+} la_phi_kind;
 
 typedef struct {
     int B, H, N;        /* batch, heads, tokens (N = 1 for la_decode_step)                   */
     int d_k, d_v;       /* key/query and value widths, each in [1, 128]                     */
     la_dtype dtype;     /* storage type of Q, K, V and O; S and z are always float32        */
     la_phi_kind phi;    /* feature map                                                      */
-    int m;              /* FAVOR+: number of random features in [1, 256]; ELU+1: must be 0  */
-    const float *W;     /* FAVOR+: device pointer to W [m, d_k] float32; ELU+1: NULL         */
+    int m;              /* FAVOR+: random features in [1, 256]; TRIG: in [1, 128]; else 0    */
+    const float *W;     /* FAVOR+ / TRIG: device pointer to W [m, d_k] float32; else NULL     */
+    int map_param;      /* DPFP: nu >= 1 (2 d_k nu <= 256); cosFormer: M >= 1; else 0         */
+    long long pos0;     /* cosFormer: position of the call's first token (>= 0); else ignored */
 } la_problem;
 
 /* ABI version of the loaded library (LA_ABI_VERSION of the build). */

@@ -25,14 +25,21 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 la_status check_problem(const la_problem *p) {
     if (!p) return LA_ERR_NULL;
     if (p->dtype != LA_F32 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
-    if (p->phi != LA_PHI_ELU1 && p->phi != LA_PHI_FAVOR && p->phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
+    if (p->phi < LA_PHI_ELU1 || p->phi > LA_PHI_COSFORMER) return LA_ERR_UNSUPPORTED;
     if (p->B < 1 || p->H < 1 || p->N < 1) return LA_ERR_SHAPE;
     if (p->d_k < 1 || p->d_k > 128 || p->d_v < 1 || p->d_v > 128) return LA_ERR_SHAPE;
-    if (p->phi == LA_PHI_FAVOR) {
-        if (p->m < 1 || p->m > 256) return LA_ERR_SHAPE;
+    if (p->phi == LA_PHI_FAVOR || p->phi == LA_PHI_TRIG) {
+        if (p->m < 1 || p->m > (p->phi == LA_PHI_TRIG ? 128 : 256)) return LA_ERR_SHAPE;
         if (!p->W) return LA_ERR_NULL;
         if (!aligned16(p->W)) return LA_ERR_ALIGN;
     } else if (p->m != 0 || p->W) {
+        return LA_ERR_SHAPE;
+    }
+    if (p->phi == LA_PHI_DPFP) {
+        if (p->map_param < 1 || 2LL * p->d_k * p->map_param > 256) return LA_ERR_SHAPE;
+    } else if (p->phi == LA_PHI_COSFORMER) {
+        if (p->map_param < 1 || p->pos0 < 0) return LA_ERR_SHAPE;
+    } else if (p->map_param != 0) {
         return LA_ERR_SHAPE;
     }
     // element counts of one slice must fit comfortably in 32-bit kernel indices
@@ -42,16 +49,28 @@ la_status check_problem(const la_problem *p) {
     return LA_OK;
 }
 
+static_assert(LA_PHI_ELU1 == kElu1 && LA_PHI_FAVOR == kFavor && LA_PHI_IDENTITY == kIdentity &&
+                  LA_PHI_DPFP == kDpfp && LA_PHI_TRIG == kTrig && LA_PHI_COSFORMER == kCosformer,
+              "feature-map codes");
+
 Shape make_shape(const la_problem *p) {
     Shape s;
     s.BH = p->B * p->H;
     s.N = p->N;
     s.dk = p->d_k;
     s.dv = p->d_v;
-    s.phi = p->phi == LA_PHI_FAVOR ? kFavor : (p->phi == LA_PHI_IDENTITY ? kIdentity : kElu1);
-    s.m = p->phi == LA_PHI_FAVOR ? p->m : 0;
-    s.dp = p->phi == LA_PHI_FAVOR ? p->m : p->d_k;
-    s.W = p->phi == LA_PHI_FAVOR ? p->W : nullptr;
+    s.phi = p->phi;  // the la_phi_kind values are the Phi values
+    s.m = (p->phi == LA_PHI_FAVOR || p->phi == LA_PHI_TRIG) ? p->m : 0;
+    s.W = (p->phi == LA_PHI_FAVOR || p->phi == LA_PHI_TRIG) ? p->W : nullptr;
+    s.param = p->map_param;
+    s.pos0 = p->phi == LA_PHI_COSFORMER ? p->pos0 : 0;
+    switch (p->phi) {
+        case LA_PHI_FAVOR: s.dp = p->m; break;
+        case LA_PHI_DPFP: s.dp = 2 * p->d_k * p->map_param; break;
+        case LA_PHI_TRIG: s.dp = 2 * p->m; break;
+        case LA_PHI_COSFORMER: s.dp = 2 * p->d_k; break;
+        default: s.dp = p->d_k;
+    }
     s.dtype = p->dtype == LA_BF16 ? kBF16 : kF32;
     s.ret = 0;
     s.gamma = nullptr;
@@ -199,8 +218,8 @@ LA_API const char *la_status_string(la_status s) {
 }
 
 LA_API int la_feature_dim(const la_problem *p) {
-    if (!p) return 0;
-    return p->phi == LA_PHI_FAVOR ? p->m : p->d_k;
+    if (check_problem(p) != LA_OK) return 0;
+    return make_shape(p).dp;
 }
 
 LA_API size_t la_workspace_bytes(const la_problem *p, int chunk) {

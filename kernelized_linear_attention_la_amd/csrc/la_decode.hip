@@ -13,6 +13,8 @@
 //
 // Retention variant (RET; "Story of Attention Part 5", section 4 recurrent
 // form): S = gamma S + phi(k) v^T, o = phi(q)^T S, with no z and no division.
+// Every feature map of the library is available; the cosFormer token sits at
+// position pos0.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -56,6 +58,35 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
             s_pq[tid] = elu1_accurate(load_as_f32(qs, tid));
             s_pk[tid] = elu1_accurate(load_as_f32(ks, tid));
         }
+    } else if (sh.phi == kCosformer) {
+        // ReLU(x) cos(pi p / 2M), ReLU(x) sin(pi p / 2M) at the token's position p = pos0
+        const double ang = 3.14159265358979323846 * (double)sh.pos0 / (2.0 * (double)sh.param);
+        const float cw = (float)cos(ang), sw = (float)sin(ang);
+        if (tid < dk) {
+            const float xq = fmaxf(load_as_f32(qs, tid), 0.f), xk = fmaxf(load_as_f32(ks, tid), 0.f);
+            s_pq[tid] = xq * cw;
+            s_pq[dk + tid] = xq * sw;
+            s_pk[tid] = xk * cw;
+            s_pk[dk + tid] = xk * sw;
+        }
+    } else if (sh.phi == kDpfp) {
+        // r = ReLU([x, -x]); block i = 1..nu holds r_j r_{(j+i) mod 2d}
+        if (tid < dk) {
+            s_x[0][tid] = load_as_f32(qs, tid);
+            s_x[1][tid] = load_as_f32(ks, tid);
+        }
+        __syncthreads();
+        const int n2 = 2 * dk;
+        auto rpm = [&](int w, int j) {
+            const float x = j < dk ? s_x[w][j] : -s_x[w][j - dk];
+            return x > 0.f ? x : 0.f;
+        };
+        for (int f = tid; f < dp; f += kThreads) {
+            const int i = f / n2 + 1, j = f - (i - 1) * n2;
+            const int jj = j + i < n2 ? j + i : j + i - n2;
+            s_pq[f] = rpm(0, j) * rpm(0, jj);
+            s_pk[f] = rpm(1, j) * rpm(1, jj);
+        }
     } else {
         if (tid < dk) {
             s_x[0][tid] = load_as_f32(qs, tid);
@@ -68,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
             s_sq[tid] = a;
         }
         __syncthreads();
+        // FAVOR+: exp(w_f . x - |x|^2 / 2) / sqrt(m); cos/sin projections: [cos(W x); sin(W x)]
         const float inv_sqrt_m = 1.0f / sqrtf(static_cast<float>(sh.m));
-        for (int f = tid; f < dp; f += kThreads) {
+        for (int f = tid; f < sh.m; f += kThreads) {
             const float *w = sh.W + (size_t)f * dk;
             float aq = 0.f, ak = 0.f;
             for (int c = 0; c < dk; ++c) {
@@ -77,8 +109,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
                 aq += wc * s_x[0][c];
                 ak += wc * s_x[1][c];
             }
-            s_pq[f] = expf(aq - 0.5f * s_sq[0]) * inv_sqrt_m;
-            s_pk[f] = expf(ak - 0.5f * s_sq[1]) * inv_sqrt_m;
+            if (sh.phi == kTrig) {
+                s_pq[f] = cosf(aq);
+                s_pq[sh.m + f] = sinf(aq);
+                s_pk[f] = cosf(ak);
+                s_pk[sh.m + f] = sinf(ak);
+            } else {
+                s_pq[f] = expf(aq - 0.5f * s_sq[0]) * inv_sqrt_m;
+                s_pk[f] = expf(ak - 0.5f * s_sq[1]) * inv_sqrt_m;
+            }
         }
     }
     __syncthreads();

@@ -73,7 +73,47 @@ __device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int ro
         }
         return;
     }
-    // FAVOR+ ("Story of Attention Part 5", 1b): exp(w_r . x - |x|^2/2) / sqrt(m)
+    if (sh.phi == kDpfp) {
+        // DPFP ("Linear Attention", feature-map table): r = ReLU([x, -x]);
+        // block i = 1..nu holds r_j r_{(j+i) mod 2d}
+        const int n2 = 2 * dk, dp = n2 * sh.param;
+        for (int e = tid; e < L.T * dk; e += kThreads) {
+            int r = e / dk;
+            sX[e] = r < nvalid ? load_as_f32(X, (size_t)(row0 + r) * dk + (e - r * dk)) : 0.f;
+        }
+        __syncthreads();
+        auto relu_pm = [&](int r, int j) {  // ReLU([x, -x])_j of row r
+            const float x = j < dk ? sX[r * dk + j] : -sX[r * dk + j - dk];
+            return x > 0.f ? x : 0.f;
+        };
+        for (int e = tid; e < L.T * dp; e += kThreads) {
+            const int r = e / dp, f = e - r * dp;
+            const int i = f / n2 + 1, j = f - (i - 1) * n2;
+            const int jj = j + i < n2 ? j + i : j + i - n2;
+            out[r * L.dpp + f] = relu_pm(r, j) * relu_pm(r, jj);
+        }
+        return;
+    }
+    if (sh.phi == kCosformer) {
+        // cosFormer ("Story of Attention Part 5", section 3): ReLU(x) cos(pi p / 2M),
+        // then ReLU(x) sin(pi p / 2M), p = pos0 + token index (phase in double)
+        for (int e = tid; e < L.T * dk; e += kThreads) {
+            const int r = e / dk, c = e - r * dk;
+            float cw = 0.f, sw = 0.f, x = 0.f;
+            if (r < nvalid) {
+                const double ang = 3.14159265358979323846 * (double)(sh.pos0 + row0 + r) / (2.0 * (double)sh.param);
+                cw = (float)cos(ang);
+                sw = (float)sin(ang);
+                x = load_as_f32(X, (size_t)(row0 + r) * dk + c);
+                x = x > 0.f ? x : 0.f;
+            }
+            out[r * L.dpp + c] = x * cw;
+            out[r * L.dpp + dk + c] = x * sw;
+        }
+        return;
+    }
+    // FAVOR+ ("Story of Attention Part 5", 1b): exp(w_r . x - |x|^2/2) / sqrt(m);
+    // cos/sin projections ("Linear Attention", feature-map table): [cos(W x); sin(W x)]
     for (int e = tid; e < L.T * dk; e += kThreads) {
         int r = e / dk, c = e - r * dk;
         sX[e] = r < nvalid ? load_as_f32(X, (size_t)(row0 + r) * dk + c) : 0.f;
@@ -97,9 +137,18 @@ __device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int ro
             for (int r = 0; r < 16; ++r)
                 if (r < L.T) acc[r] += wc * sX[r * dk + c];
         }
+        if (sh.phi == kTrig) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (r < L.T) out[r * L.dpp + f] = r < nvalid ? expf(acc[r] - 0.5f * sSq[r]) * inv_sqrt_m : 0.f;
+            for (int r = 0; r < 16; ++r)
+                if (r < L.T) {
+                    out[r * L.dpp + f] = r < nvalid ? cosf(acc[r]) : 0.f;
+                    out[r * L.dpp + sh.m + f] = r < nvalid ? sinf(acc[r]) : 0.f;
+                }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (r < L.T) out[r * L.dpp + f] = r < nvalid ? expf(acc[r] - 0.5f * sSq[r]) * inv_sqrt_m : 0.f;
+        }
     }
 }
 

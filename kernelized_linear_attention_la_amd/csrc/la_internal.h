@@ -10,7 +10,7 @@
 
 namespace la {
 
-enum Phi : int { kElu1 = 0, kFavor = 1, kIdentity = 2 };
+enum Phi : int { kElu1 = 0, kFavor = 1, kIdentity = 2, kDpfp = 3, kTrig = 4, kCosformer = 5 };
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // What one launch of the chunked kernels does over its token range.
@@ -32,8 +32,10 @@ struct Shape {
     int dk, dv;   // widths
     int dp;       // feature dimension d' (dk or m)
     int phi;      // Phi
-    int m;        // FAVOR+ features (0 for ELU+1)
-    const float *W;  // FAVOR+ rows [m, dk] (device)
+    int m;        // FAVOR+ / TRIG random features (0 otherwise)
+    const float *W;  // FAVOR+ / TRIG rows [m, dk] (device)
+    int param;    // DPFP nu, cosFormer M (0 otherwise)
+    long long pos0;  // cosFormer: position of the call's first token
     int dtype;    // Dtype of Q/K/V/O
     // Retention (decayed, unnormalised): ret = 1 and the decay of head h is
     // gamma[h] (device, [H]; slice b*H + h uses gamma[h]).  Normalised kernel

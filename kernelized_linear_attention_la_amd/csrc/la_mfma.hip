@@ -908,7 +908,8 @@ bool mfma_supported(const Shape &sh, int chunk) {
     if ((sh.phi == kIdentity) != (sh.ret != 0)) return false;  // identity map <=> retention here
     if (sh.phi == kElu1 || sh.phi == kIdentity)
         return ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128)) && (chunk == 64 || chunk == 128);
-    return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
+    if (sh.phi == kFavor) return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
+    return false;  // the other maps run on the fp32-arithmetic kernels
 }
 
 hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {

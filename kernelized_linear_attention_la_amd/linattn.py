@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_HERE, "_lib", "liblinattn.so")
 
 LA_OK = 0
 LA_F32, LA_BF16 = 0, 1
-LA_PHI_ELU1, LA_PHI_FAVOR, LA_PHI_IDENTITY = 0, 1, 2
+LA_PHI_ELU1, LA_PHI_FAVOR, LA_PHI_IDENTITY, LA_PHI_DPFP, LA_PHI_TRIG, LA_PHI_COSFORMER = 0, 1, 2, 3, 4, 5
+_PHI_CODES = {"elu1": LA_PHI_ELU1, "favor": LA_PHI_FAVOR, "identity": LA_PHI_IDENTITY, "dpfp": LA_PHI_DPFP,
+              "trig": LA_PHI_TRIG, "cosformer": LA_PHI_COSFORMER}
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_UNSUPPORTED",
                 5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
@@ -35,7 +37,8 @@ class LaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
                 ("d_k", ctypes.c_int), ("d_v", ctypes.c_int),
                 ("dtype", ctypes.c_int), ("phi", ctypes.c_int),
-                ("m", ctypes.c_int), ("W", ctypes.c_void_p)]
+                ("m", ctypes.c_int), ("W", ctypes.c_void_p), ("map_param", ctypes.c_int),
+                ("pos0", ctypes.c_longlong)]
 
 
 class LaKernelEvents(ctypes.Structure):
@@ -108,9 +111,9 @@ def status_string(status: int) -> str:
     return lib().la_status_string(int(status)).decode()
 
 
-def problem(B, H, N, d_k, d_v, dtype=LA_F32, phi=LA_PHI_ELU1, m=0, W_ptr=0) -> LaProblem:
+def problem(B, H, N, d_k, d_v, dtype=LA_F32, phi=LA_PHI_ELU1, m=0, W_ptr=0, map_param=0, pos0=0) -> LaProblem:
     return LaProblem(int(B), int(H), int(N), int(d_k), int(d_v), int(dtype), int(phi), int(m),
-                     ctypes.c_void_p(int(W_ptr)) if W_ptr else None)
+                     ctypes.c_void_p(int(W_ptr)) if W_ptr else None, int(map_param), int(pos0))
 
 
 def la_feature_dim(p: LaProblem) -> int:
@@ -153,18 +156,21 @@ def _check_qkv(q, k, v):
         raise ValueError(f"shape mismatch Q{tuple(q.shape)} K{tuple(k.shape)} V{tuple(v.shape)}")
 
 
-def _problem_of(q, v, phi, W):
+def _problem_of(q, v, phi, W, map_param=0, pos0=0):
+    """la_problem of a call: phi is a name ("elu1", "favor", "identity", "dpfp",
+    "trig", "cosformer") or code; W [m, d_k] float32 for FAVOR+ and the cos/sin
+    projections; map_param is DPFP's nu or cosFormer's M; pos0 the position of
+    the first token (cosFormer)."""
     B, H, N, dk = q.shape
     dv = v.shape[3]
-    if phi in ("favor", LA_PHI_FAVOR):
+    code = _PHI_CODES[phi] if isinstance(phi, str) else int(phi)
+    if code in (LA_PHI_FAVOR, LA_PHI_TRIG):
         if W is None:
-            raise ValueError("FAVOR+ needs the projection W [m, d_k]")
+            raise ValueError("this feature map needs the projection W [m, d_k]")
         if W.dtype != torch.float32 or not W.is_contiguous() or not W.is_cuda or W.dim() != 2 or W.shape[1] != dk:
             raise ValueError("W must be a contiguous float32 device tensor [m, d_k]")
-        return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_FAVOR, W.shape[0], W.data_ptr())
-    if phi in ("identity", LA_PHI_IDENTITY):
-        return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_IDENTITY, 0, 0)
-    return problem(B, H, N, dk, dv, _DT[q.dtype], LA_PHI_ELU1, 0, 0)
+        return problem(B, H, N, dk, dv, _DT[q.dtype], code, W.shape[0], W.data_ptr(), map_param, pos0)
+    return problem(B, H, N, dk, dv, _DT[q.dtype], code, 0, 0, map_param, pos0)
 
 
 def _state_pair(S, z, B, H, dp, dv, device, what):
@@ -187,7 +193,7 @@ def _raise(status, where):
 
 
 def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, z_in=None,
-                              S_out=None, z_out=None, out=None, workspace=None, stream=None, events=None):
+                              S_out=None, z_out=None, out=None, workspace=None, stream=None, events=None, map_param=0, pos0=0):
     """Causal chunkwise forward; returns O (same dtype as q).
 
     S_out/z_out, when given, receive the final state (they may be S_in/z_in).
@@ -197,7 +203,7 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
     la_forward_causal_chunked_timed in the C header).
     """
     _check_qkv(q, k, v)
-    p = _problem_of(q, v, phi, W)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
     B, H, N, dk = q.shape
     dv = v.shape[3]
     dp = la_feature_dim(p)
@@ -225,10 +231,10 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
 
 
 def la_forward_noncausal(q, k, v, phi="elu1", W=None, S_out=None, z_out=None, out=None, workspace=None,
-                         stream=None):
+                         stream=None, map_param=0, pos0=0):
     """Non-causal forward; returns O. S_out/z_out, when given, receive phi(K)^T V and phi(K)^T 1."""
     _check_qkv(q, k, v)
-    p = _problem_of(q, v, phi, W)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
     B, H, N, dk = q.shape
     dv = v.shape[3]
     dp = la_feature_dim(p)
@@ -245,14 +251,14 @@ def la_forward_noncausal(q, k, v, phi="elu1", W=None, S_out=None, z_out=None, ou
     return out
 
 
-def la_decode_step(q, k, v, S, z, phi="elu1", W=None, out=None, stream=None):
+def la_decode_step(q, k, v, S, z, phi="elu1", W=None, out=None, stream=None, map_param=0, pos0=0):
     """One decode step; q, k [B,H,1,d_k] (or [B,H,d_k]); v [B,H,1,d_v]. Updates S, z in place; returns o."""
     if q.dim() == 3:
         q, k, v = q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2)
     _check_qkv(q, k, v)
     if q.shape[2] != 1:
         raise ValueError("decode takes one token per slice")
-    p = _problem_of(q, v, phi, W)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
     B, H, _, dk = q.shape
     dv = v.shape[3]
     dp = la_feature_dim(p)
@@ -286,14 +292,14 @@ def _state_only(S, B, H, dp, dv, device, what):
 
 
 def la_forward_retention_chunked(q, k, v, gamma, chunk=64, phi="identity", W=None, S_in=None, S_out=None, out=None,
-                                 workspace=None, stream=None, events=None):
+                                 workspace=None, stream=None, events=None, map_param=0, pos0=0):
     """Retention (decayed, unnormalised) forward in the blockwise form; returns O.
 
     gamma: float32 device tensor [H] of per-head decays in (0, 1].
     S_out, when given, receives the final state (it may be S_in).
     """
     _check_qkv(q, k, v)
-    p = _problem_of(q, v, phi, W)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
     B, H, N, dk = q.shape
     dv = v.shape[3]
     dp = la_feature_dim(p)
@@ -313,14 +319,14 @@ def la_forward_retention_chunked(q, k, v, gamma, chunk=64, phi="identity", W=Non
     return out
 
 
-def la_retention_decode_step(q, k, v, S, gamma, phi="identity", W=None, out=None, stream=None):
+def la_retention_decode_step(q, k, v, S, gamma, phi="identity", W=None, out=None, stream=None, map_param=0, pos0=0):
     """One retention step; q, k [B,H,1,d_k] (or [B,H,d_k]); v [B,H,1,d_v]. Updates S in place; returns o."""
     if q.dim() == 3:
         q, k, v = q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2)
     _check_qkv(q, k, v)
     if q.shape[2] != 1:
         raise ValueError("decode takes one token per slice")
-    p = _problem_of(q, v, phi, W)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
     B, H, _, dk = q.shape
     dv = v.shape[3]
     dp = la_feature_dim(p)

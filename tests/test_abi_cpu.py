@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert linattn.la_abi_version() == 3
+    assert linattn.la_abi_version() == 4
     for s in range(8):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)
@@ -82,7 +82,7 @@ def _causal(p, chunk=64, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, Si=None, zi=None, So=No
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(d_k=0), 2), (dict(d_k=129), 2), (dict(d_v=200), 2),
-    (dict(dtype=7), 3), (dict(phi=5), 4), (dict(m=3), 2),
+    (dict(dtype=7), 3), (dict(phi=9), 4), (dict(m=3), 2),
     (dict(phi=linattn.LA_PHI_FAVOR, m=0, W_ptr=0x1000), 2), (dict(phi=linattn.LA_PHI_FAVOR, m=257, W_ptr=0x1000), 2),
     (dict(phi=linattn.LA_PHI_FAVOR, m=16, W_ptr=0), 1), (dict(phi=linattn.LA_PHI_FAVOR, m=16, W_ptr=0x1004), 5),
 ])
@@ -216,3 +216,24 @@ def test_gated_validation():
     assert L.la_forward_delta_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, None, FAKE, MIS, None, FAKE, None) == 5
     assert L.la_forward_delta_recurrent(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=129)), FAKE, FAKE, FAKE,
                                         None, FAKE, None, None, FAKE, None) == 2
+
+
+def test_feature_map_parameters_validation():
+    pd = lambda **kw: _p(phi=linattn.LA_PHI_DPFP, **kw)  # noqa: E731
+    assert linattn.la_feature_dim(pd(map_param=1)) == 128      # 2 d_k nu
+    assert linattn.la_feature_dim(pd(d_k=32, map_param=4)) == 256
+    assert _causal(pd(map_param=0)) == 2
+    assert _causal(pd(map_param=3)) == 2                       # 2 * 64 * 3 > 256
+    pt = lambda **kw: _p(phi=linattn.LA_PHI_TRIG, **kw)  # noqa: E731
+    assert linattn.la_feature_dim(pt(m=100, W_ptr=0x1000)) == 200
+    assert _causal(pt(m=129, W_ptr=0x1000)) == 2
+    assert _causal(pt(m=16, W_ptr=0)) == 1
+    pc = lambda **kw: _p(phi=linattn.LA_PHI_COSFORMER, **kw)  # noqa: E731
+    assert linattn.la_feature_dim(pc(map_param=512)) == 128    # 2 d_k
+    assert _causal(pc(map_param=0)) == 2
+    assert _causal(pc(map_param=8, pos0=-1)) == 2
+    assert _causal(_p(map_param=1)) == 2                       # ELU+1 takes no parameter
+    assert linattn.la_feature_dim(_p(map_param=1)) == 0        # invalid problem
+    for p in (pd(map_param=1), pt(m=16, W_ptr=0x1000), pc(map_param=100, pos0=7)):
+        assert linattn.la_workspace_bytes(p, 64) > 0
+        assert linattn.la_backward_workspace_bytes(p, 64) == 0  # no backward for these maps

@@ -1,0 +1,144 @@
+"""GPU parity of the further feature maps (DPFP, cos/sin projections, cosFormer)
+through the C ABI against the oracle: causal chunked and non-causal forwards,
+decode steps, a state hand-off across calls (cosFormer positions continue at
+pos0), retention with a further map, and the printed cosFormer worked example.
+Metric and tolerances as for the other forwards (tests/parity.py).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kernelized_linear_attention_la_amd import inputs
+from kernelized_linear_attention_la_amd import linattn as la
+from tests.parity import row_rel_err, state_rel_err, to_device, to_f64, tol_for, z_rel_err
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(*a):
+    print("[maps]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+    oracle.set_map(0, 0)
+
+
+def test_cosformer_worked_example_through_gpu():
+    with open(os.path.join(GOLDEN, "t6_cosformer_worked_example.json")) as f:
+        g = json.load(f)
+    Q, K, V = (torch.tensor(g[n], dtype=torch.float32).view(1, 1, 4, 4).cuda() for n in ("Q", "K", "V"))
+    O = la.la_forward_noncausal(Q, K, V, phi="cosformer", map_param=g["M"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np.round(to_f64(O)[0, 0], g["decimals"]), g["output"])
+
+
+def _inputs(ci, B, H, N, d, dtype, phi, m):
+    # cos/sin projections: smaller inputs keep the (signed) weights' sums away from 0
+    scale = 0.5 / np.sqrt(d) if phi == "trig" else 1.0 / np.sqrt(d)
+    fi = inputs.custom_inputs(3000 + ci, B, H, N, d, d, scale=scale, dtype=dtype)
+    W = inputs.iid_gaussian_rows(3000 + ci, m, d).astype(np.float32) if phi == "trig" else None
+    return fi, W
+
+
+CASES = [
+    # (B, H, N, d, dtype, phi, m, map_param, chunk)
+    (1, 2, 300, 32, "f32", "dpfp", 0, 2, 64),
+    (1, 1, 150, 64, "f32", "dpfp", 0, 2, 32),      # d' = 256
+    (2, 2, 333, 64, "bf16", "dpfp", 0, 1, 64),
+    (1, 2, 300, 64, "f32", "trig", 64, 0, 64),
+    (2, 1, 250, 32, "bf16", "trig", 128, 0, 128),  # d' = 256
+    (1, 2, 300, 64, "f32", "cosformer", 0, 300, 64),
+    (2, 2, 700, 64, "bf16", "cosformer", 0, 700, 128),
+    (1, 1, 517, 128, "f32", "cosformer", 0, 1024, 16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)), ids=[f"{c[5]}-B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}C{c[8]}"
+                                                    for c in CASES])
+def test_maps_against_oracle(ci):
+    B, H, N, d, dtype, phi, m, param, chunk = CASES[ci]
+    _say("case", CASES[ci])
+    fi, W = _inputs(ci, B, H, N, d, dtype, phi, m)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    Wt = torch.from_numpy(W).cuda() if W is not None else None
+    p = la._problem_of(q, v, phi, Wt, param)
+    dp = la.la_feature_dim(p)
+    S = torch.zeros(B, H, dp, d, device="cuda")
+    z = torch.zeros(B, H, dp, device="cuda")
+    O = la.la_forward_causal_chunked(q, k, v, chunk, phi=phi, W=Wt, S_out=S, z_out=z, map_param=param)
+    On = la.la_forward_noncausal(q, k, v, phi=phi, W=Wt, map_param=param)
+    torch.cuda.synchronize()
+    oracle.set_map(param, 0)
+    ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, W)
+    refn, _, _ = oracle.noncausal(phi, fi.Q.f32, fi.K.f32, fi.V.f32, W)
+    tol = tol_for(dtype)
+    e, en = row_rel_err(to_f64(O), ref), row_rel_err(to_f64(On), refn)
+    es = state_rel_err(to_f64(S), Sref)
+    _say(f"O {e:.2e} noncausal {en:.2e} S {es:.2e}")
+    assert e < tol and en < tol and es < tol
+    # z of cos/sin features can change sign: compare it like a state
+    ez = state_rel_err(to_f64(z)[..., None], zref[..., None]) if phi == "trig" else z_rel_err(to_f64(z), zref)
+    assert ez < tol, ez
+
+
+@pytest.mark.parametrize("phi,param,m", [("dpfp", 2, 0), ("trig", 0, 32), ("cosformer", 64, 0)])
+def test_maps_state_handoff_and_decode(phi, param, m):
+    """prefix forward -> S, z; then decode steps (cosFormer positions continue
+    at the prefix length) == the oracle's recurrence over the whole sequence."""
+    B, H, N, d, T = 2, 2, 40, 16, 5
+    fi, W = _inputs(50, B, H, N + T, d, "f32", phi, m)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    Wt = torch.from_numpy(W).cuda() if W is not None else None
+    p = la._problem_of(q[:, :, :N].contiguous(), v, phi, Wt, param)
+    dp = la.la_feature_dim(p)
+    S = torch.zeros(B, H, dp, d, device="cuda")
+    z = torch.zeros(B, H, dp, device="cuda")
+    la.la_forward_causal_chunked(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), 16,
+                                 phi=phi, W=Wt, S_out=S, z_out=z, map_param=param)
+    outs = []
+    for t in range(T):
+        sl = lambda x: x[:, :, N + t:N + t + 1].contiguous()  # noqa: E731
+        outs.append(la.la_decode_step(sl(q), sl(k), sl(v), S, z, phi=phi, W=Wt, map_param=param, pos0=N + t))
+    # the same continuation as one chunked call starting at position N
+    S2 = torch.zeros_like(S)
+    z2 = torch.zeros_like(z)
+    la.la_forward_causal_chunked(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), 16,
+                                 phi=phi, W=Wt, S_out=S2, z_out=z2, map_param=param)
+    Oc = la.la_forward_causal_chunked(q[:, :, N:].contiguous(), k[:, :, N:].contiguous(), v[:, :, N:].contiguous(),
+                                      16, phi=phi, W=Wt, S_in=S2, z_in=z2, S_out=S2, z_out=z2, map_param=param,
+                                      pos0=N)
+    torch.cuda.synchronize()
+    oracle.set_map(param, 0)
+    ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, W)
+    got = np.concatenate([to_f64(o) for o in outs], axis=2)
+    _say(phi, "decode", row_rel_err(got, ref[:, :, N:]), "chunked from pos0", row_rel_err(to_f64(Oc), ref[:, :, N:]))
+    assert row_rel_err(got, ref[:, :, N:]) < 1e-4
+    assert row_rel_err(to_f64(Oc), ref[:, :, N:]) < 1e-4
+    assert state_rel_err(to_f64(S), Sref) < 1e-4
+    assert state_rel_err(to_f64(S2), Sref) < 1e-4
+
+
+def test_retention_with_dpfp_map():
+    B, H, N, d = 1, 3, 200, 16
+    fi, _ = _inputs(60, B, H, N, d, "f32", "dpfp", 0)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    gam = inputs.retention_decays(H)
+    O = la.la_forward_retention_chunked(q, k, v, torch.from_numpy(gam).cuda(), 32, phi="dpfp", map_param=3)
+    torch.cuda.synchronize()
+    oracle.set_map(3, 0)
+    ref, _ = oracle.retention_recurrent("dpfp", fi.Q.f32, fi.K.f32, fi.V.f32, gam.astype(np.float64))
+    e = row_rel_err(to_f64(O), ref)
+    _say("retention dpfp", e)
+    assert e < 1e-4
