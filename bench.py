@@ -64,7 +64,7 @@ def forward_alg_flops(wl):
         per = 4 * dp * dv + (C + 1) * (dp + dv)
     else:
         per = 4 * dp * dv + 2 * dp + (C + 1) * (dp + dv) + dv
-    if wl.phi == "favor":
+    if wl.phi in ("favor", "trig"):
         per += 4 * dk * wl.m
     return wl.B * wl.H * wl.N * per
 
@@ -150,6 +150,7 @@ def run_cpu_baseline(wl, fi, seconds):
     import numpy as np
     import oracle
     nthreads = oracle.num_threads()
+    oracle.set_map(wl.map_param, 0)  # DPFP nu / cosFormer M (0 for the other maps)
     BH = wl.B * wl.H
     if wl.retention:
         # the sample runs over the first heads' slices; their decays, in slice order
@@ -279,7 +280,7 @@ def bench_forward(args, wl):
     sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(v0)) for _ in range(R)]
     S = torch.zeros(wl.B, wl.H, wl.dprime, wl.dv, device=dev)
     z = torch.zeros(wl.B, wl.H, wl.dprime, device=dev)
-    p = la._problem_of(q0, v0, wl.phi, W)
+    p = la._problem_of(q0, v0, wl.phi, W, wl.map_param)
     ws = torch.zeros(max(1, la.la_workspace_bytes(p, wl.chunk)), dtype=torch.uint8, device=dev)
 
     def step(i, stream=None, events=None):
@@ -289,7 +290,7 @@ def bench_forward(args, wl):
                                             stream=stream, events=events)
         else:
             la.la_forward_causal_chunked(q, k, v, wl.chunk, phi=wl.phi, W=W, S_out=S, z_out=z, out=o,
-                                         workspace=ws, stream=stream, events=events)
+                                         workspace=ws, stream=stream, events=events, map_param=wl.map_param)
 
     # the step sequence is launch-bound at small sizes: capture it in HIP graphs
     stream = torch.cuda.Stream()
@@ -370,7 +371,13 @@ def bench_forward(args, wl):
     chunk_bytes = tokens * (2 * wl.dk + 2 * wl.dv) * elem_bytes(wl.dtype)
     flop_per_byte = alg_flops / alg_bytes
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if flop_per_byte < ridge:
+    kname = kernel_symbol(wl, "chunk")
+    if kname.startswith("k_generic"):
+        # fp32-arithmetic kernels: against the fp32 vector ALUs
+        ach = alg_flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / FP32_VECTOR_PEAK_TFS, "traffic": None}
+    elif flop_per_byte < ridge:
         ach = chunk_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "traffic": None}
@@ -378,7 +385,6 @@ def bench_forward(args, wl):
         ach = alg_flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
-    kname = kernel_symbol(wl, "chunk")
     tb = stored_traffic(wl, kname)
     roof["traffic"] = tb
     roof["kernel"] = kname

@@ -198,10 +198,12 @@ class Workload:
     retention: bool = False  # decayed, unnormalised variant (per-head decays, no normaliser)
     backward: bool = False   # gradients of the causal form for a seeded dL/dO
     gated: str = ""          # "gla" or "delta" (gated delta rule): token-by-token recurrences
+    map_param: int = 0       # DPFP nu / cosFormer M
 
     @property
     def dprime(self) -> int:
-        return self.m if self.phi == "favor" else self.dk
+        return {"favor": self.m, "trig": 2 * self.m, "dpfp": 2 * self.dk * self.map_param,
+                "cosformer": 2 * self.dk}.get(self.phi, self.dk)
 
     def gammas(self) -> np.ndarray:
         """Per-head decays of a retention workload (float32 [H])."""
@@ -237,6 +239,13 @@ WORKLOADS = {
                  1.0 / math.sqrt(64), 64, backward=True),
         Workload("bwd_elu1_bf16_b2h16n16384d128_c128", 10, "elu1", "bf16", 2, 16, 16384, 128, 128,
                  1.0 / math.sqrt(128), 128, backward=True),
+        # further feature maps at the bf16 d = 64 shape (fp32-arithmetic kernels)
+        Workload("dpfp_bf16_b4h8n2048d64_c64", 13, "dpfp", "bf16", 4, 8, 2048, 64, 64, 1.0 / math.sqrt(64), 64,
+                 map_param=1),
+        Workload("trig_bf16_b4h8n2048d64_m64_c64", 14, "trig", "bf16", 4, 8, 2048, 64, 64, 0.5 / math.sqrt(64),
+                 64, m=64),
+        Workload("cosformer_bf16_b4h8n2048d64_c64", 15, "cosformer", "bf16", 4, 8, 2048, 64, 64,
+                 1.0 / math.sqrt(64), 64, map_param=2048),
         # gated / delta-rule states at the bf16 d = 64 shape (raw q, k; unit-norm keys)
         Workload("gla_bf16_b4h8n2048d64", 11, "identity", "bf16", 4, 8, 2048, 64, 64, 1.0 / math.sqrt(64), 1,
                  gated="gla"),
@@ -275,7 +284,11 @@ def forward_inputs(wl: Workload, N: int | None = None, workers=None) -> ForwardI
     Q = normal_bhnd(wl.wid, TENSOR_Q, shp_k, wl.scale, wl.dtype, workers=workers)
     K = normal_bhnd(wl.wid, TENSOR_K, shp_k, wl.scale, wl.dtype, workers=workers)
     V = normal_bhnd(wl.wid, TENSOR_V, shp_v, wl.scale, wl.dtype, workers=workers)
-    W = orthogonal_gaussian_rows(wl.wid, wl.m, wl.dk) if wl.phi == "favor" else None
+    W = None
+    if wl.phi == "favor":
+        W = orthogonal_gaussian_rows(wl.wid, wl.m, wl.dk)
+    elif wl.phi == "trig":  # cos/sin projections: i.i.d. N(0, I) rows, fp32
+        W = iid_gaussian_rows(wl.wid, wl.m, wl.dk).astype(np.float32)
     return ForwardInputs(wl, Q, K, V, W)
 
 
