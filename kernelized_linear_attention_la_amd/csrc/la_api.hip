@@ -167,7 +167,8 @@ bool causal_direct(const Shape &sh, const Segments &g, bool mfma) {
 // Single-pass mode: the LDS-resident variant when a segment's phi(K), V fit
 // (d = 64, 64-token chunks, at most kResChunks chunks per segment).
 int fused_mode(const Shape &sh, const Segments &g) {
-    const bool res = g.seg_chunks <= kResChunks && sh.dk == 64 && sh.dv == 64 && g.chunk == 64 && sh.phi != kFavor;
+    const bool res = g.seg_chunks <= kResChunks && sh.dk == 64 && sh.dv == 64 && g.chunk == 64 &&
+                     (sh.phi == kElu1 || sh.phi == kIdentity);
     return res ? kModeFusedRes : kModeFused;
 }
 

@@ -139,9 +139,11 @@ __device__ __forceinline__ Op8 token_operand(const uint16_t *arr, int kt, int cb
 template <int DK, int DV, int C, int PHI>
 struct Cfg {
     static constexpr bool F = PHI == kFavor;
+    // cosFormer ("Story of Attention Part 5", section 3): [ReLU(x) cos t, ReLU(x) sin t]
+    static constexpr bool CF = PHI == kCosformer;
     static constexpr int NW = C / 16;            // waves
     static constexpr int THREADS = 64 * NW;
-    static constexpr int DP = F ? 256 : DK;      // feature dimension
+    static constexpr int DP = F ? 256 : (CF ? 2 * DK : DK);  // feature dimension
     static constexpr int M = F ? 256 : 0;
     // Retention ("Story of Attention Part 5", sections 4 and 6): raw q and k,
     // decay per head, no normaliser.
@@ -264,6 +266,23 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     }
 
     const float inv_sqrt_m = G::F ? 1.0f / 16.0f : 1.0f;  // m = 256
+    // cosFormer reweighting of token t: (cos, sin) of pi (pos0 + t) / 2M, the
+    // phase formed in double so that long positions keep their accuracy
+    auto cf_phase = [&](int t, float &cw, float &sw) {
+        const double ang = 3.14159265358979323846 * (double)(a.sh.pos0 + t) / (2.0 * (double)a.sh.param);
+        cw = (float)cos(ang);
+        sw = (float)sin(ang);
+    };
+    // 8 packed bf16 values: ReLU(x) * w, rounded to bf16
+    auto relu_scale8 = [](uint4 x, float w) {
+        auto f = [&](float v) { return (v > 0.f ? v : 0.f) * w; };
+        uint4 r;
+        r.x = cvt2(f(lo_bf16(x.x)), f(hi_bf16(x.x)));
+        r.y = cvt2(f(lo_bf16(x.y)), f(hi_bf16(x.y)));
+        r.z = cvt2(f(lo_bf16(x.z)), f(hi_bf16(x.z)));
+        r.w = cvt2(f(lo_bf16(x.w)), f(hi_bf16(x.w)));
+        return r;
+    };
 
     // ---- register prefetch of a chunk: K and V rows in 8-column pieces
     // (FAVOR+: also Q), plus, for ELU+1, this wave's query rows.  Chunk
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     constexpr int UK = NEED_K ? C * DK / 8 : 0;
     constexpr int UV = NEED_K ? C * DV / 8 : 0;
     constexpr int UQ = (G::F && DO_OUT) ? C * DK / 8 : 0;
-    constexpr int KBQ = G::F ? 1 : KBF;  // ELU+1: 16-byte query pieces per lane
+    constexpr int KBQ = G::F ? 1 : G::KBD;  // 16-byte raw query pieces per lane (the lane's row)
     // prefetch ring: chunks in flight ahead of the one being computed.  Two
     // for the smaller tiles; one for d = 128 with 128-token chunks, whose
     // chunk takes several load latencies to compute and whose registers are
@@ -344,6 +363,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
             if constexpr (G::F) {  // raw rows; the feature map runs on the matrix cores
                 *reinterpret_cast<uint4 *>(&sm.XK[t * G::RX + 8 * c8]) = p.raw[i].u;
+            } else if constexpr (G::CF) {  // cos half at column 8c8, sin half at DK + 8c8
+                float cw, sw;
+                cf_phase(tt0 + t, cw, sw);
+                uint4 pc = relu_scale8(p.raw[i].u, cw), ps = relu_scale8(p.raw[i].u, sw);
+                if (!full && tt0 + t >= N) pc = ps = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = pc;
+                *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + DK + 8 * c8]) = ps;
             } else {
                 // ELU+1 on the way in (retention: raw keys); tokens past the end get phi = 0, not phi(0) = 1
                 uint4 ph;
@@ -413,7 +439,12 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         const int ks = RES ? c - c_begin : 0;  // LDS chunk slot
         if (!(RES && OUT)) stage(p, t0, ks);  // the resident phase 3 finds phi(K), V in LDS
         Op8 phq[KBF];
-        if constexpr (OUT && !G::F) {
+        if constexpr (OUT && G::CF) {  // features 32kf + 8g..: cos half (kf < KBD), then sin half
+            float cw, sw;
+            cf_phase(t0 + row, cw, sw);
+#pragma unroll
+            for (int kf = 0; kf < KBF; ++kf) phq[kf].u = relu_scale8(p.q[kf % G::KBD].u, kf < G::KBD ? cw : sw);
+        } else if constexpr (OUT && !G::F) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = RET ? p.q[kb].u : elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
         }
@@ -881,7 +912,7 @@ template <int DK, int DV, int C, int PHI>
 hipError_t launch_variant(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.sh.BH * a.sg.P)), block(C / 16 * 64);
     if (a.mode == kModeFusedRes) {
-        if constexpr (DK == 64 && DV == 64 && C == 64 && PHI != kFavor)
+        if constexpr (DK == 64 && DV == 64 && C == 64 && (PHI == kElu1 || PHI == kIdentity))
             return launch_kernel_ev(k_mfma<DK, DV, C, PHI, kModeFusedRes>, grid, block, 0, st, ev, a);
         return hipErrorNotSupported;
     }
@@ -909,6 +940,7 @@ bool mfma_supported(const Shape &sh, int chunk) {
     if (sh.phi == kElu1 || sh.phi == kIdentity)
         return ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128)) && (chunk == 64 || chunk == 128);
     if (sh.phi == kFavor) return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
+    if (sh.phi == kCosformer) return sh.dk == 64 && sh.dv == 64 && chunk == 64;
     return false;  // the other maps run on the fp32-arithmetic kernels
 }
 
@@ -917,6 +949,7 @@ hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const int C = a.sg.chunk;
     if (!mfma_supported(s, C)) return hipErrorNotSupported;
     if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st, ev);
+    if (s.phi == kCosformer) return launch_variant<64, 64, 64, kCosformer>(a, st, ev);
     if (s.phi == kIdentity) {
         if (s.dk == 64)
             return C == 64 ? launch_variant<64, 64, 64, kIdentity>(a, st, ev)

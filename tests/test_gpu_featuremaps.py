@@ -62,6 +62,11 @@ CASES = [
     (1, 2, 300, 64, "f32", "cosformer", 0, 300, 64),
     (2, 2, 700, 64, "bf16", "cosformer", 0, 700, 128),
     (1, 1, 517, 128, "f32", "cosformer", 0, 1024, 16),
+    # the matrix-core cosFormer kernel (bf16, d = 64, 64-token chunks): single
+    # segment, several segments with a ragged tail, the full bf16 d64 workload
+    (1, 1, 100, 64, "bf16", "cosformer", 0, 100, 64),
+    (4, 4, 1000, 64, "bf16", "cosformer", 0, 1000, 64),
+    (4, 8, 2048, 64, "bf16", "cosformer", 0, 2048, 64),
 ]
 
 
@@ -142,3 +147,27 @@ def test_retention_with_dpfp_map():
     e = row_rel_err(to_f64(O), ref)
     _say("retention dpfp", e)
     assert e < 1e-4
+
+
+def test_cosformer_matrix_core_handoff_with_position_offset():
+    """bf16 d64 cosFormer on the matrix cores: two calls (the second from the
+    first's state, at pos0 = split) == one call; S_out aliasing S_in."""
+    B, H, N, d, M = 2, 4, 1500, 64, 1500
+    fi, _ = _inputs(70, B, H, N, d, "bf16", "cosformer", 0)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    oracle.set_map(M, 0)
+    ref, Sref, zref = oracle.causal_recurrent("cosformer", fi.Q.f32, fi.K.f32, fi.V.f32)
+    for split in (64, 700):
+        S = torch.zeros(B, H, 2 * d, d, device="cuda")
+        z = torch.zeros(B, H, 2 * d, device="cuda")
+        c = lambda x, a_, b_: x[:, :, a_:b_].contiguous()  # noqa: E731
+        O1 = la.la_forward_causal_chunked(c(q, 0, split), c(k, 0, split), c(v, 0, split), 64, phi="cosformer",
+                                          map_param=M, S_out=S, z_out=z)
+        O2 = la.la_forward_causal_chunked(c(q, split, N), c(k, split, N), c(v, split, N), 64, phi="cosformer",
+                                          map_param=M, pos0=split, S_in=S, z_in=z, S_out=S, z_out=z)
+        torch.cuda.synchronize()
+        e = row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref)
+        _say("cosformer split", split, e)
+        assert e < 2e-2
+        assert state_rel_err(to_f64(S), Sref) < 2e-2
+        assert z_rel_err(to_f64(z), zref) < 2e-2
