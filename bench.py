@@ -229,14 +229,16 @@ def kernel_symbol(wl, slot):
         (wl.phi == "elu1" and not wl.retention and square) or
         (wl.phi == "identity" and wl.retention and square) or
         (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64) or
-        (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64))
+        (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64) or
+        (wl.phi == "dpfp" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and
+         wl.map_param == 1))
     if mfma:
         # the forward workloads all split into several segments per slice: the
         # matrix-core path runs them in one single-pass launch, mode 4 when a
         # segment's keys and values stay in LDS (d 64, 64-token chunks, at most
         # 4 chunks per segment), else mode 3 (the library's plan: about 256
         # workgroups, whole chunks per segment)
-        phi_id = {"elu1": 0, "favor": 1, "identity": 2, "cosformer": 5}[wl.phi]
+        phi_id = {"elu1": 0, "favor": 1, "identity": 2, "dpfp": 3, "cosformer": 5}[wl.phi]
         n_chunks = -(-wl.N // wl.chunk)
         P = min(-(-256 // (wl.B * wl.H)), n_chunks)
         seg = -(-n_chunks // P)

@@ -141,9 +141,12 @@ struct Cfg {
     static constexpr bool F = PHI == kFavor;
     // cosFormer ("Story of Attention Part 5", section 3): [ReLU(x) cos t, ReLU(x) sin t]
     static constexpr bool CF = PHI == kCosformer;
+    // DPFP with one shift ("Linear Attention", feature-map table): r = ReLU([x, -x]), r_j r_{j+1}
+    static constexpr bool DPF = PHI == kDpfp;
+    static constexpr bool XR = F || DPF;         // raw K, Q rows staged in LDS, the map formed there
     static constexpr int NW = C / 16;            // waves
     static constexpr int THREADS = 64 * NW;
-    static constexpr int DP = F ? 256 : (CF ? 2 * DK : DK);  // feature dimension
+    static constexpr int DP = F ? 256 : ((CF || DPF) ? 2 * DK : DK);  // feature dimension
     static constexpr int M = F ? 256 : 0;
     // Retention ("Story of Attention Part 5", sections 4 and 6): raw q and k,
     // decay per head, no normaliser.
@@ -173,8 +176,8 @@ struct Smem {
     uint16_t V[NKS][C * G::RV];         // V_aug, token-major
     uint4 STB[G::NJ][G::KBF][64];       // bf16 S_aug: B operand of phi(Q) S
     uint16_t O[G::NW][16 * G::RO];      // per-wave output staging for 16-byte stores
-    uint16_t XK[F ? C * G::RX : 1];     // FAVOR+: raw K_c, token-major
-    uint16_t XQ[F ? C * G::RX : 1];     // FAVOR+: raw Q_c, token-major
+    uint16_t XK[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP: raw K_c, token-major
+    uint16_t XQ[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP: raw Q_c, token-major
     uint16_t QP[F ? C * G::RK : 1];     // FAVOR+: phi(Q_c), token-major
 };
 
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // flight during the matrix work of chunks c and c+1.
     constexpr int UK = NEED_K ? C * DK / 8 : 0;
     constexpr int UV = NEED_K ? C * DV / 8 : 0;
-    constexpr int UQ = (G::F && DO_OUT) ? C * DK / 8 : 0;
-    constexpr int KBQ = G::F ? 1 : G::KBD;  // 16-byte raw query pieces per lane (the lane's row)
+    constexpr int UQ = (G::XR && DO_OUT) ? C * DK / 8 : 0;
+    constexpr int KBQ = G::XR ? 1 : G::KBD;  // 16-byte raw query pieces per lane (the lane's row)
     // prefetch ring: chunks in flight ahead of the one being computed.  Two
     // for the smaller tiles; one for d = 128 with 128-token chunks, whose
     // chunk takes several load latencies to compute and whose registers are
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         for (int i = 0; i < UVT; ++i) p.raw[UKT + i].u = bload16(rv, 16 * (tid + i * G::THREADS));
         if constexpr (DO_OUT) {
             const auto rq = make_rsrc(Qs + (size_t)tt0 * DK, qrows * DK * 2);
-            if constexpr (G::F) {
+            if constexpr (G::XR) {
 #pragma unroll
                 for (int i = 0; i < UQT; ++i) p.raw[UKT + UVT + i].u = bload16(rq, 16 * (tid + i * G::THREADS));
             } else {
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < UKT; ++i) {
             const int u = tid + i * G::THREADS, t = u / (DK / 8), c8 = u % (DK / 8);
-            if constexpr (G::F) {  // raw rows; the feature map runs on the matrix cores
+            if constexpr (G::XR) {  // raw rows; the feature map is formed after the barrier
                 *reinterpret_cast<uint4 *>(&sm.XK[t * G::RX + 8 * c8]) = p.raw[i].u;
             } else if constexpr (G::CF) {  // cos half at column 8c8, sin half at DK + 8c8
                 float cw, sw;
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             cf_phase(t0 + row, cw, sw);
 #pragma unroll
             for (int kf = 0; kf < KBF; ++kf) phq[kf].u = relu_scale8(p.q[kf % G::KBD].u, kf < G::KBD ? cw : sw);
-        } else if constexpr (OUT && !G::F) {
+        } else if constexpr (OUT && !G::XR) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = RET ? p.q[kb].u : elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
         }
@@ -502,6 +505,45 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                 for (int kf = 0; kf < KBF; ++kf) phq[kf].u = *reinterpret_cast<const uint4 *>(&sm.QP[row * RK + 32 * kf + 8 * g]);
             }
+        }
+
+        // ---------------- DPFP, one shift: with r = ReLU([x, -x]) (2d entries),
+        // feature j = r_j r_{(j+1) mod 2d}.  phi(K) goes to LDS token-major in
+        // 8-feature pieces; this lane's query pieces (features 32kf + 8g..)
+        // come straight from the raw row.
+        if constexpr (G::DPF) {
+            auto piece = [&](const uint16_t *xr, int j0) {  // features j0..j0+7 of raw row xr
+                float r[9];
+#pragma unroll
+                for (int e = 0; e < 9; ++e) {
+                    const int j = (j0 + e) % (2 * DK);
+                    const float x = bf16_to_f32(xr[j % DK]);
+                    const float v = j < DK ? x : -x;
+                    r[e] = v > 0.f ? v : 0.f;
+                }
+                uint4 o;
+                o.x = cvt2(r[0] * r[1], r[1] * r[2]);
+                o.y = cvt2(r[2] * r[3], r[3] * r[4]);
+                o.z = cvt2(r[4] * r[5], r[5] * r[6]);
+                o.w = cvt2(r[6] * r[7], r[7] * r[8]);
+                return o;
+            };
+            if constexpr (NEED_K) {
+                constexpr int PK = C * G::DP / 8 / G::THREADS;  // 8-feature pieces per thread
+                static_assert(PK * G::THREADS * 8 == C * G::DP, "DPFP pieces must tile the workgroup");
+#pragma unroll
+                for (int i = 0; i < PK; ++i) {
+                    const int u = tid + i * G::THREADS, t = u / (G::DP / 8), c8 = u % (G::DP / 8);
+                    uint4 v = piece(&sm.XK[t * G::RX], 8 * c8);
+                    if (t0 + t >= N) v = make_uint4(0, 0, 0, 0);  // keys past the end: phi = 0
+                    *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = v;
+                }
+            }
+            if constexpr (OUT) {
+#pragma unroll
+                for (int kf = 0; kf < KBF; ++kf) phq[kf].u = piece(&sm.XQ[row * G::RX], 32 * kf + 8 * g);
+            }
+            block_sync_lds();
         }
 
         // ---------------- outputs of this wave's 16 query rows
@@ -941,6 +983,7 @@ bool mfma_supported(const Shape &sh, int chunk) {
         return ((sh.dk == 64 && sh.dv == 64) || (sh.dk == 128 && sh.dv == 128)) && (chunk == 64 || chunk == 128);
     if (sh.phi == kFavor) return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
     if (sh.phi == kCosformer) return sh.dk == 64 && sh.dv == 64 && chunk == 64;
+    if (sh.phi == kDpfp) return sh.dk == 64 && sh.dv == 64 && sh.param == 1 && chunk == 64;
     return false;  // the other maps run on the fp32-arithmetic kernels
 }
 
@@ -950,6 +993,7 @@ hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     if (!mfma_supported(s, C)) return hipErrorNotSupported;
     if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st, ev);
     if (s.phi == kCosformer) return launch_variant<64, 64, 64, kCosformer>(a, st, ev);
+    if (s.phi == kDpfp) return launch_variant<64, 64, 64, kDpfp>(a, st, ev);
     if (s.phi == kIdentity) {
         if (s.dk == 64)
             return C == 64 ? launch_variant<64, 64, 64, kIdentity>(a, st, ev)

@@ -67,6 +67,9 @@ CASES = [
     (1, 1, 100, 64, "bf16", "cosformer", 0, 100, 64),
     (4, 4, 1000, 64, "bf16", "cosformer", 0, 1000, 64),
     (4, 8, 2048, 64, "bf16", "cosformer", 0, 2048, 64),
+    # the matrix-core DPFP kernel (one shift, bf16, d = 64, 64-token chunks)
+    (4, 4, 1000, 64, "bf16", "dpfp", 0, 1, 64),
+    (4, 8, 2048, 64, "bf16", "dpfp", 0, 1, 64),
 ]
 
 
