@@ -262,11 +262,12 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  *   ws           device workspace of at least la_backward_workspace_bytes()
  *                bytes (no initial contents required).
  *   ev           per-kernel timing hook (slots below), or NULL.
- * Five kernels are enqueued: the forward's per-segment sums and their prefix
+ * Six kernels are enqueued: the forward's per-segment sums and their prefix
  * scan, then the forward-direction pass (recomputes the outputs, writes dQ and
- * the per-token g, h to ws), the reverse scan of the per-segment sums of
- * psi g^T, psi h (writes dS_in, dz_in), and the reverse-direction pass (dK,
- * dV).  Outputs must not overlap inputs or each other.
+ * the per-token g, h to ws), the per-segment sums of psi g^T, psi h (no
+ * timing slot), their reverse scan (writes dS_in, dz_in), and the
+ * reverse-direction pass (dK, dV).  Outputs must not overlap inputs or each
+ * other.
  */
 enum { LA_BSLOT_FWD_SUMS = 0, LA_BSLOT_FWD_SCAN = 1, LA_BSLOT_DQ = 2, LA_BSLOT_RSCAN = 3, LA_BSLOT_DKV = 4,
        LA_BSLOTS = 5 };

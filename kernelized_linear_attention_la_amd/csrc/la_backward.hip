@@ -14,8 +14,8 @@
 // Kernels (one 256-thread workgroup per (slice, segment), fp32 arithmetic,
 // fp32 or bf16 storage):
 //   k_bwd_dq   chunks in order from the forward prefix: recomputes num, den,
-//              writes G_aug to the workspace and dQ, and sums psi^T G_aug of
-//              the segment;
+//              writes G_aug to the workspace and dQ;
+//   k_bwd_usum sums psi^T G_aug over each segment;
 //   k_bwd_rscan exclusive suffix of those sums (+ dS_out), in place; dS_in;
 //   k_bwd_dkv  chunks in reverse from the suffix: dK, dV.
 #include "la_device.h"
@@ -182,11 +182,6 @@ __global__ __launch_bounds__(kTh) void k_bwd_dq(BwdArgs a) {
         const int f = e / dva, c = e - f * dva;
         sS[e] = c < dv ? Sp[(size_t)f * dv + c] : zp[f];
     }
-    // this thread's elements of U = sum over the segment of psi^T G_aug
-    const int naug = dp * dva;
-    float u[kMaxU];
-#pragma unroll
-    for (int r = 0; r < kMaxU; ++r) u[r] = 0.f;
     __syncthreads();
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -277,17 +272,6 @@ __global__ __launch_bounds__(kTh) void k_bwd_dq(BwdArgs a) {
             }
             __syncthreads();
             store_input_grad(sh, L, sXq, sPQ, sDP, sH, nq, dQs, t0 + qt);
-            // U += psi^T G_aug
-#pragma unroll
-            for (int r = 0; r < kMaxU; ++r) {
-                const int e = tid + r * kTh;
-                if (e < naug) {
-                    const int f = e / dva, col = e - f * dva;
-                    float s = u[r];
-                    for (int i = 0; i < kT; ++i) s += sPQ[i * L.ldp + f] * sG[i * dva + col];
-                    u[r] = s;
-                }
-            }
             __syncthreads();
         }
         // carry the state past the chunk: S_aug += kappa^T v_aug
@@ -305,12 +289,47 @@ __global__ __launch_bounds__(kTh) void k_bwd_dq(BwdArgs a) {
             __syncthreads();
         }
     }
-    float *Us = a.U + ((size_t)bh * sg.P + seg) * naug;
-#pragma unroll
-    for (int r = 0; r < kMaxU; ++r) {
-        const int e = tid + r * kTh;
-        if (e < naug) Us[e] = u[r];
+}
+
+// U of a segment = sum over its tokens of psi_i G_aug_i^T (the reverse scan's
+// input), accumulated in LDS over 16-token tiles (psi recomputed, G_aug read
+// back from the workspace).
+template <typename T>
+__global__ __launch_bounds__(kTh) void k_bwd_usum(BwdArgs a) {
+    extern __shared__ float smem[];
+    const Shape sh = a.sh;
+    const Segments sg = a.sg;
+    const int dp = sh.dp, dk = sh.dk, dv = sh.dv;
+    const BwdLayout L = bwd_layout(dk, dp, dv);
+    const int dva = L.dva, naug = dp * dva;
+    float *sU = smem + L.offS, *sXq = smem + L.offXq, *sSqq = smem + L.offSqq, *sPQ = smem + L.offPQ;
+    float *sG = smem + L.offG;
+    const int tid = threadIdx.x;
+    const int seg = blockIdx.x % sg.P, bh = blockIdx.x / sg.P;
+    const int N = sh.N;
+    const int t_begin = seg * sg.seg_chunks * sg.chunk, t_end = min(N, t_begin + sg.seg_chunks * sg.chunk);
+    const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
+    const float *Gs = a.G + (size_t)bh * N * dva;
+    for (int e = tid; e < naug; e += kTh) sU[e] = 0.f;
+    for (int t0 = t_begin; t0 < t_end; t0 += kT) {
+        const int nq = min(kT, t_end - t0);
+        __syncthreads();  // the previous tile is consumed
+        load_phi(sh, L, Qs, t0, nq, sXq, sSqq, sPQ);
+        for (int e = tid; e < kT * dva; e += kTh) {
+            const int r = e / dva;
+            sG[e] = r < nq ? Gs[(size_t)(t0 + r) * dva + (e - r * dva)] : 0.f;
+        }
+        __syncthreads();
+        for (int e = tid; e < naug; e += kTh) {
+            const int f = e / dva, col = e - f * dva;
+            float acc = sU[e];
+            for (int i = 0; i < kT; ++i) acc += sPQ[i * L.ldp + f] * sG[i * dva + col];
+            sU[e] = acc;
+        }
     }
+    __syncthreads();
+    float *Us = a.U + ((size_t)bh * sg.P + seg) * naug;
+    for (int e = tid; e < naug; e += kTh) Us[e] = sU[e];
 }
 
 // R_aug entering each segment: dS_out_aug + the sums of the later segments,
@@ -481,6 +500,9 @@ hipError_t launch_backward(const BwdLaunch &b, hipStream_t st, KEvents ev_dq, KE
     const bool f32 = b.sh.dtype == kF32;
     hipError_t e = f32 ? launch_big_lds(k_bwd_dq<float>, grid, lds, st, ev_dq, a)
                        : launch_big_lds(k_bwd_dq<uint16_t>, grid, lds, st, ev_dq, a);
+    if (e != hipSuccess) return e;
+    e = f32 ? launch_big_lds(k_bwd_usum<float>, grid, lds, st, KEvents{}, a)
+            : launch_big_lds(k_bwd_usum<uint16_t>, grid, lds, st, KEvents{}, a);
     if (e != hipSuccess) return e;
     const int naug = b.sh.dp * (b.sh.dv + 1);
     const unsigned bps = (unsigned)((naug + kTh - 1) / kTh);
