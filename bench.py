@@ -36,6 +36,7 @@ DEFAULT_WORKLOAD = "elu1_bf16_b4h8n2048d64_c64"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 FP32_VECTOR_PEAK_TFS = 157.3  # MI355X fp32 vector ALUs (256 CUs x 256 flop/clk x 2.4 GHz), TFLOP/s
+MFMA_F32_PEAK_TFS = 157.3    # MI355X dense fp32 matrix cores, TFLOP/s
 ROTATE_BYTES = 768 << 20     # > 256 MB Infinity Cache
 
 
@@ -214,9 +215,17 @@ def run_cpu_baseline_decode(wl, fi, seconds):
                       f"{nthreads} threads of '{cpu_model()}'"}
 
 
+def backward_on_mfma(wl):
+    """The library runs the backward's two passes on fp32 matrix instructions
+    for bf16 ELU+1 with d_k = d_v = 64 and 64-token chunks."""
+    return wl.dtype == "bf16" and wl.phi == "elu1" and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64
+
+
 def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
+        if backward_on_mfma(wl) and slot in ("dq", "dkv"):
+            return f"k_bwd_{slot}_mfma"
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.gated:
         return f"k_gated<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {'true' if wl.gated == 'gla' else 'false'}>"
@@ -490,8 +499,11 @@ def bench_backward(args, wl):
     flops = backward_alg_flops(wl, which)
     ach = flops / (kern_ms * 1e-3) / 1e12
     kname = kernel_symbol(wl, which)
-    roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
-            "frac": ach / FP32_VECTOR_PEAK_TFS, "traffic": stored_traffic(wl, kname), "kernel": kname,
+    # fp32 arithmetic either way: on the matrix cores (dense fp32 MFMA peak) or in fp32 FMAs
+    bound = "mfma" if backward_on_mfma(wl) else "alu"
+    peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
+    roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+            "frac": ach / peak, "traffic": stored_traffic(wl, kname), "kernel": kname,
             "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
             "timing": "hip events around each kernel, launches queued back to back"}
     names = {la.LA_BSLOT_FWD_SUMS: "fwd_sums", la.LA_BSLOT_FWD_SCAN: "fwd_scan", la.LA_BSLOT_DQ: "dq",

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "liblinattn.so")
-SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_backward.hip", "la_gated.hip"]
+SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_backward.hip", "la_backward_mfma.hip",
+           "la_gated.hip"]
 ARCH = "gfx950"
 
 
@@ -76,6 +77,8 @@ KERNEL_SOURCES = {
     "k_bwd_rscan": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dkv": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gated": ("la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_bwd_dq_mfma": ("la_backward_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_bwd_dkv_mfma": ("la_backward_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
 }
 
 

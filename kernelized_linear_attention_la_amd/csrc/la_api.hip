@@ -456,7 +456,11 @@ struct BwdWs {
     size_t s_off, z_off, u_off, g_off, total;
 };
 
-Segments backward_plan(const Shape &sh, int chunk) { return plan_segments(sh, chunk, 1, 1, kTargetWorkgroups); }
+Segments backward_plan(const Shape &sh, int chunk) {
+    // matrix-core kernels: one workgroup per CU; fp32 kernels: several
+    return backward_mfma_supported(sh, chunk) ? plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups)
+                                              : plan_segments(sh, chunk, 1, 1, kTargetWorkgroups);
+}
 
 BwdWs bwd_ws(const Shape &sh, const Segments &g) {
     const size_t bh = (size_t)sh.BH, dp = (size_t)sh.dp, dv = (size_t)sh.dv;
@@ -465,7 +469,9 @@ BwdWs bwd_ws(const Shape &sh, const Segments &g) {
     w.z_off = w.s_off + round_up(sizeof(float) * bh * g.P * dp * dv, kAlign);
     w.u_off = w.z_off + round_up(sizeof(float) * bh * g.P * dp, kAlign);
     w.g_off = w.u_off + round_up(sizeof(float) * bh * g.P * dp * (dv + 1), kAlign);
-    w.total = w.g_off + round_up(sizeof(float) * bh * sh.N * (dv + 1), kAlign);
+    // G_aug per token: fp32 [d_v + 1] (fp32-FMA kernels) or fp32 [backward_mfma_g_floats()] (matrix cores)
+    const size_t g_row = sizeof(float) * (backward_mfma_supported(sh, g.chunk) ? backward_mfma_g_floats() : dv + 1);
+    w.total = w.g_off + round_up(g_row * bh * sh.N, kAlign);
     return w;
 }
 
@@ -521,10 +527,26 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
     a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
     a.st.S_dst = wsS; a.st.z_dst = wsz;
     a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
-    if (launch_generic(a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
+    const bool mf = backward_mfma_supported(sh, chunk);
+    if (launch_fwd(mf, a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
     if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, nullptr, nullptr, false, hs, slot(LA_BSLOT_FWD_SCAN)) !=
         hipSuccess)
         return LA_ERR_DEVICE;
+    if (mf) {
+        BwdMfmaArgs m;
+        m.BH = sh.BH; m.N = sh.N; m.P = g.P; m.seg_chunks = g.seg_chunks; m.n_chunks = g.n_chunks;
+        m.Q = static_cast<const uint16_t *>(Q); m.K = static_cast<const uint16_t *>(K);
+        m.V = static_cast<const uint16_t *>(V); m.dO = static_cast<const uint16_t *>(dO);
+        m.dQ = static_cast<uint16_t *>(dQ); m.dK = static_cast<uint16_t *>(dK); m.dV = static_cast<uint16_t *>(dV);
+        m.Spre = wsS; m.zpre = wsz;
+        m.U = reinterpret_cast<float *>(wsb + wl.u_off);
+        m.G = reinterpret_cast<float *>(wsb + wl.g_off);
+        if (launch_bwd_dq_mfma(m, hs, slot(LA_BSLOT_DQ)) != hipSuccess) return LA_ERR_DEVICE;
+        if (launch_bwd_rscan(sh.BH, g.P, sh.dp, sh.dv, m.U, dS_out, dz_out, dS_in, dz_in, hs, slot(LA_BSLOT_RSCAN)) !=
+            hipSuccess)
+            return LA_ERR_DEVICE;
+        return launch_bwd_dkv_mfma(m, hs, slot(LA_BSLOT_DKV)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+    }
     BwdLaunch b;
     b.sh = sh; b.sg = g;
     b.Q = Q; b.K = K; b.V = V; b.dO = dO;

@@ -489,6 +489,14 @@ size_t backward_lds_bytes(const Shape &sh) {
     return sizeof(float) * (size_t)bwd_layout(sh.dk, sh.dp, sh.dv).total;
 }
 
+hipError_t launch_bwd_rscan(int BH, int P, int dp, int dv, float *U, const float *dS_out, const float *dz_out,
+                            float *dS_in, float *dz_in, hipStream_t st, KEvents ev) {
+    const int naug = dp * (dv + 1);
+    const unsigned bps = (unsigned)((naug + kTh - 1) / kTh);
+    return launch_kernel_ev(k_bwd_rscan, dim3((unsigned)BH * bps), dim3(kTh), 0, st, ev, BH, P, dp, dv, U, dS_out,
+                            dz_out, dS_in, dz_in);
+}
+
 hipError_t launch_backward(const BwdLaunch &b, hipStream_t st, KEvents ev_dq, KEvents ev_scan, KEvents ev_dkv) {
     BwdArgs a;
     a.sh = b.sh; a.sg = b.sg;

@@ -147,6 +147,26 @@ struct BwdLaunch {
     float *dS_in, *dz_in;           // NULL = not wanted
 };
 bool backward_supported(const Shape &sh);
+// Reverse scan of the per-segment sums (la_backward.hip): U [BH][P][d' (d_v+1)]
+// becomes the exclusive suffixes (+ dS_out); dS_in / dz_in get the totals.
+hipError_t launch_bwd_rscan(int BH, int P, int dp, int dv, float *U, const float *dS_out, const float *dz_out,
+                            float *dS_in, float *dz_in, hipStream_t stream, KEvents ev = {});
+
+// Matrix-core backward (la_backward_mfma.hip): bf16 storage, fp32 matrix
+// instructions, ELU+1, d_k = d_v = 64, 64-token chunks.  G holds G_aug as
+// fp32 [BH][N][backward_mfma_g_floats()].
+struct BwdMfmaArgs {
+    int BH, N, P, seg_chunks, n_chunks;
+    const uint16_t *Q, *K, *V, *dO;
+    uint16_t *dQ, *dK, *dV;
+    const float *Spre, *zpre;  // forward prefix per segment
+    float *U;                  // [BH][P][64 * 65]
+    float *G;                  // [BH][N][backward_mfma_g_floats()]
+};
+bool backward_mfma_supported(const Shape &sh, int chunk);
+size_t backward_mfma_g_floats();
+hipError_t launch_bwd_dq_mfma(const BwdMfmaArgs &a, hipStream_t stream, KEvents ev = {});
+hipError_t launch_bwd_dkv_mfma(const BwdMfmaArgs &a, hipStream_t stream, KEvents ev = {});
 
 // Gated / delta-rule recurrences (la_gated.hip): one workgroup per slice.
 struct GatedArgs {
