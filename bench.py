@@ -243,14 +243,17 @@ def kernel_symbol(wl, slot):
          wl.map_param == 1))
     if mfma:
         # the forward workloads all split into several segments per slice: the
-        # matrix-core path runs them in one single-pass launch, mode 4 when a
-        # segment's keys and values stay in LDS (d 64, 64-token chunks, at most
-        # 4 chunks per segment), else mode 3 (the library's plan: about 256
-        # workgroups, whole chunks per segment)
+        # matrix-core path runs them in one single-pass launch (the library's
+        # plan: about 256 workgroups, whole chunks per segment): the
+        # whole-segment kernel at d 64 with segments of at most 256 tokens,
+        # else the chunk loop, mode 4 when a segment's keys and values stay in
+        # LDS (d 64, 64-token chunks, at most 4 chunks per segment), else mode 3
         phi_id = {"elu1": 0, "favor": 1, "identity": 2, "dpfp": 3, "cosformer": 5}[wl.phi]
         n_chunks = -(-wl.N // wl.chunk)
         P = min(-(-256 // (wl.B * wl.H)), n_chunks)
         seg = -(-n_chunks // P)
+        if P > 1 and seg * wl.chunk <= 256 and wl.dk == 64 and wl.dv == 64 and wl.phi in ("elu1", "identity"):
+            return f"k_seg<{phi_id}>"  # a whole segment (at most 256 tokens) per 16-wave workgroup
         res = seg <= 4 and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and wl.phi in ("elu1", "identity")
         return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {phi_id}, {4 if res else 3}>"
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"

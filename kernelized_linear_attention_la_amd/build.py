@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "liblinattn.so")
-SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_backward.hip", "la_backward_mfma.hip",
+SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_mfma_seg.hip", "la_backward.hip", "la_backward_mfma.hip",
            "la_gated.hip"]
 ARCH = "gfx950"
 
@@ -69,7 +69,8 @@ def build(extra_flags=(), verbose: bool = False) -> str:
 # file, the shared device helpers and argument structs, and the host code that
 # sizes its grid and segments.
 KERNEL_SOURCES = {
-    "k_mfma": ("la_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_mfma": ("la_mfma.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_seg": ("la_mfma_seg.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_generic": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_scan": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_decode": ("la_decode.hip", "la_device.h", "la_internal.h", "la_api.hip"),

@@ -129,7 +129,7 @@ Segments noncausal_plan(const Shape &sh, bool *use_mfma) {
 // Workspace: [control block][segment flags][S part][z part].
 //  * control block (kCtlBytes, fixed offset for every shape): launch counter,
 //    done count and error word of the single-pass mode;
-//  * flags: one word per (slice, segment);
+//  * flags: kFlagsPerSegment words per (slice, segment);
 //  * S part: P + 1 single-pass slots of d' x (d_v + 16) floats per slice (S,
 //    z and padding in the matrix-core accumulator order); the separate passes
 //    use P x d' x d_v of it, with the z part.
@@ -140,7 +140,7 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const Shape &sh, int P) {
-    const size_t f_bytes = round_up(sizeof(uint32_t) * (size_t)sh.BH * P, kAlign);
+    const size_t f_bytes = round_up(sizeof(uint32_t) * (size_t)sh.BH * P * kFlagsPerSegment, kAlign);
     const size_t s_bytes = round_up(sizeof(float) * (size_t)sh.BH * (P + 1) * sh.dp * (sh.dv + 16), kAlign);
     const size_t z_bytes = round_up(sizeof(float) * (size_t)sh.BH * P * sh.dp, kAlign);
     WsLayout w;
@@ -170,6 +170,12 @@ int fused_mode(const Shape &sh, const Segments &g) {
     const bool res = g.seg_chunks <= kResChunks && sh.dk == 64 && sh.dv == 64 && g.chunk == 64 &&
                      (sh.phi == kElu1 || sh.phi == kIdentity);
     return res ? kModeFusedRes : kModeFused;
+}
+
+// Single pass on the matrix cores: the whole-segment kernel where a segment
+// fits one 16-wave workgroup, else the chunk loop.
+hipError_t launch_single_pass(const FwdArgs &f, hipStream_t st, KEvents ev) {
+    return seg_supported(f.sh, f.sg) ? launch_seg(f, st, ev) : launch_mfma(f, st, ev);
 }
 
 size_t causal_ws(const Shape &sh, int chunk) {
@@ -326,7 +332,7 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
         f.fu.slots = wsS;
         f.fu.spin_ticks = kSpinTicks;
         f.fu.S_out = S_out; f.fu.z_out = z_out;
-        return launch_mfma(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+        return launch_single_pass(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
 
     // A. each segment's own sums phi(K)^T V, phi(K)^T 1
@@ -415,7 +421,7 @@ LA_API la_status la_forward_retention_chunked(const la_problem *p, const float *
         f.fu.slots = wsS;
         f.fu.spin_ticks = kSpinTicks;
         f.fu.S_out = S_out;
-        return launch_mfma(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+        return launch_single_pass(f, hs, slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
     // fp32 path: segment sums (decayed to the segment end), Horner scan, chunk loop
     FwdArgs a{};

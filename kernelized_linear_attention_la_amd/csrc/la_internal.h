@@ -22,6 +22,10 @@ enum Mode : int {
     kModeFusedRes = 4 // single pass with the segment's phi(K), V kept in LDS between the phases
 };
 
+// Hand-off flags per (slice, segment) in the single-pass workspace (the
+// whole-segment kernel flags each 16-row strip of the state on its own).
+constexpr int kFlagsPerSegment = 4;
+
 // Chunks per segment that the LDS-resident single pass can hold (d = 64, 64-token chunks).
 constexpr int kResChunks = 4;
 
@@ -76,7 +80,7 @@ struct StateArgs {
 // segment s (slot P also parks the last segment's own sums).
 struct FusedArgs {
     uint32_t *ctl;         // [3] launch counter, done count, error word
-    uint32_t *flags;       // [B*H*P] tag of the launch whose segment sums are ready
+    uint32_t *flags;       // [B*H*P*kFlagsPerSegment] tags of the launch whose segment sums are ready
     float *slots;          // [B*H][P+1][d' * (d_v + 16)] accumulator-order states
     long long spin_ticks;  // wall-clock bound of one wait (s_memrealtime ticks)
     float *S_out, *z_out;  // final state of each slice (NULL = not exported)
@@ -132,6 +136,10 @@ hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const vo
 // bf16 MFMA path; returns hipErrorNotSupported when the shape has no MFMA variant.
 hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 bool mfma_supported(const Shape &sh, int chunk);
+// Single pass with a whole segment (at most 256 tokens) per 16-wave
+// workgroup (la_mfma_seg.hip): bf16, d = 64, ELU+1 or retention, P > 1.
+bool seg_supported(const Shape &sh, const Segments &g);
+hipError_t launch_seg(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 
 // Backward of the causal normalised form (la_backward.hip): three launches
 // per call after the forward prefix is in Spre / zpre.

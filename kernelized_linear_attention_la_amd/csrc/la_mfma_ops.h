@@ -1,0 +1,129 @@
+// Matrix-core building blocks shared by the bf16 forward kernels
+// (v_mfma_f32_16x16x32_bf16 operands, bf16 packing, the feature map on packed
+// values, raw buffer resources, LDS transpose reads and barriers).
+//
+// For v_mfma_f32_16x16x32_bf16 lane l supplies A[l%16][k-slots 8(l/16)..+7],
+// B[k-slots][l%16] and receives D[4(l/16)+e][l%16], e = 0..3.  Operands that
+// contract over tokens use the k-slot order
+//     slot 8g+e  <->  token 16*(e/4) + 4g + (e%4)   inside each 32-token block,
+// the order in which a lane holds the scores of two consecutive 16x16 P^T
+// accumulator tiles, so P becomes an A operand without an LDS round trip.
+#pragma once
+
+#include "la_device.h"
+
+namespace la {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+union Op8 {
+    bf16x8_t v;
+    uint4 u;
+    uint2 q[2];
+    uint32_t u32[4];
+    uint16_t h[8];
+};
+
+__device__ __forceinline__ f32x4 mfma(const Op8 &a, const Op8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
+    return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) { return make_uint2(cvt2(a, b), cvt2(c, d)); }
+
+__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ELU+1 ("Linear Attention", feature-map table): x + 1 for x > 0, else exp(x)
+// (hardware exp2, ~1 ulp; its value for x > 0 is discarded by the select).
+__device__ __forceinline__ float elu1_hw(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+    return x > 0.f ? x + 1.f : e;
+}
+
+// ELU+1 of eight packed bf16 values, rounded back to packed bf16
+__device__ __forceinline__ uint4 elu1_bf16x8(uint4 x) {
+    uint4 r;
+    r.x = cvt2(elu1_hw(lo_bf16(x.x)), elu1_hw(hi_bf16(x.x)));
+    r.y = cvt2(elu1_hw(lo_bf16(x.y)), elu1_hw(hi_bf16(x.y)));
+    r.z = cvt2(elu1_hw(lo_bf16(x.z)), elu1_hw(hi_bf16(x.z)));
+    r.w = cvt2(elu1_hw(lo_bf16(x.w)), elu1_hw(hi_bf16(x.w)));
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3).
+// Loads past the range return zero and stores past it are dropped, without
+// a memory access, so a partial or empty chunk runs the same unconditional
+// instruction stream as a full one.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+}
+
+// Cache policy of the hand-off between workgroups of one launch (they may run
+// on different XCDs, whose L2 caches are not coherent with each other): sc1,
+// the policy of agent-scope atomics.  Stores write through to the device
+// coherence point and loads read from it, so no L2-wide write-back or
+// invalidate is needed around them.
+constexpr int kCoherent = 16;
+// Wait until this wave's stores have completed (reached the coherence point).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS transpose read: within each 16-lane group, lane i receives element i%4
+// of the 8-byte fragments addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ uint2 tr_read(const uint16_t *p) {
+    i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Operand whose k-slots run over the 32 tokens of block kt (slot order above)
+// and whose 16 rows/columns are the columns cb..cb+15 of a token-major LDS
+// array with row stride R: lane i + 16g receives arr[token(g, s)][cb + i].
+template <int R>
+__device__ __forceinline__ Op8 token_operand(const uint16_t *arr, int kt, int cb, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const uint16_t *p = arr + (32 * kt + 4 * g + (j >> 2)) * R + cb + 4 * (j & 3);
+    Op8 o;
+    o.q[0] = tr_read(p);
+    o.q[1] = tr_read(p + 16 * R);
+    return o;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (vmcnt(0)), which
+// would drain the next chunk's prefetch at each barrier; the cross-wave
+// hand-offs in these kernels go through LDS alone.
+__device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace
+}  // namespace la
