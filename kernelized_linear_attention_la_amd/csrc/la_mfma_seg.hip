@@ -121,8 +121,6 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
     }
     const int qb = w;              // this wave's 16-row query block inside the segment
     const int row = 16 * qb + c16;  // this lane's query row (A operand of phi(Q) S)
-#pragma unroll
-    for (int kb = 0; kb < kSKB; ++kb) qraw[kb] = bload16(rq, 2 * (row * kSD + 8 * g + 32 * kb));
 
     // hand-off slots: strip fb (feature rows 16fb..16fb+15, all value blocks)
     // of a state is 64 lanes x NJ x 16 bytes in accumulator order
@@ -152,14 +150,19 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
             *reinterpret_cast<uint4 *>(&sm.V[t * kSRV + kSD + 8 * half]) = make_uint4(half == 0 ? 0x3f80u : 0u, 0, 0, 0);
         }
     }
+    // the query rows go out once the keys and values (which the hand-off
+    // waits for) have arrived
+#pragma unroll
+    for (int kb = 0; kb < kSKB; ++kb) qraw[kb] = bload16(rq, 2 * (row * kSD + 8 * g + 32 * kb));
     block_sync_lds();
 
     Op8 phq[kSKB];
-#pragma unroll
-    for (int kb = 0; kb < kSKB; ++kb) phq[kb].u = RET ? qraw[kb] : elu1_bf16x8(qraw[kb]);
     f32x4 acc[NJ];
-    // local part of this wave's rows: (P (.) M) V_aug over the key blocks up to the diagonal
+    // local part of this wave's rows: (P (.) M) V_aug over the key blocks up
+    // to the diagonal (every wave calls it once, before the prefix read)
     auto local_rows = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < kSKB; ++kb) phq[kb].u = RET ? qraw[kb] : elu1_bf16x8(qraw[kb]);
 #pragma unroll
         for (int nb = 0; nb < NJ; ++nb) acc[nb] = zero4();
         for (int kt = 0; 2 * kt <= qb; ++kt) {
@@ -203,14 +206,14 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
     // retention: the state decays across each segment, so slot j enters the
     // prefix as S = lambda^(tokens of segment j-1) S + slot j (Horner form);
     // every segment before this one is full
-    if (w >= 8 && w < 8 + kStrips) {
-        // ---- 2a. sum wave: strip fb of the segment sum phi(K)^T V_aug
-        // (retention: sum_t lambda^(L-1-t) k_t v_t^T, the key weights on the operand slots),
-        // published to slot 1 + seg with flag (seg, fb); segment 0 also copies
-        // strip fb of S_in into slot 0 (only segment 0 reads S_in, so S_out may alias it)
+    // ---- 2a. sum waves 8..11: strip fb = w - 8 of the segment sum phi(K)^T V_aug
+    // (retention: sum_t lambda^(L-1-t) k_t v_t^T, the key weights on the operand
+    // slots).  The other waves wait meanwhile: the strips are what the later
+    // segments wait for, and alone the sum waves have the LDS to themselves.
+    const bool sum_wave = w >= 8 && w < 8 + kStrips;
+    f32x4 own[NJ];
+    if (sum_wave) {
         const int fb = w - 8;
-        __builtin_amdgcn_s_setprio(2);  // the other segments wait for this strip
-        f32x4 own[NJ];
 #pragma unroll
         for (int nb = 0; nb < NJ; ++nb) own[nb] = zero4();
         const int nkt = (L + 31) / 32;  // 32-token blocks holding data
@@ -228,6 +231,12 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) own[nb] = mfma(ka, token_operand<kSRV>(sm.V, kt, 16 * nb, lane), own[nb]);
         }
+    }
+    block_sync_lds();
+    if (sum_wave) {
+        // published to slot 1 + seg with flag (seg, fb); segment 0 also copies
+        // strip fb of S_in into slot 0 (only segment 0 reads S_in, so S_out may alias it)
+        const int fb = w - 8;
         if (seg < P - 1) {
             auto store_strip = [&](int i, const f32x4 *t) {
                 const auto r = slot_rsrc(i, true);
@@ -254,7 +263,6 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
             if (lane == 0)  // ... before its flag is tagged
                 __hip_atomic_store(fl + seg * kStrips + fb, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_s_setprio(0);
         if (seg == P - 1)  // kept for S_out
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) sm.OWN[fb][nb][lane] = own[nb];
