@@ -48,7 +48,7 @@ def run(cmd, log, timeout):
 
 
 def short_name(kernel_name):
-    m = re.search(r"(k_\w+<[^>]*>|k_scan|__amd_rocclr_copyBuffer\w*)", kernel_name)
+    m = re.search(r"(k_\w+<[^>]*>|k_\w+(?=\()|k_scan|__amd_rocclr_copyBuffer\w*)", kernel_name)
     return m.group(1) if m else kernel_name[:60]
 
 
