@@ -221,6 +221,11 @@ def backward_on_mfma(wl):
     return wl.dtype == "bf16" and wl.phi == "elu1" and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64
 
 
+def gla_on_chunks(wl):
+    """The library runs GLA in chunkwise form (fp32 matrix instructions) for d_k <= 64, N >= 64."""
+    return wl.gated == "gla" and wl.dk <= 64 and wl.N >= 64
+
+
 def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
@@ -228,7 +233,10 @@ def kernel_symbol(wl, slot):
             return f"k_bwd_{slot}_mfma"
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.gated:
-        return f"k_gated<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {'true' if wl.gated == 'gla' else 'false'}>"
+        t = "float" if wl.dtype == "f32" else "unsigned short"
+        if gla_on_chunks(wl):
+            return f"k_gla_chunk<{t}>"
+        return f"k_gated<{t}, {'true' if wl.gated == 'gla' else 'false'}>"
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
         return f"k_decode<{t}, {4 if wl.dv % 4 == 0 else 1}, {'true' if wl.retention else 'false'}>"
@@ -575,8 +583,12 @@ def bench_gated(args, wl):
     flops = gated_alg_flops(wl)
     ach = flops / (kern_ms * 1e-3) / 1e12
     kname = kernel_symbol(wl, "chunk")
-    roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
-            "frac": ach / FP32_VECTOR_PEAK_TFS, "traffic": stored_traffic(wl, kname), "kernel": kname,
+    # fp32 arithmetic: chunkwise GLA on the matrix cores (dense fp32 MFMA peak), the
+    # token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own
+    bound = "mfma" if gla_on_chunks(wl) else "alu"
+    peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
+    roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+            "frac": ach / peak, "traffic": stored_traffic(wl, kname), "kernel": kname,
             "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
             "timing": "hip events around each launch"}
     tokens = wl.B * wl.H * wl.N

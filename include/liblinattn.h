@@ -303,9 +303,12 @@ la_status la_backward_causal_chunked(const la_problem *p, int chunk,
  *          beta [B,H,N] fp32 (write strength), alpha [B,H,N] fp32 scalar
  *          forget gate or NULL (alpha = 1: the plain delta rule).
  * Q, K [B,H,N,d_k], V, O [B,H,N,d_v] of dtype p->dtype; the state stays fp32
- * and every step is computed in fp32 in token order.  S_in NULL = zero;
- * S_out (may be S_in, may be NULL) receives the final state.  N = 1 is the
- * decode step.  One workgroup per (b, h): no workspace.
+ * and all arithmetic is fp32.  The delta rule, and GLA with d_k > 64 or
+ * N < 64, run token by token; GLA with d_k <= 64 and N >= 64 runs in
+ * chunkwise form (64-token chunks; the same sums up to rounding order; GLA
+ * gates are expected in [0, 1], a gate of 0 is taken as 2^-115).  S_in NULL
+ * = zero; S_out (may be S_in, may be NULL) receives the final state.  N = 1
+ * is the decode step.  Workgroups per (b, h) own value columns: no workspace.
  */
 la_status la_forward_gla_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
                                    const float *alpha, const float *S_in, float *S_out, void *O, void *stream);

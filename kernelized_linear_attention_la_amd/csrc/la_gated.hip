@@ -204,6 +204,7 @@ hipError_t launch_gated_t(const GatedArgs &a, hipStream_t st, KEvents ev) {
 }  // namespace
 
 hipError_t launch_gated(const GatedArgs &a, bool gla, int dtype, hipStream_t st, KEvents ev) {
+    if (gla && gla_chunk_supported(a)) return launch_gla_chunk(a, dtype, st, ev);
     if (dtype == kF32)
         return gla ? launch_gated_t<float, true>(a, st, ev) : launch_gated_t<float, false>(a, st, ev);
     return gla ? launch_gated_t<uint16_t, true>(a, st, ev) : launch_gated_t<uint16_t, false>(a, st, ev);

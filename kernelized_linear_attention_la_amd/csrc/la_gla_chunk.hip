@@ -1,0 +1,312 @@
+// GLA's gated recurrence in chunkwise form ("Linear Attention" (aiwiki.ai),
+// gated linear attention; the same recurrence as the token-by-token kernel
+// in la_gated.hip, S_t = diag(alpha_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t).
+//
+// Unrolled over a chunk of C tokens that starts from S_0, with the gates'
+// cumulative logs l_t = sum_{s <= t} log2 alpha_s (per key channel, from the
+// chunk's first token; base 2, the hardware's exp2 and log2):
+//   o_i = S_0^T (q_i * 2^{l_i}) + sum_{t <= i} [sum_c q_ic k_tc 2^{l_ic - l_tc}] v_t
+//   S_C = diag(2^{l_C}) S_0 + sum_t (k_t * 2^{l_C - l_t}) v_t^T
+// Every factor 2^{l_i - l_t} with t <= i is a product of gates, at most 1.
+// The pair sum over channels becomes a matrix product once the factor is
+// split at a pivot p (per channel): 2^{l_i - p} 2^{p - l_t}.  Query block I
+// takes p = l at its own first token: the query part is at most 1 for every
+// key block, the key part is at most 1 for the earlier key blocks and at most
+// the block's own decay on the diagonal block; when that exceeds 2^86 for
+// some channel, the diagonal block is summed element by element instead (the
+// exact form, slower), so no value can overflow whatever the gates.
+//
+// One workgroup of 4 waves owns 16 value columns of one (b, h) slice and
+// walks its chunks in order, the 64 x 16 state slice in accumulators (wave
+// w: feature rows 16w..16w+15).  Wave w owns query rows 16w..16w+15 of each
+// chunk.  All products are v_mfma_f32_16x16x4_f32 (fp32 operands): for that
+// instruction lane l supplies A[l%16][l/16] and B[l/16][l%16] of each
+// 16x4 by 4x16 step and receives D[4(l/16)+e][l%16].  In step ks, k-slot g
+// is channel (or token) 16g + ks, so each lane walks a contiguous 16-wide
+// run of its row and reads it with 16-byte LDS loads.  d_k <= 64 (zero
+// padded; gates of padded channels count as 1).
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;       // tokens per chunk
+constexpr int kK = 64;       // key channels (d_k padded)
+constexpr int kNC = 16;      // value columns per workgroup
+constexpr int kNW = 4;       // waves
+constexpr int kThreads = 64 * kNW;
+constexpr int kRS = kK + 4;  // row stride of the 64-wide tiles (floats)
+constexpr float kPivotBound = 86.f;  // largest diagonal-block decay (in log2) taken through the pivot
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct GlaSmem {
+    float Q[kC][kRS];      // q rows (raw)
+    float K[kC][kRS];      // k rows (raw)
+    float L[kC][kRS];      // cumulative log2 gates from the chunk's first token
+    float KET[kK][kRS];    // [feature][token]: k_t 2^{l_last - l_t}, the state update's operand
+    float VT[kNC][kRS];    // [value column][token]
+    float ST[kNC][kRS];    // [value column][feature]: the state entering the chunk
+    float W[kNW][16][kRS];  // per-wave scores [query row][token]
+    float tot[4][kK];      // per 16-token quarter: sum of log2 gates (the prefix sum's carries)
+    int big[kNW];          // diagonal block b decays by more than 2^86 in some channel
+};
+
+// 16 consecutive floats of an LDS row (16-byte aligned) into registers
+__device__ __forceinline__ void row16(const float *p, float (&r)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + 4 * j);
+        r[4 * j] = v.x; r[4 * j + 1] = v.y; r[4 * j + 2] = v.z; r[4 * j + 3] = v.w;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
+    __shared__ __align__(16) GlaSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int dk = a.dk, dv = a.dv, N = a.N;
+    const int bh = blockIdx.x, col0 = kNC * blockIdx.y;
+    const int ncol = min(kNC, dv - col0);
+    const T *Q = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
+    const T *K = static_cast<const T *>(a.K) + (size_t)bh * N * dk;
+    const T *V = static_cast<const T *>(a.V) + (size_t)bh * N * dv;
+    T *O = static_cast<T *>(a.O) + (size_t)bh * N * dv;
+    const float *Al = a.alpha + (size_t)bh * N * dk;
+
+    // the state slice: wave w holds feature rows 16w + 4g + e, column c16
+    f32x4 S = zero4();
+    if (a.S_in) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 16 * w + 4 * g + e;
+            S[e] = (f < dk && c16 < ncol) ? a.S_in[((size_t)bh * dk + f) * dv + col0 + c16] : 0.f;
+        }
+    }
+
+    // Per chunk each thread stages 16 (token, channel) elements of q, k and
+    // the gates (thread: channel tid % 64, tokens 16 (tid / 64) ..+15) and 4
+    // value elements.  The next chunk's raw elements are loaded while this one
+    // is computed (out-of-range indices read element 0 and are replaced when
+    // staged, so nothing waits for the loads before then).
+    const int sc = tid & 63, sq = tid >> 6;
+    T pq[16], pk[16], pv[4];
+    float pa[16];
+    auto fetch = [&](int t0) {
+        const int nt = min(kC, N - t0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = 16 * sq + j;
+            const bool in = t < nt && sc < dk;
+            const size_t gi = (size_t)(t0 + (in ? t : 0)) * dk + (in ? sc : 0);
+            pq[j] = Q[gi];
+            pk[j] = K[gi];
+            pa[j] = Al[gi];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
+            const bool in = t < nt && cc < ncol;
+            pv[j] = V[(size_t)(t0 + (in ? t : 0)) * dv + col0 + (in ? cc : 0)];
+        }
+    };
+    auto as_f32 = [](T x) {
+        if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
+        else return static_cast<float>(x);
+    };
+
+    fetch(0);
+    for (int t0 = 0; t0 < N; t0 += kC) {
+        // ---- stage q, k, v (zero past the end and in padded channels); log2
+        // gates (1 there) summed within each 16-token quarter
+        float kf[16], lf[16];  // this thread's k and (quarter-local) l, kept for the key operand
+        {
+            const int nt = min(kC, N - t0);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int t = 16 * sq + j;
+                const bool in = t < nt && sc < dk;
+                sm.Q[t][sc] = in ? as_f32(pq[j]) : 0.f;
+                kf[j] = in ? as_f32(pk[j]) : 0.f;
+                sm.K[t][sc] = kf[j];
+                // a gate of 0 counts as 2^-115 (its factor vanishes in fp32)
+                const float al = in ? pa[j] : 1.f;
+                acc += al > 0.f ? lg2(al) : -115.f;
+                lf[j] = acc;
+                sm.L[t][sc] = acc;
+            }
+            sm.tot[sq][sc] = acc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
+                sm.VT[cc][t] = (t < nt && cc < ncol) ? as_f32(pv[j]) : 0.f;
+            }
+        }
+        // this wave's part of the state into the LDS image (rows 4g..4g+3 of column c16)
+        *reinterpret_cast<float4 *>(&sm.ST[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
+        lds_barrier();
+        if (t0 + kC < N) fetch(t0 + kC);  // in flight during this chunk
+        // ---- carry the quarter sums: l_t over the whole chunk so far; the
+        // state update's key operand (a row of 16 tokens per thread); the
+        // diagonal-block decay check
+        {
+            float carry = 0.f, lend = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float tq = sm.tot[q][sc];
+                carry += q < sq ? tq : 0.f;
+                lend += tq;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) lf[j] += carry;
+            if (sq > 0)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sm.L[16 * sq + j][sc] = lf[j];
+#pragma unroll
+            for (int j = 0; j < 16; j += 4)
+                *reinterpret_cast<float4 *>(&sm.KET[sc][16 * sq + j]) =
+                    make_float4(kf[j] * ex2(lend - lf[j]), kf[j + 1] * ex2(lend - lf[j + 1]),
+                                kf[j + 2] * ex2(lend - lf[j + 2]), kf[j + 3] * ex2(lend - lf[j + 3]));
+            // decay across block sq: l(first token) - l(last token)
+            const float dmax = lf[0] - lf[15];
+            const bool over = __builtin_amdgcn_ballot_w64(dmax > kPivotBound) != 0;
+            if (lane == 0) sm.big[sq] = over ? 1 : 0;
+        }
+        lds_barrier();
+
+        // ---- outputs of query block I = w (row i = 16I + c16 as the A operand)
+        const int I = w;
+        float qp[16], piv[16];
+        {
+            float qr[16], lr[16];
+            row16(&sm.Q[16 * I + c16][16 * g], qr);
+            row16(&sm.L[16 * I + c16][16 * g], lr);
+            row16(&sm.L[16 * I][16 * g], piv);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) qp[j] = qr[j] * ex2(lr[j] - piv[j]);  // at most |q|
+        }
+        // Independent accumulators keep several matrix-core chains in flight:
+        // every wave forms the score tiles of all four key blocks (the ones
+        // past its diagonal are dropped; the wave with the most work sets the
+        // pace anyway), and the 16-step sums run as two interleaved halves.
+        f32x4 o0 = zero4(), o1 = zero4();
+        {
+            // inter: sum_c q_ic 2^{l_ic} S_0[c][col], 2^{l_ic} = 2^{l_ic - p} 2^{p}
+            float sr[16];
+            row16(&sm.ST[c16][16 * g], sr);
+#pragma unroll
+            for (int ks = 0; ks < 16; ks += 2) {
+                o0 = mma(qp[ks] * ex2(piv[ks]), sr[ks], o0);
+                o1 = mma(qp[ks + 1] * ex2(piv[ks + 1]), sr[ks + 1], o1);
+            }
+        }
+        // scores of the four key blocks
+        {
+            f32x4 p[4];
+            float kb[4][16];
+#pragma unroll
+            for (int Tb = 0; Tb < 4; ++Tb) {
+                float kr[16], lt[16];
+                row16(&sm.K[16 * Tb + c16][16 * g], kr);
+                row16(&sm.L[16 * Tb + c16][16 * g], lt);
+                // key part 2^{p - l_t}: at most 1 before the diagonal; past it the
+                // tile is dropped, so its exponent is clamped to stay finite
+#pragma unroll
+                for (int ks = 0; ks < 16; ++ks) kb[Tb][ks] = kr[ks] * ex2(fminf(piv[ks] - lt[ks], kPivotBound));
+                p[Tb] = zero4();
+            }
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+                for (int Tb = 0; Tb < 4; ++Tb) p[Tb] = mma(qp[ks], kb[Tb][ks], p[Tb]);
+            const bool big = sm.big[I] != 0;
+            f32x4 pd = zero4();
+            if (big) {  // diagonal block element by element: sum_c q_ic k_tc 2^{l_ic - l_tc}, t <= i
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * g + e, t = 16 * I + c16;
+                    float sacc = 0.f;
+                    if (t <= i)
+                        for (int c = 0; c < kK; ++c) sacc += sm.Q[i][c] * sm.K[t][c] * ex2(sm.L[i][c] - sm.L[t][c]);
+                    pd[e] = sacc;
+                }
+            }
+#pragma unroll
+            for (int Tb = 0; Tb < 4; ++Tb) {
+                const f32x4 pv4 = (big && Tb == I) ? pd : p[Tb];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sm.W[w][4 * g + e][16 * Tb + c16] = (Tb < I || (Tb == I && 4 * g + e >= c16)) ? pv4[e] : 0.f;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // intra: sum_{t <= i} score(i, t) v_t, and the state update's products
+        float vr[16];
+        row16(&sm.VT[c16][16 * g], vr);
+        {
+            float wr[16];
+            row16(&sm.W[w][c16][16 * g], wr);
+#pragma unroll
+            for (int ks = 0; ks < 16; ks += 2) {
+                o0 = mma(wr[ks], vr[ks], o0);
+                o1 = mma(wr[ks + 1], vr[ks + 1], o1);
+            }
+        }
+        const f32x4 o = o0 + o1;
+        const int nt = min(kC, N - t0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g + e;
+            if (i < nt && c16 < ncol) store_from_f32(O, (size_t)(t0 + i) * dv + col0 + c16, o[e]);
+        }
+
+        // ---- state: S = diag(2^{l_last}) S + sum_t KE_t v_t^T (feature rows 16w..)
+        {
+            float kr[16];
+            row16(&sm.KET[16 * w + c16][16 * g], kr);
+            f32x4 u0 = zero4(), u1 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 16; ks += 2) {
+                u0 = mma(kr[ks], vr[ks], u0);
+                u1 = mma(kr[ks + 1], vr[ks + 1], u1);
+            }
+            const f32x4 u = u0 + u1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[e] = ex2(sm.L[kC - 1][16 * w + 4 * g + e]) * S[e] + u[e];
+        }
+        lds_barrier();  // every wave is done with this chunk's tiles
+    }
+    if (a.S_out) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 16 * w + 4 * g + e;
+            if (f < dk && c16 < ncol) a.S_out[((size_t)bh * dk + f) * dv + col0 + c16] = S[e];
+        }
+    }
+}
+
+}  // namespace
+
+bool gla_chunk_supported(const GatedArgs &a) { return a.dk <= kK && a.N >= kC; }
+
+hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t st, KEvents ev) {
+    const dim3 grid((unsigned)a.BH, (unsigned)((a.dv + kNC - 1) / kNC)), block(kThreads);
+    if (dtype == kF32) return launch_kernel_ev(k_gla_chunk<float>, grid, block, 0, st, ev, a);
+    return launch_kernel_ev(k_gla_chunk<uint16_t>, grid, block, 0, st, ev, a);
+}
+
+}  // namespace la

@@ -187,6 +187,9 @@ struct GatedArgs {
     float *S_out;        // [BH, dk, dv] or NULL; may be S_in
 };
 hipError_t launch_gated(const GatedArgs &a, bool gla, int dtype, hipStream_t stream, KEvents ev = {});
+// GLA in chunkwise form (la_gla_chunk.hip): d_k <= 64, N >= 64.
+bool gla_chunk_supported(const GatedArgs &a);
+hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t stream, KEvents ev = {});
 size_t backward_lds_bytes(const Shape &sh);
 hipError_t launch_backward(const BwdLaunch &b, hipStream_t stream, KEvents ev_dq = {}, KEvents ev_scan = {},
                            KEvents ev_dkv = {});

@@ -213,6 +213,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // segment's n chunks for its own sums (keys and values only); the output
     // pass over the same chunks starts at the even step n + (n & 1), so that
     // it always begins on ring slot 0 (step n of an odd segment is empty).
+    // Phase 1 of the single pass walks the segment's chunks last to first
+    // (the sums do not depend on the order; retention's decayed sums do, so it
+    // keeps the forward order): phase 3 then starts on the chunks read last,
+    // which are the likeliest to be still in the Infinity Cache.
+    auto p1_chunk = [&](int i) { return RET ? i : c_end - c_begin - 1 - i; };
     auto fetch = [&](Pref &p, int s) {
         bool live, qlive;
         int cc;
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             const int n = c_end - c_begin, cbase = DEPTH == 2 ? n + (n & 1) : n;
             const bool pa = s < n, pc = s >= cbase && s < cbase + n;
             live = pa || pc;
-            cc = c_begin + (pa ? s : (pc ? s - cbase : 0));
+            cc = c_begin + (pa ? p1_chunk(s) : (pc ? s - cbase : 0));
             qlive = pc;
             if (RES && pc) live = false, cc = c_begin + (s - cbase);  // keys, values are in LDS already
         } else {
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             for (int c = c_begin; c < c_end; ++c) body(pf[0], c, c, Out{});
         } else {
             const int n = c_end - c_begin;
-            for (int i = 0; i < n; ++i) body(pf[0], c_begin + i, i, std::false_type{});
+            for (int i = 0; i < n; ++i) body(pf[0], c_begin + p1_chunk(i), i, std::false_type{});
             publish_and_gather();
             for (int k = 0; k < n; ++k) body(pf[0], c_begin + k, n + k, std::true_type{});
         }
@@ -789,11 +794,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         // ---- phase 1: this segment's own sums, S = 0 + sum phi(K)^T V_aug
         int i = 0;
         for (; i + 2 <= n; i += 2) {
-            body(pf[0], c_begin + i, i, std::false_type{});
-            body(pf[1], c_begin + i + 1, i + 1, std::false_type{});
+            body(pf[0], c_begin + p1_chunk(i), i, std::false_type{});
+            body(pf[1], c_begin + p1_chunk(i + 1), i + 1, std::false_type{});
         }
         if (i < n) {
-            body(pf[0], c_begin + i, i, std::false_type{});  // prefetches step cbase into slot 0
+            body(pf[0], c_begin + p1_chunk(i), i, std::false_type{});  // prefetches step cbase into slot 0
             fetch(pf[DEPTH - 1], cbase + 1);                  // slot 1 held the empty step n
         }
         // ---- phase 2: publish the sums, gather the prefix of the earlier segments
