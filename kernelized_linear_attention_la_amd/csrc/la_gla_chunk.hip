@@ -15,6 +15,10 @@
 // the block's own decay on the diagonal block; when that exceeds 2^86 for
 // some channel, the diagonal block is summed element by element instead (the
 // exact form, slower), so no value can overflow whatever the gates.
+// The sums are kept per 16-token block (local sums from the block's first
+// token, plus block totals), and every exponent is formed as a short sum of
+// those: a difference of two long cumulative sums would lose the small
+// exponents of close pairs once tiny gates have made the sums large.
 //
 // One workgroup of 4 waves owns 16 value columns of one (b, h) slice and
 // walks its chunks in order, the 64 x 16 state slice in accumulators (wave
@@ -53,12 +57,12 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 struct GlaSmem {
     float Q[kC][kRS];      // q rows (raw)
     float K[kC][kRS];      // k rows (raw)
-    float L[kC][kRS];      // cumulative log2 gates from the chunk's first token
+    float L[kC][kRS];      // log2 gates summed from the first token of each 16-token block
     float KET[kK][kRS];    // [feature][token]: k_t 2^{l_last - l_t}, the state update's operand
     float VT[kNC][kRS];    // [value column][token]
     float ST[kNC][kRS];    // [value column][feature]: the state entering the chunk
     float W[kNW][16][kRS];  // per-wave scores [query row][token]
-    float tot[4][kK];      // per 16-token quarter: sum of log2 gates (the prefix sum's carries)
+    float tot[4][kK];      // per 16-token block: the sum of its log2 gates
     int big[kNW];          // diagonal block b decays by more than 2^86 in some channel
 };
 
@@ -159,27 +163,19 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
         *reinterpret_cast<float4 *>(&sm.ST[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
         lds_barrier();
         if (t0 + kC < N) fetch(t0 + kC);  // in flight during this chunk
-        // ---- carry the quarter sums: l_t over the whole chunk so far; the
-        // state update's key operand (a row of 16 tokens per thread); the
-        // diagonal-block decay check
+        // ---- the state update's key operand (a row of 16 tokens per thread):
+        // k_t 2^{l_last - l_t}, the exponent being the rest of the token's own
+        // block plus the later blocks' totals; the diagonal-block decay check
         {
-            float carry = 0.f, lend = 0.f;
+            float later = 0.f;  // totals of the blocks after this thread's
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float tq = sm.tot[q][sc];
-                carry += q < sq ? tq : 0.f;
-                lend += tq;
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) lf[j] += carry;
-            if (sq > 0)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) sm.L[16 * sq + j][sc] = lf[j];
+            for (int q = 0; q < 4; ++q) later += q > sq ? sm.tot[q][sc] : 0.f;
+            const float own = lf[15];
 #pragma unroll
             for (int j = 0; j < 16; j += 4)
                 *reinterpret_cast<float4 *>(&sm.KET[sc][16 * sq + j]) =
-                    make_float4(kf[j] * ex2(lend - lf[j]), kf[j + 1] * ex2(lend - lf[j + 1]),
-                                kf[j + 2] * ex2(lend - lf[j + 2]), kf[j + 3] * ex2(lend - lf[j + 3]));
+                    make_float4(kf[j] * ex2((own - lf[j]) + later), kf[j + 1] * ex2((own - lf[j + 1]) + later),
+                                kf[j + 2] * ex2((own - lf[j + 2]) + later), kf[j + 3] * ex2((own - lf[j + 3]) + later));
             // decay across block sq: l(first token) - l(last token)
             const float dmax = lf[0] - lf[15];
             const bool over = __builtin_amdgcn_ballot_w64(dmax > kPivotBound) != 0;
@@ -187,7 +183,8 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
         }
         lds_barrier();
 
-        // ---- outputs of query block I = w (row i = 16I + c16 as the A operand)
+        // ---- outputs of query block I = w (row i = 16I + c16 as the A operand);
+        // pivot: l at block I's first token (local sums: l_i - piv stays in the block)
         const int I = w;
         float qp[16], piv[16];
         {
@@ -203,29 +200,31 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
         // past its diagonal are dropped; the wave with the most work sets the
         // pace anyway), and the 16-step sums run as two interleaved halves.
         f32x4 o0 = zero4(), o1 = zero4();
-        {
-            // inter: sum_c q_ic 2^{l_ic} S_0[c][col], 2^{l_ic} = 2^{l_ic - p} 2^{p}
-            float sr[16];
-            row16(&sm.ST[c16][16 * g], sr);
+        // scores of the four key blocks, last to first: for T < I the key part
+        // is 2^{span + piv - l_t}, span = the totals of blocks T..I-1 (summed
+        // here, never as a difference), all terms <= 0; for T = I it is
+        // 2^{piv - l_t} within the block; past the diagonal the tile is dropped
+        // and its exponent is clamped to stay finite
+        float span[16];
 #pragma unroll
-            for (int ks = 0; ks < 16; ks += 2) {
-                o0 = mma(qp[ks] * ex2(piv[ks]), sr[ks], o0);
-                o1 = mma(qp[ks + 1] * ex2(piv[ks + 1]), sr[ks + 1], o1);
-            }
-        }
-        // scores of the four key blocks
+        for (int ks = 0; ks < 16; ++ks) span[ks] = 0.f;
         {
             f32x4 p[4];
             float kb[4][16];
 #pragma unroll
-            for (int Tb = 0; Tb < 4; ++Tb) {
+            for (int Tb = 3; Tb >= 0; --Tb) {
+                if (Tb < I) {
+                    float tr[16];
+                    row16(&sm.tot[Tb][16 * g], tr);
+#pragma unroll
+                    for (int ks = 0; ks < 16; ++ks) span[ks] += tr[ks];
+                }
                 float kr[16], lt[16];
                 row16(&sm.K[16 * Tb + c16][16 * g], kr);
                 row16(&sm.L[16 * Tb + c16][16 * g], lt);
-                // key part 2^{p - l_t}: at most 1 before the diagonal; past it the
-                // tile is dropped, so its exponent is clamped to stay finite
 #pragma unroll
-                for (int ks = 0; ks < 16; ++ks) kb[Tb][ks] = kr[ks] * ex2(fminf(piv[ks] - lt[ks], kPivotBound));
+                for (int ks = 0; ks < 16; ++ks)
+                    kb[Tb][ks] = kr[ks] * ex2(fminf(span[ks] + (piv[ks] - lt[ks]), kPivotBound));
                 p[Tb] = zero4();
             }
 #pragma unroll
@@ -250,6 +249,18 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     sm.W[w][4 * g + e][16 * Tb + c16] = (Tb < I || (Tb == I && 4 * g + e >= c16)) ? pv4[e] : 0.f;
+            }
+        }
+        {
+            // inter: sum_c q_ic 2^{l_i - l_start} S_0[c][col]; from the chunk's
+            // start, 2^{...} = 2^{l_i - piv} 2^{piv + (totals of blocks 0..I-1)}
+            // (span now holds those totals)
+            float sr[16];
+            row16(&sm.ST[c16][16 * g], sr);
+#pragma unroll
+            for (int ks = 0; ks < 16; ks += 2) {
+                o0 = mma(qp[ks] * ex2(piv[ks] + span[ks]), sr[ks], o0);
+                o1 = mma(qp[ks + 1] * ex2(piv[ks + 1] + span[ks + 1]), sr[ks + 1], o1);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -286,7 +297,10 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
             }
             const f32x4 u = u0 + u1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[e] = ex2(sm.L[kC - 1][16 * w + 4 * g + e]) * S[e] + u[e];
+            for (int e = 0; e < 4; ++e) {
+                const int f = 16 * w + 4 * g + e;  // decay of the whole chunk: the four block totals
+                S[e] = ex2((sm.tot[0][f] + sm.tot[1][f]) + (sm.tot[2][f] + sm.tot[3][f])) * S[e] + u[e];
+            }
         }
         lds_barrier();  // every wave is done with this chunk's tiles
     }

@@ -90,3 +90,55 @@ def test_state_handoff_in_place():
         torch.cuda.synchronize()
         assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
         assert state_rel_err(to_f64(S), Sref) < 1e-4
+
+
+def _extreme_gates(seed, B, H, N, dk):
+    """GLA gates that stress the chunkwise form: exact zeros (the state is
+    cleared), tiny gates (a 16-token block decays past 2^-86, so its diagonal
+    block is summed element by element), mid-range and near-one gates."""
+    rng = np.random.default_rng(seed)
+    u = rng.random((B, H, N, dk))
+    a = np.where(u < 0.1, 0.0,
+                 np.where(u < 0.3, rng.uniform(1e-4, 0.05, u.shape),
+                          np.where(u < 0.5, rng.uniform(0.5, 0.9, u.shape), rng.uniform(0.9, 1.0, u.shape))))
+    # one slice keeps near-one gates only (the pivoted path everywhere)
+    a[0, 0] = rng.uniform(0.9, 1.0, a[0, 0].shape)
+    return a.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gla_extreme_gates_against_oracle(dtype):
+    B, H, N, dk, dv = 1, 2, 300, 64, 40
+    gi = inputs.gated_inputs(2200, B, H, N, dk, dv, dtype)
+    al = _extreme_gates(2200, B, H, N, dk)
+    S_in = inputs.positive_state(2200, B, H, dk, dv, tokens=4)[0]
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    S_out = torch.empty(B, H, dk, dv, device="cuda")
+    O = la.la_forward_gla_recurrent(q, k, v, torch.from_numpy(al).cuda(), S_in=torch.from_numpy(S_in).cuda(),
+                                    S_out=S_out)
+    ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, al, S_in=S_in)
+    torch.cuda.synchronize()
+    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    _say("gla extreme gates", dtype, f"O {eo:.2e} S {es:.2e}")
+    tol = tol_for(dtype)
+    assert np.isfinite(to_f64(O)).all()
+    assert eo < tol and es < tol, (eo, es)
+
+
+def test_gla_state_handoff_across_forms():
+    """GLA in two calls == one call, S_out aliasing S_in: the first part runs token by
+    token (fewer than 64 tokens) or chunkwise, the second part chunkwise."""
+    B, H, N, d = 2, 2, 300, 32
+    gi = inputs.gated_inputs(2300, B, H, N, d, d, "f32")
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    al = torch.from_numpy(gi.alpha_ch).cuda()
+    ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch)
+    for M in (30, 100):
+        _say("gla handoff M", M)
+        S = torch.zeros(B, H, d, d, device="cuda")
+        c = lambda x, a, b: x[:, :, a:b].contiguous()  # noqa: E731
+        O1 = la.la_forward_gla_recurrent(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(al, 0, M), S_out=S)
+        O2 = la.la_forward_gla_recurrent(c(q, M, N), c(k, M, N), c(v, M, N), c(al, M, N), S_in=S, S_out=S)
+        torch.cuda.synchronize()
+        assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
+        assert state_rel_err(to_f64(S), Sref) < 1e-4
