@@ -262,6 +262,8 @@ def kernel_symbol(wl, slot):
         seg = -(-n_chunks // P)
         if P > 1 and seg * wl.chunk <= 256 and wl.dk == 64 and wl.dv == 64 and wl.phi in ("elu1", "identity"):
             return f"k_seg<{phi_id}>"  # a whole segment (at most 256 tokens) per 16-wave workgroup
+        if P > 1 and wl.phi == "favor":
+            return "k_favor"  # eight waves per workgroup, two per SIMD
         res = seg <= 4 and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and wl.phi in ("elu1", "identity")
         return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {phi_id}, {4 if res else 3}>"
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"

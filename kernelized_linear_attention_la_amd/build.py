@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "liblinattn.so")
 SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_mfma_seg.hip", "la_backward.hip", "la_backward_mfma.hip",
-           "la_gated.hip", "la_gla_chunk.hip"]
+           "la_gated.hip", "la_gla_chunk.hip", "la_favor.hip"]
 ARCH = "gfx950"
 
 
@@ -70,6 +70,7 @@ def build(extra_flags=(), verbose: bool = False) -> str:
 # sizes its grid and segments.
 KERNEL_SOURCES = {
     "k_mfma": ("la_mfma.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_favor": ("la_favor.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_seg": ("la_mfma_seg.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_generic": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_scan": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),

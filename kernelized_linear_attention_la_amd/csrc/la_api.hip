@@ -173,9 +173,12 @@ int fused_mode(const Shape &sh, const Segments &g) {
 }
 
 // Single pass on the matrix cores: the whole-segment kernel where a segment
-// fits one 16-wave workgroup, else the chunk loop.
+// fits one 16-wave workgroup, the eight-wave FAVOR+ kernel for its shape,
+// else the chunk loop.
 hipError_t launch_single_pass(const FwdArgs &f, hipStream_t st, KEvents ev) {
-    return seg_supported(f.sh, f.sg) ? launch_seg(f, st, ev) : launch_mfma(f, st, ev);
+    if (seg_supported(f.sh, f.sg)) return launch_seg(f, st, ev);
+    if (f.mode == kModeFused && favor_supported(f.sh, f.sg)) return launch_favor(f, st, ev);
+    return launch_mfma(f, st, ev);
 }
 
 size_t causal_ws(const Shape &sh, int chunk) {

@@ -140,6 +140,10 @@ bool mfma_supported(const Shape &sh, int chunk);
 // workgroup (la_mfma_seg.hip): bf16, d = 64, ELU+1 or retention, P > 1.
 bool seg_supported(const Shape &sh, const Segments &g);
 hipError_t launch_seg(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
+// FAVOR+ single pass with eight waves per workgroup (la_favor.hip): bf16,
+// d_k = d_v = 64, m = 256, 64-token chunks, P > 1.
+bool favor_supported(const Shape &sh, const Segments &g);
+hipError_t launch_favor(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 
 // Backward of the causal normalised form (la_backward.hip): three launches
 // per call after the forward prefix is in Spre / zpre.

@@ -125,5 +125,27 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// MI355X: workgroups go round-robin over 8 XCDs
+constexpr int kXcds = 8;
+
+// Workgroup order.  Workgroup b is dispatched to XCD b % 8, so the segments
+// of a slice are given workgroup numbers 8 apart: in every complete group of
+// eight slices, b = 8P group + 8 seg + slice % 8; the slices past the last
+// complete group share the remaining numbers the same way.  Within a slice
+// the segment order is the workgroup order (a segment only waits for lower
+// workgroups).
+__device__ __forceinline__ void seg_of_block(int b, int BH, int P, int &bh, int &seg) {
+    const int full = BH / kXcds, gsz = kXcds * P;
+    if (b < full * gsz) {
+        const int r = b % gsz;
+        seg = r / kXcds;
+        bh = (b / gsz) * kXcds + r % kXcds;
+    } else {
+        const int rest = BH % kXcds, r = b - full * gsz;
+        seg = r / rest;
+        bh = full * kXcds + r % rest;
+    }
+}
+
 }  // namespace
 }  // namespace la

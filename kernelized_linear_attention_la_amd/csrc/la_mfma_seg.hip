@@ -40,7 +40,6 @@ constexpr int kSRK = kSD + 8;   // phi(K) row stride (bf16): 16-row 128-bit read
 constexpr int kSRV = 144;       // V_aug row stride: 16 mod 128 keeps the transpose reads conflict free
 constexpr int kSKB = kSD / 32;  // 32-feature k-blocks
 constexpr int kStrips = kSD / 16;  // 16-row feature strips of the state, one state wave each
-constexpr int kXcds = 8;            // MI355X: workgroups go round-robin over 8 XCDs
 static_assert(kStrips <= kFlagsPerSegment, "one hand-off flag per strip");
 
 template <bool RET>
@@ -62,25 +61,6 @@ __device__ __forceinline__ void put_tile(uint4 (*STB)[kSKB][64], int fb, int nb,
     const uint2 v = pack4(s[0], s[1], s[2], s[3]);
     const int x = 16 * (fb & 1) + 4 * g;  // feature slot inside the 32-feature k-block
     reinterpret_cast<uint2 *>(&STB[nb][fb >> 1][c + 16 * (x >> 3)])[(x >> 2) & 1] = v;
-}
-
-// Workgroup order.  Workgroup b is dispatched to XCD b % 8, so the segments
-// of a slice are given workgroup numbers 8 apart: in every complete group of
-// eight slices, b = 8P group + 8 seg + slice % 8; the slices past the last
-// complete group share the remaining numbers the same way.  Within a slice
-// the segment order is the workgroup order (a segment only waits for lower
-// workgroups).
-__device__ __forceinline__ void seg_of_block(int b, int BH, int P, int &bh, int &seg) {
-    const int full = BH / kXcds, gsz = kXcds * P;
-    if (b < full * gsz) {
-        const int r = b % gsz;
-        seg = r / kXcds;
-        bh = (b / gsz) * kXcds + r % kXcds;
-    } else {
-        const int rest = BH % kXcds, r = b - full * gsz;
-        seg = r / rest;
-        bh = full * kXcds + r % rest;
-    }
 }
 
 template <int PHI>
