@@ -152,9 +152,7 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
             sq = fmaf(v0, v0, sq);
             sq = fmaf(v1, v1, sq);
         }
-        sq += __shfl_xor(sq, 1, 64);
-        sq += __shfl_xor(sq, 2, 64);
-        sq += __shfl_xor(sq, 4, 64);
+        sq = group8_sum(sq);
         return valid ? fmaf(sq, 0.5f * kLog2e, 4.0f) : __builtin_inff();
     };
     auto stage = [&](const Pref &p, int t0, bool with_q) {
@@ -210,17 +208,21 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
         Op8 ka[2][2];  // [fbl][kt]
 #pragma unroll
         for (int fbl = 0; fbl < 2; ++fbl) {
+            f32x4 u[4];  // the four token blocks' chains, issued interleaved
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) u[tb] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) u[tb] = mfma(xb[tb][kb], wr[fbl][kb][part], u[tb]);
             float ph[4][4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                f32x4 u = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int part = 0; part < 2; ++part) u = mfma(xb[tb][kb], wr[fbl][kb][part], u);
                 const float shf[4] = {shv[tb].x, shv[tb].y, shv[tb].z, shv[tb].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ph[tb][e] = __builtin_amdgcn_exp2f(fmaf(u[e], kLog2e, -shf[e]));
+                for (int e = 0; e < 4; ++e) ph[tb][e] = __builtin_amdgcn_exp2f(fmaf(u[tb][e], kLog2e, -shf[e]));
             }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
@@ -256,18 +258,23 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) shv[tb] = shift[16 * tb + c16];
 #pragma unroll
-            for (int fbl = 0; fbl < 2; ++fbl)
+            for (int fbl = 0; fbl < 2; ++fbl) {
+                f32x4 u[4];  // the four token blocks' chains, issued interleaved
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) u[tb] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int part = 0; part < 2; ++part)
+#pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) u[tb] = mfma(wr[fbl][kb][part], xb[tb][kb], u[tb]);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    f32x4 u = zero4();
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int part = 0; part < 2; ++part) u = mfma(wr[fbl][kb][part], xb[tb][kb], u);
-                    auto ph = [&](int e) { return __builtin_amdgcn_exp2f(fmaf(u[e], kLog2e, -shv[tb])); };
+                    auto ph = [&](int e) { return __builtin_amdgcn_exp2f(fmaf(u[tb][e], kLog2e, -shv[tb])); };
                     *reinterpret_cast<uint2 *>(&dst[(16 * tb + c16) * kFRK + 32 * w + 16 * fbl + 4 * g]) =
                         pack4(ph(0), ph(1), ph(2), ph(3));
                 }
+            }
         };
         project(sm.XK, sm.SH[0], sm.K);
         project(sm.XQ, sm.SH[1], sm.QP);

@@ -24,21 +24,6 @@ namespace {
 
 constexpr int kRG = 8;     // row groups per value column (lanes 8c .. 8c + 7)
 
-// x plus lane-permuted x (a DPP control word)
-template <int CTRL>
-__device__ __forceinline__ float add_dpp(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the 8 lanes of a group (lanes 8c .. 8c + 7), result in all 8:
-// swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), then
-// add the mirrored half (row_half_mirror: lane i of each 8 takes lane 7 - i).
-__device__ __forceinline__ float group8_sum(float x) {
-    x = add_dpp<0xB1>(x);
-    x = add_dpp<0x4E>(x);
-    return add_dpp<0x141>(x);
-}
-
 // R rows per lane: lane 8c + r owns rows R r .. R r + R - 1 of column
 // 64 blockIdx.y + 8w + c.
 template <typename T, bool GLA, int R>
