@@ -25,6 +25,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxDp = 256;
 constexpr int kMaxD = 128;
 constexpr int kBatch = 8;  // rows in flight per thread between load and store
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <typename T, int VW, bool RET>
 __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restrict__ q, const T *__restrict__ k,
@@ -141,8 +142,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
                 if (f < dp) {
                     const float *src = Ss + (size_t)f * dv + cg * VW;
                     if constexpr (VW == 4) {
-                        float4 t4 = *reinterpret_cast<const float4 *>(src);
-                        buf[b][0] = t4.x; buf[b][1] = t4.y; buf[b][2] = t4.z; buf[b][3] = t4.w;
+                        // streamed once per step: non-temporal, so the state does not displace cached lines
+                        const f32x4v t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(src));
+                        buf[b][0] = t4[0]; buf[b][1] = t4[1]; buf[b][2] = t4[2]; buf[b][3] = t4[3];
                     } else {
 #pragma unroll
                         for (int u = 0; u < VW; ++u) buf[b][u] = src[u];
@@ -162,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
                     }
                     float *dst = Ss + (size_t)f * dv + cg * VW;
                     if constexpr (VW == 4) {
-                        *reinterpret_cast<float4 *>(dst) = make_float4(buf[b][0], buf[b][1], buf[b][2], buf[b][3]);
+                        __builtin_nontemporal_store(f32x4v{buf[b][0], buf[b][1], buf[b][2], buf[b][3]},
+                                                    reinterpret_cast<f32x4v *>(dst));
                     } else {
 #pragma unroll
                         for (int u = 0; u < VW; ++u) dst[u] = buf[b][u];
