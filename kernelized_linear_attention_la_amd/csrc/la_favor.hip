@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
         const int qrows = pc ? rows : 0;
         p.k = bload16(make_rsrc(Ks + (size_t)tt0 * kFD, rows * kFD * 2), 16 * tid);
         p.v = bload16(make_rsrc(Vs + (size_t)tt0 * kFD, rows * kFD * 2), 16 * tid);
-        p.q = bload16(make_rsrc(Qs + (size_t)tt0 * kFD, qrows * kFD * 2), 16 * tid);
+        p.q = bload16_nt(make_rsrc(Qs + (size_t)tt0 * kFD, qrows * kFD * 2), 16 * tid);
     };
     // piece tid of a chunk is row tid / 8, columns 8 (tid % 8).  The eight
     // lanes of a row also form its exponent shift in the log2 domain,
@@ -287,47 +287,51 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
         f32x4 acc[kFNJ];
 #pragma unroll
         for (int nb = 0; nb < kFNJ; ++nb) acc[nb] = zero4();
-        // (P (.) M) V_aug, P^T = phi(K) phi(Q)^T computed transposed so that two
-        // consecutive accumulator tiles are the A operand of the value product
+        // the causal structure of query block qb as constants (qb is wave-uniform)
+        dispatch_const<4>(qb, [&](auto qbc) {
+            constexpr int QB = decltype(qbc)::value;
+            // (P (.) M) V_aug, P^T = phi(K) phi(Q)^T computed transposed so that two
+            // consecutive accumulator tiles are the A operand of the value product
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            if (2 * kt <= qb) {
-                f32x4 pt[2];
+            for (int kt = 0; kt < 2; ++kt) {
+                if (2 * kt <= QB) {
+                    f32x4 pt[2];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int jb = 2 * kt + hh;
-                    pt[hh] = zero4();
-                    if (jb <= qb) {
-                        const uint16_t *krow = &sm.K[(16 * jb + c16) * kFRK + 128 * h + 8 * g];
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int jb = 2 * kt + hh;
+                        pt[hh] = zero4();
+                        if (jb <= QB) {
+                            const uint16_t *krow = &sm.K[(16 * jb + c16) * kFRK + 128 * h + 8 * g];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            Op8 ka;
-                            ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * j);
-                            pt[hh] = mfma(ka, phq[j], pt[hh]);
-                        }
-                        if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
+                            for (int j = 0; j < 4; ++j) {
+                                Op8 ka;
+                                ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * j);
+                                pt[hh] = mfma(ka, phq[j], pt[hh]);
+                            }
+                            if (jb == QB) {  // causal mask on the diagonal block: key 4g+e <= query c16
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (4 * g + e > c16) pt[hh][e] = 0.f;
+                                for (int e = 0; e < 4; ++e)
+                                    if (4 * g + e > c16) pt[hh][e] = 0.f;
+                            }
                         }
                     }
+                    Op8 pa;
+                    pa.q[0] = pack4(pt[0][0], pt[0][1], pt[0][2], pt[0][3]);
+                    pa.q[1] = pack4(pt[1][0], pt[1][1], pt[1][2], pt[1][3]);
+#pragma unroll
+                    for (int nb = 0; nb < kFNJ; ++nb) acc[nb] = mfma(pa, token_operand<kFRV>(sm.V, kt, 16 * nb, lane), acc[nb]);
                 }
-                Op8 pa;
-                pa.q[0] = pack4(pt[0][0], pt[0][1], pt[0][2], pt[0][3]);
-                pa.q[1] = pack4(pt[1][0], pt[1][1], pt[1][2], pt[1][3]);
-#pragma unroll
-                for (int nb = 0; nb < kFNJ; ++nb) acc[nb] = mfma(pa, token_operand<kFRV>(sm.V, kt, 16 * nb, lane), acc[nb]);
             }
-        }
-        // phi(Q) S_aug with the state carried into this chunk
+            // phi(Q) S_aug with the state carried into this chunk
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int nb = 0; nb < kFNJ; ++nb) {
-                Op8 sb;
-                sb.u = sm.STB[nb][4 * h + j][lane];
-                acc[nb] = mfma(phq[j], sb, acc[nb]);
-            }
+                for (int nb = 0; nb < kFNJ; ++nb) {
+                    Op8 sb;
+                    sb.u = sm.STB[nb][4 * h + j][lane];
+                    acc[nb] = mfma(phq[j], sb, acc[nb]);
+                }
+        });
         if (h == 1) {
 #pragma unroll
             for (int nb = 0; nb < kFNJ; ++nb) sm.X[qb][nb][lane] = acc[nb];
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kFT) void k_favor(FwdArgs a) {
             for (int it = 0; it < 2; ++it) {
                 const int idx = it * 64 + lane;
                 const int r = idx >> 3, c8 = idx & 7;
-                bstore16(ro, 2 * ((16 * qb + r) * kFD + 8 * c8), *reinterpret_cast<const uint4 *>(&so[r * kFRO + 8 * c8]));
+                bstore16_nt(ro, 2 * ((16 * qb + r) * kFD + 8 * c8), *reinterpret_cast<const uint4 *>(&so[r * kFRO + 8 * c8]));
             }
         }
 

@@ -246,10 +246,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             const auto rq = make_rsrc(Qs + (size_t)tt0 * DK, qrows * DK * 2);
             if constexpr (G::XR) {
 #pragma unroll
-                for (int i = 0; i < UQT; ++i) p.raw[UKT + UVT + i].u = bload16(rq, 16 * (tid + i * G::THREADS));
+                for (int i = 0; i < UQT; ++i) p.raw[UKT + UVT + i].u = bload16_nt(rq, 16 * (tid + i * G::THREADS));
             } else {
 #pragma unroll
-                for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = bload16(rq, 2 * (row * DK + 8 * g + 32 * kb));
+                for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = bload16_nt(rq, 2 * (row * DK + 8 * g + 32 * kb));
             }
         }
     };
@@ -469,31 +469,30 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                     for (int nb = 0; nb < NJ; ++nb) acc[nb][e] *= r;
                 }
-            }
-            if constexpr (INTRA) {
-                // (P (.) M) V_aug over the key blocks up to the diagonal
+                if constexpr (INTRA) {
+                    // (P (.) M) V_aug over the key blocks up to the diagonal
 #pragma unroll
-                for (int kt = 0; kt < KBT; ++kt) {
-                    if (2 * kt <= qb) {
-                        f32x4 p[2];
+                    for (int kt = 0; kt < KBT; ++kt) {
+                        if (2 * kt <= qb) {
+                            f32x4 p[2];
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const int jb = 2 * kt + h;
-                            p[h] = zero4();
-                            if (jb <= qb) {
-                                const uint16_t *krow = &sm.K[ks][(16 * jb + c16) * RK];
+                            for (int h = 0; h < 2; ++h) {
+                                const int jb = 2 * kt + h;
+                                p[h] = zero4();
+                                if (jb <= qb) {
+                                    const uint16_t *krow = &sm.K[ks][(16 * jb + c16) * RK];
 #pragma unroll
-                                for (int kf = 0; kf < KBF; ++kf) {
-                                    Op8 ka;
-                                    ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
-                                    p[h] = mfma(ka, phq[kf], p[h]);
-                                }
-                                if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
+                                    for (int kf = 0; kf < KBF; ++kf) {
+                                        Op8 ka;
+                                        ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
+                                        p[h] = mfma(ka, phq[kf], p[h]);
+                                    }
+                                    if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e)
-                                        if (4 * g + e > c16) p[h][e] = 0.f;
-                                }
-                                if constexpr (RET) {  // decay mask lambda^(query - key)
+                                        for (int e = 0; e < 4; ++e)
+                                            if (4 * g + e > c16) p[h][e] = 0.f;
+                                    }
+                                    // decay mask lambda^(query - key)
 #pragma unroll
                                     for (int e = 0; e < 4; ++e) {
                                         const int d = 16 * (qb - jb) + c16 - 4 * g - e;
@@ -501,17 +500,60 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                                     }
                                 }
                             }
-                        }
-                        Op8 pa;
-                        pa.q[0] = pack4(p[0][0], p[0][1], p[0][2], p[0][3]);
-                        pa.q[1] = pack4(p[1][0], p[1][1], p[1][2], p[1][3]);
+                            Op8 pa;
+                            pa.q[0] = pack4(p[0][0], p[0][1], p[0][2], p[0][3]);
+                            pa.q[1] = pack4(p[1][0], p[1][1], p[1][2], p[1][3]);
 #pragma unroll
-                        for (int nb = 0; nb < NJ; ++nb)
-                            acc[nb] = mfma(pa, token_operand<RV>(sm.V[ks], kt, 16 * nb, lane), acc[nb]);
+                            for (int nb = 0; nb < NJ; ++nb)
+                                acc[nb] = mfma(pa, token_operand<RV>(sm.V[ks], kt, 16 * nb, lane), acc[nb]);
+                        }
                     }
                 }
+            } else {
+                // The normalised maps take the query block as a compile-time
+                // constant (qb is wave-uniform): the causal loop becomes straight
+                // line and the key blocks' loads can be issued ahead.  Retention
+                // keeps the run-time loop above (its decay factors spill the
+                // registers of the unrolled form).
+                dispatch_const<NW>(qb, [&](auto qbc) {
+                    constexpr int QB = decltype(qbc)::value;
+                    if constexpr (INTRA) {
+                        // (P (.) M) V_aug over the key blocks up to the diagonal
+#pragma unroll
+                        for (int kt = 0; kt < KBT; ++kt) {
+                            if (2 * kt <= QB) {
+                                f32x4 p[2];
+#pragma unroll
+                                for (int h = 0; h < 2; ++h) {
+                                    const int jb = 2 * kt + h;
+                                    p[h] = zero4();
+                                    if (jb <= QB) {
+                                        const uint16_t *krow = &sm.K[ks][(16 * jb + c16) * RK];
+#pragma unroll
+                                        for (int kf = 0; kf < KBF; ++kf) {
+                                            Op8 ka;
+                                            ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
+                                            p[h] = mfma(ka, phq[kf], p[h]);
+                                        }
+                                        if (jb == QB) {  // causal mask on the diagonal block: key 4g+e <= query c16
+#pragma unroll
+                                            for (int e = 0; e < 4; ++e)
+                                                if (4 * g + e > c16) p[h][e] = 0.f;
+                                        }
+                                    }
+                                }
+                                Op8 pa;
+                                pa.q[0] = pack4(p[0][0], p[0][1], p[0][2], p[0][3]);
+                                pa.q[1] = pack4(p[1][0], p[1][1], p[1][2], p[1][3]);
+#pragma unroll
+                                for (int nb = 0; nb < NJ; ++nb)
+                                    acc[nb] = mfma(pa, token_operand<RV>(sm.V[ks], kt, 16 * nb, lane), acc[nb]);
+                            }
+                        }
+                    }
+                    inter();
+                });
             }
-            if constexpr (!RET) inter();
             // epilogue: divide by the normaliser column (retention: none), round,
             // stage, store 16 B per lane
             float rden[4];
@@ -536,7 +578,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 const int idx = it * 64 + lane;
                 const int r = idx / (DV / 8), c8 = idx % (DV / 8);
                 const uint4 val = *reinterpret_cast<const uint4 *>(&so[r * RO + 8 * c8]);
-                bstore16(ro, 2 * ((16 * qb + r) * DV + 8 * c8), val);
+                bstore16_nt(ro, 2 * ((16 * qb + r) * DV + 8 * c8), val);
             }
         }
 

@@ -10,6 +10,8 @@
 // accumulator tiles, so P becomes an A operand without an LDS round trip.
 #pragma once
 
+#include <type_traits>
+
 #include "la_device.h"
 
 namespace la {
@@ -84,6 +86,17 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
 }
+// The same with the non-temporal cache policy (nt), for data a kernel touches
+// exactly once (queries, outputs; the keys and values of a kernel that reads
+// them once): it streams past the caches instead of displacing lines that
+// are read again.
+constexpr int kStream = 2;
+__device__ __forceinline__ uint4 bload16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream));
+}
+__device__ __forceinline__ void bstore16_nt(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kStream);
+}
 
 // Cache policy of the hand-off between workgroups of one launch (they may run
 // on different XCDs, whose L2 caches are not coherent with each other): sc1,
@@ -123,6 +136,19 @@ __device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmc
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+}
+
+// f(std::integral_constant<int, v>) for a wave-uniform v in [0, N): code that
+// depends on v (causal loop bounds, masks) becomes straight-line per value,
+// so loads of later blocks can be issued early.  Values past N - 1 take N - 1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void dispatch_const(int v, F &&f) {
+    if constexpr (I + 1 < N) {
+        if (v == I) f(std::integral_constant<int, I>{});
+        else dispatch_const<N, I + 1>(v, f);
+    } else {
+        f(std::integral_constant<int, I>{});
+    }
 }
 
 // MI355X: workgroups go round-robin over 8 XCDs

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
     uint4 kraw[PT], vraw[PT], qraw[kSKB];
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-        kraw[i] = bload16(rk, 16 * (tid + i * kSThreads));
-        vraw[i] = bload16(rv, 16 * (tid + i * kSThreads));
+        kraw[i] = bload16_nt(rk, 16 * (tid + i * kSThreads));
+        vraw[i] = bload16_nt(rv, 16 * (tid + i * kSThreads));
     }
     const int qb = w;              // this wave's 16-row query block inside the segment
     const int row = 16 * qb + c16;  // this lane's query row (A operand of phi(Q) S)
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
     // the query rows go out once the keys and values (which the hand-off
     // waits for) have arrived
 #pragma unroll
-    for (int kb = 0; kb < kSKB; ++kb) qraw[kb] = bload16(rq, 2 * (row * kSD + 8 * g + 32 * kb));
+    for (int kb = 0; kb < kSKB; ++kb) qraw[kb] = bload16_nt(rq, 2 * (row * kSD + 8 * g + 32 * kb));
     block_sync_lds();
 
     Op8 phq[kSKB];
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
 #pragma unroll
     for (int it = 0; it < 16 * kSD / 8 / 64; ++it) {
         const int idx = it * 64 + lane, r = idx / (kSD / 8), c8 = idx % (kSD / 8);
-        bstore16(ro, 2 * ((16 * qb + r) * kSD + 8 * c8), *reinterpret_cast<const uint4 *>(&so[r * kSRK + 8 * c8]));
+        bstore16_nt(ro, 2 * ((16 * qb + r) * kSD + 8 * c8), *reinterpret_cast<const uint4 *>(&so[r * kSRK + 8 * c8]));
     }
 
     // the last workgroup of the launch to finish (all flag reads done)
