@@ -226,6 +226,11 @@ def gla_on_chunks(wl):
     return wl.gated == "gla" and wl.dk <= 64 and wl.N >= 64
 
 
+def delta_on_chunks(wl):
+    """The library runs the gated delta rule in chunkwise form for d_k = 64, d_v a multiple of 16 up to 128."""
+    return wl.gated == "delta" and wl.dk == 64 and wl.dv % 16 == 0 and 16 <= wl.dv <= 128
+
+
 def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
@@ -558,9 +563,14 @@ def bench_gated(args, wl):
     o = torch.empty_like(v)
     raw = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    def step():
+    chunked = delta_on_chunks(wl)
+    ws = (torch.empty(la.la_delta_workspace_bytes(q, v), dtype=torch.uint8, device=dev) if chunked else None)
+
+    def step(events=None):
         if wl.gated == "gla":
             la.la_forward_gla_recurrent(q, k, v, a_ch, S_out=S, out=o)
+        elif chunked:
+            la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_out=S, out=o, workspace=ws, events=events)
         else:
             la.la_forward_delta_recurrent(q, k, v, be, alpha=al, S_out=S, out=o)
 
@@ -582,19 +592,39 @@ def bench_gated(args, wl):
         hev.destroy(b_)
     kern_ms = sum(durs) / len(durs)
     ms_per_step = elapsed * 1e3 / args.steps
+    extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
+    if chunked:
+        # the two launches of the chunkwise form timed one by one through the
+        # library's hook (per-chunk solves, then the scan over chunks)
+        slots = (la.LA_KSLOT_STATE, la.LA_KSLOT_CHUNK)
+        kd = {sl: [] for sl in slots}
+        for _ in range(args.steps):
+            kev = la.LaKernelEvents()
+            ev = {sl: (hev.create(), hev.create()) for sl in slots}
+            for sl in slots:
+                kev.start[sl], kev.stop[sl] = ev[sl]
+            step(events=kev)
+            torch.cuda.synchronize()
+            for sl in slots:
+                kd[sl].append(hev.elapsed_ms(*ev[sl]))
+                hev.destroy(ev[sl][0])
+                hev.destroy(ev[sl][1])
+        extra = {"kernel_avg_us": {"k_delta_prep": round(1e3 * sum(kd[slots[0]]) / len(kd[slots[0]]), 2),
+                                   "k_delta_scan": round(1e3 * sum(kd[slots[1]]) / len(kd[slots[1]]), 2)},
+                 "step_kernels_us": round(kern_ms * 1e3, 2)}
     flops = gated_alg_flops(wl)
     ach = flops / (kern_ms * 1e-3) / 1e12
-    kname = kernel_symbol(wl, "chunk")
-    # fp32 arithmetic: chunkwise GLA on the matrix cores (dense fp32 MFMA peak), the
-    # token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own
-    bound = "mfma" if gla_on_chunks(wl) else "alu"
+    kname = "k_delta_prep + k_delta_scan" if chunked else kernel_symbol(wl, "chunk")
+    # fp32 arithmetic: the chunkwise forms on the matrix cores (dense fp32 MFMA peak),
+    # the token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own,
+    # over the step's kernels (for the chunkwise delta rule both launches)
+    bound = "mfma" if (gla_on_chunks(wl) or chunked) else "alu"
     peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
     roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-            "frac": ach / peak, "traffic": stored_traffic(wl, kname), "kernel": kname,
+            "frac": ach / peak, "traffic": None if chunked else stored_traffic(wl, kname), "kernel": kname,
             "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
-            "timing": "hip events around each launch"}
+            "timing": "hip events around each call (both launches of the chunkwise form)"}
     tokens = wl.B * wl.H * wl.N
-    extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
     return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, gi
 
 
@@ -741,7 +771,7 @@ def main():
     elif wl.gated:
         value, ms, roof, extra, fi = bench_gated(args, wl)
         metric = ("GLA recurrence tokens/s (B*H*N/s)" if wl.gated == "gla"
-                  else "gated delta-rule recurrence tokens/s (B*H*N/s)")
+                  else "gated delta-rule tokens/s (B*H*N/s)")
     else:
         value, ms, roof, extra, fi = bench_forward(args, wl)
         metric = ("causal retention fwd tokens/s (B*H*N/s)" if wl.retention

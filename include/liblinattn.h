@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 4
+#define LA_ABI_VERSION 5
 
 typedef enum {
     LA_OK = 0,
@@ -316,6 +316,35 @@ la_status la_forward_gla_recurrent(const la_problem *p, const void *Q, const voi
 la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const void *K, const void *V,
                                      const float *alpha, const float *beta, const float *S_in, float *S_out,
                                      void *O, void *stream);
+
+/*
+ * The gated delta rule above in chunkwise form (64-token chunks; the pages'
+ * Gated DeltaNet, "Story of Attention Part 5", section 7, with the state
+ * written as S_t = g_t S0 + sum_s (g_t / g_s) k_s u_s^T inside a chunk, g the
+ * cumulative forget gates).  The write vectors of a chunk solve the unit
+ * lower-triangular system (I + M) U = diag(beta) V - diag(beta g) K S0,
+ * M[t][s] = beta_t (g_t / g_s) k_t . k_s for s < t, so U = Ut - W S0 with W and
+ * Ut independent of the entering state: the library forms W, Ut and the
+ * causal score matrix of every chunk at once (first launch), then runs the
+ * chunks of each (b, h) slice in order per 16 value columns (second launch).
+ * The same sums as la_forward_delta_recurrent up to rounding order (fp32
+ * arithmetic).  Arguments as there, plus:
+ *   chunk  must be 64;  p->d_k must be 64 and p->d_v a multiple of 16 up to
+ *          128, else LA_ERR_UNSUPPORTED (the token-by-token entry point takes
+ *          every shape);
+ *   ws     device workspace of at least la_delta_workspace_bytes(p, chunk)
+ *          bytes (16-byte aligned; no initial contents needed; one record per
+ *          (b, h, chunk): W, P [64 x 64], Ut [64 x d_v], gate products), owned
+ *          by the caller; else LA_ERR_WORKSPACE;
+ *   ev     optional timing hook: slot LA_KSLOT_STATE brackets the per-chunk
+ *          launch, LA_KSLOT_CHUNK the scan over chunks.
+ * Forget gates below 2^-80 are taken as 2^-80.  S_out may alias S_in.
+ */
+size_t la_delta_workspace_bytes(const la_problem *p, int chunk);
+
+la_status la_forward_delta_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
+                                   const float *alpha, const float *beta, const float *S_in, float *S_out,
+                                   void *O, void *ws, size_t ws_bytes, void *stream, la_kernel_events *ev);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "liblinattn.so")
 SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_mfma_seg.hip", "la_backward.hip", "la_backward_mfma.hip",
-           "la_gated.hip", "la_gla_chunk.hip", "la_favor.hip"]
+           "la_gated.hip", "la_gla_chunk.hip", "la_favor.hip", "la_delta_chunk.hip"]
 ARCH = "gfx950"
 
 
@@ -78,6 +78,8 @@ KERNEL_SOURCES = {
     "k_bwd_dq": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_rscan": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dkv": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_delta_prep": ("la_delta_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_delta_scan": ("la_delta_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gated": ("la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gla_chunk": ("la_gla_chunk.hip", "la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dq_mfma": ("la_backward_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),

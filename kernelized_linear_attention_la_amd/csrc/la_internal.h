@@ -194,6 +194,12 @@ hipError_t launch_gated(const GatedArgs &a, bool gla, int dtype, hipStream_t str
 // GLA in chunkwise form (la_gla_chunk.hip): d_k <= 64, N >= 64.
 bool gla_chunk_supported(const GatedArgs &a);
 hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t stream, KEvents ev = {});
+// Gated delta rule in chunkwise form (la_delta_chunk.hip): d_k = 64, d_v a
+// multiple of 16 up to 128, 64-token chunks; ws holds one record per chunk.
+bool delta_chunk_supported(int dk, int dv, int chunk);
+size_t delta_chunk_ws_bytes(int BH, int N, int dv);
+hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStream_t stream, KEvents ev_prep = {},
+                              KEvents ev_scan = {});
 size_t backward_lds_bytes(const Shape &sh);
 hipError_t launch_backward(const BwdLaunch &b, hipStream_t stream, KEvents ev_dq = {}, KEvents ev_scan = {},
                            KEvents ev_dkv = {});

@@ -196,8 +196,10 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
         const int fb = w - 8;
 #pragma unroll
         for (int nb = 0; nb < NJ; ++nb) own[nb] = zero4();
-        const int nkt = (L + 31) / 32;  // 32-token blocks holding data
-        for (int kt = 0; kt < nkt; ++kt) {
+        // every 32-token block of the segment, a fixed count so the operand
+        // loads can run ahead: rows past the end hold phi(k) = 0 and add nothing
+#pragma unroll
+        for (int kt = 0; kt < kSL / 32; ++kt) {
             Op8 ka = token_operand<kSRK>(sm.K, kt, 16 * fb, lane);
             if constexpr (RET) {
                 auto kw = [&](int sl) {

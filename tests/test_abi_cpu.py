@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert linattn.la_abi_version() == 4
+    assert linattn.la_abi_version() == 5
     for s in range(8):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)
@@ -216,6 +216,35 @@ def test_gated_validation():
     assert L.la_forward_delta_recurrent(ctypes.byref(pid), FAKE, FAKE, FAKE, None, FAKE, MIS, None, FAKE, None) == 5
     assert L.la_forward_delta_recurrent(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=129)), FAKE, FAKE, FAKE,
                                         None, FAKE, None, None, FAKE, None) == 2
+
+
+def test_delta_chunked_validation():
+    """la_forward_delta_chunked validates before any launch: shape support,
+    pointers, alignment and workspace size (no compute without a GPU)."""
+    L = linattn.lib()
+    pid = _p(phi=linattn.LA_PHI_IDENTITY)  # d_k = d_v = 64
+    need = L.la_delta_workspace_bytes(ctypes.byref(pid), 64)
+    # one record per (b, h, chunk): W and P (64 x 64), Ut (64 x d_v), gate products (2 x 64), fp32
+    n_chunks = -(-pid.N // 64)
+    assert need == 4 * pid.B * pid.H * n_chunks * (2 * 64 * 64 + 64 * 64 + 128)
+    assert L.la_delta_workspace_bytes(ctypes.byref(pid), 32) == 0
+    assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=32)), 64) == 0
+    assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_v=40)), 64) == 0
+    assert L.la_delta_workspace_bytes(ctypes.byref(_p()), 64) == 0  # ELU+1: raw q, k only
+
+    def call(p=pid, chunk=64, Q=FAKE, al=None, be=FAKE, ws=FAKE, wsb=need):
+        return L.la_forward_delta_chunked(ctypes.byref(p), chunk, Q, FAKE, FAKE, al, be, None, None, FAKE, ws, wsb,
+                                          None, None)
+    assert call(chunk=32) == 4
+    assert call(p=_p(phi=linattn.LA_PHI_IDENTITY, d_k=32)) == 4
+    assert call(p=_p()) == 4
+    assert call(be=None) == 1
+    assert call(Q=None) == 1
+    assert call(Q=MIS) == 5
+    assert call(al=ctypes.c_void_p(0x100002)) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=need - 1) == 6
+    assert call(p=_p(phi=linattn.LA_PHI_IDENTITY, B=0)) == 2
 
 
 def test_feature_map_parameters_validation():

@@ -142,3 +142,78 @@ def test_gla_state_handoff_across_forms():
         torch.cuda.synchronize()
         assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
         assert state_rel_err(to_f64(S), Sref) < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# Gated delta rule in chunkwise form (la_forward_delta_chunked): the same
+# recurrence as the oracle, evaluated through per-chunk triangular solves.
+# ---------------------------------------------------------------------------
+CHUNKED_CASES = [
+    # (B, H, N, dk, dv, dtype, with S_in)
+    (1, 2, 256, 64, 64, "f32", False),
+    (2, 3, 100, 64, 16, "f32", True),      # ragged last chunk, one 16-column block
+    (1, 1, 1, 64, 32, "f32", True),        # one token
+    (1, 2, 50, 64, 128, "f32", True),      # shorter than a chunk, widest values
+    (1, 1, 65, 64, 48, "bf16", True),      # one token past a chunk
+    (2, 4, 1000, 64, 128, "bf16", False),
+    (4, 8, 2048, 64, 64, "bf16", True),    # the gated delta-rule workload's shape
+]
+
+
+@pytest.mark.parametrize("kind", ["delta", "gated_delta"])
+@pytest.mark.parametrize("ci", range(len(CHUNKED_CASES)),
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}dv{c[4]}{c[5]}{'S' if c[6] else ''}" for c in CHUNKED_CASES])
+def test_delta_chunked_against_oracle(ci, kind):
+    B, H, N, dk, dv, dtype, state = CHUNKED_CASES[ci]
+    gi = inputs.gated_inputs(2300 + ci, B, H, N, dk, dv, dtype)
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    S_in = inputs.positive_state(2300 + ci, B, H, dk, dv, tokens=4)[0] if state else None
+    dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    alpha = gi.alpha if kind == "gated_delta" else None
+    S_out = torch.empty(B, H, dk, dv, device="cuda")
+    _say("chunked", kind, CHUNKED_CASES[ci])
+    O = la.la_forward_delta_chunked(q, k, v, dev(gi.beta), alpha=dev(alpha), S_in=dev(S_in), S_out=S_out)
+    torch.cuda.synchronize()
+    ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=alpha, S_in=S_in)
+    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    _say("chunked", kind, f"O {eo:.2e} S {es:.2e}")
+    tol = tol_for(dtype)
+    assert eo < tol and es < tol, (eo, es)
+
+
+def test_delta_chunked_handoff_and_small_gates():
+    """Two chunked calls (0..M, then M..N from the first call's state, S_out
+    aliasing S_in) equal the oracle over 0..N; forget gates down to 1e-3 and
+    exact zeros (the state is cleared) included."""
+    B, H, N, dk, dv = 2, 2, 300, 64, 32
+    gi = inputs.gated_inputs(2400, B, H, N, dk, dv, "f32")
+    rng = np.random.default_rng(2400)
+    al = gi.alpha.copy()
+    u = rng.random(al.shape)
+    al[u < 0.05] = 0.0
+    al[(u >= 0.05) & (u < 0.15)] = rng.uniform(1e-3, 0.5, al[(u >= 0.05) & (u < 0.15)].shape).astype(np.float32)
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    be, alt = torch.from_numpy(gi.beta).cuda(), torch.from_numpy(al).cuda()
+    ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=al)
+    for M in (1, 64, 130):
+        _say("chunked handoff M", M)
+        S = torch.zeros(B, H, dk, dv, device="cuda")
+        c = lambda x, a, b: x[:, :, a:b].contiguous()  # noqa: E731
+        O1 = la.la_forward_delta_chunked(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(be, 0, M), alpha=c(alt, 0, M),
+                                         S_out=S)
+        O2 = la.la_forward_delta_chunked(c(q, M, N), c(k, M, N), c(v, M, N), c(be, M, N), alpha=c(alt, M, N),
+                                         S_in=S, S_out=S)
+        torch.cuda.synchronize()
+        eo = slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref)
+        es = state_rel_err(to_f64(S), Sref)
+        _say("chunked handoff", M, f"O {eo:.2e} S {es:.2e}")
+        assert eo < 1e-4 and es < 1e-4, (eo, es)
+
+
+def test_delta_chunked_rejects_unsupported_shapes():
+    gi = inputs.gated_inputs(2500, 1, 1, 64, 32, 32, "f32")
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    be = torch.from_numpy(gi.beta).cuda()
+    with pytest.raises(RuntimeError):
+        la.la_forward_delta_chunked(q, k, v, be)  # d_k = 32: the token-by-token entry point takes it
+    assert la.la_delta_workspace_bytes(q, v) == 0
