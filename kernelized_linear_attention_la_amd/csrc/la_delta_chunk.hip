@@ -230,12 +230,16 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
 
 // One workgroup per (slice, 16 value columns): the chunks in order.  Wave w
 // owns token rows 16w..16w+15 of U and O, and feature rows 16w..16w+15 of the
-// state (fp32 accumulators for the whole slice).
+// state (fp32 accumulators for the whole slice).  The row operands of W S0,
+// Q S0 and P U come straight from global memory into registers, one chunk
+// ahead: for those products k-step j of lane group q = l/16 takes index
+// 16q + j (P U: 16kb + 4q + j), so each lane reads contiguous 16-byte runs,
+// and the B operands (state image, U) are read from LDS in the same order.
 template <typename T>
 __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, const T *__restrict__ K, T *__restrict__ O,
                                                     const float *__restrict__ ws, const float *__restrict__ S_in,
                                                     float *__restrict__ S_out, int N, int dv, int n_chunks) {
-    __shared__ float sW[kXC * kXR], sP[kXC * kXR], sQ[kXC * kXR], sK[kXC * kXR];
+    __shared__ float sK[kXC * kXR];
     __shared__ float sS[kXK * 20], sU[kXC * 20], sUg[kXC * 20], sUt[kXC * 20];
     __shared__ float sg[kXC], sgt[kXC];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
     const int ncb = dv / 16;
     const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
     const int col0 = 16 * cb;
+    const int r = c16, q = g;  // A-operand row and k group of this lane
 
     // state rows 16w + 4g + e, column col0 + c16
     f32x4d S = zero4d();
@@ -251,51 +256,50 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
         for (int e = 0; e < 4; ++e) S[e] = S_in[((size_t)bh * kXK + 16 * w + 4 * g + e) * dv + col0 + c16];
     }
 
-    // Chunk data in flight: W and P (4 float4 each per thread), the 16 Ut
-    // columns (1 float4), Q and K rows (16-byte pieces: 2 per thread for bf16,
-    // 4 for fp32), the gate products (threads 0..31).  Chunk c + 1 is fetched
-    // while chunk c is computed.
-    constexpr int QP = kXC * kXK * (int)sizeof(T) / 16 / kXT;  // 16-byte pieces of Q (and K) per thread
+    constexpr int EP = 16 / (int)sizeof(T);         // elements per 16-byte piece
+    constexpr int KP = kXC * kXK / EP / kXT;        // pieces of K per thread
+    constexpr int QR = 16 / EP;                     // pieces of this lane's 16 Q values
     struct Pre {
         float4 w[4], p[4], ut, gg;
-        uint4 q[QP], k[QP];
+        uint4 q[QR], k[KP];
     };
     auto fetch = [&](Pre &f, int c) {
         if (c >= n_chunks) return;
         const int t0 = c * kXC, L = min(kXC, N - t0);
         const float *rec = ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv);
+        const float *Wr = rec + (16 * w + r) * kXK + 16 * q;          // W[16w + r][16q ..]
+        const float *Pr = rec + kXC * kXK + (16 * w + r) * kXK + 4 * q;  // P[16w + r][16kb + 4q ..]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * kXT;  // row idx / 16, float4 idx % 16
-            f.w[i] = reinterpret_cast<const float4 *>(rec)[idx];
-            f.p[i] = reinterpret_cast<const float4 *>(rec + kXC * kXK)[idx];
+            f.w[i] = *reinterpret_cast<const float4 *>(Wr + 4 * i);
+            f.p[i] = *reinterpret_cast<const float4 *>(Pr + 16 * i);
         }
         f.ut = *reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)(tid >> 2) * dv + col0 + 4 * (tid & 3));
         if (tid < 32) f.gg = reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)kXC * dv)[tid];
-        const char *qb = reinterpret_cast<const char *>(Q + ((size_t)bh * N + t0) * kXK);
+        const bool qlive = 16 * w + r < L;
+        const T *qrow = Q + ((size_t)bh * N + t0 + 16 * w + r) * kXK + 16 * q;
+#pragma unroll
+        for (int i = 0; i < QR; ++i)
+            f.q[i] = qlive ? reinterpret_cast<const uint4 *>(qrow)[i] : make_uint4(0, 0, 0, 0);
         const char *kb = reinterpret_cast<const char *>(K + ((size_t)bh * N + t0) * kXK);
         const int bytes = L * kXK * (int)sizeof(T);
 #pragma unroll
-        for (int i = 0; i < QP; ++i) {
+        for (int i = 0; i < KP; ++i) {
             const int off = 16 * (tid + i * kXT);
-            f.q[i] = off < bytes ? *reinterpret_cast<const uint4 *>(qb + off) : make_uint4(0, 0, 0, 0);
             f.k[i] = off < bytes ? *reinterpret_cast<const uint4 *>(kb + off) : make_uint4(0, 0, 0, 0);
         }
     };
-    // 16-byte piece -> fp32 row values in LDS
-    auto put_row = [&](float *dst, int i, const uint4 &x) {
-        const int e0 = (16 * (tid + i * kXT)) / (int)sizeof(T);  // first element of the piece
-        const int t = e0 / kXK, f = e0 % kXK;
-        float *d = &dst[t * kXR + f];
+    auto unpack = [&](const uint4 &x, float *o) {
         if constexpr (sizeof(T) == 2) {
             const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                d[2 * e] = __uint_as_float(xs[e] << 16);
-                d[2 * e + 1] = __uint_as_float(xs[e] & 0xffff0000u);
+                o[2 * e] = __uint_as_float(xs[e] << 16);
+                o[2 * e + 1] = __uint_as_float(xs[e] & 0xffff0000u);
             }
         } else {
-            *reinterpret_cast<uint4 *>(d) = x;
+            o[0] = __uint_as_float(x.x); o[1] = __uint_as_float(x.y);
+            o[2] = __uint_as_float(x.z); o[3] = __uint_as_float(x.w);
         }
     };
     Pre pre;
@@ -304,38 +308,51 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
     for (int c = 0; c < n_chunks; ++c) {
         const int t0 = c * kXC, L = min(kXC, N - t0);
         const size_t tok0 = (size_t)bh * N + t0;
-        // stage chunk c, then fetch chunk c + 1
+        // operands of chunk c in registers; K, Ut, gates and the state image into LDS
+        float wa[16], qa[16], pa[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * kXT, t = idx >> 4, f4 = 4 * (idx & 15);
-            *reinterpret_cast<float4 *>(&sW[t * kXR + f4]) = pre.w[i];
-            *reinterpret_cast<float4 *>(&sP[t * kXR + f4]) = pre.p[i];
+            wa[4 * i] = pre.w[i].x; wa[4 * i + 1] = pre.w[i].y; wa[4 * i + 2] = pre.w[i].z; wa[4 * i + 3] = pre.w[i].w;
+            pa[4 * i] = pre.p[i].x; pa[4 * i + 1] = pre.p[i].y; pa[4 * i + 2] = pre.p[i].z; pa[4 * i + 3] = pre.p[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < QR; ++i) unpack(pre.q[i], &qa[EP * i]);
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            const int e0 = EP * (tid + i * kXT), t = e0 / kXK, f = e0 % kXK;
+            float o[EP];
+            unpack(pre.k[i], o);
+#pragma unroll
+            for (int e = 0; e < EP; ++e) sK[t * kXR + f + e] = o[e];
         }
         *reinterpret_cast<float4 *>(&sUt[(tid >> 2) * 20 + 4 * (tid & 3)]) = pre.ut;
         if (tid < 32) {
             const float gg[4] = {pre.gg.x, pre.gg.y, pre.gg.z, pre.gg.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 4 * tid + e;  // gate products g then g_C / g
+                const int i = 4 * tid + e;  // gate products g, then g_C / g
                 if (i < kXC) sg[i] = gg[e];
                 else sgt[i - kXC] = gg[e];
             }
         }
 #pragma unroll
-        for (int i = 0; i < QP; ++i) {
-            put_row(sQ, i, pre.q[i]);
-            put_row(sK, i, pre.k[i]);
-        }
-#pragma unroll
         for (int e = 0; e < 4; ++e) sS[(16 * w + 4 * g + e) * 20 + c16] = S[e];
         sync_lds();
         fetch(pre, c + 1);
-        sync_lds();
 
-        // U = Ut - W S0 and Q S0 for token rows 16w..16w+15
-        auto bS = [&](int k, int n) { return sS[k * 20 + n]; };
-        const f32x4d ws0 = mm4<16>([&](int m, int k) { return sW[(16 * w + m) * kXR + k]; }, bS, zero4d(), lane);
-        f32x4d o = mm4<16>([&](int m, int k) { return sQ[(16 * w + m) * kXR + k]; }, bS, zero4d(), lane);
+        // U = Ut - W S0 and Q S0 for token rows 16w..16w+15 (k = 16q + j); two
+        // accumulators per product halve the dependent chains
+        f32x4d ws0 = zero4d(), o = zero4d(), ws1 = zero4d(), o1 = zero4d();
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            const float b0 = sS[(16 * q + j) * 20 + c16], b1 = sS[(16 * q + j + 1) * 20 + c16];
+            ws0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j], b0, ws0, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], b0, o, 0, 0, 0);
+            ws1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j + 1], b1, ws1, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j + 1], b1, o1, 0, 0, 0);
+        }
+        ws0 += ws1;
+        o += o1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * w + 4 * g + e;
@@ -346,14 +363,23 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
         }
         sync_lds();
 
-        // O += P U over the keys up to this row block (P is zero above the diagonal)
-        auto bU = [&](int k, int n) { return sU[k * 20 + n]; };
-        for (int kb = 0; kb <= w; ++kb)
-            o = mm4<4>([&](int m, int k) { return sP[(16 * w + m) * kXR + 16 * kb + k]; },
-                       [&](int k, int n) { return bU(16 * kb + k, n); }, o, lane);
-        // S = g_C S0 + K^T diag(g_C / g) U for feature rows 16w..16w+15
-        const f32x4d ku = mm4<16>([&](int m, int k) { return sK[k * kXR + 16 * w + m]; },
-                                  [&](int k, int n) { return sUg[k * 20 + n]; }, zero4d(), lane);
+        // O += P U over the key blocks up to this row block (k = 16kb + 4q + j)
+        f32x4d o2 = zero4d();
+        for (int kb = 0; kb <= w; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kb + j], sU[(16 * kb + 4 * q + j) * 20 + c16], o, 0, 0, 0);
+                o2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kb + j + 1], sU[(16 * kb + 4 * q + j + 1) * 20 + c16], o2,
+                                                          0, 0, 0);
+            }
+        }
+        o += o2;
+        // S = g_C S0 + K^T diag(g_C / g) U for feature rows 16w..16w+15 (tokens
+        // 0..31 and 32..63 in two accumulators)
+        auto aK = [&](int m, int k) { return sK[k * kXR + 16 * w + m]; };
+        const f32x4d ku = mm4<8>(aK, [&](int k, int n) { return sUg[k * 20 + n]; }, zero4d(), lane) +
+                          mm4<8>([&](int m, int k) { return aK(m, k + 32); },
+                                 [&](int k, int n) { return sUg[(k + 32) * 20 + n]; }, zero4d(), lane);
         const float gC = sg[kXC - 1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[e] = gC * S[e] + ku[e];
