@@ -222,8 +222,8 @@ def backward_on_mfma(wl):
 
 
 def gla_on_chunks(wl):
-    """The library runs GLA in chunkwise form (fp32 matrix instructions) for d_k <= 64, N >= 64."""
-    return wl.gated == "gla" and wl.dk <= 64 and wl.N >= 64
+    """GLA in chunkwise form on fp32 matrix instructions (d_k <= 64): the two-launch entry point."""
+    return wl.gated == "gla" and wl.dk <= 64
 
 
 def delta_on_chunks(wl):
@@ -239,8 +239,10 @@ def kernel_symbol(wl, slot):
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.gated:
         t = "float" if wl.dtype == "f32" else "unsigned short"
+        if delta_on_chunks(wl):
+            return f"k_delta_scan<{t}>"  # the longer of the chunkwise form's two launches
         if gla_on_chunks(wl):
-            return f"k_gla_chunk<{t}>"
+            return f"k_gla_scan<{t}>"  # the scan of the two-launch form
         return f"k_gated<{t}, {'true' if wl.gated == 'gla' else 'false'}>"
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
@@ -563,11 +565,16 @@ def bench_gated(args, wl):
     o = torch.empty_like(v)
     raw = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    chunked = delta_on_chunks(wl)
-    ws = (torch.empty(la.la_delta_workspace_bytes(q, v), dtype=torch.uint8, device=dev) if chunked else None)
+    chunked = delta_on_chunks(wl) or gla_on_chunks(wl)
+    ws = None
+    if chunked:
+        nbytes = la.la_gla_workspace_bytes(q, v) if wl.gated == "gla" else la.la_delta_workspace_bytes(q, v)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step(events=None):
-        if wl.gated == "gla":
+        if wl.gated == "gla" and chunked:
+            la.la_forward_gla_chunked(q, k, v, a_ch, S_out=S, out=o, workspace=ws, events=events)
+        elif wl.gated == "gla":
             la.la_forward_gla_recurrent(q, k, v, a_ch, S_out=S, out=o)
         elif chunked:
             la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_out=S, out=o, workspace=ws, events=events)
@@ -609,16 +616,18 @@ def bench_gated(args, wl):
                 kd[sl].append(hev.elapsed_ms(*ev[sl]))
                 hev.destroy(ev[sl][0])
                 hev.destroy(ev[sl][1])
-        extra = {"kernel_avg_us": {"k_delta_prep": round(1e3 * sum(kd[slots[0]]) / len(kd[slots[0]]), 2),
-                                   "k_delta_scan": round(1e3 * sum(kd[slots[1]]) / len(kd[slots[1]]), 2)},
+        pre = "k_gla" if wl.gated == "gla" else "k_delta"
+        extra = {"kernel_avg_us": {pre + "_prep": round(1e3 * sum(kd[slots[0]]) / len(kd[slots[0]]), 2),
+                                   pre + "_scan": round(1e3 * sum(kd[slots[1]]) / len(kd[slots[1]]), 2)},
                  "step_kernels_us": round(kern_ms * 1e3, 2)}
     flops = gated_alg_flops(wl)
     ach = flops / (kern_ms * 1e-3) / 1e12
-    kname = "k_delta_prep + k_delta_scan" if chunked else kernel_symbol(wl, "chunk")
+    kname = ("k_gla_prep + k_gla_scan" if wl.gated == "gla" else "k_delta_prep + k_delta_scan") if chunked \
+        else kernel_symbol(wl, "chunk")
     # fp32 arithmetic: the chunkwise forms on the matrix cores (dense fp32 MFMA peak),
     # the token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own,
     # over the step's kernels (for the chunkwise delta rule both launches)
-    bound = "mfma" if (gla_on_chunks(wl) or chunked) else "alu"
+    bound = "mfma" if chunked else "alu"
     peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
     roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
             "frac": ach / peak, "traffic": None if chunked else stored_traffic(wl, kname), "kernel": kname,

@@ -342,6 +342,26 @@ la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const v
  */
 size_t la_delta_workspace_bytes(const la_problem *p, int chunk);
 
+/*
+ * GLA (la_forward_gla_recurrent) in two launches: the chunk form's products
+ * that do not involve the values (gate sums, decayed keys and queries, the
+ * masked pair scores with their overflow-safe pivot split) are formed once
+ * per 64-token chunk, every chunk at once; then each (b, h) slice walks its
+ * chunks per 16 value columns: O = QD S0 + P V, S_C = diag(decay) S0 + KE V.
+ * The same sums as the one-launch chunk form.  Arguments as
+ * la_forward_gla_recurrent, plus: chunk must be 64 and p->d_k <= 64 (else
+ * LA_ERR_UNSUPPORTED); any N >= 1; ws: device workspace of at least
+ * la_gla_workspace_bytes(p, chunk) bytes (16-byte aligned, no initial
+ * contents; one record of 3 x 64 x 64 + 64 floats per (b, h, chunk)), else
+ * LA_ERR_WORKSPACE; ev: optional timing hook (LA_KSLOT_STATE: the per-chunk
+ * launch, LA_KSLOT_CHUNK: the scan).  S_out may alias S_in.
+ */
+size_t la_gla_workspace_bytes(const la_problem *p, int chunk);
+
+la_status la_forward_gla_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
+                                 const float *alpha, const float *S_in, float *S_out, void *O, void *ws,
+                                 size_t ws_bytes, void *stream, la_kernel_events *ev);
+
 la_status la_forward_delta_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
                                    const float *alpha, const float *beta, const float *S_in, float *S_out,
                                    void *O, void *ws, size_t ws_bytes, void *stream, la_kernel_events *ev);

@@ -612,6 +612,38 @@ LA_API la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, 
     return gated_call(p, false, Q, K, V, alpha, beta, S_in, S_out, O, stream);
 }
 
+LA_API size_t la_gla_workspace_bytes(const la_problem *p, int chunk) {
+    if (la::check_problem(p) != LA_OK || p->phi != LA_PHI_IDENTITY || p->d_k > 64 || chunk != 64) return 0;
+    return la::gla_chunk_ws_bytes(p->B * p->H, p->N);
+}
+
+LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
+                                        const float *alpha, const float *S_in, float *S_out, void *O, void *ws,
+                                        size_t ws_bytes, void *stream, la_kernel_events *ev) {
+    using namespace la;
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->phi != LA_PHI_IDENTITY || p->d_k > 64 || chunk != 64) return LA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O || !alpha) return LA_ERR_NULL;
+    const void *ptrs[] = {Q, K, V, O, S_in, S_out, ws};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return LA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(alpha) & 3u) return LA_ERR_ALIGN;
+    if (!ws || ws_bytes < gla_chunk_ws_bytes(p->B * p->H, p->N)) return LA_ERR_WORKSPACE;
+    if (ev)
+        for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
+    GatedArgs a;
+    a.BH = p->B * p->H; a.N = p->N; a.dk = p->d_k; a.dv = p->d_v;
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.alpha = alpha; a.beta = nullptr;
+    a.S_in = S_in; a.S_out = S_out;
+    return launch_gla_split(a, p->dtype == LA_BF16 ? kBF16 : kF32, static_cast<float *>(ws),
+                            static_cast<hipStream_t>(stream), slot_events(ev, LA_KSLOT_STATE),
+                            slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
+               ? LA_OK
+               : LA_ERR_DEVICE;
+}
+
 LA_API size_t la_delta_workspace_bytes(const la_problem *p, int chunk) {
     if (la::check_problem(p) != LA_OK || p->phi != LA_PHI_IDENTITY ||
         !la::delta_chunk_supported(p->d_k, p->d_v, chunk))

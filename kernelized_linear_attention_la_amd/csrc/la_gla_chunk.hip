@@ -313,6 +313,254 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same chunk form in two launches (la_forward_gla_chunked).  Everything
+// above that does not depend on the value columns -- the gate sums, the
+// decayed keys KE[c][t] = k_tc 2^{l_last,c - l_tc}, the masked pair scores
+// P[i][t] (pivot split, element-wise diagonal block for extreme decays), the
+// decayed queries QD[i][c] = q_ic 2^{l_ic - l_start,c} and the chunk decay
+// 2^{l_last,c - l_start,c} -- is formed once per chunk by k_gla_prep (one
+// workgroup per (slice, chunk), every chunk at once) into a workspace record;
+// k_gla_scan then walks the chunks of each (slice, 16 value columns) with only
+// the three products that touch the values:
+//   O = QD S_0 + P V,   S_C = diag(decay) S_0 + KE V.
+// ---------------------------------------------------------------------------
+
+// Per-chunk record (floats): P [64][64], QD [64][64], KE [64][64], decay [64].
+__host__ __device__ inline size_t gla_rec_floats() { return 3 * kC * kK + kK; }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks, float *__restrict__ ws) {
+    __shared__ __align__(16) GlaSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int dk = a.dk, N = a.N;
+    const int bh = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks;
+    const int t0 = ch * kC, nt = min(kC, N - t0);
+    const T *Q = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
+    const T *K = static_cast<const T *>(a.K) + (size_t)bh * N * dk;
+    const float *Al = a.alpha + (size_t)bh * N * dk;
+    float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats();
+    float *P = rec, *QD = rec + kC * kK, *KE = rec + 2 * kC * kK, *DEC = rec + 3 * kC * kK;
+    auto as_f32 = [](T x) {
+        if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
+        else return static_cast<float>(x);
+    };
+
+    // stage q, k (zero past the end and in padded channels) and the log2
+    // gates (1 there) summed within each 16-token quarter: thread = channel
+    // tid % 64, tokens 16 (tid / 64) .. +15
+    const int sc = tid & 63, sq = tid >> 6;
+    float kf[16], lf[16];
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = 16 * sq + j;
+            const bool in = t < nt && sc < dk;
+            const size_t gi = (size_t)(t0 + t) * dk + sc;
+            sm.Q[t][sc] = in ? as_f32(Q[gi]) : 0.f;
+            kf[j] = in ? as_f32(K[gi]) : 0.f;
+            sm.K[t][sc] = kf[j];
+            // a gate of 0 counts as 2^-115 (its factor vanishes in fp32)
+            const float al = in ? Al[gi] : 1.f;
+            acc += al > 0.f ? lg2(al) : -115.f;
+            lf[j] = acc;
+            sm.L[t][sc] = acc;
+        }
+        sm.tot[sq][sc] = acc;
+    }
+    lds_barrier();
+    // decayed keys k_t 2^{l_last - l_t} ([feature][token]) and the diagonal-block check
+    {
+        float later = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) later += q > sq ? sm.tot[q][sc] : 0.f;
+        const float own = lf[15];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4)
+            *reinterpret_cast<float4 *>(&KE[sc * kC + 16 * sq + j]) =
+                make_float4(kf[j] * ex2((own - lf[j]) + later), kf[j + 1] * ex2((own - lf[j + 1]) + later),
+                            kf[j + 2] * ex2((own - lf[j + 2]) + later), kf[j + 3] * ex2((own - lf[j + 3]) + later));
+        const float dmax = lf[0] - lf[15];
+        const bool over = __builtin_amdgcn_ballot_w64(dmax > kPivotBound) != 0;
+        if (lane == 0) sm.big[sq] = over ? 1 : 0;
+        if (sq == 0) DEC[sc] = ex2((sm.tot[0][sc] + sm.tot[1][sc]) + (sm.tot[2][sc] + sm.tot[3][sc]));
+    }
+    lds_barrier();
+
+    // scores and decayed queries of query block I = w (as in k_gla_chunk)
+    const int I = w;
+    float qp[16], piv[16];
+    {
+        float qr[16], lr[16];
+        row16(&sm.Q[16 * I + c16][16 * g], qr);
+        row16(&sm.L[16 * I + c16][16 * g], lr);
+        row16(&sm.L[16 * I][16 * g], piv);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qp[j] = qr[j] * ex2(lr[j] - piv[j]);
+    }
+    float span[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) span[ks] = 0.f;
+    {
+        f32x4 p[4];
+        float kb[4][16];
+#pragma unroll
+        for (int Tb = 3; Tb >= 0; --Tb) {
+            if (Tb < I) {
+                float tr[16];
+                row16(&sm.tot[Tb][16 * g], tr);
+#pragma unroll
+                for (int ks = 0; ks < 16; ++ks) span[ks] += tr[ks];
+            }
+            float kr[16], lt[16];
+            row16(&sm.K[16 * Tb + c16][16 * g], kr);
+            row16(&sm.L[16 * Tb + c16][16 * g], lt);
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+                kb[Tb][ks] = kr[ks] * ex2(fminf(span[ks] + (piv[ks] - lt[ks]), kPivotBound));
+            p[Tb] = zero4();
+        }
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+            for (int Tb = 0; Tb < 4; ++Tb) p[Tb] = mma(qp[ks], kb[Tb][ks], p[Tb]);
+        const bool big = sm.big[I] != 0;
+        f32x4 pd = zero4();
+        if (big) {  // diagonal block element by element: sum_c q_ic k_tc 2^{l_ic - l_tc}, t <= i
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * g + e, t = 16 * I + c16;
+                float sacc = 0.f;
+                if (t <= i)
+                    for (int c = 0; c < kK; ++c) sacc += sm.Q[i][c] * sm.K[t][c] * ex2(sm.L[i][c] - sm.L[t][c]);
+                pd[e] = sacc;
+            }
+        }
+#pragma unroll
+        for (int Tb = 0; Tb < 4; ++Tb) {
+            const f32x4 pv4 = (big && Tb == I) ? pd : p[Tb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                P[(16 * I + 4 * g + e) * kC + 16 * Tb + c16] =
+                    (Tb < I || (Tb == I && 4 * g + e >= c16)) ? pv4[e] : 0.f;
+        }
+    }
+    // QD[i][c] = q_ic 2^{l_i - l_start} = qp 2^{piv + totals of blocks 0..I-1}
+#pragma unroll
+    for (int ks = 0; ks < 16; ks += 4)
+        *reinterpret_cast<float4 *>(&QD[(16 * I + c16) * kK + 16 * g + ks]) =
+            make_float4(qp[ks] * ex2(piv[ks] + span[ks]), qp[ks + 1] * ex2(piv[ks + 1] + span[ks + 1]),
+                        qp[ks + 2] * ex2(piv[ks + 2] + span[ks + 2]), qp[ks + 3] * ex2(piv[ks + 3] + span[ks + 3]));
+}
+
+// One workgroup per (slice, 16 value columns), the chunks in order; wave w
+// owns token rows 16w..16w+15 of O and feature rows 16w..16w+15 of the state.
+// Row operands (QD, P, KE rows) come straight from the record into registers
+// one chunk ahead; k-step j of lane group q takes index 16q + j.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks, const float *__restrict__ ws) {
+    __shared__ float sV[kC * 20], sS[kK * 20], sD[kK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int r = c16, q = g;
+    const int dk = a.dk, dv = a.dv, N = a.N;
+    const int bh = blockIdx.x, col0 = kNC * blockIdx.y;
+    const int ncol = min(kNC, dv - col0);
+    const T *V = static_cast<const T *>(a.V) + (size_t)bh * N * dv;
+    T *O = static_cast<T *>(a.O) + (size_t)bh * N * dv;
+
+    f32x4 S = zero4();
+    if (a.S_in) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 16 * w + 4 * g + e;
+            S[e] = (f < dk && c16 < ncol) ? a.S_in[((size_t)bh * dk + f) * dv + col0 + c16] : 0.f;
+        }
+    }
+    struct Pre {
+        float4 qd[4], p[4], ke[4];
+        float v[4], dec;
+    };
+    auto fetch = [&](Pre &f, int ch) {
+        if (ch >= n_chunks) return;
+        const int t0 = ch * kC, nt = min(kC, N - t0);
+        const float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats();
+        const float *Pr = rec + (16 * w + r) * kC + 16 * q;
+        const float *Qr = rec + kC * kK + (16 * w + r) * kK + 16 * q;
+        const float *Kr = rec + 2 * kC * kK + (16 * w + r) * kC + 16 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f.p[i] = *reinterpret_cast<const float4 *>(Pr + 4 * i);
+            f.qd[i] = *reinterpret_cast<const float4 *>(Qr + 4 * i);
+            f.ke[i] = *reinterpret_cast<const float4 *>(Kr + 4 * i);
+        }
+        if (tid < kK) f.dec = rec[3 * kC * kK + tid];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // values: token e / 16, column e % 16
+            const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
+            const bool in = t < nt && cc < ncol;
+            f.v[j] = in ? load_as_f32(V, (size_t)(t0 + t) * dv + col0 + cc) : 0.f;
+        }
+    };
+    Pre pre;
+    fetch(pre, 0);
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const int t0 = ch * kC, nt = min(kC, N - t0);
+        float pa[16], qa[16], ka[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pa[4 * i] = pre.p[i].x; pa[4 * i + 1] = pre.p[i].y; pa[4 * i + 2] = pre.p[i].z; pa[4 * i + 3] = pre.p[i].w;
+            qa[4 * i] = pre.qd[i].x; qa[4 * i + 1] = pre.qd[i].y; qa[4 * i + 2] = pre.qd[i].z; qa[4 * i + 3] = pre.qd[i].w;
+            ka[4 * i] = pre.ke[i].x; ka[4 * i + 1] = pre.ke[i].y; ka[4 * i + 2] = pre.ke[i].z; ka[4 * i + 3] = pre.ke[i].w;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + j * kThreads;
+            sV[(e / kNC) * 20 + e % kNC] = pre.v[j];
+        }
+        if (tid < kK) sD[tid] = pre.dec;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sS[(16 * w + 4 * g + e) * 20 + c16] = S[e];
+        lds_barrier();
+        fetch(pre, ch + 1);
+        // O = QD S_0 + P V for token rows 16w.. ; S = decay S_0 + KE V for feature rows 16w..
+        f32x4 o0 = zero4(), o1 = zero4(), u0 = zero4(), u1 = zero4();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float sb = sS[(16 * q + j) * 20 + c16], vb = sV[(16 * q + j) * 20 + c16];
+            if (j & 1) {
+                o1 = mma(qa[j], sb, o1);
+                o1 = mma(pa[j], vb, o1);
+                u1 = mma(ka[j], vb, u1);
+            } else {
+                o0 = mma(qa[j], sb, o0);
+                o0 = mma(pa[j], vb, o0);
+                u0 = mma(ka[j], vb, u0);
+            }
+        }
+        const f32x4 o = o0 + o1, u = u0 + u1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 16 * w + 4 * g + e;
+            S[e] = sD[f] * S[e] + u[e];
+            const int i = 16 * w + 4 * g + e;
+            if (i < nt && c16 < ncol) store_from_f32(O, (size_t)(t0 + i) * dv + col0 + c16, o[e]);
+        }
+        lds_barrier();  // this chunk's values, decay and state image read before the next staging
+    }
+    if (a.S_out) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 16 * w + 4 * g + e;
+            if (f < dk && c16 < ncol) a.S_out[((size_t)bh * dk + f) * dv + col0 + c16] = S[e];
+        }
+    }
+}
+
 }  // namespace
 
 bool gla_chunk_supported(const GatedArgs &a) { return a.dk <= kK && a.N >= kC; }
@@ -321,6 +569,27 @@ hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t st, KEven
     const dim3 grid((unsigned)a.BH, (unsigned)((a.dv + kNC - 1) / kNC)), block(kThreads);
     if (dtype == kF32) return launch_kernel_ev(k_gla_chunk<float>, grid, block, 0, st, ev, a);
     return launch_kernel_ev(k_gla_chunk<uint16_t>, grid, block, 0, st, ev, a);
+}
+
+size_t gla_chunk_ws_bytes(int BH, int N) {
+    const size_t n_chunks = (size_t)(N + kC - 1) / kC;
+    return sizeof(float) * (size_t)BH * n_chunks * gla_rec_floats();
+}
+
+hipError_t launch_gla_split(const GatedArgs &a, int dtype, float *ws, hipStream_t st, KEvents ev_prep,
+                            KEvents ev_scan) {
+    const int n_chunks = (a.N + kC - 1) / kC;
+    const dim3 gp((unsigned)((size_t)a.BH * n_chunks)), gs((unsigned)a.BH, (unsigned)((a.dv + kNC - 1) / kNC));
+    const dim3 blk(kThreads);
+    hipError_t e;
+    if (dtype == kF32) {
+        e = launch_kernel_ev(k_gla_prep<float>, gp, blk, 0, st, ev_prep, a, n_chunks, ws);
+        if (e != hipSuccess) return e;
+        return launch_kernel_ev(k_gla_scan<float>, gs, blk, 0, st, ev_scan, a, n_chunks, static_cast<const float *>(ws));
+    }
+    e = launch_kernel_ev(k_gla_prep<uint16_t>, gp, blk, 0, st, ev_prep, a, n_chunks, ws);
+    if (e != hipSuccess) return e;
+    return launch_kernel_ev(k_gla_scan<uint16_t>, gs, blk, 0, st, ev_scan, a, n_chunks, static_cast<const float *>(ws));
 }
 
 }  // namespace la

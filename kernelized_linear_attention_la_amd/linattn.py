@@ -28,7 +28,8 @@ EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspac
             "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
             "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step",
             "la_backward_workspace_bytes", "la_backward_causal_chunked", "la_forward_gla_recurrent",
-            "la_forward_delta_recurrent", "la_delta_workspace_bytes", "la_forward_delta_chunked")
+            "la_forward_delta_recurrent", "la_delta_workspace_bytes", "la_forward_delta_chunked",
+            "la_gla_workspace_bytes", "la_forward_gla_chunked")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 LA_BSLOT_FWD_SUMS, LA_BSLOT_FWD_SCAN, LA_BSLOT_DQ, LA_BSLOT_RSCAN, LA_BSLOT_DKV, LA_BSLOTS = 0, 1, 2, 3, 4, 5
 
@@ -104,6 +105,11 @@ def lib() -> ctypes.CDLL:
         L.la_forward_delta_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(LaKernelEvents)]
         L.la_forward_delta_chunked.restype = i
+        L.la_gla_workspace_bytes.argtypes = [P, i]
+        L.la_gla_workspace_bytes.restype = sz
+        L.la_forward_gla_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                             ctypes.POINTER(LaKernelEvents)]
+        L.la_forward_gla_chunked.restype = i
         _lib = L
     return _lib
 
@@ -462,4 +468,28 @@ def la_forward_delta_chunked(q, k, v, beta, alpha=None, S_in=None, S_out=None, o
                                         _ptr(beta), _ptr(S_in), _ptr(S_out), _ptr(out), _ptr(workspace), wsb,
                                         _stream(stream), None if events is None else ctypes.byref(events))
     _raise(st, "la_forward_delta_chunked")
+    return out
+
+
+def la_gla_workspace_bytes(q, v, chunk=64):
+    """Workspace bytes of la_forward_gla_chunked for q [B,H,N,d_k], v [B,H,N,d_v] (0: unsupported)."""
+    B, H, N, dk = q.shape
+    p = problem(B, H, N, dk, v.shape[3], _DT[q.dtype], LA_PHI_IDENTITY, 0, 0)
+    return lib().la_gla_workspace_bytes(ctypes.byref(p), int(chunk))
+
+
+def la_forward_gla_chunked(q, k, v, alpha, S_in=None, S_out=None, out=None, chunk=64, workspace=None, stream=None,
+                           events=None):
+    """GLA of la_forward_gla_recurrent in two launches (per-chunk products once, then the scan over chunks per
+    16 value columns; d_k <= 64).  workspace: a device tensor of at least la_gla_workspace_bytes bytes
+    (allocated here when None).  Returns O."""
+    p, S_in, S_out, out = _gated_common(q, k, v, S_in, S_out, out)
+    alpha = _gate(alpha, q.shape, q.device, "alpha")
+    if workspace is None:
+        workspace = torch.empty(max(la_gla_workspace_bytes(q, v, chunk), 16), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().la_forward_gla_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(S_in), _ptr(S_out), _ptr(out), _ptr(workspace), wsb, _stream(stream),
+                                      None if events is None else ctypes.byref(events))
+    _raise(st, "la_forward_gla_chunked")
     return out

@@ -218,6 +218,27 @@ def test_gated_validation():
                                         None, FAKE, None, None, FAKE, None) == 2
 
 
+def test_gla_chunked_validation():
+    L = linattn.lib()
+    pid = _p(phi=linattn.LA_PHI_IDENTITY)
+    need = L.la_gla_workspace_bytes(ctypes.byref(pid), 64)
+    assert need == 4 * pid.B * pid.H * (-(-pid.N // 64)) * (3 * 64 * 64 + 64)
+    assert L.la_gla_workspace_bytes(ctypes.byref(pid), 32) == 0
+    assert L.la_gla_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=65)), 64) == 0
+
+    def call(p=pid, chunk=64, Q=FAKE, al=FAKE, ws=FAKE, wsb=need):
+        return L.la_forward_gla_chunked(ctypes.byref(p), chunk, Q, FAKE, FAKE, al, None, None, FAKE, ws, wsb, None,
+                                        None)
+    assert call(chunk=128) == 4
+    assert call(p=_p(phi=linattn.LA_PHI_IDENTITY, d_k=65)) == 4
+    assert call(p=_p()) == 4
+    assert call(al=None) == 1
+    assert call(Q=MIS) == 5
+    assert call(al=ctypes.c_void_p(0x100002)) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=need - 1) == 6
+
+
 def test_delta_chunked_validation():
     """la_forward_delta_chunked validates before any launch: shape support,
     pointers, alignment and workspace size (no compute without a GPU)."""

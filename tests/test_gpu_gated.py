@@ -217,3 +217,67 @@ def test_delta_chunked_rejects_unsupported_shapes():
     with pytest.raises(RuntimeError):
         la.la_forward_delta_chunked(q, k, v, be)  # d_k = 32: the token-by-token entry point takes it
     assert la.la_delta_workspace_bytes(q, v) == 0
+
+
+# ---------------------------------------------------------------------------
+# GLA in two launches (la_forward_gla_chunked): per-chunk products, then the
+# scan over chunks per 16 value columns.
+# ---------------------------------------------------------------------------
+GLA_SPLIT_CASES = [
+    # (B, H, N, dk, dv, dtype, with S_in)
+    (1, 2, 256, 64, 64, "f32", False),
+    (2, 3, 100, 16, 8, "f32", True),       # narrow keys (padded channels), one partial column block
+    (1, 1, 1, 32, 32, "f32", True),        # one token
+    (1, 2, 77, 5, 3, "f32", True),         # odd widths
+    (2, 2, 130, 64, 40, "bf16", True),     # ragged chunk and column block
+    (4, 8, 2048, 64, 64, "bf16", True),    # the GLA workload's shape
+]
+
+
+@pytest.mark.parametrize("ci", range(len(GLA_SPLIT_CASES)),
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}dk{c[3]}dv{c[4]}{c[5]}{'S' if c[6] else ''}" for c in GLA_SPLIT_CASES])
+def test_gla_chunked_against_oracle(ci):
+    B, H, N, dk, dv, dtype, state = GLA_SPLIT_CASES[ci]
+    gi = inputs.gated_inputs(2600 + ci, B, H, N, dk, dv, dtype)
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    S_in = inputs.positive_state(2600 + ci, B, H, dk, dv, tokens=4)[0] if state else None
+    dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    S_out = torch.empty(B, H, dk, dv, device="cuda")
+    _say("gla split", GLA_SPLIT_CASES[ci])
+    O = la.la_forward_gla_chunked(q, k, v, dev(gi.alpha_ch), S_in=dev(S_in), S_out=S_out)
+    torch.cuda.synchronize()
+    ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch, S_in=S_in)
+    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    _say("gla split", f"O {eo:.2e} S {es:.2e}")
+    tol = tol_for(dtype)
+    assert eo < tol and es < tol, (eo, es)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gla_chunked_extreme_gates_and_handoff(dtype):
+    """Zero, tiny, mid and near-one gates (the element-wise diagonal blocks)
+    through the two-launch form, also as two calls with S_out aliasing S_in."""
+    B, H, N, dk, dv = 1, 2, 300, 64, 40
+    gi = inputs.gated_inputs(2700, B, H, N, dk, dv, dtype)
+    al = _extreme_gates(2700, B, H, N, dk)
+    S_in = inputs.positive_state(2700, B, H, dk, dv, tokens=4)[0]
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    alt = torch.from_numpy(al).cuda()
+    ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, al, S_in=S_in)
+    tol = tol_for(dtype)
+    S_out = torch.empty(B, H, dk, dv, device="cuda")
+    O = la.la_forward_gla_chunked(q, k, v, alt, S_in=torch.from_numpy(S_in).cuda(), S_out=S_out)
+    torch.cuda.synchronize()
+    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    _say("gla split extreme", dtype, f"O {eo:.2e} S {es:.2e}")
+    assert np.isfinite(to_f64(O)).all()
+    assert eo < tol and es < tol, (eo, es)
+    M = 130
+    S = torch.from_numpy(S_in).cuda()
+    c = lambda x, a, b: x[:, :, a:b].contiguous()  # noqa: E731
+    O1 = la.la_forward_gla_chunked(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(alt, 0, M), S_in=S, S_out=S)
+    O2 = la.la_forward_gla_chunked(c(q, M, N), c(k, M, N), c(v, M, N), c(alt, M, N), S_in=S, S_out=S)
+    torch.cuda.synchronize()
+    eo, es = slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref), state_rel_err(to_f64(S), Sref)
+    _say("gla split handoff", dtype, f"O {eo:.2e} S {es:.2e}")
+    assert eo < tol and es < tol, (eo, es)
