@@ -91,17 +91,20 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
     const char *vb = reinterpret_cast<const char *>(V + tok0 * dv);
     const int qk_bytes = L * kXK * (int)sizeof(T), v_bytes = L * dv * (int)sizeof(T);
     uint4 xq[QP], xk[QP], xv[VP];
+    // unconditional loads from clamped offsets (a load under a branch would
+    // wait for every outstanding load); pieces past the end become zero on use
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
         const int off = 16 * (tid + i * kXT);
-        xq[i] = off < qk_bytes ? *reinterpret_cast<const uint4 *>(qb + off) : make_uint4(0, 0, 0, 0);
-        xk[i] = off < qk_bytes ? *reinterpret_cast<const uint4 *>(kb + off) : make_uint4(0, 0, 0, 0);
+        xq[i] = *reinterpret_cast<const uint4 *>(qb + (off < qk_bytes ? off : 0));
+        xk[i] = *reinterpret_cast<const uint4 *>(kb + (off < qk_bytes ? off : 0));
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
         const int off = 16 * (tid + i * kXT);
-        xv[i] = off < v_bytes ? *reinterpret_cast<const uint4 *>(vb + off) : make_uint4(0, 0, 0, 0);
+        xv[i] = *reinterpret_cast<const uint4 *>(vb + (off < v_bytes ? off : 0));
     }
+    const uint4 zero = make_uint4(0, 0, 0, 0);
     // piece -> fp32 values at element e0 of a row-major [rows][width] block
     auto unpack = [&](const uint4 &x, float (&o)[EP]) {
         if constexpr (sizeof(T) == 2) {
@@ -134,10 +137,11 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
     for (int i = 0; i < QP; ++i) {
         const int e0 = EP * (tid + i * kXT), t = e0 / kXK, f = e0 % kXK;
         float o[EP];
-        unpack(xq[i], o);
+        const bool live = 16 * (tid + i * kXT) < qk_bytes;
+        unpack(live ? xq[i] : zero, o);
 #pragma unroll
         for (int e = 0; e < EP; ++e) sQ[t * kXR + f + e] = o[e];
-        unpack(xk[i], o);
+        unpack(live ? xk[i] : zero, o);
 #pragma unroll
         for (int e = 0; e < EP; ++e) sK[t * kXR + f + e] = o[e];
     }
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
         if (e0 < kXC * dv) {
             const int t = e0 / dv, j = e0 % dv;
             float o[EP];
-            unpack(xv[i], o);
+            unpack(16 * (tid + i * kXT) < v_bytes ? xv[i] : zero, o);
 #pragma unroll
             for (int e = 0; e < EP; ++e) sX[t * RX + kXK + j + e] = sb[t] * o[e];
         }
@@ -263,8 +267,12 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
         float4 w[4], p[4], ut, gg;
         uint4 q[QR], k[KP];
     };
-    auto fetch = [&](Pre &f, int c) {
-        if (c >= n_chunks) return;
+    // Every load is unconditional (offsets clamped to valid data; the zero
+    // selects happen where the values are used): a load under a branch makes
+    // the compiler wait for all outstanding loads right after it, which would
+    // turn the prefetch into a synchronous read.
+    auto fetch = [&](Pre &f, int c_) {
+        const int c = min(c_, n_chunks - 1);  // past the end: a harmless re-read of the last chunk
         const int t0 = c * kXC, L = min(kXC, N - t0);
         const float *rec = ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv);
         const float *Wr = rec + (16 * w + r) * kXK + 16 * q;          // W[16w + r][16q ..]
@@ -275,18 +283,17 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
             f.p[i] = *reinterpret_cast<const float4 *>(Pr + 16 * i);
         }
         f.ut = *reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)(tid >> 2) * dv + col0 + 4 * (tid & 3));
-        if (tid < 32) f.gg = reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)kXC * dv)[tid];
+        f.gg = reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)kXC * dv)[tid & 31];
         const bool qlive = 16 * w + r < L;
-        const T *qrow = Q + ((size_t)bh * N + t0 + 16 * w + r) * kXK + 16 * q;
+        const T *qrow = Q + ((size_t)bh * N + t0 + (qlive ? 16 * w + r : 0)) * kXK + 16 * q;
 #pragma unroll
-        for (int i = 0; i < QR; ++i)
-            f.q[i] = qlive ? reinterpret_cast<const uint4 *>(qrow)[i] : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < QR; ++i) f.q[i] = reinterpret_cast<const uint4 *>(qrow)[i];
         const char *kb = reinterpret_cast<const char *>(K + ((size_t)bh * N + t0) * kXK);
         const int bytes = L * kXK * (int)sizeof(T);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int off = 16 * (tid + i * kXT);
-            f.k[i] = off < bytes ? *reinterpret_cast<const uint4 *>(kb + off) : make_uint4(0, 0, 0, 0);
+            f.k[i] = *reinterpret_cast<const uint4 *>(kb + (off < bytes ? off : 0));
         }
     };
     auto unpack = [&](const uint4 &x, float *o) {
@@ -309,6 +316,10 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
         const int t0 = c * kXC, L = min(kXC, N - t0);
         const size_t tok0 = (size_t)bh * N + t0;
         // operands of chunk c in registers; K, Ut, gates and the state image into LDS
+        // (query rows and key pieces past the end read as zero)
+        const uint4 zero = make_uint4(0, 0, 0, 0);
+        const bool qlive = 16 * w + r < L;
+        const int kbytes = L * kXK * (int)sizeof(T);
         float wa[16], qa[16], pa[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -316,12 +327,12 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
             pa[4 * i] = pre.p[i].x; pa[4 * i + 1] = pre.p[i].y; pa[4 * i + 2] = pre.p[i].z; pa[4 * i + 3] = pre.p[i].w;
         }
 #pragma unroll
-        for (int i = 0; i < QR; ++i) unpack(pre.q[i], &qa[EP * i]);
+        for (int i = 0; i < QR; ++i) unpack(qlive ? pre.q[i] : zero, &qa[EP * i]);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int e0 = EP * (tid + i * kXT), t = e0 / kXK, f = e0 % kXK;
             float o[EP];
-            unpack(pre.k[i], o);
+            unpack(16 * (tid + i * kXT) < kbytes ? pre.k[i] : zero, o);
 #pragma unroll
             for (int e = 0; e < EP; ++e) sK[t * kXR + f + e] = o[e];
         }

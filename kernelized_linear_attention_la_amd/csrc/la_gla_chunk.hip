@@ -354,17 +354,28 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
     const int sc = tid & 63, sq = tid >> 6;
     float kf[16], lf[16];
     {
+        // all loads first, unconditional (clamped indices), then the selects
+        T rq[16], rk[16];
+        float ra[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = 16 * sq + j;
+            const bool in = t < nt && sc < dk;
+            const size_t gi = (size_t)(t0 + (in ? t : 0)) * dk + (in ? sc : 0);
+            rq[j] = Q[gi];
+            rk[j] = K[gi];
+            ra[j] = Al[gi];
+        }
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int t = 16 * sq + j;
             const bool in = t < nt && sc < dk;
-            const size_t gi = (size_t)(t0 + t) * dk + sc;
-            sm.Q[t][sc] = in ? as_f32(Q[gi]) : 0.f;
-            kf[j] = in ? as_f32(K[gi]) : 0.f;
+            sm.Q[t][sc] = in ? as_f32(rq[j]) : 0.f;
+            kf[j] = in ? as_f32(rk[j]) : 0.f;
             sm.K[t][sc] = kf[j];
             // a gate of 0 counts as 2^-115 (its factor vanishes in fp32)
-            const float al = in ? Al[gi] : 1.f;
+            const float al = in ? ra[j] : 1.f;
             acc += al > 0.f ? lg2(al) : -115.f;
             lf[j] = acc;
             sm.L[t][sc] = acc;
@@ -481,12 +492,17 @@ __global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks
             S[e] = (f < dk && c16 < ncol) ? a.S_in[((size_t)bh * dk + f) * dv + col0 + c16] : 0.f;
         }
     }
+    // Every load is unconditional (indices clamped to valid elements; the
+    // selects happen where the values are used): a load under a branch makes
+    // the compiler wait for all outstanding loads right after it, which would
+    // turn the prefetch into a synchronous read.
     struct Pre {
         float4 qd[4], p[4], ke[4];
-        float v[4], dec;
+        T v[4];
+        float dec;
     };
-    auto fetch = [&](Pre &f, int ch) {
-        if (ch >= n_chunks) return;
+    auto fetch = [&](Pre &f, int ch_) {
+        const int ch = min(ch_, n_chunks - 1);  // past the end: a harmless re-read of the last chunk
         const int t0 = ch * kC, nt = min(kC, N - t0);
         const float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats();
         const float *Pr = rec + (16 * w + r) * kC + 16 * q;
@@ -498,13 +514,17 @@ __global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks
             f.qd[i] = *reinterpret_cast<const float4 *>(Qr + 4 * i);
             f.ke[i] = *reinterpret_cast<const float4 *>(Kr + 4 * i);
         }
-        if (tid < kK) f.dec = rec[3 * kC * kK + tid];
+        f.dec = rec[3 * kC * kK + (tid & (kK - 1))];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // values: token e / 16, column e % 16
             const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
             const bool in = t < nt && cc < ncol;
-            f.v[j] = in ? load_as_f32(V, (size_t)(t0 + t) * dv + col0 + cc) : 0.f;
+            f.v[j] = V[(size_t)(t0 + (in ? t : 0)) * dv + col0 + (in ? cc : 0)];
         }
+    };
+    auto as_f32 = [](T x) {
+        if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
+        else return static_cast<float>(x);
     };
     Pre pre;
     fetch(pre, 0);
@@ -519,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = tid + j * kThreads;
-            sV[(e / kNC) * 20 + e % kNC] = pre.v[j];
+            const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
+            sV[t * 20 + cc] = (t < nt && cc < ncol) ? as_f32(pre.v[j]) : 0.f;
         }
         if (tid < kK) sD[tid] = pre.dec;
 #pragma unroll
