@@ -249,7 +249,11 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int ncb = dv / 16;
-    const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+    // slice fastest: the column blocks of a slice are B*H workgroups apart, so
+    // (B*H a multiple of 8) they run on one XCD and share its L2 copy of the
+    // slice's chunk records
+    const int BH = gridDim.x / ncb;
+    const int bh = blockIdx.x % BH, cb = blockIdx.x / BH;
     const int col0 = 16 * cb;
     const int r = c16, q = g;  // A-operand row and k group of this lane
 
