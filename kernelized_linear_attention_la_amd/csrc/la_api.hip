@@ -49,8 +49,9 @@ la_status check_problem(const la_problem *p) {
     return LA_OK;
 }
 
-static_assert(LA_PHI_ELU1 == kElu1 && LA_PHI_FAVOR == kFavor && LA_PHI_IDENTITY == kIdentity &&
-                  LA_PHI_DPFP == kDpfp && LA_PHI_TRIG == kTrig && LA_PHI_COSFORMER == kCosformer,
+static_assert((int)LA_PHI_ELU1 == (int)kElu1 && (int)LA_PHI_FAVOR == (int)kFavor &&
+                  (int)LA_PHI_IDENTITY == (int)kIdentity && (int)LA_PHI_DPFP == (int)kDpfp &&
+                  (int)LA_PHI_TRIG == (int)kTrig && (int)LA_PHI_COSFORMER == (int)kCosformer,
               "feature-map codes");
 
 Shape make_shape(const la_problem *p) {

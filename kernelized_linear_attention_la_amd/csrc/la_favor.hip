@@ -42,7 +42,6 @@ constexpr int kFW = 8;                 // waves
 constexpr int kFT = 64 * kFW;          // threads
 constexpr int kFNJ = kFD / 16 + 1;     // value column blocks incl. the normaliser block
 constexpr int kFKBF = kFM / 32;        // 32-feature k-blocks
-constexpr int kFFB = kFM / 16;         // 16-row feature blocks of the state
 constexpr int kFRK = kFM + 8;          // phi row stride (16-row 128-bit reads conflict free)
 constexpr int kFRV = kFD + 16 + 8;     // V_aug row stride
 constexpr int kFRX = kFD + 8;          // raw row stride
