@@ -760,8 +760,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget; 0 skips it")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the hot path shards over (batch, head) slices and sequence segments; see DESIGN.md)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard over "
+              f"(batch, head) slices, or over sequence segments with one exchange of segment states)",
               file=sys.stderr)
         sys.exit(2)
     from kernelized_linear_attention_la_amd import inputs

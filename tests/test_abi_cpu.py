@@ -287,3 +287,14 @@ def test_feature_map_parameters_validation():
     for p in (pd(map_param=1), pt(m=16, W_ptr=0x1000), pc(map_param=100, pos0=7)):
         assert linattn.la_workspace_bytes(p, 64) > 0
         assert linattn.la_backward_workspace_bytes(p, 64) == 0  # no backward for these maps
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus N > 1 exits non-zero with a message, before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
