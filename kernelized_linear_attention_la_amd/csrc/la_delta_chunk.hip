@@ -60,6 +60,19 @@ __device__ __forceinline__ f32x4d mm4(FA a, FB b, f32x4d acc, int lane) {
     return acc;
 }
 
+// One output element through a buffer store: an offset past the resource's
+// range drops the store in hardware, so partial tiles issue the same
+// unconditional stores as full ones (a store under a branch would leave the
+// compiler unable to count the stores in flight before the next wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);  // raw buffer, gfx9 word 3
+}
+template <typename T>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float v) {
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // Per-chunk workspace record (floats): W [64][64], P [64][64], Ut [64][dv],
 // g [64], g_C / g [64].
 __host__ __device__ inline size_t delta_rec_floats(int dv) { return 2 * kXC * kXK + (size_t)kXC * dv + 2 * kXC; }
@@ -357,14 +370,16 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
 
         // U = Ut - W S0 and Q S0 for token rows 16w..16w+15 (k = 16q + j); two
         // accumulators per product halve the dependent chains
+        float sb[16];  // B operands read from LDS all at once, then the products
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sb[j] = sS[(16 * q + j) * 20 + c16];
         f32x4d ws0 = zero4d(), o = zero4d(), ws1 = zero4d(), o1 = zero4d();
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-            const float b0 = sS[(16 * q + j) * 20 + c16], b1 = sS[(16 * q + j + 1) * 20 + c16];
-            ws0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j], b0, ws0, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], b0, o, 0, 0, 0);
-            ws1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j + 1], b1, ws1, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j + 1], b1, o1, 0, 0, 0);
+            ws0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j], sb[j], ws0, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], sb[j], o, 0, 0, 0);
+            ws1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j + 1], sb[j + 1], ws1, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j + 1], sb[j + 1], o1, 0, 0, 0);
         }
         ws0 += ws1;
         o += o1;
@@ -398,10 +413,11 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
         const float gC = sg[kXC - 1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[e] = gC * S[e] + ku[e];
+        const auto ro = out_rsrc(O + tok0 * dv, L * dv * (int)sizeof(T));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * w + 4 * g + e;
-            if (t < L) store_from_f32(O, (tok0 + t) * dv + col0 + c16, o[e]);
+            store_elem<T>(ro, t < L ? (t * dv + col0 + c16) * (int)sizeof(T) : L * dv * (int)sizeof(T), o[e]);
         }
         sync_lds();  // every read of this chunk's tiles done before the next staging
     }

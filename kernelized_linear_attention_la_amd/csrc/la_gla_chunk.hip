@@ -467,6 +467,19 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
                         qp[ks + 2] * ex2(piv[ks + 2] + span[ks + 2]), qp[ks + 3] * ex2(piv[ks + 3] + span[ks + 3]));
 }
 
+// One output element through a buffer store: an offset past the resource's
+// range drops the store in hardware, so partial tiles issue the same
+// unconditional stores as full ones (a store under a branch would leave the
+// compiler unable to count the stores in flight before the next wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);  // raw buffer, gfx9 word 3
+}
+template <typename T>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float v) {
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // One workgroup per (slice, 16 value columns), the chunks in order; wave w
 // owns token rows 16w..16w+15 of O and feature rows 16w..16w+15 of the state.
 // Row operands (QD, P, KE rows) come straight from the record into registers
@@ -548,27 +561,35 @@ __global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks
         lds_barrier();
         fetch(pre, ch + 1);
         // O = QD S_0 + P V for token rows 16w.. ; S = decay S_0 + KE V for feature rows 16w..
+        // (the B operands read from LDS all at once, then the products)
+        float sb[16], vb[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            sb[j] = sS[(16 * q + j) * 20 + c16];
+            vb[j] = sV[(16 * q + j) * 20 + c16];
+        }
         f32x4 o0 = zero4(), o1 = zero4(), u0 = zero4(), u1 = zero4();
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float sb = sS[(16 * q + j) * 20 + c16], vb = sV[(16 * q + j) * 20 + c16];
             if (j & 1) {
-                o1 = mma(qa[j], sb, o1);
-                o1 = mma(pa[j], vb, o1);
-                u1 = mma(ka[j], vb, u1);
+                o1 = mma(qa[j], sb[j], o1);
+                o1 = mma(pa[j], vb[j], o1);
+                u1 = mma(ka[j], vb[j], u1);
             } else {
-                o0 = mma(qa[j], sb, o0);
-                o0 = mma(pa[j], vb, o0);
-                u0 = mma(ka[j], vb, u0);
+                o0 = mma(qa[j], sb[j], o0);
+                o0 = mma(pa[j], vb[j], o0);
+                u0 = mma(ka[j], vb[j], u0);
             }
         }
         const f32x4 o = o0 + o1, u = u0 + u1;
+        const auto ro = out_rsrc(O + (size_t)t0 * dv, nt * dv * (int)sizeof(T));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int f = 16 * w + 4 * g + e;
             S[e] = sD[f] * S[e] + u[e];
             const int i = 16 * w + 4 * g + e;
-            if (i < nt && c16 < ncol) store_from_f32(O, (size_t)(t0 + i) * dv + col0 + c16, o[e]);
+            const int off = (i < nt && c16 < ncol) ? (i * dv + col0 + c16) * (int)sizeof(T) : nt * dv * (int)sizeof(T);
+            store_elem<T>(ro, off, o[e]);
         }
         lds_barrier();  // this chunk's values, decay and state image read before the next staging
     }
