@@ -281,3 +281,46 @@ def test_gla_chunked_extreme_gates_and_handoff(dtype):
     eo, es = slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref), state_rel_err(to_f64(S), Sref)
     _say("gla split handoff", dtype, f"O {eo:.2e} S {es:.2e}")
     assert eo < tol and es < tol, (eo, es)
+
+
+def test_two_launch_forms_graph_replay():
+    """The two-launch GLA and delta-rule calls captured in a HIP graph: every
+    replay (with eager calls on the same workspaces in between) reproduces the
+    eager results bit for bit (the workspace records are rewritten each call)."""
+    B, H, N, dk, dv = 2, 3, 200, 64, 48
+    gi = inputs.gated_inputs(2800, B, H, N, dk, dv, "bf16")
+    q, k, v = to_device(gi.Q), to_device(gi.K), to_device(gi.V)
+    a_ch = torch.from_numpy(np.ascontiguousarray(gi.alpha_ch)).cuda()
+    al, be = torch.from_numpy(gi.alpha).cuda(), torch.from_numpy(gi.beta).cuda()
+    S_in = torch.from_numpy(inputs.positive_state(2800, B, H, dk, dv, tokens=4)[0]).cuda()
+    ws_g = torch.empty(la.la_gla_workspace_bytes(q, v), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(la.la_delta_workspace_bytes(q, v), dtype=torch.uint8, device="cuda")
+    Sg, Sd = torch.empty_like(S_in), torch.empty_like(S_in)
+    Og = la.la_forward_gla_chunked(q, k, v, a_ch, S_in=S_in, S_out=Sg, workspace=ws_g)
+    Od = la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_in=S_in, S_out=Sd, workspace=ws_d)
+    torch.cuda.synchronize()
+    Og0, Od0, Sg0, Sd0 = Og.clone(), Od.clone(), Sg.clone(), Sd.clone()
+    ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch, S_in=S_in.cpu().numpy())
+    assert slice_rel_err(to_f64(Og0), ref) < tol_for("bf16")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):  # warm up on the capture stream
+        la.la_forward_gla_chunked(q, k, v, a_ch, S_in=S_in, S_out=Sg, out=Og, workspace=ws_g)
+        la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_in=S_in, S_out=Sd, out=Od, workspace=ws_d)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        la.la_forward_gla_chunked(q, k, v, a_ch, S_in=S_in, S_out=Sg, out=Og, workspace=ws_g)
+        la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_in=S_in, S_out=Sd, out=Od, workspace=ws_d)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        _say("two-launch graph replay", rep)
+        Og.zero_(), Od.zero_(), Sg.zero_(), Sd.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Og, Og0) and torch.equal(Sg, Sg0), rep
+        assert torch.equal(Od, Od0) and torch.equal(Sd, Sd0), rep
+        # eager calls on the same workspaces between replays
+        la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_in=S_in, workspace=ws_d)
+        la.la_forward_gla_chunked(q, k, v, a_ch, workspace=ws_g)
+        torch.cuda.synchronize()
