@@ -255,7 +255,8 @@ def kernel_symbol(wl, slot):
         (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64) or
         (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64) or
         (wl.phi == "dpfp" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and
-         wl.map_param == 1))
+         wl.map_param == 1) or
+        (wl.phi == "trig" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 64 and wl.chunk == 64))
     if mfma:
         # the forward workloads all split into several segments per slice: the
         # matrix-core path runs them in one single-pass launch (the library's
@@ -263,7 +264,7 @@ def kernel_symbol(wl, slot):
         # whole-segment kernel at d 64 with segments of at most 256 tokens,
         # else the chunk loop, mode 4 when a segment's keys and values stay in
         # LDS (d 64, 64-token chunks, at most 4 chunks per segment), else mode 3
-        phi_id = {"elu1": 0, "favor": 1, "identity": 2, "dpfp": 3, "cosformer": 5}[wl.phi]
+        phi_id = {"elu1": 0, "favor": 1, "identity": 2, "dpfp": 3, "trig": 4, "cosformer": 5}[wl.phi]
         n_chunks = -(-wl.N // wl.chunk)
         P = min(-(-256 // (wl.B * wl.H)), n_chunks)
         seg = -(-n_chunks // P)

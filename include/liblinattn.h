@@ -69,8 +69,9 @@ typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
  *   LA_PHI_COSFORMER  [ReLU(x) cos(pi p / 2M); ReLU(x) sin(pi p / 2M)] for the token at
  *                     position p = pos0 + (index within the call), M = map_param ("Story of
  *                     Attention Part 5", section 3); d' = 2 d_k
- * d' <= 256 for every map.  DPFP, TRIG and cosFormer run on the fp32-arithmetic
- * kernels for either storage type.
+ * d' <= 256 for every map.  With bf16 storage, d_k = d_v = 64 and 64-token chunks,
+ * one-shift DPFP, cosFormer and TRIG with m = 64 run on the matrix cores; the
+ * other shapes of these maps run on the fp32-arithmetic kernels.
  */
 typedef enum {
     LA_PHI_ELU1 = 0,

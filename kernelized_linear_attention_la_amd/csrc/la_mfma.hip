@@ -45,11 +45,14 @@ struct Cfg {
     static constexpr bool CF = PHI == kCosformer;
     // DPFP with one shift ("Linear Attention", feature-map table): r = ReLU([x, -x]), r_j r_{j+1}
     static constexpr bool DPF = PHI == kDpfp;
-    static constexpr bool XR = F || DPF;         // raw K, Q rows staged in LDS, the map formed there
+    // cos/sin projections ("Linear Attention", feature-map table): [cos(W x); sin(W x)], m = d_k rows of W
+    static constexpr bool TR = PHI == kTrig;
+    static constexpr bool PR = F || TR;          // the map goes through a projection X W^T on the matrix cores
+    static constexpr bool XR = PR || DPF;        // raw K, Q rows staged in LDS, the map formed there
     static constexpr int NW = C / 16;            // waves
     static constexpr int THREADS = 64 * NW;
-    static constexpr int DP = F ? 256 : ((CF || DPF) ? 2 * DK : DK);  // feature dimension
-    static constexpr int M = F ? 256 : 0;
+    static constexpr int DP = F ? 256 : ((CF || DPF || TR) ? 2 * DK : DK);  // feature dimension
+    static constexpr int M = F ? 256 : (TR ? DK : 0);  // rows of W
     // Retention ("Story of Attention Part 5", sections 4 and 6): raw q and k,
     // decay per head, no normaliser.
     static constexpr bool RET = PHI == kIdentity;
@@ -78,9 +81,9 @@ struct Smem {
     uint16_t V[NKS][C * G::RV];         // V_aug, token-major
     uint4 STB[G::NJ][G::KBF][64];       // bf16 S_aug: B operand of phi(Q) S
     uint16_t O[G::NW][16 * G::RO];      // per-wave output staging for 16-byte stores
-    uint16_t XK[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP: raw K_c, token-major
-    uint16_t XQ[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP: raw Q_c, token-major
-    uint16_t QP[F ? C * G::RK : 1];     // FAVOR+: phi(Q_c), token-major
+    uint16_t XK[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP, cos/sin: raw K_c, token-major
+    uint16_t XQ[G::XR ? C * G::RX : 1];  // FAVOR+, DPFP, cos/sin: raw Q_c, token-major
+    uint16_t QP[G::PR ? C * G::RK : 1];  // FAVOR+, cos/sin: phi(Q_c), token-major
 };
 
 // Store a 16x16 fp32 state tile (lane l holds S[16fb + 4g + e][16nb + l%16])
@@ -91,6 +94,16 @@ __device__ __forceinline__ void put_state_block(uint4 (*STB)[G::KBF][64], int fb
     uint2 v = pack4(s[0], s[1], s[2], s[3]);
     const int x = 16 * (fb & 1) + 4 * g;  // feature slot inside the 32-feature k-block
     reinterpret_cast<uint2 *>(&STB[nb][fb >> 1][c + 16 * (x >> 3)])[(x >> 2) & 1] = v;
+}
+
+// cos u and sin u through the hardware's sine and cosine, which take their
+// argument in turns: u / 2pi reduced to [-1/2, 1/2] by the period first.
+__device__ __forceinline__ void turn_cos_sin(float u, float &c, float &s) {
+    constexpr float kInvTwoPi = 0.159154943091895336f;
+    float r = u * kInvTwoPi;
+    r -= rintf(r);
+    c = __builtin_amdgcn_cosf(r);
+    s = __builtin_amdgcn_sinf(r);
 }
 
 template <int DK, int DV, int C, int PHI, int MODE>
@@ -138,15 +151,16 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // the inputs are exact in bf16, so x . w_r = x . hi_r + x . lo_r is
     // accurate to about 2^-16 relative, where a single bf16 W would shift
     // every exponent of the feature map by ~2^-9 |w_r| |x|.
-    constexpr int FWB = G::F ? 4 : 1;  // 16-feature blocks of W per wave
-    static_assert(!G::F || NW * 64 == G::M, "FAVOR+: one wave per 64 features");
-    Op8 wreg[FWB][G::F ? G::KBD : 1][2];
-    if constexpr (G::F) {
+    // The cos/sin map takes the same registers with 16 rows of W per wave.
+    constexpr int FWB = G::F ? 4 : 1;  // 16-row blocks of W per wave
+    static_assert(!G::PR || NW * 16 * FWB == G::M, "one wave per 64 (FAVOR+) or 16 (cos/sin) rows of W");
+    Op8 wreg[FWB][G::PR ? G::KBD : 1][2];
+    if constexpr (G::PR) {
 #pragma unroll
         for (int fbl = 0; fbl < FWB; ++fbl)
 #pragma unroll
             for (int kb = 0; kb < G::KBD; ++kb) {
-                const float *src = a.sh.W + (size_t)(64 * w + 16 * fbl + c16) * DK + 32 * kb + 8 * g;
+                const float *src = a.sh.W + (size_t)(16 * FWB * w + 16 * fbl + c16) * DK + 32 * kb + 8 * g;
                 const float4 w0 = *reinterpret_cast<const float4 *>(src);
                 const float4 w1 = *reinterpret_cast<const float4 *>(src + 4);
                 const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -350,15 +364,17 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         block_sync_lds();
         fetch(p, step + DEPTH);
 
-        // ---------------- FAVOR+: feature maps through projections on the matrix cores.
-        // Wave w forms U = W_w X^T for its 64 features and all C tokens: the
-        // A operands (W) are in registers, the B operands are the raw rows
-        // (lane l: token 16tb + l%16, columns 32kb + 8(l/16)..+7), and
-        // accumulator lane (4g+e, c16) of tile (fbl, tb) holds feature
-        // 64w + 16fbl + 4g + e of token 16tb + c16.  phi = exp(u - |x|^2/2)/sqrt(m)
-        // goes to LDS token-major, in natural feature order.
-        if constexpr (G::F) {
-            static_assert(C == 64, "FAVOR+: four 16-token blocks per chunk");
+        // ---------------- FAVOR+ and cos/sin: feature maps through projections
+        // on the matrix cores.  Wave w forms U = W_w X^T for its 64 (FAVOR+)
+        // or 16 (cos/sin) rows of W and all C tokens: the A operands (W) are
+        // in registers, the B operands are the raw rows (lane l: token
+        // 16tb + l%16, columns 32kb + 8(l/16)..+7), and accumulator lane
+        // (4g+e, c16) of tile (fbl, tb) holds row r = 16 FWB w + 16fbl + 4g + e
+        // of token 16tb + c16.  FAVOR+: phi_r = exp(u - |x|^2/2)/sqrt(m) at
+        // feature r; cos/sin: cos u at feature r, sin u at feature m + r.
+        // phi goes to LDS token-major, in natural feature order.
+        if constexpr (G::PR) {
+            static_assert(C == 64, "projected maps: four 16-token blocks per chunk");
             auto project = [&](const uint16_t *xr, uint16_t *dst, bool mask_tail) {
                 Op8 xb[4][G::KBD];
                 float shift[4];
@@ -368,14 +384,18 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                     for (int kb = 0; kb < G::KBD; ++kb) {
                         xb[tb][kb].u = *reinterpret_cast<const uint4 *>(&xr[(16 * tb + c16) * G::RX + 32 * kb + 8 * g]);
+                        if constexpr (G::F) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v0 = lo_bf16(xb[tb][kb].u32[e]), v1 = hi_bf16(xb[tb][kb].u32[e]);
-                            sq += v0 * v0 + v1 * v1;
+                            for (int e = 0; e < 4; ++e) {
+                                const float v0 = lo_bf16(xb[tb][kb].u32[e]), v1 = hi_bf16(xb[tb][kb].u32[e]);
+                                sq += v0 * v0 + v1 * v1;
+                            }
                         }
                     }
-                    sq += __shfl_xor(sq, 16, 64);
-                    sq += __shfl_xor(sq, 32, 64);
+                    if constexpr (G::F) {
+                        sq += __shfl_xor(sq, 16, 64);
+                        sq += __shfl_xor(sq, 32, 64);
+                    }
                     shift[tb] = 0.5f * sq;
                 }
 #pragma unroll
@@ -388,10 +408,21 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
                             for (int part = 0; part < 2; ++part) u = mfma(wreg[fbl][kb][part], xb[tb][kb], u);
                         const int t = 16 * tb + c16;
-                        uint2 v = pack4(fast_exp(u[0] - shift[tb]) * inv_sqrt_m, fast_exp(u[1] - shift[tb]) * inv_sqrt_m,
-                                        fast_exp(u[2] - shift[tb]) * inv_sqrt_m, fast_exp(u[3] - shift[tb]) * inv_sqrt_m);
-                        if (mask_tail && t0 + t >= N) v = make_uint2(0, 0);  // keys past the end: phi = 0
-                        *reinterpret_cast<uint2 *>(&dst[t * RK + 64 * w + 16 * fbl + 4 * g]) = v;
+                        const bool dead = mask_tail && t0 + t >= N;  // keys past the end: phi = 0
+                        if constexpr (G::F) {
+                            uint2 v = pack4(fast_exp(u[0] - shift[tb]) * inv_sqrt_m, fast_exp(u[1] - shift[tb]) * inv_sqrt_m,
+                                            fast_exp(u[2] - shift[tb]) * inv_sqrt_m, fast_exp(u[3] - shift[tb]) * inv_sqrt_m);
+                            if (dead) v = make_uint2(0, 0);
+                            *reinterpret_cast<uint2 *>(&dst[t * RK + 64 * w + 16 * fbl + 4 * g]) = v;
+                        } else {
+                            float cv[4], sv[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) turn_cos_sin(u[e], cv[e], sv[e]);
+                            uint2 vc = pack4(cv[0], cv[1], cv[2], cv[3]), vs = pack4(sv[0], sv[1], sv[2], sv[3]);
+                            if (dead) vc = vs = make_uint2(0, 0);
+                            *reinterpret_cast<uint2 *>(&dst[t * RK + 16 * w + 4 * g]) = vc;
+                            *reinterpret_cast<uint2 *>(&dst[t * RK + G::M + 16 * w + 4 * g]) = vs;
+                        }
                     }
             };
             if constexpr (NEED_K) project(sm.XK, sm.K[ks], true);
@@ -922,6 +953,7 @@ bool mfma_supported(const Shape &sh, int chunk) {
     if (sh.phi == kFavor) return sh.dk == 64 && sh.dv == 64 && sh.m == 256 && chunk == 64;
     if (sh.phi == kCosformer) return sh.dk == 64 && sh.dv == 64 && chunk == 64;
     if (sh.phi == kDpfp) return sh.dk == 64 && sh.dv == 64 && sh.param == 1 && chunk == 64;
+    if (sh.phi == kTrig) return sh.dk == 64 && sh.dv == 64 && sh.m == 64 && chunk == 64;
     return false;  // the other maps run on the fp32-arithmetic kernels
 }
 
@@ -932,6 +964,7 @@ hipError_t launch_mfma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     if (s.phi == kFavor) return launch_variant<64, 64, 64, kFavor>(a, st, ev);
     if (s.phi == kCosformer) return launch_variant<64, 64, 64, kCosformer>(a, st, ev);
     if (s.phi == kDpfp) return launch_variant<64, 64, 64, kDpfp>(a, st, ev);
+    if (s.phi == kTrig) return launch_variant<64, 64, 64, kTrig>(a, st, ev);
     if (s.phi == kIdentity) {
         if (s.dk == 64)
             return C == 64 ? launch_variant<64, 64, 64, kIdentity>(a, st, ev)

@@ -70,6 +70,10 @@ CASES = [
     # the matrix-core DPFP kernel (one shift, bf16, d = 64, 64-token chunks)
     (4, 4, 1000, 64, "bf16", "dpfp", 0, 1, 64),
     (4, 8, 2048, 64, "bf16", "dpfp", 0, 1, 64),
+    # the matrix-core cos/sin kernel (bf16, d = 64, m = 64, 64-token chunks)
+    (1, 1, 100, 64, "bf16", "trig", 64, 0, 64),
+    (4, 4, 1000, 64, "bf16", "trig", 64, 0, 64),
+    (4, 8, 2048, 64, "bf16", "trig", 64, 0, 64),
 ]
 
 
@@ -174,3 +178,32 @@ def test_cosformer_matrix_core_handoff_with_position_offset():
         assert e < 2e-2
         assert state_rel_err(to_f64(S), Sref) < 2e-2
         assert z_rel_err(to_f64(z), zref) < 2e-2
+
+
+@pytest.mark.parametrize("phi,param,m", [("dpfp", 1, 0), ("trig", 0, 64), ("cosformer", 777, 0)])
+def test_matrix_core_maps_continue_from_a_state(phi, param, m):
+    """The matrix-core map kernels (bf16, d = 64, 64-token chunks) started from
+    a carried (S, z): two chunked calls, the second at pos0 = the first's
+    length, == the oracle's recurrence over the whole sequence."""
+    B, H, N1, N2, d = 2, 3, 333, 444, 64
+    fi, W = _inputs(60, B, H, N1 + N2, d, "bf16", phi, m)
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    Wt = torch.from_numpy(W).cuda() if W is not None else None
+    p = la._problem_of(q, v, phi, Wt, param)
+    dp = la.la_feature_dim(p)
+    S = torch.zeros(B, H, dp, d, device="cuda")
+    z = torch.zeros(B, H, dp, device="cuda")
+    part = lambda x, a, b: x[:, :, a:b].contiguous()  # noqa: E731
+    O1 = la.la_forward_causal_chunked(part(q, 0, N1), part(k, 0, N1), part(v, 0, N1), 64, phi=phi, W=Wt,
+                                      S_out=S, z_out=z, map_param=param)
+    O2 = la.la_forward_causal_chunked(part(q, N1, N1 + N2), part(k, N1, N1 + N2), part(v, N1, N1 + N2), 64,
+                                      phi=phi, W=Wt, S_in=S, z_in=z, S_out=S, z_out=z, map_param=param, pos0=N1)
+    torch.cuda.synchronize()
+    oracle.set_map(param, 0)
+    ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, W)
+    got = np.concatenate([to_f64(O1), to_f64(O2)], axis=2)
+    tol = tol_for("bf16")
+    e, es = row_rel_err(got, ref), state_rel_err(to_f64(S), Sref)
+    ez = state_rel_err(to_f64(z)[..., None], zref[..., None])
+    _say(phi, f"continued O {e:.2e} S {es:.2e} z {ez:.2e}")
+    assert e < tol and es < tol and ez < tol
