@@ -53,14 +53,23 @@ def forward_alg_bytes(wl):
     return tok * (2 * wl.dk + 2 * wl.dv) * e + state
 
 
+def tile_chunk(wl):
+    """Chunk length the library tiles a forward with: FAVOR+ on the matrix cores
+    (bf16, d 64, m 256) runs a 128-token request on its 64-token tiling."""
+    if (wl.phi == "favor" and wl.dtype == "bf16" and not wl.retention and wl.dk == 64 and wl.dv == 64 and
+            wl.m == 256 and wl.chunk == 128):
+        return 64
+    return wl.chunk
+
+
 def forward_alg_flops(wl):
     """Algorithmic flops of one causal forward (causal half of the intra-chunk products).
 
     per token: state update 2 d' d_v, inter-chunk read 2 d' d_v (+2 d' for z),
     intra-chunk scores and values (C+1)(d' + d_v) on average, normalisation d_v,
-    FAVOR+ projection 2 d_k m for q and for k.
+    FAVOR+ projection 2 d_k m for q and for k.  C is the chunk length tiled.
     """
-    C, dp, dv, dk = wl.chunk, wl.dprime, wl.dv, wl.dk
+    C, dp, dv, dk = tile_chunk(wl), wl.dprime, wl.dv, wl.dk
     if wl.retention:  # no normaliser: no z read, no division
         per = 4 * dp * dv + (C + 1) * (dp + dv)
     else:
@@ -252,7 +261,8 @@ def kernel_symbol(wl, slot):
     mfma = wl.dtype == "bf16" and (
         (wl.phi == "elu1" and not wl.retention and square) or
         (wl.phi == "identity" and wl.retention and square) or
-        (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and wl.chunk == 64) or
+        (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and
+         tile_chunk(wl) == 64) or
         (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64) or
         (wl.phi == "dpfp" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and
          wl.map_param == 1) or
@@ -265,7 +275,7 @@ def kernel_symbol(wl, slot):
         # else the chunk loop, mode 4 when a segment's keys and values stay in
         # LDS (d 64, 64-token chunks, at most 4 chunks per segment), else mode 3
         phi_id = {"elu1": 0, "favor": 1, "identity": 2, "dpfp": 3, "trig": 4, "cosformer": 5}[wl.phi]
-        n_chunks = -(-wl.N // wl.chunk)
+        n_chunks = -(-wl.N // tile_chunk(wl))
         P = min(-(-256 // (wl.B * wl.H)), n_chunks)
         seg = -(-n_chunks // P)
         if P > 1 and seg * wl.chunk <= 256 and wl.dk == 64 and wl.dv == 64 and wl.phi in ("elu1", "identity"):
@@ -798,6 +808,8 @@ def main():
             cpu = run_cpu_baseline(wl, fi, args.cpu_seconds)
     config = {"workload": wl.name, "phi": wl.phi, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,
               "chunk": wl.chunk}
+    if tile_chunk(wl) != wl.chunk:
+        config["tile_chunk"] = tile_chunk(wl)
     if wl.m:
         config["m"] = wl.m
     if wl.retention:

@@ -101,7 +101,17 @@ Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int mi
 
 int generic_columns(const Shape &sh) { return (sh.dv + 31) / 32; }
 
-Segments causal_plan(const Shape &sh, int chunk, bool *use_mfma) {
+// FAVOR+ on the matrix cores tiles 64 tokens: at m = 256 a 128-token tile of
+// phi(K) and phi(Q) alone would take 132 KiB of the 160 KiB of LDS.  The
+// chunkwise form gives the same function for every chunk length ("Linear
+// Attention", chunkwise parallel form), so a 128-token request runs on the
+// 64-token tiling rather than on the fp32-arithmetic kernels.
+int tile_chunk(const Shape &sh, int chunk) {
+    return sh.phi == kFavor && chunk == 128 && mfma_supported(sh, 64) ? 64 : chunk;
+}
+
+Segments causal_plan(const Shape &sh, int chunk_req, bool *use_mfma) {
+    const int chunk = tile_chunk(sh, chunk_req);
     const bool mf = mfma_supported(sh, chunk);
     if (use_mfma) *use_mfma = mf;
 #ifdef LA_SEGMENTS_OVERRIDE

@@ -226,6 +226,9 @@ WORKLOADS = {
                  1024, 128, 128, 1.0 / math.sqrt(128), 64, decode_steps=64),
         Workload("favor_bf16_b2h8n8192d64_m256_c64", 5, "favor", "bf16", 2, 8, 8192, 64, 64,
                  64 ** -0.25, 64, m=256),
+        # the same at a 128-token chunk request (run on the 64-token tiling)
+        Workload("favor_bf16_b2h8n8192d64_m256_c128", 5, "favor", "bf16", 2, 8, 8192, 64, 64,
+                 64 ** -0.25, 128, m=256),
         # retention (decayed, unnormalised; raw q and k): the shapes of the
         # normalised workloads above, one decay per head
         Workload("ret_f32_b1h2n256d64_c64", 6, "identity", "f32", 1, 2, 256, 64, 64, 1.0 / math.sqrt(64), 64,

@@ -132,6 +132,10 @@ CASES = [
     # d = 64 segments too long to keep in LDS (nine chunks each)
     (4, 8, 4100, 64, 64, "bf16", "elu1", 0, 64),
     (4, 16, 740, 64, 64, "bf16", "favor", 256, 64),
+    # FAVOR+ asked for 128-token chunks (run on the 64-token matrix-core tiling):
+    # one chunk, a ragged tail, and several segments
+    (1, 1, 100, 64, 64, "bf16", "favor", 256, 128),
+    (2, 8, 1500, 64, 64, "bf16", "favor", 256, 128),
 ]
 
 
@@ -250,7 +254,7 @@ def _gather(x, samp):
 
 
 @pytest.mark.parametrize("name", ["elu1_bf16_b4h8n2048d64_c64", "elu1_bf16_b2h16n16384d128_c128",
-                                  "favor_bf16_b2h8n8192d64_m256_c64"])
+                                  "favor_bf16_b2h8n8192d64_m256_c64", "favor_bf16_b2h8n8192d64_m256_c128"])
 def test_full_size_forward_sampled(name):
     wl = inputs.WORKLOADS[name]
     _say("full", name, "generating")
