@@ -89,9 +89,11 @@ def backward_alg_flops(wl, kernel):
         later chunks 2 d' d_v, in-chunk scores and sums (C+1)(2 d' + d_v + a),
         carry 2 d' a;
     FAVOR+ adds the projection 2 d_k m per recomputed row (q in the first pass,
-    k in both) and its Jacobian 2 d_k m + 2 m per row.
+    k in both) and its Jacobian 2 d_k m + 2 m per row.  C is the chunk length
+    the kernels tile: the request on the matrix cores, at most 16 tokens on the
+    fp32-arithmetic kernels.
     """
-    C, dp, dv, dk = wl.chunk, wl.dprime, wl.dv, wl.dk
+    C, dp, dv, dk = (wl.chunk if backward_on_mfma(wl) else min(wl.chunk, 16)), wl.dprime, wl.dv, wl.dk
     a = dv + 1
     if kernel == "dq":
         per = 8 * dp * a + 2 * (C + 1) * (dp + a)

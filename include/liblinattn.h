@@ -252,7 +252,9 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  *   p            as for the forward; LA_PHI_IDENTITY is refused.  Supported
  *                while d' * (d_v + 1) <= 16640 (d' = 128 with d_v <= 128, or
  *                d' = 256 with d_v <= 64); larger: LA_ERR_UNSUPPORTED.
- *   chunk        16, 32, 64 or 128: tokens per chunk of the chunked form.
+ *   chunk        16, 32, 64 or 128: tokens per chunk of the chunked form.  The
+ *                gradients do not depend on it; the fp32-arithmetic kernels tile
+ *                at most 16 tokens whatever is asked.
  *   Q, K, V      forward inputs; dO [B,H,N,d_v] the gradient of the loss with
  *                respect to O (all of dtype p->dtype).
  *   S_in, z_in   the forward's starting state, or both NULL (zero).

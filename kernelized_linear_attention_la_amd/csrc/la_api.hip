@@ -476,10 +476,19 @@ struct BwdWs {
     size_t s_off, z_off, u_off, g_off, total;
 };
 
+// The fp32-arithmetic backward walks a chunk in 16-row tiles and pays, per
+// token, for the pairwise products with the chunk's earlier key tiles and for
+// reloading them; the chunkwise form gives the same gradients for every chunk
+// length, so it runs on chunks of at most this many tokens.
+#ifndef LA_BWD_FP32_CHUNK
+#define LA_BWD_FP32_CHUNK 16
+#endif
+constexpr int kBwdFp32Chunk = LA_BWD_FP32_CHUNK;
+
 Segments backward_plan(const Shape &sh, int chunk) {
     // matrix-core kernels: one workgroup per CU; fp32 kernels: several
-    return backward_mfma_supported(sh, chunk) ? plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups)
-                                              : plan_segments(sh, chunk, 1, 1, kTargetWorkgroups);
+    if (backward_mfma_supported(sh, chunk)) return plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups);
+    return plan_segments(sh, chunk < kBwdFp32Chunk ? chunk : kBwdFp32Chunk, 1, 1, kTargetWorkgroups);
 }
 
 BwdWs bwd_ws(const Shape &sh, const Segments &g) {
@@ -541,14 +550,26 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
     if (ev)
         for (int i = 0; i < LA_BSLOTS; ++i) ev->launched[i] = 0;
 
-    // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan
+    // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan.
+    // Behind the fp32 kernels the sums run on the matrix-core state pass when
+    // the segments are whole chunks of a length it takes (same boundaries, same P).
+    const bool mf = backward_mfma_supported(sh, chunk);
+    Segments gs = g;
+    bool sums_mf = mf;
+    if (!mf)
+        for (int c2 : {128, 64})
+            if (!sums_mf && (g.seg_chunks * g.chunk) % c2 == 0 && mfma_supported(sh, c2)) {
+                gs.chunk = c2;
+                gs.n_chunks = (sh.N + c2 - 1) / c2;
+                gs.seg_chunks = g.seg_chunks * g.chunk / c2;
+                sums_mf = true;
+            }
     FwdArgs a{};
-    a.sh = sh; a.sg = g; a.mode = kModeState;
+    a.sh = sh; a.sg = gs; a.mode = kModeState;
     a.Q = Q; a.K = K; a.V = V; a.O = nullptr;
     a.st.S_dst = wsS; a.st.z_dst = wsz;
     a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
-    const bool mf = backward_mfma_supported(sh, chunk);
-    if (launch_fwd(mf, a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
+    if (launch_fwd(sums_mf, a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
     if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, nullptr, nullptr, false, hs, slot(LA_BSLOT_FWD_SCAN)) !=
         hipSuccess)
         return LA_ERR_DEVICE;
