@@ -54,10 +54,14 @@ def forward_alg_bytes(wl):
 
 
 def tile_chunk(wl):
-    """Chunk length the library tiles a forward with: FAVOR+ on the matrix cores
-    (bf16, d 64, m 256) runs a 128-token request on its 64-token tiling."""
-    if (wl.phi == "favor" and wl.dtype == "bf16" and not wl.retention and wl.dk == 64 and wl.dv == 64 and
-            wl.m == 256 and wl.chunk == 128):
+    """Chunk length the library tiles a forward with: the maps that run on the
+    matrix cores at 64-token chunks only (FAVOR+ with m 256, one-shift DPFP,
+    cos/sin with m 64, cosFormer; bf16, d 64) run a 128-token request on that
+    64-token tiling."""
+    if wl.dtype != "bf16" or wl.retention or wl.dk != 64 or wl.dv != 64 or wl.chunk != 128:
+        return wl.chunk
+    if ((wl.phi == "favor" and wl.m == 256) or (wl.phi == "dpfp" and wl.map_param == 1) or
+            (wl.phi == "trig" and wl.m == 64) or wl.phi == "cosformer"):
         return 64
     return wl.chunk
 
@@ -265,10 +269,10 @@ def kernel_symbol(wl, slot):
         (wl.phi == "identity" and wl.retention and square) or
         (wl.phi == "favor" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 256 and
          tile_chunk(wl) == 64) or
-        (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64) or
-        (wl.phi == "dpfp" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and
+        (wl.phi == "cosformer" and not wl.retention and wl.dk == 64 and wl.dv == 64 and tile_chunk(wl) == 64) or
+        (wl.phi == "dpfp" and not wl.retention and wl.dk == 64 and wl.dv == 64 and tile_chunk(wl) == 64 and
          wl.map_param == 1) or
-        (wl.phi == "trig" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 64 and wl.chunk == 64))
+        (wl.phi == "trig" and not wl.retention and wl.dk == 64 and wl.dv == 64 and wl.m == 64 and tile_chunk(wl) == 64))
     if mfma:
         # the forward workloads all split into several segments per slice: the
         # matrix-core path runs them in one single-pass launch (the library's
@@ -285,7 +289,7 @@ def kernel_symbol(wl, slot):
         if P > 1 and wl.phi == "favor":
             return "k_favor"  # eight waves per workgroup, two per SIMD
         res = seg <= 4 and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and wl.phi in ("elu1", "identity")
-        return f"k_mfma<{wl.dk}, {wl.dv}, {wl.chunk}, {phi_id}, {4 if res else 3}>"
+        return f"k_mfma<{wl.dk}, {wl.dv}, {tile_chunk(wl)}, {phi_id}, {4 if res else 3}>"
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"
 
 

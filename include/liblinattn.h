@@ -134,8 +134,9 @@ la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K
  * the state then absorbs phi(K_c)^T V_c, phi(K_c)^T 1.
  *   chunk        in {16, 32, 64, 128}; it changes speed, never the result
  *                beyond floating-point rounding.  N need not be a multiple.
- *                FAVOR+ with bf16 storage, d_k = d_v = 64 and m = 256 runs a
- *                128-token request on its 64-token matrix-core tiling.
+ *                The maps that run on the matrix cores at 64-token chunks only
+ *                (FAVOR+, DPFP, TRIG, cosFormer with bf16 storage and d_k = d_v
+ *                = 64) run a 128-token request on that 64-token tiling.
  *   S_in, z_in   initial state (both NULL = zero state), [B,H,d',d_v] / [B,H,d'].
  *   S_out, z_out final state after token N (both NULL = not exported).  May be
  *                the same buffers as S_in, z_in (updated in place).

@@ -101,13 +101,16 @@ Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int mi
 
 int generic_columns(const Shape &sh) { return (sh.dv + 31) / 32; }
 
-// FAVOR+ on the matrix cores tiles 64 tokens: at m = 256 a 128-token tile of
-// phi(K) and phi(Q) alone would take 132 KiB of the 160 KiB of LDS.  The
-// chunkwise form gives the same function for every chunk length ("Linear
-// Attention", chunkwise parallel form), so a 128-token request runs on the
-// 64-token tiling rather than on the fp32-arithmetic kernels.
+// The projected and widened maps on the matrix cores (FAVOR+, DPFP, cos/sin,
+// cosFormer) tile 64 tokens: at m = 256 a 128-token tile of phi(K) and
+// phi(Q) alone would take 132 KiB of the 160 KiB of LDS, and the d' = 128
+// maps' 128-token tiles with their raw rows about 180 KiB.  The chunkwise form
+// gives the same function for every chunk length ("Linear Attention",
+// chunkwise parallel form), so a 128-token request runs on the 64-token tiling
+// rather than on the fp32-arithmetic kernels.
 int tile_chunk(const Shape &sh, int chunk) {
-    return sh.phi == kFavor && chunk == 128 && mfma_supported(sh, 64) ? 64 : chunk;
+    const bool tiled64 = sh.phi == kFavor || sh.phi == kDpfp || sh.phi == kTrig || sh.phi == kCosformer;
+    return tiled64 && chunk == 128 && mfma_supported(sh, 64) ? 64 : chunk;
 }
 
 Segments causal_plan(const Shape &sh, int chunk_req, bool *use_mfma) {

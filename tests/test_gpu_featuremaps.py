@@ -74,6 +74,11 @@ CASES = [
     (1, 1, 100, 64, "bf16", "trig", 64, 0, 64),
     (4, 4, 1000, 64, "bf16", "trig", 64, 0, 64),
     (4, 8, 2048, 64, "bf16", "trig", 64, 0, 64),
+    # 128-token requests of the d64 maps (run on the 64-token matrix-core tiling)
+    (2, 3, 900, 64, "bf16", "dpfp", 0, 1, 128),
+    (2, 3, 900, 64, "bf16", "trig", 64, 0, 128),
+    # bf16 cosFormer on the fp32-arithmetic kernels (32-token chunks)
+    (2, 2, 700, 64, "bf16", "cosformer", 0, 700, 32),
 ]
 
 
