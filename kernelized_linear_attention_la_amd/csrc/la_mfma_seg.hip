@@ -51,6 +51,9 @@ struct SegSmem {
     f32x4 PB[kStrips][kSD / 16][64];        // prefix strips, accumulator order (value blocks)
     float PZ[kStrips][16];                  // prefix strips, normaliser column
     f32x4 OWN[kStrips][NJ][64];             // last segment: its own sums, accumulator order
+    // retention: lambda^x for x < kSL, then the key weights lambda^(L-1-t)
+    // of the segment's tokens (0 past its end)
+    alignas(16) float DW[RET ? 2 * kSL : 4];
 };
 
 // 16x16 fp32 tile (lane l: rows 16fb + 4g + e, column 16nb + l%16) into the
@@ -130,6 +133,15 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
             *reinterpret_cast<uint4 *>(&sm.V[t * kSRV + kSD + 8 * half]) = make_uint4(half == 0 ? 0x3f80u : 0u, 0, 0, 0);
         }
     }
+    if constexpr (RET) {  // the decay tables: one exponential per thread instead of one per use
+        if (tid < kSL) {
+            sm.DW[tid] = dpow((float)tid);
+        } else if (tid < 2 * kSL) {
+            const int t = tid - kSL;
+            sm.DW[tid] = t < L ? dpow((float)(L - 1 - t)) : 0.f;
+        }
+    }
+    static_assert(kSThreads >= 2 * kSL, "one table entry per thread");
     // the query rows go out once the keys and values (which the hand-off
     // waits for) have arrived
 #pragma unroll
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int d = 16 * (qb - jb) + c16 - 4 * g - e;
-                            p[h][e] *= d >= 0 ? dpow((float)d) : 0.f;
+                            p[h][e] *= d >= 0 ? sm.DW[max(d, 0)] : 0.f;  // d <= 255
                         }
                     }
                 }
@@ -201,14 +213,13 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
 #pragma unroll
         for (int kt = 0; kt < kSL / 32; ++kt) {
             Op8 ka = token_operand<kSRK>(sm.K, kt, 16 * fb, lane);
-            if constexpr (RET) {
-                auto kw = [&](int sl) {
-                    const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
-                    return t < L ? dpow((float)(L - 1 - t)) : 0.f;
-                };
+            if constexpr (RET) {  // key weight of slot sl: token 32kt + 16(sl/4) + 4g + sl%4
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.DW[kSL + 32 * kt + 4 * g]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.DW[kSL + 32 * kt + 16 + 4 * g]);
+                const float kw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw(2 * j), hi_bf16(ka.u32[j]) * kw(2 * j + 1));
+                    ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw[2 * j], hi_bf16(ka.u32[j]) * kw[2 * j + 1]);
             }
 #pragma unroll
             for (int nb = 0; nb < NJ; ++nb) own[nb] = mfma(ka, token_operand<kSRV>(sm.V, kt, 16 * nb, lane), own[nb]);
