@@ -135,3 +135,17 @@ def test_backward_long_context_sampled_slices():
     got, ref = _run(3, 2, 16, 16384, 128, 128, "bf16", "elu1", 0, 128, False,
                     slices=(np.array([[0], [1]]), np.array([[3], [14]])))
     _check(got, ref, "bf16", "B2H16N16384 sampled")
+
+
+def test_backward_fp32_kernels_behind_matrix_core_sums():
+    # bf16 problems on the fp32-arithmetic backward whose segments are whole
+    # 64-token chunks, so the forward sums in front of it run on the matrix
+    # cores: ELU+1 d64 asking for 128-token chunks, with a carried state, and
+    # FAVOR+ at the B2 H8 N8192 shape (two slices recomputed by the oracle)
+    _say("B4 H8 N2048 d64 bf16 chunk 128, state")
+    got, ref = _run(6, 4, 8, 2048, 64, 64, "bf16", "elu1", 0, 128, True)
+    _check(got, ref, "bf16", "ELU+1 d64 chunk 128")
+    _say("B2 H8 N8192 d64 bf16 FAVOR+ m256 (slices (0,2), (1,7))")
+    got, ref = _run(7, 2, 8, 8192, 64, 64, "bf16", "favor", 256, 64, False,
+                    slices=(np.array([[0], [1]]), np.array([[2], [7]])))
+    _check(got, ref, "bf16", "FAVOR+ B2H8N8192 sampled")
