@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 5
+#define LA_ABI_VERSION 6
 
 typedef enum {
     LA_OK = 0,
@@ -108,11 +108,27 @@ int la_feature_dim(const la_problem *p);
  * only on the problem shape and chunk.  Returns 0 for an invalid problem.
  * Fill a workspace with zeros before the first call that uses it; every call
  * leaves it ready for the next one (whatever the shape).  Its first 256 bytes
- * hold the hand-off state of the single-pass causal path: keep them between
- * calls, and give calls that may run at the same time (on any streams)
- * workspaces of their own.
+ * hold the hand-off state of the single-pass causal path (launch counter,
+ * done count, error word): keep them between calls, and give calls that may
+ * run at the same time (on any streams) workspaces of their own.  Every other
+ * call that takes a workspace (non-causal forward, backward, chunkwise GLA
+ * and delta rule) leaves those 256 bytes untouched, so one buffer of the
+ * largest size asked may serve all of them in turn on one stream.
  */
 size_t la_workspace_bytes(const la_problem *p, int chunk);
+
+/*
+ * Error word of a workspace (its first 256 bytes, see la_workspace_bytes):
+ * enqueues on `stream` a copy of the word into *err (caller-owned device
+ * memory, 4-byte aligned) and, when clear != 0, resets it to 0.  The word is
+ * 0 until a single-pass causal launch on this workspace had a hand-off wait
+ * expire (each wait is bounded at about 10 s); it then reads 1 and stays 1
+ * until cleared, and the outputs of the launch that set it hold NaN where
+ * the lost hand-off mattered.  ws_bytes must be at least 256.
+ * Errors: LA_ERR_NULL (ws or err NULL), LA_ERR_ALIGN (ws not 16-byte or err
+ * not 4-byte aligned), LA_ERR_WORKSPACE (ws_bytes < 256), LA_ERR_DEVICE.
+ */
+la_status la_workspace_error(void *ws, size_t ws_bytes, unsigned int *err, int clear, void *stream);
 
 /*
  * Non-causal forward ("Story of Attention Part 5", 1a, matrix form):
@@ -266,7 +282,8 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  *   dS_in, dz_in gradient with respect to S_in, z_in, or both NULL (not
  *                written).
  *   ws           device workspace of at least la_backward_workspace_bytes()
- *                bytes (no initial contents required).
+ *                bytes (no initial contents required; its first 256 bytes
+ *                are left untouched, so a forward's workspace may be reused).
  *   ev           per-kernel timing hook (slots below), or NULL.
  * Six kernels are enqueued: the forward's per-segment sums and their prefix
  * scan, then the forward-direction pass (recomputes the outputs, writes dQ and
@@ -339,7 +356,8 @@ la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const v
  *          128, else LA_ERR_UNSUPPORTED (the token-by-token entry point takes
  *          every shape);
  *   ws     device workspace of at least la_delta_workspace_bytes(p, chunk)
- *          bytes (16-byte aligned; no initial contents needed; one record per
+ *          bytes (16-byte aligned; no initial contents needed; past its
+ *          first 256 bytes, which are left untouched, one record per
  *          (b, h, chunk): W, P [64 x 64], Ut [64 x d_v], gate products), owned
  *          by the caller; else LA_ERR_WORKSPACE;
  *   ev     optional timing hook: slot LA_KSLOT_STATE brackets the per-chunk
@@ -358,7 +376,8 @@ size_t la_delta_workspace_bytes(const la_problem *p, int chunk);
  * la_forward_gla_recurrent, plus: chunk must be 64 and p->d_k <= 64 (else
  * LA_ERR_UNSUPPORTED); any N >= 1; ws: device workspace of at least
  * la_gla_workspace_bytes(p, chunk) bytes (16-byte aligned, no initial
- * contents; one record of 3 x 64 x 64 + 64 floats per (b, h, chunk)), else
+ * contents; its first 256 bytes are left untouched, then one record of
+ * 3 x 64 x 64 + 64 floats per (b, h, chunk)), else
  * LA_ERR_WORKSPACE; ev: optional timing hook (LA_KSLOT_STATE: the per-chunk
  * launch, LA_KSLOT_CHUNK: the scan).  S_out may alias S_in.
  */

@@ -117,17 +117,6 @@ Segments causal_plan(const Shape &sh, int chunk_req, bool *use_mfma) {
     const int chunk = tile_chunk(sh, chunk_req);
     const bool mf = mfma_supported(sh, chunk);
     if (use_mfma) *use_mfma = mf;
-#ifdef LA_SEGMENTS_OVERRIDE
-    if (mf) {  // tuning builds only: fixed segment count per slice
-        Segments g;
-        g.chunk = chunk;
-        g.n_chunks = (sh.N + chunk - 1) / chunk;
-        int want = LA_SEGMENTS_OVERRIDE < g.n_chunks ? LA_SEGMENTS_OVERRIDE : g.n_chunks;
-        g.seg_chunks = (g.n_chunks + want - 1) / want;
-        g.P = (g.n_chunks + g.seg_chunks - 1) / g.seg_chunks;
-        return g;
-    }
-#endif
     return mf ? plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups) : plan_segments(sh, chunk, generic_columns(sh), 1);
 }
 
@@ -257,6 +246,17 @@ LA_API size_t la_workspace_bytes(const la_problem *p, int chunk) {
     sh.ret = 1;  // retention calls plan their own segments
     const size_t r = causal_ws(sh, chunk);
     return r > need ? r : need;
+}
+
+LA_API la_status la_workspace_error(void *ws, size_t ws_bytes, unsigned int *err, int clear, void *stream) {
+    if (!ws || !err) return LA_ERR_NULL;
+    if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(err) & 3u) != 0) return LA_ERR_ALIGN;
+    if (ws_bytes < kCtlBytes) return LA_ERR_WORKSPACE;
+    static_assert(sizeof(unsigned int) == sizeof(uint32_t), "error word");
+    return launch_ws_error(static_cast<uint32_t *>(ws), reinterpret_cast<uint32_t *>(err), clear != 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LA_OK
+               : LA_ERR_DEVICE;
 }
 
 LA_API la_status la_forward_noncausal(const la_problem *p, const void *Q, const void *K, const void *V, void *O,
@@ -474,7 +474,10 @@ LA_API la_status la_retention_decode_step(const la_problem *p, const float *gamm
 namespace la {
 namespace {
 
-// [forward prefix S][forward prefix z][per-segment sums psi^T G_aug][G_aug per token]
+// [control block, untouched][forward prefix S][forward prefix z][per-segment
+// sums psi^T G_aug][G_aug per token].  The first kCtlBytes are the forward's
+// single-pass hand-off state: a buffer shared between forward and backward
+// calls keeps it intact.
 struct BwdWs {
     size_t s_off, z_off, u_off, g_off, total;
 };
@@ -483,10 +486,7 @@ struct BwdWs {
 // token, for the pairwise products with the chunk's earlier key tiles and for
 // reloading them; the chunkwise form gives the same gradients for every chunk
 // length, so it runs on chunks of at most this many tokens.
-#ifndef LA_BWD_FP32_CHUNK
-#define LA_BWD_FP32_CHUNK 16
-#endif
-constexpr int kBwdFp32Chunk = LA_BWD_FP32_CHUNK;
+constexpr int kBwdFp32Chunk = 16;
 
 Segments backward_plan(const Shape &sh, int chunk) {
     // matrix-core kernels: one workgroup per CU; fp32 kernels: several
@@ -497,7 +497,7 @@ Segments backward_plan(const Shape &sh, int chunk) {
 BwdWs bwd_ws(const Shape &sh, const Segments &g) {
     const size_t bh = (size_t)sh.BH, dp = (size_t)sh.dp, dv = (size_t)sh.dv;
     BwdWs w;
-    w.s_off = 0;
+    w.s_off = kCtlBytes;
     w.z_off = w.s_off + round_up(sizeof(float) * bh * g.P * dp * dv, kAlign);
     w.u_off = w.z_off + round_up(sizeof(float) * bh * g.P * dp, kAlign);
     w.g_off = w.u_off + round_up(sizeof(float) * bh * g.P * dp * (dv + 1), kAlign);
@@ -649,7 +649,7 @@ LA_API la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, 
 
 LA_API size_t la_gla_workspace_bytes(const la_problem *p, int chunk) {
     if (la::check_problem(p) != LA_OK || p->phi != LA_PHI_IDENTITY || p->d_k > 64 || chunk != 64) return 0;
-    return la::gla_chunk_ws_bytes(p->B * p->H, p->N);
+    return la::kCtlBytes + la::gla_chunk_ws_bytes(p->B * p->H, p->N);
 }
 
 LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
@@ -664,7 +664,7 @@ LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const vo
     for (const void *q : ptrs)
         if (!aligned16(q)) return LA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(alpha) & 3u) return LA_ERR_ALIGN;
-    if (!ws || ws_bytes < gla_chunk_ws_bytes(p->B * p->H, p->N)) return LA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < kCtlBytes + gla_chunk_ws_bytes(p->B * p->H, p->N)) return LA_ERR_WORKSPACE;
     if (ev)
         for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
     GatedArgs a;
@@ -672,7 +672,9 @@ LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const vo
     a.Q = Q; a.K = K; a.V = V; a.O = O;
     a.alpha = alpha; a.beta = nullptr;
     a.S_in = S_in; a.S_out = S_out;
-    return launch_gla_split(a, p->dtype == LA_BF16 ? kBF16 : kF32, static_cast<float *>(ws),
+    // the records start past the control block (kept for the forward's hand-off)
+    return launch_gla_split(a, p->dtype == LA_BF16 ? kBF16 : kF32,
+                            reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes),
                             static_cast<hipStream_t>(stream), slot_events(ev, LA_KSLOT_STATE),
                             slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
                ? LA_OK
@@ -683,7 +685,7 @@ LA_API size_t la_delta_workspace_bytes(const la_problem *p, int chunk) {
     if (la::check_problem(p) != LA_OK || p->phi != LA_PHI_IDENTITY ||
         !la::delta_chunk_supported(p->d_k, p->d_v, chunk))
         return 0;
-    return la::delta_chunk_ws_bytes(p->B * p->H, p->N, p->d_v);
+    return la::kCtlBytes + la::delta_chunk_ws_bytes(p->B * p->H, p->N, p->d_v);
 }
 
 LA_API la_status la_forward_delta_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
@@ -699,7 +701,7 @@ LA_API la_status la_forward_delta_chunked(const la_problem *p, int chunk, const 
     for (const void *q : ptrs)
         if (!aligned16(q)) return LA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u)) return LA_ERR_ALIGN;
-    if (!ws || ws_bytes < delta_chunk_ws_bytes(p->B * p->H, p->N, p->d_v)) return LA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < kCtlBytes + delta_chunk_ws_bytes(p->B * p->H, p->N, p->d_v)) return LA_ERR_WORKSPACE;
     if (ev)
         for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
     GatedArgs a;
@@ -707,7 +709,9 @@ LA_API la_status la_forward_delta_chunked(const la_problem *p, int chunk, const 
     a.Q = Q; a.K = K; a.V = V; a.O = O;
     a.alpha = alpha; a.beta = beta;
     a.S_in = S_in; a.S_out = S_out;
-    return launch_delta_chunk(a, p->dtype == LA_BF16 ? kBF16 : kF32, static_cast<float *>(ws),
+    // the records start past the control block (kept for the forward's hand-off)
+    return launch_delta_chunk(a, p->dtype == LA_BF16 ? kBF16 : kF32,
+                              reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes),
                               static_cast<hipStream_t>(stream), slot_events(ev, LA_KSLOT_STATE),
                               slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
                ? LA_OK

@@ -55,8 +55,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(Shape sh, const T *__restri
             s_pk[tid] = load_as_f32(ks, tid);
         }
     } else if (sh.phi == kElu1) {
+        // the normalised query takes its power-of-two scale (cancels in the
+        // division); retention's unnormalised read keeps 1
+        const float xq = tid < dk ? load_as_f32(qs, tid) : -__builtin_huge_valf();
+        float m = xq;
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if ((tid & 63) == 0) s_den[tid >> 6] = m;
+        __syncthreads();
+        float e = 0.f;
+        if constexpr (!RET) e = elu1_query_shift(fmaxf(fmaxf(s_den[0], s_den[1]), fmaxf(s_den[2], s_den[3])));
+        __syncthreads();  // s_den is reused for the denominator below
         if (tid < dk) {
-            s_pq[tid] = elu1_accurate(load_as_f32(qs, tid));
+            s_pq[tid] = RET ? elu1_accurate(xq) : elu1_accurate_scaled(xq, e);
             s_pk[tid] = elu1_accurate(load_as_f32(ks, tid));
         }
     } else if (sh.phi == kCosformer) {

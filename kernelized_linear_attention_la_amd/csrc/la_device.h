@@ -35,6 +35,26 @@ template <> __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p
 // alpha = 1, which is x + 1 for x > 0 and exp(x) otherwise.  Accurate expf.
 __device__ __forceinline__ float elu1_accurate(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
+// Power-of-two scale of an ELU+1 query row ("Story of Attention Part 5", 1a:
+// the normaliser phi(q)^T z can drift toward zero): with qmax the row's
+// largest coordinate, e = floor(qmax log2 e) when qmax <= 0, else 0, and the
+// row's features are taken as phi(q) 2^-e.  The largest then lies in [1, 2),
+// so the products with the keys' features stay normal fp32 numbers where
+// exp(q_f) exp(k_f) would underflow; numerator and denominator scale alike and
+// the output does not change.  Rows with a positive coordinate keep e = 0.
+__device__ __forceinline__ float elu1_query_shift(float qmax) {
+    return qmax > 0.f ? 0.f : floorf(qmax * 1.44269504088896341f);
+}
+
+// ELU+1 of x times 2^-e (e <= 0 from elu1_query_shift), accurate expf: the
+// exact power-of-two product while exp(x) is a normal number, exp2 of the
+// shifted exponent below that.
+__device__ __forceinline__ float elu1_accurate_scaled(float x, float e) {
+    if (x > 0.f) return x + 1.f;
+    if (e == 0.f || x >= -87.f) return ldexpf(expf(x), static_cast<int>(-e));
+    return exp2f(fmaf(x, 1.44269504088896341f, -e));
+}
+
 // Same map with the hardware exp2 (about 1 ulp); used where the result is
 // rounded to bf16 right after.
 __device__ __forceinline__ float elu1_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }

@@ -54,7 +54,7 @@ __host__ __device__ inline GenLayout gen_layout(int dk, int dp) {
 // past nvalid become zero (they must not contribute to any sum).
 template <typename T>
 __device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int row0, int nvalid,
-                         float *sX, float *sSq, float *out) {
+                         float *sX, float *sSq, float *out, bool query = false) {
     const int tid = threadIdx.x;
     const int dk = sh.dk;
     if (sh.phi == kIdentity) {  // raw rows (retention's q and k)
@@ -65,10 +65,27 @@ __device__ void phi_tile(const Shape &sh, const GenLayout &L, const T *X, int ro
         return;
     }
     if (sh.phi == kElu1) {
+        // normalised queries: each row takes its power-of-two scale (it
+        // cancels in the division; the unnormalised retention form keeps 1)
+        const bool scaled = query && !sh.ret;
+        if (scaled) {
+            if (tid < L.T) {
+                float m = 0.f;  // rows past nvalid are zero anyway
+                if (tid < nvalid) {
+                    m = -__builtin_huge_valf();
+                    for (int c = 0; c < dk; ++c) m = fmaxf(m, load_as_f32(X, (size_t)(row0 + tid) * dk + c));
+                }
+                sSq[tid] = elu1_query_shift(m);
+            }
+            __syncthreads();
+        }
         for (int e = tid; e < L.T * dk; e += kThreads) {
             int r = e / dk, c = e - r * dk;
             float v = 0.f;
-            if (r < nvalid) v = elu1_accurate(load_as_f32(X, (size_t)(row0 + r) * dk + c));
+            if (r < nvalid) {
+                const float x = load_as_f32(X, (size_t)(row0 + r) * dk + c);
+                v = scaled ? elu1_accurate_scaled(x, sSq[r]) : elu1_accurate(x);
+            }
             out[r * L.dpp + c] = v;
         }
         return;
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_generic(FwdArgs a) {
         if constexpr (MODE != kModeState) {
             for (int qt = 0; qt < Lc; qt += L.T) {
                 const int nq = min(L.T, Lc - qt);
-                phi_tile(sh, L, Qs, t0 + qt, nq, sX, sSq, sPQ);
+                phi_tile(sh, L, Qs, t0 + qt, nq, sX, sSq, sPQ, true);
                 __syncthreads();
                 // inter-chunk read of the carried state: phiQ S, phiQ z
                 float acc[2], den[2];
@@ -384,6 +401,14 @@ __global__ __launch_bounds__(kThreads) void k_scan(int BH, int P, int nS, int nz
     if (out) out[(size_t)bh * n + idx] = acc;
 }
 
+// Copies the hand-off error word of a workspace control block (ctl[2], set by
+// a single-pass launch whose bounded wait expired) to *out, and clears it
+// when asked.  One thread; agent-scope accesses like the writers'.
+__global__ void k_ws_error(uint32_t *ctl, uint32_t *out, int clear) {
+    out[0] = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (clear) __hip_atomic_store(ctl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 
 size_t generic_lds_bytes(int dk, int dp) { return sizeof(float) * (size_t)gen_layout(dk, dp).total; }
@@ -416,6 +441,10 @@ hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const f
                             nS, nz, ws_S, ws_z, S_in, z_in, S_out, z_out, total_to_slot0 ? 1 : 0,
                             sh.ret ? sh.gamma : nullptr, sh.H,
                             seg_tokens, sh.N);
+}
+
+hipError_t launch_ws_error(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t stream) {
+    return launch_kernel(k_ws_error, dim3(1), dim3(1), 0, stream, ctl, out, clear ? 1 : 0);
 }
 
 }  // namespace la

@@ -357,9 +357,17 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             cf_phase(t0 + row, cw, sw);
 #pragma unroll
             for (int kf = 0; kf < KBF; ++kf) phq[kf].u = relu_scale8(p.q[kf % G::KBD].u, kf < G::KBD ? cw : sw);
-        } else if constexpr (OUT && !G::XR) {
+        } else if constexpr (OUT && !G::XR && RET) {
 #pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = RET ? p.q[kb].u : elu1_bf16x8(p.q[kb].u);  // rows past the end are not stored
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = p.q[kb].u;  // rows past the end are not stored
+        } else if constexpr (OUT && !G::XR) {
+            // ELU+1 with the row's power-of-two scale (cancels in the division)
+            uint4 raw[KBF], ph[KBF];
+#pragma unroll
+            for (int kb = 0; kb < KBF; ++kb) raw[kb] = p.q[kb].u;
+            elu1_query_pieces<KBF>(raw, ph);
+#pragma unroll
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = ph[kb];
         }
         block_sync_lds();
         fetch(p, step + DEPTH);

@@ -70,6 +70,53 @@ __device__ __forceinline__ uint4 elu1_bf16x8(uint4 x) {
     return r;
 }
 
+// Exponent of the power-of-two scale of an ELU+1 query row whose largest raw
+// coordinate is qmax: e = floor(qmax log2 e) when qmax <= 0 (every feature is
+// then exp(q_f) <= 1), else 0.  The row's features are taken as phi(q) 2^-e:
+// the largest lands in [1, 2), so phi(q).phi(k) stays a normal fp32 number
+// where exp(q_f) exp(k_f) alone would underflow ("Story of Attention Part 5",
+// 1a, the normaliser phi(q)^T z drifting toward zero).  A power of two scales
+// the row's numerator and denominator alike and leaves their ratio, the
+// output, unchanged; for every row with a positive coordinate e = 0 and the
+// features are bit for bit the plain ones.
+__device__ __forceinline__ float elu1_row_shift(float qmax) {
+    return qmax > 0.f ? 0.f : floorf(qmax * 1.44269504088896341f);
+}
+
+// ELU+1 of x scaled by 2^-e (e from elu1_row_shift of x's row)
+__device__ __forceinline__ float elu1_hw_scaled(float x, float e) {
+    const float v = __builtin_amdgcn_exp2f(x * 1.44269504088896341f - e);
+    return x > 0.f ? x + 1.f : v;
+}
+
+__device__ __forceinline__ float max_bf16x8(uint4 x, float m) {
+    m = fmaxf(m, fmaxf(lo_bf16(x.x), hi_bf16(x.x)));
+    m = fmaxf(m, fmaxf(lo_bf16(x.y), hi_bf16(x.y)));
+    m = fmaxf(m, fmaxf(lo_bf16(x.z), hi_bf16(x.z)));
+    return fmaxf(m, fmaxf(lo_bf16(x.w), hi_bf16(x.w)));
+}
+
+// ELU+1 of a query row held as MFMA B-operand pieces (lane l: row l % 16,
+// eight features per piece, pieces of the row spread over the lanes
+// l % 16 + 16 g), with the row's power-of-two scale (elu1_row_shift).
+template <int NKB>
+__device__ __forceinline__ void elu1_query_pieces(const uint4 (&raw)[NKB], uint4 (&out)[NKB]) {
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) m = max_bf16x8(raw[kb], m);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float e = elu1_row_shift(m);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        const uint4 x = raw[kb];
+        out[kb].x = cvt2(elu1_hw_scaled(lo_bf16(x.x), e), elu1_hw_scaled(hi_bf16(x.x), e));
+        out[kb].y = cvt2(elu1_hw_scaled(lo_bf16(x.y), e), elu1_hw_scaled(hi_bf16(x.y), e));
+        out[kb].z = cvt2(elu1_hw_scaled(lo_bf16(x.z), e), elu1_hw_scaled(hi_bf16(x.z), e));
+        out[kb].w = cvt2(elu1_hw_scaled(lo_bf16(x.w), e), elu1_hw_scaled(hi_bf16(x.w), e));
+    }
+}
+
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3).

@@ -153,8 +153,15 @@ __global__ __launch_bounds__(kSThreads) void k_seg(FwdArgs a) {
     // local part of this wave's rows: (P (.) M) V_aug over the key blocks up
     // to the diagonal (every wave calls it once, before the prefix read)
     auto local_rows = [&]() {
+        if constexpr (RET) {
 #pragma unroll
-        for (int kb = 0; kb < kSKB; ++kb) phq[kb].u = RET ? qraw[kb] : elu1_bf16x8(qraw[kb]);
+            for (int kb = 0; kb < kSKB; ++kb) phq[kb].u = qraw[kb];
+        } else {  // ELU+1 with the row's power-of-two scale (cancels in the division)
+            uint4 ph[kSKB];
+            elu1_query_pieces<kSKB>(qraw, ph);
+#pragma unroll
+            for (int kb = 0; kb < kSKB; ++kb) phq[kb].u = ph[kb];
+        }
 #pragma unroll
         for (int nb = 0; nb < NJ; ++nb) acc[nb] = zero4();
         for (int kt = 0; 2 * kt <= qb; ++kt) {

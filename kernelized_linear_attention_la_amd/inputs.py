@@ -104,26 +104,34 @@ def _fill_slices(shm_name, shape, key_prefix, scale, lo, hi):
 
 
 def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: str,
-                extra=(), workers: int | None = None) -> HostTensor:
-    """Seeded N(0, scale^2) tensor of shape [B, H, n, d] (n may be 1).
+                extra=(), workers: int | None = None, offset=0.0) -> HostTensor:
+    """Seeded N(offset, scale^2) tensor of shape [B, H, n, d] (n may be 1).
 
     Slice (b, h) depends only on (workload_id, tensor_id, *extra, b, h), so any
     slice can be regenerated on its own.  Large tensors are drawn in a small
     pool of spawned worker processes; the values do not depend on the pool.
+    offset (a number, or an array broadcast against [B, H, n, d]) is added in
+    fp64 before the rounding (serial draws only).
     """
     B, H = shape[0], shape[1]
     per = int(np.prod(shape[2:]))
     key_prefix = (workload_id, tensor_id) + tuple(extra)
     total = B * H * per
+    has_offset = not (np.isscalar(offset) and offset == 0.0)
     if workers is None:
-        workers = 1 if total < (1 << 26) else min(16, os.cpu_count() or 1)
+        workers = 1 if (total < (1 << 26) or has_offset) else min(16, os.cpu_count() or 1)
+    if has_offset and workers > 1:
+        raise ValueError("offset draws are serial")
     if workers <= 1:
         out = np.empty((B * H, per), dtype=np.float64)
         for s in range(B * H):
             b, h = divmod(s, H)
             out[s] = _slice_draw(key_prefix + (b, h), per)
         out *= scale
-        return _round_to(out.reshape(shape), dtype)
+        out = out.reshape(shape)
+        if has_offset:
+            out = out + np.asarray(offset, dtype=np.float64)
+        return _round_to(out, dtype)
 
     # worker processes run this module directly (python -m ...), so they never
     # re-import the caller's main script
@@ -311,6 +319,20 @@ def custom_inputs(seed: int, B, H, N, dk, dv, scale=1.0, dtype="f32", phi="elu1"
     W = orthogonal_gaussian_rows(1000 + seed, m, dk) if phi == "favor" else None
     wl = Workload(f"custom{seed}", 1000 + seed, phi, dtype, B, H, N, dk, dv, scale, 64, m=m)
     return ForwardInputs(wl, Q, K, V, W)
+
+
+def offset_inputs(seed: int, B, H, N, dk, dv, q_offset, k_offset, spread=0.5, v_scale=None, dtype="f32"):
+    """Inputs far on the negative side of the ELU+1 map: Q ~ N(q_offset,
+    spread^2), K ~ N(k_offset, spread^2) per coordinate (offsets are numbers or
+    arrays broadcast against [B, H, N, 1], e.g. per-row offsets), V ~ N(0,
+    v_scale^2) (default 1/sqrt(d_v)).  The same recipe as every other draw
+    (seeded per slice, fp64 -> fp32 -> storage)."""
+    vs = dv ** -0.5 if v_scale is None else v_scale
+    Q = normal_bhnd(3000 + seed, TENSOR_Q, (B, H, N, dk), spread, dtype, offset=q_offset)
+    K = normal_bhnd(3000 + seed, TENSOR_K, (B, H, N, dk), spread, dtype, offset=k_offset)
+    V = normal_bhnd(3000 + seed, TENSOR_V, (B, H, N, dv), vs, dtype)
+    wl = Workload(f"offset{seed}", 3000 + seed, "elu1", dtype, B, H, N, dk, dv, spread, 64)
+    return ForwardInputs(wl, Q, K, V, None)
 
 
 def grad_output(wid: int, B, H, N, dv, dtype, scale=1.0, workers=None) -> HostTensor:

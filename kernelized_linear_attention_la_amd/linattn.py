@@ -29,7 +29,7 @@ EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspac
             "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step",
             "la_backward_workspace_bytes", "la_backward_causal_chunked", "la_forward_gla_recurrent",
             "la_forward_delta_recurrent", "la_delta_workspace_bytes", "la_forward_delta_chunked",
-            "la_gla_workspace_bytes", "la_forward_gla_chunked")
+            "la_gla_workspace_bytes", "la_forward_gla_chunked", "la_workspace_error")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 LA_BSLOT_FWD_SUMS, LA_BSLOT_FWD_SCAN, LA_BSLOT_DQ, LA_BSLOT_RSCAN, LA_BSLOT_DKV, LA_BSLOTS = 0, 1, 2, 3, 4, 5
 
@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
         L.la_forward_gla_chunked.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                              ctypes.POINTER(LaKernelEvents)]
         L.la_forward_gla_chunked.restype = i
+        L.la_workspace_error.argtypes = [vp, sz, vp, i, vp]
+        L.la_workspace_error.restype = i
         _lib = L
     return _lib
 
@@ -198,6 +200,33 @@ def _state_pair(S, z, B, H, dp, dv, device, what):
     return S, z
 
 
+def _default_workspace(nbytes, device, zeroed, where):
+    """A workspace for a call that was given none.  Not while the current
+    stream is capturing a graph: the allocation (and, for the forward's
+    hand-off, the zero fill) would be recorded into the graph and replayed;
+    such callers pass their own workspace, zero-filled once beforehand."""
+    if torch.cuda.is_current_stream_capturing():
+        raise ValueError(f"{where}: pass workspace= (a device tensor of at least {nbytes} bytes"
+                         f"{', zero-filled before its first use' if zeroed else ''}) while the stream is capturing")
+    if zeroed:
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def la_workspace_error(workspace, err=None, clear=False, stream=None):
+    """Enqueue a copy of the workspace's hand-off error word (0: no wait ever
+    expired) into err (int32 device tensor [1], allocated when None) and clear
+    the word if asked; returns err (read it after synchronising the stream)."""
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace must be a device tensor")
+    if err is None:
+        err = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    st = lib().la_workspace_error(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err),
+                                  1 if clear else 0, _stream(stream))
+    _raise(st, "la_workspace_error")
+    return err
+
+
 def _raise(status, where):
     if status != LA_OK:
         raise LaError(status, where)
@@ -226,7 +255,7 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
     if workspace is None and nbytes > 0:
         # a fresh workspace starts zero-filled (the C contract); a caller that
         # passes its own keeps it between calls
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(nbytes, q.device, True, "la_forward_causal_chunked")
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is None:
         st = lib().la_forward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
@@ -254,7 +283,7 @@ def la_forward_noncausal(q, k, v, phi="elu1", W=None, S_out=None, z_out=None, ou
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     nbytes = la_workspace_bytes(p, 64)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(max(nbytes, 1), q.device, False, "la_forward_noncausal")
     wsb = workspace.numel() * workspace.element_size()
     st = lib().la_forward_noncausal(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_out), _ptr(z_out),
                                     _ptr(workspace), wsb, _stream(stream))
@@ -321,7 +350,7 @@ def la_forward_retention_chunked(q, k, v, gamma, chunk=64, phi="identity", W=Non
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     nbytes = la_workspace_bytes(p, chunk)
     if workspace is None and nbytes > 0:
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(nbytes, q.device, True, "la_forward_retention_chunked")
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().la_forward_retention_chunked(ctypes.byref(p), _ptr(gamma), int(chunk), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(out), _ptr(S_in), _ptr(S_out), _ptr(workspace), wsb,
@@ -387,7 +416,7 @@ def la_backward_causal_chunked(q, k, v, dO, chunk=64, phi="elu1", W=None, S_in=N
     if nbytes == 0:
         raise LaError(4, "la_backward_workspace_bytes")
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(nbytes, q.device, False, "la_backward_causal_chunked")
     wsb = workspace.numel() * workspace.element_size()
     st = lib().la_backward_causal_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dO),
                                           _ptr(S_in), _ptr(z_in), _ptr(dS_out), _ptr(dz_out), _ptr(dQ), _ptr(dK),
@@ -462,7 +491,8 @@ def la_forward_delta_chunked(q, k, v, beta, alpha=None, S_in=None, S_out=None, o
     beta = _gate(beta, q.shape[:3], q.device, "beta")
     alpha = _gate(alpha, q.shape[:3], q.device, "alpha")
     if workspace is None:
-        workspace = torch.empty(max(la_delta_workspace_bytes(q, v, chunk), 16), dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(max(la_delta_workspace_bytes(q, v, chunk), 16), q.device, False,
+                                       "la_forward_delta_chunked")
     wsb = workspace.numel() * workspace.element_size()
     st = lib().la_forward_delta_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                         _ptr(beta), _ptr(S_in), _ptr(S_out), _ptr(out), _ptr(workspace), wsb,
@@ -486,7 +516,8 @@ def la_forward_gla_chunked(q, k, v, alpha, S_in=None, S_out=None, out=None, chun
     p, S_in, S_out, out = _gated_common(q, k, v, S_in, S_out, out)
     alpha = _gate(alpha, q.shape, q.device, "alpha")
     if workspace is None:
-        workspace = torch.empty(max(la_gla_workspace_bytes(q, v, chunk), 16), dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(max(la_gla_workspace_bytes(q, v, chunk), 16), q.device, False,
+                                       "la_forward_gla_chunked")
     wsb = workspace.numel() * workspace.element_size()
     st = lib().la_forward_gla_chunked(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                       _ptr(S_in), _ptr(S_out), _ptr(out), _ptr(workspace), wsb, _stream(stream),

@@ -68,3 +68,25 @@ def slice_rel_err(y, ref):
 
 def tol_for(dtype):
     return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+GUARD_BYTES = 256
+CANARY = 0xA5
+
+
+class Guarded:
+    """A device tensor with guard bands: `t` is a contiguous view into a larger
+    uint8 buffer whose GUARD_BYTES before and after `t` hold CANARY bytes.
+    `intact()` is True while no kernel has written outside `t`'s own bytes."""
+
+    def __init__(self, shape, dtype, device="cuda", fill=None):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.buf = torch.full((GUARD_BYTES + n + GUARD_BYTES,), CANARY, dtype=torch.uint8, device=device)
+        self.n = n
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(*shape)
+        if fill is not None:
+            self.t.fill_(fill)
+
+    def intact(self):
+        head, tail = self.buf[:GUARD_BYTES], self.buf[GUARD_BYTES + self.n:]
+        return bool((head == CANARY).all()) and bool((tail == CANARY).all())

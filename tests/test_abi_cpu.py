@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert linattn.la_abi_version() == 5
+    assert linattn.la_abi_version() == 6
     for s in range(8):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)
@@ -222,7 +222,8 @@ def test_gla_chunked_validation():
     L = linattn.lib()
     pid = _p(phi=linattn.LA_PHI_IDENTITY)
     need = L.la_gla_workspace_bytes(ctypes.byref(pid), 64)
-    assert need == 4 * pid.B * pid.H * (-(-pid.N // 64)) * (3 * 64 * 64 + 64)
+    # the records start past the 256-byte control block that the forward's hand-off keeps
+    assert need == 256 + 4 * pid.B * pid.H * (-(-pid.N // 64)) * (3 * 64 * 64 + 64)
     assert L.la_gla_workspace_bytes(ctypes.byref(pid), 32) == 0
     assert L.la_gla_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=65)), 64) == 0
 
@@ -247,7 +248,7 @@ def test_delta_chunked_validation():
     need = L.la_delta_workspace_bytes(ctypes.byref(pid), 64)
     # one record per (b, h, chunk): W and P (64 x 64), Ut (64 x d_v), gate products (2 x 64), fp32
     n_chunks = -(-pid.N // 64)
-    assert need == 4 * pid.B * pid.H * n_chunks * (2 * 64 * 64 + 64 * 64 + 128)
+    assert need == 256 + 4 * pid.B * pid.H * n_chunks * (2 * 64 * 64 + 64 * 64 + 128)
     assert L.la_delta_workspace_bytes(ctypes.byref(pid), 32) == 0
     assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=32)), 64) == 0
     assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_v=40)), 64) == 0
@@ -298,3 +299,14 @@ def test_bench_refuses_several_gpus():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "--gpus 2 is not supported" in r.stderr
+
+
+def test_workspace_error_validation():
+    """la_workspace_error checks its pointers, alignment and the control block's size on the host."""
+    L = linattn.lib()
+    assert L.la_workspace_error(None, 256, FAKE, 0, None) == 1
+    assert L.la_workspace_error(FAKE, 256, None, 0, None) == 1
+    assert L.la_workspace_error(MIS, 256, FAKE, 0, None) == 5
+    assert L.la_workspace_error(FAKE, 256, ctypes.c_void_p(0x100002), 0, None) == 5
+    assert L.la_workspace_error(FAKE, 255, FAKE, 1, None) == 6
+

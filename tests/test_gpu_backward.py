@@ -149,3 +149,22 @@ def test_backward_fp32_kernels_behind_matrix_core_sums():
     got, ref = _run(7, 2, 8, 8192, 64, 64, "bf16", "favor", 256, 64, False,
                     slices=(np.array([[0], [1]]), np.array([[2], [7]])))
     _check(got, ref, "bf16", "FAVOR+ B2H8N8192 sampled")
+
+
+def test_backward_sums_on_the_128_token_state_pass():
+    # bf16 ELU+1 d64 asking for 128-token chunks at B2 H8 N8192.  The
+    # fp32-arithmetic backward tiles 16 tokens and aims at 1024 workgroups:
+    # 16 slices x 64 segments of 8 tiles, i.e. segments of exactly 128 tokens,
+    # whole chunks of the 128-token matrix-core state pass, which therefore
+    # forms the forward sums in front of it (the 64-token pass is taken only
+    # when the segments are not whole 128-token chunks).  Two slices are
+    # recomputed by the oracle, each with a carried state.
+    B, H, N = 2, 8, 8192
+    n_tiles = N // 16
+    want = -(-1024 // (B * H))
+    seg_tiles = -(-n_tiles // want)
+    assert seg_tiles * 16 == 128 and N % 128 == 0
+    _say("B2 H8 N8192 d64 bf16 chunk 128, state (slices (0,1), (1,6))")
+    got, ref = _run(8, B, H, N, 64, 64, "bf16", "elu1", 0, 128, True,
+                    slices=(np.array([[0], [1]]), np.array([[1], [6]])))
+    _check(got, ref, "bf16", "ELU+1 d64 chunk 128 on 128-token sums")

@@ -1,8 +1,11 @@
 """GPU parity of the gated and delta-rule recurrences (la_forward_gla_recurrent,
 la_forward_delta_recurrent, through the C ABI) against the oracle.
 
-Outputs: per (b, h) slice max |gpu - oracle| / max |oracle| (slice_rel_err);
-final states: state_rel_err.  1e-4 for fp32 storage, 2e-2 for bf16 (fp32
+Outputs: per row (b, h, t) max |gpu - oracle| / max |oracle| over the row
+(row_rel_err, the metric of every forward in the suite: a row that a zero
+gate left far below the slice's largest row is still held to its own scale;
+a row that is exactly zero in exact arithmetic is held to the tolerance in
+absolute terms); final states: state_rel_err.  1e-4 for fp32 storage, 2e-2 for bf16 (fp32
 state and arithmetic, outputs rounded once).
 """
 import sys
@@ -14,7 +17,7 @@ import torch
 import oracle
 from kernelized_linear_attention_la_amd import inputs
 from kernelized_linear_attention_la_amd import linattn as la
-from tests.parity import slice_rel_err, state_rel_err, to_device, to_f64, tol_for
+from tests.parity import row_rel_err, state_rel_err, to_device, to_f64, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +62,7 @@ def _run(ci, case, kind):
         O = la.la_forward_delta_recurrent(q, k, v, dev(gi.beta), alpha=dev(alpha), S_in=dev(S_in), S_out=S_out)
         ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=alpha, S_in=S_in)
     torch.cuda.synchronize()
-    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    eo, es = row_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
     _say(kind, case, f"O {eo:.2e} S {es:.2e}")
     tol = tol_for(dtype)
     assert eo < tol and es < tol, (eo, es)
@@ -88,7 +91,7 @@ def test_state_handoff_in_place():
         O2 = la.la_forward_delta_recurrent(c(q, M, N), c(k, M, N), c(v, M, N), c(be, M, N), alpha=c(al, M, N),
                                            S_in=S, S_out=S)
         torch.cuda.synchronize()
-        assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
+        assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
         assert state_rel_err(to_f64(S), Sref) < 1e-4
 
 
@@ -118,7 +121,7 @@ def test_gla_extreme_gates_against_oracle(dtype):
                                     S_out=S_out)
     ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, al, S_in=S_in)
     torch.cuda.synchronize()
-    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    eo, es = row_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
     _say("gla extreme gates", dtype, f"O {eo:.2e} S {es:.2e}")
     tol = tol_for(dtype)
     assert np.isfinite(to_f64(O)).all()
@@ -140,7 +143,7 @@ def test_gla_state_handoff_across_forms():
         O1 = la.la_forward_gla_recurrent(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(al, 0, M), S_out=S)
         O2 = la.la_forward_gla_recurrent(c(q, M, N), c(k, M, N), c(v, M, N), c(al, M, N), S_in=S, S_out=S)
         torch.cuda.synchronize()
-        assert slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
+        assert row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref) < 1e-4
         assert state_rel_err(to_f64(S), Sref) < 1e-4
 
 
@@ -175,7 +178,7 @@ def test_delta_chunked_against_oracle(ci, kind):
     O = la.la_forward_delta_chunked(q, k, v, dev(gi.beta), alpha=dev(alpha), S_in=dev(S_in), S_out=S_out)
     torch.cuda.synchronize()
     ref, Sref = oracle.delta_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.beta, alpha=alpha, S_in=S_in)
-    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    eo, es = row_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
     _say("chunked", kind, f"O {eo:.2e} S {es:.2e}")
     tol = tol_for(dtype)
     assert eo < tol and es < tol, (eo, es)
@@ -204,7 +207,7 @@ def test_delta_chunked_handoff_and_small_gates():
         O2 = la.la_forward_delta_chunked(c(q, M, N), c(k, M, N), c(v, M, N), c(be, M, N), alpha=c(alt, M, N),
                                          S_in=S, S_out=S)
         torch.cuda.synchronize()
-        eo = slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref)
+        eo = row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref)
         es = state_rel_err(to_f64(S), Sref)
         _say("chunked handoff", M, f"O {eo:.2e} S {es:.2e}")
         assert eo < 1e-4 and es < 1e-4, (eo, es)
@@ -247,7 +250,7 @@ def test_gla_chunked_against_oracle(ci):
     O = la.la_forward_gla_chunked(q, k, v, dev(gi.alpha_ch), S_in=dev(S_in), S_out=S_out)
     torch.cuda.synchronize()
     ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch, S_in=S_in)
-    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    eo, es = row_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
     _say("gla split", f"O {eo:.2e} S {es:.2e}")
     tol = tol_for(dtype)
     assert eo < tol and es < tol, (eo, es)
@@ -268,7 +271,7 @@ def test_gla_chunked_extreme_gates_and_handoff(dtype):
     S_out = torch.empty(B, H, dk, dv, device="cuda")
     O = la.la_forward_gla_chunked(q, k, v, alt, S_in=torch.from_numpy(S_in).cuda(), S_out=S_out)
     torch.cuda.synchronize()
-    eo, es = slice_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
+    eo, es = row_rel_err(to_f64(O), ref), state_rel_err(to_f64(S_out), Sref)
     _say("gla split extreme", dtype, f"O {eo:.2e} S {es:.2e}")
     assert np.isfinite(to_f64(O)).all()
     assert eo < tol and es < tol, (eo, es)
@@ -278,7 +281,7 @@ def test_gla_chunked_extreme_gates_and_handoff(dtype):
     O1 = la.la_forward_gla_chunked(c(q, 0, M), c(k, 0, M), c(v, 0, M), c(alt, 0, M), S_in=S, S_out=S)
     O2 = la.la_forward_gla_chunked(c(q, M, N), c(k, M, N), c(v, M, N), c(alt, M, N), S_in=S, S_out=S)
     torch.cuda.synchronize()
-    eo, es = slice_rel_err(to_f64(torch.cat([O1, O2], 2)), ref), state_rel_err(to_f64(S), Sref)
+    eo, es = row_rel_err(to_f64(torch.cat([O1, O2], 2)), ref), state_rel_err(to_f64(S), Sref)
     _say("gla split handoff", dtype, f"O {eo:.2e} S {es:.2e}")
     assert eo < tol and es < tol, (eo, es)
 
@@ -301,7 +304,7 @@ def test_two_launch_forms_graph_replay():
     torch.cuda.synchronize()
     Og0, Od0, Sg0, Sd0 = Og.clone(), Od.clone(), Sg.clone(), Sd.clone()
     ref, Sref = oracle.gla_recurrent(gi.Q.f32, gi.K.f32, gi.V.f32, gi.alpha_ch, S_in=S_in.cpu().numpy())
-    assert slice_rel_err(to_f64(Og0), ref) < tol_for("bf16")
+    assert row_rel_err(to_f64(Og0), ref) < tol_for("bf16")
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):  # warm up on the capture stream

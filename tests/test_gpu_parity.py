@@ -17,7 +17,7 @@ import torch
 import oracle
 from kernelized_linear_attention_la_amd import inputs
 from kernelized_linear_attention_la_amd import linattn as la
-from tests.parity import (TOL_BF16, TOL_F32, row_rel_err, state_rel_err, tol_for, to_device, to_f64,
+from tests.parity import (TOL_BF16, TOL_F32, Guarded, row_rel_err, state_rel_err, tol_for, to_device, to_f64,
                           z_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -149,19 +149,28 @@ def test_shapes_against_oracle(ci):
     q, k, v, W = _dev(fi)
     dp = m if phi == "favor" else dk
     _say("case", case)
-    S, z = _zero_state(B, H, dp, dv)
-    O = la.la_forward_causal_chunked(q, k, v, chunk, phi=phi, W=W, S_out=S, z_out=z)
+    # outputs and states inside guard bands: no kernel writes past their ends
+    gO, gS, gz = Guarded((B, H, N, dv), q.dtype), Guarded((B, H, dp, dv), torch.float32), \
+        Guarded((B, H, dp), torch.float32)
+    O = la.la_forward_causal_chunked(q, k, v, chunk, phi=phi, W=W, S_out=gS.t, z_out=gz.t, out=gO.t)
     ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
     torch.cuda.synchronize()
+    assert gO.intact() and gS.intact() and gz.intact()
+    S, z = gS.t, gz.t
     tol = tol_for(dtype)
     e = row_rel_err(to_f64(O), ref)
     assert e < tol, e
     assert state_rel_err(to_f64(S), Sref) < tol
     assert z_rel_err(to_f64(z), zref) < tol
-    On = la.la_forward_noncausal(q, k, v, phi=phi, W=W)
-    refn, _, _ = oracle.noncausal(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
+    gOn, gSn, gzn = Guarded((B, H, N, dv), q.dtype), Guarded((B, H, dp, dv), torch.float32), \
+        Guarded((B, H, dp), torch.float32)
+    On = la.la_forward_noncausal(q, k, v, phi=phi, W=W, S_out=gSn.t, z_out=gzn.t, out=gOn.t)
+    refn, Srn, zrn = oracle.noncausal(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
     torch.cuda.synchronize()
+    assert gOn.intact() and gSn.intact() and gzn.intact()
     assert row_rel_err(to_f64(On), refn) < tol
+    assert state_rel_err(to_f64(gSn.t), Srn) < tol
+    assert z_rel_err(to_f64(gzn.t), zrn) < tol
 
 
 def test_state_handoff_and_in_place_state():
@@ -217,12 +226,16 @@ def test_decode_matches_forward_and_oracle():
         q, k, v, W = _dev(fi)
         dp = m if phi == "favor" else d
         _say("decode steps", phi)
-        S, z = _zero_state(B, H, dp, d)
+        gS, gz = Guarded((B, H, dp, d), torch.float32, fill=0.0), Guarded((B, H, dp), torch.float32, fill=0.0)
+        S, z = gS.t, gz.t
         outs = []
         for t in range(N):
+            go = Guarded((B, H, 1, d), q.dtype)
             outs.append(la.la_decode_step(q[:, :, t:t + 1].contiguous(), k[:, :, t:t + 1].contiguous(),
-                                          v[:, :, t:t + 1].contiguous(), S, z, phi=phi, W=W))
-        torch.cuda.synchronize()
+                                          v[:, :, t:t + 1].contiguous(), S, z, phi=phi, W=W, out=go.t))
+            torch.cuda.synchronize()
+            assert go.intact(), t
+        assert gS.intact() and gz.intact()
         ref, Sref, zref = oracle.causal_recurrent(phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
         assert row_rel_err(to_f64(torch.cat(outs, 2)), ref) < TOL_F32
         assert state_rel_err(to_f64(S), Sref) < TOL_F32

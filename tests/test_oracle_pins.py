@@ -320,3 +320,46 @@ def test_orthogonal_rows_are_orthogonal_within_blocks():
         assert np.abs(off).max() < 1e-3 * np.diag(G).mean()
     # row lengths behave like |N(0, I_64)|: mean of |w|^2 close to 64
     assert abs((W ** 2).sum(1).mean() - 64) < 4 * math.sqrt(2 * 64 / 256) * 1.5
+
+
+# --------------------------------------------------------------------------
+# the normaliser near zero ("Story of Attention Part 5", 1a: phi(q)^T z can
+# drift toward zero and make the division unstable).  Strongly negative ELU+1
+# inputs put every feature on the exp branch, so phi(q).phi(k) is tiny.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("c", [-20.0, -60.0, -200.0])
+def test_tiny_normaliser_constant_rows_give_running_mean(c):
+    # every query and key row equal to the constant c < 0: all scores are the
+    # same number exp(2c) d, so each causal output is the plain mean of the
+    # values seen so far, and the non-causal output is the mean of all values
+    rng = np.random.default_rng(11)
+    B, H, N, dk, dv = 1, 2, 9, 4, 3
+    Q = np.full((B, H, N, dk), c)
+    K = np.full((B, H, N, dk), c)
+    V = rng.standard_normal((B, H, N, dv))
+    run_mean = np.cumsum(V, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    for O in (oracle.causal_recurrent("elu1", Q, K, V)[0], oracle.quadratic("elu1", Q, K, V),
+              oracle.causal_chunked("elu1", Q, K, V, chunk=4)[0]):
+        np.testing.assert_allclose(O, run_mean, rtol=1e-12, atol=1e-12)
+    On = oracle.noncausal("elu1", Q, K, V)[0]
+    np.testing.assert_allclose(On, np.broadcast_to(V.mean(axis=2, keepdims=True), On.shape), rtol=1e-12, atol=1e-12)
+    # the normaliser itself is the count of tokens times exp(2c) d
+    _, _, z = oracle.causal_recurrent("elu1", Q, K, V)
+    np.testing.assert_allclose(z, N * math.exp(c), rtol=1e-12)
+
+
+def test_tiny_normaliser_shift_invariance():
+    # on the exp branch phi(x - s) = exp(-s) phi(x): shifting every coordinate
+    # of all-negative query rows (or of all-negative keys, with no starting
+    # state) scales numerator and denominator alike, so the outputs do not move
+    rng = np.random.default_rng(12)
+    B, H, N, dk, dv = 1, 2, 11, 5, 3
+    Q = -np.abs(rng.standard_normal((B, H, N, dk))) - 0.1
+    K = -np.abs(rng.standard_normal((B, H, N, dk))) - 0.1
+    V = rng.standard_normal((B, H, N, dv))
+    O0 = oracle.causal_recurrent("elu1", Q, K, V)[0]
+    for s, t in ((30.0, 0.0), (0.0, 30.0), (25.0, 45.0)):
+        O = oracle.causal_recurrent("elu1", Q - s, K - t, V)[0]
+        np.testing.assert_allclose(O, O0, rtol=1e-9, atol=1e-12)
+        On = oracle.noncausal("elu1", Q - s, K - t, V)[0]
+        np.testing.assert_allclose(On, oracle.noncausal("elu1", Q, K, V)[0], rtol=1e-9, atol=1e-12)
