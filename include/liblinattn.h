@@ -52,7 +52,9 @@ typedef enum {
     LA_ERR_UNSUPPORTED = 4, /* phi kind unknown; chunk not in {16, 32, 64, 128}           */
     LA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                          */
     LA_ERR_WORKSPACE = 6,   /* ws NULL or ws_bytes below la_workspace_bytes()            */
-    LA_ERR_DEVICE = 7       /* the HIP runtime refused a launch                          */
+    LA_ERR_DEVICE = 7,      /* the HIP runtime refused a launch                          */
+    LA_ERR_SCRATCH = 8      /* la_forward_causal_chunked_noalloc: the problem needs more
+                               scratch than LA_NOALLOC_SCRATCH_BYTES                    */
 } la_status;
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -170,6 +172,30 @@ la_status la_forward_causal_chunked(const la_problem *p, int chunk,
                                     const float *S_in, const float *z_in,
                                     float *S_out, float *z_out,
                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * la_forward_causal_chunked for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with the workspace taken
+ * from a fixed device array inside the library instead of the caller's ws.
+ *   Arguments and results as la_forward_causal_chunked, without ws/ws_bytes.
+ *   The array is LA_NOALLOC_SCRATCH_BYTES (32 MiB) on every device the library
+ *   runs on, held until the process ends; a problem whose
+ *   la_workspace_bytes(p, chunk) exceeds it returns LA_ERR_SCRATCH and
+ *   launches nothing.  The call never allocates or frees memory.  Its first
+ *   call on a device looks up that device's array and enqueues one zero fill
+ *   of it on `stream` ahead of its own kernels; every call then leaves the
+ *   array ready for the next.  All calls on one device share its array:
+ *   calls that may run at the same time on one device (on different streams)
+ *   race on it and must be ordered by the caller.  The hand-off error word
+ *   of the array is not exposed.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+la_status la_forward_causal_chunked_noalloc(const la_problem *p, int chunk,
+                                            const void *Q, const void *K, const void *V, void *O,
+                                            const float *S_in, const float *z_in,
+                                            float *S_out, float *z_out, void *stream);
 
 /*
  * Per-kernel timing hook for profiling and benchmarking.  A causal call

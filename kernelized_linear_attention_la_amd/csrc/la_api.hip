@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/liblinattn.h"
 #include "la_internal.h"
 
@@ -199,6 +201,21 @@ hipError_t launch_fwd(bool mfma, const FwdArgs &a, hipStream_t st, KEvents ev = 
     return mfma ? launch_mfma(a, st, ev) : launch_generic(a, st, ev);
 }
 
+// Argument checks of a causal call (everything but the workspace).
+la_status causal_validate(const la_problem *p, int chunk, const void *Q, const void *K, const void *V, const void *O,
+                          const float *S_in, const float *z_in, const float *S_out, const float *z_out) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if (p->phi == LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // the normaliser needs a positive map
+    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O) return LA_ERR_NULL;
+    if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_in) || !aligned16(z_in) ||
+        !aligned16(S_out) || !aligned16(z_out))
+        return LA_ERR_ALIGN;
+    return LA_OK;
+}
+
 // Timing events of one kernel slot of a call (profiling hook); marks the slot launched.
 KEvents slot_events(la_kernel_events *ev, int slot) {
     KEvents k;
@@ -226,6 +243,7 @@ LA_API const char *la_status_string(la_status s) {
         case LA_ERR_ALIGN: return "pointer not 16-byte aligned";
         case LA_ERR_WORKSPACE: return "workspace missing or too small";
         case LA_ERR_DEVICE: return "HIP launch failed";
+        case LA_ERR_SCRATCH: return "problem needs more scratch than the fixed array of the allocation-free entry point";
     }
     return "unknown status";
 }
@@ -302,15 +320,9 @@ LA_API la_status la_forward_causal_chunked_timed(const la_problem *p, int chunk,
                                                  const void *V, void *O, const float *S_in, const float *z_in,
                                                  float *S_out, float *z_out, void *ws, size_t ws_bytes, void *stream,
                                                  la_kernel_events *ev) {
-    la_status st = check_problem(p);
+    la_status st = causal_validate(p, chunk, Q, K, V, O, S_in, z_in, S_out, z_out);
     if (st != LA_OK) return st;
-    if (p->phi == LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;  // the normaliser needs a positive map
-    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
-    if (!Q || !K || !V || !O) return LA_ERR_NULL;
-    if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_in) || !aligned16(z_in) ||
-        !aligned16(S_out) || !aligned16(z_out) || !aligned16(ws))
-        return LA_ERR_ALIGN;
+    if (!aligned16(ws)) return LA_ERR_ALIGN;
     Shape sh = make_shape(p);
     bool mf = false;
     Segments g = causal_plan(sh, chunk, &mf);
@@ -716,4 +728,64 @@ LA_API la_status la_forward_delta_chunked(const la_problem *p, int chunk, const 
                               slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
                ? LA_OK
                : LA_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// Causal forward for callers that cannot allocate: the workspace is a fixed
+// device array of this library
+// ---------------------------------------------------------------------------
+namespace la {
+namespace {
+
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 16-byte words");
+
+// Workspace of la_forward_causal_chunked_noalloc: each device that runs the
+// library holds its own copy until the process ends.  Host code never uses
+// this name as an address (on the host it is only a stand-in for the device
+// symbol); it uses the per-device address looked up in device_scratch().
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device: address of `scratch` there (null until set up)
+
+// Address of the current device's scratch array.  On the first call on a
+// device (with that device current) the address is looked up with
+// hipGetSymbolAddress and one zero fill of the whole array is enqueued on the
+// caller's stream, ahead of the call's own kernels, so the hand-off control
+// block and flags start at zero; afterwards every call leaves the array ready
+// for the next one, as with a caller-owned workspace.
+la_status device_scratch(hipStream_t st, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LA_ERR_DEVICE;
+        if (launch_zero_fill(ptr, kScratchBytes, st) != hipSuccess) return LA_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LA_OK;
+}
+
+}  // namespace
+}  // namespace la
+
+LA_API la_status la_forward_causal_chunked_noalloc(const la_problem *p, int chunk, const void *Q, const void *K,
+                                                   const void *V, void *O, const float *S_in, const float *z_in,
+                                                   float *S_out, float *z_out, void *stream) {
+    la_status st = causal_validate(p, chunk, Q, K, V, O, S_in, z_in, S_out, z_out);
+    if (st != LA_OK) return st;
+    const size_t need = causal_ws(make_shape(p), chunk);
+    if (need > kScratchBytes) return LA_ERR_SCRATCH;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = device_scratch(hs, &ws);
+        if (st != LA_OK) return st;
+    }
+    return la_forward_causal_chunked_timed(p, chunk, Q, K, V, O, S_in, z_in, S_out, z_out, ws,
+                                           need > 0 ? kScratchBytes : 0, stream, nullptr);
 }

@@ -443,6 +443,19 @@ hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const f
                             seg_tokens, sh.N);
 }
 
+// Zero fill of n 16-byte words (grid-stride).
+__global__ void k_zero_fill(uint4 *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream) {
+    const size_t n = bytes / 16;
+    const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads < 1024 ? (n + kThreads - 1) / kThreads : 1024);
+    return launch_kernel(k_zero_fill, dim3(blocks > 0 ? blocks : 1), dim3(kThreads), 0, stream,
+                         static_cast<uint4 *>(p), n);
+}
+
 hipError_t launch_ws_error(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t stream) {
     return launch_kernel(k_ws_error, dim3(1), dim3(1), 0, stream, ctl, out, clear ? 1 : 0);
 }

@@ -131,6 +131,9 @@ hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev = {})
 hipError_t launch_scan(const Shape &sh, int P, float *ws_S, float *ws_z, const float *S_in,
                        const float *z_in, float *S_out, float *z_out, bool total_to_slot0,
                        hipStream_t stream, KEvents ev = {}, int seg_tokens = 0);
+// Zero fill of `bytes` (a multiple of 16) at p, on the stream (a kernel, so
+// it may be recorded into a graph).
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 // Error word of a workspace control block to *out (cleared when asked).
 hipError_t launch_ws_error(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t stream);
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o,

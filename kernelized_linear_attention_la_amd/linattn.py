@@ -23,13 +23,15 @@ LA_PHI_ELU1, LA_PHI_FAVOR, LA_PHI_IDENTITY, LA_PHI_DPFP, LA_PHI_TRIG, LA_PHI_COS
 _PHI_CODES = {"elu1": LA_PHI_ELU1, "favor": LA_PHI_FAVOR, "identity": LA_PHI_IDENTITY, "dpfp": LA_PHI_DPFP,
               "trig": LA_PHI_TRIG, "cosformer": LA_PHI_COSFORMER}
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_UNSUPPORTED",
-                5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE"}
+                5: "LA_ERR_ALIGN", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_DEVICE", 8: "LA_ERR_SCRATCH"}
+LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTED = ("la_abi_version", "la_status_string", "la_feature_dim", "la_workspace_bytes",
             "la_forward_noncausal", "la_forward_causal_chunked", "la_forward_causal_chunked_timed",
             "la_decode_step", "la_forward_retention_chunked", "la_retention_decode_step",
             "la_backward_workspace_bytes", "la_backward_causal_chunked", "la_forward_gla_recurrent",
             "la_forward_delta_recurrent", "la_delta_workspace_bytes", "la_forward_delta_chunked",
-            "la_gla_workspace_bytes", "la_forward_gla_chunked", "la_workspace_error")
+            "la_gla_workspace_bytes", "la_forward_gla_chunked", "la_workspace_error",
+            "la_forward_causal_chunked_noalloc")
 LA_KSLOT_STATE, LA_KSLOT_SCAN, LA_KSLOT_CHUNK, LA_KSLOTS = 0, 1, 2, 3
 LA_BSLOT_FWD_SUMS, LA_BSLOT_FWD_SCAN, LA_BSLOT_DQ, LA_BSLOT_RSCAN, LA_BSLOT_DKV, LA_BSLOTS = 0, 1, 2, 3, 4, 5
 
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
         L.la_forward_gla_chunked.restype = i
         L.la_workspace_error.argtypes = [vp, sz, vp, i, vp]
         L.la_workspace_error.restype = i
+        L.la_forward_causal_chunked_noalloc.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.la_forward_causal_chunked_noalloc.restype = i
         _lib = L
     return _lib
 
@@ -267,6 +271,26 @@ def la_forward_causal_chunked(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, 
                                                    _ptr(out), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
                                                    _ptr(workspace), wsb, _stream(stream), ctypes.byref(events))
         _raise(st, "la_forward_causal_chunked_timed")
+    return out
+
+
+def la_forward_causal_chunked_noalloc(q, k, v, chunk=64, phi="elu1", W=None, S_in=None, z_in=None, S_out=None,
+                                      z_out=None, out=None, stream=None, map_param=0, pos0=0):
+    """la_forward_causal_chunked with the library's fixed scratch array as the
+    workspace (the C call allocates nothing; pass `out` to allocate nothing here
+    either).  Returns O."""
+    _check_qkv(q, k, v)
+    p = _problem_of(q, v, phi, W, map_param, pos0)
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    dp = la_feature_dim(p)
+    S_in, z_in = _state_pair(S_in, z_in, B, H, dp, dv, q.device, "initial state")
+    S_out, z_out = _state_pair(S_out, z_out, B, H, dp, dv, q.device, "final state")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    st = lib().la_forward_causal_chunked_noalloc(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                 _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), _stream(stream))
+    _raise(st, "la_forward_causal_chunked_noalloc")
     return out
 
 

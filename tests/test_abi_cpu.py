@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert linattn.la_abi_version() == 6
-    for s in range(8):
+    for s in range(9):
         assert linattn.status_string(s)
     assert "unknown" in linattn.status_string(99)
 
@@ -310,3 +310,23 @@ def test_workspace_error_validation():
     assert L.la_workspace_error(FAKE, 256, ctypes.c_void_p(0x100002), 0, None) == 5
     assert L.la_workspace_error(FAKE, 255, FAKE, 1, None) == 6
 
+
+
+def test_noalloc_validation_and_scratch_limit():
+    """la_forward_causal_chunked_noalloc validates like la_forward_causal_chunked and
+    refuses, before touching a device, a problem whose workspace exceeds its fixed array."""
+    L = linattn.lib()
+
+    def call(p, chunk=64, Q=FAKE, Si=None, zi=None):
+        return L.la_forward_causal_chunked_noalloc(ctypes.byref(p), chunk, Q, FAKE, FAKE, FAKE, Si, zi, None, None,
+                                                   None)
+    assert call(_p(), Q=None) == 1
+    assert call(_p(), Q=MIS) == 5
+    assert call(_p(), Si=FAKE) == 1
+    assert call(_p(), chunk=48) == 4
+    assert call(_p(B=0)) == 2
+    big = _p(B=255, H=1, N=256, d_k=128, d_v=128)
+    need = linattn.la_workspace_bytes(big, 128)
+    assert need > linattn.LA_NOALLOC_SCRATCH_BYTES
+    assert call(big, chunk=128) == 8
+    assert "scratch" in linattn.status_string(8)
