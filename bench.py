@@ -32,7 +32,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "elu1_bf16_b4h8n2048d64_c64"
+DEFAULT_WORKLOAD = "elu1_bf16_b2h16n16384d128_c128"
+# measured in the same run as the default workload and reported under "extra":
+# the decode half of the metric and the FAVOR+ chunked forward (the one
+# workload whose flops outweigh its bytes)
+EXTRA_DECODE = "decode_elu1_f32_s256h32d128_prefix1024_steps64"
+EXTRA_FAVOR = "favor_bf16_b2h8n8192d64_m256_c64"
+PREFIX_BLOCK = 64  # sequences of the decode prefix drawn and run at a time
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 FP32_VECTOR_PEAK_TFS = 157.3  # MI355X fp32 vector ALUs (256 CUs x 256 flop/clk x 2.4 GHz), TFLOP/s
@@ -201,16 +207,16 @@ def run_cpu_baseline(wl, fi, seconds):
                       f"{reps} pass(es), {el:.1f} s on {nthreads} threads of '{cpu_model()}'"}
 
 
-def run_cpu_baseline_decode(wl, fi, seconds):
+def run_cpu_baseline_decode(wl, seconds):
     """Time the fp64 oracle's decode step on a bounded sample of sequences (all heads)."""
-    import numpy as np
     import oracle
     from kernelized_linear_attention_la_amd import inputs
     nthreads = oracle.num_threads()
     n_seq = min(wl.B, 8)
     sl = (slice(0, n_seq), slice(None))
-    # starting states from the same 1024-token prefix (not timed)
-    _, S, z = oracle.causal_recurrent(wl.phi, fi.Q.f32[sl], fi.K.f32[sl], fi.V.f32[sl], fi.W)
+    # starting states from the same 1024-token prefix of those sequences (not timed)
+    fi = inputs.forward_inputs(wl, batch=(0, n_seq))
+    _, S, z = oracle.causal_recurrent(wl.phi, fi.Q.f32, fi.K.f32, fi.V.f32, fi.W)
     steps = []
     for s in range(wl.decode_steps):
         q, k, v = inputs.decode_step_inputs(wl, s)
@@ -715,7 +721,6 @@ def bench_decode(args, wl):
     from kernelized_linear_attention_la_amd import linattn as la
 
     dev = torch.device("cuda:0")
-    fi = inputs.forward_inputs(wl)
 
     def to_dev(ht):
         t = torch.from_numpy(ht.store)
@@ -723,10 +728,16 @@ def bench_decode(args, wl):
 
     S = torch.zeros(wl.B, wl.H, wl.dprime, wl.dv, device=dev)
     z = torch.zeros(wl.B, wl.H, wl.dprime, device=dev)
-    q, k, v = to_dev(fi.Q), to_dev(fi.K), to_dev(fi.V)
-    la.la_forward_causal_chunked(q, k, v, wl.chunk, S_out=S, z_out=z)  # prefix (not timed)
-    torch.cuda.synchronize()
-    del q, k, v
+    # the prefix (not timed), drawn and run a block of sequences at a time:
+    # every (sequence, head) slice is independent and its values do not
+    # depend on the block
+    for b0 in range(0, wl.B, PREFIX_BLOCK):
+        b1 = min(wl.B, b0 + PREFIX_BLOCK)
+        fb = inputs.forward_inputs(wl, batch=(b0, b1))
+        q, k, v = to_dev(fb.Q), to_dev(fb.K), to_dev(fb.V)
+        la.la_forward_causal_chunked(q, k, v, wl.chunk, S_out=S[b0:b1], z_out=z[b0:b1])
+        torch.cuda.synchronize()
+        del q, k, v, fb
     steps_in = []
     for s in range(wl.decode_steps):
         qs, ks, vs = inputs.decode_step_inputs(wl, s)
@@ -765,7 +776,39 @@ def bench_decode(args, wl):
             "traffic": stored_traffic(wl, kname), "kernel": kname, "kernel_avg_us": kern_ms * 1e3,
             "alg_bytes_per_launch": nbytes, "timing": "hip events around each launch"}
     extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3)}
-    return value, ms_per_step, roof, extra, fi
+    return value, ms_per_step, roof, extra, None
+
+
+def measure_extras(args):
+    """The metric's other halves, measured in the same run as the headline:
+    decode tokens/s with its HBM fraction (c4), and the FAVOR+ chunked forward
+    with its bf16 matrix-core fraction (c5), each kernel timed by HIP events."""
+    import torch
+    from kernelized_linear_attention_la_amd import inputs
+    short = argparse.Namespace(steps=max(1, min(args.steps, 20)), warmup=max(1, min(args.warmup, 5)))
+    out = {}
+    wl = inputs.WORKLOADS[EXTRA_DECODE]
+    value, ms, roof, _, _ = bench_decode(short, wl)
+    out["decode"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": short.steps,
+                     "kernel": roof["kernel"], "kernel_avg_us": roof["kernel_avg_us"],
+                     "hbm_achieved_GBps": roof["achieved"], "hbm_frac": roof["frac"], "traffic": roof["traffic"],
+                     "alg_bytes_per_launch": roof["alg_bytes_per_launch"]}
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wl = inputs.WORKLOADS[EXTRA_FAVOR]
+    value, ms, roof, ex, _ = bench_forward(short, wl)
+    kern_s = roof["kernel_avg_us"] * 1e-6
+    flops = forward_alg_flops(wl)
+    out["favor"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": short.steps,
+                    "kernel": roof["kernel"], "kernel_avg_us": roof["kernel_avg_us"],
+                    "alg_flops_per_launch": flops,
+                    "mfma_achieved_TFs": flops / kern_s / 1e12,
+                    "mfma_frac": flops / kern_s / (MFMA_BF16_PEAK_TFS * 1e12),
+                    "hbm_frac": roof["alg_bytes_per_launch"] / kern_s / (HBM_PEAK_GBS * 1e9),
+                    "traffic": roof["traffic"]}
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -775,6 +818,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget; 0 skips it")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode and FAVOR+ figures measured after the default workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard over "
@@ -805,7 +850,7 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         if wl.decode_steps:
-            cpu = run_cpu_baseline_decode(wl, fi, args.cpu_seconds)
+            cpu = run_cpu_baseline_decode(wl, args.cpu_seconds)
         elif wl.backward:
             cpu = run_cpu_baseline_backward(wl, fi[0], fi[1], args.cpu_seconds)
         elif wl.gated:
@@ -822,6 +867,11 @@ def main():
         config["decay_per_head"] = [float(x) for x in wl.gammas()]
     if wl.decode_steps:
         config.update({"prefix": wl.N, "decode_steps_cycled": wl.decode_steps})
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extras:
+        # the headline metric: causal forward tokens/s with its matrix-core
+        # fraction, decode tokens/s with its HBM fraction (under extra)
+        extra.update(measure_extras(args))
+        metric = "causal linear-attn fwd tokens/s (B\u00b7H\u00b7N/s) + % MFMA peak; decode tokens/s + % HBM BW"
     line = {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded i.i.d. Gaussian)",

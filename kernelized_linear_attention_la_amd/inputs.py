@@ -86,7 +86,7 @@ def _slice_draw(key, n):
     return rng.standard_normal(n)
 
 
-def _fill_slices(shm_name, shape, key_prefix, scale, lo, hi):
+def _fill_slices(shm_name, shape, key_prefix, scale, lo, hi, b0=0):
     """Worker body: draw slices [lo, hi) into a shared fp32 buffer."""
     from multiprocessing import resource_tracker, shared_memory
     shm = shared_memory.SharedMemory(name=shm_name)
@@ -98,20 +98,21 @@ def _fill_slices(shm_name, shape, key_prefix, scale, lo, hi):
         H = shape[1]
         for s in range(lo, hi):
             b, h = divmod(s, H)
-            flat[s] = (_slice_draw(tuple(key_prefix) + (b, h), per) * scale).astype(np.float32)
+            flat[s] = (_slice_draw(tuple(key_prefix) + (b0 + b, h), per) * scale).astype(np.float32)
     finally:
         shm.close()
 
 
 def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: str,
-                extra=(), workers: int | None = None, offset=0.0) -> HostTensor:
+                extra=(), workers: int | None = None, offset=0.0, b0: int = 0) -> HostTensor:
     """Seeded N(offset, scale^2) tensor of shape [B, H, n, d] (n may be 1).
 
     Slice (b, h) depends only on (workload_id, tensor_id, *extra, b, h), so any
     slice can be regenerated on its own.  Large tensors are drawn in a small
     pool of spawned worker processes; the values do not depend on the pool.
     offset (a number, or an array broadcast against [B, H, n, d]) is added in
-    fp64 before the rounding (serial draws only).
+    fp64 before the rounding (serial draws only).  b0: the first batch index
+    of the block drawn (rows b0 .. b0 + B - 1 of a larger batch, same values).
     """
     B, H = shape[0], shape[1]
     per = int(np.prod(shape[2:]))
@@ -126,7 +127,7 @@ def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: st
         out = np.empty((B * H, per), dtype=np.float64)
         for s in range(B * H):
             b, h = divmod(s, H)
-            out[s] = _slice_draw(key_prefix + (b, h), per)
+            out[s] = _slice_draw(key_prefix + (b0 + b, h), per)
         out *= scale
         out = out.reshape(shape)
         if has_offset:
@@ -148,7 +149,7 @@ def normal_bhnd(workload_id: int, tensor_id: int, shape, scale: float, dtype: st
         env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""),
                    OMP_NUM_THREADS="1")
         for lo in range(0, nsl, step):
-            job = json.dumps([shm.name, list(shape), list(key_prefix), scale, lo, min(nsl, lo + step)])
+            job = json.dumps([shm.name, list(shape), list(key_prefix), scale, lo, min(nsl, lo + step), b0])
             procs.append(subprocess.Popen([sys.executable, "-m", "kernelized_linear_attention_la_amd.inputs", job],
                                           env=env))
         codes = [p.wait() for p in procs]
@@ -287,14 +288,17 @@ class ForwardInputs:
     W: np.ndarray | None = None  # fp32 [m, dk] for FAVOR+
 
 
-def forward_inputs(wl: Workload, N: int | None = None, workers=None) -> ForwardInputs:
-    """Q, K, V of a forward workload (optionally a shorter prefix length N)."""
+def forward_inputs(wl: Workload, N: int | None = None, workers=None, batch=None) -> ForwardInputs:
+    """Q, K, V of a forward workload (optionally a shorter prefix length N;
+    optionally only the batch rows range(*batch), the same values as those
+    rows of the whole draw)."""
     n = wl.N if N is None else N
-    shp_k = (wl.B, wl.H, n, wl.dk)
-    shp_v = (wl.B, wl.H, n, wl.dv)
-    Q = normal_bhnd(wl.wid, TENSOR_Q, shp_k, wl.scale, wl.dtype, workers=workers)
-    K = normal_bhnd(wl.wid, TENSOR_K, shp_k, wl.scale, wl.dtype, workers=workers)
-    V = normal_bhnd(wl.wid, TENSOR_V, shp_v, wl.scale, wl.dtype, workers=workers)
+    b0, b1 = (0, wl.B) if batch is None else batch
+    shp_k = (b1 - b0, wl.H, n, wl.dk)
+    shp_v = (b1 - b0, wl.H, n, wl.dv)
+    Q = normal_bhnd(wl.wid, TENSOR_Q, shp_k, wl.scale, wl.dtype, workers=workers, b0=b0)
+    K = normal_bhnd(wl.wid, TENSOR_K, shp_k, wl.scale, wl.dtype, workers=workers, b0=b0)
+    V = normal_bhnd(wl.wid, TENSOR_V, shp_v, wl.scale, wl.dtype, workers=workers, b0=b0)
     W = None
     if wl.phi == "favor":
         W = orthogonal_gaussian_rows(wl.wid, wl.m, wl.dk)
@@ -394,4 +398,4 @@ if __name__ == "__main__":
     import json
     import sys
     _a = json.loads(sys.argv[1])
-    _fill_slices(_a[0], tuple(_a[1]), tuple(_a[2]), _a[3], _a[4], _a[5])
+    _fill_slices(_a[0], tuple(_a[1]), tuple(_a[2]), _a[3], _a[4], _a[5], _a[6] if len(_a) > 6 else 0)
