@@ -296,6 +296,8 @@ def kernel_symbol(wl, slot):
             return "k_favor"  # eight waves per workgroup, two per SIMD
         res = seg <= 4 and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and wl.phi in ("elu1", "identity")
         return f"k_mfma<{wl.dk}, {wl.dv}, {tile_chunk(wl)}, {phi_id}, {4 if res else 3}>"
+    if wl.dtype == "f32" and wl.phi == "elu1" and not wl.retention and wl.dk == wl.dv and wl.dk in (64, 128):
+        return f"k_f32mma<{wl.dk}, {mode}>"  # fp32 storage on fp32 matrix instructions
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"
 
 
@@ -427,7 +429,12 @@ def bench_forward(args, wl):
     flop_per_byte = alg_flops / alg_bytes
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
     kname = kernel_symbol(wl, "chunk")
-    if kname.startswith("k_generic"):
+    if kname.startswith("k_f32mma"):
+        # fp32 storage: fp32 arithmetic on the matrix cores, against the dense fp32 MFMA peak
+        ach = alg_flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_F32_PEAK_TFS, "traffic": None}
+    elif kname.startswith("k_generic"):
         # fp32-arithmetic kernels: against the fp32 vector ALUs
         ach = alg_flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": ach, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
@@ -731,12 +738,20 @@ def bench_decode(args, wl):
     # the prefix (not timed), drawn and run a block of sequences at a time:
     # every (sequence, head) slice is independent and its values do not
     # depend on the block
+    hev = HipEvents(la.lib())
+    prefix_ms = 0.0
+    raw = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for b0 in range(0, wl.B, PREFIX_BLOCK):
         b1 = min(wl.B, b0 + PREFIX_BLOCK)
         fb = inputs.forward_inputs(wl, batch=(b0, b1))
         q, k, v = to_dev(fb.Q), to_dev(fb.K), to_dev(fb.V)
+        e0, e1 = hev.create(), hev.create()
+        hev.record(e0, raw)
         la.la_forward_causal_chunked(q, k, v, wl.chunk, S_out=S[b0:b1], z_out=z[b0:b1])
-        torch.cuda.synchronize()
+        hev.record(e1, raw)
+        prefix_ms += hev.elapsed_ms(e0, e1)  # synchronises on e1
+        hev.destroy(e0)
+        hev.destroy(e1)
         del q, k, v, fb
     steps_in = []
     for s in range(wl.decode_steps):
@@ -753,7 +768,6 @@ def bench_decode(args, wl):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    hev = HipEvents(la.lib())
     ev_pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -775,7 +789,11 @@ def bench_decode(args, wl):
     roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
             "traffic": stored_traffic(wl, kname), "kernel": kname, "kernel_avg_us": kern_ms * 1e3,
             "alg_bytes_per_launch": nbytes, "timing": "hip events around each launch"}
-    extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3)}
+    extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3),
+             # the state-building prefix (not part of the step): fp32 causal forward over every
+             # sequence, summed over the blocks it is run in, timed by HIP events around each call
+             "prefix_forward_ms": prefix_ms,
+             "prefix_forward_kernel": kernel_symbol(wl, "chunk")}
     return value, ms_per_step, roof, extra, None
 
 
@@ -788,8 +806,9 @@ def measure_extras(args):
     short = argparse.Namespace(steps=max(1, min(args.steps, 20)), warmup=max(1, min(args.warmup, 5)))
     out = {}
     wl = inputs.WORKLOADS[EXTRA_DECODE]
-    value, ms, roof, _, _ = bench_decode(short, wl)
+    value, ms, roof, dex, _ = bench_decode(short, wl)
     out["decode"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": short.steps,
+                     "prefix_forward_ms": dex["prefix_forward_ms"], "prefix_forward_kernel": dex["prefix_forward_kernel"],
                      "kernel": roof["kernel"], "kernel_avg_us": roof["kernel_avg_us"],
                      "hbm_achieved_GBps": roof["achieved"], "hbm_frac": roof["frac"], "traffic": roof["traffic"],
                      "alg_bytes_per_launch": roof["alg_bytes_per_launch"]}

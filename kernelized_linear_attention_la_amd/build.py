@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "liblinattn.so")
 SOURCES = ["la_api.hip", "la_generic.hip", "la_decode.hip", "la_mfma.hip", "la_mfma_seg.hip", "la_backward.hip", "la_backward_mfma.hip",
-           "la_gated.hip", "la_gla_chunk.hip", "la_favor.hip", "la_delta_chunk.hip"]
+           "la_gated.hip", "la_gla_chunk.hip", "la_favor.hip", "la_delta_chunk.hip", "la_f32mma.hip"]
 ARCH = "gfx950"
 
 
@@ -45,6 +45,15 @@ def _compile(src: str, extra) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+def device_asm(src: str, extra=()) -> str:
+    """The gfx950 assembly text of one source, compiled with the library's flags."""
+    cmd = [hipcc()] + compile_flags() + list(extra) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{' '.join(cmd)}\n{r.stderr}")
+    return r.stdout
 
 
 def build(extra_flags=(), verbose: bool = False) -> str:
@@ -73,6 +82,7 @@ KERNEL_SOURCES = {
     "k_favor": ("la_favor.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_seg": ("la_mfma_seg.hip", "la_mfma_ops.h", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_generic": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_f32mma": ("la_f32mma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_scan": ("la_generic.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_decode": ("la_decode.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dq": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),

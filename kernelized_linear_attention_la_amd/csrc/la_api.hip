@@ -101,7 +101,10 @@ Segments plan_segments(const Shape &sh, int chunk, int columns_per_slice, int mi
     return g;
 }
 
-int generic_columns(const Shape &sh) { return (sh.dv + 31) / 32; }
+// Workgroups per (slice, segment) on the fp32-arithmetic path: one 32-column
+// value slab each on the FMA kernels; the fp32 matrix-instruction kernel
+// covers every column in one workgroup.
+int generic_columns(const Shape &sh) { return f32mma_supported(sh) ? 1 : (sh.dv + 31) / 32; }
 
 // The projected and widened maps on the matrix cores (FAVOR+, DPFP, cos/sin,
 // cosFormer) tile 64 tokens: at m = 256 a 128-token tile of phi(K) and

@@ -414,6 +414,7 @@ __global__ void k_ws_error(uint32_t *ctl, uint32_t *out, int clear) {
 size_t generic_lds_bytes(int dk, int dp) { return sizeof(float) * (size_t)gen_layout(dk, dp).total; }
 
 hipError_t launch_generic(const FwdArgs &a, hipStream_t stream, KEvents ev) {
+    if (f32mma_supported(a.sh)) return launch_f32mma(a, stream, ev);
     const int nslab = (a.sh.dv + kVS - 1) / kVS;
     const size_t grid = (size_t)a.sh.BH * a.sg.P * nslab;
     const size_t lds = generic_lds_bytes(a.sh.dk, a.sh.dp);

@@ -138,6 +138,11 @@ hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_ws_error(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t stream);
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v, void *o,
                          float *S, float *z, hipStream_t stream);
+// fp32 storage on fp32 matrix instructions (la_f32mma.hip): ELU+1,
+// normalised, d_k = d_v in {64, 128}; one workgroup per (slice, segment)
+// covers every value column.  launch_generic takes it where it applies.
+bool f32mma_supported(const Shape &sh);
+hipError_t launch_f32mma(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 // bf16 MFMA path; returns hipErrorNotSupported when the shape has no MFMA variant.
 hipError_t launch_mfma(const FwdArgs &a, hipStream_t stream, KEvents ev = {});
 bool mfma_supported(const Shape &sh, int chunk);
