@@ -100,10 +100,10 @@ def backward_alg_flops(wl, kernel):
         carry 2 d' a;
     FAVOR+ adds the projection 2 d_k m per recomputed row (q in the first pass,
     k in both) and its Jacobian 2 d_k m + 2 m per row.  C is the chunk length
-    the kernels tile: the request on the matrix cores, at most 16 tokens on the
-    fp32-arithmetic kernels.
+    the kernels tile: 64 (d 64) or 32 (d 128) tokens on the matrix cores, at
+    most 16 tokens on the fp32-arithmetic kernels.
     """
-    C, dp, dv, dk = (wl.chunk if backward_on_mfma(wl) else min(wl.chunk, 16)), wl.dprime, wl.dv, wl.dk
+    C, dp, dv, dk = backward_tile(wl), wl.dprime, wl.dv, wl.dk
     a = dv + 1
     if kernel == "dq":
         per = 8 * dp * a + 2 * (C + 1) * (dp + a)
@@ -238,8 +238,18 @@ def run_cpu_baseline_decode(wl, seconds):
 
 def backward_on_mfma(wl):
     """The library runs the backward's two passes on fp32 matrix instructions
-    for bf16 ELU+1 with d_k = d_v = 64 and 64-token chunks."""
-    return wl.dtype == "bf16" and wl.phi == "elu1" and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64
+    for bf16 ELU+1 with d_k = d_v = 64 and 64-token chunks, or d_k = d_v = 128
+    and chunks of a multiple of 32 tokens (run on 32-token tiles)."""
+    if wl.dtype != "bf16" or wl.phi != "elu1" or wl.dk != wl.dv:
+        return False
+    return (wl.dk == 64 and wl.chunk == 64) or (wl.dk == 128 and wl.chunk % 32 == 0)
+
+
+def backward_tile(wl):
+    """Tokens per tile of the backward kernels that run this workload."""
+    if backward_on_mfma(wl):
+        return 64 if wl.dk == 64 else 32
+    return min(wl.chunk, 16)
 
 
 def gla_on_chunks(wl):
@@ -256,7 +266,7 @@ def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
         if backward_on_mfma(wl) and slot in ("dq", "dkv"):
-            return f"k_bwd_{slot}_mfma"
+            return f"k_bwd_{slot}_mfma<{wl.dk}, {backward_tile(wl)}>"
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.gated:
         t = "float" if wl.dtype == "f32" else "unsigned short"

@@ -505,7 +505,7 @@ constexpr int kBwdFp32Chunk = 16;
 
 Segments backward_plan(const Shape &sh, int chunk) {
     // matrix-core kernels: one workgroup per CU; fp32 kernels: several
-    if (backward_mfma_supported(sh, chunk)) return plan_segments(sh, chunk, 1, 1, kMfmaWorkgroups);
+    if (backward_mfma_supported(sh, chunk)) return plan_segments(sh, backward_mfma_tile(sh), 1, 1, kMfmaWorkgroups);
     return plan_segments(sh, chunk < kBwdFp32Chunk ? chunk : kBwdFp32Chunk, 1, 1, kTargetWorkgroups);
 }
 
@@ -517,7 +517,7 @@ BwdWs bwd_ws(const Shape &sh, const Segments &g) {
     w.u_off = w.z_off + round_up(sizeof(float) * bh * g.P * dp, kAlign);
     w.g_off = w.u_off + round_up(sizeof(float) * bh * g.P * dp * (dv + 1), kAlign);
     // G_aug per token: fp32 [d_v + 1] (fp32-FMA kernels) or fp32 [backward_mfma_g_floats()] (matrix cores)
-    const size_t g_row = sizeof(float) * (backward_mfma_supported(sh, g.chunk) ? backward_mfma_g_floats() : dv + 1);
+    const size_t g_row = sizeof(float) * (backward_mfma_supported(sh, g.chunk) ? backward_mfma_g_floats(sh) : dv + 1);
     w.total = w.g_off + round_up(g_row * bh * sh.N, kAlign);
     return w;
 }
@@ -569,12 +569,13 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
         for (int i = 0; i < LA_BSLOTS; ++i) ev->launched[i] = 0;
 
     // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan.
-    // Behind the fp32 kernels the sums run on the matrix-core state pass when
-    // the segments are whole chunks of a length it takes (same boundaries, same P).
+    // The sums run on the matrix-core state pass when the segments are whole
+    // chunks of a length it takes (same boundaries, same P): the backward's own
+    // tile, else 128 or 64 tokens.
     const bool mf = backward_mfma_supported(sh, chunk);
     Segments gs = g;
-    bool sums_mf = mf;
-    if (!mf)
+    bool sums_mf = mfma_supported(sh, g.chunk);
+    if (!sums_mf)
         for (int c2 : {128, 64})
             if (!sums_mf && (g.seg_chunks * g.chunk) % c2 == 0 && mfma_supported(sh, c2)) {
                 gs.chunk = c2;
@@ -593,7 +594,7 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
         return LA_ERR_DEVICE;
     if (mf) {
         BwdMfmaArgs m;
-        m.BH = sh.BH; m.N = sh.N; m.P = g.P; m.seg_chunks = g.seg_chunks; m.n_chunks = g.n_chunks;
+        m.D = sh.dk; m.BH = sh.BH; m.N = sh.N; m.P = g.P; m.seg_chunks = g.seg_chunks; m.n_chunks = g.n_chunks;
         m.Q = static_cast<const uint16_t *>(Q); m.K = static_cast<const uint16_t *>(K);
         m.V = static_cast<const uint16_t *>(V); m.dO = static_cast<const uint16_t *>(dO);
         m.dQ = static_cast<uint16_t *>(dQ); m.dK = static_cast<uint16_t *>(dK); m.dV = static_cast<uint16_t *>(dV);

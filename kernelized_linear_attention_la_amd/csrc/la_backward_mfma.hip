@@ -1,7 +1,10 @@
 // Backward of the causal normalised form on the matrix cores: ELU+1,
-// d_k = d_v = 64, 64-token chunks, bf16 storage (the derivation and the
-// fp32-FMA kernels are in la_backward.hip; this file runs the same chunked
-// algebra with v_mfma_f32_16x16x4_f32).
+// d_k = d_v = D, bf16 storage, D = 64 on 64-token tiles and D = 128 on
+// 32-token tiles (the derivation and the fp32-FMA kernels are in
+// la_backward.hip; this file runs the same chunked algebra with
+// v_mfma_f32_16x16x4_f32; the chunkwise form gives the same gradients for
+// every chunk length, so a D = 128 call asking for 64- or 128-token chunks
+// runs on 32-token tiles).
 //
 // The arithmetic stays fp32 throughout: the normalised backward cancels
 // (g_i . v_j + h_i = g_i . (v_j - o_i), and o_i, h_i come from the recomputed
@@ -11,13 +14,19 @@
 // C[4(l/16)+e][l%16]; both operands are single fp32 values, so either
 // orientation of a tile is read straight from its one row-major copy in LDS.
 // Per chunk the tiles are phi(Q), phi(K), [V | 1 | 0], G_aug, the carried
-// state image and a score tile; value-column widths are padded to 68 for
-// contractions and 80 (five 16-column blocks) for outputs.
+// state image and a score tile; value-column widths are padded to D + 4 for
+// contractions and D + 16 (whole 16-column blocks) for outputs.
 //
-// Per chunk, wave w owns query rows 16w..16w+15 (dQ pass) or key rows
-// (dK/dV pass) for the row products, and feature rows 16w..16w+15 of the
-// carried states (S_aug, U in the dQ pass; R_aug in the dK/dV pass), kept in
-// fp32 accumulators and mirrored into LDS for the products that read them.
+// Four waves.  The row products of a chunk (scores, num, dphi(Q); dphi(K),
+// dV) are split over (16-row block, column split): with 64-token tiles each
+// wave owns one row block and every column, with 32-token tiles the two
+// waves of a row block share its columns and exchange the row statistics of
+// G_aug (normaliser, dO . o) through LDS.  Wave w also owns feature rows
+// 16 (4q + w) .. +15 of the carried states (S_aug, U in the dQ pass; R_aug in
+// the dK/dV pass), kept in fp32 accumulators and mirrored into LDS for the
+// products that read them.
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -36,15 +45,40 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-constexpr int kD = 64;          // d_k = d_v = d'
-constexpr int kC = 64;          // tokens per chunk
-constexpr int kVK = 68;         // value columns in contractions (v | 1 | 0 0 0)
-constexpr int kVN = 80;         // value columns in outputs (five 16-column blocks)
-constexpr int kNW = 4;          // waves
+constexpr int kNW = 4;  // waves
 constexpr int kThreads = 64 * kNW;
-constexpr int kR64 = 64 + 4;    // row stride of 64-wide tiles (floats)
-constexpr int kRV = kVN + 4;    // row stride of value-wide tiles
-constexpr int kGW = kVK;        // G_aug floats per token in the workspace
+
+template <int D, int C>
+struct BCfg {
+    static constexpr int RB = C / 16;               // 16-row blocks of a tile
+    static constexpr int CS = kNW / RB;             // waves sharing a row block (column splits)
+    static constexpr int VK = D + 4;                // value columns in contractions (v | 1 | 0 0 0)
+    static constexpr int NVB = D / 16 + 1;          // 16-column blocks of [v | 1 | 0..] in outputs
+    static constexpr int NDB = D / 16;              // 16-column blocks of d-wide outputs
+    static constexpr int RX = D + 4;                // row stride of the phi tiles (floats)
+    static constexpr int RV = 16 * NVB + 4;         // row stride of value-wide tiles
+    static constexpr int RW = C + 4;                // row stride of the score tile
+    static constexpr int FBW = D / 16 / kNW;        // 16-row feature blocks of a carried state per wave
+    static constexpr int NSB = RB / CS;             // 16-key score blocks per wave
+    static constexpr int NDW = NDB / CS;            // d-wide output blocks per wave
+    static constexpr int NV0 = (NVB + CS - 1) / CS; // value blocks of split 0 (split 1: the rest)
+    static constexpr bool STAGE = RW >= D;          // d-wide rows leave through the score tile
+    static_assert(RB * CS == kNW && RB % CS == 0 && NDB % CS == 0 && FBW >= 1, "wave split");
+    static_assert(CS <= 2 && (!STAGE || CS == 1), "one or two column splits");
+};
+
+template <int D, int C>
+struct BTiles {
+    using B = BCfg<D, C>;
+    float P[C * B::RX];    // phi(Q) rows [token][feature]
+    float K[C * B::RX];    // phi(K) rows
+    float V[C * B::RV];    // [v | 1 | 0] rows
+    float G[C * B::RV];    // G_aug rows [token][value column]
+    float S[D * B::RV];    // carried state, rows [feature][value column]
+    float W[C * B::RW];    // masked scores of the tile
+    float DEN[C];          // normaliser of each query row (dQ pass)
+    float DOT[B::CS][C];   // dO . num of each query row over one column split
+};
 
 // C[16 rows at m0][16 NB columns at n0] += A B over K (a multiple of 4).
 // TA: A is given as its transpose (row-major [k][m]); TB: B as its transpose ([n][k]).
@@ -72,72 +106,75 @@ __device__ __forceinline__ void put_rows(float *T, int ld, int m0, int n0, f32x4
 
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
-struct Tiles {
-    float P[kC * kR64];  // phi(Q) rows [token][feature]
-    float K[kC * kR64];  // phi(K) rows
-    float V[kC * kRV];   // [v | 1 | 0] rows
-    float G[kC * kRV];   // G_aug rows [token][value column]
-    float S[kD * kRV];   // carried state, rows [feature][value column]
-    float W[kC * kR64];  // masked scores, rows of the owning wave
-};
-
-// phi(X) rows t0.. of one chunk (rows past `rows` are zero)
+// phi(X) rows t0.. of one tile (rows past `rows` are zero)
+template <int D, int C>
 __device__ void stage_phi(const uint16_t *X, int t0, int rows, float *R, int tid) {
+    constexpr int RX = BCfg<D, C>::RX;
 #pragma unroll
-    for (int i = 0; i < kC * kD / 8 / kThreads; ++i) {
-        const int u = tid + i * kThreads, t = u / (kD / 8), c8 = u % (kD / 8);
+    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+        const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
         uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < rows) x = *reinterpret_cast<const uint4 *>(&X[(size_t)(t0 + t) * kD + 8 * c8]);
+        if (t < rows) x = *reinterpret_cast<const uint4 *>(&X[(size_t)(t0 + t) * D + 8 * c8]);
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
         float4 a, b;
         a.x = elu1(lo_bf16(w[0])); a.y = elu1(hi_bf16(w[0])); a.z = elu1(lo_bf16(w[1])); a.w = elu1(hi_bf16(w[1]));
         b.x = elu1(lo_bf16(w[2])); b.y = elu1(hi_bf16(w[2])); b.z = elu1(lo_bf16(w[3])); b.w = elu1(hi_bf16(w[3]));
         if (t >= rows) a = b = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4 *>(&R[t * kR64 + 8 * c8]) = a;
-        *reinterpret_cast<float4 *>(&R[t * kR64 + 8 * c8 + 4]) = b;
+        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8]) = a;
+        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8 + 4]) = b;
     }
 }
 
-// [v | 1 | 0] rows of one chunk (columns 64..kRV-1 written too)
+// [v | 1 | 0] rows of one tile (columns D..RV-1 written too)
+template <int D, int C>
 __device__ void stage_vaug(const uint16_t *V, int t0, int rows, float *R, int tid) {
+    constexpr int RV = BCfg<D, C>::RV;
 #pragma unroll
-    for (int i = 0; i < kC * kD / 8 / kThreads; ++i) {
-        const int u = tid + i * kThreads, t = u / (kD / 8), c8 = u % (kD / 8);
+    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+        const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
         uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < rows) x = *reinterpret_cast<const uint4 *>(&V[(size_t)(t0 + t) * kD + 8 * c8]);
-        *reinterpret_cast<float4 *>(&R[t * kRV + 8 * c8]) =
+        if (t < rows) x = *reinterpret_cast<const uint4 *>(&V[(size_t)(t0 + t) * D + 8 * c8]);
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8]) =
             make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
-        *reinterpret_cast<float4 *>(&R[t * kRV + 8 * c8 + 4]) =
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8 + 4]) =
             make_float4(lo_bf16(x.z), hi_bf16(x.z), lo_bf16(x.w), hi_bf16(x.w));
     }
-    for (int u = tid; u < kC * (kRV - kD); u += kThreads) {
-        const int t = u / (kRV - kD), c = kD + u % (kRV - kD);
-        R[t * kRV + c] = (c == kD && t < rows) ? 1.f : 0.f;
+    for (int u = tid; u < C * (RV - D); u += kThreads) {
+        const int t = u / (RV - D), c = D + u % (RV - D);
+        R[t * RV + c] = (c == D && t < rows) ? 1.f : 0.f;
     }
 }
 
-// G_aug rows (fp32 in the workspace, kGW per token) of one chunk
+// G_aug rows (fp32 in the workspace, VK per token) of one tile
+template <int D, int C>
 __device__ void stage_g(const float *Gw, int t0, int rows, float *R, int tid) {
-    for (int u = tid; u < kC * kRV / 4; u += kThreads) {
-        const int t = u / (kRV / 4), c4 = u % (kRV / 4);
+    constexpr int RV = BCfg<D, C>::RV, VK = BCfg<D, C>::VK;
+    for (int u = tid; u < C * RV / 4; u += kThreads) {
+        const int t = u / (RV / 4), c4 = u % (RV / 4);
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < rows && 4 * c4 < kGW) x = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + t) * kGW + 4 * c4]);
-        *reinterpret_cast<float4 *>(&R[t * kRV + 4 * c4]) = x;
+        if (t < rows && 4 * c4 < VK) x = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + t) * VK + 4 * c4]);
+        *reinterpret_cast<float4 *>(&R[t * RV + 4 * c4]) = x;
     }
 }
 
-// this wave's 16 feature rows of a carried state (5 accumulator blocks) into the LDS image
-__device__ __forceinline__ void put_state(const f32x4 (&S)[5], float *T, int w, int lane) {
+// this wave's feature rows of a carried state into the LDS image
+template <int D, int C>
+__device__ __forceinline__ void put_state(const f32x4 (&S)[BCfg<D, C>::FBW][BCfg<D, C>::NVB], float *T, int w,
+                                          int lane) {
+    using B = BCfg<D, C>;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) put_rows(T, kRV, 16 * w, 16 * j, S[j], lane);
+    for (int q = 0; q < B::FBW; ++q)
+#pragma unroll
+        for (int j = 0; j < B::NVB; ++j) put_rows(T, B::RV, 16 * (kNW * q + w), 16 * j, S[q][j], lane);
 }
 
+// 16 rows x D columns of T (rows m0..) -> bf16 rows of dst, 16 bytes per lane
+template <int D>
 __device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int rows, uint16_t *dst, size_t row0,
                                            int lane) {
-    // 16 rows x 64 columns of T (rows m0..) -> bf16 rows of dst, 16 bytes per lane
 #pragma unroll
-    for (int it = 0; it < 16 * kD / 8 / 64; ++it) {
-        const int idx = it * 64 + lane, r = idx / (kD / 8), c8 = idx % (kD / 8);
+    for (int it = 0; it < 16 * D / 8 / 64; ++it) {
+        const int idx = it * 64 + lane, r = idx / (D / 8), c8 = idx % (D / 8);
         if (m0 + r < rows) {
             const float *s = &T[(m0 + r) * ld + 8 * c8];
             uint4 o;
@@ -145,13 +182,53 @@ __device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int r
             o.y = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
             o.z = f32_to_bf16(s[4]) | (static_cast<uint32_t>(f32_to_bf16(s[5])) << 16);
             o.w = f32_to_bf16(s[6]) | (static_cast<uint32_t>(f32_to_bf16(s[7])) << 16);
-            *reinterpret_cast<uint4 *>(&dst[(row0 + m0 + r) * kD + 8 * c8]) = o;
+            *reinterpret_cast<uint4 *>(&dst[(row0 + m0 + r) * D + 8 * c8]) = o;
         }
     }
 }
 
+// accumulator blocks (rows m0 + 4g + e, columns n0 + 16 j + c16) -> bf16 rows of dst
+template <int D, int NB>
+__device__ __forceinline__ void store_acc(const f32x4 (&v)[NB], int m0, int n0, int rows, uint16_t *dst, size_t row0,
+                                          int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = m0 + 4 * g + e;
+            if (r < rows) dst[(row0 + r) * D + n0 + 16 * j + c] = f32_to_bf16(v[j][e]);
+        }
+}
+
+// d-wide row blocks of this wave to dst: through the score tile (one column
+// split: the wave's own rows of W) or straight from the accumulators
+template <int D, int C>
+__device__ __forceinline__ void store_dwide(const f32x4 (&v)[BCfg<D, C>::NDW], float *W, int m0, int cs, int rows,
+                                            uint16_t *dst, size_t row0, int lane) {
+    using B = BCfg<D, C>;
+    if constexpr (B::STAGE) {
+        wave_lds_sync();  // every lane has read this wave's rows of W
+#pragma unroll
+        for (int j = 0; j < B::NDW; ++j) put_rows(W, B::RW, m0, 16 * j, v[j], lane);
+        wave_lds_sync();
+        store_rows<D>(W, B::RW, m0, rows, dst, row0, lane);
+    } else {
+        store_acc<D, B::NDW>(v, m0, 16 * cs * B::NDW, rows, dst, row0, lane);
+    }
+}
+
+// the row products of a row block are shared by its column splits
+template <int CS>
+__device__ __forceinline__ void row_sync() {
+    if constexpr (CS == 1)
+        wave_lds_sync();
+    else
+        block_sync_lds();
+}
+
 // ---------------------------------------------------------------------------
-// dQ pass.  Chunks in order from the forward prefix [S | z] of the segment:
+// dQ pass.  Tiles in order from the forward prefix [S | z] of the segment:
 //   num_aug = (P (.) M) V_aug + phi(Q) S_aug          P = phi(Q) phi(K)^T
 //   G_aug   = [dO / den | -(dO . o) / den | 0]
 //   dphi(Q) = (A (.) M) phi(K) + G_aug S_aug^T        A = G_aug V_aug^T
@@ -159,284 +236,339 @@ __device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int r
 //   U      += phi(Q)^T G_aug    (segment sums for the reverse scan)
 //   S_aug  += phi(K)^T V_aug
 // ---------------------------------------------------------------------------
+template <int D, int C>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
-    __shared__ Tiles sm;
+    using B = BCfg<D, C>;
+    constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
+                  NDW = B::NDW, CS = B::CS, RB = B::RB;
+    __shared__ BTiles<D, C> sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
+    // row block and column split of the row products (one split: the column
+    // offsets stay compile-time constants)
+    const int rb = CS == 1 ? w : w % RB, cs = CS == 1 ? 0 : w / RB;
+    const int m0 = 16 * rb;
     const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
     const int N = a.N;
     const int c_begin = seg * a.seg_chunks, c_end = min(a.n_chunks, c_begin + a.seg_chunks);
-    const uint16_t *Qs = a.Q + (size_t)bh * N * kD;
-    const uint16_t *Ks = a.K + (size_t)bh * N * kD;
-    const uint16_t *Vs = a.V + (size_t)bh * N * kD;
-    const uint16_t *dOs = a.dO + (size_t)bh * N * kD;
-    uint16_t *dQs = a.dQ + (size_t)bh * N * kD;
-    float *Gw = a.G + (size_t)bh * N * kGW;
-    const int m0 = 16 * w;
+    const uint16_t *Qs = a.Q + (size_t)bh * N * D;
+    const uint16_t *Ks = a.K + (size_t)bh * N * D;
+    const uint16_t *Vs = a.V + (size_t)bh * N * D;
+    const uint16_t *dOs = a.dO + (size_t)bh * N * D;
+    uint16_t *dQs = a.dQ + (size_t)bh * N * D;
+    float *Gw = a.G + (size_t)bh * N * VK;
 
-    // carried state S_aug (feature rows 16w.., value columns 16j + c16) and U
-    f32x4 S[5], U[5];
+    // carried state S_aug (feature rows 16 (4q + w) + 4g + e, value columns 16j + c16) and U
+    f32x4 S[FBW][NVB], U[FBW][NVB];
     {
-        const float *Sp = a.Spre + ((size_t)bh * a.P + seg) * kD * kD;
-        const float *zp = a.zpre + ((size_t)bh * a.P + seg) * kD;
+        const float *Sp = a.Spre + ((size_t)bh * a.P + seg) * D * D;
+        const float *zp = a.zpre + ((size_t)bh * a.P + seg) * D;
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
+        for (int q = 0; q < FBW; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int f = m0 + 4 * g + e, col = 16 * j + c16;
-                S[j][e] = col < kD ? Sp[f * kD + col] : (col == kD ? zp[f] : 0.f);
-            }
-            U[j] = zero4();
-        }
-    }
-    put_state(S, sm.S, w, lane);
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const int t0 = c * kC, rows = min(kC, N - t0);
-        block_sync_lds();  // the previous chunk's tiles are consumed, the state image is complete
-        stage_phi(Qs, t0, rows, sm.P, tid);
-        stage_phi(Ks, t0, rows, sm.K, tid);
-        stage_vaug(Vs, t0, rows, sm.V, tid);
-        block_sync_lds();
-
-        // scores P = phi(Q) phi(K)^T of this wave's queries, masked (key <= query)
-        {
-            f32x4 p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = zero4();
-            mm<kD, 4, false, true>(sm.P, kR64, m0, sm.K, kR64, 0, p, lane);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (16 * j + c16 > m0 + 4 * g + e) p[j][e] = 0.f;
-                put_rows(sm.W, kR64, m0, 16 * j, p[j], lane);
-            }
-        }
-        wave_lds_sync();
-        // num_aug = (P (.) M) V_aug + phi(Q) S_aug
-        f32x4 num[5];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) num[j] = zero4();
-        mm<kC, 5, false, false>(sm.W, kR64, m0, sm.V, kRV, 0, num, lane);
-        mm<kD, 5, false, false>(sm.P, kR64, m0, sm.S, kRV, 0, num, lane);
-        // G_aug: den is column 64 (block 4, lane c16 = 0 of each row group)
-        f32x4 gv[5];
-        {
-            float rden[4], dot[4];
-            f32x4 dov[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rden[e] = 1.f / __shfl(num[4][e], lane & 48, 64);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dot[e] = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NVB; ++j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = m0 + 4 * g + e;
-                    const float d = t < rows ? bf16_to_f32(dOs[(size_t)(t0 + t) * kD + 16 * j + c16]) : 0.f;
+                    const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
+                    S[q][j][e] = col < D ? Sp[f * D + col] : (col == D ? zp[f] : 0.f);
+                }
+                U[q][j] = zero4();
+            }
+    }
+    put_state<D, C>(S, sm.S, w, lane);
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * C, rows = min(C, N - t0);
+        block_sync_lds();  // the previous tile's tiles are consumed, the state image is complete
+        stage_phi<D, C>(Qs, t0, rows, sm.P, tid);
+        stage_phi<D, C>(Ks, t0, rows, sm.K, tid);
+        stage_vaug<D, C>(Vs, t0, rows, sm.V, tid);
+        block_sync_lds();
+
+        // scores P = phi(Q) phi(K)^T of this wave's key blocks, masked (key <= query)
+        {
+            f32x4 p[NSB];
+#pragma unroll
+            for (int j = 0; j < NSB; ++j) p[j] = zero4();
+            mm<D, NSB, false, true>(sm.P, RX, m0, sm.K, RX, 16 * cs * NSB, p, lane);
+#pragma unroll
+            for (int j = 0; j < NSB; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * (cs * NSB + j) + c16 > m0 + 4 * g + e) p[j][e] = 0.f;
+                put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), p[j], lane);
+            }
+        }
+        row_sync<CS>();
+        // num_aug = (P (.) M) V_aug + phi(Q) S_aug and G_aug over this wave's value
+        // blocks (a compile-time range: the accumulators keep fixed registers)
+        auto g_aug = [&](auto split) {
+            constexpr int SP = decltype(split)::value;
+            constexpr int NB0 = SP * B::NV0, NBN = SP == 0 ? B::NV0 : NVB - B::NV0;
+            f32x4 num[NBN];
+#pragma unroll
+            for (int j = 0; j < NBN; ++j) num[j] = zero4();
+            mm<C, NBN, false, false>(sm.W, RW, m0, sm.V, RV, 16 * NB0, num, lane);
+            mm<D, NBN, false, false>(sm.P, RX, m0, sm.S, RV, 16 * NB0, num, lane);
+            // dO of this wave's columns and its share of the row sums dO . num
+            f32x4 dov[NBN];
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NBN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = m0 + 4 * g + e, col = 16 * (NB0 + j) + c16;
+                    const float d = (t < rows && col < D) ? bf16_to_f32(dOs[(size_t)(t0 + t) * D + col]) : 0.f;
                     dov[j][e] = d;
-                    dot[e] += d * (num[j][e] * rden[e]);
+                    part[e] += d * num[j][e];
                 }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {  // row sums over the 16 lanes of a row group
-                float x = dot[e];
+                float x = part[e];
                 x += __shfl_xor(x, 1, 64);
                 x += __shfl_xor(x, 2, 64);
                 x += __shfl_xor(x, 4, 64);
                 x += __shfl_xor(x, 8, 64);
-                dot[e] = x;
+                part[e] = x;
             }
+            if (c16 == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.DOT[SP][m0 + 4 * g + e] = part[e];
+                    // the normaliser is column D: column 0 of the last value block
+                    if constexpr (NB0 + NBN == NVB) sm.DEN[m0 + 4 * g + e] = num[NBN - 1][e];
+                }
+            }
+            row_sync<CS>();
+            float rden[4], dot[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool in = m0 + 4 * g + e < rows;
+                const int r = m0 + 4 * g + e;
+                rden[e] = 1.f / sm.DEN[r];
+                float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) gv[j][e] = in ? dov[j][e] * rden[e] : 0.f;
-                gv[4][e] = (c16 == 0 && in) ? -dot[e] * rden[e] : 0.f;
+                for (int k = 0; k < CS; ++k) s += sm.DOT[k][r];
+                dot[e] = s * rden[e];  // dO . o
             }
-        }
 #pragma unroll
-        for (int j = 0; j < 5; ++j) put_rows(sm.G, kRV, m0, 16 * j, gv[j], lane);
-        wave_lds_sync();
-        // G_aug rows to the workspace (kGW floats per token) for the dK/dV pass
-        for (int idx = lane; idx < 16 * kGW / 4; idx += 64) {
-            const int r = idx / (kGW / 4), c4 = idx % (kGW / 4);
+            for (int j = 0; j < NBN; ++j) {
+                f32x4 gv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool in = m0 + 4 * g + e < rows;
+                    const int col = 16 * (NB0 + j) + c16;
+                    gv[e] = !in ? 0.f : (col < D ? dov[j][e] * rden[e] : (col == D ? -dot[e] * rden[e] : 0.f));
+                }
+                put_rows(sm.G, RV, m0, 16 * (NB0 + j), gv, lane);
+            }
+        };
+        if constexpr (CS == 1) {
+            g_aug(std::integral_constant<int, 0>{});
+        } else {
+            if (cs == 0)
+                g_aug(std::integral_constant<int, 0>{});
+            else
+                g_aug(std::integral_constant<int, 1>{});
+        }
+        row_sync<CS>();  // G_aug rows of the row block are complete
+        // G_aug rows to the workspace (VK floats per token) for the dK/dV pass
+        for (int idx = lane + 64 * cs; idx < 16 * VK / 4; idx += 64 * CS) {
+            const int r = idx / (VK / 4), c4 = idx % (VK / 4);
             if (m0 + r < rows)
-                *reinterpret_cast<float4 *>(&Gw[(size_t)(t0 + m0 + r) * kGW + 4 * c4]) =
-                    *reinterpret_cast<const float4 *>(&sm.G[(m0 + r) * kRV + 4 * c4]);
+                *reinterpret_cast<float4 *>(&Gw[(size_t)(t0 + m0 + r) * VK + 4 * c4]) =
+                    *reinterpret_cast<const float4 *>(&sm.G[(m0 + r) * RV + 4 * c4]);
         }
         // A = G_aug V_aug^T, masked; dphi(Q) = (A (.) M) phi(K) + G_aug S_aug^T
         {
-            f32x4 s[4];
+            f32x4 s[NSB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = zero4();
-            mm<kVK, 4, false, true>(sm.G, kRV, m0, sm.V, kRV, 0, s, lane);
-            wave_lds_sync();  // every lane has read the scores P before W is overwritten
+            for (int j = 0; j < NSB; ++j) s[j] = zero4();
+            mm<VK, NSB, false, true>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NSB; ++j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * j + c16 > m0 + 4 * g + e) s[j][e] = 0.f;
-                put_rows(sm.W, kR64, m0, 16 * j, s[j], lane);
+                    if (16 * (cs * NSB + j) + c16 > m0 + 4 * g + e) s[j][e] = 0.f;
+                put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), s[j], lane);
             }
         }
-        wave_lds_sync();
-        f32x4 dp[4];
+        row_sync<CS>();
+        f32x4 dp[NDW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dp[j] = zero4();
-        mm<kC, 4, false, false>(sm.W, kR64, m0, sm.K, kR64, 0, dp, lane);
-        mm<kVK, 4, false, true>(sm.G, kRV, m0, sm.S, kRV, 0, dp, lane);
+        for (int j = 0; j < NDW; ++j) dp[j] = zero4();
+        mm<C, NDW, false, false>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
+        mm<VK, NDW, false, true>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
         // dQ = dphi * min(phi(q), 1) (elu'(q): 1 for q > 0, exp(q) = phi(q) otherwise)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NDW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp[j][e] *= fminf(sm.P[(m0 + 4 * g + e) * kR64 + 16 * j + c16], 1.f);
-        wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) put_rows(sm.W, kR64, m0, 16 * j, dp[j], lane);
-        wave_lds_sync();
-        store_rows(sm.W, kR64, m0, rows, dQs, t0, lane);
+            for (int e = 0; e < 4; ++e)
+                dp[j][e] *= fminf(sm.P[(m0 + 4 * g + e) * RX + 16 * (cs * NDW + j) + c16], 1.f);
+        store_dwide<D, C>(dp, sm.W, m0, cs, rows, dQs, t0, lane);
         block_sync_lds();  // every wave's G_aug rows are in LDS, the state image is read
         // U += phi(Q)^T G_aug, S_aug += phi(K)^T V_aug (this wave's feature rows)
-        mm<kC, 5, true, false>(sm.P, kR64, m0, sm.G, kRV, 0, U, lane);
-        mm<kC, 5, true, false>(sm.K, kR64, m0, sm.V, kRV, 0, S, lane);
-        put_state(S, sm.S, w, lane);
-    }
-    // segment sums U, layout [feature][d_v + 1] (value columns 0..64)
-    float *Us = a.U + ((size_t)bh * a.P + seg) * kD * (kD + 1);
 #pragma unroll
-    for (int j = 0; j < 5; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int f = m0 + 4 * g + e, col = 16 * j + c16;
-            if (col <= kD) Us[f * (kD + 1) + col] = U[j][e];
+        for (int q = 0; q < FBW; ++q) {
+            const int f0 = 16 * (kNW * q + w);
+            mm<C, NVB, true, false>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
+            mm<C, NVB, true, false>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
         }
+        put_state<D, C>(S, sm.S, w, lane);
+    }
+    // segment sums U, layout [feature][d_v + 1] (value columns 0..D)
+    float *Us = a.U + ((size_t)bh * a.P + seg) * D * (D + 1);
+#pragma unroll
+    for (int q = 0; q < FBW; ++q)
+#pragma unroll
+        for (int j = 0; j < NVB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
+                if (col <= D) Us[f * (D + 1) + col] = U[q][j][e];
+            }
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV pass.  Chunks in reverse from R_aug = dS_out_aug + the later
-// segments' sums (key rows j of this wave):
+// dK / dV pass.  Tiles in reverse from R_aug = dS_out_aug + the later
+// segments' sums (key rows of this wave's row block):
 //   dphi(K) = (B (.) M') phi(Q) + V_aug R_aug^T       B = V_aug G_aug^T
 //   dV      = (P' (.) M') G     + phi(K) R            P' = phi(K) phi(Q)^T
 //   (M': query >= key),  dK = dphi(K) * min(phi(k), 1)
 //   R_aug  += phi(Q)^T G_aug
 // ---------------------------------------------------------------------------
+template <int D, int C>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
-    __shared__ Tiles sm;
+    using B = BCfg<D, C>;
+    constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
+                  NDW = B::NDW, CS = B::CS, RB = B::RB;
+    __shared__ BTiles<D, C> sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
+    const int rb = CS == 1 ? w : w % RB, cs = CS == 1 ? 0 : w / RB;
+    const int m0 = 16 * rb;
     const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
     const int N = a.N;
     const int c_begin = seg * a.seg_chunks, c_end = min(a.n_chunks, c_begin + a.seg_chunks);
-    const uint16_t *Qs = a.Q + (size_t)bh * N * kD;
-    const uint16_t *Ks = a.K + (size_t)bh * N * kD;
-    const uint16_t *Vs = a.V + (size_t)bh * N * kD;
-    uint16_t *dKs = a.dK + (size_t)bh * N * kD;
-    uint16_t *dVs = a.dV + (size_t)bh * N * kD;
-    const float *Gw = a.G + (size_t)bh * N * kGW;
-    const int m0 = 16 * w;
+    const uint16_t *Qs = a.Q + (size_t)bh * N * D;
+    const uint16_t *Ks = a.K + (size_t)bh * N * D;
+    const uint16_t *Vs = a.V + (size_t)bh * N * D;
+    uint16_t *dKs = a.dK + (size_t)bh * N * D;
+    uint16_t *dVs = a.dV + (size_t)bh * N * D;
+    const float *Gw = a.G + (size_t)bh * N * VK;
 
-    f32x4 R[5];
+    f32x4 R[FBW][NVB];
     {
-        const float *Rs = a.U + ((size_t)bh * a.P + seg) * kD * (kD + 1);
+        const float *Rs = a.U + ((size_t)bh * a.P + seg) * D * (D + 1);
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int q = 0; q < FBW; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int f = m0 + 4 * g + e, col = 16 * j + c16;
-                R[j][e] = col <= kD ? Rs[f * (kD + 1) + col] : 0.f;
-            }
+            for (int j = 0; j < NVB; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
+                    R[q][j][e] = col <= D ? Rs[f * (D + 1) + col] : 0.f;
+                }
     }
-    put_state(R, sm.S, w, lane);
+    put_state<D, C>(R, sm.S, w, lane);
 
     for (int c = c_end - 1; c >= c_begin; --c) {
-        const int t0 = c * kC, rows = min(kC, N - t0);
+        const int t0 = c * C, rows = min(C, N - t0);
         block_sync_lds();
-        stage_phi(Qs, t0, rows, sm.P, tid);
-        stage_phi(Ks, t0, rows, sm.K, tid);
-        stage_vaug(Vs, t0, rows, sm.V, tid);
-        stage_g(Gw, t0, rows, sm.G, tid);
+        stage_phi<D, C>(Qs, t0, rows, sm.P, tid);
+        stage_phi<D, C>(Ks, t0, rows, sm.K, tid);
+        stage_vaug<D, C>(Vs, t0, rows, sm.V, tid);
+        stage_g<D, C>(Gw, t0, rows, sm.G, tid);
         block_sync_lds();
 
         // dphi(K): B = V_aug G_aug^T masked (query >= key), times phi(Q); + V_aug R_aug^T
-        f32x4 dk[4];
         {
-            f32x4 b[4];
+            f32x4 b[NSB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = zero4();
-            mm<kVK, 4, false, true>(sm.V, kRV, m0, sm.G, kRV, 0, b, lane);
+            for (int j = 0; j < NSB; ++j) b[j] = zero4();
+            mm<VK, NSB, false, true>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NSB; ++j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * j + c16 < m0 + 4 * g + e) b[j][e] = 0.f;
-                put_rows(sm.W, kR64, m0, 16 * j, b[j], lane);
+                    if (16 * (cs * NSB + j) + c16 < m0 + 4 * g + e) b[j][e] = 0.f;
+                put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), b[j], lane);
             }
         }
-        wave_lds_sync();
+        row_sync<CS>();
+        f32x4 dk[NDW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dk[j] = zero4();
-        mm<kC, 4, false, false>(sm.W, kR64, m0, sm.P, kR64, 0, dk, lane);
-        mm<kVK, 4, false, true>(sm.V, kRV, m0, sm.S, kRV, 0, dk, lane);
+        for (int j = 0; j < NDW; ++j) dk[j] = zero4();
+        mm<C, NDW, false, false>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
+        mm<VK, NDW, false, true>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
         // dV: P' = phi(K) phi(Q)^T masked, times G; + phi(K) R
-        f32x4 dv[4];
+        f32x4 dv[NDW];
         {
-            f32x4 p[4];
+            f32x4 p[NSB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = zero4();
-            mm<kD, 4, false, true>(sm.K, kR64, m0, sm.P, kR64, 0, p, lane);
-            wave_lds_sync();  // every lane has read the scores B before W is overwritten
+            for (int j = 0; j < NSB; ++j) p[j] = zero4();
+            mm<D, NSB, false, true>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
+            row_sync<CS>();  // the row block's waves have read the scores B before W is overwritten
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NSB; ++j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * j + c16 < m0 + 4 * g + e) p[j][e] = 0.f;
-                put_rows(sm.W, kR64, m0, 16 * j, p[j], lane);
+                    if (16 * (cs * NSB + j) + c16 < m0 + 4 * g + e) p[j][e] = 0.f;
+                put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), p[j], lane);
             }
         }
-        wave_lds_sync();
+        row_sync<CS>();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dv[j] = zero4();
-        mm<kC, 4, false, false>(sm.W, kR64, m0, sm.G, kRV, 0, dv, lane);
-        mm<kD, 4, false, false>(sm.K, kR64, m0, sm.S, kRV, 0, dv, lane);
-        // dK = dphi(K) * min(phi(k), 1); dK and dV rows leave through W
+        for (int j = 0; j < NDW; ++j) dv[j] = zero4();
+        mm<C, NDW, false, false>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
+        mm<D, NDW, false, false>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
+        // dK = dphi(K) * min(phi(k), 1)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NDW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dk[j][e] *= fminf(sm.K[(m0 + 4 * g + e) * kR64 + 16 * j + c16], 1.f);
-        wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) put_rows(sm.W, kR64, m0, 16 * j, dk[j], lane);
-        wave_lds_sync();
-        store_rows(sm.W, kR64, m0, rows, dKs, t0, lane);
-        wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) put_rows(sm.W, kR64, m0, 16 * j, dv[j], lane);
-        wave_lds_sync();
-        store_rows(sm.W, kR64, m0, rows, dVs, t0, lane);
+            for (int e = 0; e < 4; ++e)
+                dk[j][e] *= fminf(sm.K[(m0 + 4 * g + e) * RX + 16 * (cs * NDW + j) + c16], 1.f);
+        store_dwide<D, C>(dk, sm.W, m0, cs, rows, dKs, t0, lane);
+        store_dwide<D, C>(dv, sm.W, m0, cs, rows, dVs, t0, lane);
         block_sync_lds();  // the state image is no longer read
         // R_aug += phi(Q)^T G_aug (this wave's feature rows)
-        mm<kC, 5, true, false>(sm.P, kR64, m0, sm.G, kRV, 0, R, lane);
-        put_state(R, sm.S, w, lane);
+#pragma unroll
+        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
+        put_state<D, C>(R, sm.S, w, lane);
     }
 }
+
+template <int D, int C>
+constexpr size_t lds_bytes() {
+    return sizeof(BTiles<D, C>);
+}
+static_assert(lds_bytes<64, 64>() <= 160 * 1024 && lds_bytes<128, 32>() <= 160 * 1024, "tiles fit the LDS");
 
 }  // namespace
 
 bool backward_mfma_supported(const Shape &sh, int chunk) {
-    return sh.dtype == kBF16 && sh.phi == kElu1 && sh.dk == kD && sh.dv == kD && chunk == kC;
+    if (sh.dtype != kBF16 || sh.phi != kElu1 || sh.dk != sh.dv) return false;
+    if (sh.dk == 64) return chunk == 64;
+    return sh.dk == 128 && chunk % 32 == 0;  // on 32-token tiles
 }
 
-size_t backward_mfma_g_floats() { return kGW; }
+int backward_mfma_tile(const Shape &sh) { return sh.dk == 128 ? 32 : 64; }
+
+size_t backward_mfma_g_floats(const Shape &sh) { return (size_t)sh.dk + 4; }
 
 hipError_t launch_bwd_dq_mfma(const BwdMfmaArgs &a, hipStream_t st, KEvents ev) {
-    return launch_kernel_ev(k_bwd_dq_mfma, dim3((unsigned)((size_t)a.BH * a.P)), dim3(kThreads), 0, st, ev, a);
+    const dim3 grid((unsigned)((size_t)a.BH * a.P)), block(kThreads);
+    if (a.D == 64) return launch_kernel_ev(k_bwd_dq_mfma<64, 64>, grid, block, 0, st, ev, a);
+    if (a.D == 128) return launch_kernel_ev(k_bwd_dq_mfma<128, 32>, grid, block, 0, st, ev, a);
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_dkv_mfma(const BwdMfmaArgs &a, hipStream_t st, KEvents ev) {
-    return launch_kernel_ev(k_bwd_dkv_mfma, dim3((unsigned)((size_t)a.BH * a.P)), dim3(kThreads), 0, st, ev, a);
+    const dim3 grid((unsigned)((size_t)a.BH * a.P)), block(kThreads);
+    if (a.D == 64) return launch_kernel_ev(k_bwd_dkv_mfma<64, 64>, grid, block, 0, st, ev, a);
+    if (a.D == 128) return launch_kernel_ev(k_bwd_dkv_mfma<128, 32>, grid, block, 0, st, ev, a);
+    return hipErrorNotSupported;
 }
 
 }  // namespace la

@@ -178,15 +178,17 @@ hipError_t launch_bwd_rscan(int BH, int P, int dp, int dv, float *U, const float
 // instructions, ELU+1, d_k = d_v = 64, 64-token chunks.  G holds G_aug as
 // fp32 [BH][N][backward_mfma_g_floats()].
 struct BwdMfmaArgs {
-    int BH, N, P, seg_chunks, n_chunks;
+    int D, BH, N, P, seg_chunks, n_chunks;  // d_k = d_v = D; chunks are backward_mfma_tile() tokens
     const uint16_t *Q, *K, *V, *dO;
     uint16_t *dQ, *dK, *dV;
     const float *Spre, *zpre;  // forward prefix per segment
-    float *U;                  // [BH][P][64 * 65]
+    float *U;                  // [BH][P][D * (D + 1)]
     float *G;                  // [BH][N][backward_mfma_g_floats()]
 };
+// bf16 ELU+1, d_k = d_v = 64 with 64-token chunks, or 128 with chunks of a multiple of 32
 bool backward_mfma_supported(const Shape &sh, int chunk);
-size_t backward_mfma_g_floats();
+int backward_mfma_tile(const Shape &sh);            // tokens per tile: 64 (d 64), 32 (d 128)
+size_t backward_mfma_g_floats(const Shape &sh);     // G_aug floats per token: d_v + 4
 hipError_t launch_bwd_dq_mfma(const BwdMfmaArgs &a, hipStream_t stream, KEvents ev = {});
 hipError_t launch_bwd_dkv_mfma(const BwdMfmaArgs &a, hipStream_t stream, KEvents ev = {});
 

@@ -90,8 +90,12 @@ CASES = [
     (2, 1, 77, 16, 8, "f32", "favor", 24, 32, True),
     (2, 2, 333, 64, 64, "bf16", "elu1", 0, 64, False),
     (1, 2, 190, 64, 64, "bf16", "favor", 256, 64, True),  # largest FAVOR+ feature count
-    (1, 2, 300, 128, 128, "bf16", "elu1", 0, 128, True),  # largest widths
+    (1, 2, 300, 128, 128, "bf16", "elu1", 0, 128, True),  # largest widths (matrix cores, 32-token tiles)
     (1, 1, 517, 128, 96, "f32", "elu1", 0, 16, True),
+    (2, 2, 333, 128, 128, "bf16", "elu1", 0, 32, True),   # d128 matrix cores, ragged tail
+    (1, 3, 1000, 128, 128, "bf16", "elu1", 0, 64, False),
+    (1, 2, 150, 128, 128, "bf16", "elu1", 0, 16, True),   # d128 bf16 on the fp32-arithmetic kernels
+    (1, 1, 17, 128, 128, "bf16", "elu1", 0, 128, True),   # one partial tile
 ]
 
 
@@ -119,6 +123,17 @@ def test_backward_ignores_workspace_contents():
     _say("workspace filled with 0xFF")
     got, ref = _run(5, 2, 2, 200, 64, 64, "f32", "elu1", 0, 64, True, workspace_fill=255)
     _check(got, ref, "f32", "dirty workspace")
+
+
+def test_backward_d128_matrix_cores_many_segments_and_dirty_workspace():
+    # bf16 ELU+1 d128 on the matrix-core kernels: 2 x 4 slices of 4096 tokens
+    # give several segments of 32-token tiles per slice, so the forward sums,
+    # both scans and the segment hand-off of the gradient sums all take part;
+    # the workspace starts as 0xFF bytes (no initial contents are needed)
+    _say("B2 H4 N4096 d128 bf16 chunk 128, state, dirty workspace (slices (0,1), (1,3))")
+    got, ref = _run(9, 2, 4, 4096, 128, 128, "bf16", "elu1", 0, 128, True,
+                    slices=(np.array([[0], [1]]), np.array([[1], [3]])), workspace_fill=255)
+    _check(got, ref, "bf16", "ELU+1 d128 B2H4N4096")
 
 
 def test_backward_mid_size_bf16_workload():
