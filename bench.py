@@ -306,8 +306,10 @@ def kernel_symbol(wl, slot):
             return "k_favor"  # eight waves per workgroup, two per SIMD
         res = seg <= 4 and wl.dk == 64 and wl.dv == 64 and wl.chunk == 64 and wl.phi in ("elu1", "identity")
         return f"k_mfma<{wl.dk}, {wl.dv}, {tile_chunk(wl)}, {phi_id}, {4 if res else 3}>"
-    if wl.dtype == "f32" and wl.phi == "elu1" and not wl.retention and wl.dk == wl.dv and wl.dk in (64, 128):
-        return f"k_f32mma<{wl.dk}, {mode}>"  # fp32 storage on fp32 matrix instructions
+    if (wl.dtype == "f32" and ((wl.phi == "elu1" and not wl.retention) or (wl.phi == "identity" and wl.retention))
+            and wl.dk == wl.dv and wl.dk in (64, 128)):
+        # fp32 storage on fp32 matrix instructions (ELU+1, or retention's identity map)
+        return f"k_f32mma<{wl.dk}, {mode}, {'true' if wl.retention else 'false'}>"
     return f"k_generic<{'float' if wl.dtype == 'f32' else 'unsigned short'}, {mode}>"
 
 

@@ -1,5 +1,6 @@
 // Chunkwise kernels for fp32 storage on fp32 matrix instructions
-// (v_mfma_f32_16x16x4_f32): ELU+1, normalised, d_k = d_v = D in {64, 128}.
+// (v_mfma_f32_16x16x4_f32), d_k = d_v = D in {64, 128}: ELU+1 normalised, or
+// retention (identity map, decay lambda per head, no normaliser).
 //
 // The chunkwise causal form ("Linear Attention", chunkwise parallel form;
 // "Story of Attention Part 5", section 6 blockwise split with decay 1 and the
@@ -24,6 +25,11 @@
 //     mirrored into an LDS image that the next tile's outputs read.
 // Modes as the other chunk kernels: segment sums (kModeState), causal from a
 // prefix state (kModeCausal), non-causal read of a fixed state (kModeRead).
+// Retention ("Story of Attention Part 5", section 4 and the blockwise split of
+// section 6): the scores take lambda^(i-t) inside a tile, the carried state is
+// read with lambda^(i+1) for tile row i, and the state moves on as
+// S <- lambda^L S + sum_t lambda^(L-1-t) k_t v_t^T; the powers come from a
+// table of lambda^0..lambda^32 formed once per workgroup.
 #include <type_traits>
 
 #include "la_device.h"
@@ -38,9 +44,9 @@ constexpr int kFT = 32;       // tokens per tile
 constexpr int kFW4 = 4;       // waves
 constexpr int kFThr = 64 * kFW4;
 
-template <int D>
+template <int D, bool RET>
 struct F32Cfg {
-    static constexpr int NJ = D / 16 + 1;    // value blocks + the normaliser block
+    static constexpr int NJ = D / 16 + (RET ? 0 : 1);  // value blocks (+ the normaliser block)
     // row strides (floats): 2 mod 32 makes the 16-row x 4-column operand reads
     // of phi(Q), phi(K) conflict free; 4 mod 8 puts the two 16-lane halves of a
     // value-row read in opposite halves of the banks
@@ -51,14 +57,15 @@ struct F32Cfg {
     static constexpr int FBW = D / 64;       // 16-row feature blocks per wave (D/4 rows)
 };
 
-template <int D>
+template <int D, bool RET>
 struct F32Smem {
-    using G = F32Cfg<D>;
-    float Q[kFT * G::RX];   // phi(Q) rows (queries scaled per row by a power of two)
+    using G = F32Cfg<D, RET>;
+    float Q[kFT * G::RX];   // phi(Q) rows (ELU+1: scaled per row by a power of two)
     float K[kFT * G::RX];   // phi(K) rows
     float V[kFT * G::RV];   // [V | 1 | 0..] rows
     float S[D * G::RV];     // image of the carried state S_aug, rows = features
     float DEN[2][16];       // normaliser of each query block, for the waves without it
+    float DW[kFT + 1];      // retention: lambda^x, x = 0..32
 };
 
 __device__ __forceinline__ f32x4_t z4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
@@ -66,13 +73,13 @@ __device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool RET>
 __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
-    using G = F32Cfg<D>;
-    constexpr int NJ = G::NJ, RX = G::RX, RV = G::RV, VA = G::VA, FBW = G::FBW;
+    using G = F32Cfg<D, RET>;
+    constexpr int NJ = G::NJ, RX = G::RX, RV = G::RV, FBW = G::FBW;
     constexpr bool OUT = MODE != kModeState;
     constexpr bool NEED_K = MODE != kModeRead;
-    __shared__ F32Smem<D> sm;
+    __shared__ F32Smem<D, RET> sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
@@ -87,6 +94,10 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
     const float *Ks = static_cast<const float *>(a.K) + (size_t)bh * N * D;
     const float *Vs = static_cast<const float *>(a.V) + (size_t)bh * N * D;
     float *Os = OUT ? static_cast<float *>(a.O) + (size_t)bh * N * D : nullptr;
+    if constexpr (RET) {  // ordered before use by the first barrier of the tile loop
+        const float l2 = log2f(a.sh.gamma[bh % a.sh.H]);
+        if (tid <= kFT) sm.DW[tid] = tid == 0 ? 1.f : exp2f(l2 * (float)tid);
+    }
 
     constexpr int SPLIT = G::SPLIT;
     const int qb = w & 1;                                          // query block of this wave
@@ -152,20 +163,26 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
             const bool in = t < rows;
             if constexpr (OUT) {
                 const float4 x = pq[i];
-                float m = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+                float2 y0, y1;
+                if constexpr (RET) {
+                    y0 = make_float2(x.x, x.y);
+                    y1 = make_float2(x.z, x.w);
+                } else {
+                    float m = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
 #pragma unroll
-                for (int o = 1; o < D / 4; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                const float e = elu1_query_shift(m);
-                float2 y0 = make_float2(elu1_accurate_scaled(x.x, e), elu1_accurate_scaled(x.y, e));
-                float2 y1 = make_float2(elu1_accurate_scaled(x.z, e), elu1_accurate_scaled(x.w, e));
+                    for (int o = 1; o < D / 4; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                    const float e = elu1_query_shift(m);
+                    y0 = make_float2(elu1_accurate_scaled(x.x, e), elu1_accurate_scaled(x.y, e));
+                    y1 = make_float2(elu1_accurate_scaled(x.z, e), elu1_accurate_scaled(x.w, e));
+                }
                 if (!in) y0 = y1 = make_float2(0.f, 0.f);
                 *reinterpret_cast<float2 *>(&sm.Q[t * RX + 4 * c4]) = y0;
                 *reinterpret_cast<float2 *>(&sm.Q[t * RX + 4 * c4 + 2]) = y1;
             }
             if constexpr (NEED_K) {
                 const float4 x = pk[i];
-                float2 y0 = make_float2(elu1_accurate(x.x), elu1_accurate(x.y));
-                float2 y1 = make_float2(elu1_accurate(x.z), elu1_accurate(x.w));
+                float2 y0 = RET ? make_float2(x.x, x.y) : make_float2(elu1_accurate(x.x), elu1_accurate(x.y));
+                float2 y1 = RET ? make_float2(x.z, x.w) : make_float2(elu1_accurate(x.z), elu1_accurate(x.w));
                 float4 v = pv[i];
                 if (!in) {
                     y0 = y1 = make_float2(0.f, 0.f);
@@ -196,6 +213,26 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
                 f32x4_t acc[NBN];
 #pragma unroll
                 for (int j = 0; j < NBN; ++j) acc[j] = z4();
+                // phi(Q) S_aug with the state carried into this tile
+                auto inter = [&]() {
+#pragma unroll 2
+                    for (int k = 0; k < D; k += 4) {
+                        const float av = sm.Q[(16 * qb + c16) * RX + k + g];
+#pragma unroll
+                        for (int j = 0; j < NBN; ++j)
+                            acc[j] = mma4(av, sm.S[(k + g) * RV + 16 * (NB0 + j) + c16], acc[j]);
+                    }
+                };
+                if constexpr (RET) {
+                    // retention reads the carried state first, lambda^(i+1) for tile row i
+                    inter();
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float r = sm.DW[16 * qb + 4 * g + e + 1];
+#pragma unroll
+                        for (int j = 0; j < NBN; ++j) acc[j][e] *= r;
+                    }
+                }
                 if constexpr (MODE == kModeCausal) {
                     // (P (.) M) V_aug for key blocks tb <= qb: P^T tile (keys x queries)
 #pragma unroll
@@ -209,10 +246,17 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
                             pu = mma4(sm.K[(16 * tb + c16) * RX + k + 4 + g], sm.Q[(16 * qb + c16) * RX + k + 4 + g], pu);
                         }
                         pt += pu;
-                        if (tb == qb)  // diagonal: key 4g + e <= query c16
+                        if constexpr (RET) {  // lambda^(query - key), 0 above the diagonal
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int d = 16 * (qb - tb) + c16 - 4 * g - e;
+                                pt[e] = d >= 0 ? pt[e] * sm.DW[d] : 0.f;
+                            }
+                        } else if (tb == qb) {  // diagonal: key 4g + e <= query c16
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 if (4 * g + e > c16) pt[e] = 0.f;
+                        }
                         // value product, k-slot e of lane group g <-> key 16 tb + 4g + e
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -223,24 +267,20 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
                         }
                     }
                 }
-                // phi(Q) S_aug with the state carried into this tile
-#pragma unroll 2
-                for (int k = 0; k < D; k += 4) {
-                    const float av = sm.Q[(16 * qb + c16) * RX + k + g];
-#pragma unroll
-                    for (int j = 0; j < NBN; ++j) acc[j] = mma4(av, sm.S[(k + g) * RV + 16 * (NB0 + j) + c16], acc[j]);
-                }
-                // the normaliser (column D: the last block of the second value half, column 0)
-                if constexpr (NB0 != 0) {
-                    if (c16 == 0)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sm.DEN[qb][4 * g + e] = acc[NBN - 1][e];
-                }
-                __syncthreads();
                 const int rows = min(kFT, t_end - t0);
-                float rden[4];
+                float rden[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (!RET) {
+                    inter();
+                    // the normaliser (column D: the last block of the second value half, column 0)
+                    if constexpr (NB0 != 0) {
+                        if (c16 == 0)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rden[e] = 1.0f / sm.DEN[qb][4 * g + e];
+                            for (int e = 0; e < 4; ++e) sm.DEN[qb][4 * g + e] = acc[NBN - 1][e];
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rden[e] = 1.0f / sm.DEN[qb][4 * g + e];
+                }
 #pragma unroll
                 for (int j = 0; j < NBN; ++j) {
                     const int col = 16 * (NB0 + j) + c16;
@@ -259,13 +299,23 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
         }
 
         if constexpr (NEED_K) {
-            // S_aug += phi(K)^T V_aug over the tile's 32 tokens
+            // S_aug += phi(K)^T V_aug over the tile's 32 tokens (retention:
+            // S = lambda^L S + sum_t lambda^(L-1-t) k_t v_t^T over its L tokens)
+            const int L = min(kFT, t_end - t0);
+            if constexpr (RET) {
+                const float carry = sm.DW[L];
+#pragma unroll
+                for (int q = 0; q < FBW; ++q)
+#pragma unroll
+                    for (int nb = 0; nb < NJ; ++nb) S[q][nb] *= carry;
+            }
 #pragma unroll
             for (int q = 0; q < FBW; ++q) {
                 const int f0 = (D / 4) * w + 16 * q;
 #pragma unroll 2
                 for (int t = 0; t < kFT; t += 4) {
-                    const float av = sm.K[(t + g) * RX + f0 + c16];  // A[f][t] = phi(K)^T
+                    float av = sm.K[(t + g) * RX + f0 + c16];  // A[f][t] = phi(K)^T
+                    if constexpr (RET) av *= t + g < L ? sm.DW[L - 1 - t - g] : 0.f;
 #pragma unroll
                     for (int nb = 0; nb < NJ; ++nb) S[q][nb] = mma4(av, sm.V[(t + g) * RV + 16 * nb + c16], S[q][nb]);
                 }
@@ -294,13 +344,15 @@ __global__ __launch_bounds__(kFThr) void k_f32mma(FwdArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool RET>
 hipError_t launch_d(const FwdArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.sh.BH * a.sg.P)), block(kFThr);
     switch (a.mode) {
-        case kModeState: return launch_kernel_ev(k_f32mma<D, kModeState>, grid, block, 0, st, ev, a);
-        case kModeCausal: return launch_kernel_ev(k_f32mma<D, kModeCausal>, grid, block, 0, st, ev, a);
-        case kModeRead: return launch_kernel_ev(k_f32mma<D, kModeRead>, grid, block, 0, st, ev, a);
+        case kModeState: return launch_kernel_ev(k_f32mma<D, kModeState, RET>, grid, block, 0, st, ev, a);
+        case kModeCausal: return launch_kernel_ev(k_f32mma<D, kModeCausal, RET>, grid, block, 0, st, ev, a);
+        case kModeRead:
+            if constexpr (!RET) return launch_kernel_ev(k_f32mma<D, kModeRead, RET>, grid, block, 0, st, ev, a);
+            return hipErrorNotSupported;  // retention is causal only
         default: return hipErrorNotSupported;
     }
 }
@@ -308,12 +360,14 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t st, KEvents ev) {
 }  // namespace
 
 bool f32mma_supported(const Shape &sh) {
-    return sh.dtype == kF32 && sh.phi == kElu1 && sh.ret == 0 && sh.dk == sh.dv && (sh.dk == 64 || sh.dk == 128);
+    const bool map = (sh.phi == kElu1 && sh.ret == 0) || (sh.phi == kIdentity && sh.ret != 0);
+    return sh.dtype == kF32 && map && sh.dk == sh.dv && (sh.dk == 64 || sh.dk == 128);
 }
 
 hipError_t launch_f32mma(const FwdArgs &a, hipStream_t st, KEvents ev) {
     if (!f32mma_supported(a.sh)) return hipErrorNotSupported;
-    return a.sh.dk == 64 ? launch_d<64>(a, st, ev) : launch_d<128>(a, st, ev);
+    if (a.sh.ret) return a.sh.dk == 64 ? launch_d<64, true>(a, st, ev) : launch_d<128, true>(a, st, ev);
+    return a.sh.dk == 64 ? launch_d<64, false>(a, st, ev) : launch_d<128, false>(a, st, ev);
 }
 
 }  // namespace la

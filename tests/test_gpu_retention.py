@@ -73,6 +73,12 @@ CASES = [
     (1, 1, 517, 128, 96, "f32", "identity", 0, 16, True),
     (1, 2, 300, 64, 64, "f32", "elu1", 0, 64, True),
     (2, 1, 77, 16, 8, "f32", "favor", 24, 32, False),
+    # fp32 matrix-instruction retention (d 64 / 128): ragged tails, one partial tile,
+    # several segments of 32-token tiles, a carried state
+    (2, 2, 333, 64, 64, "f32", "identity", 0, 32, True),
+    (1, 3, 1000, 128, 128, "f32", "identity", 0, 128, True),
+    (1, 1, 19, 128, 128, "f32", "identity", 0, 64, False),
+    (4, 4, 2050, 64, 64, "f32", "identity", 0, 64, True),
     (1, 2, 333, 64, 64, "bf16", "elu1", 0, 64, False),
     # bf16 matrix-core retention: every (d, chunk) pair, one and several segments, ragged tails, tiny N
     (1, 1, 13, 64, 64, "bf16", "identity", 0, 64, False),
@@ -113,6 +119,36 @@ def test_shapes_against_oracle(ci):
     assert e < tol, e
     es = state_rel_err(to_f64(S), Sref)
     assert es < tol, es
+
+
+def test_extreme_decays_on_the_fp32_matrix_kernels():
+    # lambda = 0 (each output is q_i . k_i v_i), 1 (the unnormalised running sum),
+    # 0.5 and 0.999, one per head, d = 64 and 128 on fp32 storage, several segments.
+    # With lambda = 0 a row is one dot product, and where q_i . k_i cancels its
+    # fp32 rounding is large against the row itself: that head is held to the
+    # forward-error bound instead (error over the same recurrence on |Q|, |K|,
+    # |V|, |S_in|, the magnitude of the terms summed); the others to the
+    # per-row metric.
+    gam = np.array([0.0, 1.0, 0.5, 0.999], dtype=np.float32)
+    for d, N in ((64, 1100), (128, 700)):
+        _say("fp32 extreme decays d", d, "N", N)
+        fi = inputs.custom_inputs(41 + d, 2, 4, N, d, d, scale=d ** -0.5, dtype="f32")
+        q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+        S0 = (np.random.default_rng(d).standard_normal((2, 4, d, d)) * 0.1).astype(np.float32)
+        S = torch.zeros(2, 4, d, d, device="cuda")
+        O = la.la_forward_retention_chunked(q, k, v, _gam(gam), 64, S_in=torch.from_numpy(S0).cuda(), S_out=S)
+        g64 = gam.astype(np.float64)
+        ref, Sref = oracle.retention_recurrent("identity", fi.Q.f32, fi.K.f32, fi.V.f32, g64, S_in=S0)
+        mag, _ = oracle.retention_recurrent("identity", np.abs(fi.Q.f32), np.abs(fi.K.f32), np.abs(fi.V.f32), g64,
+                                            S_in=np.abs(S0))
+        torch.cuda.synchronize()
+        got = to_f64(O)
+        fwd = (np.abs(got - ref).max(-1) / np.abs(mag).max(-1)).max()
+        _say("d", d, "forward-error bound", f"{fwd:.2e}", "per-row (lambda > 0)",
+             f"{row_rel_err(got[:, 1:], ref[:, 1:]):.2e}")
+        assert fwd < TOL_F32, d
+        assert row_rel_err(got[:, 1:], ref[:, 1:]) < TOL_F32, d
+        assert state_rel_err(to_f64(S), Sref) < TOL_F32, d
 
 
 def test_handoff_in_place_state_and_chunk_invariance():
