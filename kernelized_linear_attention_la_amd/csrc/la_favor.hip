@@ -43,7 +43,8 @@ constexpr int kFT = 64 * kFW;          // threads
 constexpr int kFNJ = kFD / 16 + 1;     // value column blocks incl. the normaliser block
 constexpr int kFKBF = kFM / 32;        // 32-feature k-blocks
 constexpr int kFRK = kFM + 8;          // phi row stride (16-row 128-bit reads conflict free)
-constexpr int kFRV = kFD + 16 + 8;     // V_aug row stride
+constexpr int kFRV = kFD + 16;         // V_aug row stride: 40 dwords (5 x 8 mod 64), the eight rows of a
+                                        // transposed read fall on disjoint bank groups
 constexpr int kFRX = kFD + 8;          // raw row stride
 constexpr int kFRO = kFD + 8;          // output staging row stride
 constexpr int kFSlot = kFM * (kFD + 16);  // floats per hand-off slot
