@@ -238,9 +238,10 @@ def run_cpu_baseline_decode(wl, seconds):
 
 def backward_on_mfma(wl):
     """The library runs the backward's two passes on fp32 matrix instructions
-    for bf16 ELU+1 with d_k = d_v = 64 and 64-token chunks, or d_k = d_v = 128
-    and chunks of a multiple of 32 tokens (run on 32-token tiles)."""
-    if wl.dtype != "bf16" or wl.phi != "elu1" or wl.dk != wl.dv:
+    for ELU+1 (bf16 or fp32 storage) with d_k = d_v = 64 and 64-token chunks,
+    or d_k = d_v = 128 and chunks of a multiple of 32 tokens (run on 32-token
+    tiles)."""
+    if wl.dtype not in ("bf16", "f32") or wl.phi != "elu1" or wl.dk != wl.dv:
         return False
     return (wl.dk == 64 and wl.chunk == 64) or (wl.dk == 128 and wl.chunk % 32 == 0)
 
@@ -266,7 +267,7 @@ def kernel_symbol(wl, slot):
     """rocprofv3 name of the kernel a slot runs for this workload (labels only)."""
     if wl.backward:
         if backward_on_mfma(wl) and slot in ("dq", "dkv"):
-            return f"k_bwd_{slot}_mfma<{wl.dk}, {backward_tile(wl)}>"
+            return f"k_bwd_{slot}_mfma<{wl.dk}, {backward_tile(wl)}, {'float' if wl.dtype == 'f32' else 'unsigned short'}>"
         return f"k_bwd_{slot}<{'float' if wl.dtype == 'f32' else 'unsigned short'}>"
     if wl.gated:
         t = "float" if wl.dtype == "f32" else "unsigned short"

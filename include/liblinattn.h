@@ -296,11 +296,12 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  *                while d' * (d_v + 1) <= 16640 (d' = 128 with d_v <= 128, or
  *                d' = 256 with d_v <= 64); larger: LA_ERR_UNSUPPORTED.
  *   chunk        16, 32, 64 or 128: tokens per chunk of the chunked form.  The
- *                gradients do not depend on it.  bf16 ELU+1 with d_k = d_v =
- *                64 and 64-token chunks, or d_k = d_v = 128 and chunks of 32,
- *                64 or 128 tokens (run on 32-token tiles), take fp32 matrix
- *                instructions; everything else runs on fp32-arithmetic kernels
- *                that tile at most 16 tokens whatever is asked.
+ *                gradients do not depend on it.  ELU+1 (bf16 or fp32) with
+ *                d_k = d_v = 64 and 64-token chunks, or d_k = d_v = 128 and
+ *                chunks of 32, 64 or 128 tokens (run on 32-token tiles), takes
+ *                fp32 matrix instructions; everything else runs on
+ *                fp32-arithmetic kernels that tile at most 16 tokens whatever
+ *                is asked.
  *   Q, K, V      forward inputs; dO [B,H,N,d_v] the gradient of the loss with
  *                respect to O (all of dtype p->dtype).
  *   S_in, z_in   the forward's starting state, or both NULL (zero).

@@ -595,9 +595,9 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
     if (mf) {
         BwdMfmaArgs m;
         m.D = sh.dk; m.BH = sh.BH; m.N = sh.N; m.P = g.P; m.seg_chunks = g.seg_chunks; m.n_chunks = g.n_chunks;
-        m.Q = static_cast<const uint16_t *>(Q); m.K = static_cast<const uint16_t *>(K);
-        m.V = static_cast<const uint16_t *>(V); m.dO = static_cast<const uint16_t *>(dO);
-        m.dQ = static_cast<uint16_t *>(dQ); m.dK = static_cast<uint16_t *>(dK); m.dV = static_cast<uint16_t *>(dV);
+        m.f32 = sh.dtype == kF32;
+        m.Q = Q; m.K = K; m.V = V; m.dO = dO;
+        m.dQ = dQ; m.dK = dK; m.dV = dV;
         m.Spre = wsS; m.zpre = wsz;
         m.U = reinterpret_cast<float *>(wsb + wl.u_off);
         m.G = reinterpret_cast<float *>(wsb + wl.g_off);

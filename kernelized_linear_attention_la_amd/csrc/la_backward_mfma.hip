@@ -1,5 +1,5 @@
 // Backward of the causal normalised form on the matrix cores: ELU+1,
-// d_k = d_v = D, bf16 storage, D = 64 on 64-token tiles and D = 128 on
+// d_k = d_v = D, bf16 or fp32 storage, D = 64 on 64-token tiles and D = 128 on
 // 32-token tiles (the derivation and the fp32-FMA kernels are in
 // la_backward.hip; this file runs the same chunked algebra with
 // v_mfma_f32_16x16x4_f32; the chunkwise form gives the same gradients for
@@ -106,38 +106,63 @@ __device__ __forceinline__ void put_rows(float *T, int ld, int m0, int n0, f32x4
 
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
+// eight consecutive stored values (16 bytes of bf16, 32 of fp32) as float4 pairs
+__device__ __forceinline__ void load8(const uint16_t *p, float4 &a, float4 &b) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    a = make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
+    b = make_float4(lo_bf16(x.z), hi_bf16(x.z), lo_bf16(x.w), hi_bf16(x.w));
+}
+__device__ __forceinline__ void load8(const float *p, float4 &a, float4 &b) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+}
+__device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ void store1(uint16_t *p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ void store1(float *p, float v) { *p = v; }
+// eight consecutive values to storage (16 bytes of bf16, 32 of fp32)
+__device__ __forceinline__ void store8(uint16_t *p, const float *s) {
+    uint4 o;
+    o.x = f32_to_bf16(s[0]) | (static_cast<uint32_t>(f32_to_bf16(s[1])) << 16);
+    o.y = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
+    o.z = f32_to_bf16(s[4]) | (static_cast<uint32_t>(f32_to_bf16(s[5])) << 16);
+    o.w = f32_to_bf16(s[6]) | (static_cast<uint32_t>(f32_to_bf16(s[7])) << 16);
+    *reinterpret_cast<uint4 *>(p) = o;
+}
+__device__ __forceinline__ void store8(float *p, const float *s) {
+    *reinterpret_cast<float4 *>(p) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(s[4], s[5], s[6], s[7]);
+}
+
 // phi(X) rows t0.. of one tile (rows past `rows` are zero)
-template <int D, int C>
-__device__ void stage_phi(const uint16_t *X, int t0, int rows, float *R, int tid) {
+template <int D, int C, typename T>
+__device__ void stage_phi(const T *X, int t0, int rows, float *R, int tid) {
     constexpr int RX = BCfg<D, C>::RX;
 #pragma unroll
     for (int i = 0; i < C * D / 8 / kThreads; ++i) {
         const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < rows) x = *reinterpret_cast<const uint4 *>(&X[(size_t)(t0 + t) * D + 8 * c8]);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-        float4 a, b;
-        a.x = elu1(lo_bf16(w[0])); a.y = elu1(hi_bf16(w[0])); a.z = elu1(lo_bf16(w[1])); a.w = elu1(hi_bf16(w[1]));
-        b.x = elu1(lo_bf16(w[2])); b.y = elu1(hi_bf16(w[2])); b.z = elu1(lo_bf16(w[3])); b.w = elu1(hi_bf16(w[3]));
-        if (t >= rows) a = b = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (t < rows) {
+            load8(&X[(size_t)(t0 + t) * D + 8 * c8], a, b);
+            a = make_float4(elu1(a.x), elu1(a.y), elu1(a.z), elu1(a.w));
+            b = make_float4(elu1(b.x), elu1(b.y), elu1(b.z), elu1(b.w));
+        }
         *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8]) = a;
         *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8 + 4]) = b;
     }
 }
 
 // [v | 1 | 0] rows of one tile (columns D..RV-1 written too)
-template <int D, int C>
-__device__ void stage_vaug(const uint16_t *V, int t0, int rows, float *R, int tid) {
+template <int D, int C, typename T>
+__device__ void stage_vaug(const T *V, int t0, int rows, float *R, int tid) {
     constexpr int RV = BCfg<D, C>::RV;
 #pragma unroll
     for (int i = 0; i < C * D / 8 / kThreads; ++i) {
         const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < rows) x = *reinterpret_cast<const uint4 *>(&V[(size_t)(t0 + t) * D + 8 * c8]);
-        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8]) =
-            make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
-        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8 + 4]) =
-            make_float4(lo_bf16(x.z), hi_bf16(x.z), lo_bf16(x.w), hi_bf16(x.w));
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (t < rows) load8(&V[(size_t)(t0 + t) * D + 8 * c8], a, b);
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8]) = a;
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8 + 4]) = b;
     }
     for (int u = tid; u < C * (RV - D); u += kThreads) {
         const int t = u / (RV - D), c = D + u % (RV - D);
@@ -168,28 +193,19 @@ __device__ __forceinline__ void put_state(const f32x4 (&S)[BCfg<D, C>::FBW][BCfg
         for (int j = 0; j < B::NVB; ++j) put_rows(T, B::RV, 16 * (kNW * q + w), 16 * j, S[q][j], lane);
 }
 
-// 16 rows x D columns of T (rows m0..) -> bf16 rows of dst, 16 bytes per lane
-template <int D>
-__device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int rows, uint16_t *dst, size_t row0,
-                                           int lane) {
+// 16 rows x D columns of T (rows m0..) -> rows of dst, 8 values per lane and step
+template <int D, typename ST>
+__device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int rows, ST *dst, size_t row0, int lane) {
 #pragma unroll
     for (int it = 0; it < 16 * D / 8 / 64; ++it) {
         const int idx = it * 64 + lane, r = idx / (D / 8), c8 = idx % (D / 8);
-        if (m0 + r < rows) {
-            const float *s = &T[(m0 + r) * ld + 8 * c8];
-            uint4 o;
-            o.x = f32_to_bf16(s[0]) | (static_cast<uint32_t>(f32_to_bf16(s[1])) << 16);
-            o.y = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
-            o.z = f32_to_bf16(s[4]) | (static_cast<uint32_t>(f32_to_bf16(s[5])) << 16);
-            o.w = f32_to_bf16(s[6]) | (static_cast<uint32_t>(f32_to_bf16(s[7])) << 16);
-            *reinterpret_cast<uint4 *>(&dst[(row0 + m0 + r) * D + 8 * c8]) = o;
-        }
+        if (m0 + r < rows) store8(&dst[(row0 + m0 + r) * D + 8 * c8], &T[(m0 + r) * ld + 8 * c8]);
     }
 }
 
-// accumulator blocks (rows m0 + 4g + e, columns n0 + 16 j + c16) -> bf16 rows of dst
-template <int D, int NB>
-__device__ __forceinline__ void store_acc(const f32x4 (&v)[NB], int m0, int n0, int rows, uint16_t *dst, size_t row0,
+// accumulator blocks (rows m0 + 4g + e, columns n0 + 16 j + c16) -> rows of dst
+template <int D, int NB, typename ST>
+__device__ __forceinline__ void store_acc(const f32x4 (&v)[NB], int m0, int n0, int rows, ST *dst, size_t row0,
                                           int lane) {
     const int g = lane >> 4, c = lane & 15;
 #pragma unroll
@@ -197,15 +213,15 @@ __device__ __forceinline__ void store_acc(const f32x4 (&v)[NB], int m0, int n0, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = m0 + 4 * g + e;
-            if (r < rows) dst[(row0 + r) * D + n0 + 16 * j + c] = f32_to_bf16(v[j][e]);
+            if (r < rows) store1(&dst[(row0 + r) * D + n0 + 16 * j + c], v[j][e]);
         }
 }
 
 // d-wide row blocks of this wave to dst: through the score tile (one column
 // split: the wave's own rows of W) or straight from the accumulators
-template <int D, int C>
+template <int D, int C, typename ST>
 __device__ __forceinline__ void store_dwide(const f32x4 (&v)[BCfg<D, C>::NDW], float *W, int m0, int cs, int rows,
-                                            uint16_t *dst, size_t row0, int lane) {
+                                            ST *dst, size_t row0, int lane) {
     using B = BCfg<D, C>;
     if constexpr (B::STAGE) {
         wave_lds_sync();  // every lane has read this wave's rows of W
@@ -236,7 +252,7 @@ __device__ __forceinline__ void row_sync() {
 //   U      += phi(Q)^T G_aug    (segment sums for the reverse scan)
 //   S_aug  += phi(K)^T V_aug
 // ---------------------------------------------------------------------------
-template <int D, int C>
+template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
@@ -252,11 +268,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
     const int N = a.N;
     const int c_begin = seg * a.seg_chunks, c_end = min(a.n_chunks, c_begin + a.seg_chunks);
-    const uint16_t *Qs = a.Q + (size_t)bh * N * D;
-    const uint16_t *Ks = a.K + (size_t)bh * N * D;
-    const uint16_t *Vs = a.V + (size_t)bh * N * D;
-    const uint16_t *dOs = a.dO + (size_t)bh * N * D;
-    uint16_t *dQs = a.dQ + (size_t)bh * N * D;
+    const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * D;
+    const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * D;
+    const T *Vs = static_cast<const T *>(a.V) + (size_t)bh * N * D;
+    const T *dOs = static_cast<const T *>(a.dO) + (size_t)bh * N * D;
+    T *dQs = static_cast<T *>(a.dQ) + (size_t)bh * N * D;
     float *Gw = a.G + (size_t)bh * N * VK;
 
     // carried state S_aug (feature rows 16 (4q + w) + 4g + e, value columns 16j + c16) and U
@@ -281,9 +297,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C, rows = min(C, N - t0);
         block_sync_lds();  // the previous tile's tiles are consumed, the state image is complete
-        stage_phi<D, C>(Qs, t0, rows, sm.P, tid);
-        stage_phi<D, C>(Ks, t0, rows, sm.K, tid);
-        stage_vaug<D, C>(Vs, t0, rows, sm.V, tid);
+        stage_phi<D, C, T>(Qs, t0, rows, sm.P, tid);
+        stage_phi<D, C, T>(Ks, t0, rows, sm.K, tid);
+        stage_vaug<D, C, T>(Vs, t0, rows, sm.V, tid);
         block_sync_lds();
 
         // scores P = phi(Q) phi(K)^T of this wave's key blocks, masked (key <= query)
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = m0 + 4 * g + e, col = 16 * (NB0 + j) + c16;
-                    const float d = (t < rows && col < D) ? bf16_to_f32(dOs[(size_t)(t0 + t) * D + col]) : 0.f;
+                    const float d = (t < rows && col < D) ? load1(&dOs[(size_t)(t0 + t) * D + col]) : 0.f;
                     dov[j][e] = d;
                     part[e] += d * num[j][e];
                 }
@@ -405,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 dp[j][e] *= fminf(sm.P[(m0 + 4 * g + e) * RX + 16 * (cs * NDW + j) + c16], 1.f);
-        store_dwide<D, C>(dp, sm.W, m0, cs, rows, dQs, t0, lane);
+        store_dwide<D, C, T>(dp, sm.W, m0, cs, rows, dQs, t0, lane);
         block_sync_lds();  // every wave's G_aug rows are in LDS, the state image is read
         // U += phi(Q)^T G_aug, S_aug += phi(K)^T V_aug (this wave's feature rows)
 #pragma unroll
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 //   (M': query >= key),  dK = dphi(K) * min(phi(k), 1)
 //   R_aug  += phi(Q)^T G_aug
 // ---------------------------------------------------------------------------
-template <int D, int C>
+template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
@@ -451,11 +467,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
     const int N = a.N;
     const int c_begin = seg * a.seg_chunks, c_end = min(a.n_chunks, c_begin + a.seg_chunks);
-    const uint16_t *Qs = a.Q + (size_t)bh * N * D;
-    const uint16_t *Ks = a.K + (size_t)bh * N * D;
-    const uint16_t *Vs = a.V + (size_t)bh * N * D;
-    uint16_t *dKs = a.dK + (size_t)bh * N * D;
-    uint16_t *dVs = a.dV + (size_t)bh * N * D;
+    const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * D;
+    const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * D;
+    const T *Vs = static_cast<const T *>(a.V) + (size_t)bh * N * D;
+    T *dKs = static_cast<T *>(a.dK) + (size_t)bh * N * D;
+    T *dVs = static_cast<T *>(a.dV) + (size_t)bh * N * D;
     const float *Gw = a.G + (size_t)bh * N * VK;
 
     f32x4 R[FBW][NVB];
@@ -476,9 +492,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * C, rows = min(C, N - t0);
         block_sync_lds();
-        stage_phi<D, C>(Qs, t0, rows, sm.P, tid);
-        stage_phi<D, C>(Ks, t0, rows, sm.K, tid);
-        stage_vaug<D, C>(Vs, t0, rows, sm.V, tid);
+        stage_phi<D, C, T>(Qs, t0, rows, sm.P, tid);
+        stage_phi<D, C, T>(Ks, t0, rows, sm.K, tid);
+        stage_vaug<D, C, T>(Vs, t0, rows, sm.V, tid);
         stage_g<D, C>(Gw, t0, rows, sm.G, tid);
         block_sync_lds();
 
@@ -529,8 +545,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 dk[j][e] *= fminf(sm.K[(m0 + 4 * g + e) * RX + 16 * (cs * NDW + j) + c16], 1.f);
-        store_dwide<D, C>(dk, sm.W, m0, cs, rows, dKs, t0, lane);
-        store_dwide<D, C>(dv, sm.W, m0, cs, rows, dVs, t0, lane);
+        store_dwide<D, C, T>(dk, sm.W, m0, cs, rows, dKs, t0, lane);
+        store_dwide<D, C, T>(dv, sm.W, m0, cs, rows, dVs, t0, lane);
         block_sync_lds();  // the state image is no longer read
         // R_aug += phi(Q)^T G_aug (this wave's feature rows)
 #pragma unroll
@@ -548,7 +564,7 @@ static_assert(lds_bytes<64, 64>() <= 160 * 1024 && lds_bytes<128, 32>() <= 160 *
 }  // namespace
 
 bool backward_mfma_supported(const Shape &sh, int chunk) {
-    if (sh.dtype != kBF16 || sh.phi != kElu1 || sh.dk != sh.dv) return false;
+    if ((sh.dtype != kBF16 && sh.dtype != kF32) || sh.phi != kElu1 || sh.dk != sh.dv) return false;
     if (sh.dk == 64) return chunk == 64;
     return sh.dk == 128 && chunk % 32 == 0;  // on 32-token tiles
 }
@@ -559,15 +575,23 @@ size_t backward_mfma_g_floats(const Shape &sh) { return (size_t)sh.dk + 4; }
 
 hipError_t launch_bwd_dq_mfma(const BwdMfmaArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.BH * a.P)), block(kThreads);
-    if (a.D == 64) return launch_kernel_ev(k_bwd_dq_mfma<64, 64>, grid, block, 0, st, ev, a);
-    if (a.D == 128) return launch_kernel_ev(k_bwd_dq_mfma<128, 32>, grid, block, 0, st, ev, a);
+    if (a.D == 64)
+        return a.f32 ? launch_kernel_ev(k_bwd_dq_mfma<64, 64, float>, grid, block, 0, st, ev, a)
+                     : launch_kernel_ev(k_bwd_dq_mfma<64, 64, uint16_t>, grid, block, 0, st, ev, a);
+    if (a.D == 128)
+        return a.f32 ? launch_kernel_ev(k_bwd_dq_mfma<128, 32, float>, grid, block, 0, st, ev, a)
+                     : launch_kernel_ev(k_bwd_dq_mfma<128, 32, uint16_t>, grid, block, 0, st, ev, a);
     return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_dkv_mfma(const BwdMfmaArgs &a, hipStream_t st, KEvents ev) {
     const dim3 grid((unsigned)((size_t)a.BH * a.P)), block(kThreads);
-    if (a.D == 64) return launch_kernel_ev(k_bwd_dkv_mfma<64, 64>, grid, block, 0, st, ev, a);
-    if (a.D == 128) return launch_kernel_ev(k_bwd_dkv_mfma<128, 32>, grid, block, 0, st, ev, a);
+    if (a.D == 64)
+        return a.f32 ? launch_kernel_ev(k_bwd_dkv_mfma<64, 64, float>, grid, block, 0, st, ev, a)
+                     : launch_kernel_ev(k_bwd_dkv_mfma<64, 64, uint16_t>, grid, block, 0, st, ev, a);
+    if (a.D == 128)
+        return a.f32 ? launch_kernel_ev(k_bwd_dkv_mfma<128, 32, float>, grid, block, 0, st, ev, a)
+                     : launch_kernel_ev(k_bwd_dkv_mfma<128, 32, uint16_t>, grid, block, 0, st, ev, a);
     return hipErrorNotSupported;
 }
 

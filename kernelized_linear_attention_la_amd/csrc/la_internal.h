@@ -179,13 +179,14 @@ hipError_t launch_bwd_rscan(int BH, int P, int dp, int dv, float *U, const float
 // fp32 [BH][N][backward_mfma_g_floats()].
 struct BwdMfmaArgs {
     int D, BH, N, P, seg_chunks, n_chunks;  // d_k = d_v = D; chunks are backward_mfma_tile() tokens
-    const uint16_t *Q, *K, *V, *dO;
-    uint16_t *dQ, *dK, *dV;
+    int f32;                                // storage: fp32 (1) or bf16 (0)
+    const void *Q, *K, *V, *dO;
+    void *dQ, *dK, *dV;
     const float *Spre, *zpre;  // forward prefix per segment
     float *U;                  // [BH][P][D * (D + 1)]
     float *G;                  // [BH][N][backward_mfma_g_floats()]
 };
-// bf16 ELU+1, d_k = d_v = 64 with 64-token chunks, or 128 with chunks of a multiple of 32
+// ELU+1 (bf16 or fp32), d_k = d_v = 64 with 64-token chunks, or 128 with chunks of a multiple of 32
 bool backward_mfma_supported(const Shape &sh, int chunk);
 int backward_mfma_tile(const Shape &sh);            // tokens per tile: 64 (d 64), 32 (d 128)
 size_t backward_mfma_g_floats(const Shape &sh);     // G_aug floats per token: d_v + 4

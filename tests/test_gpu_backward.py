@@ -96,6 +96,10 @@ CASES = [
     (1, 3, 1000, 128, 128, "bf16", "elu1", 0, 64, False),
     (1, 2, 150, 128, 128, "bf16", "elu1", 0, 16, True),   # d128 bf16 on the fp32-arithmetic kernels
     (1, 1, 17, 128, 128, "bf16", "elu1", 0, 128, True),   # one partial tile
+    # fp32 storage on the matrix-core kernels (fp32 arithmetic, 1e-4)
+    (2, 2, 700, 64, 64, "f32", "elu1", 0, 64, True),
+    (1, 2, 333, 128, 128, "f32", "elu1", 0, 32, True),
+    (1, 1, 1000, 128, 128, "f32", "elu1", 0, 128, False),
 ]
 
 

@@ -118,6 +118,10 @@ CASES = [
     (1, 2, 190, 64, 64, "bf16", "favor", 256, 64),
     (2, 1, 77, 16, 8, "f32", "favor", 24, 32),
     (1, 1, 5000, 64, 64, "bf16", "elu1", 0, 64),
+    # fp32 matrix-instruction kernel past the one-workgroup size: segment sums,
+    # scan and the causal pass, ragged tails
+    (1, 2, 2000, 64, 64, "f32", "elu1", 0, 64),
+    (1, 1, 1500, 128, 128, "f32", "elu1", 0, 128),
     # bf16 matrix-core variants: every (d, chunk) pair, ragged tails, tiny N
     (2, 2, 1000, 128, 128, "bf16", "elu1", 0, 64),
     (1, 3, 777, 64, 64, "bf16", "elu1", 0, 128),
