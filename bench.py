@@ -39,6 +39,7 @@ DEFAULT_WORKLOAD = "elu1_bf16_b2h16n16384d128_c128"
 EXTRA_DECODE = "decode_elu1_f32_s256h32d128_prefix1024_steps64"
 EXTRA_FAVOR = "favor_bf16_b2h8n8192d64_m256_c64"
 PREFIX_BLOCK = 64  # sequences of the decode prefix drawn and run at a time
+EVENT_BATCH = 64  # decode launches timed per batch of HIP events
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 FP32_VECTOR_PEAK_TFS = 157.3  # MI355X fp32 vector ALUs (256 CUs x 256 flop/clk x 2.4 GHz), TFLOP/s
@@ -628,20 +629,33 @@ def bench_gated(args, wl):
         step()
     torch.cuda.synchronize()
     hev = HipEvents(la.lib())
-    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    # the K timed steps: launches only, back to back on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        hev.record(pairs[i][0], raw)
         step()
-        hev.record(pairs[i][1], raw)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    durs = [hev.elapsed_ms(a_, b_) for a_, b_ in pairs]
+    ms_per_step = elapsed * 1e3 / args.steps
+    # per-call time: HIP events around each call in batches of EVENT_BATCH,
+    # queued behind a short GPU sleep (as for decode)
+    pairs = [(hev.create(), hev.create()) for _ in range(EVENT_BATCH)]
+    durs = []
+    done = 0
+    while done < args.steps:
+        n = min(EVENT_BATCH, args.steps - done)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for i in range(n):
+            hev.record(pairs[i][0], raw)
+            step()
+            hev.record(pairs[i][1], raw)
+        torch.cuda.synchronize()
+        durs += [hev.elapsed_ms(*pairs[i]) for i in range(n)]
+        done += n
     for a_, b_ in pairs:
         hev.destroy(a_)
         hev.destroy(b_)
     kern_ms = sum(durs) / len(durs)
-    ms_per_step = elapsed * 1e3 / args.steps
     extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
     if chunked:
         # the two launches of the chunkwise form timed one by one through the
@@ -781,27 +795,43 @@ def bench_decode(args, wl):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev_pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    # the K timed steps: launches only, back to back on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        hev.record(ev_pairs[i][0], raw_stream)
         step(args.warmup + i)
-        hev.record(ev_pairs[i][1], raw_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    durs = [hev.elapsed_ms(a, b) for a, b in ev_pairs]
+    ms_per_step = elapsed * 1e3 / args.steps
+    # per-kernel time over K more steps: HIP events around each launch, in
+    # batches of EVENT_BATCH queued behind a short GPU sleep so the kernels run
+    # back to back (hundreds of outstanding timing events at once have
+    # stretched both the events and the host's enqueue rate on this runtime,
+    # while the kernel trace showed unchanged kernels)
+    ev_pairs = [(hev.create(), hev.create()) for _ in range(EVENT_BATCH)]
+    durs = []
+    done = 0
+    while done < args.steps:
+        n = min(EVENT_BATCH, args.steps - done)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for i in range(n):
+            hev.record(ev_pairs[i][0], raw_stream)
+            step(args.warmup + args.steps + done + i)
+            hev.record(ev_pairs[i][1], raw_stream)
+        torch.cuda.synchronize()
+        durs += [hev.elapsed_ms(*ev_pairs[i]) for i in range(n)]
+        done += n
     for a, b in ev_pairs:
         hev.destroy(a)
         hev.destroy(b)
     kern_ms = sum(durs) / len(durs)
-    ms_per_step = elapsed * 1e3 / args.steps
     value = wl.B / (ms_per_step * 1e-3)  # one generated token per sequence per step
     nbytes = decode_alg_bytes(wl)
     ach = nbytes / (kern_ms * 1e-3) / 1e9
     kname = kernel_symbol(wl, "decode")
     roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
             "traffic": stored_traffic(wl, kname), "kernel": kname, "kernel_avg_us": kern_ms * 1e3,
-            "alg_bytes_per_launch": nbytes, "timing": "hip events around each launch"}
+            "alg_bytes_per_launch": nbytes, "timing": "hip events around each launch, batches of 64 queued back to back"}
     extra = {"head_steps_per_s": wl.B * wl.H / (ms_per_step * 1e-3),
              # the state-building prefix (not part of the step): fp32 causal forward over every
              # sequence, summed over the blocks it is run in, timed by HIP events around each call
@@ -846,8 +876,8 @@ def measure_extras(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)  # >= 100 ms of timed work on the long-context workload
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget; 0 skips it")
     ap.add_argument("--no-extras", action="store_true",
