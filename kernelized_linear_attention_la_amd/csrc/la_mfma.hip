@@ -205,9 +205,16 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // chunk takes several load latencies to compute and whose registers are
     // needed by the 8-wave tiles.
     constexpr int DEPTH = (DK == 128 && C == 128) ? 1 : 2;
+    // ELU+1: a prefetched chunk's keys and this lane's query pieces are
+    // mapped in registers at the end of the chunk before the one that stages
+    // them (pre_map), not while every wave stages at once: a wave that
+    // finishes its matrix work early then runs its exponentials while the
+    // other wave of its SIMD is still reading LDS and issuing MFMAs.
+    constexpr bool PRE = PHI == kElu1;
     struct Pref {
         Op8 raw[(UK + UV + UQ) / G::THREADS > 0 ? (UK + UV + UQ) / G::THREADS : 1];
         Op8 q[KBQ];
+        bool klive, qlive;  // rows loaded (wave-uniform); dead pieces are not mapped
     };
     Pref pf[DEPTH];
     // Query block of this wave.  Waves w and w + 4 share a SIMD; with eight
@@ -250,6 +257,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         const int tt0 = cc * C;
         const int rows = live ? min(C, N - tt0) : 0;
         const int qrows = qlive ? min(C, N - tt0) : 0;
+        p.klive = live;
+        p.qlive = qlive;
         const auto rk = make_rsrc(Ks + (size_t)tt0 * DK, rows * DK * 2);
         const auto rv = make_rsrc(Vs + (size_t)tt0 * DV, rows * DV * 2);
 #pragma unroll
@@ -284,10 +293,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = pc;
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + DK + 8 * c8]) = ps;
             } else {
-                // ELU+1 on the way in (retention: raw keys); tokens past the end get phi = 0, not phi(0) = 1
-                uint4 ph;
-                if constexpr (RET) ph = p.raw[i].u;
-                else ph = elu1_bf16x8(p.raw[i].u);
+                // ELU+1 keys arrive mapped (pre_map; retention: raw keys); tokens
+                // past the end get phi = 0, not phi(0) = 1
+                static_assert(RET || PRE, "the remaining maps are ELU+1 and the identity");
+                uint4 ph = p.raw[i].u;
                 if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = ph;
             }
@@ -301,6 +310,27 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         for (int i = 0; i < UVT; ++i) {
             const int u = tid + i * G::THREADS, t = u / (DV / 8), c8 = u % (DV / 8);
             *reinterpret_cast<uint4 *>(&sm.V[ks][t * RV + 8 * c8]) = p.raw[UKT + i].u;
+        }
+    };
+
+    // ELU+1 of a prefetched chunk in registers: keys piece by piece, query
+    // pieces with their row's power-of-two scale (cancels in the division)
+    auto pre_map = [&](Pref &p) {
+        if constexpr (PRE) {
+            if (p.klive) {
+#pragma unroll
+                for (int i = 0; i < UKT; ++i) p.raw[i].u = elu1_bf16x8(p.raw[i].u);
+            }
+            if constexpr (DO_OUT) {
+                if (p.qlive) {
+                    uint4 raw[KBQ], ph[KBQ];
+#pragma unroll
+                    for (int kb = 0; kb < KBQ; ++kb) raw[kb] = p.q[kb].u;
+                    elu1_query_pieces<KBQ>(raw, ph);
+#pragma unroll
+                    for (int kb = 0; kb < KBQ; ++kb) p.q[kb].u = ph[kb];
+                }
+            }
         }
     };
 
@@ -361,13 +391,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = p.q[kb].u;  // rows past the end are not stored
         } else if constexpr (OUT && !G::XR) {
-            // ELU+1 with the row's power-of-two scale (cancels in the division)
-            uint4 raw[KBF], ph[KBF];
 #pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) raw[kb] = p.q[kb].u;
-            elu1_query_pieces<KBF>(raw, ph);
-#pragma unroll
-            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = ph[kb];
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = p.q[kb].u;  // mapped by pre_map
         }
         block_sync_lds();
         fetch(p, step + DEPTH);
@@ -657,6 +682,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 }
             }
         }
+        pre_map(p);        // the chunk fetched above, mapped before the barrier
         block_sync_lds();  // every wave is done with this chunk's tiles and the old state image
         if constexpr (CARRY) {
 #pragma unroll
@@ -854,6 +880,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // uses ring slot s % 2.  (A one-slot ring walks the chunks one by one.)
     static_assert(DEPTH == 1 || DEPTH == 2, "ring of one or two slots");
     using Out = std::integral_constant<bool, DO_OUT>;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) pre_map(pf[d]);
     if constexpr (DEPTH == 1) {
         if constexpr (!FUSED) {
             for (int c = c_begin; c < c_end; ++c) body(pf[0], c, c, Out{});
@@ -884,6 +912,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         }
         // ---- phase 2: publish the sums, gather the prefix of the earlier segments
         publish_and_gather();
+        if (i < n) pre_map(pf[DEPTH - 1]);
         // ---- phase 3: the chunk loop from the prefix state (step cbase + k = chunk k)
         int k = 0;
         for (; k + 2 <= n; k += 2) {

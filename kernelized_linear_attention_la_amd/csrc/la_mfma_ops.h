@@ -54,10 +54,12 @@ __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // ELU+1 ("Linear Attention", feature-map table): x + 1 for x > 0, else exp(x)
-// (hardware exp2, ~1 ulp; its value for x > 0 is discarded by the select).
+// (hardware exp2, ~1 ulp).  Since 1 + x <= exp(x) <= 1 for x <= 0 and
+// 1 < 1 + x < exp(x) for x > 0, the map is the median of {x + 1, exp(x), 1}:
+// one v_med3_f32 in place of a compare and a select.
 __device__ __forceinline__ float elu1_hw(float x) {
     const float e = __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
-    return x > 0.f ? x + 1.f : e;
+    return __builtin_amdgcn_fmed3f(x + 1.f, e, 1.f);
 }
 
 // ELU+1 of eight packed bf16 values, rounded back to packed bf16
@@ -83,10 +85,14 @@ __device__ __forceinline__ float elu1_row_shift(float qmax) {
     return qmax > 0.f ? 0.f : floorf(qmax * 1.44269504088896341f);
 }
 
-// ELU+1 of x scaled by 2^-e (e from elu1_row_shift of x's row)
-__device__ __forceinline__ float elu1_hw_scaled(float x, float e) {
+// ELU+1 of x scaled by 2^-e (e from elu1_row_shift of x's row), as a median
+// like elu1_hw with cap = 1 when e = 0 and cap = +inf when e < 0: a row with
+// e < 0 has every x <= 0, and its scaled exp(x) 2^-e >= exp(x) >= 1 + x, so
+// the median {x + 1, exp(x) 2^-e, +inf} is the scaled exponential.
+__device__ __forceinline__ float elu1_row_cap(float e) { return e == 0.f ? 1.f : __builtin_huge_valf(); }
+__device__ __forceinline__ float elu1_hw_scaled(float x, float e, float cap) {
     const float v = __builtin_amdgcn_exp2f(x * 1.44269504088896341f - e);
-    return x > 0.f ? x + 1.f : v;
+    return __builtin_amdgcn_fmed3f(x + 1.f, v, cap);
 }
 
 __device__ __forceinline__ float max_bf16x8(uint4 x, float m) {
@@ -106,14 +112,14 @@ __device__ __forceinline__ void elu1_query_pieces(const uint4 (&raw)[NKB], uint4
     for (int kb = 0; kb < NKB; ++kb) m = max_bf16x8(raw[kb], m);
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const float e = elu1_row_shift(m);
+    const float e = elu1_row_shift(m), cap = elu1_row_cap(e);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         const uint4 x = raw[kb];
-        out[kb].x = cvt2(elu1_hw_scaled(lo_bf16(x.x), e), elu1_hw_scaled(hi_bf16(x.x), e));
-        out[kb].y = cvt2(elu1_hw_scaled(lo_bf16(x.y), e), elu1_hw_scaled(hi_bf16(x.y), e));
-        out[kb].z = cvt2(elu1_hw_scaled(lo_bf16(x.z), e), elu1_hw_scaled(hi_bf16(x.z), e));
-        out[kb].w = cvt2(elu1_hw_scaled(lo_bf16(x.w), e), elu1_hw_scaled(hi_bf16(x.w), e));
+        out[kb].x = cvt2(elu1_hw_scaled(lo_bf16(x.x), e, cap), elu1_hw_scaled(hi_bf16(x.x), e, cap));
+        out[kb].y = cvt2(elu1_hw_scaled(lo_bf16(x.y), e, cap), elu1_hw_scaled(hi_bf16(x.y), e, cap));
+        out[kb].z = cvt2(elu1_hw_scaled(lo_bf16(x.z), e, cap), elu1_hw_scaled(hi_bf16(x.z), e, cap));
+        out[kb].w = cvt2(elu1_hw_scaled(lo_bf16(x.w), e, cap), elu1_hw_scaled(hi_bf16(x.w), e, cap));
     }
 }
 
