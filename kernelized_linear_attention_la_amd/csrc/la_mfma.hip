@@ -205,11 +205,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // chunk takes several load latencies to compute and whose registers are
     // needed by the 8-wave tiles.
     constexpr int DEPTH = (DK == 128 && C == 128) ? 1 : 2;
-    // ELU+1: a prefetched chunk's keys and this lane's query pieces are
-    // mapped in registers at the end of the chunk before the one that stages
-    // them (pre_map), not while every wave stages at once: a wave that
-    // finishes its matrix work early then runs its exponentials while the
-    // other wave of its SIMD is still reading LDS and issuing MFMAs.
+    // ELU+1 with 128-token chunks at d = 128: a prefetched chunk's keys and
+    // this lane's query pieces are mapped in registers at the end of the
+    // chunk before the one that stages them (pre_map), not while every wave
+    // stages at once: a wave that finishes its matrix work early then runs
+    // its exponentials while the other wave of its SIMD is still reading LDS
+    // and issuing MFMAs.  (The other tilings map while staging; there the
+    // exponentials are a smaller share of the chunk.)
     constexpr bool PRE = PHI == kElu1;
     struct Pref {
         Op8 raw[(UK + UV + UQ) / G::THREADS > 0 ? (UK + UV + UQ) / G::THREADS : 1];
@@ -293,10 +295,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = pc;
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + DK + 8 * c8]) = ps;
             } else {
-                // ELU+1 keys arrive mapped (pre_map; retention: raw keys); tokens
-                // past the end get phi = 0, not phi(0) = 1
-                static_assert(RET || PRE, "the remaining maps are ELU+1 and the identity");
-                uint4 ph = p.raw[i].u;
+                // ELU+1 on the way in, unless pre_map has applied it (retention:
+                // raw keys); tokens past the end get phi = 0, not phi(0) = 1
+                uint4 ph;
+                if constexpr (RET || PRE) ph = p.raw[i].u;
+                else ph = elu1_bf16x8(p.raw[i].u);
                 if (!full && tt0 + t >= N) ph = make_uint4(0, 0, 0, 0);
                 *reinterpret_cast<uint4 *>(&sm.K[ks][t * RK + 8 * c8]) = ph;
             }
@@ -390,9 +393,17 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
         } else if constexpr (OUT && !G::XR && RET) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = p.q[kb].u;  // rows past the end are not stored
-        } else if constexpr (OUT && !G::XR) {
+        } else if constexpr (OUT && !G::XR && PRE) {
 #pragma unroll
             for (int kb = 0; kb < KBF; ++kb) phq[kb].u = p.q[kb].u;  // mapped by pre_map
+        } else if constexpr (OUT && !G::XR) {
+            // ELU+1 with the row's power-of-two scale (cancels in the division)
+            uint4 raw[KBF], ph[KBF];
+#pragma unroll
+            for (int kb = 0; kb < KBF; ++kb) raw[kb] = p.q[kb].u;
+            elu1_query_pieces<KBF>(raw, ph);
+#pragma unroll
+            for (int kb = 0; kb < KBF; ++kb) phq[kb].u = ph[kb];
         }
         block_sync_lds();
         fetch(p, step + DEPTH);
@@ -523,6 +534,41 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     }
                 }
             };
+            // epilogue: divide by the normaliser column (retention: none), round,
+            // stage, store 16 B per lane.  At d = 64 it runs inside each
+            // query-block case, so the accumulators never pass a control-flow
+            // join: there the compiler otherwise places some accumulating
+            // products with the destination two registers above the accumulator
+            // input, a placement the matrix cores do not read correctly (the
+            // assembly test scans for it).  At d = 128 one shared copy measured
+            // faster (192 -> 182 us on B2 H16 N16384) and places none.
+            constexpr bool EPI_IN_CASE = DK == 64;
+            auto epilogue = [&]() {
+                float rden[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rden[e] = RET ? 1.f : __builtin_amdgcn_rcpf(__shfl(acc[NJ - 1][e], lane & 48, 64));
+                uint16_t *so = sm.O[w];
+#pragma unroll
+                for (int nb = 0; nb < DV / 16; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        const uint32_t two = RET ? cvt2(acc[nb][e], acc[nb][e + 1])
+                                                 : cvt2(acc[nb][e] * rden[e], acc[nb][e + 1] * rden[e + 1]);
+                        so[(4 * g + e) * RO + 16 * nb + c16] = static_cast<uint16_t>(two);
+                        so[(4 * g + e + 1) * RO + 16 * nb + c16] = static_cast<uint16_t>(two >> 16);
+                    }
+                wave_lds_sync();
+                constexpr int PIECES = 16 * DV / 8;  // 16-byte pieces of the wave's 16 rows
+                const auto ro = make_rsrc(Os + (size_t)t0 * DV, min(C, N - t0) * DV * 2);
+#pragma unroll
+                for (int it = 0; it < PIECES / 64; ++it) {
+                    const int idx = it * 64 + lane;
+                    const int r = idx / (DV / 8), c8 = idx % (DV / 8);
+                    const uint4 val = *reinterpret_cast<const uint4 *>(&so[r * RO + 8 * c8]);
+                    bstore16_nt(ro, 2 * ((16 * qb + r) * DV + 8 * c8), val);
+                }
+            };
             if constexpr (RET) {
                 // retention reads the carried state first, scaled per query row by
                 // lambda^(i+1) (the Lambda of the blockwise form), then adds the intra part
@@ -573,6 +619,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         }
                     }
                 }
+                epilogue();
             } else {
                 // The normalised maps take the query block as a compile-time
                 // constant (qb is wave-uniform): the causal loop becomes straight
@@ -616,33 +663,9 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                         }
                     }
                     inter();
+                    if constexpr (EPI_IN_CASE) epilogue();
                 });
-            }
-            // epilogue: divide by the normaliser column (retention: none), round,
-            // stage, store 16 B per lane
-            float rden[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                rden[e] = RET ? 1.f : __builtin_amdgcn_rcpf(__shfl(acc[NJ - 1][e], lane & 48, 64));
-            uint16_t *so = sm.O[w];
-#pragma unroll
-            for (int nb = 0; nb < DV / 16; ++nb)
-#pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const uint32_t two = RET ? cvt2(acc[nb][e], acc[nb][e + 1])
-                                             : cvt2(acc[nb][e] * rden[e], acc[nb][e + 1] * rden[e + 1]);
-                    so[(4 * g + e) * RO + 16 * nb + c16] = static_cast<uint16_t>(two);
-                    so[(4 * g + e + 1) * RO + 16 * nb + c16] = static_cast<uint16_t>(two >> 16);
-                }
-            wave_lds_sync();
-            constexpr int PIECES = 16 * DV / 8;  // 16-byte pieces of the wave's 16 rows
-            const auto ro = make_rsrc(Os + (size_t)t0 * DV, min(C, N - t0) * DV * 2);
-#pragma unroll
-            for (int it = 0; it < PIECES / 64; ++it) {
-                const int idx = it * 64 + lane;
-                const int r = idx / (DV / 8), c8 = idx % (DV / 8);
-                const uint4 val = *reinterpret_cast<const uint4 *>(&so[r * RO + 8 * c8]);
-                bstore16_nt(ro, 2 * ((16 * qb + r) * DV + 8 * c8), val);
+                if constexpr (!EPI_IN_CASE) epilogue();
             }
         }
 

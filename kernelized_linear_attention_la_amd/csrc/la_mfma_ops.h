@@ -105,14 +105,27 @@ __device__ __forceinline__ float max_bf16x8(uint4 x, float m) {
 // ELU+1 of a query row held as MFMA B-operand pieces (lane l: row l % 16,
 // eight features per piece, pieces of the row spread over the lanes
 // l % 16 + 16 g), with the row's power-of-two scale (elu1_row_shift).
+// A row with a coordinate whose sign bit is clear has qmax >= 0 and scale
+// exponent 0, so the exact maximum is taken only when some row of the wave
+// has every sign bit set (a wave-uniform branch).
 template <int NKB>
 __device__ __forceinline__ void elu1_query_pieces(const uint4 (&raw)[NKB], uint4 (&out)[NKB]) {
-    float m = -__builtin_huge_valf();
+    uint32_t all = ~0u;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) m = max_bf16x8(raw[kb], m);
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const float e = elu1_row_shift(m), cap = elu1_row_cap(e);
+    for (int kb = 0; kb < NKB; ++kb) all &= raw[kb].x & raw[kb].y & raw[kb].z & raw[kb].w;
+    int neg = (all & 0x80008000u) == 0x80008000u;
+    neg &= __shfl_xor(neg, 16, 64);
+    neg &= __shfl_xor(neg, 32, 64);
+    float e = 0.f, cap = 1.f;
+    if (__builtin_amdgcn_ballot_w64(neg) != 0) {
+        float m = -__builtin_huge_valf();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) m = max_bf16x8(raw[kb], m);
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        e = elu1_row_shift(m);
+        cap = elu1_row_cap(e);
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         const uint4 x = raw[kb];
