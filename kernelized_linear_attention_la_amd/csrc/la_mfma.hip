@@ -138,6 +138,29 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
     // retention decay lambda = gamma[h]; lambda^x = exp2(x log2 lambda), 1 at x = 0
     const float l2 = RET ? log2f(a.sh.gamma[bh % a.sh.H]) : 0.f;
     auto dpow = [&](float x) { return x == 0.f ? 1.f : __builtin_amdgcn_exp2f(x * l2); };
+    // Most decay powers of the chunk loop are products of one per-lane power
+    // and wave-uniform powers (scalar registers), every exponent >= 0, so no
+    // factor overflows, lambda = 0 included:
+    //   off-diagonal score tile (jb < qb), lambda^(16(qb-jb) + c16 - 4g - e)
+    //     = lambda^(16(qb-jb-1)) * lambda^(c16 + 12 - 4g) * lambda^(4 - e);
+    //   key weight of slot 4h + j in a full chunk, lambda^(C-1-t) with
+    //   t = 32kt + 16h + 4g + j,
+    //     = lambda^(C-32-32kt) * lambda^(12 - 4g) * lambda^(16(1-h) + 3 - j).
+    // The diagonal tile and a partial last chunk take the exponentials, and
+    // so does d = 64 (whose single pass is the whole-segment kernel): there
+    // the factored form let the compiler place an accumulating product two
+    // registers above its accumulator input, which the assembly test rejects.
+    constexpr bool RFAC = RET && DK == 128;
+    auto uni = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x))); };
+    float dec_lane = 1.f, kw_lane = 1.f, dec_e[4], kw_slot[8];
+    if constexpr (RFAC) {
+        dec_lane = dpow((float)(c16 + 12 - 4 * g));
+        kw_lane = dpow((float)(12 - 4 * g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dec_e[e] = uni(dpow((float)(4 - e)));
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) kw_slot[sl] = uni(dpow((float)(16 * (1 - (sl >> 2)) + 3 - (sl & 3))));
+    }
 
     const T *Qs = static_cast<const T *>(a.Q) + (size_t)bh * N * DK;
     const T *Ks = static_cast<const T *>(a.K) + (size_t)bh * N * DK;
@@ -597,16 +620,17 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                                         ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * kf + 8 * g);
                                         p[h] = mfma(ka, phq[kf], p[h]);
                                     }
-                                    if (jb == qb) {  // causal mask on the diagonal block: key 4g+e <= query c16
+                                    // decay mask lambda^(query - key), 0 above the diagonal
+                                    if (jb == qb || !RFAC) {
 #pragma unroll
-                                        for (int e = 0; e < 4; ++e)
-                                            if (4 * g + e > c16) p[h][e] = 0.f;
-                                    }
-                                    // decay mask lambda^(query - key)
+                                        for (int e = 0; e < 4; ++e) {
+                                            const int d = 16 * (qb - jb) + c16 - 4 * g - e;
+                                            p[h][e] *= d >= 0 ? dpow((float)d) : 0.f;
+                                        }
+                                    } else {
+                                        const float f = uni(dpow((float)(16 * (qb - jb - 1)))) * dec_lane;
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e) {
-                                        const int d = 16 * (qb - jb) + c16 - 4 * g - e;
-                                        p[h][e] *= d >= 0 ? dpow((float)d) : 0.f;
+                                        for (int e = 0; e < 4; ++e) p[h][e] *= f * dec_e[e];
                                     }
                                 }
                             }
@@ -689,14 +713,22 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
                     for (int kt = 0; kt < KBT; ++kt) {
                         Op8 ka = token_operand<RK>(sm.K[ks], kt, 16 * fb, lane);
                         if constexpr (RET) {
-                            // key weight of slot sl: token 32kt + 16(sl/4) + 4g + sl%4
-                            auto kw = [&](int sl) {
-                                const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
-                                return t < Lc ? dpow((float)(Lc - 1 - t)) : 0.f;
-                            };
+                            if (RFAC && Lc == C) {  // full chunk: products of powers
+                                const float f = uni(dpow((float)(C - 32 - 32 * kt))) * kw_lane;
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw(2 * j), hi_bf16(ka.u32[j]) * kw(2 * j + 1));
+                                for (int j = 0; j < 4; ++j)
+                                    ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * (f * kw_slot[2 * j]),
+                                                     hi_bf16(ka.u32[j]) * (f * kw_slot[2 * j + 1]));
+                            } else {
+                                // key weight of slot sl: token 32kt + 16(sl/4) + 4g + sl%4
+                                auto kw = [&](int sl) {
+                                    const int t = 32 * kt + 16 * (sl >> 2) + 4 * g + (sl & 3);
+                                    return t < Lc ? dpow((float)(Lc - 1 - t)) : 0.f;
+                                };
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    ka.u32[j] = cvt2(lo_bf16(ka.u32[j]) * kw(2 * j), hi_bf16(ka.u32[j]) * kw(2 * j + 1));
+                            }
                         }
 #pragma unroll
                         for (int nb = 0; nb < NJ; ++nb)

@@ -151,6 +151,37 @@ def test_extreme_decays_on_the_fp32_matrix_kernels():
         assert state_rel_err(to_f64(S), Sref) < TOL_F32, d
 
 
+@pytest.mark.parametrize("d,chunk", [(128, 128), (128, 64), (64, 64), (64, 128)])
+def test_extreme_decays_on_the_bf16_matrix_kernels(d, chunk):
+    # One decay per head through the bf16 matrix-core kernels (d = 128 forms most
+    # of its decay powers as products of powers): lambda = 0, 1e-4, 0.5, 0.9,
+    # 0.999, 1; several segments, a ragged last chunk, a carried state.  Heads
+    # whose rows are (nearly) one dot product (lambda = 0, 1e-4) are held to the
+    # forward-error bound, as in the fp32 test above; the others to the per-row
+    # metric.
+    gam = np.array([0.0, 1e-4, 0.5, 0.9, 0.999, 1.0], dtype=np.float32)
+    B, H, N = 2, 6, 1500
+    _say("bf16 extreme decays d", d, "chunk", chunk, "N", N)
+    fi = inputs.custom_inputs(77 + d + chunk, B, H, N, d, d, scale=d ** -0.5, dtype="bf16")
+    q, k, v = to_device(fi.Q), to_device(fi.K), to_device(fi.V)
+    S0 = (np.random.default_rng(d + chunk).standard_normal((B, H, d, d)) * 0.1).astype(np.float32)
+    S = torch.zeros(B, H, d, d, device="cuda")
+    O = la.la_forward_retention_chunked(q, k, v, _gam(gam), chunk, S_in=torch.from_numpy(S0).cuda(), S_out=S)
+    g64 = gam.astype(np.float64)
+    ref, Sref = oracle.retention_recurrent("identity", fi.Q.f32, fi.K.f32, fi.V.f32, g64, S_in=S0)
+    mag, _ = oracle.retention_recurrent("identity", np.abs(fi.Q.f32), np.abs(fi.K.f32), np.abs(fi.V.f32), g64,
+                                        S_in=np.abs(S0))
+    torch.cuda.synchronize()
+    got = to_f64(O)
+    assert np.isfinite(got).all()
+    fwd = (np.abs(got[:, :2] - ref[:, :2]).max(-1) / np.abs(mag[:, :2]).max(-1)).max()
+    per_row = row_rel_err(got[:, 2:], ref[:, 2:])
+    _say("forward-error bound (lambda 0, 1e-4)", f"{fwd:.2e}", "per-row (lambda >= 0.5)", f"{per_row:.2e}")
+    assert fwd < TOL_BF16
+    assert per_row < TOL_BF16
+    assert state_rel_err(to_f64(S), Sref) < TOL_BF16
+
+
 def test_handoff_in_place_state_and_chunk_invariance():
     """forward(0..M) then forward(M..N) from its state (S_in aliasing S_out) == forward(0..N), for each chunk."""
     for dtype, d in (("f32", 64), ("bf16", 64), ("bf16", 128)):
