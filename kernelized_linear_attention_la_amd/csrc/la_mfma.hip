@@ -560,12 +560,13 @@ __global__ __launch_bounds__(C / 16 * 64) void k_mfma(FwdArgs a) {
             // epilogue: divide by the normaliser column (retention: none), round,
             // stage, store 16 B per lane.  At d = 64 it runs inside each
             // query-block case, so the accumulators never pass a control-flow
-            // join: there the compiler otherwise places some accumulating
+            // join: for ELU+1 the compiler otherwise places some accumulating
             // products with the destination two registers above the accumulator
             // input, a placement the matrix cores do not read correctly (the
-            // assembly test scans for it).  At d = 128 one shared copy measured
-            // faster (192 -> 182 us on B2 H16 N16384) and places none.
-            constexpr bool EPI_IN_CASE = DK == 64;
+            // assembly test scans for it), and DPFP and cos/sin measured 0.5 us
+            // faster so.  cosFormer (2 us less) and d = 128 (B2 H16 N16384: 182
+            // against 192 us) keep one shared copy, which places none.
+            constexpr bool EPI_IN_CASE = DK == 64 && PHI != kCosformer;
             auto epilogue = [&]() {
                 float rden[4];
 #pragma unroll
