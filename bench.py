@@ -868,13 +868,15 @@ def measure_extras(args):
     with its bf16 matrix-core fraction (c5), each kernel timed by HIP events."""
     import torch
     from kernelized_linear_attention_la_amd import inputs
-    # 200 steps: the first graph launch's latency inside the timed loop is then
-    # well under 1% of the loop
-    short = argparse.Namespace(steps=max(1, min(args.steps, 200)), warmup=max(1, min(args.warmup, 5)))
+    # at least 100 ms of timed work each (decode ~0.2 ms, FAVOR+ ~0.07 ms per
+    # step) after 10 warm-up steps; the first graph launch's latency inside a
+    # timed loop is then well under 1% of it
+    dec_args = argparse.Namespace(steps=max(1, args.steps), warmup=max(1, min(args.warmup, 10)))
+    fav_args = argparse.Namespace(steps=max(1, 3 * args.steps), warmup=max(1, min(args.warmup, 10)))
     out = {}
     wl = inputs.WORKLOADS[EXTRA_DECODE]
-    value, ms, roof, dex, _ = bench_decode(short, wl)
-    out["decode"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": short.steps,
+    value, ms, roof, dex, _ = bench_decode(dec_args, wl)
+    out["decode"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": dec_args.steps,
                      "prefix_forward_ms": dex["prefix_forward_ms"], "prefix_forward_kernel": dex["prefix_forward_kernel"],
                      "kernel": roof["kernel"], "kernel_avg_us": roof["kernel_avg_us"],
                      "hbm_achieved_GBps": roof["achieved"], "hbm_frac": roof["frac"], "traffic": roof["traffic"],
@@ -882,10 +884,10 @@ def measure_extras(args):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     wl = inputs.WORKLOADS[EXTRA_FAVOR]
-    value, ms, roof, ex, _ = bench_forward(short, wl)
+    value, ms, roof, ex, _ = bench_forward(fav_args, wl)
     kern_s = roof["kernel_avg_us"] * 1e-6
     flops = forward_alg_flops(wl)
-    out["favor"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": short.steps,
+    out["favor"] = {"workload": wl.name, "tokens_per_s": value, "ms_per_step": ms, "steps": fav_args.steps,
                     "kernel": roof["kernel"], "kernel_avg_us": roof["kernel_avg_us"],
                     "alg_flops_per_launch": flops,
                     "mfma_achieved_TFs": flops / kern_s / 1e12,
@@ -900,7 +902,7 @@ def measure_extras(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)  # >= 100 ms of timed work on the long-context workload
+    ap.add_argument("--steps", type=int, default=600)  # >= 100 ms of timed work on the long-context workload
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget; 0 skips it")
