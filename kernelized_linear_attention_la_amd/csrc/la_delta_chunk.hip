@@ -77,12 +77,15 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, fl
 // g [64], g_C / g [64].
 __host__ __device__ inline size_t delta_rec_floats(int dv) { return 2 * kXC * kXK + (size_t)kXC * dv + 2 * kXC; }
 
-template <typename T>
+// DVM: the largest d_v the instance takes (64 or 128); the right-hand sides
+// are sized for it, so at d_v <= 64 the workgroup needs 69 KB of LDS and two
+// of them share a CU.
+template <typename T, int DVM>
 __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, const T *__restrict__ K,
                                                     const T *__restrict__ V, const float *__restrict__ alpha,
                                                     const float *__restrict__ beta, int N, int dv, int n_chunks,
                                                     float *__restrict__ ws) {
-    constexpr int RX = kXK + 128 + 4;  // row stride of the right-hand sides / solution [64][64 + d_v]
+    constexpr int RX = kXK + DVM + 4;  // row stride of the right-hand sides / solution [64][64 + d_v]
     // sQ is only read by the Gram tiles; the right-hand sides reuse its space afterwards
     __shared__ float sK[kXC * kXR], sM[kXC * kXR];
     __shared__ float sQX[kXC * RX];
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
     // chunk rows in 16-byte pieces, all in flight at once (rows past the end: zero)
     constexpr int EP = 16 / (int)sizeof(T);                    // elements per piece
     constexpr int QP = kXC * kXK / EP / kXT;                   // pieces of Q (and of K) per thread
-    constexpr int VP = kXC * 128 / EP / kXT;                   // pieces of V per thread, at most
+    constexpr int VP = kXC * DVM / EP / kXT;                   // pieces of V per thread, at most
     const char *qb = reinterpret_cast<const char *>(Q + tok0 * kXK);
     const char *kb = reinterpret_cast<const char *>(K + tok0 * kXK);
     const char *vb = reinterpret_cast<const char *>(V + tok0 * dv);
@@ -447,16 +450,20 @@ hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStrea
     if (dtype == kF32) {
         auto *q = static_cast<const float *>(a.Q), *k = static_cast<const float *>(a.K),
              *v = static_cast<const float *>(a.V);
-        e = launch_kernel_ev(k_delta_prep<float>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta, a.N, a.dv,
-                             n_chunks, ws);
+        e = a.dv <= 64 ? launch_kernel_ev(k_delta_prep<float, 64>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
+                                          a.N, a.dv, n_chunks, ws)
+                       : launch_kernel_ev(k_delta_prep<float, 128>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
+                                          a.N, a.dv, n_chunks, ws);
         if (e != hipSuccess) return e;
         return launch_kernel_ev(k_delta_scan<float>, gs, blk, 0, st, ev_scan, q, k, static_cast<float *>(a.O),
                                 static_cast<const float *>(ws), a.S_in, a.S_out, a.N, a.dv, n_chunks);
     }
     auto *q = static_cast<const uint16_t *>(a.Q), *k = static_cast<const uint16_t *>(a.K),
          *v = static_cast<const uint16_t *>(a.V);
-    e = launch_kernel_ev(k_delta_prep<uint16_t>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta, a.N, a.dv,
-                         n_chunks, ws);
+    e = a.dv <= 64 ? launch_kernel_ev(k_delta_prep<uint16_t, 64>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
+                                      a.N, a.dv, n_chunks, ws)
+                   : launch_kernel_ev(k_delta_prep<uint16_t, 128>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
+                                      a.N, a.dv, n_chunks, ws);
     if (e != hipSuccess) return e;
     return launch_kernel_ev(k_delta_scan<uint16_t>, gs, blk, 0, st, ev_scan, q, k, static_cast<uint16_t *>(a.O),
                             static_cast<const float *>(ws), a.S_in, a.S_out, a.N, a.dv, n_chunks);

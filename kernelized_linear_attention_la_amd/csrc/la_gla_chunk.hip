@@ -66,6 +66,17 @@ struct GlaSmem {
     int big[kNW];          // diagonal block b decays by more than 2^86 in some channel
 };
 
+// The per-chunk preparation (k_gla_prep) uses only the first fields: its own
+// 53 KB layout lets two of its workgroups share a CU (the one-launch kernel's
+// layout, 97 KB, allows one).
+struct GlaPrepSmem {
+    float Q[kC][kRS];
+    float K[kC][kRS];
+    float L[kC][kRS];
+    float tot[4][kK];
+    int big[kNW];
+};
+
 // 16 consecutive floats of an LDS row (16-byte aligned) into registers
 __device__ __forceinline__ void row16(const float *p, float (&r)[16]) {
 #pragma unroll
@@ -331,7 +342,7 @@ __host__ __device__ inline size_t gla_rec_floats() { return 3 * kC * kK + kK; }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks, float *__restrict__ ws) {
-    __shared__ __align__(16) GlaSmem sm;
+    __shared__ __align__(16) GlaPrepSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
