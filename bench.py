@@ -280,7 +280,7 @@ def backward_tile(wl):
 
 
 def gla_on_chunks(wl):
-    """GLA in chunkwise form on fp32 matrix instructions (d_k <= 64): the two-launch entry point."""
+    """GLA in chunkwise form on fp32 matrix instructions (d_k <= 64): the three-launch entry point."""
     return wl.gated == "gla" and wl.dk <= 64
 
 
@@ -300,7 +300,7 @@ def kernel_symbol(wl, slot):
         if delta_on_chunks(wl):
             return f"k_delta_scan<{t}>"  # the longer of the chunkwise form's two launches
         if gla_on_chunks(wl):
-            return f"k_gla_scan<{t}>"  # the scan of the two-launch form
+            return f"k_gla_prep<{t}>"  # the longest of the chunkwise form's three launches
         return f"k_gated<{t}, {'true' if wl.gated == 'gla' else 'false'}>"
     if wl.decode_steps and slot == "decode":
         t = "float" if wl.dtype == "f32" else "unsigned short"
@@ -698,9 +698,12 @@ def bench_gated(args, wl):
     kern_ms = sum(durs) / len(durs)
     extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
     if chunked:
-        # the two launches of the chunkwise form timed one by one through the
-        # library's hook (per-chunk solves, then the scan over chunks)
-        slots = (la.LA_KSLOT_STATE, la.LA_KSLOT_CHUNK)
+        # the launches of the chunkwise form timed one by one through the
+        # library's hook: GLA's per-chunk products, state chain and outputs;
+        # the delta rule's per-chunk solves and scan over chunks
+        names = ({la.LA_KSLOT_STATE: "k_gla_prep", la.LA_KSLOT_SCAN: "k_gla_chain", la.LA_KSLOT_CHUNK: "k_gla_out"}
+                 if wl.gated == "gla" else {la.LA_KSLOT_STATE: "k_delta_prep", la.LA_KSLOT_CHUNK: "k_delta_scan"})
+        slots = tuple(names)
         kd = {sl: [] for sl in slots}
         for _ in range(args.steps):
             kev = la.LaKernelEvents()
@@ -713,14 +716,12 @@ def bench_gated(args, wl):
                 kd[sl].append(hev.elapsed_ms(*ev[sl]))
                 hev.destroy(ev[sl][0])
                 hev.destroy(ev[sl][1])
-        pre = "k_gla" if wl.gated == "gla" else "k_delta"
-        extra = {"kernel_avg_us": {pre + "_prep": round(1e3 * sum(kd[slots[0]]) / len(kd[slots[0]]), 2),
-                                   pre + "_scan": round(1e3 * sum(kd[slots[1]]) / len(kd[slots[1]]), 2)},
+        extra = {"kernel_avg_us": {names[sl]: round(1e3 * sum(kd[sl]) / len(kd[sl]), 2) for sl in slots},
                  "step_kernels_us": round(kern_ms * 1e3, 2)}
     flops = gated_alg_flops(wl)
     ach = flops / (kern_ms * 1e-3) / 1e12
-    kname = ("k_gla_prep + k_gla_scan" if wl.gated == "gla" else "k_delta_prep + k_delta_scan") if chunked \
-        else kernel_symbol(wl, "chunk")
+    kname = ("k_gla_prep + k_gla_chain + k_gla_out" if wl.gated == "gla" else "k_delta_prep + k_delta_scan") \
+        if chunked else kernel_symbol(wl, "chunk")
     # fp32 arithmetic: the chunkwise forms on the matrix cores (dense fp32 MFMA peak),
     # the token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own,
     # over the step's kernels (for the chunkwise delta rule both launches)
@@ -729,7 +730,7 @@ def bench_gated(args, wl):
     roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
             "frac": ach / peak, "traffic": None if chunked else stored_traffic(wl, kname), "kernel": kname,
             "kernel_avg_us": kern_ms * 1e3, "alg_flops_per_launch": flops,
-            "timing": "hip events around each call (both launches of the chunkwise form)"}
+            "timing": "hip events around each call (every launch of the chunkwise form)"}
     tokens = wl.B * wl.H * wl.N
     return tokens / (ms_per_step * 1e-3), ms_per_step, roof, extra, gi
 

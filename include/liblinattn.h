@@ -398,19 +398,24 @@ la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const v
 size_t la_delta_workspace_bytes(const la_problem *p, int chunk);
 
 /*
- * GLA (la_forward_gla_recurrent) in two launches: the chunk form's products
- * that do not involve the values (gate sums, decayed keys and queries, the
- * masked pair scores with their overflow-safe pivot split) are formed once
- * per 64-token chunk, every chunk at once; then each (b, h) slice walks its
- * chunks per 16 value columns: O = QD S0 + P V, S_C = diag(decay) S0 + KE V.
- * The same sums as the one-launch chunk form.  Arguments as
- * la_forward_gla_recurrent, plus: chunk must be 64 and p->d_k <= 64 (else
- * LA_ERR_UNSUPPORTED); any N >= 1; ws: device workspace of at least
- * la_gla_workspace_bytes(p, chunk) bytes (16-byte aligned, no initial
- * contents; its first 256 bytes are left untouched, then one record of
- * 3 x 64 x 64 + 64 floats per (b, h, chunk)), else
- * LA_ERR_WORKSPACE; ev: optional timing hook (LA_KSLOT_STATE: the per-chunk
- * launch, LA_KSLOT_CHUNK: the scan).  S_out may alias S_in.
+ * GLA (la_forward_gla_recurrent) in chunkwise form, three launches ("Linear
+ * Attention", gated linear attention; chunkwise parallel form).  With S_c
+ * the state entering 64-token chunk c, O_c = QD_c S_c + P_c V_c and
+ * S_{c+1} = diag(decay_c) S_c + KE_c^T V_c, where QD are the decayed
+ * queries, P the masked pair scores (overflow-safe pivot split), KE the
+ * decayed keys and decay the chunk's gate product per key channel.
+ *   1. every chunk at once: QD, P, KE, decay, P V and KE^T V;
+ *   2. the state chain, element by element over the chunks (the only serial
+ *      step): S_c of every chunk, S_out;
+ *   3. every chunk at once: O = QD S_c + P V.
+ * Arguments as la_forward_gla_recurrent, plus: chunk must be 64 and
+ * p->d_k <= 64 (else LA_ERR_UNSUPPORTED); any N >= 1; ws: device workspace
+ * of at least la_gla_workspace_bytes(p, chunk) bytes (16-byte aligned, no
+ * initial contents; its first 256 bytes are left untouched, then one record
+ * of 64 x 64 + 2 x 64 x dvp + 64 floats per (b, h, chunk), dvp = d_v rounded
+ * up to 16), else LA_ERR_WORKSPACE; ev: optional timing hook (LA_KSLOT_STATE:
+ * the per-chunk products, LA_KSLOT_SCAN: the state chain, LA_KSLOT_CHUNK: the
+ * outputs).  S_out may alias S_in.
  */
 size_t la_gla_workspace_bytes(const la_problem *p, int chunk);
 

@@ -93,7 +93,8 @@ KERNEL_SOURCES = {
     "k_gated": ("la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gla_chunk": ("la_gla_chunk.hip", "la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gla_prep": ("la_gla_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
-    "k_gla_scan": ("la_gla_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_gla_chain": ("la_gla_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_gla_out": ("la_gla_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dq_mfma": ("la_backward_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_bwd_dkv_mfma": ("la_backward_mfma.hip", "la_device.h", "la_internal.h", "la_api.hip"),
 }

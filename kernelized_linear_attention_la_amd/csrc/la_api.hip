@@ -665,7 +665,7 @@ LA_API la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, 
 
 LA_API size_t la_gla_workspace_bytes(const la_problem *p, int chunk) {
     if (la::check_problem(p) != LA_OK || p->phi != LA_PHI_IDENTITY || p->d_k > 64 || chunk != 64) return 0;
-    return la::kCtlBytes + la::gla_chunk_ws_bytes(p->B * p->H, p->N);
+    return la::kCtlBytes + la::gla_chunk_ws_bytes(p->B * p->H, p->N, p->d_v);
 }
 
 LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const void *Q, const void *K, const void *V,
@@ -680,7 +680,7 @@ LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const vo
     for (const void *q : ptrs)
         if (!aligned16(q)) return LA_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(alpha) & 3u) return LA_ERR_ALIGN;
-    if (!ws || ws_bytes < kCtlBytes + gla_chunk_ws_bytes(p->B * p->H, p->N)) return LA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < kCtlBytes + gla_chunk_ws_bytes(p->B * p->H, p->N, p->d_v)) return LA_ERR_WORKSPACE;
     if (ev)
         for (int i = 0; i < LA_KSLOTS; ++i) ev->launched[i] = 0;
     GatedArgs a;
@@ -692,7 +692,7 @@ LA_API la_status la_forward_gla_chunked(const la_problem *p, int chunk, const vo
     return launch_gla_split(a, p->dtype == LA_BF16 ? kBF16 : kF32,
                             reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes),
                             static_cast<hipStream_t>(stream), slot_events(ev, LA_KSLOT_STATE),
-                            slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
+                            slot_events(ev, LA_KSLOT_SCAN), slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
                ? LA_OK
                : LA_ERR_DEVICE;
 }

@@ -66,13 +66,13 @@ struct GlaSmem {
     int big[kNW];          // diagonal block b decays by more than 2^86 in some channel
 };
 
-// The per-chunk preparation (k_gla_prep) uses only the first fields: its own
-// 53 KB layout lets two of its workgroups share a CU (the one-launch kernel's
-// layout, 97 KB, allows one).
+// The per-chunk preparation (k_gla_prep) has its own 70 KB layout, so two of
+// its workgroups share a CU (the one-launch kernel's layout, 97 KB, allows one).
 struct GlaPrepSmem {
-    float Q[kC][kRS];
+    float Q[kC][kRS];   // q rows; later V^T [value column][token]
     float K[kC][kRS];
     float L[kC][kRS];
+    float KE[kK][kRS];  // decayed keys [channel][token]
     float tot[4][kK];
     int big[kNW];
 };
@@ -325,35 +325,46 @@ __global__ __launch_bounds__(kThreads) void k_gla_chunk(GatedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The same chunk form in two launches (la_forward_gla_chunked).  Everything
-// above that does not depend on the value columns -- the gate sums, the
-// decayed keys KE[c][t] = k_tc 2^{l_last,c - l_tc}, the masked pair scores
-// P[i][t] (pivot split, element-wise diagonal block for extreme decays), the
-// decayed queries QD[i][c] = q_ic 2^{l_ic - l_start,c} and the chunk decay
-// 2^{l_last,c - l_start,c} -- is formed once per chunk by k_gla_prep (one
-// workgroup per (slice, chunk), every chunk at once) into a workspace record;
-// k_gla_scan then walks the chunks of each (slice, 16 value columns) with only
-// the three products that touch the values:
-//   O = QD S_0 + P V,   S_C = diag(decay) S_0 + KE V.
+// The same chunk form in three launches (la_forward_gla_chunked).  Given the
+// state S_c entering chunk c, the chunk's outputs and the next state are
+//   O = QD S_c + P V,   S_{c+1} = diag(decay) S_c + KE^T V,
+// with the decayed queries QD[i][ch] = q_i,ch 2^{l_i,ch - l_start,ch}, the
+// masked pair scores P (pivot split, element-wise diagonal block for extreme
+// decays), the decayed keys KE[t][ch] = k_t,ch 2^{l_last,ch - l_t,ch} and the
+// chunk decay 2^{l_last - l_start}.  P V and KE^T V do not involve the state,
+// so the only serial step from chunk to chunk is element-wise:
+//  1. k_gla_prep, one workgroup per (slice, chunk), every chunk at once:
+//     gate sums, QD, P, KE, decay, and the products P V and KE^T V, into a
+//     workspace record;
+//  2. k_gla_chain, one thread per four state entries: S_c for every chunk
+//     from S_in by S_{c+1} = decay (.) S_c + (KE^T V)_c (written over the
+//     chunk's KE^T V in its record), S_out at the end;
+//  3. k_gla_out, one workgroup per (slice, chunk): O = QD S_c + P V.
 // ---------------------------------------------------------------------------
 
-// Per-chunk record (floats): P [64][64], QD [64][64], KE [64][64], decay [64].
-__host__ __device__ inline size_t gla_rec_floats() { return 3 * kC * kK + kK; }
+// Per-chunk record (floats), dvp = d_v rounded up to 16:
+//   QD [64 tokens][64 channels]
+//   PVT [dvp][64 tokens]      (P V)^T
+//   KST [dvp][64 channels]    (KE^T V)^T; after k_gla_chain S_c^T
+//   DEC [64]                  the chunk's decay per channel
+__host__ __device__ inline int gla_dvp(int dv) { return (dv + kNC - 1) / kNC * kNC; }
+__host__ __device__ inline size_t gla_rec_floats(int dvp) { return (size_t)kC * kK + 2 * (size_t)dvp * kC + kK; }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks, float *__restrict__ ws) {
+__global__ __launch_bounds__(kThreads, 2) void k_gla_prep(GatedArgs a, int n_chunks, float *__restrict__ ws) {
     __shared__ __align__(16) GlaPrepSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int dk = a.dk, N = a.N;
+    const int dk = a.dk, dv = a.dv, dvp = gla_dvp(dv), N = a.N;
     const int bh = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks;
     const int t0 = ch * kC, nt = min(kC, N - t0);
     const T *Q = static_cast<const T *>(a.Q) + (size_t)bh * N * dk;
     const T *K = static_cast<const T *>(a.K) + (size_t)bh * N * dk;
+    const T *V = static_cast<const T *>(a.V) + (size_t)bh * N * dv;
     const float *Al = a.alpha + (size_t)bh * N * dk;
-    float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats();
-    float *P = rec, *QD = rec + kC * kK, *KE = rec + 2 * kC * kK, *DEC = rec + 3 * kC * kK;
+    float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats(dvp);
+    float *QD = rec, *PVT = rec + kC * kK, *KST = PVT + (size_t)dvp * kC, *DEC = KST + (size_t)dvp * kK;
     auto as_f32 = [](T x) {
         if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
         else return static_cast<float>(x);
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
     // stage q, k (zero past the end and in padded channels) and the log2
     // gates (1 there) summed within each 16-token quarter: thread = channel
     // tid % 64, tokens 16 (tid / 64) .. +15
-    const int sc = tid & 63, sq = tid >> 6;
+    const int sc = tid & 63, sq = w;  // sq wave-uniform: the token tests below stay scalar
     float kf[16], lf[16];
     {
         // all loads first, unconditional (clamped indices), then the selects
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
         sm.tot[sq][sc] = acc;
     }
     lds_barrier();
-    // decayed keys k_t 2^{l_last - l_t} ([feature][token]) and the diagonal-block check
+    // decayed keys k_t 2^{l_last - l_t} ([channel][token]) and the diagonal-block check
     {
         float later = 0.f;
 #pragma unroll
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
         const float own = lf[15];
 #pragma unroll
         for (int j = 0; j < 16; j += 4)
-            *reinterpret_cast<float4 *>(&KE[sc * kC + 16 * sq + j]) =
+            *reinterpret_cast<float4 *>(&sm.KE[sc][16 * sq + j]) =
                 make_float4(kf[j] * ex2((own - lf[j]) + later), kf[j + 1] * ex2((own - lf[j + 1]) + later),
                             kf[j + 2] * ex2((own - lf[j + 2]) + later), kf[j + 3] * ex2((own - lf[j + 3]) + later));
         const float dmax = lf[0] - lf[15];
@@ -412,7 +423,10 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
     }
     lds_barrier();
 
-    // scores and decayed queries of query block I = w (as in k_gla_chunk)
+    // scores of query block I = w, transposed: accumulator lane (4g+e, c16)
+    // of key block Tb holds P[16I + c16][16Tb + 4g + e], which is the B
+    // operand of the value product below as it stands (k-slot g of step
+    // (Tb, e) = token 16Tb + 4g + e)
     const int I = w;
     float qp[16], piv[16];
     {
@@ -426,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
     float span[16];
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) span[ks] = 0.f;
+    f32x4 pt[4];
     {
-        f32x4 p[4];
         float kb[4][16];
 #pragma unroll
         for (int Tb = 3; Tb >= 0; --Tb) {
@@ -443,39 +457,86 @@ __global__ __launch_bounds__(kThreads) void k_gla_prep(GatedArgs a, int n_chunks
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks)
                 kb[Tb][ks] = kr[ks] * ex2(fminf(span[ks] + (piv[ks] - lt[ks]), kPivotBound));
-            p[Tb] = zero4();
+            pt[Tb] = zero4();
         }
+        // QD[i][c] = q_ic 2^{l_i - l_start} = qp 2^{piv + totals of blocks 0..I-1}
+#pragma unroll
+        for (int ks = 0; ks < 16; ks += 4)
+            *reinterpret_cast<float4 *>(&QD[(16 * I + c16) * kK + 16 * g + ks]) =
+                make_float4(qp[ks] * ex2(piv[ks] + span[ks]), qp[ks + 1] * ex2(piv[ks + 1] + span[ks + 1]),
+                            qp[ks + 2] * ex2(piv[ks + 2] + span[ks + 2]), qp[ks + 3] * ex2(piv[ks + 3] + span[ks + 3]));
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
-            for (int Tb = 0; Tb < 4; ++Tb) p[Tb] = mma(qp[ks], kb[Tb][ks], p[Tb]);
+            for (int Tb = 0; Tb < 4; ++Tb) pt[Tb] = mma(kb[Tb][ks], qp[ks], pt[Tb]);
         const bool big = sm.big[I] != 0;
         f32x4 pd = zero4();
         if (big) {  // diagonal block element by element: sum_c q_ic k_tc 2^{l_ic - l_tc}, t <= i
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * g + e, t = 16 * I + c16;
+                const int t = 16 * I + 4 * g + e, i = 16 * I + c16;
                 float sacc = 0.f;
                 if (t <= i)
                     for (int c = 0; c < kK; ++c) sacc += sm.Q[i][c] * sm.K[t][c] * ex2(sm.L[i][c] - sm.L[t][c]);
                 pd[e] = sacc;
             }
         }
+        // causal mask: key 16Tb + 4g + e <= query 16I + c16
 #pragma unroll
-        for (int Tb = 0; Tb < 4; ++Tb) {
-            const f32x4 pv4 = (big && Tb == I) ? pd : p[Tb];
+        for (int Tb = 0; Tb < 4; ++Tb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                P[(16 * I + 4 * g + e) * kC + 16 * Tb + c16] =
-                    (Tb < I || (Tb == I && 4 * g + e >= c16)) ? pv4[e] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const float v = (big && Tb == I) ? pd[e] : pt[Tb][e];
+                pt[Tb][e] = (Tb < I || (Tb == I && 4 * g + e <= c16)) ? v : 0.f;
+            }
+    }
+    // value products, 64 columns at a time: V^T [column][token] goes to the
+    // rows of sm.Q; wave w
+    // forms (P V)^T for its query block and (KE^T V)^T for channels 16w..16w+15,
+    // both with A = V^T (lane: column c16, tokens 16Tb + 4g..+3)
+    for (int cg = 0; cg < dvp; cg += 64) {
+        T rv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = 16 * sq + j;
+            const bool in = t < nt && cg + sc < dv;
+            rv[j] = V[(size_t)(t0 + (in ? t : 0)) * dv + (in ? cg + sc : 0)];
+        }
+        float vr[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) vr[j] = (16 * sq + j < nt && cg + sc < dv) ? as_f32(rv[j]) : 0.f;
+        lds_barrier();  // every read of the staged rows (scores, QD; the previous column group) done
+#pragma unroll
+        for (int j = 0; j < 16; j += 4)
+            *reinterpret_cast<float4 *>(&sm.Q[sc][16 * sq + j]) = make_float4(vr[j], vr[j + 1], vr[j + 2], vr[j + 3]);
+        lds_barrier();
+#pragma unroll 1
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = cg + 16 * cb;
+            if (col < dvp) {  // wave-uniform
+                f32x4 pv = zero4(), kv = zero4();
+#pragma unroll
+                for (int Tb = 0; Tb < 4; ++Tb) {
+                    const float4 va = *reinterpret_cast<const float4 *>(&sm.Q[16 * cb + c16][16 * Tb + 4 * g]);
+                    const float4 kk = *reinterpret_cast<const float4 *>(&sm.KE[16 * w + c16][16 * Tb + 4 * g]);
+                    pv = mma(va.x, pt[Tb][0], pv);
+                    kv = mma(va.x, kk.x, kv);
+                    pv = mma(va.y, pt[Tb][1], pv);
+                    kv = mma(va.y, kk.y, kv);
+                    pv = mma(va.z, pt[Tb][2], pv);
+                    kv = mma(va.z, kk.z, kv);
+                    pv = mma(va.w, pt[Tb][3], pv);
+                    kv = mma(va.w, kk.w, kv);
+                }
+                // lane (4g+e, c16): (P V)[16I + c16][col + 4g + e], (KE^T V)[16w + c16][col + 4g + e]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    PVT[(size_t)(col + 4 * g + e) * kC + 16 * I + c16] = pv[e];
+                    KST[(size_t)(col + 4 * g + e) * kK + 16 * w + c16] = kv[e];
+                }
+            }
         }
     }
-    // QD[i][c] = q_ic 2^{l_i - l_start} = qp 2^{piv + totals of blocks 0..I-1}
-#pragma unroll
-    for (int ks = 0; ks < 16; ks += 4)
-        *reinterpret_cast<float4 *>(&QD[(16 * I + c16) * kK + 16 * g + ks]) =
-            make_float4(qp[ks] * ex2(piv[ks] + span[ks]), qp[ks + 1] * ex2(piv[ks + 1] + span[ks + 1]),
-                        qp[ks + 2] * ex2(piv[ks + 2] + span[ks + 2]), qp[ks + 3] * ex2(piv[ks + 3] + span[ks + 3]));
 }
 
 // One output element through a buffer store: an offset past the resource's
@@ -491,124 +552,110 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, fl
     else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
-// One workgroup per (slice, 16 value columns), the chunks in order; wave w
-// owns token rows 16w..16w+15 of O and feature rows 16w..16w+15 of the state.
-// Row operands (QD, P, KE rows) come straight from the record into registers
-// one chunk ahead; k-step j of lane group q takes index 16q + j.
+// The state entering every chunk: S_0 = S_in, S_{c+1} = decay_c (.) S_c +
+// (KE^T V)_c, element by element.  Thread: one value column and four
+// channels of one slice; the records of the next kRing chunks are in flight
+// (their loads do not depend on the state).  S_c overwrites (KE^T V)_c in
+// the record once read (same thread, same address: program order).
+constexpr int kRing = 8;
+__global__ __launch_bounds__(256) void k_gla_chain(GatedArgs a, int n_chunks, float *__restrict__ ws) {
+    const int dk = a.dk, dv = a.dv, dvp = gla_dvp(dv);
+    const int per_slice = dvp * (kK / 4);
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    if (gid >= a.BH * per_slice) return;  // no barriers in this kernel
+    const int bh = gid / per_slice, rem = gid % per_slice, col = rem / (kK / 4), f0 = 4 * (rem % (kK / 4));
+    const size_t recf = gla_rec_floats(dvp);
+    float *const base = ws + (size_t)bh * n_chunks * recf;
+    const size_t kst = (size_t)kC * kK + (size_t)dvp * kC + (size_t)col * kK + f0;
+    const size_t dec = (size_t)kC * kK + 2 * (size_t)dvp * kC + f0;
+
+    float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.S_in && col < dv) {
+        const float *si = a.S_in + (size_t)bh * dk * dv + col;
+        S.x = f0 < dk ? si[(size_t)f0 * dv] : 0.f;
+        S.y = f0 + 1 < dk ? si[(size_t)(f0 + 1) * dv] : 0.f;
+        S.z = f0 + 2 < dk ? si[(size_t)(f0 + 2) * dv] : 0.f;
+        S.w = f0 + 3 < dk ? si[(size_t)(f0 + 3) * dv] : 0.f;
+    }
+    float4 kv[kRing], dc[kRing];
+    auto fetch = [&](int r, int c) {  // past the end: a harmless re-read of the last chunk
+        const float *rec = base + (size_t)min(c, n_chunks - 1) * recf;
+        kv[r] = *reinterpret_cast<const float4 *>(rec + kst);
+        dc[r] = *reinterpret_cast<const float4 *>(rec + dec);
+    };
+    auto step = [&](int r, int c) {
+        float4 *dst = reinterpret_cast<float4 *>(base + (size_t)c * recf + kst);
+        const float4 sc = S;
+        S = make_float4(fmaf(dc[r].x, S.x, kv[r].x), fmaf(dc[r].y, S.y, kv[r].y), fmaf(dc[r].z, S.z, kv[r].z),
+                        fmaf(dc[r].w, S.w, kv[r].w));
+        *dst = sc;
+    };
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) fetch(r, r);
+    int c = 0;
+    for (; c + kRing <= n_chunks; c += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+            step(r, c + r);
+            fetch(r, c + r + kRing);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRing; ++r)
+        if (c + r < n_chunks) step(r, c + r);
+    if (a.S_out && col < dv) {
+        float *so = a.S_out + (size_t)bh * dk * dv + col;
+        if (f0 < dk) so[(size_t)f0 * dv] = S.x;
+        if (f0 + 1 < dk) so[(size_t)(f0 + 1) * dv] = S.y;
+        if (f0 + 2 < dk) so[(size_t)(f0 + 2) * dv] = S.z;
+        if (f0 + 3 < dk) so[(size_t)(f0 + 3) * dv] = S.w;
+    }
+}
+
+// O = QD S_c + P V, one workgroup per (slice, chunk); wave w owns token rows
+// 16w..16w+15.  A = QD rows (k-slot g of step ks = channel 16g + ks), B = S_c
+// (lane: column c16, channels 16g..16g+15, a contiguous run of the record's
+// S_c^T), C = (P V) rows; every load of the chunk is issued before the products.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_gla_scan(GatedArgs a, int n_chunks, const float *__restrict__ ws) {
-    __shared__ float sV[kC * 20], sS[kK * 20], sD[kK];
+__global__ __launch_bounds__(kThreads) void k_gla_out(GatedArgs a, int n_chunks, const float *__restrict__ ws) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int r = c16, q = g;
-    const int dk = a.dk, dv = a.dv, N = a.N;
-    const int bh = blockIdx.x, col0 = kNC * blockIdx.y;
-    const int ncol = min(kNC, dv - col0);
-    const T *V = static_cast<const T *>(a.V) + (size_t)bh * N * dv;
+    const int dv = a.dv, dvp = gla_dvp(dv), N = a.N;
+    const int bh = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks;
+    const int t0 = ch * kC, nt = min(kC, N - t0);
+    const float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats(dvp);
+    const float *QD = rec, *PVT = rec + kC * kK, *SST = PVT + (size_t)dvp * kC;
     T *O = static_cast<T *>(a.O) + (size_t)bh * N * dv;
+    const auto ro = out_rsrc(O + (size_t)t0 * dv, nt * dv * (int)sizeof(T));
 
-    f32x4 S = zero4();
-    if (a.S_in) {
+    float qa[16];
+    row16(QD + (16 * w + c16) * kK + 16 * g, qa);
+    for (int cb0 = 0; cb0 < dvp; cb0 += 64) {
+        float sb[4][16];
+        float4 pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int f = 16 * w + 4 * g + e;
-            S[e] = (f < dk && c16 < ncol) ? a.S_in[((size_t)bh * dk + f) * dv + col0 + c16] : 0.f;
-        }
-    }
-    // Every load is unconditional (indices clamped to valid elements; the
-    // selects happen where the values are used): a load under a branch makes
-    // the compiler wait for all outstanding loads right after it, which would
-    // turn the prefetch into a synchronous read.
-    struct Pre {
-        float4 qd[4], p[4], ke[4];
-        T v[4];
-        float dec;
-    };
-    auto fetch = [&](Pre &f, int ch_) {
-        const int ch = min(ch_, n_chunks - 1);  // past the end: a harmless re-read of the last chunk
-        const int t0 = ch * kC, nt = min(kC, N - t0);
-        const float *rec = ws + ((size_t)bh * n_chunks + ch) * gla_rec_floats();
-        const float *Pr = rec + (16 * w + r) * kC + 16 * q;
-        const float *Qr = rec + kC * kK + (16 * w + r) * kK + 16 * q;
-        const float *Kr = rec + 2 * kC * kK + (16 * w + r) * kC + 16 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f.p[i] = *reinterpret_cast<const float4 *>(Pr + 4 * i);
-            f.qd[i] = *reinterpret_cast<const float4 *>(Qr + 4 * i);
-            f.ke[i] = *reinterpret_cast<const float4 *>(Kr + 4 * i);
-        }
-        f.dec = rec[3 * kC * kK + (tid & (kK - 1))];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // values: token e / 16, column e % 16
-            const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
-            const bool in = t < nt && cc < ncol;
-            f.v[j] = V[(size_t)(t0 + (in ? t : 0)) * dv + col0 + (in ? cc : 0)];
-        }
-    };
-    auto as_f32 = [](T x) {
-        if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
-        else return static_cast<float>(x);
-    };
-    Pre pre;
-    fetch(pre, 0);
-    for (int ch = 0; ch < n_chunks; ++ch) {
-        const int t0 = ch * kC, nt = min(kC, N - t0);
-        float pa[16], qa[16], ka[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pa[4 * i] = pre.p[i].x; pa[4 * i + 1] = pre.p[i].y; pa[4 * i + 2] = pre.p[i].z; pa[4 * i + 3] = pre.p[i].w;
-            qa[4 * i] = pre.qd[i].x; qa[4 * i + 1] = pre.qd[i].y; qa[4 * i + 2] = pre.qd[i].z; qa[4 * i + 3] = pre.qd[i].w;
-            ka[4 * i] = pre.ke[i].x; ka[4 * i + 1] = pre.ke[i].y; ka[4 * i + 2] = pre.ke[i].z; ka[4 * i + 3] = pre.ke[i].w;
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = min(cb0 + 16 * cb, dvp - 16);  // past d_v: a re-read, not stored
+            row16(SST + (size_t)(col + c16) * kK + 16 * g, sb[cb]);
+            pv[cb] = *reinterpret_cast<const float4 *>(PVT + (size_t)(col + c16) * kC + 16 * w + 4 * g);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = tid + j * kThreads, t = e / kNC, cc = e % kNC;
-            sV[t * 20 + cc] = (t < nt && cc < ncol) ? as_f32(pre.v[j]) : 0.f;
-        }
-        if (tid < kK) sD[tid] = pre.dec;
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = cb0 + 16 * cb;
+            f32x4 o0 = f32x4{pv[cb].x, pv[cb].y, pv[cb].z, pv[cb].w}, o1 = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(16 * w + 4 * g + e) * 20 + c16] = S[e];
-        lds_barrier();
-        fetch(pre, ch + 1);
-        // O = QD S_0 + P V for token rows 16w.. ; S = decay S_0 + KE V for feature rows 16w..
-        // (the B operands read from LDS all at once, then the products)
-        float sb[16], vb[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            sb[j] = sS[(16 * q + j) * 20 + c16];
-            vb[j] = sV[(16 * q + j) * 20 + c16];
-        }
-        f32x4 o0 = zero4(), o1 = zero4(), u0 = zero4(), u1 = zero4();
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (j & 1) {
-                o1 = mma(qa[j], sb[j], o1);
-                o1 = mma(pa[j], vb[j], o1);
-                u1 = mma(ka[j], vb[j], u1);
-            } else {
-                o0 = mma(qa[j], sb[j], o0);
-                o0 = mma(pa[j], vb[j], o0);
-                u0 = mma(ka[j], vb[j], u0);
+            for (int ks = 0; ks < 16; ks += 2) {
+                o0 = mma(qa[ks], sb[cb][ks], o0);
+                o1 = mma(qa[ks + 1], sb[cb][ks + 1], o1);
             }
-        }
-        const f32x4 o = o0 + o1, u = u0 + u1;
-        const auto ro = out_rsrc(O + (size_t)t0 * dv, nt * dv * (int)sizeof(T));
+            const f32x4 o = o0 + o1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int f = 16 * w + 4 * g + e;
-            S[e] = sD[f] * S[e] + u[e];
-            const int i = 16 * w + 4 * g + e;
-            const int off = (i < nt && c16 < ncol) ? (i * dv + col0 + c16) * (int)sizeof(T) : nt * dv * (int)sizeof(T);
-            store_elem<T>(ro, off, o[e]);
-        }
-        lds_barrier();  // this chunk's values, decay and state image read before the next staging
-    }
-    if (a.S_out) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int f = 16 * w + 4 * g + e;
-            if (f < dk && c16 < ncol) a.S_out[((size_t)bh * dk + f) * dv + col0 + c16] = S[e];
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * g + e, j = col + c16;
+                const int off = (i < nt && j < dv && col < dvp) ? (i * dv + j) * (int)sizeof(T) : nt * dv * (int)sizeof(T);
+                store_elem<T>(ro, off, o[e]);
+            }
         }
     }
 }
@@ -623,25 +670,30 @@ hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t st, KEven
     return launch_kernel_ev(k_gla_chunk<uint16_t>, grid, block, 0, st, ev, a);
 }
 
-size_t gla_chunk_ws_bytes(int BH, int N) {
+size_t gla_chunk_ws_bytes(int BH, int N, int dv) {
     const size_t n_chunks = (size_t)(N + kC - 1) / kC;
-    return sizeof(float) * (size_t)BH * n_chunks * gla_rec_floats();
+    return sizeof(float) * (size_t)BH * n_chunks * gla_rec_floats(gla_dvp(dv));
 }
 
 hipError_t launch_gla_split(const GatedArgs &a, int dtype, float *ws, hipStream_t st, KEvents ev_prep,
-                            KEvents ev_scan) {
+                            KEvents ev_chain, KEvents ev_out) {
     const int n_chunks = (a.N + kC - 1) / kC;
-    const dim3 gp((unsigned)((size_t)a.BH * n_chunks)), gs((unsigned)a.BH, (unsigned)((a.dv + kNC - 1) / kNC));
-    const dim3 blk(kThreads);
+    const dim3 gp((unsigned)((size_t)a.BH * n_chunks)), blk(kThreads);
+    const size_t chain_threads = (size_t)a.BH * gla_dvp(a.dv) * (kK / 4);
+    const dim3 gc((unsigned)((chain_threads + 255) / 256)), bc(256);
     hipError_t e;
     if (dtype == kF32) {
         e = launch_kernel_ev(k_gla_prep<float>, gp, blk, 0, st, ev_prep, a, n_chunks, ws);
-        if (e != hipSuccess) return e;
-        return launch_kernel_ev(k_gla_scan<float>, gs, blk, 0, st, ev_scan, a, n_chunks, static_cast<const float *>(ws));
+        if (e == hipSuccess) e = launch_kernel_ev(k_gla_chain, gc, bc, 0, st, ev_chain, a, n_chunks, ws);
+        if (e == hipSuccess)
+            e = launch_kernel_ev(k_gla_out<float>, gp, blk, 0, st, ev_out, a, n_chunks, static_cast<const float *>(ws));
+        return e;
     }
     e = launch_kernel_ev(k_gla_prep<uint16_t>, gp, blk, 0, st, ev_prep, a, n_chunks, ws);
-    if (e != hipSuccess) return e;
-    return launch_kernel_ev(k_gla_scan<uint16_t>, gs, blk, 0, st, ev_scan, a, n_chunks, static_cast<const float *>(ws));
+    if (e == hipSuccess) e = launch_kernel_ev(k_gla_chain, gc, bc, 0, st, ev_chain, a, n_chunks, ws);
+    if (e == hipSuccess)
+        e = launch_kernel_ev(k_gla_out<uint16_t>, gp, blk, 0, st, ev_out, a, n_chunks, static_cast<const float *>(ws));
+    return e;
 }
 
 }  // namespace la

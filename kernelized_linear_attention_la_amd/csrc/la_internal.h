@@ -207,11 +207,12 @@ hipError_t launch_gated(const GatedArgs &a, bool gla, int dtype, hipStream_t str
 // GLA in chunkwise form (la_gla_chunk.hip): d_k <= 64, N >= 64.
 bool gla_chunk_supported(const GatedArgs &a);
 hipError_t launch_gla_chunk(const GatedArgs &a, int dtype, hipStream_t stream, KEvents ev = {});
-// The same chunk form in two launches (per-chunk products once, then the scan
-// per 16 value columns); ws holds one record per chunk.  Same support.
-size_t gla_chunk_ws_bytes(int BH, int N);
+// The same chunk form in three launches (every product per chunk at once, the
+// element-wise state chain over chunks, the outputs per chunk at once); ws
+// holds one record per chunk.  Same support.
+size_t gla_chunk_ws_bytes(int BH, int N, int dv);
 hipError_t launch_gla_split(const GatedArgs &a, int dtype, float *ws, hipStream_t stream, KEvents ev_prep = {},
-                            KEvents ev_scan = {});
+                            KEvents ev_chain = {}, KEvents ev_out = {});
 // Gated delta rule in chunkwise form (la_delta_chunk.hip): d_k = 64, d_v a
 // multiple of 16 up to 128, 64-token chunks; ws holds one record per chunk.
 bool delta_chunk_supported(int dk, int dv, int chunk);

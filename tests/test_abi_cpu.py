@@ -222,8 +222,13 @@ def test_gla_chunked_validation():
     L = linattn.lib()
     pid = _p(phi=linattn.LA_PHI_IDENTITY)
     need = L.la_gla_workspace_bytes(ctypes.byref(pid), 64)
-    # the records start past the 256-byte control block that the forward's hand-off keeps
-    assert need == 256 + 4 * pid.B * pid.H * (-(-pid.N // 64)) * (3 * 64 * 64 + 64)
+    # the records start past the 256-byte control block that the forward's hand-off keeps;
+    # one per (b, h, chunk): QD 64 x 64, (P V)^T and (KE^T V)^T dvp x 64 (d_v rounded up to 16), decay 64
+    dvp = -(-pid.d_v // 16) * 16
+    assert need == 256 + 4 * pid.B * pid.H * (-(-pid.N // 64)) * (64 * 64 + 2 * dvp * 64 + 64)
+    p40 = _p(phi=linattn.LA_PHI_IDENTITY, d_v=40)
+    assert L.la_gla_workspace_bytes(ctypes.byref(p40), 64) == \
+        256 + 4 * p40.B * p40.H * (-(-p40.N // 64)) * (64 * 64 + 2 * 48 * 64 + 64)
     assert L.la_gla_workspace_bytes(ctypes.byref(pid), 32) == 0
     assert L.la_gla_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=65)), 64) == 0
 

@@ -223,8 +223,8 @@ def test_delta_chunked_rejects_unsupported_shapes():
 
 
 # ---------------------------------------------------------------------------
-# GLA in two launches (la_forward_gla_chunked): per-chunk products, then the
-# scan over chunks per 16 value columns.
+# GLA in chunkwise form (la_forward_gla_chunked): every chunk's products at
+# once, the element-wise state chain over chunks, the outputs of every chunk.
 # ---------------------------------------------------------------------------
 GLA_SPLIT_CASES = [
     # (B, H, N, dk, dv, dtype, with S_in)
@@ -233,6 +233,9 @@ GLA_SPLIT_CASES = [
     (1, 1, 1, 32, 32, "f32", True),        # one token
     (1, 2, 77, 5, 3, "f32", True),         # odd widths
     (2, 2, 130, 64, 40, "bf16", True),     # ragged chunk and column block
+    (1, 2, 200, 64, 80, "f32", True),      # two column groups of the per-chunk value products
+    (2, 2, 190, 48, 128, "bf16", True),    # two full column groups, padded channels
+    (1, 1, 600, 64, 24, "f32", True),      # ten chunks: more than one round of the chain's prefetch ring
     (4, 8, 2048, 64, 64, "bf16", True),    # the GLA workload's shape
 ]
 
@@ -259,7 +262,7 @@ def test_gla_chunked_against_oracle(ci):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_gla_chunked_extreme_gates_and_handoff(dtype):
     """Zero, tiny, mid and near-one gates (the element-wise diagonal blocks)
-    through the two-launch form, also as two calls with S_out aliasing S_in."""
+    through the chunkwise form, also as two calls with S_out aliasing S_in."""
     B, H, N, dk, dv = 1, 2, 300, 64, 40
     gi = inputs.gated_inputs(2700, B, H, N, dk, dv, dtype)
     al = _extreme_gates(2700, B, H, N, dk)
@@ -287,7 +290,7 @@ def test_gla_chunked_extreme_gates_and_handoff(dtype):
 
 
 def test_two_launch_forms_graph_replay():
-    """The two-launch GLA and delta-rule calls captured in a HIP graph: every
+    """The chunkwise GLA (three launches) and delta-rule (two) calls captured in a HIP graph: every
     replay (with eager calls on the same workspaces in between) reproduces the
     eager results bit for bit (the workspace records are rewritten each call)."""
     B, H, N, dk, dv = 2, 3, 200, 64, 48
@@ -317,7 +320,7 @@ def test_two_launch_forms_graph_replay():
         la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_in=S_in, S_out=Sd, out=Od, workspace=ws_d)
     torch.cuda.synchronize()
     for rep in range(4):
-        _say("two-launch graph replay", rep)
+        _say("chunkwise gated graph replay", rep)
         Og.zero_(), Od.zero_(), Sg.zero_(), Sd.zero_()
         g.replay()
         torch.cuda.synchronize()
