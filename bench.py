@@ -298,7 +298,7 @@ def kernel_symbol(wl, slot):
     if wl.gated:
         t = "float" if wl.dtype == "f32" else "unsigned short"
         if delta_on_chunks(wl):
-            return f"k_delta_scan<{t}>"  # the longer of the chunkwise form's two launches
+            return f"k_delta_prep<{t}, {64 if wl.dv <= 64 else 128}>"  # the longest of the chunkwise form's launches
         if gla_on_chunks(wl):
             return f"k_gla_prep<{t}>"  # the longest of the chunkwise form's three launches
         return f"k_gated<{t}, {'true' if wl.gated == 'gla' else 'false'}>"
@@ -699,10 +699,11 @@ def bench_gated(args, wl):
     extra = {"per_token_latency_ns": kern_ms * 1e6 / wl.N}
     if chunked:
         # the launches of the chunkwise form timed one by one through the
-        # library's hook: GLA's per-chunk products, state chain and outputs;
-        # the delta rule's per-chunk solves and scan over chunks
+        # library's hook: the per-chunk products (GLA) or operators (delta
+        # rule), the state chain over chunks, the outputs of every chunk
         names = ({la.LA_KSLOT_STATE: "k_gla_prep", la.LA_KSLOT_SCAN: "k_gla_chain", la.LA_KSLOT_CHUNK: "k_gla_out"}
-                 if wl.gated == "gla" else {la.LA_KSLOT_STATE: "k_delta_prep", la.LA_KSLOT_CHUNK: "k_delta_scan"})
+                 if wl.gated == "gla" else
+                 {la.LA_KSLOT_STATE: "k_delta_prep", la.LA_KSLOT_SCAN: "k_delta_scan", la.LA_KSLOT_CHUNK: "k_delta_out"})
         slots = tuple(names)
         kd = {sl: [] for sl in slots}
         for _ in range(args.steps):
@@ -713,18 +714,19 @@ def bench_gated(args, wl):
             step(events=kev)
             torch.cuda.synchronize()
             for sl in slots:
-                kd[sl].append(hev.elapsed_ms(*ev[sl]))
+                if kev.launched[sl]:  # only the slots whose kernel the call enqueued
+                    kd[sl].append(hev.elapsed_ms(*ev[sl]))
                 hev.destroy(ev[sl][0])
                 hev.destroy(ev[sl][1])
-        extra = {"kernel_avg_us": {names[sl]: round(1e3 * sum(kd[sl]) / len(kd[sl]), 2) for sl in slots},
+        extra = {"kernel_avg_us": {names[sl]: round(1e3 * sum(kd[sl]) / len(kd[sl]), 2) for sl in slots if kd[sl]},
                  "step_kernels_us": round(kern_ms * 1e3, 2)}
     flops = gated_alg_flops(wl)
     ach = flops / (kern_ms * 1e-3) / 1e12
-    kname = ("k_gla_prep + k_gla_chain + k_gla_out" if wl.gated == "gla" else "k_delta_prep + k_delta_scan") \
+    kname = ("k_gla_prep + k_gla_chain + k_gla_out" if wl.gated == "gla" else "k_delta_prep + k_delta_scan + k_delta_out") \
         if chunked else kernel_symbol(wl, "chunk")
     # fp32 arithmetic: the chunkwise forms on the matrix cores (dense fp32 MFMA peak),
     # the token-by-token recurrences in fp32 FMAs; the flops are the recurrence's own,
-    # over the step's kernels (for the chunkwise delta rule both launches)
+    # over the step's kernels (every launch of the chunkwise forms)
     bound = "mfma" if chunked else "alu"
     peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
     roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",

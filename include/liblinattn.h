@@ -378,9 +378,13 @@ la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const v
  * cumulative forget gates).  The write vectors of a chunk solve the unit
  * lower-triangular system (I + M) U = diag(beta) V - diag(beta g) K S0,
  * M[t][s] = beta_t (g_t / g_s) k_t . k_s for s < t, so U = Ut - W S0 with W and
- * Ut independent of the entering state: the library forms W, Ut and the
- * causal score matrix of every chunk at once (first launch), then runs the
- * chunks of each (b, h) slice in order per 16 value columns (second launch).
+ * Ut independent of the entering state.  Substituted, O = Qt S0 + P Ut with
+ * Qt = diag(g) Q - P W (P the causal score matrix) and the chunk's final
+ * state A S0 + B with A = g_C I - K^T diag(g_C / g) W, B = K^T diag(g_C / g) Ut:
+ * the library forms Qt, A, P Ut and B of every chunk at once (first launch),
+ * runs the chunks of each (b, h) slice in order per 16 value columns, one
+ * product on the state per chunk (second launch), then forms the outputs of
+ * every chunk at once (third launch).
  * The same sums as la_forward_delta_recurrent up to rounding order (fp32
  * arithmetic).  Arguments as there, plus:
  *   chunk  must be 64;  p->d_k must be 64 and p->d_v a multiple of 16 up to
@@ -389,10 +393,11 @@ la_status la_forward_delta_recurrent(const la_problem *p, const void *Q, const v
  *   ws     device workspace of at least la_delta_workspace_bytes(p, chunk)
  *          bytes (16-byte aligned; no initial contents needed; past its
  *          first 256 bytes, which are left untouched, one record per
- *          (b, h, chunk): W, P [64 x 64], Ut [64 x d_v], gate products), owned
- *          by the caller; else LA_ERR_WORKSPACE;
+ *          (b, h, chunk): Qt, A [64 x 64], (P Ut)^T, B^T [d_v x 64], fp32),
+ *          owned by the caller; else LA_ERR_WORKSPACE;
  *   ev     optional timing hook: slot LA_KSLOT_STATE brackets the per-chunk
- *          launch, LA_KSLOT_CHUNK the scan over chunks.
+ *          launch, LA_KSLOT_SCAN the state chain over chunks, LA_KSLOT_CHUNK
+ *          the outputs of every chunk.
  * Forget gates below 2^-80 are taken as 2^-80.  S_out may alias S_in.
  */
 size_t la_delta_workspace_bytes(const la_problem *p, int chunk);

@@ -90,6 +90,7 @@ KERNEL_SOURCES = {
     "k_bwd_dkv": ("la_backward.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_delta_prep": ("la_delta_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_delta_scan": ("la_delta_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
+    "k_delta_out": ("la_delta_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gated": ("la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gla_chunk": ("la_gla_chunk.hip", "la_gated.hip", "la_device.h", "la_internal.h", "la_api.hip"),
     "k_gla_prep": ("la_gla_chunk.hip", "la_device.h", "la_internal.h", "la_api.hip"),

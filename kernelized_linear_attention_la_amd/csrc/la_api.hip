@@ -729,7 +729,7 @@ LA_API la_status la_forward_delta_chunked(const la_problem *p, int chunk, const 
     return launch_delta_chunk(a, p->dtype == LA_BF16 ? kBF16 : kF32,
                               reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes),
                               static_cast<hipStream_t>(stream), slot_events(ev, LA_KSLOT_STATE),
-                              slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
+                              slot_events(ev, LA_KSLOT_SCAN), slot_events(ev, LA_KSLOT_CHUNK)) == hipSuccess
                ? LA_OK
                : LA_ERR_DEVICE;
 }

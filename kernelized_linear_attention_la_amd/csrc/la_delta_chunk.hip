@@ -22,14 +22,23 @@
 // Every ratio g_t / g_s with s <= t is a product of gates in [0, 1], formed as
 // exp2 of a difference of cumulative log2 gates (gates below 2^-80 count as 2^-80).
 //
+// Substituting U = Ut - W S0 leaves two operators and two S0-free terms per
+// chunk:
+//     O   = Qt S0 + P Ut,   Qt = diag(g) Q - P W,
+//     S_C = A S0 + B,       A = g_C I - KG W,  B = KG Ut,  KG = K^T diag(g_C / g),
+// so the step from chunk to chunk is one product (A S0) and the outputs one
+// more, off that chain.
+//
 // Two launches:
 //  * k_delta_prep, one workgroup per (slice, chunk), all chunks at once: the
-//    Gram matrices K K^T and Q K^T on fp32 matrix instructions, M and P, and
-//    W, Ut by blocked forward substitution (16-row blocks: the update from the
+//    Gram matrices K K^T and Q K^T on fp32 matrix instructions, M and P, W and
+//    Ut by blocked forward substitution (16-row blocks: the update from the
 //    solved blocks on matrix instructions, the diagonal block by substitution
-//    with one right-hand column per thread), into the workspace.
+//    with one right-hand column per thread), then P [W | Ut] and
+//    KG [W | Ut] on matrix instructions: Qt, A, (P Ut)^T, B^T into the
+//    workspace.
 //  * k_delta_scan, one workgroup per (slice, 16 value columns), the chunks in
-//    order: U = Ut - W S0, O, and the state carried in fp32 accumulators.
+//    order: S <- A S + B and O = Qt S + P Ut, the state in fp32 accumulators.
 // All arithmetic is fp32 (v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16]
 // and B[l/16][l%16] of a 16x4 by 4x16 step and receives C[4(l/16)+e][l%16]).
 #include "la_device.h"
@@ -47,6 +56,9 @@ constexpr int kXT = 256;       // threads (4 waves)
 constexpr float kMinLog2Gate = -80.f;
 
 __device__ __forceinline__ f32x4d zero4d() { return f32x4d{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }  // bf16 bits
 
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -73,9 +85,9 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, fl
     else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
-// Per-chunk workspace record (floats): W [64][64], P [64][64], Ut [64][dv],
-// g [64], g_C / g [64].
-__host__ __device__ inline size_t delta_rec_floats(int dv) { return 2 * kXC * kXK + (size_t)kXC * dv + 2 * kXC; }
+// Per-chunk workspace record (floats): Qt [64 tokens][64], A [64][64]
+// (P [64][64] while the record is built), (P Ut)^T [dv][64 tokens], B^T [dv][64].
+__host__ __device__ inline size_t delta_rec_floats(int dv) { return 2 * kXC * kXK + 2 * (size_t)kXC * dv; }
 
 // DVM: the largest d_v the instance takes (64 or 128); the right-hand sides
 // are sized for it, so at d_v <= 64 the workgroup needs 69 KB of LDS and two
@@ -164,7 +176,8 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
     __syncthreads();
 
     float *rec = ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv);
-    float *W = rec, *P = rec + kXC * kXK, *Ut = rec + 2 * kXC * kXK, *gv = Ut + (size_t)kXC * dv, *gt = gv + kXC;
+    float *Qt = rec, *Am = rec + kXC * kXK, *PUT = rec + 2 * kXC * kXK, *BT = PUT + (size_t)kXC * dv;
+    float *const P = Am;  // P until the operator A replaces it
 
     // Gram tiles of row block w: K K^T (strictly lower part -> M) and Q K^T
     // (lower part with the diagonal -> P); tiles above the diagonal are zero
@@ -182,10 +195,6 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
             sM[t * kXR + s] = s < t ? sb[t] * ratio * gk[e] : 0.f;
             P[t * kXK + s] = ratio * gq[e];
         }
-    }
-    if (tid < kXC) {
-        gv[tid] = __builtin_amdgcn_exp2f(sl[tid]);
-        gt[tid] = __builtin_amdgcn_exp2f(sl[kXC - 1] - sl[tid]);
     }
     __syncthreads();  // every read of sQ done: its space takes the right-hand sides
     // R = [diag(b g) K | diag(b) V]
@@ -237,31 +246,118 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
                 x[r] = v;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 16 * b + r;
-                sX[t * RX + j] = x[r];
-                if (j < kXK) W[t * kXK + j] = x[r];
-                else Ut[(size_t)t * dv + (j - kXK)] = x[r];
-            }
+            for (int r = 0; r < 16; ++r) sX[(16 * b + r) * RX + j] = x[r];
         }
         __syncthreads();
     }
+
+    // Tiles of the two operator products over X = [W | Ut] (16-column block n:
+    // n < 4 the W part, else value columns 16 (n - 4)..), split over the waves.
+    // Qt = diag(g) Q - P W and (P Ut)^T: P is lower triangular, so row block m
+    // takes key blocks 0..m (k-slot q of step (kb, j) = token 16kb + 4q + j: a
+    // lane reads four consecutive entries of its P row).
+    const int r = c16, q = g;
+    const int nxt = ncol / 16;  // column blocks of X
+    const T *Qg = Q + tok0 * kXK;
+    // wave w takes column blocks w, w + 4, .. in pairs (two independent
+    // accumulation chains sharing the P row operand; a pair's second block
+    // past the last is computed on the last block and not stored).  The P row
+    // pieces (token 16kb + 4q..+3 of row 16m + r) and the queries of the
+    // wave's Qt column block w are loaded before the products, all at once.
+    float4 prow[4][4];
+    T qv[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            prow[m][kb] = *reinterpret_cast<const float4 *>(&P[(16 * m + r) * kXK + 16 * kb + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // clamped rows, zero past the end at use
+            const int t = 16 * m + 4 * g + e;
+            qv[m][e] = Qg[(t < L ? t : 0) * kXK + 16 * w + c16];
+        }
+    }
+    auto store_p = [&](int m, int n, const f32x4d &acc, const T (&qm)[4]) {
+        if (n < 4) {  // n == w: the wave's own query column block
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * m + 4 * g + e;
+                const float qf = t < L ? to_f32(qm[e]) : 0.f;
+                Qt[t * kXK + 16 * n + c16] = __builtin_amdgcn_exp2f(sl[t]) * qf - acc[e];
+            }
+        } else {
+            *reinterpret_cast<float4 *>(&PUT[(size_t)(16 * (n - 4) + c16) * kXC + 16 * m + 4 * g]) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        for (int n0 = w; n0 < nxt; n0 += 8) {
+            const int n1 = n0 + 4, n1c = min(n1, nxt - 1);
+            f32x4d acc0 = zero4d(), acc1 = zero4d();
+#pragma unroll
+            for (int kb = 0; kb <= m; ++kb) {
+                const float pav[4] = {prow[m][kb].x, prow[m][kb].y, prow[m][kb].z, prow[m][kb].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float *xr = &sX[(16 * kb + 4 * q + j) * RX + c16];
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n0], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n1c], acc1, 0, 0, 0);
+                }
+            }
+            store_p(m, n0, acc0, qv[m]);
+            if (n1 < nxt) store_p(m, n1, acc1, qv[m]);
+        }
+    }
+    __syncthreads();  // every read of P done before A takes its place
+    // A = g_C I - KG W and B^T = (KG Ut)^T, KG[f][t] = k_t,f g_C / g_t over all tokens
+    const float lC = sl[kXC - 1], gC = __builtin_amdgcn_exp2f(lC);
+    float gk[16];  // g_C / g_t for this lane's tokens t = 4i + q
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gk[i] = __builtin_amdgcn_exp2f(lC - sl[4 * i + q]);
+    auto store_a = [&](int m, int n, const f32x4d &acc) {
+        if (n < 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int f = 16 * m + 4 * g + e, f2 = 16 * n + c16;
+                Am[f * kXK + f2] = (f == f2 ? gC : 0.f) - acc[e];
+            }
+        } else {
+            *reinterpret_cast<float4 *>(&BT[(size_t)(16 * (n - 4) + c16) * kXK + 16 * m + 4 * g]) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
+    for (int m = 0; m < 4; ++m) {
+        float ka[16];  // KG[16m + r][t], t = 4i + q
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ka[i] = sK[(4 * i + q) * kXR + 16 * m + r] * gk[i];
+        for (int n0 = w; n0 < nxt; n0 += 8) {
+            const int n1 = n0 + 4, n1c = min(n1, nxt - 1);
+            f32x4d acc0 = zero4d(), acc1 = zero4d();
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float *xr = &sX[(4 * i + q) * RX + c16];
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i], xr[16 * n0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i], xr[16 * n1c], acc1, 0, 0, 0);
+            }
+            store_a(m, n0, acc0);
+            if (n1 < nxt) store_a(m, n1, acc1);
+        }
+    }
 }
 
-// One workgroup per (slice, 16 value columns): the chunks in order.  Wave w
-// owns token rows 16w..16w+15 of U and O, and feature rows 16w..16w+15 of the
-// state (fp32 accumulators for the whole slice).  The row operands of W S0,
-// Q S0 and P U come straight from global memory into registers, one chunk
-// ahead: for those products k-step j of lane group q = l/16 takes index
-// 16q + j (P U: 16kb + 4q + j), so each lane reads contiguous 16-byte runs,
-// and the B operands (state image, U) are read from LDS in the same order.
-template <typename T>
-__global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, const T *__restrict__ K, T *__restrict__ O,
-                                                    const float *__restrict__ ws, const float *__restrict__ S_in,
-                                                    float *__restrict__ S_out, int N, int dv, int n_chunks) {
-    __shared__ float sK[kXC * kXR];
-    __shared__ float sS[kXK * 20], sU[kXC * 20], sUg[kXC * 20], sUt[kXC * 20];
-    __shared__ float sg[kXC], sgt[kXC];
+// The state chain: one workgroup per (slice, 16 value columns), the chunks
+// in order.  Wave w owns feature rows 16w..16w+15 of the state (fp32
+// accumulators).  Per chunk: the state entering it, S_c, is written over the
+// chunk's B^T in the record (same lane, same address, after that lane's read
+// of it), then S <- A S + B with the state image as the B operand (k-slot q
+// of step j = feature 16q + j, so a lane's A row is a contiguous 16-float run
+// read straight from the record into registers four chunks ahead) and B as
+// the accumulators' starting value.  The state image alternates between two
+// LDS buffers, so one barrier per chunk orders its writes and reads.
+__global__ __launch_bounds__(kXT) void k_delta_scan(float *__restrict__ ws, const float *__restrict__ S_in,
+                                                    float *__restrict__ S_out, int dv, int n_chunks) {
+    __shared__ __align__(16) float sS[2][16 * kXR];  // [value column][feature], transposed
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int ncb = dv / 16;
@@ -279,154 +375,123 @@ __global__ __launch_bounds__(kXT) void k_delta_scan(const T *__restrict__ Q, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[e] = S_in[((size_t)bh * kXK + 16 * w + 4 * g + e) * dv + col0 + c16];
     }
-
-    constexpr int EP = 16 / (int)sizeof(T);         // elements per 16-byte piece
-    constexpr int KP = kXC * kXK / EP / kXT;        // pieces of K per thread
-    constexpr int QR = 16 / EP;                     // pieces of this lane's 16 Q values
     struct Pre {
-        float4 w[4], p[4], ut, gg;
-        uint4 q[QR], k[KP];
+        float4 a[4], bt;
     };
-    // Every load is unconditional (offsets clamped to valid data; the zero
-    // selects happen where the values are used): a load under a branch makes
-    // the compiler wait for all outstanding loads right after it, which would
-    // turn the prefetch into a synchronous read.
+    const size_t bt_off = 2 * kXC * kXK + (size_t)kXC * dv + (size_t)(col0 + c16) * kXK + 16 * w + 4 * g;
     auto fetch = [&](Pre &f, int c_) {
         const int c = min(c_, n_chunks - 1);  // past the end: a harmless re-read of the last chunk
-        const int t0 = c * kXC, L = min(kXC, N - t0);
         const float *rec = ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv);
-        const float *Wr = rec + (16 * w + r) * kXK + 16 * q;          // W[16w + r][16q ..]
-        const float *Pr = rec + kXC * kXK + (16 * w + r) * kXK + 4 * q;  // P[16w + r][16kb + 4q ..]
+        const float *Ar = rec + kXC * kXK + (16 * w + r) * kXK + 16 * q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f.w[i] = *reinterpret_cast<const float4 *>(Wr + 4 * i);
-            f.p[i] = *reinterpret_cast<const float4 *>(Pr + 16 * i);
-        }
-        f.ut = *reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)(tid >> 2) * dv + col0 + 4 * (tid & 3));
-        f.gg = reinterpret_cast<const float4 *>(rec + 2 * kXC * kXK + (size_t)kXC * dv)[tid & 31];
-        const bool qlive = 16 * w + r < L;
-        const T *qrow = Q + ((size_t)bh * N + t0 + (qlive ? 16 * w + r : 0)) * kXK + 16 * q;
-#pragma unroll
-        for (int i = 0; i < QR; ++i) f.q[i] = reinterpret_cast<const uint4 *>(qrow)[i];
-        const char *kb = reinterpret_cast<const char *>(K + ((size_t)bh * N + t0) * kXK);
-        const int bytes = L * kXK * (int)sizeof(T);
-#pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            const int off = 16 * (tid + i * kXT);
-            f.k[i] = *reinterpret_cast<const uint4 *>(kb + (off < bytes ? off : 0));
-        }
+        for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const float4 *>(Ar + 4 * i);
+        f.bt = *reinterpret_cast<const float4 *>(rec + bt_off);
     };
-    auto unpack = [&](const uint4 &x, float *o) {
-        if constexpr (sizeof(T) == 2) {
-            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    // the records of the next kDepth chunks in flight: chunk c sits in ring
+    // slot c % kDepth (the loop runs in groups of kDepth, so every step's slot
+    // is a compile-time choice) and is refilled with chunk c + kDepth
+    constexpr int kDepth = 4;
+    Pre pre[kDepth];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[2 * e] = __uint_as_float(xs[e] << 16);
-                o[2 * e + 1] = __uint_as_float(xs[e] & 0xffff0000u);
-            }
-        } else {
-            o[0] = __uint_as_float(x.x); o[1] = __uint_as_float(x.y);
-            o[2] = __uint_as_float(x.z); o[3] = __uint_as_float(x.w);
-        }
-    };
-    Pre pre;
-    fetch(pre, 0);
+    for (int d = 0; d < kDepth; ++d) fetch(pre[d], d);
 
-    for (int c = 0; c < n_chunks; ++c) {
-        const int t0 = c * kXC, L = min(kXC, N - t0);
-        const size_t tok0 = (size_t)bh * N + t0;
-        // operands of chunk c in registers; K, Ut, gates and the state image into LDS
-        // (query rows and key pieces past the end read as zero)
-        const uint4 zero = make_uint4(0, 0, 0, 0);
-        const bool qlive = 16 * w + r < L;
-        const int kbytes = L * kXK * (int)sizeof(T);
-        float wa[16], qa[16], pa[16];
+    auto step = [&](Pre &p, int c) {
+        float *img = sS[c & 1];
+        *reinterpret_cast<float4 *>(&img[c16 * kXR + 16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
+        float aa[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            wa[4 * i] = pre.w[i].x; wa[4 * i + 1] = pre.w[i].y; wa[4 * i + 2] = pre.w[i].z; wa[4 * i + 3] = pre.w[i].w;
-            pa[4 * i] = pre.p[i].x; pa[4 * i + 1] = pre.p[i].y; pa[4 * i + 2] = pre.p[i].z; pa[4 * i + 3] = pre.p[i].w;
+            aa[4 * i] = p.a[i].x; aa[4 * i + 1] = p.a[i].y; aa[4 * i + 2] = p.a[i].z; aa[4 * i + 3] = p.a[i].w;
         }
-#pragma unroll
-        for (int i = 0; i < QR; ++i) unpack(qlive ? pre.q[i] : zero, &qa[EP * i]);
-#pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            const int e0 = EP * (tid + i * kXT), t = e0 / kXK, f = e0 % kXK;
-            float o[EP];
-            unpack(16 * (tid + i * kXT) < kbytes ? pre.k[i] : zero, o);
-#pragma unroll
-            for (int e = 0; e < EP; ++e) sK[t * kXR + f + e] = o[e];
-        }
-        *reinterpret_cast<float4 *>(&sUt[(tid >> 2) * 20 + 4 * (tid & 3)]) = pre.ut;
-        if (tid < 32) {
-            const float gg[4] = {pre.gg.x, pre.gg.y, pre.gg.z, pre.gg.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * tid + e;  // gate products g, then g_C / g
-                if (i < kXC) sg[i] = gg[e];
-                else sgt[i - kXC] = gg[e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(16 * w + 4 * g + e) * 20 + c16] = S[e];
+        // B joins after the products: as the accumulators' starting value its
+        // prefetch would be loaded into accumulator registers, whose moves wait
+        // for every load in flight
+        const float4 bt = p.bt;
+        f32x4d s0 = zero4d(), s1 = zero4d();
+        // S_c over this lane's own B^T entries (read above, into bt)
+        *reinterpret_cast<float4 *>(ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv) + bt_off) =
+            make_float4(S[0], S[1], S[2], S[3]);
         sync_lds();
-        fetch(pre, c + 1);
-
-        // U = Ut - W S0 and Q S0 for token rows 16w..16w+15 (k = 16q + j); two
-        // accumulators per product halve the dependent chains
-        float sb[16];  // B operands read from LDS all at once, then the products
+        fetch(p, c + kDepth);
+        float sb[16];  // B operands: a lane's 16 features of its column, four 16-byte reads
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sb[j] = sS[(16 * q + j) * 20 + c16];
-        f32x4d ws0 = zero4d(), o = zero4d(), ws1 = zero4d(), o1 = zero4d();
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = *reinterpret_cast<const float4 *>(&img[c16 * kXR + 16 * q + 4 * i]);
+            sb[4 * i] = v.x; sb[4 * i + 1] = v.y; sb[4 * i + 2] = v.z; sb[4 * i + 3] = v.w;
+        }
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-            ws0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j], sb[j], ws0, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], sb[j], o, 0, 0, 0);
-            ws1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[j + 1], sb[j + 1], ws1, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j + 1], sb[j + 1], o1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[j], sb[j], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[j + 1], sb[j + 1], s1, 0, 0, 0);
         }
-        ws0 += ws1;
-        o += o1;
+        S = s0 + s1 + f32x4d{bt.x, bt.y, bt.z, bt.w};
+    };
+    int c = 0;
+    for (; c + kDepth <= n_chunks; c += kDepth) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * w + 4 * g + e;
-            const float u = sUt[t * 20 + c16] - ws0[e];
-            sU[t * 20 + c16] = u;
-            sUg[t * 20 + c16] = sgt[t] * u;
-            o[e] *= sg[t];
-        }
-        sync_lds();
-
-        // O += P U over the key blocks up to this row block (k = 16kb + 4q + j)
-        f32x4d o2 = zero4d();
-        for (int kb = 0; kb <= w; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 4; j += 2) {
-                o = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kb + j], sU[(16 * kb + 4 * q + j) * 20 + c16], o, 0, 0, 0);
-                o2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kb + j + 1], sU[(16 * kb + 4 * q + j + 1) * 20 + c16], o2,
-                                                          0, 0, 0);
-            }
-        }
-        o += o2;
-        // S = g_C S0 + K^T diag(g_C / g) U for feature rows 16w..16w+15 (tokens
-        // 0..31 and 32..63 in two accumulators)
-        auto aK = [&](int m, int k) { return sK[k * kXR + 16 * w + m]; };
-        const f32x4d ku = mm4<8>(aK, [&](int k, int n) { return sUg[k * 20 + n]; }, zero4d(), lane) +
-                          mm4<8>([&](int m, int k) { return aK(m, k + 32); },
-                                 [&](int k, int n) { return sUg[(k + 32) * 20 + n]; }, zero4d(), lane);
-        const float gC = sg[kXC - 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[e] = gC * S[e] + ku[e];
-        const auto ro = out_rsrc(O + tok0 * dv, L * dv * (int)sizeof(T));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * w + 4 * g + e;
-            store_elem<T>(ro, t < L ? (t * dv + col0 + c16) * (int)sizeof(T) : L * dv * (int)sizeof(T), o[e]);
-        }
-        sync_lds();  // every read of this chunk's tiles done before the next staging
+        for (int d = 0; d < kDepth; ++d) step(pre[d], c + d);
     }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+        if (c + d < n_chunks) step(pre[d], c + d);
     if (S_out) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) S_out[((size_t)bh * kXK + 16 * w + 4 * g + e) * dv + col0 + c16] = S[e];
+    }
+}
+
+// O = Qt S_c + P Ut, one workgroup per (slice, chunk), every chunk at once;
+// wave w owns token rows 16w..16w+15.  A = Qt rows (k-slot q of step j =
+// feature 16q + j), B = S_c (a lane's 16 features of one column are one
+// contiguous run of the record's S_c^T), C = the P Ut rows; every load of a
+// 64-column group is issued before its products.
+template <typename T>
+__global__ __launch_bounds__(kXT) void k_delta_out(T *__restrict__ O, const float *__restrict__ ws, int N, int dv,
+                                                   int n_chunks) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int bh = blockIdx.x / n_chunks, c = blockIdx.x % n_chunks;
+    const int t0 = c * kXC, L = min(kXC, N - t0);
+    const float *rec = ws + ((size_t)bh * n_chunks + c) * delta_rec_floats(dv);
+    const float *Qt = rec, *PUT = rec + 2 * kXC * kXK, *SST = PUT + (size_t)kXC * dv;
+    const auto ro = out_rsrc(O + ((size_t)bh * N + t0) * dv, L * dv * (int)sizeof(T));
+    float qa[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4 *>(Qt + (16 * w + c16) * kXK + 16 * g + 4 * i);
+        qa[4 * i] = v.x; qa[4 * i + 1] = v.y; qa[4 * i + 2] = v.z; qa[4 * i + 3] = v.w;
+    }
+    for (int cb0 = 0; cb0 < dv; cb0 += 64) {
+        float sb[4][16];
+        float4 pu[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = min(cb0 + 16 * cb, dv - 16);  // past d_v: a re-read, not stored
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 v = *reinterpret_cast<const float4 *>(SST + (size_t)(col + c16) * kXK + 16 * g + 4 * i);
+                sb[cb][4 * i] = v.x; sb[cb][4 * i + 1] = v.y; sb[cb][4 * i + 2] = v.z; sb[cb][4 * i + 3] = v.w;
+            }
+            pu[cb] = *reinterpret_cast<const float4 *>(PUT + (size_t)(col + c16) * kXC + 16 * w + 4 * g);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = cb0 + 16 * cb;
+            f32x4d o0 = f32x4d{pu[cb].x, pu[cb].y, pu[cb].z, pu[cb].w}, o1 = zero4d();
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], sb[cb][j], o0, 0, 0, 0);
+                o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j + 1], sb[cb][j + 1], o1, 0, 0, 0);
+            }
+            const f32x4d o = o0 + o1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * g + e, j = col + c16;
+                const int off = (t < L && col < dv) ? (t * dv + j) * (int)sizeof(T) : L * dv * (int)sizeof(T);
+                store_elem<T>(ro, off, o[e]);
+            }
+        }
     }
 }
 
@@ -442,7 +507,7 @@ size_t delta_chunk_ws_bytes(int BH, int N, int dv) {
 }
 
 hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStream_t st, KEvents ev_prep,
-                              KEvents ev_scan) {
+                              KEvents ev_scan, KEvents ev_out) {
     if (!delta_chunk_supported(a.dk, a.dv, kXC)) return hipErrorNotSupported;
     const int n_chunks = (a.N + kXC - 1) / kXC;
     const dim3 gp((unsigned)((size_t)a.BH * n_chunks)), gs((unsigned)((size_t)a.BH * (a.dv / 16))), blk(kXT);
@@ -454,9 +519,11 @@ hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStrea
                                           a.N, a.dv, n_chunks, ws)
                        : launch_kernel_ev(k_delta_prep<float, 128>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
                                           a.N, a.dv, n_chunks, ws);
-        if (e != hipSuccess) return e;
-        return launch_kernel_ev(k_delta_scan<float>, gs, blk, 0, st, ev_scan, q, k, static_cast<float *>(a.O),
-                                static_cast<const float *>(ws), a.S_in, a.S_out, a.N, a.dv, n_chunks);
+        if (e == hipSuccess) e = launch_kernel_ev(k_delta_scan, gs, blk, 0, st, ev_scan, ws, a.S_in, a.S_out, a.dv, n_chunks);
+        if (e == hipSuccess)
+            e = launch_kernel_ev(k_delta_out<float>, gp, blk, 0, st, ev_out, static_cast<float *>(a.O),
+                                 static_cast<const float *>(ws), a.N, a.dv, n_chunks);
+        return e;
     }
     auto *q = static_cast<const uint16_t *>(a.Q), *k = static_cast<const uint16_t *>(a.K),
          *v = static_cast<const uint16_t *>(a.V);
@@ -464,9 +531,11 @@ hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStrea
                                       a.N, a.dv, n_chunks, ws)
                    : launch_kernel_ev(k_delta_prep<uint16_t, 128>, gp, blk, 0, st, ev_prep, q, k, v, a.alpha, a.beta,
                                       a.N, a.dv, n_chunks, ws);
-    if (e != hipSuccess) return e;
-    return launch_kernel_ev(k_delta_scan<uint16_t>, gs, blk, 0, st, ev_scan, q, k, static_cast<uint16_t *>(a.O),
-                            static_cast<const float *>(ws), a.S_in, a.S_out, a.N, a.dv, n_chunks);
+    if (e == hipSuccess) e = launch_kernel_ev(k_delta_scan, gs, blk, 0, st, ev_scan, ws, a.S_in, a.S_out, a.dv, n_chunks);
+    if (e == hipSuccess)
+        e = launch_kernel_ev(k_delta_out<uint16_t>, gp, blk, 0, st, ev_out, static_cast<uint16_t *>(a.O),
+                             static_cast<const float *>(ws), a.N, a.dv, n_chunks);
+    return e;
 }
 
 }  // namespace la

@@ -215,10 +215,11 @@ hipError_t launch_gla_split(const GatedArgs &a, int dtype, float *ws, hipStream_
                             KEvents ev_chain = {}, KEvents ev_out = {});
 // Gated delta rule in chunkwise form (la_delta_chunk.hip): d_k = 64, d_v a
 // multiple of 16 up to 128, 64-token chunks; ws holds one record per chunk.
+// Three launches: the per-chunk operators, the state chain, the outputs.
 bool delta_chunk_supported(int dk, int dv, int chunk);
 size_t delta_chunk_ws_bytes(int BH, int N, int dv);
 hipError_t launch_delta_chunk(const GatedArgs &a, int dtype, float *ws, hipStream_t stream, KEvents ev_prep = {},
-                              KEvents ev_scan = {});
+                              KEvents ev_scan = {}, KEvents ev_out = {});
 size_t backward_lds_bytes(const Shape &sh);
 hipError_t launch_backward(const BwdLaunch &b, hipStream_t stream, KEvents ev_dq = {}, KEvents ev_scan = {},
                            KEvents ev_dkv = {});

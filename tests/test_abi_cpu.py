@@ -251,9 +251,9 @@ def test_delta_chunked_validation():
     L = linattn.lib()
     pid = _p(phi=linattn.LA_PHI_IDENTITY)  # d_k = d_v = 64
     need = L.la_delta_workspace_bytes(ctypes.byref(pid), 64)
-    # one record per (b, h, chunk): W and P (64 x 64), Ut (64 x d_v), gate products (2 x 64), fp32
+    # one record per (b, h, chunk): Qt and A (64 x 64), (P Ut)^T and B^T (d_v x 64), fp32
     n_chunks = -(-pid.N // 64)
-    assert need == 256 + 4 * pid.B * pid.H * n_chunks * (2 * 64 * 64 + 64 * 64 + 128)
+    assert need == 256 + 4 * pid.B * pid.H * n_chunks * (2 * 64 * 64 + 2 * 64 * pid.d_v)
     assert L.la_delta_workspace_bytes(ctypes.byref(pid), 32) == 0
     assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_k=32)), 64) == 0
     assert L.la_delta_workspace_bytes(ctypes.byref(_p(phi=linattn.LA_PHI_IDENTITY, d_v=40)), 64) == 0
