@@ -134,51 +134,87 @@ __device__ __forceinline__ void store8(float *p, const float *s) {
     *reinterpret_cast<float4 *>(p + 4) = make_float4(s[4], s[5], s[6], s[7]);
 }
 
-// phi(X) rows t0.. of one tile (rows past `rows` are zero)
-template <int D, int C, typename T>
-__device__ void stage_phi(const T *X, int t0, int rows, float *R, int tid) {
-    constexpr int RX = BCfg<D, C>::RX;
-#pragma unroll
-    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
-        const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (t < rows) {
-            load8(&X[(size_t)(t0 + t) * D + 8 * c8], a, b);
-            a = make_float4(elu1(a.x), elu1(a.y), elu1(a.z), elu1(a.w));
-            b = make_float4(elu1(b.x), elu1(b.y), elu1(b.z), elu1(b.w));
-        }
-        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8]) = a;
-        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8 + 4]) = b;
-    }
+// Staging loads are unconditional (rows clamped to the tile's last valid
+// row, zeros selected where the values are used) and a tile's pieces are all
+// issued before the first is used: a load under a branch makes the compiler
+// wait for every load in flight right after it, one memory round trip per
+// piece.
+
+// v where `in`, else zeros, per component (a select of whole float4 values
+// can be lowered through scratch memory)
+__device__ __forceinline__ float4 keep4(bool in, float4 v) {
+    return make_float4(in ? v.x : 0.f, in ? v.y : 0.f, in ? v.z : 0.f, in ? v.w : 0.f);
 }
 
-// [v | 1 | 0] rows of one tile (columns D..RV-1 written too)
+// A tile's rows as 16-byte pieces in registers: loaded for the next chunk
+// while the current one computes, written to LDS once its tiles are free.
+template <int D, int C>
+struct RowPieces {
+    static constexpr int NI = C * D / 8 / kThreads;
+    float4 a[NI], b[NI];
+};
 template <int D, int C, typename T>
-__device__ void stage_vaug(const T *V, int t0, int rows, float *R, int tid) {
+__device__ __forceinline__ void load_rows(const T *X, int t0, int rows, RowPieces<D, C> &p, int tid) {
+#pragma unroll
+    for (int i = 0; i < RowPieces<D, C>::NI; ++i) {
+        const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
+        load8(&X[(size_t)(t0 + (t < rows ? t : 0)) * D + 8 * c8], p.a[i], p.b[i]);
+    }
+}
+// phi(X) rows of one tile (rows past `rows` are zero)
+template <int D, int C>
+__device__ __forceinline__ void put_phi(const RowPieces<D, C> &p, int rows, float *R, int tid) {
+    constexpr int RX = BCfg<D, C>::RX;
+#pragma unroll
+    for (int i = 0; i < RowPieces<D, C>::NI; ++i) {
+        const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
+        const bool in = t < rows;
+        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8]) =
+            keep4(in, make_float4(elu1(p.a[i].x), elu1(p.a[i].y), elu1(p.a[i].z), elu1(p.a[i].w)));
+        *reinterpret_cast<float4 *>(&R[t * RX + 8 * c8 + 4]) =
+            keep4(in, make_float4(elu1(p.b[i].x), elu1(p.b[i].y), elu1(p.b[i].z), elu1(p.b[i].w)));
+    }
+}
+// [v | 1 | 0] rows of one tile (columns D..RV-1 written too)
+template <int D, int C>
+__device__ __forceinline__ void put_vaug(const RowPieces<D, C> &p, int rows, float *R, int tid) {
     constexpr int RV = BCfg<D, C>::RV;
 #pragma unroll
-    for (int i = 0; i < C * D / 8 / kThreads; ++i) {
+    for (int i = 0; i < RowPieces<D, C>::NI; ++i) {
         const int u = tid + i * kThreads, t = u / (D / 8), c8 = u % (D / 8);
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (t < rows) load8(&V[(size_t)(t0 + t) * D + 8 * c8], a, b);
-        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8]) = a;
-        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8 + 4]) = b;
+        const bool in = t < rows;
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8]) = keep4(in, p.a[i]);
+        *reinterpret_cast<float4 *>(&R[t * RV + 8 * c8 + 4]) = keep4(in, p.b[i]);
     }
     for (int u = tid; u < C * (RV - D); u += kThreads) {
         const int t = u / (RV - D), c = D + u % (RV - D);
         R[t * RV + c] = (c == D && t < rows) ? 1.f : 0.f;
     }
 }
-
 // G_aug rows (fp32 in the workspace, VK per token) of one tile
 template <int D, int C>
-__device__ void stage_g(const float *Gw, int t0, int rows, float *R, int tid) {
-    constexpr int RV = BCfg<D, C>::RV, VK = BCfg<D, C>::VK;
-    for (int u = tid; u < C * RV / 4; u += kThreads) {
-        const int t = u / (RV / 4), c4 = u % (RV / 4);
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < rows && 4 * c4 < VK) x = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + t) * VK + 4 * c4]);
-        *reinterpret_cast<float4 *>(&R[t * RV + 4 * c4]) = x;
+struct GPieces {
+    static constexpr int RV = BCfg<D, C>::RV, NU = C * RV / 4, NI = (NU + kThreads - 1) / kThreads;
+    float4 x[NI];
+};
+template <int D, int C>
+__device__ __forceinline__ void load_g(const float *Gw, int t0, int rows, GPieces<D, C> &p, int tid) {
+    using G = GPieces<D, C>;
+    constexpr int VK = BCfg<D, C>::VK;
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+        const int u = min(tid + i * kThreads, G::NU - 1), t = u / (G::RV / 4), c4 = u % (G::RV / 4);
+        p.x[i] = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + (t < rows ? t : 0)) * VK + 4 * min(c4, VK / 4 - 1)]);
+    }
+}
+template <int D, int C>
+__device__ __forceinline__ void put_g(const GPieces<D, C> &p, int rows, float *R, int tid) {
+    using G = GPieces<D, C>;
+    constexpr int VK = BCfg<D, C>::VK;
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+        const int u = tid + i * kThreads, t = u / (G::RV / 4), c4 = u % (G::RV / 4);
+        if (u < G::NU) *reinterpret_cast<float4 *>(&R[t * G::RV + 4 * c4]) = keep4(t < rows && 4 * c4 < VK, p.x[i]);
     }
 }
 
@@ -294,12 +330,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     }
     put_state<D, C>(S, sm.S, w, lane);
 
+    // the rows of chunk c are loaded during chunk c - 1 (the last chunk
+    // re-reads itself: every load stays unconditional)
+    RowPieces<D, C> xq, xk, xv;
+    auto fetch = [&](int cc) {
+        const int tt0 = cc * C, rr = min(C, N - tt0);
+        load_rows<D, C>(Qs, tt0, rr, xq, tid);
+        load_rows<D, C>(Ks, tt0, rr, xk, tid);
+        load_rows<D, C>(Vs, tt0, rr, xv, tid);
+    };
+    fetch(c_begin);
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C, rows = min(C, N - t0);
         block_sync_lds();  // the previous tile's tiles are consumed, the state image is complete
-        stage_phi<D, C, T>(Qs, t0, rows, sm.P, tid);
-        stage_phi<D, C, T>(Ks, t0, rows, sm.K, tid);
-        stage_vaug<D, C, T>(Vs, t0, rows, sm.V, tid);
+        put_phi<D, C>(xq, rows, sm.P, tid);
+        put_phi<D, C>(xk, rows, sm.K, tid);
+        put_vaug<D, C>(xv, rows, sm.V, tid);
+        fetch(min(c + 1, c_end - 1));
         block_sync_lds();
 
         // scores P = phi(Q) phi(K)^T of this wave's key blocks, masked (key <= query)
@@ -331,11 +378,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 dov[NBN];
             float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+            for (int j = 0; j < NBN; ++j)  // unconditional loads (clamped), selects at use
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = m0 + 4 * g + e, col = 16 * (NB0 + j) + c16;
+                    dov[j][e] = load1(&dOs[(size_t)(t0 + (t < rows ? t : 0)) * D + (col < D ? col : 0)]);
+                }
+#pragma unroll
             for (int j = 0; j < NBN; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = m0 + 4 * g + e, col = 16 * (NB0 + j) + c16;
-                    const float d = (t < rows && col < D) ? load1(&dOs[(size_t)(t0 + t) * D + col]) : 0.f;
+                    const float d = (t < rows && col < D) ? dov[j][e] : 0.f;
                     dov[j][e] = d;
                     part[e] += d * num[j][e];
                 }
@@ -489,13 +543,26 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     }
     put_state<D, C>(R, sm.S, w, lane);
 
+    // the chunks from last to first; the rows of chunk c are loaded during
+    // chunk c + 1 (the first chunk re-reads itself: every load stays unconditional)
+    RowPieces<D, C> xq, xk, xv;
+    GPieces<D, C> xg;
+    auto fetch = [&](int cc) {
+        const int tt0 = cc * C, rr = min(C, N - tt0);
+        load_rows<D, C>(Qs, tt0, rr, xq, tid);
+        load_rows<D, C>(Ks, tt0, rr, xk, tid);
+        load_rows<D, C>(Vs, tt0, rr, xv, tid);
+        load_g<D, C>(Gw, tt0, rr, xg, tid);
+    };
+    fetch(c_end - 1);
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * C, rows = min(C, N - t0);
         block_sync_lds();
-        stage_phi<D, C, T>(Qs, t0, rows, sm.P, tid);
-        stage_phi<D, C, T>(Ks, t0, rows, sm.K, tid);
-        stage_vaug<D, C, T>(Vs, t0, rows, sm.V, tid);
-        stage_g<D, C>(Gw, t0, rows, sm.G, tid);
+        put_phi<D, C>(xq, rows, sm.P, tid);
+        put_phi<D, C>(xk, rows, sm.K, tid);
+        put_vaug<D, C>(xv, rows, sm.V, tid);
+        put_g<D, C>(xg, rows, sm.G, tid);
+        fetch(max(c - 1, c_begin));
         block_sync_lds();
 
         // dphi(K): B = V_aug G_aug^T masked (query >= key), times phi(Q); + V_aug R_aug^T
