@@ -60,6 +60,34 @@ __device__ __forceinline__ f32x4d zero4d() { return f32x4d{0.f, 0.f, 0.f, 0.f}; 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }  // bf16 bits
 
+// bf16 matrix-instruction operands (v_mfma_f32_16x16x32_bf16: lane l supplies
+// A[l%16][8(l/16)..+7] and B[8(l/16)..+7][l%16]) and the split of fp32 values
+// into bf16 hi and lo parts, x = hi + lo to about 2^-17 relative
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
+typedef float df32x2 __attribute__((ext_vector_type(2)));
+union D8 {
+    dbf16x8 v;
+    uint32_t u[4];
+};
+__device__ __forceinline__ uint32_t dbf2(float a, float b) {  // round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(df32x2{a, b}, dbf16x2));
+}
+__device__ __forceinline__ void dsplit8(const float (&x)[8], D8 &hi, D8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t h = dbf2(x[2 * e], x[2 * e + 1]);
+        hi.u[e] = h;
+        lo.u[e] = dbf2(x[2 * e] - __uint_as_float(h << 16), x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+    }
+}
+// a b in three bf16 passes (hi hi + hi lo + lo hi), accumulated in fp32
+__device__ __forceinline__ f32x4d mma3(const D8 &ah, const D8 &al, const D8 &bh, const D8 &bl, f32x4d c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bh.v, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // acc[16 rows at m0][16 columns at n0] += A B over K = 4 * KS.
@@ -290,23 +318,51 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
                 make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     };
+    // bf16 storage: both products in three bf16 passes (k-slot 8q + j of key
+    // pair hp = token 16(2hp + j/4) + 4q + j%4 for P X, 32h + 4j + q for KG X);
+    // fp32 storage keeps fp32 operands, its results being held to fp32 accuracy
+    constexpr bool BF = sizeof(T) == 2;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        for (int n0 = w; n0 < nxt; n0 += 8) {
-            const int n1 = n0 + 4, n1c = min(n1, nxt - 1);
-            f32x4d acc0 = zero4d(), acc1 = zero4d();
+        if constexpr (BF) {
+            D8 ah[2], al[2];
 #pragma unroll
-            for (int kb = 0; kb <= m; ++kb) {
-                const float pav[4] = {prow[m][kb].x, prow[m][kb].y, prow[m][kb].z, prow[m][kb].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float *xr = &sX[(16 * kb + 4 * q + j) * RX + c16];
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n0], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n1c], acc1, 0, 0, 0);
-                }
+            for (int hp = 0; 2 * hp <= m; ++hp) {
+                const float pa[8] = {prow[m][2 * hp].x,     prow[m][2 * hp].y,     prow[m][2 * hp].z,
+                                     prow[m][2 * hp].w,     prow[m][2 * hp + 1].x, prow[m][2 * hp + 1].y,
+                                     prow[m][2 * hp + 1].z, prow[m][2 * hp + 1].w};
+                dsplit8(pa, ah[hp], al[hp]);
             }
-            store_p(m, n0, acc0, qv[m]);
-            if (n1 < nxt) store_p(m, n1, acc1, qv[m]);
+            for (int n = w; n < nxt; n += 4) {
+                f32x4d acc = zero4d();
+#pragma unroll
+                for (int hp = 0; 2 * hp <= m; ++hp) {
+                    float xv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xv[j] = sX[(16 * (2 * hp + j / 4) + 4 * q + j % 4) * RX + 16 * n + c16];
+                    D8 xh, xl;
+                    dsplit8(xv, xh, xl);
+                    acc = mma3(ah[hp], al[hp], xh, xl, acc);
+                }
+                store_p(m, n, acc, qv[m]);
+            }
+        } else {
+            for (int n0 = w; n0 < nxt; n0 += 8) {
+                const int n1 = n0 + 4, n1c = min(n1, nxt - 1);
+                f32x4d acc0 = zero4d(), acc1 = zero4d();
+#pragma unroll
+                for (int kb = 0; kb <= m; ++kb) {
+                    const float pav[4] = {prow[m][kb].x, prow[m][kb].y, prow[m][kb].z, prow[m][kb].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float *xr = &sX[(16 * kb + 4 * q + j) * RX + c16];
+                        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n0], acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pav[j], xr[16 * n1c], acc1, 0, 0, 0);
+                    }
+                }
+                store_p(m, n0, acc0, qv[m]);
+                if (n1 < nxt) store_p(m, n1, acc1, qv[m]);
+            }
         }
     }
     __syncthreads();  // every read of P done before A takes its place
@@ -331,6 +387,30 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
         float ka[16];  // KG[16m + r][t], t = 4i + q
 #pragma unroll
         for (int i = 0; i < 16; ++i) ka[i] = sK[(4 * i + q) * kXR + 16 * m + r] * gk[i];
+        if constexpr (BF) {
+            D8 ah[2], al[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float a8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a8[j] = ka[8 * h + j];
+                dsplit8(a8, ah[h], al[h]);
+            }
+            for (int n = w; n < nxt; n += 4) {
+                f32x4d acc = zero4d();
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float xv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xv[j] = sX[(4 * (8 * h + j) + q) * RX + 16 * n + c16];
+                    D8 xh, xl;
+                    dsplit8(xv, xh, xl);
+                    acc = mma3(ah[h], al[h], xh, xl, acc);
+                }
+                store_a(m, n, acc);
+            }
+            continue;
+        }
         for (int n0 = w; n0 < nxt; n0 += 8) {
             const int n1 = n0 + 4, n1c = min(n1, nxt - 1);
             f32x4d acc0 = zero4d(), acc1 = zero4d();

@@ -54,6 +54,31 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// bf16 matrix-instruction operands (v_mfma_f32_16x16x32_bf16: lane l supplies
+// A[l%16][8(l/16)..+7] and B[8(l/16)..+7][l%16]) and the split of fp32 values
+// into bf16 hi and lo parts, x = hi + lo to about 2^-17 relative
+typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 gbf16x2 __attribute__((ext_vector_type(2)));
+typedef float gf32x2 __attribute__((ext_vector_type(2)));
+union B8 {
+    gbf16x8 v;
+    uint32_t u[4];
+};
+__device__ __forceinline__ uint32_t bf2(float a, float b) {  // round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(gf32x2{a, b}, gbf16x2));
+}
+__device__ __forceinline__ void split8(const float (&x)[8], B8 &hi, B8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t h = bf2(x[2 * e], x[2 * e + 1]);
+        hi.u[e] = h;
+        lo.u[e] = bf2(x[2 * e] - __uint_as_float(h << 16), x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+    }
+}
+__device__ __forceinline__ f32x4 mma8(const B8 &a, const B8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
 struct GlaSmem {
     float Q[kC][kRS];      // q rows (raw)
     float K[kC][kRS];      // k rows (raw)
@@ -491,9 +516,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_gla_prep(GatedArgs a, int n_chu
             }
     }
     // value products, 64 columns at a time: V^T [column][token] goes to the
-    // rows of sm.Q; wave w
-    // forms (P V)^T for its query block and (KE^T V)^T for channels 16w..16w+15,
-    // both with A = V^T (lane: column c16, tokens 16Tb + 4g..+3)
+    // rows of sm.Q; wave w forms (P V)^T for its query block and (KE^T V)^T for
+    // channels 16w..16w+15 on bf16 matrix instructions, with A = V^T (lane:
+    // column c16) and k-slot 8g + j of half h = token 16(2h + j/4) + 4g + j%4,
+    // so the score accumulators are the B operand of (P V)^T as they stand and
+    // KE is read as four-token runs.  bf16 storage: P and KE enter as bf16
+    // hi + lo parts and V is exact in bf16.  fp32 storage keeps fp32 operands
+    // (v_mfma_f32_16x16x4_f32, k-slot g of step (Tb, e) = token 16Tb + 4g + e),
+    // as its results are held to fp32 accuracy.
+    constexpr bool BF = sizeof(T) == 2;
+    B8 ph[2], pl[2];
+    if constexpr (BF) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float pp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pp[j] = pt[2 * h + j / 4][j % 4];
+            split8(pp, ph[h], pl[h]);
+        }
+    }
+    B8 kh[2], kl[2];
+    bool ke_split = !BF;
     for (int cg = 0; cg < dvp; cg += 64) {
         T rv[16];
 #pragma unroll
@@ -510,23 +553,55 @@ __global__ __launch_bounds__(kThreads, 2) void k_gla_prep(GatedArgs a, int n_chu
         for (int j = 0; j < 16; j += 4)
             *reinterpret_cast<float4 *>(&sm.Q[sc][16 * sq + j]) = make_float4(vr[j], vr[j + 1], vr[j + 2], vr[j + 3]);
         lds_barrier();
+        if (!ke_split) {  // KE of channels 16w + c16 (first group only; KE does not change)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float kk[8];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const float4 k4 = *reinterpret_cast<const float4 *>(&sm.KE[16 * w + c16][16 * (2 * h + s2) + 4 * g]);
+                    kk[4 * s2] = k4.x; kk[4 * s2 + 1] = k4.y; kk[4 * s2 + 2] = k4.z; kk[4 * s2 + 3] = k4.w;
+                }
+                split8(kk, kh[h], kl[h]);
+            }
+            ke_split = true;
+        }
 #pragma unroll 1
         for (int cb = 0; cb < 4; ++cb) {
             const int col = cg + 16 * cb;
             if (col < dvp) {  // wave-uniform
                 f32x4 pv = zero4(), kv = zero4();
+                if constexpr (BF) {
 #pragma unroll
-                for (int Tb = 0; Tb < 4; ++Tb) {
-                    const float4 va = *reinterpret_cast<const float4 *>(&sm.Q[16 * cb + c16][16 * Tb + 4 * g]);
-                    const float4 kk = *reinterpret_cast<const float4 *>(&sm.KE[16 * w + c16][16 * Tb + 4 * g]);
-                    pv = mma(va.x, pt[Tb][0], pv);
-                    kv = mma(va.x, kk.x, kv);
-                    pv = mma(va.y, pt[Tb][1], pv);
-                    kv = mma(va.y, kk.y, kv);
-                    pv = mma(va.z, pt[Tb][2], pv);
-                    kv = mma(va.z, kk.z, kv);
-                    pv = mma(va.w, pt[Tb][3], pv);
-                    kv = mma(va.w, kk.w, kv);
+                    for (int h = 0; h < 2; ++h) {
+                        float vv[8];
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            const float4 v4 =
+                                *reinterpret_cast<const float4 *>(&sm.Q[16 * cb + c16][16 * (2 * h + s2) + 4 * g]);
+                            vv[4 * s2] = v4.x; vv[4 * s2 + 1] = v4.y; vv[4 * s2 + 2] = v4.z; vv[4 * s2 + 3] = v4.w;
+                        }
+                        B8 vh, vl;
+                        split8(vv, vh, vl);  // vl = 0: V is exact in bf16
+                        pv = mma8(vh, ph[h], pv);
+                        kv = mma8(vh, kh[h], kv);
+                        pv = mma8(vh, pl[h], pv);
+                        kv = mma8(vh, kl[h], kv);
+                    }
+                } else {
+#pragma unroll
+                    for (int Tb = 0; Tb < 4; ++Tb) {
+                        const float4 va = *reinterpret_cast<const float4 *>(&sm.Q[16 * cb + c16][16 * Tb + 4 * g]);
+                        const float4 kk = *reinterpret_cast<const float4 *>(&sm.KE[16 * w + c16][16 * Tb + 4 * g]);
+                        pv = mma(va.x, pt[Tb][0], pv);
+                        kv = mma(va.x, kk.x, kv);
+                        pv = mma(va.y, pt[Tb][1], pv);
+                        kv = mma(va.y, kk.y, kv);
+                        pv = mma(va.z, pt[Tb][2], pv);
+                        kv = mma(va.z, kk.z, kv);
+                        pv = mma(va.w, pt[Tb][3], pv);
+                        kv = mma(va.w, kk.w, kv);
+                    }
                 }
                 // lane (4g+e, c16): (P V)[16I + c16][col + 4g + e], (KE^T V)[16w + c16][col + 4g + e]
 #pragma unroll
