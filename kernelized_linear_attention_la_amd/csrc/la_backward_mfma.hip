@@ -82,17 +82,76 @@ struct BTiles {
 
 // C[16 rows at m0][16 NB columns at n0] += A B over K (a multiple of 4).
 // TA: A is given as its transpose (row-major [k][m]); TB: B as its transpose ([n][k]).
-template <int K, int NB, bool TA, bool TB>
+// bf16 matrix-instruction operands (v_mfma_f32_16x16x32_bf16: lane l supplies
+// A[l%16][8(l/16)..+7] and B[8(l/16)..+7][l%16], and receives the same
+// accumulator lanes as the fp32 instruction) and the split of fp32 values
+// into bf16 hi and lo parts, x = hi + lo to about 2^-17 relative
+typedef __bf16 wbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 wbf16x2 __attribute__((ext_vector_type(2)));
+typedef float wf32x2 __attribute__((ext_vector_type(2)));
+union W8 {
+    wbf16x8 v;
+    uint32_t u[4];
+};
+__device__ __forceinline__ uint32_t wbf2(float a, float b) {  // round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(wf32x2{a, b}, wbf16x2));
+}
+__device__ __forceinline__ void wsplit8(const float (&x)[8], W8 &hi, W8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t h = wbf2(x[2 * e], x[2 * e + 1]);
+        hi.u[e] = h;
+        lo.u[e] = wbf2(x[2 * e] - __uint_as_float(h << 16), x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+    }
+}
+
+// acc[j] (rows m0.., columns n0 + 16j..) += A B over K, A and B read from
+// row-major fp32 LDS tiles, either transposed (TA: A stored [k][m]; TB: B
+// stored [n][k]).  W3 (bf16 storage): three bf16 passes (hi hi + hi lo +
+// lo hi) per 32-wide k step, k padded with zeros to a multiple of 32; the
+// normalised backward cancels, so single bf16 operands would lose several
+// percent, while the split keeps about 2^-16.  Otherwise fp32 operands.
+template <int K, int NB, bool TA, bool TB, bool W3 = false>
 __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float *B, int ldb, int n0, f32x4 (&acc)[NB],
                                    int lane) {
     const int r = lane & 15, q = lane >> 4;
+    if constexpr (!W3) {
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4) {
-        const float a = TA ? A[(k0 + q) * lda + m0 + r] : A[(m0 + r) * lda + k0 + q];
+        for (int k0 = 0; k0 < K; k0 += 4) {
+            const float a = TA ? A[(k0 + q) * lda + m0 + r] : A[(m0 + r) * lda + k0 + q];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const float b = TB ? B[(n0 + 16 * j + r) * ldb + k0 + q] : B[(k0 + q) * ldb + n0 + 16 * j + r];
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+            for (int j = 0; j < NB; ++j) {
+                const float b = TB ? B[(n0 + 16 * j + r) * ldb + k0 + q] : B[(k0 + q) * ldb + n0 + 16 * j + r];
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = k0 + 8 * q + e, kc = k < K ? k : K - 1;
+                const float v = TA ? A[kc * lda + m0 + r] : A[(m0 + r) * lda + kc];
+                av[e] = k < K ? v : 0.f;
+            }
+            W8 ah, al;
+            wsplit8(av, ah, al);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                float bv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int k = k0 + 8 * q + e, kc = k < K ? k : K - 1;
+                    const float v = TB ? B[(n0 + 16 * j + r) * ldb + kc] : B[kc * ldb + n0 + 16 * j + r];
+                    bv[e] = k < K ? v : 0.f;
+                }
+                W8 bh, bl;
+                wsplit8(bv, bh, bl);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bh.v, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, acc[j], 0, 0, 0);
+            }
         }
     }
 }
@@ -291,6 +350,9 @@ __device__ __forceinline__ void row_sync() {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
+    // bf16 storage at d = 64: products in three bf16 passes (at d = 128 they
+    // measured no faster than the fp32 products)
+    constexpr bool W3 = sizeof(T) == 2 && D == 64;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -354,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 p[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) p[j] = zero4();
-            mm<D, NSB, false, true>(sm.P, RX, m0, sm.K, RX, 16 * cs * NSB, p, lane);
+            mm<D, NSB, false, true, W3>(sm.P, RX, m0, sm.K, RX, 16 * cs * NSB, p, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -372,8 +434,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 num[NBN];
 #pragma unroll
             for (int j = 0; j < NBN; ++j) num[j] = zero4();
-            mm<C, NBN, false, false>(sm.W, RW, m0, sm.V, RV, 16 * NB0, num, lane);
-            mm<D, NBN, false, false>(sm.P, RX, m0, sm.S, RV, 16 * NB0, num, lane);
+            mm<C, NBN, false, false, W3>(sm.W, RW, m0, sm.V, RV, 16 * NB0, num, lane);
+            mm<D, NBN, false, false, W3>(sm.P, RX, m0, sm.S, RV, 16 * NB0, num, lane);
             // dO of this wave's columns and its share of the row sums dO . num
             f32x4 dov[NBN];
             float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -454,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 s[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) s[j] = zero4();
-            mm<VK, NSB, false, true>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
+            mm<VK, NSB, false, true, W3>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -467,8 +529,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
         f32x4 dp[NDW];
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dp[j] = zero4();
-        mm<C, NDW, false, false>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
-        mm<VK, NDW, false, true>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
+        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
+        mm<VK, NDW, false, true, W3>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
         // dQ = dphi * min(phi(q), 1) (elu'(q): 1 for q > 0, exp(q) = phi(q) otherwise)
 #pragma unroll
         for (int j = 0; j < NDW; ++j)
@@ -481,8 +543,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
         for (int q = 0; q < FBW; ++q) {
             const int f0 = 16 * (kNW * q + w);
-            mm<C, NVB, true, false>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
-            mm<C, NVB, true, false>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
+            mm<C, NVB, true, false, W3>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
+            mm<C, NVB, true, false, W3>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
         }
         put_state<D, C>(S, sm.S, w, lane);
     }
@@ -510,6 +572,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
+    // bf16 storage at d = 64: products in three bf16 passes (at d = 128 they
+    // measured no faster than the fp32 products)
+    constexpr bool W3 = sizeof(T) == 2 && D == 64;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -570,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
             f32x4 b[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) b[j] = zero4();
-            mm<VK, NSB, false, true>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
+            mm<VK, NSB, false, true, W3>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -583,15 +648,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         f32x4 dk[NDW];
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dk[j] = zero4();
-        mm<C, NDW, false, false>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
-        mm<VK, NDW, false, true>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
+        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
+        mm<VK, NDW, false, true, W3>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
         // dV: P' = phi(K) phi(Q)^T masked, times G; + phi(K) R
         f32x4 dv[NDW];
         {
             f32x4 p[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) p[j] = zero4();
-            mm<D, NSB, false, true>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
+            mm<D, NSB, false, true, W3>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
             row_sync<CS>();  // the row block's waves have read the scores B before W is overwritten
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
@@ -604,8 +669,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         row_sync<CS>();
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dv[j] = zero4();
-        mm<C, NDW, false, false>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
-        mm<D, NDW, false, false>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
+        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
+        mm<D, NDW, false, false, W3>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
         // dK = dphi(K) * min(phi(k), 1)
 #pragma unroll
         for (int j = 0; j < NDW; ++j)
@@ -617,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         block_sync_lds();  // the state image is no longer read
         // R_aug += phi(Q)^T G_aug (this wave's feature rows)
 #pragma unroll
-        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
+        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false, W3>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
         put_state<D, C>(R, sm.S, w, lane);
     }
 }
