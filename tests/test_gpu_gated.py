@@ -160,6 +160,8 @@ CHUNKED_CASES = [
     (1, 1, 65, 64, 48, "bf16", True),      # one token past a chunk
     (2, 4, 1000, 64, 128, "bf16", False),
     (4, 8, 2048, 64, 64, "bf16", True),    # the gated delta-rule workload's shape
+    (1, 2, 420, 64, 32, "f32", True),      # seven chunks: one full round of the scan's ring and a ragged tail
+    (2, 1, 300, 64, 80, "bf16", True),     # five chunks, d_v past one 64-column group
 ]
 
 
