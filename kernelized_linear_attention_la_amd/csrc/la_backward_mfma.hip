@@ -111,7 +111,7 @@ __device__ __forceinline__ void wsplit8(const float (&x)[8], W8 &hi, W8 &lo) {
 // lo hi) per 32-wide k step, k padded with zeros to a multiple of 32; the
 // normalised backward cancels, so single bf16 operands would lose several
 // percent, while the split keeps about 2^-16.  Otherwise fp32 operands.
-template <int K, int NB, bool TA, bool TB, bool W3 = false>
+template <int K, int NB, bool TA, bool TB, bool W3 = false, bool UNR = false>
 __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float *B, int ldb, int n0, f32x4 (&acc)[NB],
                                    int lane) {
     const int r = lane & 15, q = lane >> 4;
@@ -126,7 +126,8 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
             }
         }
     } else {
-#pragma unroll 1
+        // UNR: the 32-wide steps unrolled (more loads in flight, more registers)
+#pragma unroll UNR ? 8 : 1
         for (int k0 = 0; k0 < K; k0 += 32) {
             float av[8];
 #pragma unroll
@@ -350,8 +351,9 @@ __device__ __forceinline__ void row_sync() {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
-    // bf16 storage at d = 64: products in three bf16 passes (at d = 128 they
-    // measured no faster than the fp32 products)
+    // bf16 storage at d = 64: products in three bf16 passes, one 32-wide k
+    // step at a time (unrolled, this kernel spills); at d = 128 they measured
+    // no faster than the fp32 products
     constexpr bool W3 = sizeof(T) == 2 && D == 64;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
@@ -572,9 +574,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
-    // bf16 storage at d = 64: products in three bf16 passes (at d = 128 they
-    // measured no faster than the fp32 products)
-    constexpr bool W3 = sizeof(T) == 2 && D == 64;
+    // bf16 storage: products in three bf16 passes, the k steps unrolled
+    constexpr bool W3 = sizeof(T) == 2, UNR = true;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
             f32x4 b[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) b[j] = zero4();
-            mm<VK, NSB, false, true, W3>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
+            mm<VK, NSB, false, true, W3, UNR>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -648,15 +649,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         f32x4 dk[NDW];
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dk[j] = zero4();
-        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
-        mm<VK, NDW, false, true, W3>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
+        mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
+        mm<VK, NDW, false, true, W3, UNR>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
         // dV: P' = phi(K) phi(Q)^T masked, times G; + phi(K) R
         f32x4 dv[NDW];
         {
             f32x4 p[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) p[j] = zero4();
-            mm<D, NSB, false, true, W3>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
+            mm<D, NSB, false, true, W3, UNR>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
             row_sync<CS>();  // the row block's waves have read the scores B before W is overwritten
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
@@ -669,8 +670,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         row_sync<CS>();
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dv[j] = zero4();
-        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
-        mm<D, NDW, false, false, W3>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
+        mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
+        mm<D, NDW, false, false, W3, UNR>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
         // dK = dphi(K) * min(phi(k), 1)
 #pragma unroll
         for (int j = 0; j < NDW; ++j)
@@ -682,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         block_sync_lds();  // the state image is no longer read
         // R_aug += phi(Q)^T G_aug (this wave's feature rows)
 #pragma unroll
-        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false, W3>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
+        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false, W3, UNR>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
         put_state<D, C>(R, sm.S, w, lane);
     }
 }
