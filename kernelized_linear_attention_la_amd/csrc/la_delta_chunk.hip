@@ -207,21 +207,45 @@ __global__ __launch_bounds__(kXT) void k_delta_prep(const T *__restrict__ Q, con
     float *Qt = rec, *Am = rec + kXC * kXK, *PUT = rec + 2 * kXC * kXK, *BT = PUT + (size_t)kXC * dv;
     float *const P = Am;  // P until the operator A replaces it
 
-    // Gram tiles of row block w: K K^T (strictly lower part -> M) and Q K^T
-    // (lower part with the diagonal -> P); tiles above the diagonal are zero
-    for (int cb = 0; cb < 4; ++cb) {
-        f32x4d gk = zero4d(), gq = zero4d();
-        if (cb <= w) {
+    // Gram tiles: K K^T of row block w (strictly lower part -> M) and Q K^T
+    // of row block 3 - w (lower part with the diagonal -> P), five tiles per
+    // wave; tiles above the diagonal are zero.  bf16 storage: q and k are exact
+    // in bf16, so each tile is two bf16 matrix instructions (k-slot 8g + j of
+    // step kk = feature 32kk + 8g + j) with no rounding of the operands.
+    auto gram = [&](const float *X, int rb, int cb) {
+        f32x4d acc = zero4d();
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float *xa = &X[(16 * rb + c16) * kXR + 32 * kk + 8 * g];
+                const float *xb = &sK[(16 * cb + c16) * kXR + 32 * kk + 8 * g];
+                D8 a8, b8;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a8.u[e] = dbf2(xa[2 * e], xa[2 * e + 1]);
+                    b8.u[e] = dbf2(xb[2 * e], xb[2 * e + 1]);
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8.v, b8.v, acc, 0, 0, 0);
+            }
+        } else {
             auto bk = [&](int k, int n) { return sK[(16 * cb + n) * kXR + k]; };
-            gk = mm4<16>([&](int m, int k) { return sK[(16 * w + m) * kXR + k]; }, bk, gk, lane);
-            gq = mm4<16>([&](int m, int k) { return sQ[(16 * w + m) * kXR + k]; }, bk, gq, lane);
+            acc = mm4<16>([&](int m, int k) { return X[(16 * rb + m) * kXR + k]; }, bk, acc, lane);
         }
+        return acc;
+    };
+    const int rk = w, rq = 3 - w;
+    for (int cb = 0; cb < 4; ++cb) {
+        const f32x4d gk = cb <= rk ? gram(sK, rk, cb) : zero4d();
+        const f32x4d gq = cb <= rq ? gram(sQ, rq, cb) : zero4d();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = 16 * w + 4 * g + e, s = 16 * cb + c16;
-            const float ratio = s <= t ? __builtin_amdgcn_exp2f(sl[t] - sl[s]) : 0.f;
-            sM[t * kXR + s] = s < t ? sb[t] * ratio * gk[e] : 0.f;
-            P[t * kXK + s] = ratio * gq[e];
+            const int s = 16 * cb + c16;
+            const int t = 16 * rk + 4 * g + e;
+            const float rat_k = s < t ? __builtin_amdgcn_exp2f(sl[t] - sl[s]) : 0.f;
+            sM[t * kXR + s] = s < t ? sb[t] * rat_k * gk[e] : 0.f;
+            const int t2 = 16 * rq + 4 * g + e;
+            const float rat_q = s <= t2 ? __builtin_amdgcn_exp2f(sl[t2] - sl[s]) : 0.f;
+            P[t2 * kXK + s] = rat_q * gq[e];
         }
     }
     __syncthreads();  // every read of sQ done: its space takes the right-hand sides
