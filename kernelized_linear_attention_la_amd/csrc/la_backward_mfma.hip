@@ -68,7 +68,7 @@ struct BCfg {
 };
 
 template <int D, int C>
-struct BTiles {
+struct alignas(16) BTiles {  // every row stride and tile size a multiple of 4 floats
     using B = BCfg<D, C>;
     float P[C * B::RX];    // phi(Q) rows [token][feature]
     float K[C * B::RX];    // phi(K) rows
@@ -79,6 +79,22 @@ struct BTiles {
     float DEN[C];          // normaliser of each query row (dQ pass)
     float DOT[B::CS][C];   // dO . num of each query row over one column split
 };
+
+// v = row[k..k+3], row[k+16..k+19] from a 16-byte aligned LDS row, zeros past
+// K (a multiple of 4, so each 4-wide piece lies wholly inside or outside)
+template <int K>
+__device__ __forceinline__ void row8(const float *row, int k, float (&v)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kh = k + 16 * h;
+        const float4 x = *reinterpret_cast<const float4 *>(row + (K % 32 == 0 || kh < K ? kh : K - 4));
+        const bool in = K % 32 == 0 || kh < K;
+        v[4 * h + 0] = in ? x.x : 0.f;
+        v[4 * h + 1] = in ? x.y : 0.f;
+        v[4 * h + 2] = in ? x.z : 0.f;
+        v[4 * h + 3] = in ? x.w : 0.f;
+    }
+}
 
 // C[16 rows at m0][16 NB columns at n0] += A B over K (a multiple of 4).
 // TA: A is given as its transpose (row-major [k][m]); TB: B as its transpose ([n][k]).
@@ -110,10 +126,13 @@ __device__ __forceinline__ void wsplit8(const float (&x)[8], W8 &hi, W8 &lo) {
 // stored [n][k]).  W3 (bf16 storage): three bf16 passes (hi hi + hi lo +
 // lo hi) per 32-wide k step, k padded with zeros to a multiple of 32; the
 // normalised backward cancels, so single bf16 operands would lose several
-// percent, while the split keeps about 2^-16.  Otherwise fp32 operands.
-template <int K, int NB, bool TA, bool TB, bool W3 = false, bool UNR = false>
+// percent, while the split keeps about 2^-16.  EA / EB: that operand is exact
+// in bf16 (V_aug of bf16 storage), its lo part is zero and its pass is
+// skipped (same result).  Otherwise fp32 operands.
+template <int K, int NB, bool TA, bool TB, bool W3 = false, bool UNR = false, bool EA = false, bool EB = false>
 __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float *B, int ldb, int n0, f32x4 (&acc)[NB],
                                    int lane) {
+    static_assert(K % 4 == 0, "k in pieces of four");
     const int r = lane & 15, q = lane >> 4;
     if constexpr (!W3) {
 #pragma unroll
@@ -126,32 +145,45 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
             }
         }
     } else {
-        // UNR: the 32-wide steps unrolled (more loads in flight, more registers)
+        // UNR: the 32-wide steps unrolled (more loads in flight, more registers).
+        // Lane group q supplies k = k0 + 4q + {0..3} and k0 + 16 + 4q + {0..3}
+        // (the same permutation of k for A and B, so the sum is unchanged): a
+        // read across rows then puts the four groups on rows 4 apart, which the
+        // row strides (4 mod 16 floats) map to distinct LDS bank windows, and a
+        // read along a row is still two 16-byte pieces.
 #pragma unroll UNR ? 8 : 1
         for (int k0 = 0; k0 < K; k0 += 32) {
             float av[8];
+            if constexpr (TA) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = k0 + 8 * q + e, kc = k < K ? k : K - 1;
-                const float v = TA ? A[kc * lda + m0 + r] : A[(m0 + r) * lda + kc];
-                av[e] = k < K ? v : 0.f;
+                for (int e = 0; e < 8; ++e) {
+                    const int k = k0 + 4 * q + (e & 3) + 16 * (e >> 2), kc = k < K ? k : K - 1;
+                    const float v = A[kc * lda + m0 + r];
+                    av[e] = k < K ? v : 0.f;
+                }
+            } else {
+                row8<K>(A + (m0 + r) * lda, k0 + 4 * q, av);
             }
             W8 ah, al;
             wsplit8(av, ah, al);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 float bv[8];
+                if constexpr (TB) {
+                    row8<K>(B + (n0 + 16 * j + r) * ldb, k0 + 4 * q, bv);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int k = k0 + 8 * q + e, kc = k < K ? k : K - 1;
-                    const float v = TB ? B[(n0 + 16 * j + r) * ldb + kc] : B[kc * ldb + n0 + 16 * j + r];
-                    bv[e] = k < K ? v : 0.f;
+                    for (int e = 0; e < 8; ++e) {
+                        const int k = k0 + 4 * q + (e & 3) + 16 * (e >> 2), kc = k < K ? k : K - 1;
+                        const float v = B[kc * ldb + n0 + 16 * j + r];
+                        bv[e] = k < K ? v : 0.f;
+                    }
                 }
                 W8 bh, bl;
                 wsplit8(bv, bh, bl);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bh.v, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, acc[j], 0, 0, 0);
+                if constexpr (!EB) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, acc[j], 0, 0, 0);
+                if constexpr (!EA) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, acc[j], 0, 0, 0);
             }
         }
     }
@@ -351,10 +383,9 @@ __device__ __forceinline__ void row_sync() {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
-    // bf16 storage at d = 64: products in three bf16 passes, one 32-wide k
-    // step at a time (unrolled, this kernel spills); at d = 128 they measured
-    // no faster than the fp32 products
-    constexpr bool W3 = sizeof(T) == 2 && D == 64;
+    // bf16 storage: products in bf16 passes (two where V_aug is an operand),
+    // the k steps unrolled
+    constexpr bool W3 = sizeof(T) == 2, UNR = true;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -418,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 p[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) p[j] = zero4();
-            mm<D, NSB, false, true, W3>(sm.P, RX, m0, sm.K, RX, 16 * cs * NSB, p, lane);
+            mm<D, NSB, false, true, W3, UNR>(sm.P, RX, m0, sm.K, RX, 16 * cs * NSB, p, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -436,8 +467,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 num[NBN];
 #pragma unroll
             for (int j = 0; j < NBN; ++j) num[j] = zero4();
-            mm<C, NBN, false, false, W3>(sm.W, RW, m0, sm.V, RV, 16 * NB0, num, lane);
-            mm<D, NBN, false, false, W3>(sm.P, RX, m0, sm.S, RV, 16 * NB0, num, lane);
+            mm<C, NBN, false, false, W3, UNR, false, true>(sm.W, RW, m0, sm.V, RV, 16 * NB0, num, lane);
+            mm<D, NBN, false, false, W3, UNR>(sm.P, RX, m0, sm.S, RV, 16 * NB0, num, lane);
             // dO of this wave's columns and its share of the row sums dO . num
             f32x4 dov[NBN];
             float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -518,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             f32x4 s[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) s[j] = zero4();
-            mm<VK, NSB, false, true, W3>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
+            mm<VK, NSB, false, true, W3, UNR, false, true>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -531,8 +562,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
         f32x4 dp[NDW];
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dp[j] = zero4();
-        mm<C, NDW, false, false, W3>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
-        mm<VK, NDW, false, true, W3>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
+        mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
+        mm<VK, NDW, false, true, W3, UNR>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
         // dQ = dphi * min(phi(q), 1) (elu'(q): 1 for q > 0, exp(q) = phi(q) otherwise)
 #pragma unroll
         for (int j = 0; j < NDW; ++j)
@@ -545,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
         for (int q = 0; q < FBW; ++q) {
             const int f0 = 16 * (kNW * q + w);
-            mm<C, NVB, true, false, W3>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
-            mm<C, NVB, true, false, W3>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
+            mm<C, NVB, true, false, W3, UNR>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
+            mm<C, NVB, true, false, W3, UNR, false, true>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
         }
         put_state<D, C>(S, sm.S, w, lane);
     }
@@ -574,7 +605,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
-    // bf16 storage: products in three bf16 passes, the k steps unrolled
+    // bf16 storage: products in bf16 passes (two where V_aug is an operand),
+    // the k steps unrolled
     constexpr bool W3 = sizeof(T) == 2, UNR = true;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
@@ -636,7 +668,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
             f32x4 b[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) b[j] = zero4();
-            mm<VK, NSB, false, true, W3, UNR>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
+            mm<VK, NSB, false, true, W3, UNR, true, false>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -650,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dk[j] = zero4();
         mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.P, RX, 16 * cs * NDW, dk, lane);
-        mm<VK, NDW, false, true, W3, UNR>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
+        mm<VK, NDW, false, true, W3, UNR, true, false>(sm.V, RV, m0, sm.S, RV, 16 * cs * NDW, dk, lane);
         // dV: P' = phi(K) phi(Q)^T masked, times G; + phi(K) R
         f32x4 dv[NDW];
         {
