@@ -135,8 +135,36 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
     static_assert(K % 4 == 0, "k in pieces of four");
     const int r = lane & 15, q = lane >> 4;
     if constexpr (!W3) {
+        // whole 16-wide k groups: lane group q supplies k = kb + 4q + t in step
+        // t, so a row-direction operand is one 16-byte piece and a column read
+        // puts the four groups on rows 4 apart; a shorter tail takes k0 + q
+        constexpr int K16 = K / 16 * 16;
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 4) {
+        for (int kb = 0; kb < K16; kb += 16) {
+            float a[4];
+            if constexpr (TA) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) a[t] = A[(kb + 4 * q + t) * lda + m0 + r];
+            } else {
+                const float4 x = *reinterpret_cast<const float4 *>(A + (m0 + r) * lda + kb + 4 * q);
+                a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                float b[4];
+                if constexpr (TB) {
+                    const float4 x = *reinterpret_cast<const float4 *>(B + (n0 + 16 * j + r) * ldb + kb + 4 * q);
+                    b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) b[t] = B[(kb + 4 * q + t) * ldb + n0 + 16 * j + r];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc[j], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int k0 = K16; k0 < K; k0 += 4) {
             const float a = TA ? A[(k0 + q) * lda + m0 + r] : A[(m0 + r) * lda + k0 + q];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
