@@ -263,10 +263,11 @@ def run_cpu_baseline_decode(wl, seconds):
 
 
 def backward_on_mfma(wl):
-    """The library runs the backward's two passes on fp32 matrix instructions
-    for ELU+1 (bf16 or fp32 storage) with d_k = d_v = 64 and 64-token chunks,
-    or d_k = d_v = 128 and chunks of a multiple of 32 tokens (run on 32-token
-    tiles)."""
+    """The library runs the backward's two passes on matrix instructions for
+    ELU+1 (bf16 or fp32 storage) with d_k = d_v = 64 and 64-token chunks, or
+    d_k = d_v = 128 and chunks of a multiple of 32 tokens (run on 32-token
+    tiles): fp32 products for fp32 storage, fp32 operands split into bf16 hi
+    and lo parts (two or three bf16 passes per product) for bf16 storage."""
     if wl.dtype not in ("bf16", "f32") or wl.phi != "elu1" or wl.dk != wl.dv:
         return False
     return (wl.dk == 64 and wl.chunk == 64) or (wl.dk == 128 and wl.chunk % 32 == 0)
@@ -603,7 +604,8 @@ def bench_backward(args, wl):
     flops = backward_alg_flops(wl, which)
     ach = flops / (kern_ms * 1e-3) / 1e12
     kname = kernel_symbol(wl, which)
-    # fp32 arithmetic either way: on the matrix cores (dense fp32 MFMA peak) or in fp32 FMAs
+    # fp32-class products either way: on the matrix cores (fp32 instructions, or bf16 hi/lo passes
+    # that keep about 2^-16 of an fp32 product; priced at the dense fp32 MFMA peak) or in fp32 FMAs
     bound = "mfma" if backward_on_mfma(wl) else "alu"
     peak = MFMA_F32_PEAK_TFS if bound == "mfma" else FP32_VECTOR_PEAK_TFS
     roof = {"bound": bound, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
