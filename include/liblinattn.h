@@ -298,8 +298,11 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  *   chunk        16, 32, 64 or 128: tokens per chunk of the chunked form.  The
  *                gradients do not depend on it.  ELU+1 (bf16 or fp32) with
  *                d_k = d_v = 64 and 64-token chunks, or d_k = d_v = 128 and
- *                chunks of 32, 64 or 128 tokens (run on 32-token tiles), takes
- *                fp32 matrix instructions; everything else runs on
+ *                chunks of 32, 64 or 128 tokens (run on 32-token tiles), runs
+ *                on matrix instructions with fp32-class products (fp32
+ *                instructions for fp32 storage; for bf16 storage bf16
+ *                instructions on operands split into hi and lo parts, about
+ *                2^-16 relative); everything else runs on
  *                fp32-arithmetic kernels that tile at most 16 tokens whatever
  *                is asked.
  *   Q, K, V      forward inputs; dO [B,H,N,d_v] the gradient of the loss with
