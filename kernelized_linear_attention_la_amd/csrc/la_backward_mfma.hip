@@ -1,18 +1,21 @@
 // Backward of the causal normalised form on the matrix cores: ELU+1,
 // d_k = d_v = D, bf16 or fp32 storage, D = 64 on 64-token tiles and D = 128 on
 // 32-token tiles (the derivation and the fp32-FMA kernels are in
-// la_backward.hip; this file runs the same chunked algebra with
-// v_mfma_f32_16x16x4_f32; the chunkwise form gives the same gradients for
-// every chunk length, so a D = 128 call asking for 64- or 128-token chunks
-// runs on 32-token tiles).
+// la_backward.hip; this file runs the same chunked algebra on the matrix
+// cores; the chunkwise form gives the same gradients for every chunk length,
+// so a D = 128 call asking for 64- or 128-token chunks runs on 32-token tiles).
 //
-// The arithmetic stays fp32 throughout: the normalised backward cancels
+// The products stay fp32-class throughout: the normalised backward cancels
 // (g_i . v_j + h_i = g_i . (v_j - o_i), and o_i, h_i come from the recomputed
-// forward), so operands rounded to bf16 lose several percent of the gradient;
-// fp32 matrix instructions keep the fp32 result.  For that instruction lane l
-// supplies A[l%16][l/16] and B[l/16][l%16] of a 16x4 by 4x16 step and receives
-// C[4(l/16)+e][l%16]; both operands are single fp32 values, so either
-// orientation of a tile is read straight from its one row-major copy in LDS.
+// forward), so operands rounded once to bf16 lose several percent of the
+// gradient.  fp32 storage runs v_mfma_f32_16x16x4_f32 on fp32 operands; bf16
+// storage splits each fp32 operand into bf16 hi and lo parts at the read and
+// runs v_mfma_f32_16x16x32_bf16 passes (hi hi + hi lo + lo hi, or two passes
+// where an operand is exact in bf16), about 2^-16 relative.  Every tile has
+// one row-major fp32 copy in LDS, read in either orientation: along a row as
+// aligned 16-byte pieces, down a column element by element, with the k
+// assignment of each instruction chosen so that both kinds of read are free
+// of LDS bank conflicts at the 4 mod 16 row strides.
 // Per chunk the tiles are phi(Q), phi(K), [V | 1 | 0], G_aug, the carried
 // state image and a score tile; value-column widths are padded to D + 4 for
 // contractions and D + 16 (whole 16-column blocks) for outputs.
