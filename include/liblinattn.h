@@ -322,8 +322,12 @@ la_status la_retention_decode_step(const la_problem *p, const float *gamma, cons
  * scan, then the forward-direction pass (recomputes the outputs, writes dQ and
  * the per-token g, h to ws), the per-segment sums of psi g^T, psi h (no
  * timing slot), their reverse scan (writes dS_in, dz_in), and the
- * reverse-direction pass (dK, dV); on the matrix-instruction kernels the
- * forward-direction pass also forms the per-segment sums (five kernels).
+ * reverse-direction pass (dK, dV).  On the matrix-instruction kernels three:
+ * the forward's per-segment sums, the forward-direction pass (it adds the
+ * earlier segments' sums to S_in, z_in itself and also forms the per-segment
+ * sums of psi g^T, psi h) and the reverse-direction pass (it adds the later
+ * segments' sums to dS_out, dz_out itself; its first segment writes dS_in,
+ * dz_in); LA_BSLOT_FWD_SCAN and LA_BSLOT_RSCAN are then not launched.
  * Outputs must not overlap inputs or each other.
  */
 enum { LA_BSLOT_FWD_SUMS = 0, LA_BSLOT_FWD_SCAN = 1, LA_BSLOT_DQ = 2, LA_BSLOT_RSCAN = 3, LA_BSLOT_DKV = 4,

@@ -568,8 +568,9 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
     if (ev)
         for (int i = 0; i < LA_BSLOTS; ++i) ev->launched[i] = 0;
 
-    // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan.
-    // The sums run on the matrix-core state pass when the segments are whole
+    // forward prefix entering each segment: per-segment sums, then S_in + exclusive scan
+    // (a scan launch for the fp32-FMA passes; the matrix-core passes add the
+    // sums in their prologues).  The sums run on the matrix-core state pass when the segments are whole
     // chunks of a length it takes (same boundaries, same P): the backward's own
     // tile, else 128 or 64 tokens.
     const bool mf = backward_mfma_supported(sh, chunk);
@@ -589,24 +590,26 @@ LA_API la_status la_backward_causal_chunked(const la_problem *p, int chunk, cons
     a.st.S_dst = wsS; a.st.z_dst = wsz;
     a.st.dst_slice = g.P * nS; a.st.dst_seg = nS; a.st.zdst_slice = g.P * nz; a.st.zdst_seg = nz;
     if (launch_fwd(sums_mf, a, hs, slot(LA_BSLOT_FWD_SUMS)) != hipSuccess) return LA_ERR_DEVICE;
-    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, nullptr, nullptr, false, hs, slot(LA_BSLOT_FWD_SCAN)) !=
-        hipSuccess)
-        return LA_ERR_DEVICE;
     if (mf) {
+        // the matrix-core passes gather their starting states from the
+        // per-segment sums themselves (no scan launches)
         BwdMfmaArgs m;
         m.D = sh.dk; m.BH = sh.BH; m.N = sh.N; m.P = g.P; m.seg_chunks = g.seg_chunks; m.n_chunks = g.n_chunks;
         m.f32 = sh.dtype == kF32;
         m.Q = Q; m.K = K; m.V = V; m.dO = dO;
         m.dQ = dQ; m.dK = dK; m.dV = dV;
-        m.Spre = wsS; m.zpre = wsz;
+        m.Ssum = wsS; m.zsum = wsz;
+        m.S_in = S_in; m.z_in = z_in;
+        m.dS_out = dS_out; m.dz_out = dz_out;
+        m.dS_in = dS_in; m.dz_in = dz_in;
         m.U = reinterpret_cast<float *>(wsb + wl.u_off);
         m.G = reinterpret_cast<float *>(wsb + wl.g_off);
         if (launch_bwd_dq_mfma(m, hs, slot(LA_BSLOT_DQ)) != hipSuccess) return LA_ERR_DEVICE;
-        if (launch_bwd_rscan(sh.BH, g.P, sh.dp, sh.dv, m.U, dS_out, dz_out, dS_in, dz_in, hs, slot(LA_BSLOT_RSCAN)) !=
-            hipSuccess)
-            return LA_ERR_DEVICE;
         return launch_bwd_dkv_mfma(m, hs, slot(LA_BSLOT_DKV)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
     }
+    if (launch_scan(sh, g.P, wsS, wsz, S_in, z_in, nullptr, nullptr, false, hs, slot(LA_BSLOT_FWD_SCAN)) !=
+        hipSuccess)
+        return LA_ERR_DEVICE;
     BwdLaunch b;
     b.sh = sh; b.sg = g;
     b.Q = Q; b.K = K; b.V = V; b.dO = dO;

@@ -352,6 +352,41 @@ __device__ __forceinline__ void put_state(const f32x4 (&S)[BCfg<D, C>::FBW][BCfg
         for (int j = 0; j < B::NVB; ++j) put_rows(T, B::RV, 16 * (kNW * q + w), 16 * j, S[q][j], lane);
 }
 
+// Carried-state accumulators (feature row 16 (4q + w) + 4g + e, augmented
+// column 16j + c16 <= D) += the sums of segments first, first + step, ..
+// (count of them), added in that order; at(p, f, col) is a readable address
+// for every column (columns past D are loaded and not added).  PB segments'
+// loads are in flight at a time.
+template <int D, int C, typename Acc, typename At>
+__device__ __forceinline__ void add_segments(Acc &S, int first, int count, int step, At at, int w, int lane) {
+    using B = BCfg<D, C>;
+    constexpr int PER = B::FBW * B::NVB * 4, PB = PER * 8 <= 160 ? 8 : 160 / PER;
+    const int g = lane >> 4, c16 = lane & 15;
+    for (int i0 = 0; i0 < count; i0 += PB) {
+        float v[PB][B::FBW][B::NVB][4];
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int p = first + step * (i0 + b < count ? i0 + b : 0);
+#pragma unroll
+            for (int q = 0; q < B::FBW; ++q)
+#pragma unroll
+                for (int j = 0; j < B::NVB; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[b][q][j][e] = *at(p, 16 * (kNW * q + w) + 4 * g + e, 16 * j + c16);
+        }
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+            if (i0 + b < count)
+#pragma unroll
+                for (int q = 0; q < B::FBW; ++q)
+#pragma unroll
+                    for (int j = 0; j < B::NVB; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * j + c16 <= D) S[q][j][e] += v[b][q][j][e];
+    }
+}
+
 // 16 rows x D columns of T (rows m0..) -> rows of dst, 8 values per lane and step
 template <int D, typename ST>
 __device__ __forceinline__ void store_rows(const float *T, int ld, int m0, int rows, ST *dst, size_t row0, int lane) {
@@ -437,11 +472,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     T *dQs = static_cast<T *>(a.dQ) + (size_t)bh * N * D;
     float *Gw = a.G + (size_t)bh * N * VK;
 
-    // carried state S_aug (feature rows 16 (4q + w) + 4g + e, value columns 16j + c16) and U
+    // carried state S_aug (feature rows 16 (4q + w) + 4g + e, value columns
+    // 16j + c16) entering the segment: [S_in | z_in] (or zero) plus the
+    // forward sums of segments 0 .. seg - 1, in that order; and U
     f32x4 S[FBW][NVB], U[FBW][NVB];
     {
-        const float *Sp = a.Spre + ((size_t)bh * a.P + seg) * D * D;
-        const float *zp = a.zpre + ((size_t)bh * a.P + seg) * D;
 #pragma unroll
         for (int q = 0; q < FBW; ++q)
 #pragma unroll
@@ -449,10 +484,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
-                    S[q][j][e] = col < D ? Sp[f * D + col] : (col == D ? zp[f] : 0.f);
+                    float s0 = 0.f;
+                    if (a.S_in) {
+                        const float x = col < D ? a.S_in[((size_t)bh * D + f) * D + col] : a.z_in[(size_t)bh * D + f];
+                        s0 = col <= D ? x : 0.f;
+                    }
+                    S[q][j][e] = s0;
                 }
                 U[q][j] = zero4();
             }
+        const float *Sg = a.Ssum + (size_t)bh * a.P * D * D, *zg = a.zsum + (size_t)bh * a.P * D;
+        add_segments<D, C>(S, 0, seg, 1, [&](int p, int f, int col) {
+            return col < D ? Sg + ((size_t)p * D + f) * D + col : zg + (size_t)p * D + f;
+        }, w, lane);
     }
     put_state<D, C>(S, sm.S, w, lane);
 
@@ -657,9 +701,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     T *dVs = static_cast<T *>(a.dV) + (size_t)bh * N * D;
     const float *Gw = a.G + (size_t)bh * N * VK;
 
+    // R_aug entering the segment from above: [dS_out | dz_out] (or zero) plus
+    // the sums of segments P - 1 down to seg + 1, in that order; segment 0
+    // adds its own sum as well for dS_in, dz_in (the gradient of the starting
+    // state)
     f32x4 R[FBW][NVB];
     {
-        const float *Rs = a.U + ((size_t)bh * a.P + seg) * D * (D + 1);
 #pragma unroll
         for (int q = 0; q < FBW; ++q)
 #pragma unroll
@@ -667,8 +714,35 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
-                    R[q][j][e] = col <= D ? Rs[f * (D + 1) + col] : 0.f;
+                    float r0 = 0.f;
+                    if (a.dS_out) {
+                        const float x =
+                            col < D ? a.dS_out[((size_t)bh * D + f) * D + col] : a.dz_out[(size_t)bh * D + f];
+                        r0 = col <= D ? x : 0.f;
+                    }
+                    R[q][j][e] = r0;
                 }
+        const float *Ug = a.U + (size_t)bh * a.P * D * (D + 1);
+        auto at = [&](int p, int f, int col) { return Ug + ((size_t)p * D + f) * (D + 1) + (col < D ? col : D); };
+        add_segments<D, C>(R, a.P - 1, a.P - 1 - seg, -1, at, w, lane);
+        if (seg == 0 && a.dS_in) {
+            f32x4 T0[FBW][NVB];
+#pragma unroll
+            for (int q = 0; q < FBW; ++q)
+#pragma unroll
+                for (int j = 0; j < NVB; ++j) T0[q][j] = R[q][j];
+            add_segments<D, C>(T0, 0, 1, 1, at, w, lane);
+#pragma unroll
+            for (int q = 0; q < FBW; ++q)
+#pragma unroll
+                for (int j = 0; j < NVB; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 16 * (kNW * q + w) + 4 * g + e, col = 16 * j + c16;
+                        if (col < D) a.dS_in[((size_t)bh * D + f) * D + col] = T0[q][j][e];
+                        else if (col == D) a.dz_in[(size_t)bh * D + f] = T0[q][j][e];
+                    }
+        }
     }
     put_state<D, C>(R, sm.S, w, lane);
 

@@ -182,8 +182,11 @@ struct BwdMfmaArgs {
     int f32;                                // storage: fp32 (1) or bf16 (0)
     const void *Q, *K, *V, *dO;
     void *dQ, *dK, *dV;
-    const float *Spre, *zpre;  // forward prefix per segment
-    float *U;                  // [BH][P][D * (D + 1)]
+    const float *Ssum, *zsum;  // forward sums per segment, [BH][P][D][D] and [BH][P][D]
+    const float *S_in, *z_in;  // forward starting state [BH][D][D], [BH][D], or both null (zero)
+    const float *dS_out, *dz_out;  // gradient of the final state, or both null (zero)
+    float *dS_in, *dz_in;      // gradient of the starting state (written), or both null
+    float *U;                  // [BH][P][D * (D + 1)]: per-segment sums of phi(Q)^T G_aug
     float *G;                  // [BH][N][backward_mfma_g_floats()]
 };
 // ELU+1 (bf16 or fp32), d_k = d_v = 64 with 64-token chunks, or 128 with chunks of a multiple of 32
