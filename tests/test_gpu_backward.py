@@ -89,6 +89,8 @@ CASES = [
     (1, 1, 40, 5, 3, "f32", "elu1", 0, 32, True),       # odd widths
     (2, 1, 77, 16, 8, "f32", "favor", 24, 32, True),
     (2, 2, 333, 64, 64, "bf16", "elu1", 0, 64, False),
+    (1, 2, 2048, 64, 64, "bf16", "elu1", 0, 64, True),   # d64 matrix cores, 32 one-chunk segments a slice:
+                                                         # the passes' starting-state gathers span four rounds
     (1, 2, 190, 64, 64, "bf16", "favor", 256, 64, True),  # largest FAVOR+ feature count
     (1, 2, 300, 128, 128, "bf16", "elu1", 0, 128, True),  # largest widths (matrix cores, 32-token tiles)
     (1, 1, 517, 128, 96, "f32", "elu1", 0, 16, True),
@@ -131,9 +133,10 @@ def test_backward_ignores_workspace_contents():
 
 def test_backward_d128_matrix_cores_many_segments_and_dirty_workspace():
     # bf16 ELU+1 d128 on the matrix-core kernels: 2 x 4 slices of 4096 tokens
-    # give several segments of 32-token tiles per slice, so the forward sums,
-    # both scans and the segment hand-off of the gradient sums all take part;
-    # the workspace starts as 0xFF bytes (no initial contents are needed)
+    # give several segments of 32-token tiles per slice, so the forward sums
+    # and both passes' gathers of the other segments' sums (the starting
+    # state of the dQ pass, the suffix and dS_in of the dK/dV pass) all take
+    # part; the workspace starts as 0xFF bytes (no initial contents are needed)
     _say("B2 H4 N4096 d128 bf16 chunk 128, state, dirty workspace (slices (0,1), (1,3))")
     got, ref = _run(9, 2, 4, 4096, 128, 128, "bf16", "elu1", 0, 128, True,
                     slices=(np.array([[0], [1]]), np.array([[1], [3]])), workspace_fill=255)

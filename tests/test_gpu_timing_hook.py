@@ -4,9 +4,10 @@ Every call that takes the hook must report, in `launched`, the kernels it
 enqueued, record a positive duration for each of them, and give results bit
 for bit equal to the same call without the hook (the events only bracket the
 launches).  Covered: the causal single pass (bf16, d = 64), the causal fp32
-path in three launches (segment sums, their scan, the chunk pass), and the
+path in three launches (segment sums, their scan, the chunk pass), the
 chunkwise GLA and gated delta-rule calls (per-chunk launch, state chain,
-outputs).
+outputs), and the backward: three launches on the matrix cores (forward sums,
+dQ pass, dK/dV pass; no scan launches) and five on the fp32-arithmetic kernels.
 """
 import ctypes
 import sys
@@ -38,17 +39,17 @@ def _device():
 
 
 class _Events:
-    """hipEvent pairs for the three slots, through the runtime the library links."""
+    """hipEvent pairs for the slots, through the runtime the library links."""
 
-    def __init__(self):
+    def __init__(self, slots=SLOTS, kind=None):
         self.lib = la.lib()
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.kev = la.LaKernelEvents()
+        self.kev = (kind or la.LaKernelEvents)()
         self.pairs = {}
-        for sl in SLOTS:
+        for sl in slots:
             pair = []
             for _ in range(2):
                 ev = ctypes.c_void_p()
@@ -70,18 +71,21 @@ class _Events:
             self.lib.hipEventDestroy(b)
 
 
-def _check(name, run, expect):
-    """run(events) -> tuple of result tensors; expect: the slots that must be launched."""
+def _check(name, run, expect, slots=SLOTS, kind=None, exact=False):
+    """run(events) -> tuple of result tensors; expect: the slots that must be
+    launched (exact: and no others)."""
     ref = [t.clone() for t in run(None)]
     torch.cuda.synchronize()
-    ev = _Events()
+    ev = _Events(slots, kind)
     try:
         got = run(ev.kev)
         torch.cuda.synchronize()
-        launched = [sl for sl in SLOTS if ev.kev.launched[sl]]
+        launched = [sl for sl in slots if ev.kev.launched[sl]]
         times = {sl: ev.elapsed_ms(sl) for sl in launched}
         _say(name, "launched", launched, "ms", {k: round(v, 4) for k, v in times.items()})
         assert set(expect) <= set(launched), (launched, expect)
+        if exact:
+            assert set(launched) == set(expect), (launched, expect)
         assert all(t > 0 for t in times.values()), times
         for a, b in zip(ref, got):
             assert torch.equal(a, b), name
@@ -141,3 +145,29 @@ def test_delta_chunked_reports_three_launches(dtype):
         O = la.la_forward_delta_chunked(q, k, v, be, alpha=al, S_out=S, workspace=ws, events=events)
         return O, S.clone()
     _check(f"delta chunked {dtype}", run, SLOTS)
+
+
+BSLOTS = (la.LA_BSLOT_FWD_SUMS, la.LA_BSLOT_FWD_SCAN, la.LA_BSLOT_DQ, la.LA_BSLOT_RSCAN, la.LA_BSLOT_DKV)
+
+
+@pytest.mark.parametrize("path", ["matrix cores", "fp32 arithmetic"])
+def test_backward_reports_its_launches(path):
+    # bf16 ELU+1 d64 with 64-token chunks runs on the matrix cores (the passes
+    # gather their starting states: no scan launches); FAVOR+ runs on the
+    # fp32-arithmetic kernels with both scans
+    if path == "matrix cores":
+        fi = inputs.custom_inputs(9104, 1, 2, 1000, 64, 64, scale=64 ** -0.5, dtype="bf16", phi="elu1", m=0)
+        phi, W, expect = "elu1", None, (la.LA_BSLOT_FWD_SUMS, la.LA_BSLOT_DQ, la.LA_BSLOT_DKV)
+    else:
+        fi = inputs.custom_inputs(9105, 1, 2, 300, 32, 32, scale=32 ** -0.25, dtype="bf16", phi="favor", m=32)
+        phi, W, expect = "favor", torch.from_numpy(fi.W).cuda(), BSLOTS
+    dp = 32 if phi == "favor" else 64
+    dO = inputs.grad_output(9106, 1, 2, fi.Q.f32.shape[2], fi.V.f32.shape[3], "bf16")
+    q, k, v, g = to_device(fi.Q), to_device(fi.K), to_device(fi.V), to_device(dO)
+    S_in, z_in = (torch.from_numpy(x).cuda() for x in inputs.positive_state(9107, 1, 2, dp, v.shape[3]))
+    dS, dz = (torch.from_numpy(x).cuda() for x in inputs.state_grads(9107, 1, 2, dp, v.shape[3]))
+
+    def run(events):
+        return la.la_backward_causal_chunked(q, k, v, g, 64, phi=phi, W=W, S_in=S_in, z_in=z_in, dS_out=dS,
+                                             dz_out=dz, state_grad=True, events=events)
+    _check(f"backward, {path}", run, expect, slots=BSLOTS, kind=la.LaBackwardEvents, exact=True)
