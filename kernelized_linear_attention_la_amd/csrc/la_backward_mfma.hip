@@ -76,11 +76,13 @@ struct alignas(16) BTiles {  // every row stride and tile size a multiple of 4 f
     float P[C * B::RX];    // phi(Q) rows [token][feature]
     float K[C * B::RX];    // phi(K) rows
     float V[C * B::RV];    // [v | 1 | 0] rows
-    float G[C * B::RV];    // G_aug rows [token][value column]
+    float G[C * B::RV];    // rows [token][value column]: bf16 storage G'_aug = [dO | -(dO . o) | 0]
+                           // (G_aug = G'_aug / den), fp32 storage G_aug
     float S[D * B::RV];    // carried state, rows [feature][value column]
     float W[C * B::RW];    // masked scores of the tile
     float DEN[C];          // normaliser of each query row (dQ pass)
     float DOT[B::CS][C];   // dO . num of each query row over one column split
+    float RDEN[C];         // bf16 storage: 1 / normaliser of each query row (0 past the last row)
 };
 
 // v = row[k..k+3], row[k+16..k+19] from a 16-byte aligned LDS row, zeros past
@@ -131,10 +133,14 @@ __device__ __forceinline__ void wsplit8(const float (&x)[8], W8 &hi, W8 &lo) {
 // normalised backward cancels, so single bf16 operands would lose several
 // percent, while the split keeps about 2^-16.  EA / EB: that operand is exact
 // in bf16 (V_aug of bf16 storage), its lo part is zero and its pass is
-// skipped (same result).  Otherwise fp32 operands.
-template <int K, int NB, bool TA, bool TB, bool W3 = false, bool UNR = false, bool EA = false, bool EB = false>
+// skipped (same result); AXK / BXK: the operand is exact for k < AXK / BXK
+// (a k step wholly below skips the pass); BXN: B is exact in its columns
+// below BXN (whole 16-column blocks).  Otherwise fp32 operands.  AS: A(m, k)
+// is multiplied by as[k] as it is read.
+template <int K, int NB, bool TA, bool TB, bool W3 = false, bool UNR = false, bool EA = false, bool EB = false,
+          int AXK = 0, int BXK = 0, int BXN = 0, bool AS = false>
 __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float *B, int ldb, int n0, f32x4 (&acc)[NB],
-                                   int lane) {
+                                   int lane, const float *as = nullptr) {
     static_assert(K % 4 == 0, "k in pieces of four");
     const int r = lane & 15, q = lane >> 4;
     if constexpr (!W3) {
@@ -152,6 +158,10 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
                 const float4 x = *reinterpret_cast<const float4 *>(A + (m0 + r) * lda + kb + 4 * q);
                 a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
             }
+            if constexpr (AS) {
+                const float4 sc = *reinterpret_cast<const float4 *>(as + kb + 4 * q);
+                a[0] *= sc.x; a[1] *= sc.y; a[2] *= sc.z; a[3] *= sc.w;
+            }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 float b[4];
@@ -168,7 +178,8 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
         }
 #pragma unroll
         for (int k0 = K16; k0 < K; k0 += 4) {
-            const float a = TA ? A[(k0 + q) * lda + m0 + r] : A[(m0 + r) * lda + k0 + q];
+            float a = TA ? A[(k0 + q) * lda + m0 + r] : A[(m0 + r) * lda + k0 + q];
+            if constexpr (AS) a *= as[k0 + q];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const float b = TB ? B[(n0 + 16 * j + r) * ldb + k0 + q] : B[(k0 + q) * ldb + n0 + 16 * j + r];
@@ -195,6 +206,13 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
             } else {
                 row8<K>(A + (m0 + r) * lda, k0 + 4 * q, av);
             }
+            if constexpr (AS) {
+                float sv[8];
+                row8<K>(as, k0 + 4 * q, sv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) av[e] *= sv[e];
+            }
+            const bool ax = EA || k0 + 32 <= AXK;  // A exact in bf16 over this k step
             W8 ah, al;
             wsplit8(av, ah, al);
 #pragma unroll
@@ -210,11 +228,12 @@ __device__ __forceinline__ void mm(const float *A, int lda, int m0, const float 
                         bv[e] = k < K ? v : 0.f;
                     }
                 }
+                const bool bx = EB || k0 + 32 <= BXK || n0 + 16 * j + 16 <= BXN;  // B exact here
                 W8 bh, bl;
                 wsplit8(bv, bh, bl);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bh.v, acc[j], 0, 0, 0);
-                if constexpr (!EB) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, acc[j], 0, 0, 0);
-                if constexpr (!EA) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, acc[j], 0, 0, 0);
+                if (!bx) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah.v, bl.v, acc[j], 0, 0, 0);
+                if (!ax) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al.v, bh.v, acc[j], 0, 0, 0);
             }
         }
     }
@@ -330,14 +349,21 @@ __device__ __forceinline__ void load_g(const float *Gw, int t0, int rows, GPiece
         p.x[i] = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + (t < rows ? t : 0)) * VK + 4 * min(c4, VK / 4 - 1)]);
     }
 }
+// stored row: [dO | -(dO . o) | den | 0 0]; the tile gets [dO | -(dO . o) | 0 0 0]
+// and RDEN the reciprocal of den (0 past the last row)
 template <int D, int C>
-__device__ __forceinline__ void put_g(const GPieces<D, C> &p, int rows, float *R, int tid) {
+__device__ __forceinline__ void put_g(const GPieces<D, C> &p, int rows, float *R, float *RDEN, int tid) {
     using G = GPieces<D, C>;
     constexpr int VK = BCfg<D, C>::VK;
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
         const int u = tid + i * kThreads, t = u / (G::RV / 4), c4 = u % (G::RV / 4);
-        if (u < G::NU) *reinterpret_cast<float4 *>(&R[t * G::RV + 4 * c4]) = keep4(t < rows && 4 * c4 < VK, p.x[i]);
+        float4 x = keep4(t < rows && 4 * c4 < VK, p.x[i]);
+        if (4 * c4 == D) {
+            if (u < G::NU) RDEN[t] = t < rows ? 1.f / x.y : 0.f;
+            x.y = 0.f;
+        }
+        if (u < G::NU) *reinterpret_cast<float4 *>(&R[t * G::RV + 4 * c4]) = x;
     }
 }
 
@@ -450,8 +476,9 @@ template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
     // bf16 storage: products in bf16 passes (two where V_aug is an operand),
-    // the k steps unrolled
-    constexpr bool W3 = sizeof(T) == 2, UNR = true;
+    // the k steps unrolled; the tile holds G'_aug (GP), whose dO columns are
+    // exact in bf16
+    constexpr bool W3 = sizeof(T) == 2, UNR = true, GP = W3;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -591,6 +618,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
                 for (int k = 0; k < CS; ++k) s += sm.DOT[k][r];
                 dot[e] = s * rden[e];  // dO . o
             }
+            // G'_aug = [dO | -(dO . o) | 0]: its dO columns are the stored values
+            // (exact in bf16); the factor 1 / den goes to dphi(Q) and U instead.
+            // fp32 storage keeps G_aug = G'_aug / den in the tile.
 #pragma unroll
             for (int j = 0; j < NBN; ++j) {
                 f32x4 gv;
@@ -598,10 +628,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const bool in = m0 + 4 * g + e < rows;
                     const int col = 16 * (NB0 + j) + c16;
-                    gv[e] = !in ? 0.f : (col < D ? dov[j][e] * rden[e] : (col == D ? -dot[e] * rden[e] : 0.f));
+                    if constexpr (GP)
+                        gv[e] = !in ? 0.f : (col < D ? dov[j][e] : (col == D ? -dot[e] : 0.f));
+                    else
+                        gv[e] = !in ? 0.f : (col < D ? dov[j][e] * rden[e] : (col == D ? -dot[e] * rden[e] : 0.f));
                 }
                 put_rows(sm.G, RV, m0, 16 * (NB0 + j), gv, lane);
             }
+            if (GP && SP == 0 && c16 == 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.RDEN[m0 + 4 * g + e] = m0 + 4 * g + e < rows ? rden[e] : 0.f;
         };
         if constexpr (CS == 1) {
             g_aug(std::integral_constant<int, 0>{});
@@ -612,19 +648,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
                 g_aug(std::integral_constant<int, 1>{});
         }
         row_sync<CS>();  // G_aug rows of the row block are complete
-        // G_aug rows to the workspace (VK floats per token) for the dK/dV pass
+        // G'_aug rows to the workspace (VK floats per token, den in column D + 1;
+        // fp32 storage: G_aug) for the dK/dV pass
         for (int idx = lane + 64 * cs; idx < 16 * VK / 4; idx += 64 * CS) {
             const int r = idx / (VK / 4), c4 = idx % (VK / 4);
-            if (m0 + r < rows)
-                *reinterpret_cast<float4 *>(&Gw[(size_t)(t0 + m0 + r) * VK + 4 * c4]) =
-                    *reinterpret_cast<const float4 *>(&sm.G[(m0 + r) * RV + 4 * c4]);
+            if (m0 + r < rows) {
+                float4 x = *reinterpret_cast<const float4 *>(&sm.G[(m0 + r) * RV + 4 * c4]);
+                if (GP && 4 * c4 == D) x.y = sm.DEN[m0 + r];
+                *reinterpret_cast<float4 *>(&Gw[(size_t)(t0 + m0 + r) * VK + 4 * c4]) = x;
+            }
         }
-        // A = G_aug V_aug^T, masked; dphi(Q) = (A (.) M) phi(K) + G_aug S_aug^T
+        // A' = G'_aug V_aug^T, masked; dphi(Q) = ((A' (.) M) phi(K) + G'_aug S_aug^T) / den
         {
             f32x4 s[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) s[j] = zero4();
-            mm<VK, NSB, false, true, W3, UNR, false, true>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
+            mm<VK, NSB, false, true, W3, UNR, false, true, GP ? D : 0>(sm.G, RV, m0, sm.V, RV, 16 * cs * NSB, s, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
 #pragma unroll
@@ -638,20 +677,27 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dp[j] = zero4();
         mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.K, RX, 16 * cs * NDW, dp, lane);
-        mm<VK, NDW, false, true, W3, UNR>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
+        mm<VK, NDW, false, true, W3, UNR, false, false, GP ? D : 0>(sm.G, RV, m0, sm.S, RV, 16 * cs * NDW, dp, lane);
         // dQ = dphi * min(phi(q), 1) (elu'(q): 1 for q > 0, exp(q) = phi(q) otherwise)
 #pragma unroll
         for (int j = 0; j < NDW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (GP) dp[j][e] *= sm.RDEN[m0 + 4 * g + e];
                 dp[j][e] *= fminf(sm.P[(m0 + 4 * g + e) * RX + 16 * (cs * NDW + j) + c16], 1.f);
+            }
         store_dwide<D, C, T>(dp, sm.W, m0, cs, rows, dQs, t0, lane);
         block_sync_lds();  // every wave's G_aug rows are in LDS, the state image is read
-        // U += phi(Q)^T G_aug, S_aug += phi(K)^T V_aug (this wave's feature rows)
+        // U += phi(Q)^T G_aug = (phi(Q) / den)^T G'_aug, S_aug += phi(K)^T V_aug
+        // (this wave's feature rows)
 #pragma unroll
         for (int q = 0; q < FBW; ++q) {
             const int f0 = 16 * (kNW * q + w);
-            mm<C, NVB, true, false, W3, UNR>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
+            if constexpr (GP)
+                mm<C, NVB, true, false, W3, UNR, false, false, 0, 0, D, true>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane,
+                                                                               sm.RDEN);
+            else
+                mm<C, NVB, true, false, W3, UNR>(sm.P, RX, f0, sm.G, RV, 0, U[q], lane);
             mm<C, NVB, true, false, W3, UNR, false, true>(sm.K, RX, f0, sm.V, RV, 0, S[q], lane);
         }
         put_state<D, C>(S, sm.S, w, lane);
@@ -681,8 +727,9 @@ template <int D, int C, typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
     using B = BCfg<D, C>;
     // bf16 storage: products in bf16 passes (two where V_aug is an operand),
-    // the k steps unrolled
-    constexpr bool W3 = sizeof(T) == 2, UNR = true;
+    // the k steps unrolled; the tile holds G'_aug (GP), whose dO columns are
+    // exact in bf16
+    constexpr bool W3 = sizeof(T) == 2, UNR = true, GP = W3;
     constexpr int RX = B::RX, RV = B::RV, RW = B::RW, VK = B::VK, NVB = B::NVB, FBW = B::FBW, NSB = B::NSB,
                   NDW = B::NDW, CS = B::CS, RB = B::RB;
     __shared__ BTiles<D, C> sm;
@@ -764,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         put_phi<D, C>(xq, rows, sm.P, tid);
         put_phi<D, C>(xk, rows, sm.K, tid);
         put_vaug<D, C>(xv, rows, sm.V, tid);
-        put_g<D, C>(xg, rows, sm.G, tid);
+        put_g<D, C>(xg, rows, sm.G, sm.RDEN, tid);
         fetch(max(c - 1, c_begin));
         block_sync_lds();
 
@@ -773,12 +820,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
             f32x4 b[NSB];
 #pragma unroll
             for (int j = 0; j < NSB; ++j) b[j] = zero4();
-            mm<VK, NSB, false, true, W3, UNR, true, false>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
+            mm<VK, NSB, false, true, W3, UNR, true, false, 0, GP ? D : 0>(sm.V, RV, m0, sm.G, RV, 16 * cs * NSB, b, lane);
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
+                const float rq = sm.RDEN[16 * (cs * NSB + j) + c16];  // column = query token
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * (cs * NSB + j) + c16 < m0 + 4 * g + e) b[j][e] = 0.f;
+                    b[j][e] = 16 * (cs * NSB + j) + c16 < m0 + 4 * g + e ? 0.f : b[j][e] * (GP ? rq : 1.f);
                 put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), b[j], lane);
             }
         }
@@ -796,18 +844,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
             for (int j = 0; j < NSB; ++j) p[j] = zero4();
             mm<D, NSB, false, true, W3, UNR>(sm.K, RX, m0, sm.P, RX, 16 * cs * NSB, p, lane);
             row_sync<CS>();  // the row block's waves have read the scores B before W is overwritten
+            // P' / den of the query (column), so that P' G_aug = (P' / den) G'_aug
+            // (bf16 storage)
 #pragma unroll
             for (int j = 0; j < NSB; ++j) {
+                const float rq = sm.RDEN[16 * (cs * NSB + j) + c16];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * (cs * NSB + j) + c16 < m0 + 4 * g + e) p[j][e] = 0.f;
+                    p[j][e] = 16 * (cs * NSB + j) + c16 < m0 + 4 * g + e ? 0.f : p[j][e] * (GP ? rq : 1.f);
                 put_rows(sm.W, RW, m0, 16 * (cs * NSB + j), p[j], lane);
             }
         }
         row_sync<CS>();
 #pragma unroll
         for (int j = 0; j < NDW; ++j) dv[j] = zero4();
-        mm<C, NDW, false, false, W3, UNR>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
+        mm<C, NDW, false, false, W3, UNR, false, GP>(sm.W, RW, m0, sm.G, RV, 16 * cs * NDW, dv, lane);
         mm<D, NDW, false, false, W3, UNR>(sm.K, RX, m0, sm.S, RV, 16 * cs * NDW, dv, lane);
         // dK = dphi(K) * min(phi(k), 1)
 #pragma unroll
@@ -818,9 +869,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(BwdMfmaArgs a) {
         store_dwide<D, C, T>(dk, sm.W, m0, cs, rows, dKs, t0, lane);
         store_dwide<D, C, T>(dv, sm.W, m0, cs, rows, dVs, t0, lane);
         block_sync_lds();  // the state image is no longer read
-        // R_aug += phi(Q)^T G_aug (this wave's feature rows)
+        // R_aug += phi(Q)^T G_aug = (phi(Q) / den)^T G'_aug (this wave's feature rows)
 #pragma unroll
-        for (int q = 0; q < FBW; ++q) mm<C, NVB, true, false, W3, UNR>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV, 0, R[q], lane);
+        for (int q = 0; q < FBW; ++q)
+            mm<C, NVB, true, false, W3, UNR, false, false, 0, 0, GP ? D : 0, GP>(sm.P, RX, 16 * (kNW * q + w), sm.G, RV,
+                                                                                  0, R[q], lane, sm.RDEN);
         put_state<D, C>(R, sm.S, w, lane);
     }
 }
