@@ -267,7 +267,8 @@ def backward_on_mfma(wl):
     ELU+1 (bf16 or fp32 storage) with d_k = d_v = 64 and 64-token chunks, or
     d_k = d_v = 128 and chunks of a multiple of 32 tokens (run on 32-token
     tiles): fp32 products for fp32 storage, fp32 operands split into bf16 hi
-    and lo parts (two or three bf16 passes per product) for bf16 storage."""
+    and lo parts (one to three bf16 passes per k step: the lo pass of an
+    operand exact in bf16 is skipped) for bf16 storage."""
     if wl.dtype not in ("bf16", "f32") or wl.phi != "elu1" or wl.dk != wl.dv:
         return False
     return (wl.dk == 64 and wl.chunk == 64) or (wl.dk == 128 and wl.chunk % 32 == 0)

@@ -10,8 +10,10 @@
 // forward), so operands rounded once to bf16 lose several percent of the
 // gradient.  fp32 storage runs v_mfma_f32_16x16x4_f32 on fp32 operands; bf16
 // storage splits each fp32 operand into bf16 hi and lo parts at the read and
-// runs v_mfma_f32_16x16x32_bf16 passes (hi hi + hi lo + lo hi, or two passes
-// where an operand is exact in bf16), about 2^-16 relative.  Every tile has
+// runs v_mfma_f32_16x16x32_bf16 passes (hi hi + hi lo + lo hi; the lo pass of
+// an operand that is exact in bf16 is skipped: V_aug, and the dO columns of
+// G'_aug = [dO | -(dO . o)], which bf16 storage keeps in place of G_aug with
+// 1/den applied outside the products), about 2^-16 relative.  Every tile has
 // one row-major fp32 copy in LDS, read in either orientation: along a row as
 // aligned 16-byte pieces, down a column element by element, with the k
 // assignment of each instruction chosen so that both kinds of read are free
