@@ -351,8 +351,10 @@ __device__ __forceinline__ void load_g(const float *Gw, int t0, int rows, GPiece
         p.x[i] = *reinterpret_cast<const float4 *>(&Gw[(size_t)(t0 + (t < rows ? t : 0)) * VK + 4 * min(c4, VK / 4 - 1)]);
     }
 }
-// stored row: [dO | -(dO . o) | den | 0 0]; the tile gets [dO | -(dO . o) | 0 0 0]
-// and RDEN the reciprocal of den (0 past the last row)
+// stored row (bf16 storage): [dO | -(dO . o) | den | 0 0]; the tile gets
+// [dO | -(dO . o) | 0 0 0] and RDEN the reciprocal of den (0 past the last
+// row).  fp32 storage stores G_aug, whose column D + 1 is zero: RDEN is then
+// not read.
 template <int D, int C>
 __device__ __forceinline__ void put_g(const GPieces<D, C> &p, int rows, float *R, float *RDEN, int tid) {
     using G = GPieces<D, C>;
@@ -661,6 +663,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             }
         }
         // A' = G'_aug V_aug^T, masked; dphi(Q) = ((A' (.) M) phi(K) + G'_aug S_aug^T) / den
+        // (fp32 storage: G_aug in the tile, no division)
         {
             f32x4 s[NSB];
 #pragma unroll
@@ -690,8 +693,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(BwdMfmaArgs a) {
             }
         store_dwide<D, C, T>(dp, sm.W, m0, cs, rows, dQs, t0, lane);
         block_sync_lds();  // every wave's G_aug rows are in LDS, the state image is read
-        // U += phi(Q)^T G_aug = (phi(Q) / den)^T G'_aug, S_aug += phi(K)^T V_aug
-        // (this wave's feature rows)
+        // U += phi(Q)^T G_aug (bf16 storage: (phi(Q) / den)^T G'_aug), S_aug +=
+        // phi(K)^T V_aug (this wave's feature rows)
 #pragma unroll
         for (int q = 0; q < FBW; ++q) {
             const int f0 = 16 * (kNW * q + w);
